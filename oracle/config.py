@@ -1,0 +1,36 @@
+"""Format parameters of the packed cache (oracle side).
+
+Reading adopted (the pages name no sizes): head_dim D = 128, b in {2, 3, 4}
+bits, token block B in {64, 128}, pack run R = 32 tokens with R dividing B.
+The run is the unit that gets its own width and offset; the block is the unit
+of quantisation (K), permutation and append.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    head_dim: int = 128
+    bits: int = 4
+    block: int = 64
+    run: int = 32
+    permute: bool = True
+
+    def __post_init__(self):
+        assert self.bits in (2, 3, 4), "b must be 2, 3 or 4"
+        assert self.block in (64, 128), "B must be 64 or 128"
+        assert self.run == 32, "R must be 32"
+        assert self.block % self.run == 0
+        assert self.head_dim == 128, "D must be 128"
+
+    @property
+    def levels(self) -> int:
+        """L = 2^b - 1, the largest quantised value."""
+        return (1 << self.bits) - 1
+
+    def runs(self, n: int) -> int:
+        """Number of runs in a block holding n tokens: ceil(n / R)."""
+        return -(-n // self.run)

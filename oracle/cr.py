@@ -1,0 +1,55 @@
+"""Exact compression-ratio accounting (oracle).
+
+The pages report PackKV's "memory reduction rate" relative to quantisation
+baselines (abstract; TL;DR) without defining it.  Reading adopted: report
+the compression ratio CR = fp16 bytes / compressed bytes, three ways, plus
+the same ratio for plain b-bit quantisation with the same fp16 parameters:
+
+* ideal    - payload bits (each run at R * w) + 8 header bits per run
+             + parameter bits (K: 32 per channel per block; V: 32 per token);
+* physical - the record bytes as stored, 16-byte padding included;
+* full     - physical plus the one-byte-per-token permutation table.
+
+plain quantisation = T * D * b bits + the same parameter bits.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .stream import StreamCache
+from .unpack import decode_record
+
+
+def ratios(cache: StreamCache, which: str) -> dict:
+    cfg = cache.cfg
+    D, R, b = cfg.head_dim, cfg.run, cfg.bits
+    raw_bits = 16 * cache.n_tokens * D
+    ideal = 0
+    params = 0
+    arena = cache.arena(which)
+    off = cache.offsets(which)
+    for j in range(len(cache.blocks)):
+        n = cache.block_tokens(j)
+        d = decode_record(which, arena[off[j]:off[j + 1]], n, D, cfg.block, R)
+        par = 32 * D if which == "K" else 32 * n
+        ideal += R * int(d.w.sum()) + 8 * d.w.size + par
+        params += par
+    phys = 8 * len(arena)
+    full = phys + 8 * cache.n_tokens
+    plain = cache.n_tokens * D * b + params
+    return {
+        "cr_ideal": raw_bits / ideal,
+        "cr_phys": raw_bits / phys,
+        "cr_full": raw_bits / full,
+        "cr_plain_quant": raw_bits / plain,
+        "ideal_bits": ideal,
+        "phys_bytes": len(arena),
+    }
+
+
+def closed_form_full_width(which: str, bits: int, block: int, run: int, D: int) -> float:
+    """CR when every run needs the full b bits: 16 / (b + 8/R + 32/B) for K,
+    16 / (b + 8/R + 32/D) for V (per-value bit cost of payload, header, params)."""
+    per = block if which == "K" else D
+    return 16.0 / (bits + 8.0 / run + 32.0 / per)

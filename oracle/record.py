@@ -1,0 +1,114 @@
+"""Channel-direction bit-packing and the block record layout (oracle encoder).
+
+PackKV's second step packs the quantised integers losslessly "in channel
+direction" (Fig. 2 caption, step (2)); Fig. 4's caption calls the context
+(token) axis the channel direction, i.e. a packed unit is the values of one
+channel over consecutive tokens.  Readings adopted:
+
+* a run is R = 32 consecutive slots of one channel inside a block; run r of
+  a block holding n tokens covers slots r*R .. min(r*R + R, n) - 1;
+* each (run, channel) is stored at its own minimal width
+  w = bit_length(max - min) (0 <= w <= b) relative to its minimum m, as
+  u = q - m; the header byte of the run is (w << 4) | m;
+* the R slots of a run fill exactly w little-endian 32-bit words, slot i in
+  bits [i*w, i*w + w) of the run's 32*w-bit string; slots past n hold u = 0.
+
+Record of one block (all integers little-endian, every section contiguous):
+
+    K:  scale[D] fp16 | zero[D] fp16 | hdr[nr][D] u8 | 0-pad to 16 B |
+        payload | 0-pad to 16 B
+    V:  scale[B] fp16 | zero[B] fp16 (slot order; slots >= n hold 0) |
+        hdr[nr][D] u8 | 0-pad to 16 B | payload | 0-pad to 16 B
+
+payload = for r in 0..nr-1, for c in 0..D-1: the w words of run (r, c).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .fp16bits import f16_bits
+
+
+def _pad16(n: int) -> int:
+    return (n + 15) & ~15
+
+
+def run_widths(q_slots: np.ndarray, run: int):
+    """Per-(run, channel) minimum m and width w of slot-ordered ints [n, D].
+
+    w = bit_length(max - min): the fewest bits that hold every q - min.
+    Returns (w, m), each int64 [nr, D].
+    """
+    q = np.asarray(q_slots, dtype=np.int64)
+    n, D = q.shape
+    nr = -(-n // run)
+    w = np.zeros((nr, D), np.int64)
+    m = np.zeros((nr, D), np.int64)
+    for r in range(nr):
+        seg = q[r * run:min(n, (r + 1) * run)]
+        lo = seg.min(axis=0)
+        hi = seg.max(axis=0)
+        m[r] = lo
+        w[r] = [int(x).bit_length() for x in (hi - lo)]
+    return w, m
+
+
+def pack_payload(q_slots: np.ndarray, w: np.ndarray, m: np.ndarray, run: int) -> bytes:
+    """The payload words of all (run, channel) pairs, run-major then channel."""
+    q = np.asarray(q_slots, dtype=np.int64)
+    n, D = q.shape
+    out = bytearray()
+    for r in range(w.shape[0]):
+        for c in range(D):
+            wr = int(w[r, c])
+            if wr == 0:
+                continue
+            bits = 0
+            for i in range(run):
+                t = r * run + i
+                u = int(q[t, c] - m[r, c]) if t < n else 0
+                assert 0 <= u < (1 << wr)
+                bits |= u << (i * wr)
+            out += bits.to_bytes(4 * wr, "little")
+    return bytes(out)
+
+
+def header_bytes(w: np.ndarray, m: np.ndarray) -> bytes:
+    assert np.all(w <= 4) and np.all(m <= 15) and np.all(m >= 0)
+    return ((w << 4) | m).astype(np.uint8).tobytes()
+
+
+def build_record(kind: str, q_slots, scale, zero, block: int, run: int) -> bytes:
+    """Assemble the record bytes of one block.
+
+    kind 'K': scale/zero have D entries (per channel).
+    kind 'V': scale/zero have n entries in slot order, padded to B with 0.
+    """
+    q = np.asarray(q_slots, dtype=np.int64)
+    n, D = q.shape
+    if kind == "K":
+        assert len(scale) == D and len(zero) == D
+        sc, ze = np.asarray(scale), np.asarray(zero)
+    elif kind == "V":
+        assert len(scale) == n and len(zero) == n
+        sc = np.zeros(block)
+        ze = np.zeros(block)
+        sc[:n] = scale
+        ze[:n] = zero
+    else:
+        raise ValueError(kind)
+    w, m = run_widths(q, run)
+    head = f16_bits(sc).astype("<u2").tobytes() + f16_bits(ze).astype("<u2").tobytes()
+    head += header_bytes(w, m)
+    head += bytes(_pad16(len(head)) - len(head))
+    body = pack_payload(q, w, m, run)
+    body += bytes(_pad16(len(body)) - len(body))
+    return head + body
+
+
+def record_size(kind: str, w: np.ndarray, D: int, block: int) -> int:
+    """Closed-form record size in bytes from the run widths."""
+    nr = w.shape[0]
+    params = 4 * (D if kind == "K" else block)
+    return _pad16(params + nr * D) + _pad16(4 * int(w.sum()))

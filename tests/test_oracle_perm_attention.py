@@ -1,0 +1,179 @@
+"""Pins of the oracle's permutation, attention products, CR and append."""
+
+import itertools
+
+import numpy as np
+import pytest
+
+import kvsynth
+from oracle import Config, perm, stream, attention, cr, record
+
+
+def brute_groups(qk, qv, R):
+    """Greedy grouping by exhaustive choice: at each step try every R-subset of
+    the remaining tokens that contains the seed and keep the one whose sorted
+    (distance, index) keys are lexicographically smallest."""
+    feats = np.concatenate([qk, qv], axis=1)
+    remaining = list(range(len(qk)))
+    out = []
+    while remaining:
+        seed = remaining[0]
+        key = {t: (int(np.abs(feats[t] - feats[seed]).sum()), t) for t in remaining}
+        k = min(R, len(remaining))
+        best = min((sorted(key[t] for t in sub) for sub in itertools.combinations(remaining, k)
+                    if seed in sub))
+        out.extend(t for _, t in best)
+        remaining = [t for t in remaining if t not in {t for _, t in best}]
+    return out
+
+
+def test_greedy_order_matches_exhaustive_search():
+    rng = np.random.default_rng(0)
+    for trial in range(30):
+        n = int(rng.integers(1, 9))
+        qk = rng.integers(0, 4, (n, 3))
+        qv = rng.integers(0, 4, (n, 2))
+        assert perm.greedy_order(qk, qv, 2) == brute_groups(qk, qv, 2)
+        assert perm.greedy_order(qk, qv, 3) == brute_groups(qk, qv, 3)
+
+
+@pytest.mark.parametrize("n", [1, 17, 64])
+def test_permutation_is_a_bijection_with_seed_first(n):
+    rng = np.random.default_rng(n)
+    qk = rng.integers(0, 16, (n, 128))
+    qv = rng.integers(0, 16, (n, 128))
+    order = perm.greedy_order(qk, qv, 32)
+    assert sorted(order) == list(range(n))
+    taken = set()
+    for g in range(0, n, 32):
+        assert order[g] == min(set(range(n)) - taken)
+        taken |= set(order[g:g + 32])
+
+
+def test_identity_fallback_and_switch():
+    rng = np.random.default_rng(1)
+    qk = rng.integers(0, 16, (64, 128))
+    qv = rng.integers(0, 16, (64, 128))
+    p = perm.block_permutation(qk, qv, 32, True)
+    ident = list(range(64))
+    assert perm.payload_words(qk, qv, p, 32) <= perm.payload_words(qk, qv, ident, 32)
+    if list(p) != ident:
+        assert perm.payload_words(qk, qv, p, 32) < perm.payload_words(qk, qv, ident, 32)
+    assert list(perm.block_permutation(qk, qv, 32, False)) == ident
+
+
+def test_grouping_recovers_clusters():
+    """Shuffled clustered tokens: the grouping puts each cluster in one run."""
+    k, v = kvsynth.structured_kv(64, 128, 64, 32, seed=4, noise=0.0)
+    code = stream.encode_block(k, v, Config(bits=4, block=64))
+    rows = k[code.perm].astype(np.float64)
+    for g in (0, 32):
+        assert np.all(rows[g:g + 32] == rows[g])
+    assert record.run_widths(code.qk_slots, 32)[0].max() == 0
+
+
+def test_attention_is_unchanged_by_the_permutation():
+    k, v = kvsynth.structured_kv(300, 128, 64, 32, seed=7)
+    q = np.random.default_rng(2).standard_normal((2, 128)).astype(np.float16)
+    outs = []
+    for p in (True, False):
+        c = stream.compress(k, v, Config(bits=4, block=64, permute=p))
+        kh, vh, _, _ = stream.decode_stream(c)
+        s = attention.qk(q, kh)
+        outs.append(attention.pv(attention.softmax(s, 128), vh))
+        # the dequantised rows are the same multiset: equal after un-permuting
+        if p:
+            kt, vt = stream.token_order(c, kh), stream.token_order(c, vh)
+        else:
+            assert np.array_equal(kt, kh) and np.array_equal(vt, vh)
+    assert attention.rel_l2(outs[0], outs[1]) < 1e-12
+
+
+def test_gemv_definitions_against_loops():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((3, 8))
+    K = rng.standard_normal((5, 8))
+    V = rng.standard_normal((5, 8))
+    s = attention.qk(q, K)
+    for g in range(3):
+        for t in range(5):
+            assert abs(s[g, t] - sum(q[g, c] * K[t, c] for c in range(8))) < 1e-12
+    p = attention.softmax(s, 8)
+    o = attention.pv(p, V)
+    for g in range(3):
+        for c in range(8):
+            assert abs(o[g, c] - sum(p[g, t] * V[t, c] for t in range(5))) < 1e-12
+    onehot = np.zeros((1, 5))
+    onehot[0, 3] = 1
+    assert np.array_equal(attention.pv(onehot, V)[0], V[3])
+    assert np.allclose(attention.qk(2 * q, K), 2 * s)
+
+
+def test_softmax_properties():
+    s = np.random.default_rng(4).standard_normal((4, 1000)) * 30
+    p = attention.softmax(s, 128)
+    assert np.all(np.abs(p.sum(-1) - 1) < 1e-14) and np.all(p >= 0)
+    assert np.allclose(attention.softmax(s + 123.0, 128), p, rtol=1e-12, atol=0)
+    one = attention.softmax(np.array([[0.0, 0.0]]), 128)
+    assert np.all(one == 0.5)
+
+
+@pytest.mark.parametrize("bits,block", [(4, 64), (2, 64), (3, 64), (4, 128)])
+def test_cr_matches_closed_form_when_every_run_is_full_width(bits, block):
+    """Construct blocks whose every run spans 0..L in every channel."""
+    L = (1 << bits) - 1
+    T = 4 * block
+    rng = np.random.default_rng(bits)
+    qk = rng.integers(0, L + 1, (T, 128))
+    qk[::32] = 0
+    qk[1::32] = L
+    qv = rng.integers(0, L + 1, (T, 128))
+    qv[:, 126], qv[:, 127] = 0, L          # every token spans 0..L
+    qv[0::32], qv[1::32], qv[2::32], qv[3::32] = 0, L, 0, L
+    qv[0::32, 5] = L                       # rows 0-3 of every run: each token
+    qv[1::32, 5] = 0                       # still spans 0..L, and every
+    qv[2::32, 6] = L                       # channel sees both 0 and L
+    qv[3::32, 6] = 0
+    c = stream.compress(qk.astype(np.float16), qv.astype(np.float16),
+                        Config(bits=bits, block=block, permute=False))
+    for which in "KV":
+        r = cr.ratios(c, which)
+        cf = cr.closed_form_full_width(which, bits, block, 32, 128)
+        assert abs(r["cr_ideal"] - cf) < 1e-12
+        assert abs(r["cr_phys"] - cf) < 1e-12     # all sections 16-byte aligned here
+    assert abs(cr.closed_form_full_width("K", 4, 64, 32, 128) - 1024 / 304) < 1e-15
+
+
+def test_cr_counts_the_bits_the_packer_writes():
+    k, v = kvsynth.structured_kv(250, 128, 64, 32, seed=3)
+    c = stream.compress(k, v, Config(bits=3, block=64))
+    for which in "KV":
+        r = cr.ratios(c, which)
+        total = 0
+        for j, b in enumerate(c.blocks):
+            rec = b.k_record if which == "K" else b.v_record
+            qs = b.qk_slots if which == "K" else b.qv_slots
+            w, m = record.run_widths(qs, 32)
+            payload = record.pack_payload(qs, w, m, 32)
+            par = 32 * 128 if which == "K" else 32 * len(b.perm)
+            total += 8 * len(payload) + 8 * w.size + par
+        assert r["ideal_bits"] == total
+
+
+@pytest.mark.parametrize("t0,extra", [(0, 70), (50, 30), (64, 65), (130, 1)])
+def test_append_equals_one_shot(t0, extra):
+    cfg = Config(bits=3, block=64)
+    w = kvsynth.WORKLOADS["append-64k"]
+    k, v = kvsynth.stream_kv(w, 3, tokens=t0 + extra)
+    if t0:
+        c = stream.compress(k[:t0], v[:t0], cfg)
+    else:
+        c = stream.StreamCache(cfg, [], 0, k[:0], v[:0])
+    c = stream.append(c, k[t0:], v[t0:])
+    ref = stream.compress(k, v, cfg)
+    assert c.n_tokens == ref.n_tokens
+    for which in "KV":
+        assert c.arena(which) == ref.arena(which)
+        assert np.array_equal(c.offsets(which), ref.offsets(which))
+    assert np.array_equal(c.perm_table(), ref.perm_table())
+    assert np.array_equal(c.tail_k, ref.tail_k) and np.array_equal(c.tail_v, ref.tail_v)

@@ -1,0 +1,126 @@
+"""Pins of the oracle's packing: widths, record layout, lossless round trip.
+
+``bitstring_decode`` below reads a record through a string of '0'/'1'
+characters, a third way of reading the layout, independent of both the
+oracle's encoder (big integers) and its decoder (64-bit windows).
+"""
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import kvsynth
+from oracle import Config, record, unpack, stream, quant
+
+
+def bitstring_decode(kind, buf, n, D, B, R):
+    nr = -(-n // R)
+    npar = D if kind == "K" else B
+    hdr = list(buf[4 * npar:4 * npar + nr * D])
+    p0 = -(-(4 * npar + nr * D) // 16) * 16
+    q = np.zeros((nr * R, D), np.int64)
+    pos = p0
+    for r in range(nr):
+        for c in range(D):
+            w, m = hdr[r * D + c] >> 4, hdr[r * D + c] & 15
+            words = buf[pos:pos + 4 * w]
+            pos += 4 * w
+            # bit k of the run = bit (k % 32) of word k // 32
+            s = "".join(format(words[4 * j + (k // 8) % 4], "08b")[::-1][k % 8]
+                        for j in range(w) for k in range(32))
+            for i in range(R):
+                u = int(s[i * w:(i + 1) * w][::-1], 2) if w else 0
+                q[r * R + i, c] = m + u
+    return q[:n], pos
+
+
+def test_width_is_minimal():
+    for span in range(0, 16):
+        w = int(span).bit_length()
+        assert (1 << w) > span and (w == 0 or (1 << (w - 1)) <= span)
+        qs = np.array([[3], [3 + span]])
+        ww, mm = record.run_widths(qs, 32)
+        assert ww[0, 0] == w and mm[0, 0] == 3
+
+
+@pytest.mark.parametrize("bits,block", [(2, 64), (3, 64), (4, 64), (4, 128), (3, 128)])
+@pytest.mark.parametrize("n", [1, 5, 31, 32, 33, 63, 64, 100, 128])
+def test_record_roundtrip_and_layout(bits, block, n):
+    if n > block:
+        pytest.skip("n > B")
+    cfg = Config(bits=bits, block=block)
+    rng = np.random.default_rng(n * 7 + bits)
+    if n % 2:
+        k, v = kvsynth.structured_kv(n, 128, block, 32, seed=n)
+    else:
+        k = rng.standard_normal((n, 128)).astype(np.float16)
+        v = rng.standard_normal((n, 128)).astype(np.float16)
+    code = stream.encode_block(k, v, cfg)
+    for kind, rec, qs in (("K", code.k_record, code.qk_slots), ("V", code.v_record, code.qv_slots)):
+        d = unpack.decode_record(kind, rec, n, 128, block, 32)
+        assert np.array_equal(d.q, qs)
+        bq, end = bitstring_decode(kind, rec, n, 128, block, 32)
+        assert np.array_equal(bq, qs)
+        assert len(rec) == d.size == record.record_size(kind, d.w, 128, block)
+        assert len(rec) % 16 == 0
+        assert not any(rec[end:])                         # tail padding is zero
+        npar = 128 if kind == "K" else block
+        hdr_end = 4 * npar + d.w.size
+        p0 = -(-hdr_end // 16) * 16
+        assert not any(rec[hdr_end:p0])                   # header padding is zero
+        assert np.all(d.w <= bits)
+        # padding slots of a partial last run are zero bits: re-pack check
+        assert record.pack_payload(qs, d.w, d.m, 32) == rec[p0:p0 + 4 * int(d.w.sum())]
+
+
+def test_v_params_are_slot_ordered_and_zero_padded():
+    cfg = Config(bits=4, block=64)
+    k, v = kvsynth.structured_kv(40, 128, 64, 32, seed=2)
+    code = stream.encode_block(k, v, cfg)
+    _, sv, zv = quant.quantize_v_tokens(v, 4)
+    d = unpack.decode_record("V", code.v_record, 40, 128, 64, 32)
+    assert np.array_equal(d.scale, sv[code.perm]) and np.array_equal(d.zero, zv[code.perm])
+    raw = np.frombuffer(code.v_record[:256], "<u2")
+    assert not raw[40:64].any() and not raw[64 + 40:128].any()
+
+
+@settings(max_examples=40, deadline=None)
+@given(st.integers(1, 64), st.sampled_from([2, 3, 4]), st.integers(0, 2**31 - 1))
+def test_hypothesis_roundtrip(n, bits, seed):
+    rng = np.random.default_rng(seed)
+    cfg = Config(bits=bits, block=64)
+    # mixture: some channels nearly constant so narrow widths appear
+    base = rng.standard_normal((1, 128)) * 3
+    spread = np.where(rng.random(128) < 0.5, 0.01, 1.0)
+    k = (base + spread * rng.standard_normal((n, 128))).astype(np.float16)
+    v = rng.standard_normal((n, 128)).astype(np.float16)
+    code = stream.encode_block(k, v, cfg)
+    for kind, rec, qs in (("K", code.k_record, code.qk_slots), ("V", code.v_record, code.qv_slots)):
+        d = unpack.decode_record(kind, rec, n, 128, 64, 32)
+        assert np.array_equal(d.q, qs)
+
+
+def test_lossless_grid_values_are_reproduced_exactly():
+    """If every group is zero + k*h with k spanning 0..L, decoding returns the input."""
+    rng = np.random.default_rng(9)
+    cfg = Config(bits=4, block=64)
+    T, D, L = 200, 128, 15
+    # K: per channel and per block, an fp16 grid
+    k = np.empty((T, D))
+    for j in range(0, T, 64):
+        n = min(64, T - j)
+        kk = rng.integers(0, L + 1, (n, D))
+        kk[0], kk[-1] = 0, L
+        h = 2.0 ** rng.integers(-6, 2, D)
+        z = rng.integers(-40, 40, D) * h
+        k[j:j + n] = z + kk * h
+    kint = rng.integers(0, L + 1, (T, D))
+    kint[:, 0], kint[:, 1] = 0, L
+    hv = 2.0 ** rng.integers(-6, 2, (T, 1))
+    v = rng.integers(-40, 40, (T, 1)) * hv + kint * hv
+    k16, v16 = k.astype(np.float16), v.astype(np.float16)
+    assert np.array_equal(k16.astype(np.float64), k) and np.array_equal(v16.astype(np.float64), v)
+    c = stream.compress(k16, v16, cfg)
+    kh, vh, _, _ = stream.decode_stream(c)
+    assert np.array_equal(stream.token_order(c, kh), k)
+    assert np.array_equal(stream.token_order(c, vh), v)
