@@ -1,0 +1,10 @@
+"""decode_gemv_amd - PackKV's compressed KV cache and fused decompress-GEMVs on MI355X.
+
+The hot path lives in the HIP library ``libpackkv.so`` (C ABI in
+``include/packkv.h``); this package only marshals torch tensors into it.
+"""
+
+from ._lib import PackKVError, load as load_library  # noqa: F401
+from .cache import PackedKVCache, softmax_rows  # noqa: F401
+
+__all__ = ["PackedKVCache", "softmax_rows", "PackKVError", "load_library"]

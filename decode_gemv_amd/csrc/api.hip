@@ -1,0 +1,294 @@
+// C ABI of the packkv library: argument validation, work decomposition and
+// kernel launches on the caller's stream.  No device memory is allocated
+// here; every buffer belongs to the caller.
+#include <stdlib.h>
+#include <string.h>
+
+#include "kernels.hpp"
+
+using namespace packkv;
+
+namespace {
+
+constexpr uint64_t kArenaSlack = 64;   // over-read room for 16-byte vector loads
+
+int check_cfg(const packkv_config_t* c) {
+  if (!c) return PACKKV_EINVAL;
+  if (c->head_dim != kD || c->run_tokens != kR) return PACKKV_EUNSUPPORTED;
+  if (c->bits < 2 || c->bits > 4) return PACKKV_EUNSUPPORTED;
+  if (c->block_tokens != 64 && c->block_tokens != 128) return PACKKV_EUNSUPPORTED;
+  if (c->permute != 0 && c->permute != 1) return PACKKV_EINVAL;
+  return PACKKV_OK;
+}
+
+int64_t max_blocks_of(const packkv_config_t* c, int64_t max_tokens) {
+  return (max_tokens + c->block_tokens - 1) / c->block_tokens;
+}
+
+uint64_t stride_bytes(const packkv_config_t* c, int64_t max_tokens) {
+  const int B = c->block_tokens;
+  const uint64_t rk = (uint64_t)max_record_bytes(false, B, c->bits);
+  const uint64_t rv = (uint64_t)max_record_bytes(true, B, c->bits);
+  const uint64_t per = rk > rv ? rk : rv;
+  const uint64_t need = (uint64_t)max_blocks_of(c, max_tokens) * per + kArenaSlack;
+  return (need + 255) & ~(uint64_t)255;
+}
+
+int check_cache(const packkv_cache_t* c) {
+  if (!c) return PACKKV_EINVAL;
+  int e = check_cfg(&c->cfg);
+  if (e) return e;
+  if (c->n_streams < 1 || c->max_tokens < 1 || c->n_tokens < 0 || c->n_tokens > c->max_tokens)
+    return PACKKV_EINVAL;
+  if (!c->k_arena || !c->v_arena || !c->k_off || !c->v_off || !c->perm || !c->tail_k || !c->tail_v ||
+      !c->status)
+    return PACKKV_EINVAL;
+  if (c->arena_stride % 256 || c->arena_stride >= (1ull << 32) ||
+      c->arena_stride < stride_bytes(&c->cfg, c->max_tokens))
+    return PACKKV_EINVAL;
+  if (max_blocks_of(&c->cfg, c->max_tokens) >= (1ll << 31)) return PACKKV_EINVAL;
+  return PACKKV_OK;
+}
+
+// Blocks per workgroup for the GEMVs: enough workgroups to fill 256 CUs
+// several times over, at most 64 blocks each.
+int gemv_blocks_per_wg(int64_t n_streams, int nb) {
+  static int env = -1;
+  if (env < 0) {
+    const char* s = getenv("PACKKV_BLOCKS_PER_WG");
+    env = s ? atoi(s) : 0;
+  }
+  if (env > 0) return env > 64 ? 64 : (env < 4 ? 4 : env);
+  int64_t total = n_streams * (int64_t)nb;
+  int64_t j = (total + 8191) / 8192;
+  if (j < 4) j = 4;
+  if (j > 64) j = 64;
+  return (int)j;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PACKKV_OK : PACKKV_EHIP; }
+
+GemvArgs gemv_args(const packkv_cache_t* c, bool is_v) {
+  GemvArgs a;
+  memset(&a, 0, sizeof(a));
+  a.arena = is_v ? c->v_arena : c->k_arena;
+  a.arena_stride = c->arena_stride;
+  a.off = is_v ? c->v_off : c->k_off;
+  a.off_stride = max_blocks_of(&c->cfg, c->max_tokens) + 1;
+  a.n_tokens = c->n_tokens;
+  a.nb = (int)((c->n_tokens + c->cfg.block_tokens - 1) / c->cfg.block_tokens);
+  a.bits = c->cfg.bits;
+  a.blocks_per_wg = gemv_blocks_per_wg(c->n_streams, a.nb);
+  a.splits = (a.nb + a.blocks_per_wg - 1) / a.blocks_per_wg;
+  a.status = c->status;
+  return a;
+}
+
+EncArgs enc_args(const packkv_cache_t* c) {
+  EncArgs a;
+  memset(&a, 0, sizeof(a));
+  a.bits = c->cfg.bits;
+  a.B = c->cfg.block_tokens;
+  a.permute = c->cfg.permute;
+  a.k_arena = c->k_arena;
+  a.v_arena = c->v_arena;
+  a.arena_stride = c->arena_stride;
+  a.arena_limit = c->arena_stride - kArenaSlack;
+  a.k_off = c->k_off;
+  a.v_off = c->v_off;
+  a.off_stride = max_blocks_of(&c->cfg, c->max_tokens) + 1;
+  a.perm = c->perm;
+  a.perm_stride = max_blocks_of(&c->cfg, c->max_tokens) * c->cfg.block_tokens;
+  a.status = c->status;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int packkv_cache_sizes(const packkv_config_t* cfg, int32_t n_streams, int64_t max_tokens,
+                       packkv_sizes_t* out) {
+  int e = check_cfg(cfg);
+  if (e) return e;
+  if (!out || n_streams < 1 || max_tokens < 1) return PACKKV_EINVAL;
+  const int64_t mb = max_blocks_of(cfg, max_tokens);
+  out->max_blocks = mb;
+  out->arena_stride = stride_bytes(cfg, max_tokens);
+  if (out->arena_stride >= (1ull << 32)) return PACKKV_EINVAL;
+  out->arena_bytes = (uint64_t)n_streams * out->arena_stride;
+  out->off_bytes = (uint64_t)n_streams * (uint64_t)(mb + 1) * 4;
+  out->perm_bytes = (uint64_t)n_streams * (uint64_t)mb * (uint64_t)cfg->block_tokens;
+  out->tail_bytes = (uint64_t)n_streams * (uint64_t)cfg->block_tokens * kD * 2;
+  return PACKKV_OK;
+}
+
+uint64_t packkv_arena_stride_bytes(const packkv_config_t* cfg, int64_t max_tokens) {
+  if (check_cfg(cfg) || max_tokens < 1) return 0;
+  return stride_bytes(cfg, max_tokens);
+}
+
+uint64_t packkv_pv_workspace_bytes(const packkv_cache_t* c, int32_t group) {
+  if (check_cache(c) || group < 1) return 0;
+  const int64_t mb = max_blocks_of(&c->cfg, c->max_tokens);
+  const int64_t splits = (mb + 3) / 4;     // blocks per workgroup is at least 4
+  return (uint64_t)c->n_streams * (uint64_t)group * (uint64_t)splits * kD * sizeof(float);
+}
+
+int packkv_compress_block(packkv_cache_t* c, const void* k_f16, const void* v_f16, int64_t n_tokens,
+                          void* stream) {
+  int e = check_cache(c);
+  if (e) return e;
+  if (!k_f16 || !v_f16 || n_tokens < 1) return PACKKV_EINVAL;
+  if (c->n_tokens != 0) return PACKKV_ESTATE;
+  if (n_tokens > c->max_tokens) return PACKKV_ECAPACITY;
+  hipStream_t st = (hipStream_t)stream;
+  const int B = c->cfg.block_tokens;
+  const int nb = (int)((n_tokens + B - 1) / B);
+  EncArgs a = enc_args(c);
+  a.k = (const uint16_t*)k_f16;
+  a.v = (const uint16_t*)v_f16;
+  a.src_stream = n_tokens * kD;
+  a.src_block = (int64_t)B * kD;
+  a.n_tokens = n_tokens;
+  a.mode = kPass1;
+  if ((e = hip_status(launch_encode(a, c->n_streams, nb, st)))) return e;
+  if ((e = hip_status(launch_scan_offsets(c->k_off, c->v_off, a.off_stride, c->n_streams, nb, st))))
+    return e;
+  a.mode = kPass2;
+  if ((e = hip_status(launch_encode(a, c->n_streams, nb, st)))) return e;
+  const int64_t nfull = n_tokens / B;
+  const int rem = (int)(n_tokens - nfull * B);
+  if (rem) {
+    e = hip_status(launch_stage_tail((const uint16_t*)k_f16 + nfull * B * kD,
+                                     (const uint16_t*)v_f16 + nfull * B * kD, n_tokens * kD, c->tail_k,
+                                     c->tail_v, B, 0, rem, c->n_streams, st));
+    if (e) return e;
+  }
+  c->n_tokens = n_tokens;
+  return PACKKV_OK;
+}
+
+int packkv_append_tokens(packkv_cache_t* c, const void* k_f16, const void* v_f16, int32_t n_new,
+                         void* stream) {
+  int e = check_cache(c);
+  if (e) return e;
+  if (!k_f16 || !v_f16 || n_new < 1) return PACKKV_EINVAL;
+  if (c->n_tokens + n_new > c->max_tokens) return PACKKV_ECAPACITY;
+  hipStream_t st = (hipStream_t)stream;
+  const int B = c->cfg.block_tokens;
+  EncArgs a = enc_args(c);
+  a.k = c->tail_k;
+  a.v = c->tail_v;
+  a.src_stream = (int64_t)B * kD;
+  a.src_block = 0;
+  a.mode = kTail;
+  int done = 0;
+  while (done < n_new) {
+    const int64_t T = c->n_tokens;
+    const int n_tail = (int)(T % B);
+    const int cnt = (n_new - done) < (B - n_tail) ? (n_new - done) : (B - n_tail);
+    e = hip_status(launch_stage_tail((const uint16_t*)k_f16 + (int64_t)done * kD,
+                                     (const uint16_t*)v_f16 + (int64_t)done * kD, (int64_t)n_new * kD,
+                                     c->tail_k, c->tail_v, B, n_tail, cnt, c->n_streams, st));
+    if (e) return e;
+    a.block0 = (int)(T / B);
+    a.n_tokens = T + cnt;
+    if ((e = hip_status(launch_encode(a, c->n_streams, 1, st)))) return e;
+    c->n_tokens = T + cnt;
+    done += cnt;
+  }
+  return PACKKV_OK;
+}
+
+int packkv_qk_gemv(const packkv_cache_t* c, const void* q_f16, int32_t group, float* scores, int64_t ld,
+                   void* stream) {
+  int e = check_cache(c);
+  if (e) return e;
+  if (!q_f16 || !scores || group < 1) return PACKKV_EINVAL;
+  if (c->n_tokens < 1) return PACKKV_ESTATE;
+  if (ld < c->n_tokens) return PACKKV_EINVAL;
+  GemvArgs a = gemv_args(c, false);
+  a.G = group;
+  a.q = (const uint16_t*)q_f16;
+  a.scores = scores;
+  a.ld = ld;
+  return hip_status(launch_qk(a, c->cfg.block_tokens, c->n_streams, (hipStream_t)stream));
+}
+
+int packkv_pv_gemv(const packkv_cache_t* c, const float* p, int64_t ld, int32_t group, float* out,
+                   void* workspace, uint64_t ws_bytes, void* stream) {
+  int e = check_cache(c);
+  if (e) return e;
+  if (!p || !out || !workspace || group < 1) return PACKKV_EINVAL;
+  if (c->n_tokens < 1) return PACKKV_ESTATE;
+  if (ld < c->n_tokens) return PACKKV_EINVAL;
+  GemvArgs a = gemv_args(c, true);
+  a.G = group;
+  a.p = p;
+  a.ld = ld;
+  a.ws = (float*)workspace;
+  const uint64_t need = (uint64_t)c->n_streams * group * a.splits * kD * sizeof(float);
+  if (ws_bytes < need) return PACKKV_EINVAL;
+  return hip_status(launch_pv(a, c->cfg.block_tokens, c->n_streams, out, (hipStream_t)stream));
+}
+
+int packkv_decompress(const packkv_cache_t* c, int32_t which, int32_t mode, void* out, void* stream) {
+  int e = check_cache(c);
+  if (e) return e;
+  if (!out || (which != 0 && which != 1) || (mode != 0 && mode != 1)) return PACKKV_EINVAL;
+  if (c->n_tokens < 1) return PACKKV_ESTATE;
+  GemvArgs a = gemv_args(c, which == 1);
+  const int64_t perm_stride = max_blocks_of(&c->cfg, c->max_tokens) * c->cfg.block_tokens;
+  return hip_status(launch_decompress(a, c->cfg.block_tokens, which == 1, c->n_streams, c->perm,
+                                      perm_stride, mode, out, (hipStream_t)stream));
+}
+
+int packkv_softmax_rows(const float* scores, float* p, int32_t rows, int64_t T, int64_t ld, float scale,
+                        void* stream) {
+  if (!scores || !p || rows < 1 || T < 1 || ld < T) return PACKKV_EINVAL;
+  return hip_status(launch_softmax(scores, p, rows, T, ld, scale, (hipStream_t)stream));
+}
+
+int packkv_check(const packkv_cache_t* c, void* stream) {
+  if (!c || !c->status) return PACKKV_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipStreamSynchronize(st) != hipSuccess) return PACKKV_EHIP;
+  int32_t v = 0;
+  if (hipMemcpy(&v, c->status, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return PACKKV_EHIP;
+  if (v) {
+    const int32_t zero = 0;
+    if (hipMemcpy(c->status, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return PACKKV_EHIP;
+  }
+  return v;
+}
+
+int packkv_stats(const packkv_cache_t* c, uint64_t* out, void* stream) {
+  int e = check_cache(c);
+  if (e) return e;
+  if (!out) return PACKKV_EINVAL;
+  if (c->n_tokens < 1) return PACKKV_ESTATE;
+  hipStream_t st = (hipStream_t)stream;
+  for (int which = 0; which < 2; ++which) {
+    GemvArgs a = gemv_args(c, which == 1);
+    e = hip_status(launch_stats(a, c->cfg.block_tokens, which == 1, c->n_streams,
+                                (unsigned long long*)out, st));
+    if (e) return e;
+  }
+  return PACKKV_OK;
+}
+
+const char* packkv_status_str(int s) {
+  switch (s) {
+    case PACKKV_OK: return "ok";
+    case PACKKV_EINVAL: return "invalid argument";
+    case PACKKV_EUNSUPPORTED: return "unsupported configuration";
+    case PACKKV_ECAPACITY: return "capacity exceeded";
+    case PACKKV_ECORRUPT: return "corrupt record";
+    case PACKKV_EHIP: return "HIP runtime error";
+    case PACKKV_ESTATE: return "invalid cache state";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+// Shared device and host helpers of the packkv library (gfx950 / CDNA4).
+//
+// Record layout (one block of B tokens of one stream), from the PackKV
+// pipeline of quantise -> reorder tokens -> lossless channel-direction
+// bit-packing (Fig. 2 caption; TL;DR):
+//   K: scale[D] f16 | zero[D] f16 | hdr[nr][D] u8 | pad16 | payload | pad16
+//   V: scale[B] f16 | zero[B] f16 | hdr[nr][D] u8 | pad16 | payload | pad16
+// hdr = (w << 4) | m per (run, channel); payload = for run r, channel c: w
+// little-endian u32 words, slot i of the run in bits [i*w, i*w + w).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "packkv.h"
+
+namespace packkv {
+
+constexpr int kD = 128;        // head_dim
+constexpr int kR = 32;         // run length (slots)
+constexpr int kWave = 64;      // CDNA wavefront
+
+__host__ __device__ constexpr int pad16(int x) { return (x + 15) & ~15; }
+__host__ __device__ constexpr int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
+
+// Geometry of a record holding n tokens (nr runs) of a block of B tokens.
+__host__ __device__ constexpr int n_params(bool is_v, int B) { return is_v ? B : kD; }
+__host__ __device__ constexpr int hdr_offset(bool is_v, int B) { return 4 * n_params(is_v, B); }
+__host__ __device__ constexpr int payload_offset(bool is_v, int B, int nr) {
+  return pad16(4 * n_params(is_v, B) + nr * kD);
+}
+__host__ __device__ constexpr int max_record_bytes(bool is_v, int B, int bits) {
+  return payload_offset(is_v, B, B / kR) + 4 * (B / kR) * kD * bits;
+}
+
+// ---------------------------------------------------------------------------
+// fp16 bit helpers (exact).  Only positive finite patterns are used for steps.
+__device__ __forceinline__ double f16_bits_to_double(uint32_t h) {
+  uint32_t e = (h >> 10) & 31u, mant = h & 1023u;
+  double v = (e == 0) ? ldexp((double)mant, -24) : ldexp((double)(1024u + mant), (int)e - 25);
+  return (h & 0x8000u) ? -v : v;
+}
+__device__ __forceinline__ float f16_bits_to_float(uint32_t h) {
+  return (float)f16_bits_to_double(h);  // exact: fp16 values are fp32 values
+}
+
+// ---------------------------------------------------------------------------
+// Spread the fields of one 8-slot group into eight 4-bit nibbles.
+// Input: the group's 8*w bits at the bottom of x.  Output: nibble i = field i.
+__device__ __forceinline__ uint32_t spread3to4(uint32_t x) {
+  uint32_t a = (x & 0xFFFu) | ((x & 0xFFF000u) << 4);
+  uint32_t b = (a & 0x003F003Fu) | ((a & 0x0FC00FC0u) << 2);
+  return (b & 0x07070707u) | ((b & 0x38383838u) << 1);
+}
+__device__ __forceinline__ uint32_t spread2to4(uint32_t x) {
+  uint32_t a = (x & 0xFFu) | ((x & 0xFF00u) << 8);
+  uint32_t b = (a & 0x000F000Fu) | ((a & 0x00F000F0u) << 4);
+  return (b & 0x03030303u) | ((b & 0x0C0C0C0Cu) << 2);
+}
+__device__ __forceinline__ uint32_t spread1to4(uint32_t x) {
+  uint32_t a = (x & 0xFu) | ((x & 0xF0u) << 12);
+  uint32_t b = (a & 0x00030003u) | ((a & 0x000C000Cu) << 6);
+  return (b & 0x01010101u) | ((b & 0x02020202u) << 3);
+}
+
+// 32 bits of the run's bit string starting at bit p (p a compile-time
+// multiple of 8 inside a switch), from its words w0..w3.
+template <int P>
+__device__ __forceinline__ uint32_t bits_at(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  constexpr int wi = P >> 5, sh = P & 31;
+  uint32_t lo = wi == 0 ? w0 : wi == 1 ? w1 : wi == 2 ? w2 : w3;
+  uint32_t hi = wi == 0 ? w1 : wi == 1 ? w2 : wi == 2 ? w3 : 0u;
+  if constexpr (sh == 0) return lo;
+  else return __builtin_amdgcn_alignbit(hi, lo, sh);
+}
+
+// Decode one run (R = 32 slots) stored at width w with minimum m into four
+// nibble words: word k holds q = m + u of slots 8k .. 8k+7 (nibble i = slot
+// 8k+i).  Valid for m + 2^w - 1 <= 15.  `wd` holds the run's first four
+// payload words (words past the run are ignored).
+__device__ __forceinline__ void run_to_nibbles(int w, uint32_t m, const uint32_t wd[4], uint32_t out[4]) {
+  const uint32_t a = wd[0], b = wd[1], c = wd[2], d = wd[3];
+  switch (w) {
+    case 4: out[0] = a; out[1] = b; out[2] = c; out[3] = d; break;
+    case 3:
+      out[0] = spread3to4(bits_at<0>(a, b, c, d));
+      out[1] = spread3to4(bits_at<24>(a, b, c, d));
+      out[2] = spread3to4(bits_at<48>(a, b, c, d));
+      out[3] = spread3to4(bits_at<72>(a, b, c, d));
+      break;
+    case 2:
+      out[0] = spread2to4(a);
+      out[1] = spread2to4(a >> 16);
+      out[2] = spread2to4(b);
+      out[3] = spread2to4(b >> 16);
+      break;
+    case 1:
+      out[0] = spread1to4(a);
+      out[1] = spread1to4(a >> 8);
+      out[2] = spread1to4(a >> 16);
+      out[3] = spread1to4(a >> 24);
+      break;
+    default: out[0] = out[1] = out[2] = out[3] = 0u; break;
+  }
+  const uint32_t mm = m * 0x11111111u;   // m in every nibble; no carries
+  out[0] += mm; out[1] += mm; out[2] += mm; out[3] += mm;
+}
+
+// Latch the first device-side error code.
+__device__ __forceinline__ void latch(int32_t* status, int code) {
+  if (status) atomicCAS(status, 0, code);
+}
+
+// Wave-wide sum with butterfly shuffles.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+// Inclusive prefix sum across the 64 lanes of a wave (Hillis-Steele).
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+}  // namespace packkv

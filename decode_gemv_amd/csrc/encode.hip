@@ -1,0 +1,381 @@
+// PackKV encoder on the GPU: quantise -> reorder tokens -> bit-pack, one
+// workgroup per block (Fig. 2 caption, steps (1) and (2); Fig. 5 caption for
+// the two quantisation granularities; abstract for the growing cache).
+//
+// Bit-exact contract with the fp64 oracle:
+//   * zero = group minimum (fp16, -0 stored as +0);
+//   * scale = smallest positive fp16 h with h * L >= max - min (exact fp64
+//     comparisons on fp16 values), 0 for a constant group;
+//   * q = rint((x - min) / scale) in fp64 (exact subtraction, IEEE division,
+//     round half to even), clamped to [0, L];
+//   * permutation = greedy L1 grouping with key (distance, index), identity
+//     unless the payload shrinks strictly;
+//   * run width = bit_length(max - min), u = q - min packed LSB-first.
+// This file must be built without fast-math flags.
+#include "kernels.hpp"
+
+namespace packkv {
+
+// Smallest positive fp16 pattern h with value(h) * L >= d, for d > 0.
+__device__ uint32_t min_f16_step(double d, int L) {
+  double y = d / (double)L;
+  uint32_t h;
+  if (y >= 65504.0) {
+    h = 0x7BFFu;
+  } else {
+    int e;
+    (void)frexp(y, &e);
+    int E = e - 1;                                   // y in [2^E, 2^(E+1))
+    if (E < -14) h = (uint32_t)floor(ldexp(y, 24));  // subnormal range
+    else h = ((uint32_t)(E + 15) << 10) | ((uint32_t)floor(ldexp(y, 10 - E)) - 1024u);
+  }
+  if (h == 0) h = 1;
+  while (h < 0x7BFFu && f16_bits_to_double(h) * L < d) ++h;
+  while (h > 1u && f16_bits_to_double(h - 1) * L >= d) --h;
+  return h;
+}
+
+__device__ __forceinline__ bool f16_less(uint32_t a, uint32_t b) {
+  return f16_bits_to_double(a) < f16_bits_to_double(b);
+}
+
+// Quantise one group of `cnt` fp16 values (stride `st` in `src`) into q[i*qs].
+__device__ void quant_group(const uint16_t* src, int cnt, int st, int L,
+                            uint8_t* q, int qs, uint16_t* scale_out, uint16_t* zero_out) {
+  uint32_t mnb = src[0], mxb = src[0];
+  for (int i = 1; i < cnt; ++i) {
+    uint32_t x = src[(int64_t)i * st];
+    if (f16_less(x, mnb)) mnb = x;
+    if (f16_less(mxb, x)) mxb = x;
+  }
+  const double mn = f16_bits_to_double(mnb), mx = f16_bits_to_double(mxb);
+  const double d = mx - mn;
+  const uint32_t hb = d > 0.0 ? min_f16_step(d, L) : 0u;
+  const double h = f16_bits_to_double(hb);
+  *scale_out = (uint16_t)hb;
+  *zero_out = (uint16_t)(mn == 0.0 ? 0u : mnb);
+  for (int i = 0; i < cnt; ++i) {
+    uint32_t qq = 0;
+    if (hb) {
+      double r = rint((f16_bits_to_double(src[(int64_t)i * st]) - mn) / h);
+      r = r < 0.0 ? 0.0 : (r > (double)L ? (double)L : r);
+      qq = (uint32_t)r;
+    }
+    q[i * qs] = (uint8_t)qq;
+  }
+}
+
+// Min and width of run r, channel c of the slot-ordered ints q[order[slot]][c].
+__device__ __forceinline__ void run_stats(const uint8_t* q, const uint8_t* order, int r, int c,
+                                          int n, uint32_t& m, uint32_t& w) {
+  const int s0 = r * kR, s1 = min(n, s0 + kR);
+  uint32_t lo = 255, hi = 0;
+  for (int sl = s0; sl < s1; ++sl) {
+    uint32_t x = q[order[sl] * kD + c];
+    lo = min(lo, x);
+    hi = max(hi, x);
+  }
+  m = lo;
+  w = 32u - __clz(hi - lo);
+}
+
+// Block-wide (256 threads) exclusive scan of one value per thread.
+__device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh /*[256]*/, uint32_t* total) {
+  const int t = threadIdx.x;
+  sh[t] = v;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    uint32_t a = t >= o ? sh[t - o] : 0u;
+    __syncthreads();
+    sh[t] += a;
+    __syncthreads();
+  }
+  uint32_t incl = sh[t];
+  *total = sh[255];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(256) void k_encode(EncArgs a) {
+  constexpr int NT = 256;
+  __shared__ uint8_t qk[128 * kD];
+  __shared__ uint8_t qv[128 * kD];
+  __shared__ uint16_t ksc[kD], kze[kD], vsc[128], vze[128];
+  __shared__ uint8_t order[128], ident[128], alive[128];
+  __shared__ uint32_t key[128];
+  __shared__ uint8_t wk[4 * kD], mk[4 * kD], wv[4 * kD], mv[4 * kD];
+  __shared__ uint32_t scan_sh[NT];
+  __shared__ uint32_t red[4];
+
+  const int tid = threadIdx.x;
+  const int B = a.B, L = (1 << a.bits) - 1;
+  const int s = blockIdx.y;
+  const int j = a.mode == kTail ? a.block0 : blockIdx.x;
+  const int64_t t0 = (int64_t)j * B;
+  if (t0 >= a.n_tokens) return;
+  const int n = (int)imin64(B, a.n_tokens - t0);
+  const int nr = (n + kR - 1) / kR;
+  const uint16_t* ks = a.k + s * a.src_stream + (a.mode == kTail ? 0 : j * a.src_block);
+  const uint16_t* vs = a.v + s * a.src_stream + (a.mode == kTail ? 0 : j * a.src_block);
+
+  // (1) quantise: K per channel over the block's tokens, V per token.
+  if (tid < kD) {
+    quant_group(ks + tid, n, kD, L, qk + tid, kD, &ksc[tid], &kze[tid]);
+  } else if (tid - kD < n) {
+    const int t = tid - kD;
+    quant_group(vs + (int64_t)t * kD, kD, 1, L, qv + t * kD, 1, &vsc[t], &vze[t]);
+  }
+  if (tid < 128) ident[tid] = (uint8_t)tid;
+  __syncthreads();
+
+  // (2) token order inside the block.
+  uint8_t* perm_g = a.perm + s * a.perm_stride + (int64_t)j * B;
+  if (a.mode == kPass2) {
+    if (tid < n) order[tid] = perm_g[tid];
+    __syncthreads();
+  } else {
+    if (tid < 128) order[tid] = (uint8_t)tid;
+    if (a.permute && n > 1) {
+      if (tid < 128) alive[tid] = tid < n;
+      __syncthreads();
+      for (int r = 0; r < nr; ++r) {
+        const int base = r * kR;
+        // seed = smallest remaining token index
+        if (tid == 0) {
+          int sd = 0;
+          while (!alive[sd]) ++sd;
+          red[0] = (uint32_t)sd;
+        }
+        __syncthreads();
+        const int sd = (int)red[0];
+        if (tid < n) {
+          uint32_t k0 = 0xFFFFFFFFu;
+          if (alive[tid]) {
+            const uint32_t* rt = reinterpret_cast<const uint32_t*>(qk + tid * kD);
+            const uint32_t* rs = reinterpret_cast<const uint32_t*>(qk + sd * kD);
+            const uint32_t* vt = reinterpret_cast<const uint32_t*>(qv + tid * kD);
+            const uint32_t* vd = reinterpret_cast<const uint32_t*>(qv + sd * kD);
+            uint32_t dist = 0;
+            for (int i = 0; i < kD / 4; ++i) {
+              dist = __builtin_amdgcn_sad_u8(rt[i], rs[i], dist);
+              dist = __builtin_amdgcn_sad_u8(vt[i], vd[i], dist);
+            }
+            k0 = (dist << 8) | (uint32_t)tid;
+          }
+          key[tid] = k0;
+        }
+        __syncthreads();
+        if (tid < n && alive[tid]) {
+          const uint32_t mine = key[tid];
+          int rank = 0;
+          for (int u = 0; u < n; ++u) rank += key[u] < mine;
+          if (rank < kR) {
+            order[base + rank] = (uint8_t)tid;
+            alive[tid] = 0;
+          }
+        }
+        __syncthreads();
+      }
+      // identity fallback: keep the grouping only if the payload shrinks.
+      if (tid < 2) red[tid] = 0;
+      __syncthreads();
+      uint32_t sum_g = 0, sum_i = 0;
+      for (int it = tid; it < 2 * nr * kD; it += NT) {
+        const bool is_v = it >= nr * kD;
+        const int rc = is_v ? it - nr * kD : it;
+        const uint8_t* q = is_v ? qv : qk;
+        uint32_t m, w;
+        run_stats(q, order, rc / kD, rc % kD, n, m, w);
+        sum_g += w;
+        run_stats(q, ident, rc / kD, rc % kD, n, m, w);
+        sum_i += w;
+      }
+      atomicAdd(&red[0], sum_g);
+      atomicAdd(&red[1], sum_i);
+      __syncthreads();
+      const bool keep = red[0] < red[1];
+      __syncthreads();
+      if (!keep && tid < 128) order[tid] = (uint8_t)tid;
+      __syncthreads();
+    } else {
+      __syncthreads();
+    }
+  }
+
+  // (3) per-run minima and widths in the chosen order.
+  for (int it = tid; it < 2 * nr * kD; it += NT) {
+    const bool is_v = it >= nr * kD;
+    const int rc = is_v ? it - nr * kD : it;
+    uint32_t m, w;
+    run_stats(is_v ? qv : qk, order, rc / kD, rc % kD, n, m, w);
+    (is_v ? wv : wk)[rc] = (uint8_t)w;
+    (is_v ? mv : mk)[rc] = (uint8_t)m;
+  }
+  __syncthreads();
+
+  // payload word offsets of every (run, channel), run-major: up to 512 per
+  // tensor, two per thread.
+  uint32_t totk, totv;
+  const int nrc = nr * kD;
+  uint32_t k_a = 2 * tid < nrc ? wk[2 * tid] : 0u, k_b = 2 * tid + 1 < nrc ? wk[2 * tid + 1] : 0u;
+  uint32_t v_a = 2 * tid < nrc ? wv[2 * tid] : 0u, v_b = 2 * tid + 1 < nrc ? wv[2 * tid + 1] : 0u;
+  const uint32_t k_ex = block_excl_scan(k_a + k_b, scan_sh, &totk);
+  const uint32_t v_ex = block_excl_scan(v_a + v_b, scan_sh, &totv);
+
+  const uint32_t k_pay = (uint32_t)payload_offset(false, B, nr);
+  const uint32_t v_pay = (uint32_t)payload_offset(true, B, nr);
+  const uint32_t k_size = k_pay + (uint32_t)pad16(4 * (int)totk);
+  const uint32_t v_size = v_pay + (uint32_t)pad16(4 * (int)totv);
+  uint32_t* koff = a.k_off + s * a.off_stride;
+  uint32_t* voff = a.v_off + s * a.off_stride;
+
+  if (a.mode == kPass1) {
+    if (tid < B) perm_g[tid] = tid < n ? order[tid] : (uint8_t)0xFF;
+    if (tid == 0) {
+      koff[j + 1] = k_size;       // sizes; a later scan turns them into offsets
+      voff[j + 1] = v_size;
+    }
+    return;
+  }
+
+  // (4) write the records.
+  uint32_t kbase, vbase;
+  if (a.mode == kTail) {
+    if (j == 0) {
+      kbase = 0u;
+      vbase = 0u;
+    } else {
+      kbase = koff[j];
+      vbase = voff[j];
+    }
+  } else {
+    kbase = koff[j];
+    vbase = voff[j];
+  }
+  if ((uint64_t)kbase + k_size > a.arena_limit || (uint64_t)vbase + v_size > a.arena_limit) {
+    if (tid == 0) latch(a.status, PACKKV_ECAPACITY);
+    return;
+  }
+  uint8_t* krec = a.k_arena + s * a.arena_stride + kbase;
+  uint8_t* vrec = a.v_arena + s * a.arena_stride + vbase;
+
+  // params
+  if (tid < kD) {
+    reinterpret_cast<uint16_t*>(krec)[tid] = ksc[tid];
+    reinterpret_cast<uint16_t*>(krec)[kD + tid] = kze[tid];
+  }
+  if (tid < B) {
+    const bool ok = tid < n;
+    reinterpret_cast<uint16_t*>(vrec)[tid] = ok ? vsc[order[tid]] : (uint16_t)0;
+    reinterpret_cast<uint16_t*>(vrec)[B + tid] = ok ? vze[order[tid]] : (uint16_t)0;
+  }
+  // headers and the zero padding up to the payload
+  {
+    const uint32_t kh = (uint32_t)hdr_offset(false, B), vh = (uint32_t)hdr_offset(true, B);
+    for (uint32_t i = tid; i < k_pay - kh; i += NT)
+      krec[kh + i] = i < (uint32_t)nrc ? (uint8_t)((wk[i] << 4) | mk[i]) : (uint8_t)0;
+    for (uint32_t i = tid; i < v_pay - vh; i += NT)
+      vrec[vh + i] = i < (uint32_t)nrc ? (uint8_t)((wv[i] << 4) | mv[i]) : (uint8_t)0;
+  }
+  // payload: each thread packs its two (run, channel) entries of K and of V
+  for (int e = 0; e < 4; ++e) {
+    const bool is_v = e >= 2;
+    const int rc = 2 * tid + (e & 1);
+    if (rc >= nrc) continue;
+    const uint8_t* q = is_v ? qv : qk;
+    const uint32_t w = (is_v ? wv : wk)[rc];
+    const uint32_t m = (is_v ? mv : mk)[rc];
+    const uint32_t woff = (is_v ? v_ex : k_ex) + ((e & 1) ? (is_v ? v_a : k_a) : 0u);
+    if (w == 0) continue;
+    const int r = rc / kD, c = rc % kD;
+    uint64_t lo = 0, hi = 0;          // the run's 128-bit string
+    for (int i = 0; i < kR; ++i) {
+      const int sl = r * kR + i;
+      const uint64_t u = sl < n ? (uint64_t)(q[order[sl] * kD + c] - m) : 0ull;
+      const int p = i * (int)w;
+      if (p < 64) {
+        lo |= u << p;
+        if (p + (int)w > 64) hi |= u >> (64 - p);
+      } else {
+        hi |= u << (p - 64);
+      }
+    }
+    uint32_t* dst = reinterpret_cast<uint32_t*>((is_v ? vrec + v_pay : krec + k_pay)) + woff;
+    const uint32_t words[4] = {(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+    for (uint32_t i = 0; i < w; ++i) dst[i] = words[i];
+  }
+  // zero padding after the payload
+  if (tid < 4) {
+    uint32_t* kt = reinterpret_cast<uint32_t*>(krec + k_pay) + totk;
+    uint32_t* vt = reinterpret_cast<uint32_t*>(vrec + v_pay) + totv;
+    if (totk + tid < (k_size - k_pay) / 4) kt[tid] = 0u;
+    if (totv + tid < (v_size - v_pay) / 4) vt[tid] = 0u;
+  }
+  if (a.mode == kTail) {
+    if (tid < B) perm_g[tid] = tid < n ? order[tid] : (uint8_t)0xFF;
+    if (tid == 0) {
+      if (j == 0) {
+        koff[0] = 0u;
+        voff[0] = 0u;
+      }
+      koff[j + 1] = kbase + k_size;
+      voff[j + 1] = vbase + v_size;
+    }
+  }
+}
+
+// Per stream: sizes in off[1..nb] -> byte offsets (off[0] = 0).
+__global__ __launch_bounds__(256) void k_scan_offsets(uint32_t* k_off, uint32_t* v_off,
+                                                      int64_t off_stride, int nb) {
+  __shared__ uint32_t sh[256];
+  uint32_t* off = (blockIdx.y == 0 ? k_off : v_off) + blockIdx.x * off_stride;
+  uint32_t carry = 0;
+  for (int base = 0; base < nb; base += 256) {
+    const int i = base + threadIdx.x;
+    const uint32_t v = i < nb ? off[i + 1] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan(v, sh, &tot);
+    if (i < nb) off[i + 1] = carry + ex + v;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) off[0] = 0u;
+}
+
+// Copy `cnt` tokens [S][cnt][D] fp16 into the tail staging at token `at`.
+__global__ void k_stage_tail(const uint16_t* k, const uint16_t* v, int64_t src_stream,
+                             uint16_t* tk, uint16_t* tv, int B, int at, int cnt) {
+  const int s = blockIdx.x;
+  for (int i = threadIdx.x; i < cnt * kD; i += blockDim.x) {
+    tk[(int64_t)s * B * kD + (int64_t)at * kD + i] = k[s * src_stream + i];
+    tv[(int64_t)s * B * kD + (int64_t)at * kD + i] = v[s * src_stream + i];
+  }
+}
+
+}  // namespace packkv
+
+// ---------------------------------------------------------------------------
+// Launch helpers used by the C ABI layer.
+namespace packkv {
+
+hipError_t launch_encode(const EncArgs& a, int n_streams, int n_blocks, hipStream_t st) {
+  dim3 grid(a.mode == kTail ? 1 : n_blocks, n_streams);
+  hipLaunchKernelGGL(k_encode, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_offsets(uint32_t* k_off, uint32_t* v_off, int64_t off_stride,
+                               int n_streams, int nb, hipStream_t st) {
+  hipLaunchKernelGGL(k_scan_offsets, dim3(n_streams, 2), dim3(256), 0, st, k_off, v_off,
+                     off_stride, nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_tail(const uint16_t* k, const uint16_t* v, int64_t src_stream,
+                             uint16_t* tk, uint16_t* tv, int B, int at, int cnt,
+                             int n_streams, hipStream_t st) {
+  hipLaunchKernelGGL(k_stage_tail, dim3(n_streams), dim3(256), 0, st, k, v, src_stream, tk, tv,
+                     B, at, cnt);
+  return hipGetLastError();
+}
+
+}  // namespace packkv

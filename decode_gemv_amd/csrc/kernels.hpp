@@ -1,0 +1,65 @@
+// Kernel argument blocks and launchers shared by the kernels and the C ABI.
+#pragma once
+
+#include "common.hpp"
+
+namespace packkv {
+
+enum EncMode : int { kPass1 = 0, kPass2 = 1, kTail = 2 };
+
+struct EncArgs {
+  const uint16_t* k;        // raw fp16 source of token 0 of stream 0
+  const uint16_t* v;
+  int64_t src_stream;       // elements between streams in the source
+  int64_t src_block;        // elements between blocks in the source
+  int64_t n_tokens;         // total tokens per stream after this call
+  int32_t bits, B, permute, mode;
+  int32_t block0;           // kTail: index of the block being (re)encoded
+  uint8_t* k_arena;
+  uint8_t* v_arena;
+  uint64_t arena_limit;     // usable bytes per stream region
+  uint64_t arena_stride;
+  uint32_t* k_off;
+  uint32_t* v_off;
+  int64_t off_stride;       // max_blocks + 1
+  uint8_t* perm;
+  int64_t perm_stride;      // max_blocks * B
+  int32_t* status;
+};
+
+struct GemvArgs {
+  const uint8_t* arena;
+  uint64_t arena_stride;
+  const uint32_t* off;
+  int64_t off_stride;
+  int64_t n_tokens;
+  int32_t nb;            // records per stream = ceil(T / B)
+  int32_t bits;
+  int32_t blocks_per_wg;
+  int32_t splits;        // workgroups per stream
+  int32_t G;
+  const uint16_t* q;     // K: q [S][G][D] fp16
+  const float* p;        // V: p [S][G][ld] fp32
+  float* scores;         // K: [S][G][ld]
+  int64_t ld;
+  float* ws;             // V: partial sums [S][G][splits][D]
+  int32_t* status;
+};
+
+
+hipError_t launch_encode(const EncArgs& a, int n_streams, int n_blocks, hipStream_t st);
+hipError_t launch_scan_offsets(uint32_t* k_off, uint32_t* v_off, int64_t off_stride,
+                               int n_streams, int nb, hipStream_t st);
+hipError_t launch_stage_tail(const uint16_t* k, const uint16_t* v, int64_t src_stream,
+                             uint16_t* tk, uint16_t* tv, int B, int at, int cnt,
+                             int n_streams, hipStream_t st);
+hipError_t launch_qk(const GemvArgs& a, int B, int n_streams, hipStream_t st);
+hipError_t launch_pv(const GemvArgs& a, int B, int n_streams, float* out, hipStream_t st);
+hipError_t launch_decompress(const GemvArgs& a, int B, bool is_v, int n_streams, const uint8_t* perm,
+                             int64_t perm_stride, int mode, void* out, hipStream_t st);
+hipError_t launch_stats(const GemvArgs& a, int B, bool is_v, int n_streams, unsigned long long* out,
+                        hipStream_t st);
+hipError_t launch_softmax(const float* scores, float* p, int rows, int64_t T, int64_t ld, float scale,
+                          hipStream_t st);
+
+}  // namespace packkv

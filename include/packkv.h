@@ -1,0 +1,216 @@
+/*
+ * packkv.h - C ABI of the MI355X (gfx950) PackKV decode library.
+ *
+ * PackKV ("PackKV: Reducing KV Cache Memory Footprint through LLM-Aware Lossy
+ * Compression", arXiv 2512.24449) keeps the attention KV cache quantised,
+ * token-reordered and bit-packed, and fuses decompression into the two
+ * decode-time matrix-vector products (abstract; TL;DR; Fig. 1 and Fig. 2
+ * captions):
+ *
+ *   K side:  scores[t] = q . K_hat[t]
+ *   V side:  out       = sum_t p[t] * V_hat[t]
+ *
+ * Packed format (one record per block of B tokens of one stream; integers
+ * little-endian):
+ *   K record: scale[D] fp16 | zero[D] fp16 | hdr[nr][D] u8 | 0-pad to 16 B |
+ *             payload | 0-pad to 16 B
+ *   V record: scale[B] fp16 | zero[B] fp16 (slot order, 0 past n) |
+ *             hdr[nr][D] u8 | 0-pad to 16 B | payload | 0-pad to 16 B
+ *   nr = ceil(n / R) runs of R = 32 slots; hdr = (w << 4) | m for the run's
+ *   width w = bit_length(max - min) and minimum m; payload = for each run r,
+ *   for each channel c, w u32 words holding u = q - m of slot i in bits
+ *   [i*w, i*w + w).  Quantisation: K per channel over the block's tokens, V
+ *   per token over D channels; zero = group minimum, scale = the smallest
+ *   fp16 h with h * (2^b - 1) >= max - min, q = round-half-even((x-min)/h).
+ *   Slot i of block j holds token j*B + perm[j][i]; the permutation is the
+ *   greedy L1 grouping of the block's quantised (K, V) rows (identity when it
+ *   does not shrink the payload).
+ *
+ * Conventions for every entry point
+ *   - Every pointer inside packkv_cache_t and every tensor argument is DEVICE
+ *     memory owned by the caller (e.g. allocated with torch on ROCm).  The
+ *     library never allocates or frees device memory and keeps no global
+ *     mutable state; calls on different caches are independent.
+ *   - `stream` is a hipStream_t passed as void*.  Every call only enqueues
+ *     work on that stream and returns without synchronising, except
+ *     packkv_check, which synchronises the stream.
+ *   - Host-detectable precondition failures (null pointer, unsupported
+ *     configuration, size over capacity, bad stride) return a nonzero
+ *     status BEFORE anything is launched; a failed launch returns
+ *     PACKKV_EHIP.  Conditions only the device can see (arena overflow, a
+ *     corrupt header) set *cache->status, skip the affected writes, and are
+ *     reported by packkv_check.
+ *   - Inputs are never modified.  Outputs are written over [0, n_tokens);
+ *     entries of a leading dimension past that are left untouched.
+ *   - scores, p and the decompressed ints are in SLOT order (attention does
+ *     not depend on the order of bound (K, V) pairs, TL;DR); perm maps slots
+ *     back to tokens.
+ */
+#ifndef PACKKV_H_
+#define PACKKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  PACKKV_OK = 0,
+  PACKKV_EINVAL = 1,       /* bad argument (null pointer, size, stride)        */
+  PACKKV_EUNSUPPORTED = 2, /* configuration outside D=128, b 2..4, B 64/128, R 32 */
+  PACKKV_ECAPACITY = 3,    /* tokens over max_tokens, or arena region overflow */
+  PACKKV_ECORRUPT = 4,     /* a record header is inconsistent                  */
+  PACKKV_EHIP = 5,         /* a HIP runtime call or kernel launch failed       */
+  PACKKV_ESTATE = 6        /* call not valid in the cache's current state      */
+};
+
+/* Format parameters. */
+typedef struct {
+  int32_t head_dim;     /* D: must be 128                                    */
+  int32_t bits;         /* b: 2, 3 or 4                                      */
+  int32_t block_tokens; /* B: 64 or 128                                      */
+  int32_t run_tokens;   /* R: must be 32                                     */
+  int32_t permute;      /* 1: greedy grouping inside blocks, 0: identity     */
+} packkv_config_t;
+
+/*
+ * A packed cache of S independent streams (stream = batch entry x KV head),
+ * all holding the same number of tokens.  The caller fills every field and
+ * allocates every array with the sizes packkv_cache_sizes() reports, zeroed
+ * where noted.  n_tokens is maintained by the library's host code: the
+ * compress and append calls update it when they return PACKKV_OK.
+ */
+typedef struct {
+  packkv_config_t cfg;
+  int32_t n_streams;      /* S >= 1                                           */
+  int64_t max_tokens;     /* capacity per stream                              */
+  int64_t n_tokens;       /* tokens currently held per stream (start at 0)    */
+  uint64_t arena_stride;  /* bytes per stream region of each arena (multiple of
+                             256, >= packkv_arena_stride_bytes, < 2^32)       */
+  uint8_t* k_arena;       /* [S][arena_stride] K records, back to back        */
+  uint8_t* v_arena;       /* [S][arena_stride] V records                      */
+  uint32_t* k_off;        /* [S][max_blocks + 1] byte offset of each record
+                             within its stream region; entry nb = used bytes  */
+  uint32_t* v_off;        /* [S][max_blocks + 1]                              */
+  uint8_t* perm;          /* [S][max_blocks][B] slot -> in-block token index,
+                             0xFF for empty slots                             */
+  uint16_t* tail_k;       /* [S][B][D] fp16 raw tokens of the open tail block */
+  uint16_t* tail_v;       /* [S][B][D]                                        */
+  int32_t* status;        /* [1] device error latch, zero-initialised         */
+} packkv_cache_t;
+
+/* Sizes (in bytes) of every array of a cache. */
+typedef struct {
+  uint64_t arena_stride;  /* per stream, worst case (every run at w = b)      */
+  uint64_t arena_bytes;   /* S * arena_stride, for each of k_arena, v_arena   */
+  uint64_t off_bytes;     /* S * (max_blocks + 1) * 4, for each of k_off, v_off */
+  uint64_t perm_bytes;    /* S * max_blocks * B                               */
+  uint64_t tail_bytes;    /* S * B * D * 2, for each of tail_k, tail_v        */
+  int64_t max_blocks;     /* ceil(max_tokens / B)                             */
+} packkv_sizes_t;
+
+/* Validate cfg and report the sizes of a cache for S streams of up to
+ * max_tokens tokens.  Host only.  Returns PACKKV_OK, EINVAL or EUNSUPPORTED. */
+int packkv_cache_sizes(const packkv_config_t* cfg, int32_t n_streams,
+                       int64_t max_tokens, packkv_sizes_t* out);
+
+/* Worst-case bytes of one stream's arena region (every run at full width b,
+ * plus slack for the kernels' vector over-reads), rounded up to 256 B.  0 on
+ * an invalid cfg. */
+uint64_t packkv_arena_stride_bytes(const packkv_config_t* cfg, int64_t max_tokens);
+
+/* Bytes of workspace packkv_pv_gemv needs for `group` queries per stream. */
+uint64_t packkv_pv_workspace_bytes(const packkv_cache_t* cache, int32_t group);
+
+/*
+ * packkv_compress_block - encode n_tokens tokens of every stream at once
+ * (prefill).  Abstract: PackKV compresses the KV cache; Fig. 2 caption and
+ * TL;DR: quantise, reorder, then bit-pack losslessly in channel direction.
+ *   k_f16, v_f16: device fp16 [S][n_tokens][D], token order, contiguous.
+ * The cache must be empty (n_tokens == 0, else PACKKV_ESTATE) and
+ * 1 <= n_tokens <= max_tokens (else EINVAL / ECAPACITY).  Writes every
+ * record, k_off/v_off[0 .. nb], perm, and the raw tail staging (the last,
+ * partial block's tokens).  Sets cache->n_tokens on success.
+ */
+int packkv_compress_block(packkv_cache_t* cache, const void* k_f16, const void* v_f16,
+                          int64_t n_tokens, void* stream);
+
+/*
+ * packkv_append_tokens - append n_new tokens to every stream (decode).
+ * Abstract: the method stays compatible with the dynamically growing cache.
+ * The open tail block is kept as raw fp16 and re-encoded in full on every
+ * call; closed blocks never change, so appending gives exactly the bytes a
+ * one-shot compress of all tokens gives.
+ *   k_f16, v_f16: device fp16 [S][n_new][D].
+ * n_new >= 1 and n_tokens + n_new <= max_tokens (else EINVAL / ECAPACITY).
+ * Updates cache->n_tokens on success.
+ */
+int packkv_append_tokens(packkv_cache_t* cache, const void* k_f16, const void* v_f16,
+                         int32_t n_new, void* stream);
+
+/*
+ * packkv_qk_gemv - fused K decompress + GEMV (TL;DR: decompression integrated
+ * into the matrix-vector product, no writeback of decompressed data).
+ *   q_f16:  device fp16 [S][group][D].
+ *   scores: device fp32 [S][group][ld]; scores[s][g][j*B + i] =
+ *           q[s][g] . K_hat[s][block j, slot i] for every j*B + i < n_tokens.
+ * group >= 1, ld >= n_tokens, n_tokens >= 1, else EINVAL / ESTATE.
+ */
+int packkv_qk_gemv(const packkv_cache_t* cache, const void* q_f16, int32_t group,
+                   float* scores, int64_t ld, void* stream);
+
+/*
+ * packkv_pv_gemv - fused V decompress + GEMV with a split-T partial-sum
+ * reduction in a fixed order (Fig. 1 caption: weighted V vectors summed).
+ *   p:         device fp32 [S][group][ld], slot order (as scores).
+ *   out:       device fp32 [S][group][D]; out[s][g][c] =
+ *              sum_t p[s][g][t] * V_hat[s][t][c].
+ *   workspace: device memory of at least packkv_pv_workspace_bytes(cache,
+ *              group) bytes (ws_bytes), holding the split partial sums.
+ * Results are bitwise reproducible run to run.
+ */
+int packkv_pv_gemv(const packkv_cache_t* cache, const float* p, int64_t ld, int32_t group,
+                   float* out, void* workspace, uint64_t ws_bytes, void* stream);
+
+/*
+ * packkv_decompress - decode the cache (test and debug path).
+ *   which: 0 = K, 1 = V.
+ *   mode 0: out is uint8 [S][n_tokens][D], the quantised ints q in SLOT order.
+ *   mode 1: out is fp32 [S][n_tokens][D], x_hat = zero + scale * q rounded
+ *           once to fp32, in TOKEN order (through perm).
+ */
+int packkv_decompress(const packkv_cache_t* cache, int32_t which, int32_t mode,
+                      void* out, void* stream);
+
+/*
+ * packkv_softmax_rows - p = exp(s*scale - max) / sum over the first T entries
+ * of each of `rows` rows (row stride ld); the step between the two GEMVs
+ * (Fig. 1 caption).  scores and p may be the same buffer.
+ */
+int packkv_softmax_rows(const float* scores, float* p, int32_t rows, int64_t T,
+                        int64_t ld, float scale, void* stream);
+
+/* Synchronise `stream`, then return and clear the device error latch
+ * (PACKKV_OK if no kernel reported a problem). */
+int packkv_check(const packkv_cache_t* cache, void* stream);
+
+/*
+ * packkv_stats - width histogram and byte counts of the cache, into device
+ * memory out[32] (uint64): out[0..4] K runs with w = 0..4, out[5..9] the
+ * same for V, out[10] K record bytes, out[11] V record bytes, out[12] K
+ * payload words, out[13] V payload words, out[14] K runs, out[15] V runs.
+ * out must be zeroed by the caller.
+ */
+int packkv_stats(const packkv_cache_t* cache, uint64_t* out, void* stream);
+
+/* Static text for a status code. */
+const char* packkv_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PACKKV_H_ */

@@ -1,0 +1,55 @@
+"""Helpers for the GPU parity tests: seeded inputs, oracle references, comparisons."""
+
+import sys
+
+import numpy as np
+
+import kvsynth
+import oracle
+from oracle import stream as ostream
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def make_kv(law: str, S: int, T: int, block: int, seed: int = 0):
+    """fp16 K, V [S][T][D] for one of the small parity laws."""
+    ks, vs = [], []
+    for s in range(S):
+        if law in ("gauss", "bimodal"):
+            w = kvsynth.Workload("t", 1, S, 1, T, 128, 4, block, law)
+            k, v = kvsynth.stream_kv(w, s, seed=seed, tokens=T)
+        elif law == "struct":
+            k, v = kvsynth.structured_kv(T, 128, block, 32, seed=seed + s)
+        elif law == "mixed":            # half the channels nearly constant: narrow runs
+            k, v = kvsynth.structured_kv(T, 128, block, 32, seed=seed + s, noise=0.3, shuffle=False)
+        elif law == "grid":             # values on an fp16 grid: exact dequantisation
+            rng = np.random.default_rng([seed, s])
+            k = (rng.integers(-60, 60, (T, 128)) * 0.125).astype(np.float16)
+            v = (rng.integers(-60, 60, (T, 128)) * 0.0625).astype(np.float16)
+        else:
+            raise ValueError(law)
+        ks.append(k)
+        vs.append(v)
+    return np.stack(ks), np.stack(vs)
+
+
+def oracle_streams(K, V, bits, block, permute=True):
+    cfg = oracle.Config(bits=bits, block=block, permute=permute)
+    return [ostream.compress(K[s], V[s], cfg) for s in range(K.shape[0])]
+
+
+def rel_l2(y, ref):
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(y - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def worst_row_rel(y, ref):
+    y = np.asarray(y, np.float64).reshape(-1, y.shape[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    num = np.linalg.norm(y - ref, axis=1)
+    den = np.maximum(np.linalg.norm(ref, axis=1), 1e-300)
+    return float((num / den).max())

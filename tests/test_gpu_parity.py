@@ -1,0 +1,197 @@
+"""GPU parity: the HIP path against the fp64 oracle on small seeded inputs.
+
+Bit-exact: records (padding included), offsets, permutation, tail staging,
+decompressed ints and fp32 x_hat.  Floating point: rel-L2 <= 1e-4 per output
+tensor (fp64 norms) for both GEMVs and the softmax helper.
+"""
+
+import numpy as np
+import pytest
+
+from gpu_common import say, make_kv, oracle_streams, rel_l2, worst_row_rel
+from oracle import stream as ostream, attention
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+
+CASES = [
+    # id, bits, block, S, T, permute, law
+    ("b4B64-gauss", 4, 64, 3, 200, True, "gauss"),
+    ("b4B64-struct", 4, 64, 2, 331, True, "struct"),
+    ("b4B64-mixed", 4, 64, 2, 256, True, "mixed"),
+    ("b2B64-bimodal", 2, 64, 2, 190, True, "bimodal"),
+    ("b2B64-struct", 2, 64, 2, 97, True, "struct"),
+    ("b3B64-struct", 3, 64, 2, 257, True, "struct"),
+    ("b3B64-gauss", 3, 64, 2, 130, True, "gauss"),
+    ("b4B128-gauss", 4, 128, 2, 300, True, "gauss"),
+    ("b3B128-struct", 3, 128, 2, 390, True, "struct"),
+    ("b2B128-mixed", 2, 128, 2, 129, True, "mixed"),
+    ("b4B64-identity", 4, 64, 2, 150, False, "struct"),
+    ("b4B64-one-token", 4, 64, 1, 1, True, "gauss"),
+    ("b4B64-grid", 4, 64, 2, 64, True, "grid"),
+]
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch, torch.device("cuda:0")
+
+
+def gpu_cache(torch, dev, K, V, bits, block, permute, max_tokens=None):
+    from decode_gemv_amd import PackedKVCache
+    S, T, _ = K.shape
+    c = PackedKVCache(S, max_tokens or T + 70, bits=bits, block=block, permute=permute, device=str(dev))
+    c.compress(torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev))
+    return c
+
+
+def assert_state_equal(c, refs):
+    """Bit-exact comparison of the whole packed state with the oracle streams."""
+    T = c.n_tokens
+    B = c.block
+    nb = -(-T // B)
+    for which in "KV":
+        arena = c.arena(which).cpu().numpy()
+        offs = c.offsets(which).cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+        for s, ref in enumerate(refs):
+            ro = ref.offsets(which)
+            assert np.array_equal(offs[s, :nb + 1], ro), f"{which} offsets differ, stream {s}"
+            got = arena[s, :ro[-1]].tobytes()
+            exp = ref.arena(which)
+            if got != exp:
+                bad = next(i for i in range(len(exp)) if got[i] != exp[i])
+                blk = int(np.searchsorted(ro, bad, side="right") - 1)
+                raise AssertionError(f"{which} record bytes differ, stream {s}, block {blk}, "
+                                     f"byte {bad - ro[blk]} of the record")
+    perm = c.perm_table().cpu().numpy()
+    for s, ref in enumerate(refs):
+        assert np.array_equal(perm[s, :nb], ref.perm_table()), f"perm differs, stream {s}"
+        nt = T % B
+        tk = c.tail_k.view(c.n_streams, B, 128)[s, :nt].cpu().numpy()
+        tv = c.tail_v.view(c.n_streams, B, 128)[s, :nt].cpu().numpy()
+        assert np.array_equal(tk.view(np.uint16), ref.tail_k.view(np.uint16))
+        assert np.array_equal(tv.view(np.uint16), ref.tail_v.view(np.uint16))
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_encoder_and_decoder_bit_exact(torch_dev, case):
+    torch, dev = torch_dev
+    cid, bits, block, S, T, permute, law = case
+    say("encode", cid)
+    K, V = make_kv(law, S, T, block)
+    refs = oracle_streams(K, V, bits, block, permute)
+    c = gpu_cache(torch, dev, K, V, bits, block, permute)
+    assert c.check() == 0
+    assert_state_equal(c, refs)
+    say("decompress", cid)
+    for which, mode in (("K", 0), ("V", 0), ("K", 1), ("V", 1)):
+        got = c.decompress(which, mode).cpu().numpy()
+        assert c.check() == 0
+        for s, ref in enumerate(refs):
+            kh, vh, qk, qv = ostream.decode_stream(ref)
+            if mode == 0:
+                assert np.array_equal(got[s].astype(np.int64), qk if which == "K" else qv)
+            else:
+                exp = ostream.token_order(ref, kh if which == "K" else vh).astype(np.float32)
+                assert np.array_equal(got[s].view(np.uint32), exp.view(np.uint32)), \
+                    f"{which} x_hat not the correctly rounded fp32 of the exact value"
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("G", [1, 3, 4])
+def test_gemvs_within_tolerance(torch_dev, case, G):
+    torch, dev = torch_dev
+    cid, bits, block, S, T, permute, law = case
+    K, V = make_kv(law, S, T, block)
+    refs = oracle_streams(K, V, bits, block, permute)
+    c = gpu_cache(torch, dev, K, V, bits, block, permute)
+    rng = np.random.default_rng(G)
+    q = rng.standard_normal((S, G, 128)).astype(np.float16)
+    say("qk", cid, "G", G)
+    scores = c.qk(torch.from_numpy(q).to(dev)).cpu().numpy()
+    assert c.check() == 0
+    ref_s = np.stack([attention.qk(q[s], ostream.decode_stream(refs[s])[0]) for s in range(S)])
+    assert rel_l2(scores, ref_s) <= TOL, (rel_l2(scores, ref_s), worst_row_rel(scores, ref_s))
+    # p: a softmax of the oracle scores, rounded to fp32 - the same input to both sides
+    p = np.stack([attention.softmax(ref_s[s], 128) for s in range(S)]).astype(np.float32)
+    say("pv", cid, "G", G)
+    out = c.pv(torch.from_numpy(p).to(dev)).cpu().numpy()
+    assert c.check() == 0
+    ref_o = np.stack([attention.pv(p[s].astype(np.float64), ostream.decode_stream(refs[s])[1])
+                      for s in range(S)])
+    assert rel_l2(out, ref_o) <= TOL, (rel_l2(out, ref_o), worst_row_rel(out, ref_o))
+
+
+def test_softmax_helper(torch_dev):
+    torch, dev = torch_dev
+    from decode_gemv_amd import softmax_rows
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal((5, 1000)) * 20).astype(np.float32)
+    say("softmax")
+    p = softmax_rows(torch.from_numpy(x).to(dev), 1000, 0.125).cpu().numpy()
+    ref = np.stack([attention.softmax(r.astype(np.float64) * 0.125 * np.sqrt(128), 128) for r in x])
+    assert rel_l2(p, ref) <= TOL
+    assert np.all(np.abs(p.sum(1) - 1) < 1e-5)
+
+
+@pytest.mark.parametrize("bits,block,t0,steps", [(3, 64, 60, 70), (4, 128, 0, 130), (2, 64, 64, 1)])
+def test_append_matches_one_shot(torch_dev, bits, block, t0, steps):
+    torch, dev = torch_dev
+    from decode_gemv_amd import PackedKVCache
+    S = 2
+    K, V = make_kv("gauss", S, t0 + steps + 5, block, seed=3)
+    c = PackedKVCache(S, t0 + steps + 10, bits=bits, block=block, device=str(dev))
+    Kd, Vd = torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev)
+    say("append", bits, block, t0, steps)
+    if t0:
+        c.compress(Kd[:, :t0].contiguous(), Vd[:, :t0].contiguous())
+    for t in range(t0, t0 + steps):
+        c.append(Kd[:, t:t + 1].contiguous(), Vd[:, t:t + 1].contiguous())
+    # a multi-token append crossing a block boundary
+    c.append(Kd[:, t0 + steps:].contiguous(), Vd[:, t0 + steps:].contiguous())
+    assert c.check() == 0
+    refs = oracle_streams(K, V, bits, block)
+    assert c.n_tokens == K.shape[1]
+    assert_state_equal(c, refs)
+
+
+def test_outputs_leave_the_leading_dimension_alone(torch_dev):
+    torch, dev = torch_dev
+    K, V = make_kv("gauss", 2, 100, 64)
+    c = gpu_cache(torch, dev, K, V, 4, 64, True)
+    q = torch.from_numpy(np.ones((2, 2, 128), np.float16)).to(dev)
+    sc = torch.full((2, 2, 107), float("nan"), device=dev)
+    say("ld canary")
+    c.qk(q, sc)
+    s = sc.cpu().numpy()
+    assert np.all(np.isfinite(s[:, :, :100])) and np.all(np.isnan(s[:, :, 100:]))
+
+
+def test_pv_is_bitwise_reproducible(torch_dev):
+    torch, dev = torch_dev
+    K, V = make_kv("gauss", 2, 1000, 64)
+    c = gpu_cache(torch, dev, K, V, 4, 64, True)
+    p = torch.rand(2, 1, 1000, device=dev)
+    say("determinism")
+    a = c.pv(p).clone()
+    b = c.pv(p).clone()
+    assert torch.equal(a, b)
+
+
+def test_corrupt_header_is_reported_not_used(torch_dev):
+    torch, dev = torch_dev
+    K, V = make_kv("gauss", 1, 128, 64)
+    c = gpu_cache(torch, dev, K, V, 4, 64, True)
+    arena = c.arena("K")
+    arena[0, 512 + 5] = 0x70          # width 7 > b: invalid
+    q = torch.ones(1, 1, 128, dtype=torch.float16, device=dev)
+    sc = torch.full((1, 1, 128), float("nan"), device=dev)
+    say("corrupt header")
+    c.qk(q, sc)
+    from decode_gemv_amd import _lib
+    assert c.check() == _lib.ECORRUPT
+    s = sc.cpu().numpy()
+    assert np.all(np.isnan(s[0, 0, :64])) and np.all(np.isfinite(s[0, 0, 64:]))
+    assert c.check() == 0               # the latch was cleared
