@@ -34,14 +34,12 @@ __host__ __device__ constexpr int max_record_bytes(bool is_v, int B, int bits) {
 }
 
 // ---------------------------------------------------------------------------
-// fp16 bit helpers (exact).  Only positive finite patterns are used for steps.
-__device__ __forceinline__ double f16_bits_to_double(uint32_t h) {
-  uint32_t e = (h >> 10) & 31u, mant = h & 1023u;
-  double v = (e == 0) ? ldexp((double)mant, -24) : ldexp((double)(1024u + mant), (int)e - 25);
-  return (h & 0x8000u) ? -v : v;
-}
+// fp16 bit helpers (exact).
 __device__ __forceinline__ float f16_bits_to_float(uint32_t h) {
-  return (float)f16_bits_to_double(h);  // exact: fp16 values are fp32 values
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);   // v_cvt_f32_f16, exact
+}
+__device__ __forceinline__ double f16_bits_to_double(uint32_t h) {
+  return (double)f16_bits_to_float(h);                        // both conversions exact
 }
 
 // ---------------------------------------------------------------------------
@@ -106,30 +104,84 @@ __device__ __forceinline__ void run_to_nibbles(int w, uint32_t m, const uint32_t
   out[0] += mm; out[1] += mm; out[2] += mm; out[3] += mm;
 }
 
+// A run stored at the full width BITS: its BITS words -> four container words.
+template <int BITS>
+__device__ __forceinline__ void full_to_nibbles(const uint32_t wd[4], uint32_t out[4]) {
+  if constexpr (BITS == 4) {
+    out[0] = wd[0]; out[1] = wd[1]; out[2] = wd[2]; out[3] = wd[3];
+  } else if constexpr (BITS == 3) {
+    out[0] = spread3to4(bits_at<0>(wd[0], wd[1], wd[2], 0u));
+    out[1] = spread3to4(bits_at<24>(wd[0], wd[1], wd[2], 0u));
+    out[2] = spread3to4(bits_at<48>(wd[0], wd[1], wd[2], 0u));
+    out[3] = spread3to4(bits_at<72>(wd[0], wd[1], wd[2], 0u));
+  } else {
+    out[0] = spread2to4(wd[0]);
+    out[1] = spread2to4(wd[0] >> 16);
+    out[2] = spread2to4(wd[1]);
+    out[3] = spread2to4(wd[1] >> 16);
+  }
+}
+
+// m (0..15) in all eight nibbles of a word.
+__device__ __forceinline__ uint32_t nibble_splat(uint32_t m) {
+  const uint32_t t = (m & 15u) * 0x1111u;     // fits 24 bits: v_mul_u32_u24
+  return t | (t << 16);
+}
+
+// Four header bytes (w << 4 | m) of runs that are all at the full width BITS
+// with a consistent minimum (m + 2^(BITS-1) <= 2^BITS - 1): SWAR test.
+template <int BITS>
+__device__ __forceinline__ bool hdr4_full(uint32_t x) {
+  constexpr uint32_t want = (uint32_t)BITS * 0x10101010u;
+  constexpr uint32_t mbad = (0x0Fu & ~((1u << (BITS - 1)) - 1u)) * 0x01010101u;
+  return ((x ^ want) & (0xF0F0F0F0u | mbad)) == 0u;
+}
+
 // Latch the first device-side error code.
 __device__ __forceinline__ void latch(int32_t* status, int code) {
   if (status) atomicCAS(status, 0, code);
 }
 
-// Wave-wide sum with butterfly shuffles.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+// Cross-lane helpers on DPP (VALU only, no LDS round trips).
+// dpp<CTRL>(v): row_shr:n = 0x110+n, row_bcast:15 = 0x142, row_bcast:31 = 0x143;
+// lanes without a source read 0, lanes of disabled rows get 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, true));
+}
+// Inclusive prefix sum over the 64 lanes (Hillis-Steele inside 16-lane rows,
+// then row broadcasts).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_i<0x111>(v);
+  v += dpp_i<0x112>(v);
+  v += dpp_i<0x114>(v);
+  v += dpp_i<0x118>(v);
+  v += dpp_i<0x142, 0xA>(v);
+  v += dpp_i<0x143, 0xC>(v);
   return v;
+}
+__device__ __forceinline__ float wave_incl_scan_f(float v) {
+  v += dpp_f<0x111>(v);
+  v += dpp_f<0x112>(v);
+  v += dpp_f<0x114>(v);
+  v += dpp_f<0x118>(v);
+  v += dpp_f<0x142, 0xA>(v);
+  v += dpp_f<0x143, 0xC>(v);
+  return v;
+}
+// Wave-wide sums, returned as wave-uniform values.
+__device__ __forceinline__ float wave_sum(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_incl_scan_f(v)), 63));
 }
 __device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return __builtin_amdgcn_readlane(wave_incl_scan(v), 63);
 }
-// Inclusive prefix sum across the 64 lanes of a wave (Hillis-Steele).
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  return v;
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
 }
 
 }  // namespace packkv

@@ -75,47 +75,131 @@ __device__ __forceinline__ void store_record(uint8_t* lds, uint32_t bytes, int l
 }
 
 // Header decode + width scan for the lane's runs (NRL runs per lane, run
-// index l + 64k).  Returns false if the record is inconsistent.
+// index l + 64k).  Returns false if the record is inconsistent.  When every
+// run is at full width the offsets are implicit and no scan is needed;
+// `aligned` then reports that every run starts on a 16-byte boundary.
 template <int NRL>
 __device__ __forceinline__ bool scan_runs(const uint8_t* rec, int hdr_off, int pay_off, uint32_t size,
                                           int nruns, int bits, int lane,
-                                          int w[NRL], uint32_t m[NRL], uint32_t off[NRL]) {
+                                          int w[NRL], uint32_t m[NRL], uint32_t off[NRL], bool& full) {
   const int L = (1 << bits) - 1;
-  int bad = 0;
-  uint32_t base = 0;
+  bool bad = false, narrow = false;
 #pragma unroll
   for (int k = 0; k < NRL; ++k) {
     const int ri = lane + 64 * k;
-    uint32_t h = ri < nruns ? rec[hdr_off + ri] : 0u;
+    const uint32_t h = ri < nruns ? rec[hdr_off + ri] : 0u;
     w[k] = (int)(h >> 4);
     m[k] = h & 15u;
     // a valid run has max - m in [2^(w-1), 2^w - 1] and max <= L
     bad |= (w[k] > bits) | ((int)m[k] > L) | (w[k] > 0 && (int)m[k] + (1 << (w[k] - 1)) > L);
-    const int incl = wave_incl_scan(w[k], lane);
-    off[k] = base + (uint32_t)(incl - w[k]);
-    base += (uint32_t)__shfl(incl, 63, kWave);
+    narrow |= w[k] != bits;
   }
-  bad = wave_sum_i(bad);
-  return bad == 0 && (uint32_t)pad16(pay_off + 4 * (int)base) == size;
+  if (__ballot(bad)) return false;
+  uint32_t base;
+  full = __ballot(narrow) == 0;
+  if (full) {
+#pragma unroll
+    for (int k = 0; k < NRL; ++k) off[k] = (uint32_t)((lane + 64 * k) * bits);
+    base = (uint32_t)(NRL * 64 * bits);
+  } else {
+    base = 0;
+#pragma unroll
+    for (int k = 0; k < NRL; ++k) {
+      const int incl = wave_incl_scan(w[k]);
+      off[k] = base + (uint32_t)(incl - w[k]);
+      base += (uint32_t)__builtin_amdgcn_readlane(incl, 63);
+    }
+  }
+  return (uint32_t)pad16(pay_off + 4 * (int)base) == size;
 }
 
-// Read the first four payload words of a run from LDS (may run past the run
-// into padding; the staging buffer has 16 bytes of slack).
-__device__ __forceinline__ void run_words(const uint8_t* rec, int pay_off, uint32_t off, uint32_t wd[4]) {
+// The first four payload words of a run (may run past the run into the next
+// run or the padding; the staging buffer has 16 bytes of slack).  `al16`:
+// the run starts on a 16-byte boundary.
+__device__ __forceinline__ void run_words(const uint8_t* rec, int pay_off, uint32_t off, bool al16, uint32_t wd[4]) {
   const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + pay_off) + off;
-  wd[0] = p[0]; wd[1] = p[1]; wd[2] = p[2]; wd[3] = p[3];
+  if (al16) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    wd[0] = v.x; wd[1] = v.y; wd[2] = v.z; wd[3] = v.w;
+  } else {
+    wd[0] = p[0]; wd[1] = p[1]; wd[2] = p[2]; wd[3] = p[3];
+  }
 }
 
 // ---------------------------------------------------------------------------
+// Shared per-block decode: header check, run offsets, container words.
+//
+// Fast path (uniform per wave): every run of a full block is at the full width
+// BITS with a consistent minimum; offsets are then implicit and each run is
+// BITS words at (run index) * BITS.  Otherwise the headers are validated one
+// by one and a wave prefix sum gives the offsets.
+template <int B, int BITS, bool IS_V>
+struct BlockDecoder {
+  static constexpr int NR = B / kR;
+  static constexpr int NRL = NR * kD / 64;          // runs per lane: run l + 64k, r = k/2
+  static constexpr int HDR = hdr_offset(IS_V, B);
+
+  // Decode the lane's runs of the staged record into container words
+  // nib[k][0..3] (run l + 64k).  Returns false if the record is inconsistent.
+  __device__ __forceinline__ static bool decode(const uint8_t* rec, uint32_t size, int nr, int lane,
+                                                uint32_t nib[NRL][4]) {
+    const int pay = payload_offset(IS_V, B, nr);
+    bool fast = false;
+    if (nr == NR) {
+      bool ok = true;
+#pragma unroll
+      for (int i = 0; i < NR / 2; ++i)                // header dwords lane + 64i
+        ok &= hdr4_full<BITS>(reinterpret_cast<const uint32_t*>(rec + HDR)[lane + 64 * i]);
+      fast = __ballot(!ok) == 0 && (uint32_t)(pay + 4 * NR * kD * BITS) == size;
+    }
+    if (fast) {
+#pragma unroll
+      for (int k = 0; k < NRL; ++k) {
+        const uint32_t m = rec[HDR + lane + 64 * k] & 15u;
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + pay) + (lane + 64 * k) * BITS;
+        uint32_t wd[4] = {0u, 0u, 0u, 0u};
+        if constexpr (BITS == 4) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+          wd[0] = v.x; wd[1] = v.y; wd[2] = v.z; wd[3] = v.w;
+        } else if constexpr (BITS == 2) {
+          const uint2 v = *reinterpret_cast<const uint2*>(p);
+          wd[0] = v.x; wd[1] = v.y;
+        } else {
+          wd[0] = p[0]; wd[1] = p[1]; wd[2] = p[2];
+        }
+        full_to_nibbles<BITS>(wd, nib[k]);
+        const uint32_t mm = nibble_splat(m);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) nib[k][kk] += mm;
+      }
+      return true;
+    }
+    int w[NRL];
+    uint32_t m[NRL], ro[NRL];
+    bool full;
+    if (!scan_runs<NRL>(rec, HDR, pay, size, nr * kD, BITS, lane, w, m, ro, full)) return false;
+#pragma unroll
+    for (int k = 0; k < NRL; ++k) {
+      uint32_t wd[4];
+      nib[k][0] = nib[k][1] = nib[k][2] = nib[k][3] = 0u;
+      if ((k >> 1) < nr) {
+        run_words(rec, pay, ro[k], false, wd);
+        run_to_nibbles(w[k], m[k], wd, nib[k]);
+      }
+    }
+    return true;
+  }
+};
+
+// ---------------------------------------------------------------------------
 // K side.
-template <int B, int GT>
+template <int B, int BITS, int GT>
 __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
-  constexpr int NR = B / kR;                       // runs per block
-  constexpr int NRL = NR * kD / 64;                // runs per lane
+  using Dec = BlockDecoder<B, BITS, false>;
+  constexpr int NRL = Dec::NRL;
   constexpr int REC = max_record_bytes(false, B, 4);
   constexpr int NCH = (REC + 1023) / 1024;
   constexpr int ROWW = kD + 4;                     // plane row: 128 words + 16 B pad
-  constexpr int HDR = hdr_offset(false, B);
   constexpr int REDB = GT * 64 * 9 * 4;            // channel-group reduction
   constexpr int BUF = (REC + 16) > REDB ? (REC + 16) : REDB;
   __shared__ __attribute__((aligned(16))) uint8_t rec[BUF];
@@ -129,29 +213,29 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
   const int j0 = split * a.blocks_per_wg;
   const int j1 = min(a.nb, j0 + a.blocks_per_wg);
   if (j0 >= j1) return;
+  const int nj = j1 - j0;
   const uint8_t* arena = a.arena + (uint64_t)s * a.arena_stride;
   const uint32_t* offs = a.off + (int64_t)s * a.off_stride;
   const float unit_inv = 1.0f / fp8_unit();
-
   // offsets of this workgroup's records: lane i holds off[j0 + i]
-  const int nj = j1 - j0;
-  uint32_t my_off = lane <= nj ? offs[j0 + lane] : 0u;
-  uint32_t my_off2 = lane + 64 <= nj ? offs[j0 + 64 + lane] : 0u;
+  const uint32_t my_off = lane <= nj ? offs[j0 + lane] : 0u;
+  const uint32_t my_off2 = lane + 64 <= nj ? offs[j0 + 64 + lane] : 0u;
   auto off_of = [&](int i) -> uint32_t {
-    return i < 64 ? (uint32_t)__shfl((int)my_off, i, kWave) : (uint32_t)__shfl((int)my_off2, i - 64, kWave);
+    return i < 64 ? readlane_u32(my_off, i) : readlane_u32(my_off2, i - 64);
   };
-
   const int g8 = lane & 7, cg = lane >> 3;
 
   for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
     // queries for the channels this lane stages (c = lane, lane + 64)
-    float qa[GT], qb[GT];
+    float qa[GT], qb[GT], qau[GT], qbu[GT];
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       const bool ok = gq0 + g < a.G;
       const uint16_t* qp = a.q + ((int64_t)s * a.G + gq0 + g) * kD;
       qa[g] = ok ? f16_bits_to_float(qp[lane]) : 0.f;
       qb[g] = ok ? f16_bits_to_float(qp[lane + 64]) : 0.f;
+      qau[g] = qa[g] * unit_inv;
+      qbu[g] = qb[g] * unit_inv;
     }
     u32x4 pre[NCH];
     {
@@ -175,27 +259,16 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
       }
       __syncthreads();
 
-      const int pay = payload_offset(false, B, nr);
-      int w[NRL];
-      uint32_t m[NRL], ro[NRL];
-      if (!scan_runs<NRL>(rec, HDR, pay, size, nr * kD, a.bits, lane, w, m, ro)) {
+      uint32_t nib[NRL][4];
+      if (!Dec::decode(rec, size, nr, lane, nib)) {
         if (lane == 0) latch(a.status, PACKKV_ECORRUPT);
         continue;
       }
-      // decode every run of the lane into the container plane
 #pragma unroll
       for (int k = 0; k < NRL; ++k) {
-        const int ri = lane + 64 * k;
-        const int r = ri / kD, c = ri % kD;
-        uint32_t wd[4], nib[4];
-        if (r < nr) {
-          run_words(rec, pay, ro[k], wd);
-          run_to_nibbles(w[k], m[k], wd, nib);
-        } else {
-          nib[0] = nib[1] = nib[2] = nib[3] = 0u;
-        }
+        const int r = k >> 1, c = lane + 64 * (k & 1);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) plane[(r * 4 + kk) * ROWW + c] = nib[kk];
+        for (int kk = 0; kk < 4; ++kk) plane[(r * 4 + kk) * ROWW + c] = nib[k][kk];
       }
       // q' = q * scale (per channel), beta = q . zero
       float beta[GT];
@@ -205,9 +278,9 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
         const float za = f16_bits_to_float(sc[kD + lane]), zb = f16_bits_to_float(sc[kD + lane + 64]);
 #pragma unroll
         for (int g = 0; g < GT; ++g) {
-          qs[g * kD + lane] = qa[g] * sa * unit_inv;
-          qs[g * kD + lane + 64] = qb[g] * sb * unit_inv;
-          beta[g] = wave_sum(qa[g] * za + qb[g] * zb);
+          qs[g * kD + lane] = qau[g] * sa;
+          qs[g * kD + lane + 64] = qbu[g] * sb;
+          beta[g] = wave_sum(fmaf(qa[g], za, qb[g] * zb));
         }
       }
       __syncthreads();
@@ -225,7 +298,7 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int c0 = cg * 16 + i4 * 4;
-          const uint4 nw = *reinterpret_cast<const uint4*>(&plane[row * ROWW + c0]);
+          const u32x4 nw = *reinterpret_cast<const u32x4*>(&plane[row * ROWW + c0]);
           const uint32_t words[4] = {nw.x, nw.y, nw.z, nw.w};
           float qq[GT][4];
 #pragma unroll
@@ -266,13 +339,14 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
 
 // ---------------------------------------------------------------------------
 // V side: split-T partial sums into ws, then a fixed-order reduction.
-template <int B, int GT>
+template <int B, int BITS, int GT>
 __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
-  constexpr int NR = B / kR;
-  constexpr int NRL = NR * kD / 64;
+  using Dec = BlockDecoder<B, BITS, true>;
+  constexpr int NR = Dec::NR;
+  constexpr int NRL = Dec::NRL;                    // run l + 64k: r = k/2, channel l + 64(k&1)
+  constexpr int NH = B / 64;                       // slots per lane
   constexpr int REC = max_record_bytes(true, B, 4);
   constexpr int NCH = (REC + 1023) / 1024;
-  constexpr int HDR = hdr_offset(true, B);
   __shared__ __attribute__((aligned(16))) uint8_t rec[REC + 16];
   __shared__ __attribute__((aligned(16))) float pp[GT * B];
 
@@ -281,14 +355,14 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
   const int split = blockIdx.x % a.splits;
   const int j0 = split * a.blocks_per_wg;
   const int j1 = min(a.nb, j0 + a.blocks_per_wg);
+  const int nj = max(0, j1 - j0);
   const uint8_t* arena = a.arena + (uint64_t)s * a.arena_stride;
   const uint32_t* offs = a.off + (int64_t)s * a.off_stride;
   const float unit_inv = 1.0f / fp8_unit();
-  const int nj = max(0, j1 - j0);
-  uint32_t my_off = lane <= nj ? offs[j0 + lane] : 0u;
-  uint32_t my_off2 = lane + 64 <= nj ? offs[j0 + 64 + lane] : 0u;
+  const uint32_t my_off = lane <= nj ? offs[j0 + lane] : 0u;
+  const uint32_t my_off2 = lane + 64 <= nj ? offs[j0 + 64 + lane] : 0u;
   auto off_of = [&](int i) -> uint32_t {
-    return i < 64 ? (uint32_t)__shfl((int)my_off, i, kWave) : (uint32_t)__shfl((int)my_off2, i - 64, kWave);
+    return i < 64 ? readlane_u32(my_off, i) : readlane_u32(my_off2, i - 64);
   };
 
   for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
@@ -296,10 +370,24 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
     float pz[GT];
 #pragma unroll
     for (int g = 0; g < GT; ++g) { acc[g][0] = acc[g][1] = 0.f; pz[g] = 0.f; }
+    // weights of the lane's slots (slot h*64 + lane) for block j
+    auto load_p = [&](int j, float pv[GT][NH]) {
+      const int n = (int)imin64(B, a.n_tokens - (int64_t)j * B);
+#pragma unroll
+      for (int g = 0; g < GT; ++g)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          const int sl = h * 64 + lane;
+          pv[g][h] = (sl < n && gq0 + g < a.G)
+                         ? a.p[((int64_t)s * a.G + gq0 + g) * a.ld + (int64_t)j * B + sl] : 0.f;
+        }
+    };
     u32x4 pre[NCH];
+    float pnext[GT][NH];
     if (nj > 0) {
       const uint32_t o0 = off_of(0), s0 = off_of(1) - o0;
       if (record_ok(o0, s0, a.arena_stride, REC)) load_record<NCH>(arena + o0, s0, lane, pre);
+      load_p(j0, pnext);
     }
     for (int jj = 0; jj < nj; ++jj) {
       const int j = j0 + jj;
@@ -312,60 +400,59 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
         break;
       }
       store_record<NCH>(rec, size, lane, pre);
+      float pcur[GT][NH];
+#pragma unroll
+      for (int g = 0; g < GT; ++g)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) pcur[g][h] = pnext[g][h];
       if (jj + 1 < nj) {
         const uint32_t o1 = off_of(jj + 1), s1 = off_of(jj + 2) - o1;
         if (record_ok(o1, s1, a.arena_stride, REC)) load_record<NCH>(arena + o1, s1, lane, pre);
+        load_p(j + 1, pnext);
       }
       __syncthreads();
-      // p' = p * scale per slot; sum p * zero
+      // p' = p * scale per slot (to LDS); sum p * zero (per lane)
       {
         const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec);
 #pragma unroll
-        for (int h = 0; h < B / 64; ++h) {
+        for (int h = 0; h < NH; ++h) {
           const int sl = h * 64 + lane;
+          const float scl = f16_bits_to_float(sc[sl]) * unit_inv, zer = f16_bits_to_float(sc[B + sl]);
 #pragma unroll
           for (int g = 0; g < GT; ++g) {
-            float pv = 0.f;
-            if (sl < n && gq0 + g < a.G)
-              pv = a.p[((int64_t)s * a.G + gq0 + g) * a.ld + (int64_t)j * B + sl];
-            pp[g * B + sl] = pv * f16_bits_to_float(sc[sl]) * unit_inv;
-            pz[g] = fmaf(pv, f16_bits_to_float(sc[B + sl]), pz[g]);
+            pp[g * B + sl] = pcur[g][h] * scl;
+            pz[g] = fmaf(pcur[g][h], zer, pz[g]);
           }
         }
       }
+      uint32_t nib[NRL][4];
+      const bool ok = Dec::decode(rec, size, nr, lane, nib);
       __syncthreads();
-      const int pay = payload_offset(true, B, nr);
-      int w[NRL];
-      uint32_t m[NRL], ro[NRL];
-      if (!scan_runs<NRL>(rec, HDR, pay, size, nr * kD, a.bits, lane, w, m, ro)) {
+      if (!ok) {
         if (lane == 0) latch(a.status, PACKKV_ECORRUPT);
         continue;
       }
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         if (r >= nr) break;
-        float pr[GT][32];
 #pragma unroll
-        for (int g = 0; g < GT; ++g)
+        for (int kk = 0; kk < 4; ++kk) {
+          float pr[GT][8];
 #pragma unroll
-          for (int i = 0; i < 32; i += 4) {
-            const float4 t = *reinterpret_cast<const float4*>(&pp[g * B + r * 32 + i]);
-            pr[g][i] = t.x; pr[g][i + 1] = t.y; pr[g][i + 2] = t.z; pr[g][i + 3] = t.w;
+          for (int g = 0; g < GT; ++g) {
+            const float4 t0 = *reinterpret_cast<const float4*>(&pp[g * B + r * 32 + kk * 8]);
+            const float4 t1 = *reinterpret_cast<const float4*>(&pp[g * B + r * 32 + kk * 8 + 4]);
+            pr[g][0] = t0.x; pr[g][1] = t0.y; pr[g][2] = t0.z; pr[g][3] = t0.w;
+            pr[g][4] = t1.x; pr[g][5] = t1.y; pr[g][6] = t1.z; pr[g][7] = t1.w;
           }
 #pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-          const int k = r * 2 + ch;            // run index lane + 64k = r*128 + ch*64 + lane
-          uint32_t wd[4], nib[4];
-          run_words(rec, pay, ro[k], wd);
-          run_to_nibbles(w[k], m[k], wd, nib);
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
+          for (int ch = 0; ch < 2; ++ch) {
             float f[8];
-            nibbles_to_f32(nib[kk], f);
+            nibbles_to_f32(nib[2 * r + ch][kk], f);
 #pragma unroll
             for (int g = 0; g < GT; ++g)
 #pragma unroll
-              for (int i = 0; i < 8; ++i) acc[g][ch] = fmaf(pr[g][kk * 8 + i], f[i], acc[g][ch]);
+              for (int i = 0; i < 8; ++i) acc[g][ch] = fmaf(pr[g][i], f[i], acc[g][ch]);
           }
         }
       }
@@ -422,7 +509,8 @@ __global__ __launch_bounds__(64) void k_decompress(GemvArgs a, const uint8_t* pe
   const int pay = payload_offset(IS_V, B, nr);
   int w[NRL];
   uint32_t m[NRL], ro[NRL];
-  if (!scan_runs<NRL>(rec, HDR, pay, size, nr * kD, a.bits, lane, w, m, ro)) {
+  bool full;
+  if (!scan_runs<NRL>(rec, HDR, pay, size, nr * kD, a.bits, lane, w, m, ro, full)) {
     if (lane == 0) latch(a.status, PACKKV_ECORRUPT);
     return;
   }
@@ -434,7 +522,7 @@ __global__ __launch_bounds__(64) void k_decompress(GemvArgs a, const uint8_t* pe
     const int r = ri / kD, c = ri % kD;
     if (r >= nr) continue;
     uint32_t wd[4], nib[4];
-    run_words(rec, pay, ro[k], wd);
+    run_words(rec, pay, ro[k], false, wd);
     run_to_nibbles(w[k], m[k], wd, nib);
     for (int i = 0; i < kR; ++i) {
       const int sl = r * kR + i;
@@ -494,50 +582,100 @@ __global__ __launch_bounds__(64) void k_stats(GemvArgs a, unsigned long long* ou
 }
 
 // Softmax over the first T entries of each row: p = exp(s*scale - max)/sum.
-__global__ __launch_bounds__(256) void k_softmax(const float* scores, float* p, int64_t T, int64_t ld,
-                                                 float scale) {
-  __shared__ float red[8];
+// One workgroup of 1024 threads per row: an online (max, sum) pass, then the
+// normalising write pass.
+__device__ __forceinline__ void online_add(float& m, float& sum, float v) {
+  if (v > m) {
+    sum = sum * __expf(m - v) + 1.0f;
+    m = v;
+  } else {
+    sum += __expf(v - m);
+  }
+}
+__device__ __forceinline__ void online_merge(float& m, float& sum, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;
+  sum = sum * __expf(m - M) + s2 * __expf(m2 - M);
+  m = M;
+}
+
+__global__ __launch_bounds__(1024) void k_softmax(const float* scores, float* p, int64_t T, int64_t ld,
+                                                  float scale) {
+  __shared__ float sm[16], ss[16];
   const float* x = scores + (int64_t)blockIdx.x * ld;
   float* y = p + (int64_t)blockIdx.x * ld;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  float mx = -INFINITY;
-  for (int64_t i = tid; i < T; i += 256) mx = fmaxf(mx, x[i] * scale);
-  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-  if (lane == 0) red[wv] = mx;
+  const bool vec = ((ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(p) & 15) == 0);
+  const int64_t T4 = vec ? (T >> 2) : 0;
+  float m = -INFINITY, sum = 0.f;
+  for (int64_t i = tid; i < T4; i += 1024) {
+    const float4 v = reinterpret_cast<const float4*>(x)[i];
+    online_add(m, sum, v.x * scale);
+    online_add(m, sum, v.y * scale);
+    online_add(m, sum, v.z * scale);
+    online_add(m, sum, v.w * scale);
+  }
+  for (int64_t i = 4 * T4 + tid; i < T; i += 1024) online_add(m, sum, x[i] * scale);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, kWave), s2 = __shfl_xor(sum, o, kWave);
+    online_merge(m, sum, m2, s2);
+  }
+  if (lane == 0) { sm[wv] = m; ss[wv] = sum; }
   __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  float sum = 0.f;
-  for (int64_t i = tid; i < T; i += 256) sum += expf(x[i] * scale - mx);
-  sum = wave_sum(sum);
-  if (lane == 0) red[4 + wv] = sum;
-  __syncthreads();
-  const float inv = 1.0f / ((red[4] + red[5]) + (red[6] + red[7]));
-  for (int64_t i = tid; i < T; i += 256) y[i] = expf(x[i] * scale - mx) * inv;
+  m = sm[0];
+  sum = ss[0];
+  for (int i = 1; i < 16; ++i) online_merge(m, sum, sm[i], ss[i]);
+  const float inv = 1.0f / sum;
+  for (int64_t i = tid; i < T4; i += 1024) {
+    const float4 v = reinterpret_cast<const float4*>(x)[i];
+    float4 r;
+    r.x = __expf(v.x * scale - m) * inv;
+    r.y = __expf(v.y * scale - m) * inv;
+    r.z = __expf(v.z * scale - m) * inv;
+    r.w = __expf(v.w * scale - m) * inv;
+    reinterpret_cast<float4*>(y)[i] = r;
+  }
+  for (int64_t i = 4 * T4 + tid; i < T; i += 1024) y[i] = __expf(x[i] * scale - m) * inv;
 }
 
 // ---------------------------------------------------------------------------
 // Launchers.
-template <int B>
-static hipError_t qk_dispatch(const GemvArgs& a, int n_streams, hipStream_t st) {
-  dim3 grid(n_streams * a.splits), block(64);
-  if (a.G == 1) hipLaunchKernelGGL((k_qk_gemv<B, 1>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((k_qk_gemv<B, 4>), grid, block, 0, st, a);
-  return hipGetLastError();
+template <int B, int BITS>
+static void qk_launch(const GemvArgs& a, dim3 grid, hipStream_t st) {
+  if (a.G == 1) hipLaunchKernelGGL((k_qk_gemv<B, BITS, 1>), grid, dim3(64), 0, st, a);
+  else hipLaunchKernelGGL((k_qk_gemv<B, BITS, 4>), grid, dim3(64), 0, st, a);
+}
+template <int B, int BITS>
+static void pv_launch(const GemvArgs& a, dim3 grid, hipStream_t st) {
+  if (a.G == 1) hipLaunchKernelGGL((k_pv_gemv<B, BITS, 1>), grid, dim3(64), 0, st, a);
+  else hipLaunchKernelGGL((k_pv_gemv<B, BITS, 4>), grid, dim3(64), 0, st, a);
 }
 hipError_t launch_qk(const GemvArgs& a, int B, int n_streams, hipStream_t st) {
-  return B == 64 ? qk_dispatch<64>(a, n_streams, st) : qk_dispatch<128>(a, n_streams, st);
-}
-
-template <int B>
-static hipError_t pv_dispatch(const GemvArgs& a, int n_streams, hipStream_t st) {
-  dim3 grid(n_streams * a.splits), block(64);
-  if (a.G == 1) hipLaunchKernelGGL((k_pv_gemv<B, 1>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((k_pv_gemv<B, 4>), grid, block, 0, st, a);
+  const dim3 grid(n_streams * a.splits);
+  switch (B * 8 + a.bits) {
+    case 64 * 8 + 2: qk_launch<64, 2>(a, grid, st); break;
+    case 64 * 8 + 3: qk_launch<64, 3>(a, grid, st); break;
+    case 64 * 8 + 4: qk_launch<64, 4>(a, grid, st); break;
+    case 128 * 8 + 2: qk_launch<128, 2>(a, grid, st); break;
+    case 128 * 8 + 3: qk_launch<128, 3>(a, grid, st); break;
+    default: qk_launch<128, 4>(a, grid, st); break;
+  }
   return hipGetLastError();
 }
+
 hipError_t launch_pv(const GemvArgs& a, int B, int n_streams, float* out, hipStream_t st) {
-  hipError_t e = B == 64 ? pv_dispatch<64>(a, n_streams, st) : pv_dispatch<128>(a, n_streams, st);
+  const dim3 grid(n_streams * a.splits);
+  switch (B * 8 + a.bits) {
+    case 64 * 8 + 2: pv_launch<64, 2>(a, grid, st); break;
+    case 64 * 8 + 3: pv_launch<64, 3>(a, grid, st); break;
+    case 64 * 8 + 4: pv_launch<64, 4>(a, grid, st); break;
+    case 128 * 8 + 2: pv_launch<128, 2>(a, grid, st); break;
+    case 128 * 8 + 3: pv_launch<128, 3>(a, grid, st); break;
+    default: pv_launch<128, 4>(a, grid, st); break;
+  }
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_pv_reduce, dim3(n_streams * a.G), dim3(128), 0, st, a.ws, a.splits, out);
   return hipGetLastError();
@@ -571,7 +709,7 @@ hipError_t launch_stats(const GemvArgs& a, int B, bool is_v, int n_streams, unsi
 
 hipError_t launch_softmax(const float* scores, float* p, int rows, int64_t T, int64_t ld, float scale,
                           hipStream_t st) {
-  hipLaunchKernelGGL(k_softmax, dim3(rows), dim3(256), 0, st, scores, p, T, ld, scale);
+  hipLaunchKernelGGL(k_softmax, dim3(rows), dim3(1024), 0, st, scores, p, T, ld, scale);
   return hipGetLastError();
 }
 

@@ -29,6 +29,13 @@ def make_kv(law: str, S: int, T: int, block: int, seed: int = 0):
             rng = np.random.default_rng([seed, s])
             k = (rng.integers(-60, 60, (T, 128)) * 0.125).astype(np.float16)
             v = (rng.integers(-60, 60, (T, 128)) * 0.0625).astype(np.float16)
+        elif law == "subnormal":        # fp16 subnormals, signed zeros, tiny ranges
+            rng = np.random.default_rng([seed, s, 7])
+            bits = rng.integers(0, 0x0400, (2, T, 128)).astype(np.uint16)
+            bits |= (rng.random((2, T, 128)) < 0.5).astype(np.uint16) << 15
+            big = rng.random((2, T, 128)) < 0.02           # a few normal values
+            bits[big] = rng.integers(0x0400, 0x1400, int(big.sum())).astype(np.uint16)
+            k, v = bits[0].view(np.float16), bits[1].view(np.float16)
         else:
             raise ValueError(law)
         ks.append(k)

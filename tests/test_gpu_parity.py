@@ -29,6 +29,7 @@ CASES = [
     ("b4B64-identity", 4, 64, 2, 150, False, "struct"),
     ("b4B64-one-token", 4, 64, 1, 1, True, "gauss"),
     ("b4B64-grid", 4, 64, 2, 64, True, "grid"),
+    ("b3B64-subnormal", 3, 64, 2, 100, True, "subnormal"),
 ]
 
 
