@@ -122,10 +122,14 @@ __device__ __forceinline__ void full_to_nibbles(const uint32_t wd[4], uint32_t o
   }
 }
 
-// m (0..15) in all eight nibbles of a word.
+// m (0..15) in all eight nibbles of a word: one shift-or and a byte broadcast
+// (written as v_perm_b32 so that it is not turned into a quarter-rate
+// 32-bit multiply; register-only ALU instruction, no memory access).
 __device__ __forceinline__ uint32_t nibble_splat(uint32_t m) {
-  const uint32_t t = (m & 15u) * 0x1111u;     // fits 24 bits: v_mul_u32_u24
-  return t | (t << 16);
+  const uint32_t b = (m & 15u) | ((m & 15u) << 4);
+  uint32_t r;
+  asm("v_perm_b32 %0, %1, %1, %2" : "=v"(r) : "v"(b), "v"(0u));
+  return r;
 }
 
 // Four header bytes (w << 4 | m) of runs that are all at the full width BITS

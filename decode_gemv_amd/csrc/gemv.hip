@@ -140,51 +140,92 @@ struct BlockDecoder {
   static constexpr int HDR = hdr_offset(IS_V, B);
 
   // Decode the lane's runs of the staged record into container words
-  // nib[k][0..3] (run l + 64k).  Returns false if the record is inconsistent.
+  // nib[k][0..3] (run l + 64k).  Returns false if the record is inconsistent
+  // (a width above BITS, or widths that do not add up to the record size).
   __device__ __forceinline__ static bool decode(const uint8_t* rec, uint32_t size, int nr, int lane,
                                                 uint32_t nib[NRL][4]) {
-    const int pay = payload_offset(IS_V, B, nr);
-    bool fast = false;
     if (nr == NR) {
+      constexpr int pay = payload_offset(IS_V, B, NR);
+      uint32_t h[NRL];
+#pragma unroll
+      for (int k = 0; k < NRL; ++k) h[k] = rec[HDR + lane + 64 * k];
       bool ok = true;
 #pragma unroll
       for (int i = 0; i < NR / 2; ++i)                // header dwords lane + 64i
         ok &= hdr4_full<BITS>(reinterpret_cast<const uint32_t*>(rec + HDR)[lane + 64 * i]);
-      fast = __ballot(!ok) == 0 && (uint32_t)(pay + 4 * NR * kD * BITS) == size;
-    }
-    if (fast) {
+      if (__ballot(!ok) == 0 && (uint32_t)(pay + 4 * NR * kD * BITS) == size) {
+        // every run at full width: offsets are implicit, loads aligned
 #pragma unroll
-      for (int k = 0; k < NRL; ++k) {
-        const uint32_t m = rec[HDR + lane + 64 * k] & 15u;
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + pay) + (lane + 64 * k) * BITS;
-        uint32_t wd[4] = {0u, 0u, 0u, 0u};
-        if constexpr (BITS == 4) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(p);
-          wd[0] = v.x; wd[1] = v.y; wd[2] = v.z; wd[3] = v.w;
-        } else if constexpr (BITS == 2) {
-          const uint2 v = *reinterpret_cast<const uint2*>(p);
-          wd[0] = v.x; wd[1] = v.y;
-        } else {
-          wd[0] = p[0]; wd[1] = p[1]; wd[2] = p[2];
+        for (int k = 0; k < NRL; ++k) {
+          const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + pay) + (lane + 64 * k) * BITS;
+          uint32_t wd[4] = {0u, 0u, 0u, 0u};
+          if constexpr (BITS == 4) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+            wd[0] = v.x; wd[1] = v.y; wd[2] = v.z; wd[3] = v.w;
+          } else if constexpr (BITS == 2) {
+            const uint2 v = *reinterpret_cast<const uint2*>(p);
+            wd[0] = v.x; wd[1] = v.y;
+          } else {
+            wd[0] = p[0]; wd[1] = p[1]; wd[2] = p[2];
+          }
+          full_to_nibbles<BITS>(wd, nib[k]);
+          const uint32_t mm = nibble_splat(h[k]);
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) nib[k][kk] += mm;
         }
-        full_to_nibbles<BITS>(wd, nib[k]);
-        const uint32_t mm = nibble_splat(m);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) nib[k][kk] += mm;
+        return true;
       }
-      return true;
+      return decode_general(rec, size, NR, lane, h, nib);
     }
-    int w[NRL];
-    uint32_t m[NRL], ro[NRL];
-    bool full;
-    if (!scan_runs<NRL>(rec, HDR, pay, size, nr * kD, BITS, lane, w, m, ro, full)) return false;
+    uint32_t h[NRL];
+#pragma unroll
+    for (int k = 0; k < NRL; ++k) h[k] = (k >> 1) < nr ? rec[HDR + lane + 64 * k] : 0u;
+    return decode_general(rec, size, nr, lane, h, nib);
+  }
+
+  // Some run is narrower (or the block is partial).  Offsets follow from the
+  // full-width layout minus the width deficit of every earlier run; only
+  // groups that hold a narrow run need a scan.  Every run is decoded as if it
+  // were full width, then the narrow ones are redone (rare, exec-masked).
+  __device__ __forceinline__ static bool decode_general(const uint8_t* rec, uint32_t size, int nr, int lane,
+                                                        const uint32_t h[NRL], uint32_t nib[NRL][4]) {
+    const int pay = payload_offset(IS_V, B, nr);
+    const int nruns = nr * kD;
+    bool bad = false;
+    uint32_t off[NRL];
+    uint32_t running = 0;                              // deficit of earlier groups
 #pragma unroll
     for (int k = 0; k < NRL; ++k) {
-      uint32_t wd[4];
-      nib[k][0] = nib[k][1] = nib[k][2] = nib[k][3] = 0u;
-      if ((k >> 1) < nr) {
-        run_words(rec, pay, ro[k], false, wd);
-        run_to_nibbles(w[k], m[k], wd, nib[k]);
+      const int w = (int)(h[k] >> 4);
+      bad |= w > BITS;
+      const int d = (lane + 64 * k) < nruns ? BITS - w : 0;
+      const uint32_t base = (uint32_t)((lane + 64 * k) * BITS) - running;
+      if (__ballot(d != 0) == 0) {
+        off[k] = base;
+      } else {
+        const int incl = wave_incl_scan(d);
+        off[k] = base - (uint32_t)(incl - d);
+        running += (uint32_t)__builtin_amdgcn_readlane(incl, 63);
+      }
+    }
+    const uint32_t total = (uint32_t)(nruns * BITS) - running;
+    if (__ballot(bad) || (uint32_t)pad16(pay + 4 * (int)total) != size) return false;
+    uint32_t wd[NRL][4];
+#pragma unroll
+    for (int k = 0; k < NRL; ++k) {
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + pay) + off[k];
+      wd[k][0] = p[0]; wd[k][1] = p[1]; wd[k][2] = p[2]; wd[k][3] = p[3];
+      full_to_nibbles<BITS>(wd[k], nib[k]);
+      const uint32_t mm = nibble_splat(h[k]);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) nib[k][kk] += mm;
+    }
+#pragma unroll
+    for (int k = 0; k < NRL; ++k) {
+      const int w = (int)(h[k] >> 4);
+      if (w != BITS) {
+        if ((k >> 1) < nr) run_to_nibbles(w, h[k] & 15u, wd[k], nib[k]);
+        else nib[k][0] = nib[k][1] = nib[k][2] = nib[k][3] = 0u;
       }
     }
     return true;
@@ -199,7 +240,7 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
   constexpr int NRL = Dec::NRL;
   constexpr int REC = max_record_bytes(false, B, 4);
   constexpr int NCH = (REC + 1023) / 1024;
-  constexpr int ROWW = kD + 4;                     // plane row: 128 words + 16 B pad
+  constexpr int ROWW = kD + 8;                     // plane row: 128 words + 32 B pad
   constexpr int REDB = GT * 64 * 9 * 4;            // channel-group reduction
   constexpr int BUF = (REC + 16) > REDB ? (REC + 16) : REDB;
   __shared__ __attribute__((aligned(16))) uint8_t rec[BUF];
@@ -297,7 +338,9 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
         const int row = h * 8 + g8;
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          const int c0 = cg * 16 + i4 * 4;
+          // rotate the quad order per channel group: with the 136-word row
+          // pitch, 16 lanes of a 16-byte read then cover all 64 banks once
+          const int c0 = cg * 16 + ((i4 + cg) & 3) * 4;
           const u32x4 nw = *reinterpret_cast<const u32x4*>(&plane[row * ROWW + c0]);
           const uint32_t words[4] = {nw.x, nw.y, nw.z, nw.w};
           float qq[GT][4];
