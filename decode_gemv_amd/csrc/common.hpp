@@ -72,6 +72,16 @@ __device__ __forceinline__ uint32_t bits_at(uint32_t w0, uint32_t w1, uint32_t w
   else return __builtin_amdgcn_alignbit(hi, lo, sh);
 }
 
+// m (0..15) in all eight nibbles of a word: one shift-or and a byte broadcast
+// (written as v_perm_b32 so that it is not turned into a quarter-rate
+// 32-bit multiply; register-only ALU instruction, no memory access).
+__device__ __forceinline__ uint32_t nibble_splat(uint32_t m) {
+  const uint32_t b = (m & 15u) | ((m & 15u) << 4);
+  uint32_t r;
+  asm("v_perm_b32 %0, %1, %1, %2" : "=v"(r) : "v"(b), "v"(0u));
+  return r;
+}
+
 // Decode one run (R = 32 slots) stored at width w with minimum m into four
 // nibble words: word k holds q = m + u of slots 8k .. 8k+7 (nibble i = slot
 // 8k+i).  Valid for m + 2^w - 1 <= 15.  `wd` holds the run's first four
@@ -100,7 +110,7 @@ __device__ __forceinline__ void run_to_nibbles(int w, uint32_t m, const uint32_t
       break;
     default: out[0] = out[1] = out[2] = out[3] = 0u; break;
   }
-  const uint32_t mm = m * 0x11111111u;   // m in every nibble; no carries
+  const uint32_t mm = nibble_splat(m);   // m in every nibble; no carries
   out[0] += mm; out[1] += mm; out[2] += mm; out[3] += mm;
 }
 
@@ -120,16 +130,6 @@ __device__ __forceinline__ void full_to_nibbles(const uint32_t wd[4], uint32_t o
     out[2] = spread2to4(wd[1]);
     out[3] = spread2to4(wd[1] >> 16);
   }
-}
-
-// m (0..15) in all eight nibbles of a word: one shift-or and a byte broadcast
-// (written as v_perm_b32 so that it is not turned into a quarter-rate
-// 32-bit multiply; register-only ALU instruction, no memory access).
-__device__ __forceinline__ uint32_t nibble_splat(uint32_t m) {
-  const uint32_t b = (m & 15u) | ((m & 15u) << 4);
-  uint32_t r;
-  asm("v_perm_b32 %0, %1, %1, %2" : "=v"(r) : "v"(b), "v"(0u));
-  return r;
 }
 
 // Four header bytes (w << 4 | m) of runs that are all at the full width BITS
@@ -177,6 +177,25 @@ __device__ __forceinline__ float wave_incl_scan_f(float v) {
   v += dpp_f<0x143, 0xC>(v);
   return v;
 }
+// Wave-wide maximum of non-negative floats (returned wave-uniform).
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  v = fmaxf(v, dpp_f<0x111>(v));
+  v = fmaxf(v, dpp_f<0x112>(v));
+  v = fmaxf(v, dpp_f<0x114>(v));
+  v = fmaxf(v, dpp_f<0x118>(v));
+  v = fmaxf(v, dpp_f<0x142, 0xA>(v));
+  v = fmaxf(v, dpp_f<0x143, 0xC>(v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+// Bitwise OR over each group of 8 consecutive lanes (result in all 8 lanes):
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], then row_half_mirror.
+__device__ __forceinline__ uint32_t or8(uint32_t v) {
+  v |= (uint32_t)dpp_i<0xB1>((int)v);
+  v |= (uint32_t)dpp_i<0x4E>((int)v);
+  v |= (uint32_t)dpp_i<0x141>((int)v);
+  return v;
+}
+
 // Wave-wide sums, returned as wave-uniform values.
 __device__ __forceinline__ float wave_sum(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_incl_scan_f(v)), 63));

@@ -142,93 +142,68 @@ struct BlockDecoder {
   // Decode the lane's runs of the staged record into container words
   // nib[k][0..3] (run l + 64k).  Returns false if the record is inconsistent
   // (a width above BITS, or widths that do not add up to the record size).
+  // One code path for every block: offsets start from the full-width layout;
+  // a block holding narrower runs (or a partial block) corrects them with
+  // the width deficit of earlier runs, and its narrow runs are re-decoded at
+  // the end.  Both corrections are uniform branches taken by few blocks.
   __device__ __forceinline__ static bool decode(const uint8_t* rec, uint32_t size, int nr, int lane,
                                                 uint32_t nib[NRL][4]) {
-    if (nr == NR) {
-      constexpr int pay = payload_offset(IS_V, B, NR);
-      uint32_t h[NRL];
+    const int pay = payload_offset(IS_V, B, nr);
+    const int nruns = nr * kD;
+    uint32_t h[NRL];
 #pragma unroll
-      for (int k = 0; k < NRL; ++k) h[k] = rec[HDR + lane + 64 * k];
+    for (int k = 0; k < NRL; ++k) h[k] = (k >> 1) < nr ? rec[HDR + lane + 64 * k] : 0u;
+    bool all_full = false;
+    if (nr == NR) {
       bool ok = true;
 #pragma unroll
       for (int i = 0; i < NR / 2; ++i)                // header dwords lane + 64i
         ok &= hdr4_full<BITS>(reinterpret_cast<const uint32_t*>(rec + HDR)[lane + 64 * i]);
-      if (__ballot(!ok) == 0 && (uint32_t)(pay + 4 * NR * kD * BITS) == size) {
-        // every run at full width: offsets are implicit, loads aligned
-#pragma unroll
-        for (int k = 0; k < NRL; ++k) {
-          const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + pay) + (lane + 64 * k) * BITS;
-          uint32_t wd[4] = {0u, 0u, 0u, 0u};
-          if constexpr (BITS == 4) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(p);
-            wd[0] = v.x; wd[1] = v.y; wd[2] = v.z; wd[3] = v.w;
-          } else if constexpr (BITS == 2) {
-            const uint2 v = *reinterpret_cast<const uint2*>(p);
-            wd[0] = v.x; wd[1] = v.y;
-          } else {
-            wd[0] = p[0]; wd[1] = p[1]; wd[2] = p[2];
-          }
-          full_to_nibbles<BITS>(wd, nib[k]);
-          const uint32_t mm = nibble_splat(h[k]);
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) nib[k][kk] += mm;
-        }
-        return true;
-      }
-      return decode_general(rec, size, NR, lane, h, nib);
+      all_full = __ballot(!ok) == 0;
     }
-    uint32_t h[NRL];
-#pragma unroll
-    for (int k = 0; k < NRL; ++k) h[k] = (k >> 1) < nr ? rec[HDR + lane + 64 * k] : 0u;
-    return decode_general(rec, size, nr, lane, h, nib);
-  }
-
-  // Some run is narrower (or the block is partial).  Offsets follow from the
-  // full-width layout minus the width deficit of every earlier run; only
-  // groups that hold a narrow run need a scan.  Every run is decoded as if it
-  // were full width, then the narrow ones are redone (rare, exec-masked).
-  __device__ __forceinline__ static bool decode_general(const uint8_t* rec, uint32_t size, int nr, int lane,
-                                                        const uint32_t h[NRL], uint32_t nib[NRL][4]) {
-    const int pay = payload_offset(IS_V, B, nr);
-    const int nruns = nr * kD;
-    bool bad = false;
     uint32_t off[NRL];
-    uint32_t running = 0;                              // deficit of earlier groups
 #pragma unroll
-    for (int k = 0; k < NRL; ++k) {
-      const int w = (int)(h[k] >> 4);
-      bad |= w > BITS;
-      const int d = (lane + 64 * k) < nruns ? BITS - w : 0;
-      const uint32_t base = (uint32_t)((lane + 64 * k) * BITS) - running;
-      if (__ballot(d != 0) == 0) {
-        off[k] = base;
-      } else {
-        const int incl = wave_incl_scan(d);
-        off[k] = base - (uint32_t)(incl - d);
-        running += (uint32_t)__builtin_amdgcn_readlane(incl, 63);
+    for (int k = 0; k < NRL; ++k) off[k] = (uint32_t)((lane + 64 * k) * BITS);
+    uint32_t total = (uint32_t)(nruns * BITS);
+    bool bad = false;
+    if (!all_full) {
+      uint32_t running = 0;                            // deficit of earlier groups
+#pragma unroll
+      for (int k = 0; k < NRL; ++k) {
+        const int w = (int)(h[k] >> 4);
+        bad |= w > BITS;
+        const int d = (lane + 64 * k) < nruns ? BITS - w : 0;
+        off[k] -= running;
+        if (__ballot(d != 0) != 0) {
+          const int incl = wave_incl_scan(d);
+          off[k] -= (uint32_t)(incl - d);
+          running += (uint32_t)__builtin_amdgcn_readlane(incl, 63);
+        }
       }
+      total -= running;
     }
-    const uint32_t total = (uint32_t)(nruns * BITS) - running;
-    if (__ballot(bad) || (uint32_t)pad16(pay + 4 * (int)total) != size) return false;
+    const bool ok = __ballot(bad) == 0 && (uint32_t)pad16(pay + 4 * (int)total) == size;
     uint32_t wd[NRL][4];
 #pragma unroll
     for (int k = 0; k < NRL; ++k) {
-      const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + pay) + off[k];
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + pay) + (ok ? off[k] : 0u);
       wd[k][0] = p[0]; wd[k][1] = p[1]; wd[k][2] = p[2]; wd[k][3] = p[3];
       full_to_nibbles<BITS>(wd[k], nib[k]);
       const uint32_t mm = nibble_splat(h[k]);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) nib[k][kk] += mm;
     }
+    if (!all_full && ok) {
 #pragma unroll
-    for (int k = 0; k < NRL; ++k) {
-      const int w = (int)(h[k] >> 4);
-      if (w != BITS) {
-        if ((k >> 1) < nr) run_to_nibbles(w, h[k] & 15u, wd[k], nib[k]);
-        else nib[k][0] = nib[k][1] = nib[k][2] = nib[k][3] = 0u;
+      for (int k = 0; k < NRL; ++k) {
+        const int w = (int)(h[k] >> 4);
+        if (w != BITS) {
+          if ((k >> 1) < nr) run_to_nibbles(w, h[k] & 15u, wd[k], nib[k]);
+          else nib[k][0] = nib[k][1] = nib[k][2] = nib[k][3] = 0u;
+        }
       }
     }
-    return true;
+    return ok;
   }
 };
 
@@ -382,16 +357,30 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
 
 // ---------------------------------------------------------------------------
 // V side: split-T partial sums into ws, then a fixed-order reduction.
+//
+//   out[c] = sum_t p_t zero_t + sum_t p'_t q[t][c],   p'_t = p_t scale_t >= 0
+//
+// The second sum runs over the slots of a run, which is the axis a container
+// word packs (8 slots of one channel).  Per block and query, p' is written as
+// a 20-bit fixed-point integer relative to the block's largest p'
+// (P_t = round(p'_t 2^E), P_t < 2^20) and split into five 4-bit digits; the
+// digit words of 8 slots are built once per block with DPP and shared through
+// LDS.  One v_dot8_u32_u4 then multiplies a container word by a digit word:
+// 5 instructions per 8 elements, with exact integer sums that are scaled by
+// 2^-E once per block and channel.  Per element the weight error is at most
+// 2^-21 of the block's largest weight.
 template <int B, int BITS, int GT>
 __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
   using Dec = BlockDecoder<B, BITS, true>;
   constexpr int NR = Dec::NR;
   constexpr int NRL = Dec::NRL;                    // run l + 64k: r = k/2, channel l + 64(k&1)
   constexpr int NH = B / 64;                       // slots per lane
+  constexpr int NG = B / 8;                        // 8-slot groups per block
+  constexpr int ND = 5;                            // 4-bit digits of p'
   constexpr int REC = max_record_bytes(true, B, 4);
   constexpr int NCH = (REC + 1023) / 1024;
   __shared__ __attribute__((aligned(16))) uint8_t rec[REC + 16];
-  __shared__ __attribute__((aligned(16))) float pp[GT * B];
+  __shared__ __attribute__((aligned(16))) uint32_t dig[GT][ND][NG];
 
   const int lane = threadIdx.x;
   const int s = blockIdx.x / a.splits;
@@ -401,12 +390,12 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
   const int nj = max(0, j1 - j0);
   const uint8_t* arena = a.arena + (uint64_t)s * a.arena_stride;
   const uint32_t* offs = a.off + (int64_t)s * a.off_stride;
-  const float unit_inv = 1.0f / fp8_unit();
   const uint32_t my_off = lane <= nj ? offs[j0 + lane] : 0u;
   const uint32_t my_off2 = lane + 64 <= nj ? offs[j0 + 64 + lane] : 0u;
   auto off_of = [&](int i) -> uint32_t {
     return i < 64 ? readlane_u32(my_off, i) : readlane_u32(my_off2, i - 64);
   };
+  const int nib_shift = 4 * (lane & 7);
 
   for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
     float acc[GT][2];
@@ -454,17 +443,38 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
         load_p(j + 1, pnext);
       }
       __syncthreads();
-      // p' = p * scale per slot (to LDS); sum p * zero (per lane)
+      // p' = p * scale per slot, sum p * zero, and the digit words of p'
+      int E[GT];
+      bool live[GT];
       {
         const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec);
+        float pp[GT][NH];
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
           const int sl = h * 64 + lane;
-          const float scl = f16_bits_to_float(sc[sl]) * unit_inv, zer = f16_bits_to_float(sc[B + sl]);
+          const float scl = f16_bits_to_float(sc[sl]), zer = f16_bits_to_float(sc[B + sl]);
 #pragma unroll
           for (int g = 0; g < GT; ++g) {
-            pp[g * B + sl] = pcur[g][h] * scl;
+            pp[g][h] = pcur[g][h] * scl;
             pz[g] = fmaf(pcur[g][h], zer, pz[g]);
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+          float mx = pp[g][0];
+#pragma unroll
+          for (int h = 1; h < NH; ++h) mx = fmaxf(mx, pp[g][h]);
+          const float M = wave_max_nonneg(mx);
+          live[g] = M > 0.f;
+          E[g] = live[g] ? 19 - ilogbf(M) : 0;          // M * 2^E in [2^19, 2^20)
+#pragma unroll
+          for (int h = 0; h < NH; ++h) {
+            const uint32_t P = min((uint32_t)(ldexpf(pp[g][h], E[g]) + 0.5f), 0xFFFFFu);
+#pragma unroll
+            for (int d = 0; d < ND; ++d) {
+              const uint32_t wv = or8(((P >> (4 * d)) & 15u) << nib_shift);
+              if ((lane & 7) == 0) dig[g][d][h * 8 + (lane >> 3)] = wv;
+            }
           }
         }
       }
@@ -476,27 +486,36 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
         continue;
       }
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        if (r >= nr) break;
+      for (int g = 0; g < GT; ++g) {
+        if (!live[g]) continue;
+        uint32_t sd[2][ND];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          float pr[GT][8];
+        for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
-          for (int g = 0; g < GT; ++g) {
-            const float4 t0 = *reinterpret_cast<const float4*>(&pp[g * B + r * 32 + kk * 8]);
-            const float4 t1 = *reinterpret_cast<const float4*>(&pp[g * B + r * 32 + kk * 8 + 4]);
-            pr[g][0] = t0.x; pr[g][1] = t0.y; pr[g][2] = t0.z; pr[g][3] = t0.w;
-            pr[g][4] = t1.x; pr[g][5] = t1.y; pr[g][6] = t1.z; pr[g][7] = t1.w;
+          for (int d = 0; d < ND; ++d) sd[ch][d] = 0u;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          if (r >= nr) break;
+          uint32_t W[ND][4];
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            const u32x4 t = *reinterpret_cast<const u32x4*>(&dig[g][d][4 * r]);
+            W[d][0] = t.x; W[d][1] = t.y; W[d][2] = t.z; W[d][3] = t.w;
           }
 #pragma unroll
-          for (int ch = 0; ch < 2; ++ch) {
-            float f[8];
-            nibbles_to_f32(nib[2 * r + ch][kk], f);
+          for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
-            for (int g = 0; g < GT; ++g)
+            for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-              for (int i = 0; i < 8; ++i) acc[g][ch] = fmaf(pr[g][i], f[i], acc[g][ch]);
-          }
+              for (int d = 0; d < ND; ++d)
+                sd[ch][d] = __builtin_amdgcn_udot8(nib[2 * r + ch][kk], W[d][kk], sd[ch][d], false);
+        }
+        const float unit = ldexpf(1.0f, -E[g]);
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+          // each digit sum is <= NR*32*15*15 < 2^15, so the total stays below 2^32
+          uint32_t x = sd[ch][0] + (sd[ch][1] << 4) + (sd[ch][2] << 8) + (sd[ch][3] << 12) + (sd[ch][4] << 16);
+          acc[g][ch] = fmaf((float)x, unit, acc[g][ch]);
         }
       }
     }

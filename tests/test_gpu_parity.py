@@ -196,3 +196,35 @@ def test_corrupt_header_is_reported_not_used(torch_dev):
     s = sc.cpu().numpy()
     assert np.all(np.isnan(s[0, 0, :64])) and np.all(np.isfinite(s[0, 0, 64:]))
     assert c.check() == 0               # the latch was cleared
+
+
+@pytest.mark.parametrize("law", ["uniform", "one-hot", "peaked", "sparse-blocks", "wide-range"])
+def test_pv_weight_laws(torch_dev, law):
+    """V GEMV precision across weight distributions (fp64 oracle, rel-L2 <= 1e-4)."""
+    torch, dev = torch_dev
+    S, T = 2, 1000
+    K, V = make_kv("gauss", S, T, 64)
+    refs = oracle_streams(K, V, 4, 64)
+    c = gpu_cache(torch, dev, K, V, 4, 64, True)
+    rng = np.random.default_rng(11)
+    if law == "uniform":
+        p = np.full((S, 1, T), 1.0 / T)
+    elif law == "one-hot":
+        p = np.zeros((S, 1, T))
+        p[:, 0, 517] = 1.0
+    elif law == "peaked":
+        z = rng.standard_normal((S, 1, T)) * 6
+        p = np.exp(z - z.max(-1, keepdims=True))
+        p /= p.sum(-1, keepdims=True)
+    elif law == "sparse-blocks":        # whole blocks of zero weight
+        p = rng.random((S, 1, T))
+        p[:, :, 64:640] = 0.0
+        p /= p.sum(-1, keepdims=True)
+    else:                               # weights spanning ~30 orders of magnitude
+        p = np.exp(rng.uniform(-70, 0, (S, 1, T)))
+    p = p.astype(np.float32)
+    say("pv law", law)
+    out = c.pv(torch.from_numpy(p).to(dev)).cpu().numpy()
+    assert c.check() == 0
+    ref = np.stack([attention.pv(p[s].astype(np.float64), ostream.decode_stream(refs[s])[1]) for s in range(S)])
+    assert rel_l2(out, ref) <= TOL, (rel_l2(out, ref), worst_row_rel(out, ref))
