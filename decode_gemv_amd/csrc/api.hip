@@ -59,8 +59,12 @@ int gemv_blocks_per_wg(int64_t n_streams, int nb) {
     env = s ? atoi(s) : 0;
   }
   if (env > 0) return env > 64 ? 64 : (env < 4 ? 4 : env);
+  // about two rounds of one-wave workgroups over the chip's resident slots
+  // (16 per CU), each workgroup taking an even number of blocks: the GEMVs
+  // process blocks in pairs
   int64_t total = n_streams * (int64_t)nb;
-  int64_t j = (total + 8191) / 8192;
+  int64_t j = (total + 7679) / 7680;
+  j += j & 1;
   if (j < 4) j = 4;
   if (j > 64) j = 64;
   return (int)j;

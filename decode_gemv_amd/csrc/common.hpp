@@ -178,14 +178,16 @@ __device__ __forceinline__ float wave_incl_scan_f(float v) {
   return v;
 }
 // Wave-wide maximum of non-negative floats (returned wave-uniform).
-__device__ __forceinline__ float wave_max_nonneg(float v) {
-  v = fmaxf(v, dpp_f<0x111>(v));
-  v = fmaxf(v, dpp_f<0x112>(v));
-  v = fmaxf(v, dpp_f<0x114>(v));
-  v = fmaxf(v, dpp_f<0x118>(v));
-  v = fmaxf(v, dpp_f<0x142, 0xA>(v));
-  v = fmaxf(v, dpp_f<0x143, 0xC>(v));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  // for x >= 0 the fp32 order is the order of the bit patterns as signed ints
+  int v = __float_as_int(x);
+  v = max(v, dpp_i<0x111>(v));
+  v = max(v, dpp_i<0x112>(v));
+  v = max(v, dpp_i<0x114>(v));
+  v = max(v, dpp_i<0x118>(v));
+  v = max(v, dpp_i<0x142, 0xA>(v));
+  v = max(v, dpp_i<0x143, 0xC>(v));
+  return __int_as_float(__builtin_amdgcn_readlane(v, 63));
 }
 // Bitwise OR over each group of 8 consecutive lanes (result in all 8 lanes):
 // quad_perm [1,0,3,2], quad_perm [2,3,0,1], then row_half_mirror.

@@ -52,16 +52,24 @@ __device__ __forceinline__ bool record_ok(uint32_t o, uint32_t size, uint64_t st
   return size >= 16u && size <= (uint32_t)rec_max && (uint64_t)o + size <= stride;
 }
 
+// Raw buffer resource over [base, base + bytes): the hardware range check
+// turns every load at or past `bytes` into zero without a memory access, so
+// loads can be issued unconditionally (bytes = 0 for "nothing to load") and
+// the compiler can count outstanding loads exactly instead of draining them.
+constexpr int kBufferFormat = 0x00020000;          // 32-bit data format
+constexpr int kNonTemporal = 2;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFormat);
+}
+
 // Record staging: chunks of 16 bytes, lane l takes chunks l, l+64, ...
+// Chunks past `bytes` (a multiple of 16) read as zero and are not stored.
 template <int NCH>
 __device__ __forceinline__ void load_record(const uint8_t* g, uint32_t bytes, int lane, u32x4 pre[NCH]) {
-  const u32x4* src = reinterpret_cast<const u32x4*>(g);
-  const int nch = (int)(bytes >> 4);
+  const __amdgpu_buffer_rsrc_t r = buffer_rsrc(g, bytes);
 #pragma unroll
-  for (int k = 0; k < NCH; ++k) {
-    const int c = lane + 64 * k;
-    if (c < nch) pre[k] = __builtin_nontemporal_load(src + c);
-  }
+  for (int k = 0; k < NCH; ++k)
+    pre[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (lane + 64 * k), 0, kNonTemporal));
 }
 template <int NCH>
 __device__ __forceinline__ void store_record(uint8_t* lds, uint32_t bytes, int lane, const u32x4 pre[NCH]) {
@@ -253,33 +261,39 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
       qau[g] = qa[g] * unit_inv;
       qbu[g] = qb[g] * unit_inv;
     }
-    u32x4 pre[NCH];
-    {
-      const uint32_t o0 = off_of(0), s0 = off_of(1) - o0;
-      if (record_ok(o0, s0, a.arena_stride, REC)) load_record<NCH>(arena + o0, s0, lane, pre);
-    }
-    for (int jj = 0; jj < nj; ++jj) {
+    // two records in flight: block jj + 2 is requested while block jj is
+    // processed, alternating between the register sets pa and pb
+    auto request = [&](int jj, u32x4 (&pre)[NCH]) __attribute__((always_inline)) {
+      const bool in = jj < nj;
+      const uint32_t o = in ? off_of(jj) : 0u, size = in ? off_of(jj + 1) - o : 0u;
+      load_record<NCH>(arena + o, record_ok(o, size, a.arena_stride, REC) ? size : 0u, lane, pre);
+    };
+    // The loop body has no exits: a missing block (jj >= nj) or a corrupt
+    // record is staged as zero bytes and writes nothing. An exit inside the
+    // body would give the wait-count analysis a path on which only one
+    // register set has loads in flight, and it would then drain both.
+    bool corrupt = false;
+    auto process = [&](int jj, u32x4 (&pre)[NCH]) __attribute__((always_inline)) {
+      const bool in = jj < nj;
       const int j = j0 + jj;
-      const uint32_t o = off_of(jj), size = off_of(jj + 1) - o;
-      const int n = (int)imin64(B, a.n_tokens - (int64_t)j * B);
+      const uint32_t o = in ? off_of(jj) : 0u, size0 = in ? off_of(jj + 1) - o : 0u;
+      const bool rok = record_ok(o, size0, a.arena_stride, REC);
+      corrupt |= in && !rok;
+      const uint32_t size = rok ? size0 : 0u;
+      const int n = in ? (int)imin64(B, a.n_tokens - (int64_t)j * B) : 0;
       const int nr = (n + kR - 1) / kR;
       __syncthreads();
-      if (!record_ok(o, size, a.arena_stride, REC)) {
-        if (lane == 0) latch(a.status, PACKKV_ECORRUPT);
-        break;
-      }
       store_record<NCH>(rec, size, lane, pre);
-      if (jj + 1 < nj) {
-        const uint32_t o1 = off_of(jj + 1), s1 = off_of(jj + 2) - o1;
-        if (record_ok(o1, s1, a.arena_stride, REC)) load_record<NCH>(arena + o1, s1, lane, pre);
-      }
+      request(jj + 2, pre);
+      // keep each request's loads together and in order, so that the wait
+      // for one record never has to drain the other record's loads
+      __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
 
       uint32_t nib[NRL][4];
-      if (!Dec::decode(rec, size, nr, lane, nib)) {
-        if (lane == 0) latch(a.status, PACKKV_ECORRUPT);
-        continue;
-      }
+      // a corrupt record is computed on but its scores are not written
+      const bool ok = Dec::decode(rec, size, nr, lane, nib) && rok;
+      corrupt |= rok && !ok;
 #pragma unroll
       for (int k = 0; k < NRL; ++k) {
         const int r = k >> 1, c = lane + 64 * (k & 1);
@@ -341,17 +355,31 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) red[(g * 64 + g8 * 8 + i) * 9 + cg] = acc[g][i];
         __syncthreads();
-        const int64_t t = (int64_t)j * B + h * 64 + lane;
+        // range-checked stores: slots past n, absent queries and corrupt
+        // records write nothing
+        const uint32_t valid = ok ? (uint32_t)max(0, min(64, n - h * 64)) : 0u;
 #pragma unroll
         for (int g = 0; g < GT; ++g) {
           float sum = beta[g];
 #pragma unroll
           for (int u = 0; u < 8; ++u) sum += red[(g * 64 + lane) * 9 + u];
-          if (gq0 + g < a.G && h * 64 + lane < n)
-            a.scores[((int64_t)s * a.G + gq0 + g) * a.ld + t] = sum;
+          const bool gok = gq0 + g < a.G;
+          float* row0 = a.scores + ((int64_t)s * a.G + (gok ? gq0 + g : 0)) * a.ld + (int64_t)j * B + h * 64;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), buffer_rsrc(row0, gok ? 4u * valid : 0u),
+                                                4 * lane, 0, 0);
         }
       }
+    };
+    u32x4 pa[NCH], pb[NCH];
+    request(0, pa);
+    __builtin_amdgcn_sched_barrier(0);
+    request(1, pb);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int jj = 0; jj < nj; jj += 2) {
+      process(jj, pa);
+      process(jj + 1, pb);
     }
+    if (corrupt && lane == 0) latch(a.status, PACKKV_ECORRUPT);
   }
 }
 
@@ -402,24 +430,27 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
     float pz[GT];
 #pragma unroll
     for (int g = 0; g < GT; ++g) { acc[g][0] = acc[g][1] = 0.f; pz[g] = 0.f; }
-    // weights of the lane's slots (slot h*64 + lane) for block j
-    auto load_p = [&](int j, float pv[GT][NH]) {
-      const int n = (int)imin64(B, a.n_tokens - (int64_t)j * B);
+    // weights of the lane's slots (slot h*64 + lane) for block j; zero past
+    // the valid slots, for absent queries, and when `valid` is false
+    auto load_p = [&](int j, bool valid, float pv[GT][NH]) {
+      const int64_t left = a.n_tokens - (int64_t)j * B;
+      const uint32_t nbytes = valid && left > 0 ? 4u * (uint32_t)imin64(B, left) : 0u;
 #pragma unroll
-      for (int g = 0; g < GT; ++g)
+      for (int g = 0; g < GT; ++g) {
+        const bool gok = gq0 + g < a.G;
+        const float* src = a.p + ((int64_t)s * a.G + (gok ? gq0 + g : 0)) * a.ld + (int64_t)(valid ? j : 0) * B;
+        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(src, gok ? nbytes : 0u);
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          const int sl = h * 64 + lane;
-          pv[g][h] = (sl < n && gq0 + g < a.G)
-                         ? a.p[((int64_t)s * a.G + gq0 + g) * a.ld + (int64_t)j * B + sl] : 0.f;
-        }
+        for (int h = 0; h < NH; ++h)
+          pv[g][h] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 4 * (h * 64 + lane), 0, 0));
+      }
     };
     u32x4 pre[NCH];
     float pnext[GT][NH];
-    if (nj > 0) {
-      const uint32_t o0 = off_of(0), s0 = off_of(1) - o0;
-      if (record_ok(o0, s0, a.arena_stride, REC)) load_record<NCH>(arena + o0, s0, lane, pre);
-      load_p(j0, pnext);
+    {
+      const uint32_t o0 = nj > 0 ? off_of(0) : 0u, s0 = nj > 0 ? off_of(1) - o0 : 0u;
+      load_record<NCH>(arena + o0, record_ok(o0, s0, a.arena_stride, REC) ? s0 : 0u, lane, pre);
+      load_p(j0, nj > 0, pnext);
     }
     for (int jj = 0; jj < nj; ++jj) {
       const int j = j0 + jj;
@@ -437,10 +468,11 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
       for (int g = 0; g < GT; ++g)
 #pragma unroll
         for (int h = 0; h < NH; ++h) pcur[g][h] = pnext[g][h];
-      if (jj + 1 < nj) {
-        const uint32_t o1 = off_of(jj + 1), s1 = off_of(jj + 2) - o1;
-        if (record_ok(o1, s1, a.arena_stride, REC)) load_record<NCH>(arena + o1, s1, lane, pre);
-        load_p(j + 1, pnext);
+      {
+        const bool more = jj + 1 < nj;
+        const uint32_t o1 = more ? off_of(jj + 1) : 0u, s1 = more ? off_of(jj + 2) - o1 : 0u;
+        load_record<NCH>(arena + o1, record_ok(o1, s1, a.arena_stride, REC) ? s1 : 0u, lane, pre);
+        load_p(j + 1, more, pnext);
       }
       __syncthreads();
       // p' = p * scale per slot, sum p * zero, and the digit words of p'
