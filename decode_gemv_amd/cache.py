@@ -54,7 +54,7 @@ class PackedKVCache:
         self._c = _lib.CacheT(self.cfg, n_streams, max_tokens, 0, sz.arena_stride,
                               _ptr(self.k_arena), _ptr(self.v_arena), _ptr(self.k_off), _ptr(self.v_off),
                               _ptr(self.perm), _ptr(self.tail_k), _ptr(self.tail_v), _ptr(self.status))
-        self._ws: Optional[torch.Tensor] = None
+        self._ws: dict = {}
 
     # ------------------------------------------------------------------ state
     @property
@@ -112,10 +112,15 @@ class PackedKVCache:
         return scores
 
     def workspace(self, group: int) -> torch.Tensor:
+        """The V GEMV workspace for `group` queries per stream, zero-filled when
+        first made (its per-stream counters must start at zero; each call
+        leaves them at zero), then reused."""
         need = int(_lib.load().packkv_pv_workspace_bytes(ctypes.byref(self._c), group))
-        if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.empty(max(need, 16), dtype=torch.uint8, device=self.k_arena.device)
-        return self._ws
+        ws = self._ws.get(group)
+        if ws is None or ws.numel() < need:
+            ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=self.k_arena.device)
+            self._ws[group] = ws
+        return ws
 
     def pv(self, p: torch.Tensor, out: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -132,11 +132,17 @@ uint64_t packkv_arena_stride_bytes(const packkv_config_t* cfg, int64_t max_token
   return stride_bytes(cfg, max_tokens);
 }
 
-uint64_t packkv_pv_workspace_bytes(const packkv_cache_t* c, int32_t group) {
-  if (check_cache(c) || group < 1) return 0;
+// V workspace: fp32 partial sums [S][G][splits][D] for the largest split
+// count the cache can need, then one u32 arrival counter per stream.
+static uint64_t pv_partial_bytes(const packkv_cache_t* c, int32_t group) {
   const int64_t mb = max_blocks_of(&c->cfg, c->max_tokens);
   const int64_t splits = (mb + 3) / 4;     // blocks per workgroup is at least 4
   return (uint64_t)c->n_streams * (uint64_t)group * (uint64_t)splits * kD * sizeof(float);
+}
+
+uint64_t packkv_pv_workspace_bytes(const packkv_cache_t* c, int32_t group) {
+  if (check_cache(c) || group < 1) return 0;
+  return pv_partial_bytes(c, group) + (((uint64_t)c->n_streams * 4u + 255u) & ~(uint64_t)255u);
 }
 
 int packkv_compress_block(packkv_cache_t* c, const void* k_f16, const void* v_f16, int64_t n_tokens,
@@ -232,9 +238,10 @@ int packkv_pv_gemv(const packkv_cache_t* c, const float* p, int64_t ld, int32_t 
   a.p = p;
   a.ld = ld;
   a.ws = (float*)workspace;
-  const uint64_t need = (uint64_t)c->n_streams * group * a.splits * kD * sizeof(float);
-  if (ws_bytes < need) return PACKKV_EINVAL;
-  return hip_status(launch_pv(a, c->cfg.block_tokens, c->n_streams, out, (hipStream_t)stream));
+  a.tickets = (uint32_t*)((uint8_t*)workspace + pv_partial_bytes(c, group));
+  a.out = out;
+  if (ws_bytes < packkv_pv_workspace_bytes(c, group)) return PACKKV_EINVAL;
+  return hip_status(launch_pv(a, c->cfg.block_tokens, c->n_streams, (hipStream_t)stream));
 }
 
 int packkv_decompress(const packkv_cache_t* c, int32_t which, int32_t mode, void* out, void* stream) {

@@ -414,8 +414,7 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
   const int s = blockIdx.x / a.splits;
   const int split = blockIdx.x % a.splits;
   const int j0 = split * a.blocks_per_wg;
-  const int j1 = min(a.nb, j0 + a.blocks_per_wg);
-  const int nj = max(0, j1 - j0);
+  const int nj = max(0, min(a.nb, j0 + a.blocks_per_wg) - j0);
   const uint8_t* arena = a.arena + (uint64_t)s * a.arena_stride;
   const uint32_t* offs = a.off + (int64_t)s * a.off_stride;
   const uint32_t my_off = lane <= nj ? offs[j0 + lane] : 0u;
@@ -424,6 +423,7 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
     return i < 64 ? readlane_u32(my_off, i) : readlane_u32(my_off2, i - 64);
   };
   const int nib_shift = 4 * (lane & 7);
+  bool corrupt = false;
 
   for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
     float acc[GT][2];
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
     for (int g = 0; g < GT; ++g) { acc[g][0] = acc[g][1] = 0.f; pz[g] = 0.f; }
     // weights of the lane's slots (slot h*64 + lane) for block j; zero past
     // the valid slots, for absent queries, and when `valid` is false
-    auto load_p = [&](int j, bool valid, float pv[GT][NH]) {
+    auto load_p = [&](int j, bool valid, float (&pv)[GT][NH]) __attribute__((always_inline)) {
       const int64_t left = a.n_tokens - (int64_t)j * B;
       const uint32_t nbytes = valid && left > 0 ? 4u * (uint32_t)imin64(B, left) : 0u;
 #pragma unroll
@@ -445,42 +445,44 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
           pv[g][h] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 4 * (h * 64 + lane), 0, 0));
       }
     };
-    u32x4 pre[NCH];
-    float pnext[GT][NH];
-    {
-      const uint32_t o0 = nj > 0 ? off_of(0) : 0u, s0 = nj > 0 ? off_of(1) - o0 : 0u;
-      load_record<NCH>(arena + o0, record_ok(o0, s0, a.arena_stride, REC) ? s0 : 0u, lane, pre);
-      load_p(j0, nj > 0, pnext);
-    }
-    for (int jj = 0; jj < nj; ++jj) {
+    // two blocks in flight (record and weights), alternating register sets;
+    // a missing block (jj >= nj) is requested as zero bytes
+    auto request = [&](int jj, u32x4 (&pre)[NCH], float (&pv)[GT][NH]) __attribute__((always_inline)) {
+      const bool in = jj < nj;
+      const uint32_t o = in ? off_of(jj) : 0u, size = in ? off_of(jj + 1) - o : 0u;
+      load_record<NCH>(arena + o, record_ok(o, size, a.arena_stride, REC) ? size : 0u, lane, pre);
+      load_p(j0 + jj, in, pv);
+    };
+    // The loop body has no exits (see the K GEMV): a missing or corrupt
+    // block contributes nothing.
+    auto process = [&](int jj, u32x4 (&pre)[NCH], float (&pv)[GT][NH]) __attribute__((always_inline)) {
+      const bool in = jj < nj;
       const int j = j0 + jj;
-      const uint32_t o = off_of(jj), size = off_of(jj + 1) - o;
-      const int n = (int)imin64(B, a.n_tokens - (int64_t)j * B);
+      const uint32_t o = in ? off_of(jj) : 0u, size0 = in ? off_of(jj + 1) - o : 0u;
+      const bool rok = record_ok(o, size0, a.arena_stride, REC);
+      corrupt |= in && !rok;
+      const uint32_t size = rok ? size0 : 0u;
+      const int n = in ? (int)imin64(B, a.n_tokens - (int64_t)j * B) : 0;
       const int nr = (n + kR - 1) / kR;
       __syncthreads();
-      if (!record_ok(o, size, a.arena_stride, REC)) {
-        if (lane == 0) latch(a.status, PACKKV_ECORRUPT);
-        break;
-      }
       store_record<NCH>(rec, size, lane, pre);
       float pcur[GT][NH];
 #pragma unroll
       for (int g = 0; g < GT; ++g)
 #pragma unroll
-        for (int h = 0; h < NH; ++h) pcur[g][h] = pnext[g][h];
-      {
-        const bool more = jj + 1 < nj;
-        const uint32_t o1 = more ? off_of(jj + 1) : 0u, s1 = more ? off_of(jj + 2) - o1 : 0u;
-        load_record<NCH>(arena + o1, record_ok(o1, s1, a.arena_stride, REC) ? s1 : 0u, lane, pre);
-        load_p(j + 1, more, pnext);
-      }
+        for (int h = 0; h < NH; ++h) pcur[g][h] = pv[g][h];
+      request(jj + 2, pre, pv);
+      __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
       // p' = p * scale per slot, sum p * zero, and the digit words of p'
       int E[GT];
       bool live[GT];
+      float pzb[GT];
       {
         const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec);
         float pp[GT][NH];
+#pragma unroll
+        for (int g = 0; g < GT; ++g) pzb[g] = 0.f;
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
           const int sl = h * 64 + lane;
@@ -488,7 +490,7 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
 #pragma unroll
           for (int g = 0; g < GT; ++g) {
             pp[g][h] = pcur[g][h] * scl;
-            pz[g] = fmaf(pcur[g][h], zer, pz[g]);
+            pzb[g] = fmaf(pcur[g][h], zer, pzb[g]);
           }
         }
 #pragma unroll
@@ -511,15 +513,12 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
         }
       }
       uint32_t nib[NRL][4];
-      const bool ok = Dec::decode(rec, size, nr, lane, nib);
+      const bool ok = Dec::decode(rec, size, nr, lane, nib) && rok;
+      corrupt |= rok && !ok;
       __syncthreads();
-      if (!ok) {
-        if (lane == 0) latch(a.status, PACKKV_ECORRUPT);
-        continue;
-      }
 #pragma unroll
       for (int g = 0; g < GT; ++g) {
-        if (!live[g]) continue;
+        if (!ok || !live[g]) continue;
         uint32_t sd[2][ND];
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch)
@@ -550,6 +549,19 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
           acc[g][ch] = fmaf((float)x, unit, acc[g][ch]);
         }
       }
+#pragma unroll
+      for (int g = 0; g < GT; ++g)
+        if (ok) pz[g] += pzb[g];
+    };
+    u32x4 pa[NCH], pb[NCH];
+    float va[GT][NH], vb[GT][NH];
+    request(0, pa, va);
+    __builtin_amdgcn_sched_barrier(0);
+    request(1, pb, vb);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int jj = 0; jj < nj; jj += 2) {
+      process(jj, pa, va);
+      process(jj + 1, pb, vb);
     }
     // partial result of this split
 #pragma unroll
@@ -557,20 +569,39 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
       const float z = wave_sum(pz[g]);
       if (gq0 + g < a.G) {
         float* dst = a.ws + (((int64_t)s * a.G + gq0 + g) * a.splits + split) * kD;
-        dst[lane] = acc[g][0] + z;
-        dst[lane + 64] = acc[g][1] + z;
+        __hip_atomic_store(dst + lane, acc[g][0] + z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + lane + 64, acc[g][1] + z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
-}
+  if (corrupt && lane == 0) latch(a.status, PACKKV_ECORRUPT);
 
-__global__ __launch_bounds__(128) void k_pv_reduce(const float* ws, int splits, float* out) {
-  const int row = blockIdx.x;          // s * G + g
-  const int c = threadIdx.x;
-  const float* src = ws + (int64_t)row * splits * kD + c;
-  float sum = 0.f;
-  for (int i = 0; i < splits; ++i) sum += src[(int64_t)i * kD];
-  out[(int64_t)row * kD + c] = sum;
+  // Split-T reduction: the last workgroup of stream s to arrive sums the
+  // partials in split order (so the result does not depend on which one it
+  // is) and puts the stream's counter back to zero for the next call.
+  // The partials are written with device-coherent stores (they go past this
+  // XCD's L2) and the workgroup waits for them to complete before it takes
+  // its ticket; the last workgroup reads them back with device-coherent
+  // loads.  No cache write-back or invalidation is needed, which a release
+  // fence in every workgroup would cost.
+  __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0)
+  uint32_t ticket = 0;
+  if (lane == 0) ticket = __hip_atomic_fetch_add(&a.tickets[s], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  ticket = __builtin_amdgcn_readfirstlane(ticket);
+  if (ticket != (uint32_t)a.splits - 1u) return;
+  for (int g = 0; g < a.G; ++g) {
+    const float* src = a.ws + ((int64_t)s * a.G + g) * a.splits * kD;
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < a.splits; ++i) {
+      s0 += __hip_atomic_load(src + (int64_t)i * kD + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s1 += __hip_atomic_load(src + (int64_t)i * kD + lane + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    float* dst = a.out + ((int64_t)s * a.G + g) * kD;
+    dst[lane] = s0;
+    dst[lane + 64] = s1;
+  }
+  if (lane == 0) __hip_atomic_store(&a.tickets[s], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -759,7 +790,7 @@ hipError_t launch_qk(const GemvArgs& a, int B, int n_streams, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_pv(const GemvArgs& a, int B, int n_streams, float* out, hipStream_t st) {
+hipError_t launch_pv(const GemvArgs& a, int B, int n_streams, hipStream_t st) {
   const dim3 grid(n_streams * a.splits);
   switch (B * 8 + a.bits) {
     case 64 * 8 + 2: pv_launch<64, 2>(a, grid, st); break;
@@ -769,9 +800,6 @@ hipError_t launch_pv(const GemvArgs& a, int B, int n_streams, float* out, hipStr
     case 128 * 8 + 3: pv_launch<128, 3>(a, grid, st); break;
     default: pv_launch<128, 4>(a, grid, st); break;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_pv_reduce, dim3(n_streams * a.G), dim3(128), 0, st, a.ws, a.splits, out);
   return hipGetLastError();
 }
 

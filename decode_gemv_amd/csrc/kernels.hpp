@@ -43,6 +43,8 @@ struct GemvArgs {
   float* scores;         // K: [S][G][ld]
   int64_t ld;
   float* ws;             // V: partial sums [S][G][splits][D]
+  uint32_t* tickets;     // V: per-stream arrival counters, zero between calls
+  float* out;            // V: [S][G][D]
   int32_t* status;
 };
 
@@ -54,7 +56,7 @@ hipError_t launch_stage_tail(const uint16_t* k, const uint16_t* v, int64_t src_s
                              uint16_t* tk, uint16_t* tv, int B, int at, int cnt,
                              int n_streams, hipStream_t st);
 hipError_t launch_qk(const GemvArgs& a, int B, int n_streams, hipStream_t st);
-hipError_t launch_pv(const GemvArgs& a, int B, int n_streams, float* out, hipStream_t st);
+hipError_t launch_pv(const GemvArgs& a, int B, int n_streams, hipStream_t st);
 hipError_t launch_decompress(const GemvArgs& a, int B, bool is_v, int n_streams, const uint8_t* perm,
                              int64_t perm_stride, int mode, void* out, hipStream_t st);
 hipError_t launch_stats(const GemvArgs& a, int B, bool is_v, int n_streams, unsigned long long* out,

@@ -122,7 +122,8 @@ int packkv_cache_sizes(const packkv_config_t* cfg, int32_t n_streams,
  * an invalid cfg. */
 uint64_t packkv_arena_stride_bytes(const packkv_config_t* cfg, int64_t max_tokens);
 
-/* Bytes of workspace packkv_pv_gemv needs for `group` queries per stream. */
+/* Bytes of workspace packkv_pv_gemv needs for `group` queries per stream:
+ * fp32 split partial sums, then one 32-bit counter per stream. */
 uint64_t packkv_pv_workspace_bytes(const packkv_cache_t* cache, int32_t group);
 
 /*
@@ -169,8 +170,15 @@ int packkv_qk_gemv(const packkv_cache_t* cache, const void* q_f16, int32_t group
  *   out:       device fp32 [S][group][D]; out[s][g][c] =
  *              sum_t p[s][g][t] * V_hat[s][t][c].
  *   workspace: device memory of at least packkv_pv_workspace_bytes(cache,
- *              group) bytes (ws_bytes), holding the split partial sums.
- * Results are bitwise reproducible run to run.
+ *              group) bytes (ws_bytes), caller-owned.  It holds the split
+ *              partial sums and, at its end, one counter per stream that
+ *              the last-arriving workgroup of each stream uses to find that
+ *              it should do the final sum.  The counters must be zero when
+ *              a workspace is first used (allocate it zero-filled); every
+ *              call leaves them zero again.  Calls that share a workspace
+ *              must not run concurrently.
+ * The partial sums are added in split order, so results are bitwise
+ * reproducible run to run.  Single kernel launch.
  */
 int packkv_pv_gemv(const packkv_cache_t* cache, const float* p, int64_t ld, int32_t group,
                    float* out, void* workspace, uint64_t ws_bytes, void* stream);
