@@ -62,32 +62,34 @@ def generate(w: kvsynth.Workload, torch, dev):
     return K, V
 
 
-def cpu_baseline(w: kvsynth.Workload, n_streams: int) -> dict:
-    """The fp64 oracle's decode step on a sample of streams, single-threaded."""
+def cpu_baseline(w: kvsynth.Workload, n_streams: int, n_steps: int) -> dict:
+    """The fp64 oracle's decode steps on a sample of streams, single-threaded."""
     from threadpoolctl import threadpool_limits
     import oracle
     from oracle import stream as ostream, attention
     cfg = oracle.Config(bits=w.bits, block=w.block)
     with threadpool_limits(limits=1):
-        caches, qs, kv_new = [], [], []
+        caches = []
         for s in range(n_streams):
             k, v = kvsynth.stream_kv(w, s)
             caches.append(ostream.compress(k, v, cfg))          # prefill: not timed
-            qs.append(kvsynth.stream_q(w, s, step=0))
-            kv_new.append(kvsynth.append_kv(w, s, 0))
+        steps = [[(kvsynth.stream_q(w, s, step=i), kvsynth.append_kv(w, s, i)) for s in range(n_streams)]
+                 for i in range(n_steps)]
         nbytes = 0
         t0 = time.perf_counter()
-        for s in range(n_streams):
-            c = ostream.append(caches[s], *kv_new[s])           # tail re-encode
-            kh, vh, _, _ = ostream.decode_stream(c)               # unpack + fp64 dequant
-            p = attention.softmax(attention.qk(qs[s], kh), w.head_dim)
-            attention.pv(p, vh)
-            nbytes += len(c.arena("K")) + len(c.arena("V")) + 8 * (len(c.blocks) + 1)
+        for i in range(n_steps):
+            for s in range(n_streams):
+                q, kv_new = steps[i][s]
+                caches[s] = c = ostream.append(caches[s], *kv_new)   # tail re-encode
+                kh, vh, _, _ = ostream.decode_stream(c)                # unpack + fp64 dequant
+                p = attention.softmax(attention.qk(q, kh), w.head_dim)
+                attention.pv(p, vh)
+                nbytes += len(c.arena("K")) + len(c.arena("V")) + 2 * 4 * (len(c.blocks) + 1)
         dt = time.perf_counter() - t0
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_streams} of {w.streams} streams at the full {w.tokens} tokens, one decode "
-                      f"step each (tail re-encode, unpack, fp64 dequantise, K GEMV, softmax, V GEMV), "
-                      f"{dt:.2f} s; value = compressed bytes decoded per second"}
+            "sample": f"{n_streams} of {w.streams} streams at {w.tokens}+ tokens, {n_steps} decode steps each "
+                      f"(tail re-encode, unpack, fp64 dequantise, K GEMV, softmax, V GEMV), {dt:.1f} s of "
+                      f"single-threaded CPU time; value = compressed bytes (records + offsets) decoded per second"}
 
 
 def load_traffic(workload: str):
@@ -104,17 +106,133 @@ def load_traffic(workload: str):
     return e
 
 
+def summarize_profile(pdir: str, workload: str) -> None:
+    """Write profiles/<kernels>_<workload>.md and the workload's entry of
+    profiles/traffic.json from a profile directory holding a kernel-trace run
+    (kt/, whose stdout kt.log ends with this script's JSON line) and counter
+    passes p*/ (rocprofv3 --pmc, CSV output), among them one FETCH_SIZE and
+    one WRITE_SIZE pass over a run that ends with the 1 GiB device copy.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read
+    for that copy of known size (bytes moved / counter bytes), so `traffic`
+    is in the same bytes as the algorithmic figure."""
+    import csv
+    import glob
+    import re
+
+    def short(name):
+        name = name.replace("void ", "").replace("packkv::", "")
+        return re.sub(r"\(.*", "", name)
+
+    stats = {}
+    with open(os.path.join(pdir, "kt", "run_kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            stats[short(r["Name"])] = (int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                                       float(r["MaxNs"]) / 1e3)
+    bench_line = None
+    for line in open(os.path.join(pdir, "kt.log")):
+        if line.startswith("{") and '"metric"' in line:
+            bench_line = json.loads(line)
+    counters, copy = {}, {}
+    for f in sorted(glob.glob(os.path.join(pdir, "p*", "run_counter_collection.csv"))):
+        per = {}
+        for r in csv.DictReader(open(f)):
+            key = (int(r["Dispatch_Id"]), short(r["Kernel_Name"]), r["Counter_Name"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        acc = {}
+        for (d, k, c), v in per.items():
+            if "copyBuffer" in k:                       # the largest copy is the 1 GiB probe
+                copy[c] = max(copy.get(c, 0.0), v)
+                continue
+            acc.setdefault((k, c), []).append(v)
+        for (k, c), vs in acc.items():
+            counters.setdefault(k, {})[c] = sum(vs) / len(vs)
+    probe = 1 << 30
+    f_fetch = probe / (copy["FETCH_SIZE"] * 1024) if copy.get("FETCH_SIZE") else None
+    f_write = probe / (copy["WRITE_SIZE"] * 1024) if copy.get("WRITE_SIZE") else None
+
+    def traffic(k):
+        c = counters.get(k, {})
+        if f_fetch is None or f_write is None or "FETCH_SIZE" not in c or "WRITE_SIZE" not in c:
+            return None
+        return int(c["FETCH_SIZE"] * 1024 * f_fetch + c["WRITE_SIZE"] * 1024 * f_write)
+
+    gemvs = {"qk": next((k for k in stats if k.startswith("k_qk_gemv")), None),
+             "pv": next((k for k in stats if k.startswith("k_pv_gemv")), None)}
+    if not bench_line:
+        raise SystemExit(f"{pdir}/kt.log holds no bench line")
+    # the hash of the sources the profiled run was built from, not of today's
+    entry = {"kernel_source": bench_line["kernel_source"], "fetch_factor": f_fetch, "write_factor": f_write}
+    for tag, k in gemvs.items():
+        if k and traffic(k) is not None:
+            entry[tag] = traffic(k)
+    tf = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
+    tf[workload] = entry
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(tf, f, indent=1, sort_keys=True)
+
+    alg = {gemvs[t]: b for t, b in bench_line["alg_bytes_per_launch"].items() if gemvs.get(t)}
+    lines = [f"# Kernel trace and counters: {workload}", "",
+             "Commands (repository root, one rocprofv3 process each):", "", "```",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/kt -o run -- "
+             f"python bench.py --workload {workload} --steps 20 --warmup 5 --no-cpu-baseline > <dir>/kt.log",
+             f"rocprofv3 --pmc <counters> --output-format csv -d <dir>/p<i> -o run -- "
+             f"python bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline",
+             f"python bench.py --summarize <dir> --workload {workload}", "```", "",
+             "Counter passes: (1) SQ_WAVES SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU SQ_INSTS_VMEM_RD "
+             "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_LDS; (2) SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS "
+             "SQ_ACTIVE_INST_VMEM SQ_ACTIVE_INST_SCA SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_LDS_BANK_CONFLICT "
+             "SQ_ACTIVE_INST_ANY; (3) FETCH_SIZE; (4) WRITE_SIZE; (5) GRBM_GUI_ACTIVE SQ_INSTS_VALU_CVT "
+             "SQ_INSTS_VALU_FMA_F32 SQ_INSTS_VALU_INT32.", "",
+             f"Kernel source hash: `{entry['kernel_source']}`", "",
+             "## Kernel durations (rocprofv3 --stats)", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for k, (n, avg, mn, mx) in sorted(stats.items(), key=lambda x: -x[1][0] * x[1][1]):
+        lines.append(f"| {k} | {n} | {avg:.1f} | {mn:.1f} | {mx:.1f} |")
+    lines += ["", "## HBM traffic per launch", "",
+              f"1 GiB device copy: FETCH_SIZE {copy.get('FETCH_SIZE', 0):.0f} KiB, WRITE_SIZE "
+              f"{copy.get('WRITE_SIZE', 0):.0f} KiB, so fetch factor {f_fetch and round(f_fetch, 4)}, "
+              f"write factor {f_write and round(f_write, 4)}.", "",
+              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | traffic bytes | algorithmic bytes | traffic / alg |",
+              "|---|---|---|---|---|---|"]
+    for tag, k in gemvs.items():
+        if not k or k not in counters:
+            continue
+        c = counters[k]
+        t = traffic(k)
+        a = alg.get(k)
+        ratio = f"{t / a:.3f}" if (t and a) else "-"
+        lines.append(f"| {k} | {c.get('FETCH_SIZE', 0):.0f} | {c.get('WRITE_SIZE', 0):.0f} | {t} | {a or '-'} | {ratio} |")
+    lines += ["", "## Other counters (average per dispatch)", ""]
+    for k in [gemvs["qk"], gemvs["pv"]] + [x for x in counters if x.startswith(("k_softmax", "k_encode"))]:
+        if k and k in counters:
+            c = counters[k]
+            lines.append(f"- **{k}**: " + ", ".join(f"{n} {v:.4g}" for n, v in sorted(c.items())))
+    if bench_line:
+        lines += ["", "## Bench line of the traced run", "", "```", json.dumps(bench_line), "```"]
+    name = f"decode_step_{workload}.md"
+    with open(os.path.join(ROOT, "profiles", name), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote profiles/{name} and the {workload} entry of profiles/traffic.json")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b-32k", choices=sorted(kvsynth.WORKLOADS))
-    ap.add_argument("--cpu-streams", type=int, default=2, help="streams in the oracle's timed sample")
+    ap.add_argument("--cpu-streams", type=int, default=4, help="streams in the oracle's timed sample")
+    ap.add_argument("--cpu-steps", type=int, default=30, help="decode steps per sampled stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
                     help="size of a plain device copy run after timing (counter calibration)")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="write the profiles/ summary and traffic entry from a rocprofv3 profile directory")
     args = ap.parse_args()
+    if args.summarize:
+        summarize_profile(args.summarize, args.workload)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the packed cache is per stream and this build runs on a "
               "single MI355X; --gpus must be 1", file=sys.stderr)
@@ -232,7 +350,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
-        cpu = cpu_baseline(w, args.cpu_streams)
+        cpu = cpu_baseline(w, args.cpu_streams, args.cpu_steps)
 
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -251,6 +369,8 @@ def main():
         "prefill_ms": round(prefill_s * 1e3, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "alg_bytes_per_launch": {"qk": int(qk_alg), "pv": int(pv_alg)},
+        "kernel_source": kernel_source_hash(),
     }
     print(json.dumps(res), flush=True)
 

@@ -192,10 +192,30 @@ struct BlockDecoder {
     }
     const bool ok = __ballot(bad) == 0 && (uint32_t)pad16(pay + 4 * (int)total) == size;
     uint32_t wd[NRL][4];
+    if (all_full && BITS != 3) {
+      // runs of 4 (2) words at a 16 (8) byte aligned lane stride: one wide
+      // LDS read per run instead of 4 (2) dword reads that would hit the
+      // same banks
+#pragma unroll
+      for (int k = 0; k < NRL; ++k) {
+        if (BITS == 4) {
+          const u32x4 t = reinterpret_cast<const u32x4*>(rec + pay)[ok ? lane + 64 * k : 0];
+          wd[k][0] = t.x; wd[k][1] = t.y; wd[k][2] = t.z; wd[k][3] = t.w;
+        } else {
+          const uint2 t = reinterpret_cast<const uint2*>(rec + pay)[ok ? lane + 64 * k : 0];
+          wd[k][0] = t.x; wd[k][1] = t.y; wd[k][2] = wd[k][3] = 0u;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NRL; ++k) {
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + pay) + (ok ? off[k] : 0u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wd[k][i] = i < BITS ? p[i] : 0u;
+      }
+    }
 #pragma unroll
     for (int k = 0; k < NRL; ++k) {
-      const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + pay) + (ok ? off[k] : 0u);
-      wd[k][0] = p[0]; wd[k][1] = p[1]; wd[k][2] = p[2]; wd[k][3] = p[3];
       full_to_nibbles<BITS>(wd[k], nib[k]);
       const uint32_t mm = nibble_splat(h[k]);
 #pragma unroll
