@@ -1,0 +1,173 @@
+"""Full-size GPU parity: every measured workload at its real shape, in the
+launch configuration bench.py times.
+
+The oracle cannot follow a whole 256-stream cache in seconds, so each test
+checks (1) one sampled stream completely - every record byte, the offsets,
+the permutation and the tail, and its K-GEMV scores and V-GEMV output within
+rel-L2 1e-4 of the fp64 oracle - and (2) one sampled block of every stream,
+re-encoded by the oracle on its own (a closed block depends only on its own
+tokens): its K and V record bytes and its scores.  Every row also has to
+satisfy what holds at any size (finite outputs, softmax rows summing to 1).
+"""
+
+import concurrent.futures as cf
+
+import numpy as np
+import pytest
+
+import kvsynth
+import oracle
+from gpu_common import say, rel_l2, worst_row_rel
+from oracle import stream as ostream, attention
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch, torch.device("cuda:0")
+
+
+def host_streams(w, tokens):
+    """Seeded fp16 K, V of every stream, [S][tokens][D] each (host)."""
+    S, D = w.streams, w.head_dim
+    K = np.empty((S, tokens, D), np.float16)
+    V = np.empty_like(K)
+    with cf.ThreadPoolExecutor(16) as ex:
+        for s, (k, v) in enumerate(ex.map(lambda i: kvsynth.stream_kv(w, i, tokens=tokens), range(S))):
+            K[s], V[s] = k, v
+    return K, V
+
+
+def stream_state_equal(c, ref, s):
+    """Bit-exact records, offsets, permutation and tail staging of stream s."""
+    T, B = c.n_tokens, c.block
+    nb = -(-T // B)
+    for which in "KV":
+        offs = c.offsets(which)[s, :nb + 1].cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+        ro = ref.offsets(which)
+        assert np.array_equal(offs, ro), f"{which} offsets of stream {s} differ"
+        got = c.arena(which)[s, :int(ro[-1])].cpu().numpy().tobytes()
+        assert got == ref.arena(which), f"{which} records of stream {s} differ"
+    assert np.array_equal(c.perm_table()[s, :nb].cpu().numpy(), ref.perm_table())
+    nt = T % B
+    tk = c.tail_k.view(c.n_streams, B, 128)[s, :nt].cpu().numpy()
+    assert np.array_equal(tk.view(np.uint16), ref.tail_k.view(np.uint16))
+
+
+def check_offsets_all_streams(c, cfg):
+    """Every stream: offsets start at 0, increase by a legal record size."""
+    T, B = c.n_tokens, c.block
+    nb = -(-T // B)
+    nr_full = B // 32
+    for which in "KV":
+        offs = c.offsets(which)[:, :nb + 1].cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+        assert np.all(offs[:, 0] == 0)
+        sizes = np.diff(offs, axis=1)
+        params = 4 * 128 if which == "K" else 4 * B
+        lo = params + nr_full * 128                        # header only (narrowest runs)
+        hi = params + nr_full * 128 + 16 + nr_full * 128 * 4 * cfg.bits
+        assert np.all(sizes[:, :-1] >= lo) and np.all(sizes <= hi), f"{which} record sizes out of range"
+
+
+def sampled_blocks(c, w, K, V, cfg, scores, rng):
+    """One random closed block per stream, re-encoded by the oracle alone."""
+    B = w.block
+    nb_closed = c.n_tokens // B
+    ka = c.arena("K").cpu().numpy()
+    va = c.arena("V").cpu().numpy()
+    ko = c.offsets("K").cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+    vo = c.offsets("V").cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+    worst = 0.0
+    for s in range(w.streams):
+        j = int(rng.integers(nb_closed))
+        code = ostream.encode_block(K[s, j * B:(j + 1) * B], V[s, j * B:(j + 1) * B], cfg)
+        assert ka[s, ko[s, j]:ko[s, j + 1]].tobytes() == code.k_record, f"K record ({s}, {j})"
+        assert va[s, vo[s, j]:vo[s, j + 1]].tobytes() == code.v_record, f"V record ({s}, {j})"
+        one = ostream.StreamCache(cfg, [code], B, K[s, :0], V[s, :0])
+        kh = ostream.decode_stream(one)[0]
+        q = kvsynth.stream_q(w, s)
+        ref = attention.qk(q, kh)
+        worst = max(worst, rel_l2(scores[s, :, j * B:(j + 1) * B], ref))
+    assert worst <= TOL, worst
+
+
+@pytest.mark.parametrize("name", ["single-head-4k", "llama7b-32k", "gqa-128k", "2bit-16k"])
+def test_fullsize_workload(torch_dev, name):
+    torch, dev = torch_dev
+    from decode_gemv_amd import PackedKVCache, softmax_rows
+    w = kvsynth.WORKLOADS[name]
+    S, G, T, D = w.streams, w.group, w.tokens, w.head_dim
+    cfg = oracle.Config(bits=w.bits, block=w.block)
+    say("fullsize", name, "S", S, "T", T, "G", G)
+    K, V = host_streams(w, T)
+    c = PackedKVCache(S, T + 8, bits=w.bits, block=w.block, device=str(dev))
+    c.compress(torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev))
+    assert c.check() == 0
+    check_offsets_all_streams(c, cfg)
+    q = np.stack([kvsynth.stream_q(w, s) for s in range(S)])
+    say("fullsize gemvs", name)
+    scores_d = c.qk(torch.from_numpy(q).to(dev))
+    p_d = softmax_rows(scores_d, T, 1.0 / np.sqrt(D))
+    out = c.pv(p_d).cpu().numpy()
+    assert c.check() == 0
+    scores = scores_d.cpu().numpy()
+    p = p_d.cpu().numpy()
+    assert np.all(np.isfinite(scores)) and np.all(np.isfinite(out))
+    assert np.all(np.abs(p.sum(-1) - 1.0) < 1e-4)
+    say("fullsize sampled blocks", name)
+    sampled_blocks(c, w, K, V, cfg, scores, np.random.default_rng(7))
+    s = S - 1                                   # the stream at the far end of the arenas
+    say("fullsize oracle stream", name, s)
+    ref = ostream.compress(K[s], V[s], cfg)
+    stream_state_equal(c, ref, s)
+    kh, vh, _, _ = ostream.decode_stream(ref)
+    ref_sc = attention.qk(q[s], kh)
+    assert rel_l2(scores[s], ref_sc) <= TOL, (rel_l2(scores[s], ref_sc), worst_row_rel(scores[s], ref_sc))
+    ref_out = attention.pv(p[s].astype(np.float64), vh)
+    assert rel_l2(out[s], ref_out) <= TOL, (rel_l2(out[s], ref_out), worst_row_rel(out[s], ref_out))
+
+
+def test_fullsize_streaming_append(torch_dev):
+    """Prefill 65536 tokens, then 256 single-token appends over 256 streams;
+    the sampled stream is checked against the oracle after steps 1, 64, 65
+    and 256 (records, offsets, scores, V output)."""
+    torch, dev = torch_dev
+    from decode_gemv_amd import PackedKVCache, softmax_rows
+    w = kvsynth.WORKLOADS["append-64k"]
+    S, G, T0, D, n_app = w.streams, w.group, w.tokens, w.head_dim, w.append_steps
+    cfg = oracle.Config(bits=w.bits, block=w.block)
+    say("fullsize append", S, T0, n_app)
+    K, V = host_streams(w, T0)
+    c = PackedKVCache(S, T0 + n_app, bits=w.bits, block=w.block, device=str(dev))
+    c.compress(torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev))
+    assert c.check() == 0
+    s = S - 1
+    ref = ostream.compress(K[s], V[s], cfg)
+    del K, V
+    for step in range(1, n_app + 1):
+        new = [kvsynth.append_kv(w, i, step - 1) for i in range(S)]
+        kn = torch.from_numpy(np.stack([a for a, _ in new])).to(dev)
+        vn = torch.from_numpy(np.stack([b for _, b in new])).to(dev)
+        c.append(kn, vn)
+        ostream.append(ref, *new[s])
+        if step not in (1, 64, 65, n_app):
+            continue
+        say("append step", step)
+        assert c.check() == 0
+        T = c.n_tokens
+        stream_state_equal(c, ref, s)
+        q = np.stack([kvsynth.stream_q(w, i, step=step) for i in range(S)])
+        scores_d = c.qk(torch.from_numpy(q).to(dev))
+        p_d = softmax_rows(scores_d, T, 1.0 / np.sqrt(D))
+        out = c.pv(p_d).cpu().numpy()
+        assert c.check() == 0
+        scores = scores_d.cpu().numpy()
+        p = p_d.cpu().numpy()
+        assert np.all(np.isfinite(scores)) and np.all(np.isfinite(out))
+        kh, vh, _, _ = ostream.decode_stream(ref)
+        assert rel_l2(scores[s], attention.qk(q[s], kh)) <= TOL
+        assert rel_l2(out[s], attention.pv(p[s].astype(np.float64), vh)) <= TOL
