@@ -245,7 +245,7 @@ def main():
     dev = torch.device("cuda:0")
     S, G, T0, D = w.streams, w.group, w.tokens, w.head_dim
     n_steps = args.warmup + args.steps
-    T_max = T0 + n_steps
+    T_max = T0 + 2 * n_steps                 # room for the fused pass's appends too
     log(w.describe())
 
     t = time.perf_counter()
@@ -310,6 +310,30 @@ def main():
     assert cache.check() == 0
     kb1, vb1, nb1 = used_bytes()
 
+    # the same steps through the fused attention kernel (one launch replaces
+    # K GEMV, softmax and V GEMV); the step's appends continue the cache
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_steps)]
+    aws = cache.attention_workspace(G)
+    fout = torch.empty((S, G, D), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    for i in range(n_steps):
+        if i == args.warmup:
+            torch.cuda.synchronize()
+            tf0 = time.perf_counter()
+        e = fev[i]
+        e[0].record()
+        cache.append(kn[i], vn[i])
+        e[1].record()
+        cache.attention(qn[i], scale, out=fout, workspace=aws)
+        e[2].record()
+    torch.cuda.synchronize()
+    fwall = time.perf_counter() - tf0
+    assert cache.check() == 0
+    kb2, vb2, _ = used_bytes()
+
+    t_attn = float(np.mean([x[1].elapsed_time(x[2]) for x in fev[args.warmup:]]))
+    f_ms_step = fwall / args.steps * 1e3
+    f_bytes = (kb1 + kb2 + vb1 + vb2) / 2 + 8 * S * (nb1 + 1)
     timed = ev[args.warmup:]
     def avg_ms(a, b):
         return float(np.mean([x[a].elapsed_time(x[b]) for x in timed]))
@@ -369,6 +393,11 @@ def main():
         "prefill_ms": round(prefill_s * 1e3, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "fused_attention": {
+            "ms_per_step": round(f_ms_step, 4), "attention_ms": round(t_attn, 4),
+            "value": round(f_bytes / (f_ms_step * 1e-3) / 1e9, 1),
+            "attention_GBps": round(f_bytes / (t_attn * 1e-3) / 1e9, 1),
+            "note": "append + one fused launch (K GEMV, softmax, V GEMV) per step; value as above"},
         "alg_bytes_per_launch": {"qk": int(qk_alg), "pv": int(pv_alg)},
         "kernel_source": kernel_source_hash(),
     }

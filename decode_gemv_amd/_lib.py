@@ -47,6 +47,9 @@ _SIGS = {
     "packkv_cache_sizes": (c_int32, [ctypes.POINTER(Config), c_int32, c_int64, ctypes.POINTER(Sizes)]),
     "packkv_arena_stride_bytes": (c_uint64, [ctypes.POINTER(Config), c_int64]),
     "packkv_pv_workspace_bytes": (c_uint64, [ctypes.POINTER(CacheT), c_int32]),
+    "packkv_attention_workspace_bytes": (c_uint64, [ctypes.POINTER(CacheT), c_int32]),
+    "packkv_attention_decode": (c_int32, [ctypes.POINTER(CacheT), c_void_p, c_int32, ctypes.c_float, c_void_p,
+                                          c_void_p, c_uint64, c_void_p]),
     "packkv_compress_block": (c_int32, [ctypes.POINTER(CacheT), c_void_p, c_void_p, c_int64, c_void_p]),
     "packkv_append_tokens": (c_int32, [ctypes.POINTER(CacheT), c_void_p, c_void_p, c_int32, c_void_p]),
     "packkv_qk_gemv": (c_int32, [ctypes.POINTER(CacheT), c_void_p, c_int32, c_void_p, c_int64, c_void_p]),

@@ -55,6 +55,7 @@ class PackedKVCache:
                               _ptr(self.k_arena), _ptr(self.v_arena), _ptr(self.k_off), _ptr(self.v_off),
                               _ptr(self.perm), _ptr(self.tail_k), _ptr(self.tail_v), _ptr(self.status))
         self._ws: dict = {}
+        self._aws: dict = {}
 
     # ------------------------------------------------------------------ state
     @property
@@ -134,6 +135,34 @@ class PackedKVCache:
         _lib.check(_lib.load().packkv_pv_gemv(ctypes.byref(self._c), _ptr(p), ld, G, _ptr(out), _ptr(ws),
                                               ws.numel() * ws.element_size(), _stream()),
                    "packkv_pv_gemv")
+        return out
+
+    def attention_workspace(self, group: int) -> torch.Tensor:
+        """The fused-attention workspace for `group` queries per stream,
+        zero-filled when first made, then reused."""
+        need = int(_lib.load().packkv_attention_workspace_bytes(ctypes.byref(self._c), group))
+        ws = self._aws.get(group)
+        if ws is None or ws.numel() < need:
+            ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=self.k_arena.device)
+            self._aws[group] = ws
+        return ws
+
+    def attention(self, q: torch.Tensor, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """out[s][g] = softmax(scale * q[s][g] . K_hat[s]^T) V_hat[s] in one launch;
+        q fp16 [S][G][D], scale defaults to 1/sqrt(D)."""
+        S, G, d = q.shape
+        if q.dtype != torch.float16 or S != self.n_streams or d != D or not q.is_contiguous():
+            raise ValueError("q must be contiguous fp16 [S][G][D]")
+        if out is None:
+            out = torch.empty(S, G, D, dtype=torch.float32, device=q.device)
+        if out.dtype != torch.float32 or tuple(out.shape) != (S, G, D) or not out.is_contiguous():
+            raise ValueError("out must be contiguous fp32 [S][G][D]")
+        ws = self.attention_workspace(G) if workspace is None else workspace
+        sc = D ** -0.5 if scale is None else float(scale)
+        _lib.check(_lib.load().packkv_attention_decode(ctypes.byref(self._c), _ptr(q), G, sc, _ptr(out), _ptr(ws),
+                                                       ws.numel() * ws.element_size(), _stream()),
+                   "packkv_attention_decode")
         return out
 
     def decompress(self, which: str, mode: int) -> torch.Tensor:

@@ -4,6 +4,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <cmath>
+
 #include "kernels.hpp"
 
 using namespace packkv;
@@ -242,6 +244,50 @@ int packkv_pv_gemv(const packkv_cache_t* c, const float* p, int64_t ld, int32_t 
   a.out = out;
   if (ws_bytes < packkv_pv_workspace_bytes(c, group)) return PACKKV_EINVAL;
   return hip_status(launch_pv(a, c->cfg.block_tokens, c->n_streams, (hipStream_t)stream));
+}
+
+// Attention workspace: per (stream, query, split) kAttnPartial floats, then
+// one u32 arrival counter per stream.
+static uint64_t attn_partial_bytes(const packkv_cache_t* c, int32_t group) {
+  const int64_t mb = max_blocks_of(&c->cfg, c->max_tokens);
+  const int64_t splits = (mb + 3) / 4;     // blocks per workgroup is at least 4
+  return (uint64_t)c->n_streams * (uint64_t)group * (uint64_t)splits * kAttnPartial * sizeof(float);
+}
+
+uint64_t packkv_attention_workspace_bytes(const packkv_cache_t* c, int32_t group) {
+  if (check_cache(c) || group < 1) return 0;
+  return attn_partial_bytes(c, group) + (((uint64_t)c->n_streams * 4u + 255u) & ~(uint64_t)255u);
+}
+
+int packkv_attention_decode(const packkv_cache_t* c, const void* q_f16, int32_t group, float scale, float* out,
+                            void* workspace, uint64_t ws_bytes, void* stream) {
+  int e = check_cache(c);
+  if (e) return e;
+  if (!q_f16 || !out || !workspace || group < 1 || !(scale > 0.f) || !std::isfinite(scale)) return PACKKV_EINVAL;
+  if (c->n_tokens < 1) return PACKKV_ESTATE;
+  if (ws_bytes < packkv_attention_workspace_bytes(c, group)) return PACKKV_EINVAL;
+  const GemvArgs g = gemv_args(c, false);
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k_arena = c->k_arena;
+  a.v_arena = c->v_arena;
+  a.arena_stride = c->arena_stride;
+  a.k_off = c->k_off;
+  a.v_off = c->v_off;
+  a.off_stride = g.off_stride;
+  a.n_tokens = c->n_tokens;
+  a.nb = g.nb;
+  a.bits = c->cfg.bits;
+  a.blocks_per_wg = g.blocks_per_wg;
+  a.splits = g.splits;
+  a.G = group;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  a.q = (const uint16_t*)q_f16;
+  a.ws = (float*)workspace;
+  a.tickets = (uint32_t*)((uint8_t*)workspace + attn_partial_bytes(c, group));
+  a.out = out;
+  a.status = c->status;
+  return hip_status(launch_attention(a, c->cfg.block_tokens, c->n_streams, (hipStream_t)stream));
 }
 
 int packkv_decompress(const packkv_cache_t* c, int32_t which, int32_t mode, void* out, void* stream) {

@@ -236,175 +236,141 @@ struct BlockDecoder {
 };
 
 // ---------------------------------------------------------------------------
-// K side.
+// Offsets of a workgroup's records: lane i holds off[j0 + i] and
+// off[j0 + 64 + i] (up to 128 blocks), read back with readlane.
+struct RecordOffsets {
+  uint32_t lo, hi;
+  __device__ __forceinline__ void load(const uint32_t* offs, int j0, int nj, int lane) {
+    lo = lane <= nj ? offs[j0 + lane] : 0u;
+    hi = lane + 64 <= nj ? offs[j0 + 64 + lane] : 0u;
+  }
+  __device__ __forceinline__ uint32_t operator()(int i) const {
+    return i < 64 ? readlane_u32(lo, i) : readlane_u32(hi, i - 64);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// K side, one staged block.
+//
+//   scores[g][t] = beta_g + sum_c q'_g[c] (m + u)[t][c],   q' = q * scale
+//
+// The record's containers go to an LDS plane [slot group][channel] (row
+// pitch 136 words; the quad order rotates per channel group, so 16 lanes of a
+// 16-byte read cover the 64 banks once).  Lane (g8, cg) then covers 8 slots
+// x 16 channels: each container word becomes 8 floats through 4
+// v_cvt_pk_f32_fp8 (a byte n <= 15 read as e4m3 is exactly n * 2^-9; 2^9 is
+// folded into q'), one FMA per element, and an LDS transpose sums the 8
+// channel groups.  Lane l ends with the scores of slots h*64 + l.
 template <int B, int BITS, int GT>
-__global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
+struct KBlock {
   using Dec = BlockDecoder<B, BITS, false>;
-  constexpr int NRL = Dec::NRL;
-  constexpr int REC = max_record_bytes(false, B, 4);
-  constexpr int NCH = (REC + 1023) / 1024;
-  constexpr int ROWW = kD + 8;                     // plane row: 128 words + 32 B pad
-  constexpr int REDB = GT * 64 * 9 * 4;            // channel-group reduction
-  constexpr int BUF = (REC + 16) > REDB ? (REC + 16) : REDB;
-  __shared__ __attribute__((aligned(16))) uint8_t rec[BUF];
-  __shared__ __attribute__((aligned(16))) uint32_t plane[(B / 8) * ROWW];
-  __shared__ __attribute__((aligned(16))) float qs[GT * kD];
-  float* red = reinterpret_cast<float*>(rec);      // reuses the staging buffer
+  static constexpr int NRL = Dec::NRL;
+  static constexpr int NH = B / 64;
+  static constexpr int ROWW = kD + 8;
+  static constexpr int PLANE_WORDS = (B / 8) * ROWW;
+  static constexpr int RED_BYTES = GT * 64 * 9 * 4;   // channel-group reduction
 
-  const int lane = threadIdx.x;
-  const int s = blockIdx.x / a.splits;
-  const int split = blockIdx.x % a.splits;
-  const int j0 = split * a.blocks_per_wg;
-  const int j1 = min(a.nb, j0 + a.blocks_per_wg);
-  if (j0 >= j1) return;
-  const int nj = j1 - j0;
-  const uint8_t* arena = a.arena + (uint64_t)s * a.arena_stride;
-  const uint32_t* offs = a.off + (int64_t)s * a.off_stride;
-  const float unit_inv = 1.0f / fp8_unit();
-  // offsets of this workgroup's records: lane i holds off[j0 + i]
-  const uint32_t my_off = lane <= nj ? offs[j0 + lane] : 0u;
-  const uint32_t my_off2 = lane + 64 <= nj ? offs[j0 + 64 + lane] : 0u;
-  auto off_of = [&](int i) -> uint32_t {
-    return i < 64 ? readlane_u32(my_off, i) : readlane_u32(my_off2, i - 64);
-  };
-  const int g8 = lane & 7, cg = lane >> 3;
+  uint32_t* plane;
+  float* qs;                                          // [GT][D] q' of the block
+  int lane, g8, cg;
+  float qa[GT], qb[GT], qau[GT], qbu[GT];             // queries at channels lane, lane + 64
 
-  for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
-    // queries for the channels this lane stages (c = lane, lane + 64)
-    float qa[GT], qb[GT], qau[GT], qbu[GT];
+  __device__ __forceinline__ void init(uint32_t* plane_, float* qs_, int lane_) {
+    plane = plane_;
+    qs = qs_;
+    lane = lane_;
+    g8 = lane & 7;
+    cg = lane >> 3;
+  }
+  __device__ __forceinline__ void set_queries(const uint16_t* q, int64_t s, int G, int gq0) {
+    const float unit_inv = 1.0f / fp8_unit();
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
-      const bool ok = gq0 + g < a.G;
-      const uint16_t* qp = a.q + ((int64_t)s * a.G + gq0 + g) * kD;
+      const bool ok = gq0 + g < G;
+      const uint16_t* qp = q + (s * G + gq0 + g) * kD;
       qa[g] = ok ? f16_bits_to_float(qp[lane]) : 0.f;
       qb[g] = ok ? f16_bits_to_float(qp[lane + 64]) : 0.f;
       qau[g] = qa[g] * unit_inv;
       qbu[g] = qb[g] * unit_inv;
     }
-    // two records in flight: block jj + 2 is requested while block jj is
-    // processed, alternating between the register sets pa and pb
-    auto request = [&](int jj, u32x4 (&pre)[NCH]) __attribute__((always_inline)) {
-      const bool in = jj < nj;
-      const uint32_t o = in ? off_of(jj) : 0u, size = in ? off_of(jj + 1) - o : 0u;
-      load_record<NCH>(arena + o, record_ok(o, size, a.arena_stride, REC) ? size : 0u, lane, pre);
-    };
-    // The loop body has no exits: a missing block (jj >= nj) or a corrupt
-    // record is staged as zero bytes and writes nothing. An exit inside the
-    // body would give the wait-count analysis a path on which only one
-    // register set has loads in flight, and it would then drain both.
-    bool corrupt = false;
-    auto process = [&](int jj, u32x4 (&pre)[NCH]) __attribute__((always_inline)) {
-      const bool in = jj < nj;
-      const int j = j0 + jj;
-      const uint32_t o = in ? off_of(jj) : 0u, size0 = in ? off_of(jj + 1) - o : 0u;
-      const bool rok = record_ok(o, size0, a.arena_stride, REC);
-      corrupt |= in && !rok;
-      const uint32_t size = rok ? size0 : 0u;
-      const int n = in ? (int)imin64(B, a.n_tokens - (int64_t)j * B) : 0;
-      const int nr = (n + kR - 1) / kR;
-      __syncthreads();
-      store_record<NCH>(rec, size, lane, pre);
-      request(jj + 2, pre);
-      // keep each request's loads together and in order, so that the wait
-      // for one record never has to drain the other record's loads
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-
-      uint32_t nib[NRL][4];
-      // a corrupt record is computed on but its scores are not written
-      const bool ok = Dec::decode(rec, size, nr, lane, nib) && rok;
-      corrupt |= rok && !ok;
-#pragma unroll
-      for (int k = 0; k < NRL; ++k) {
-        const int r = k >> 1, c = lane + 64 * (k & 1);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) plane[(r * 4 + kk) * ROWW + c] = nib[k][kk];
-      }
-      // q' = q * scale (per channel), beta = q . zero
-      float beta[GT];
-      {
-        const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec);
-        const float sa = f16_bits_to_float(sc[lane]), sb = f16_bits_to_float(sc[lane + 64]);
-        const float za = f16_bits_to_float(sc[kD + lane]), zb = f16_bits_to_float(sc[kD + lane + 64]);
-#pragma unroll
-        for (int g = 0; g < GT; ++g) {
-          qs[g * kD + lane] = qau[g] * sa;
-          qs[g * kD + lane + 64] = qbu[g] * sb;
-          beta[g] = wave_sum(fmaf(qa[g], za, qb[g] * zb));
-        }
-      }
-      __syncthreads();
-
-      // container plane x q': lane (g8, cg) covers slot group g8 of a 64-slot
-      // half and channels cg*16 .. cg*16+15
-#pragma unroll
-      for (int h = 0; h < B / 64; ++h) {
-        float acc[GT][8];
-#pragma unroll
-        for (int g = 0; g < GT; ++g)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
-        const int row = h * 8 + g8;
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          // rotate the quad order per channel group: with the 136-word row
-          // pitch, 16 lanes of a 16-byte read then cover all 64 banks once
-          const int c0 = cg * 16 + ((i4 + cg) & 3) * 4;
-          const u32x4 nw = *reinterpret_cast<const u32x4*>(&plane[row * ROWW + c0]);
-          const uint32_t words[4] = {nw.x, nw.y, nw.z, nw.w};
-          float qq[GT][4];
-#pragma unroll
-          for (int g = 0; g < GT; ++g) {
-            const float4 t = *reinterpret_cast<const float4*>(&qs[g * kD + c0]);
-            qq[g][0] = t.x; qq[g][1] = t.y; qq[g][2] = t.z; qq[g][3] = t.w;
-          }
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            float f[8];
-            nibbles_to_f32(words[cc], f);
-#pragma unroll
-            for (int g = 0; g < GT; ++g)
-#pragma unroll
-              for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(qq[g][cc], f[i], acc[g][i]);
-          }
-        }
-        // reduce the 8 channel groups: red[g][slot][cg], slot = g8*8 + i
-        __syncthreads();
-#pragma unroll
-        for (int g = 0; g < GT; ++g)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) red[(g * 64 + g8 * 8 + i) * 9 + cg] = acc[g][i];
-        __syncthreads();
-        // range-checked stores: slots past n, absent queries and corrupt
-        // records write nothing
-        const uint32_t valid = ok ? (uint32_t)max(0, min(64, n - h * 64)) : 0u;
-#pragma unroll
-        for (int g = 0; g < GT; ++g) {
-          float sum = beta[g];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) sum += red[(g * 64 + lane) * 9 + u];
-          const bool gok = gq0 + g < a.G;
-          float* row0 = a.scores + ((int64_t)s * a.G + (gok ? gq0 + g : 0)) * a.ld + (int64_t)j * B + h * 64;
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), buffer_rsrc(row0, gok ? 4u * valid : 0u),
-                                                4 * lane, 0, 0);
-        }
-      }
-    };
-    u32x4 pa[NCH], pb[NCH];
-    request(0, pa);
-    __builtin_amdgcn_sched_barrier(0);
-    request(1, pb);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int jj = 0; jj < nj; jj += 2) {
-      process(jj, pa);
-      process(jj + 1, pb);
-    }
-    if (corrupt && lane == 0) latch(a.status, PACKKV_ECORRUPT);
   }
-}
+
+  // rec: the staged record (size bytes, nr runs); afterwards it serves as the
+  // reduction buffer.  Returns whether the record decoded consistently.
+  __device__ __forceinline__ bool run(uint8_t* rec, uint32_t size, int nr, float (&score)[GT][NH]) {
+    uint32_t nib[NRL][4];
+    const bool ok = Dec::decode(rec, size, nr, lane, nib);
+#pragma unroll
+    for (int k = 0; k < NRL; ++k) {
+      const int r = k >> 1, c = lane + 64 * (k & 1);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) plane[(r * 4 + kk) * ROWW + c] = nib[k][kk];
+    }
+    // q' = q * scale (per channel), beta = q . zero
+    float beta[GT];
+    {
+      const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec);
+      const float sa = f16_bits_to_float(sc[lane]), sb = f16_bits_to_float(sc[lane + 64]);
+      const float za = f16_bits_to_float(sc[kD + lane]), zb = f16_bits_to_float(sc[kD + lane + 64]);
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        qs[g * kD + lane] = qau[g] * sa;
+        qs[g * kD + lane + 64] = qbu[g] * sb;
+        beta[g] = wave_sum(fmaf(qa[g], za, qb[g] * zb));
+      }
+    }
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(rec);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      float acc[GT][8];
+#pragma unroll
+      for (int g = 0; g < GT; ++g)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
+      const int row = h * 8 + g8;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int c0 = cg * 16 + ((i4 + cg) & 3) * 4;
+        const u32x4 nw = *reinterpret_cast<const u32x4*>(&plane[row * ROWW + c0]);
+        const uint32_t words[4] = {nw.x, nw.y, nw.z, nw.w};
+        float qq[GT][4];
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+          const float4 t = *reinterpret_cast<const float4*>(&qs[g * kD + c0]);
+          qq[g][0] = t.x; qq[g][1] = t.y; qq[g][2] = t.z; qq[g][3] = t.w;
+        }
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          float f[8];
+          nibbles_to_f32(words[cc], f);
+#pragma unroll
+          for (int g = 0; g < GT; ++g)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(qq[g][cc], f[i], acc[g][i]);
+        }
+      }
+      // reduce the 8 channel groups: red[g][slot][cg], slot = g8*8 + i
+      __syncthreads();
+#pragma unroll
+      for (int g = 0; g < GT; ++g)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) red[(g * 64 + g8 * 8 + i) * 9 + cg] = acc[g][i];
+      __syncthreads();
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        float sum = beta[g];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += red[(g * 64 + lane) * 9 + u];
+        score[g][h] = sum;
+      }
+    }
+    return ok;
+  }
+};
 
 // ---------------------------------------------------------------------------
-// V side: split-T partial sums into ws, then a fixed-order reduction.
+// V side, one staged block.
 //
 //   out[c] = sum_t p_t zero_t + sum_t p'_t q[t][c],   p'_t = p_t scale_t >= 0
 //
@@ -416,33 +382,261 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
 // LDS.  One v_dot8_u32_u4 then multiplies a container word by a digit word:
 // 5 instructions per 8 elements, with exact integer sums that are scaled by
 // 2^-E once per block and channel.  Per element the weight error is at most
-// 2^-21 of the block's largest weight.
+// 2^-21 of the block's largest weight.  Lane l accumulates channels l and
+// l + 64.
 template <int B, int BITS, int GT>
-__global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
+struct VBlock {
   using Dec = BlockDecoder<B, BITS, true>;
-  constexpr int NR = Dec::NR;
-  constexpr int NRL = Dec::NRL;                    // run l + 64k: r = k/2, channel l + 64(k&1)
-  constexpr int NH = B / 64;                       // slots per lane
-  constexpr int NG = B / 8;                        // 8-slot groups per block
-  constexpr int ND = 5;                            // 4-bit digits of p'
-  constexpr int REC = max_record_bytes(true, B, 4);
+  static constexpr int NR = Dec::NR;
+  static constexpr int NRL = Dec::NRL;                // run l + 64k: r = k/2, channel l + 64(k&1)
+  static constexpr int NH = B / 64;                   // slots per lane
+  static constexpr int NG = B / 8;                    // 8-slot groups per block
+  static constexpr int ND = 5;                        // 4-bit digits of p'
+  static constexpr int DIG_WORDS = GT * ND * NG;
+
+  uint32_t* dig;                                      // [GT][ND][NG]
+  int lane, nib_shift;
+
+  __device__ __forceinline__ void init(uint32_t* dig_, int lane_) {
+    dig = dig_;
+    lane = lane_;
+    nib_shift = 4 * (lane & 7);
+  }
+
+  // pw[g][h]: weight of slot h*64 + lane (0 past the valid slots).  use:
+  // whether the block may contribute (its record is in range).  Returns
+  // whether the record decoded consistently; a block that does not adds
+  // nothing.
+  __device__ __forceinline__ bool run(const uint8_t* rec, uint32_t size, int nr, bool use,
+                                      const float (&pw)[GT][NH], float (&acc)[GT][2], float (&pz)[GT]) {
+    int E[GT];
+    bool live[GT];
+    float pzb[GT];
+    {
+      const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec);
+      float pp[GT][NH];
+#pragma unroll
+      for (int g = 0; g < GT; ++g) pzb[g] = 0.f;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const int sl = h * 64 + lane;
+        const float scl = f16_bits_to_float(sc[sl]), zer = f16_bits_to_float(sc[B + sl]);
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+          pp[g][h] = pw[g][h] * scl;
+          pzb[g] = fmaf(pw[g][h], zer, pzb[g]);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        float mx = pp[g][0];
+#pragma unroll
+        for (int h = 1; h < NH; ++h) mx = fmaxf(mx, pp[g][h]);
+        const float M = wave_max_nonneg(mx);
+        live[g] = M > 0.f;
+        E[g] = live[g] ? 19 - ilogbf(M) : 0;          // M * 2^E in [2^19, 2^20)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          const uint32_t P = min((uint32_t)(ldexpf(pp[g][h], E[g]) + 0.5f), 0xFFFFFu);
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            const uint32_t wv = or8(((P >> (4 * d)) & 15u) << nib_shift);
+            if ((lane & 7) == 0) dig[(g * ND + d) * NG + h * 8 + (lane >> 3)] = wv;
+          }
+        }
+      }
+    }
+    uint32_t nib[NRL][4];
+    const bool ok = Dec::decode(rec, size, nr, lane, nib) && use;
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      if (!ok || !live[g]) continue;
+      uint32_t sd[2][ND];
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+        for (int d = 0; d < ND; ++d) sd[ch][d] = 0u;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        if (r >= nr) break;
+        uint32_t W[ND][4];
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const u32x4 t = *reinterpret_cast<const u32x4*>(&dig[(g * ND + d) * NG + 4 * r]);
+          W[d][0] = t.x; W[d][1] = t.y; W[d][2] = t.z; W[d][3] = t.w;
+        }
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+              sd[ch][d] = __builtin_amdgcn_udot8(nib[2 * r + ch][kk], W[d][kk], sd[ch][d], false);
+      }
+      const float unit = ldexpf(1.0f, -E[g]);
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        // each digit sum is <= NR*32*15*15 < 2^15, so the total stays below 2^32
+        const uint32_t x = sd[ch][0] + (sd[ch][1] << 4) + (sd[ch][2] << 8) + (sd[ch][3] << 12) + (sd[ch][4] << 16);
+        acc[g][ch] = fmaf((float)x, unit, acc[g][ch]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < GT; ++g)
+      if (ok) pz[g] += pzb[g];
+    return ok;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Streaming skeleton shared by the GEMVs.  A workgroup (one wave) takes J
+// consecutive blocks of one stream.  Records are staged into LDS from
+// registers; two are in flight, alternating between the register sets of a
+// pair: block jj + 2 is requested while block jj is processed.  A scheduling
+// barrier keeps each request's loads together, so the wait for one record
+// never has to drain the other.  The loop body has no exits: a missing block
+// (jj >= nj) is requested as zero bytes, and a missing or corrupt block
+// contributes nothing (an exit inside the body would give the wait-count
+// analysis a path on which only one register set has loads in flight, and
+// it would then drain both at every block).
+template <int NCH, int REC>
+struct RecordStream {
+  const uint8_t* arena;
+  uint64_t stride;
+  RecordOffsets offs;
+  int nj, lane;
+  __device__ __forceinline__ void request(int jj, u32x4 (&pre)[NCH]) const {
+    const bool in = jj < nj;
+    const uint32_t o = in ? offs(jj) : 0u, size = in ? offs(jj + 1) - o : 0u;
+    load_record<NCH>(arena + o, record_ok(o, size, stride, REC) ? size : 0u, lane, pre);
+  }
+  // size of block jj's record, 0 if jj is missing; rok: in range and sane
+  __device__ __forceinline__ uint32_t size_of(int jj, bool& rok) const {
+    const bool in = jj < nj;
+    const uint32_t o = in ? offs(jj) : 0u, size = in ? offs(jj + 1) - o : 0u;
+    rok = record_ok(o, size, stride, REC);
+    return rok ? size : 0u;
+  }
+};
+
+template <int B, int BITS, int GT>
+__global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
+  using KB = KBlock<B, BITS, GT>;
+  constexpr int NH = KB::NH;
+  constexpr int REC = max_record_bytes(false, B, 4);
   constexpr int NCH = (REC + 1023) / 1024;
-  __shared__ __attribute__((aligned(16))) uint8_t rec[REC + 16];
-  __shared__ __attribute__((aligned(16))) uint32_t dig[GT][ND][NG];
+  constexpr int BUF = (REC + 16) > KB::RED_BYTES ? (REC + 16) : KB::RED_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t rec[BUF];
+  __shared__ __attribute__((aligned(16))) uint32_t plane[KB::PLANE_WORDS];
+  __shared__ __attribute__((aligned(16))) float qs[GT * kD];
 
   const int lane = threadIdx.x;
   const int s = blockIdx.x / a.splits;
   const int split = blockIdx.x % a.splits;
   const int j0 = split * a.blocks_per_wg;
   const int nj = max(0, min(a.nb, j0 + a.blocks_per_wg) - j0);
-  const uint8_t* arena = a.arena + (uint64_t)s * a.arena_stride;
-  const uint32_t* offs = a.off + (int64_t)s * a.off_stride;
-  const uint32_t my_off = lane <= nj ? offs[j0 + lane] : 0u;
-  const uint32_t my_off2 = lane + 64 <= nj ? offs[j0 + 64 + lane] : 0u;
-  auto off_of = [&](int i) -> uint32_t {
-    return i < 64 ? readlane_u32(my_off, i) : readlane_u32(my_off2, i - 64);
-  };
-  const int nib_shift = 4 * (lane & 7);
+  RecordStream<NCH, REC> rs;
+  rs.arena = a.arena + (uint64_t)s * a.arena_stride;
+  rs.stride = a.arena_stride;
+  rs.offs.load(a.off + (int64_t)s * a.off_stride, j0, nj, lane);
+  rs.nj = nj;
+  rs.lane = lane;
+  KB kb;
+  kb.init(plane, qs, lane);
+  bool corrupt = false;
+
+  for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
+    kb.set_queries(a.q, s, a.G, gq0);
+    auto process = [&](int jj, u32x4 (&pre)[NCH]) __attribute__((always_inline)) {
+      const int j = j0 + jj;
+      bool rok;
+      const uint32_t size = rs.size_of(jj, rok);
+      corrupt |= jj < nj && !rok;
+      const int n = jj < nj ? (int)imin64(B, a.n_tokens - (int64_t)j * B) : 0;
+      __syncthreads();
+      store_record<NCH>(rec, size, lane, pre);
+      rs.request(jj + 2, pre);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      float score[GT][NH];
+      const bool ok = kb.run(rec, size, (n + kR - 1) / kR, score) && rok;
+      corrupt |= rok && !ok;
+      // range-checked stores: slots past n, absent queries and corrupt
+      // records write nothing
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const uint32_t valid = ok ? (uint32_t)max(0, min(64, n - h * 64)) : 0u;
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+          const bool gok = gq0 + g < a.G;
+          float* row0 = a.scores + ((int64_t)s * a.G + (gok ? gq0 + g : 0)) * a.ld + (int64_t)j * B + h * 64;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score[g][h]),
+                                                buffer_rsrc(row0, gok ? 4u * valid : 0u), 4 * lane, 0, 0);
+        }
+      }
+    };
+    u32x4 pa[NCH], pb[NCH];
+    rs.request(0, pa);
+    __builtin_amdgcn_sched_barrier(0);
+    rs.request(1, pb);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int jj = 0; jj < nj; jj += 2) {
+      process(jj, pa);
+      process(jj + 1, pb);
+    }
+  }
+  if (corrupt && lane == 0) latch(a.status, PACKKV_ECORRUPT);
+}
+
+// Split-T reduction of the V GEMV and of fused attention: each workgroup
+// stores its partial results with device-coherent stores (they go past this
+// XCD's L2), waits for them, and takes a ticket from the stream's counter.
+// The workgroup that draws the last ticket is the only one that goes on: it
+// reads every partial back with device-coherent loads, sums them in split
+// order (so the result does not depend on which workgroup it is), and puts
+// the counter back to zero for the next call.  No cache write-back or
+// invalidation is needed; a release fence in every workgroup (an L2
+// write-back on this multi-XCD part) made the V GEMV three times slower.
+__device__ __forceinline__ void store_partial(float* dst, float v) {
+  __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_partial(const float* src) {
+  return __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool last_to_arrive(uint32_t* ticket, int splits, int lane) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0): partials stored
+  uint32_t t = 0;
+  if (lane == 0) t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  t = __builtin_amdgcn_readfirstlane(t);
+  return t == (uint32_t)splits - 1u;
+}
+__device__ __forceinline__ void reset_ticket(uint32_t* ticket, int lane) {
+  if (lane == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int B, int BITS, int GT>
+__global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
+  using VB = VBlock<B, BITS, GT>;
+  constexpr int NH = VB::NH;
+  constexpr int REC = max_record_bytes(true, B, 4);
+  constexpr int NCH = (REC + 1023) / 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t rec[REC + 16];
+  __shared__ __attribute__((aligned(16))) uint32_t dig[VB::DIG_WORDS];
+
+  const int lane = threadIdx.x;
+  const int s = blockIdx.x / a.splits;
+  const int split = blockIdx.x % a.splits;
+  const int j0 = split * a.blocks_per_wg;
+  const int nj = max(0, min(a.nb, j0 + a.blocks_per_wg) - j0);
+  RecordStream<NCH, REC> rs;
+  rs.arena = a.arena + (uint64_t)s * a.arena_stride;
+  rs.stride = a.arena_stride;
+  rs.offs.load(a.off + (int64_t)s * a.off_stride, j0, nj, lane);
+  rs.nj = nj;
+  rs.lane = lane;
+  VB vb;
+  vb.init(dig, lane);
   bool corrupt = false;
 
   for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
@@ -450,138 +644,54 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
     float pz[GT];
 #pragma unroll
     for (int g = 0; g < GT; ++g) { acc[g][0] = acc[g][1] = 0.f; pz[g] = 0.f; }
-    // weights of the lane's slots (slot h*64 + lane) for block j; zero past
-    // the valid slots, for absent queries, and when `valid` is false
-    auto load_p = [&](int j, bool valid, float (&pv)[GT][NH]) __attribute__((always_inline)) {
-      const int64_t left = a.n_tokens - (int64_t)j * B;
-      const uint32_t nbytes = valid && left > 0 ? 4u * (uint32_t)imin64(B, left) : 0u;
+    // weights of the lane's slots (slot h*64 + lane) for block jj; zero past
+    // the valid slots, for absent queries and missing blocks
+    auto load_p = [&](int jj, float (&pv)[GT][NH]) __attribute__((always_inline)) {
+      const bool in = jj < nj;
+      const int64_t left = a.n_tokens - (int64_t)(j0 + jj) * B;
+      const uint32_t nbytes = in && left > 0 ? 4u * (uint32_t)imin64(B, left) : 0u;
 #pragma unroll
       for (int g = 0; g < GT; ++g) {
         const bool gok = gq0 + g < a.G;
-        const float* src = a.p + ((int64_t)s * a.G + (gok ? gq0 + g : 0)) * a.ld + (int64_t)(valid ? j : 0) * B;
+        const float* src = a.p + ((int64_t)s * a.G + (gok ? gq0 + g : 0)) * a.ld + (int64_t)(in ? j0 + jj : 0) * B;
         const __amdgpu_buffer_rsrc_t r = buffer_rsrc(src, gok ? nbytes : 0u);
 #pragma unroll
         for (int h = 0; h < NH; ++h)
           pv[g][h] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 4 * (h * 64 + lane), 0, 0));
       }
     };
-    // two blocks in flight (record and weights), alternating register sets;
-    // a missing block (jj >= nj) is requested as zero bytes
     auto request = [&](int jj, u32x4 (&pre)[NCH], float (&pv)[GT][NH]) __attribute__((always_inline)) {
-      const bool in = jj < nj;
-      const uint32_t o = in ? off_of(jj) : 0u, size = in ? off_of(jj + 1) - o : 0u;
-      load_record<NCH>(arena + o, record_ok(o, size, a.arena_stride, REC) ? size : 0u, lane, pre);
-      load_p(j0 + jj, in, pv);
+      rs.request(jj, pre);
+      load_p(jj, pv);
     };
-    // The loop body has no exits (see the K GEMV): a missing or corrupt
-    // block contributes nothing.
     auto process = [&](int jj, u32x4 (&pre)[NCH], float (&pv)[GT][NH]) __attribute__((always_inline)) {
-      const bool in = jj < nj;
       const int j = j0 + jj;
-      const uint32_t o = in ? off_of(jj) : 0u, size0 = in ? off_of(jj + 1) - o : 0u;
-      const bool rok = record_ok(o, size0, a.arena_stride, REC);
-      corrupt |= in && !rok;
-      const uint32_t size = rok ? size0 : 0u;
-      const int n = in ? (int)imin64(B, a.n_tokens - (int64_t)j * B) : 0;
-      const int nr = (n + kR - 1) / kR;
+      bool rok;
+      const uint32_t size = rs.size_of(jj, rok);
+      corrupt |= jj < nj && !rok;
+      const int n = jj < nj ? (int)imin64(B, a.n_tokens - (int64_t)j * B) : 0;
       __syncthreads();
       store_record<NCH>(rec, size, lane, pre);
-      float pcur[GT][NH];
+      float pw[GT][NH];
 #pragma unroll
       for (int g = 0; g < GT; ++g)
 #pragma unroll
-        for (int h = 0; h < NH; ++h) pcur[g][h] = pv[g][h];
+        for (int h = 0; h < NH; ++h) pw[g][h] = pv[g][h];
       request(jj + 2, pre, pv);
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
-      // p' = p * scale per slot, sum p * zero, and the digit words of p'
-      int E[GT];
-      bool live[GT];
-      float pzb[GT];
-      {
-        const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec);
-        float pp[GT][NH];
-#pragma unroll
-        for (int g = 0; g < GT; ++g) pzb[g] = 0.f;
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          const int sl = h * 64 + lane;
-          const float scl = f16_bits_to_float(sc[sl]), zer = f16_bits_to_float(sc[B + sl]);
-#pragma unroll
-          for (int g = 0; g < GT; ++g) {
-            pp[g][h] = pcur[g][h] * scl;
-            pzb[g] = fmaf(pcur[g][h], zer, pzb[g]);
-          }
-        }
-#pragma unroll
-        for (int g = 0; g < GT; ++g) {
-          float mx = pp[g][0];
-#pragma unroll
-          for (int h = 1; h < NH; ++h) mx = fmaxf(mx, pp[g][h]);
-          const float M = wave_max_nonneg(mx);
-          live[g] = M > 0.f;
-          E[g] = live[g] ? 19 - ilogbf(M) : 0;          // M * 2^E in [2^19, 2^20)
-#pragma unroll
-          for (int h = 0; h < NH; ++h) {
-            const uint32_t P = min((uint32_t)(ldexpf(pp[g][h], E[g]) + 0.5f), 0xFFFFFu);
-#pragma unroll
-            for (int d = 0; d < ND; ++d) {
-              const uint32_t wv = or8(((P >> (4 * d)) & 15u) << nib_shift);
-              if ((lane & 7) == 0) dig[g][d][h * 8 + (lane >> 3)] = wv;
-            }
-          }
-        }
-      }
-      uint32_t nib[NRL][4];
-      const bool ok = Dec::decode(rec, size, nr, lane, nib) && rok;
+      const bool ok = vb.run(rec, size, (n + kR - 1) / kR, rok, pw, acc, pz);
       corrupt |= rok && !ok;
-      __syncthreads();
-#pragma unroll
-      for (int g = 0; g < GT; ++g) {
-        if (!ok || !live[g]) continue;
-        uint32_t sd[2][ND];
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-          for (int d = 0; d < ND; ++d) sd[ch][d] = 0u;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          if (r >= nr) break;
-          uint32_t W[ND][4];
-#pragma unroll
-          for (int d = 0; d < ND; ++d) {
-            const u32x4 t = *reinterpret_cast<const u32x4*>(&dig[g][d][4 * r]);
-            W[d][0] = t.x; W[d][1] = t.y; W[d][2] = t.z; W[d][3] = t.w;
-          }
-#pragma unroll
-          for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-              for (int d = 0; d < ND; ++d)
-                sd[ch][d] = __builtin_amdgcn_udot8(nib[2 * r + ch][kk], W[d][kk], sd[ch][d], false);
-        }
-        const float unit = ldexpf(1.0f, -E[g]);
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-          // each digit sum is <= NR*32*15*15 < 2^15, so the total stays below 2^32
-          uint32_t x = sd[ch][0] + (sd[ch][1] << 4) + (sd[ch][2] << 8) + (sd[ch][3] << 12) + (sd[ch][4] << 16);
-          acc[g][ch] = fmaf((float)x, unit, acc[g][ch]);
-        }
-      }
-#pragma unroll
-      for (int g = 0; g < GT; ++g)
-        if (ok) pz[g] += pzb[g];
     };
     u32x4 pa[NCH], pb[NCH];
-    float va[GT][NH], vb[GT][NH];
+    float va[GT][NH], vb2[GT][NH];
     request(0, pa, va);
     __builtin_amdgcn_sched_barrier(0);
-    request(1, pb, vb);
+    request(1, pb, vb2);
     __builtin_amdgcn_sched_barrier(0);
     for (int jj = 0; jj < nj; jj += 2) {
       process(jj, pa, va);
-      process(jj + 1, pb, vb);
+      process(jj + 1, pb, vb2);
     }
     // partial result of this split
 #pragma unroll
@@ -589,39 +699,209 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
       const float z = wave_sum(pz[g]);
       if (gq0 + g < a.G) {
         float* dst = a.ws + (((int64_t)s * a.G + gq0 + g) * a.splits + split) * kD;
-        __hip_atomic_store(dst + lane, acc[g][0] + z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(dst + lane + 64, acc[g][1] + z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        store_partial(dst + lane, acc[g][0] + z);
+        store_partial(dst + lane + 64, acc[g][1] + z);
       }
     }
   }
   if (corrupt && lane == 0) latch(a.status, PACKKV_ECORRUPT);
-
-  // Split-T reduction: the last workgroup of stream s to arrive sums the
-  // partials in split order (so the result does not depend on which one it
-  // is) and puts the stream's counter back to zero for the next call.
-  // The partials are written with device-coherent stores (they go past this
-  // XCD's L2) and the workgroup waits for them to complete before it takes
-  // its ticket; the last workgroup reads them back with device-coherent
-  // loads.  No cache write-back or invalidation is needed, which a release
-  // fence in every workgroup would cost.
-  __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0)
-  uint32_t ticket = 0;
-  if (lane == 0) ticket = __hip_atomic_fetch_add(&a.tickets[s], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  ticket = __builtin_amdgcn_readfirstlane(ticket);
-  if (ticket != (uint32_t)a.splits - 1u) return;
+  if (!last_to_arrive(&a.tickets[s], a.splits, lane)) return;
   for (int g = 0; g < a.G; ++g) {
     const float* src = a.ws + ((int64_t)s * a.G + g) * a.splits * kD;
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll 8
     for (int i = 0; i < a.splits; ++i) {
-      s0 += __hip_atomic_load(src + (int64_t)i * kD + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s1 += __hip_atomic_load(src + (int64_t)i * kD + lane + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s0 += load_partial(src + (int64_t)i * kD + lane);
+      s1 += load_partial(src + (int64_t)i * kD + lane + 64);
     }
     float* dst = a.out + ((int64_t)s * a.G + g) * kD;
     dst[lane] = s0;
     dst[lane + 64] = s1;
   }
-  if (lane == 0) __hip_atomic_store(&a.tickets[s], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  reset_ticket(&a.tickets[s], lane);
+}
+
+// ---------------------------------------------------------------------------
+// Fused decode attention:
+//
+//   out[g] = sum_t softmax_t(scale * q_g . K_hat[t]) V_hat[t]
+//
+// in one pass over both packed caches, with no scores or weights in HBM.
+// A workgroup takes J consecutive blocks of one stream and walks them in
+// pairs: the K records of blocks jj and jj+1 give their scores (KBlock), a
+// running-max softmax update turns them into weights exp(s - m) (earlier
+// sums are rescaled when m grows), and the V records of the same two blocks
+// take those weights (VBlock).  The record stream alternates K, K, V, V
+// through the same two register sets, two records in flight.  Each split
+// leaves (partial out[D], its max m, its weight sum l); the last workgroup of
+// the stream merges the splits in split order with the usual rescaling.
+__device__ __forceinline__ float wave_max_f(float v) {
+  // DPP with bound_ctrl off: lanes without a source keep their own value
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x111, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x112, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x114, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x118, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x142, 0xA, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x143, 0xC, 0xF, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+// 2^x without the range fix-ups of exp2f: arguments here are <= 0 and a
+// result that underflows is a weight of 0
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int B, int BITS, int GT>
+__global__ __launch_bounds__(64) void k_attn_decode(AttnArgs a) {
+  using KB = KBlock<B, BITS, GT>;
+  using VB = VBlock<B, BITS, GT>;
+  constexpr int NH = B / 64;
+  constexpr int REC_K = max_record_bytes(false, B, 4);
+  constexpr int REC_V = max_record_bytes(true, B, 4);
+  constexpr int REC = REC_K > REC_V ? REC_K : REC_V;
+  constexpr int NCH = (REC + 1023) / 1024;
+  constexpr int BUF = (REC + 16) > KB::RED_BYTES ? (REC + 16) : KB::RED_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t rec[BUF];
+  __shared__ __attribute__((aligned(16))) uint32_t plane[KB::PLANE_WORDS];
+  __shared__ __attribute__((aligned(16))) float qs[GT * kD];
+  __shared__ __attribute__((aligned(16))) uint32_t dig[VB::DIG_WORDS];
+
+  const int lane = threadIdx.x;
+  const int s = blockIdx.x / a.splits;
+  const int split = blockIdx.x % a.splits;
+  const int j0 = split * a.blocks_per_wg;
+  const int nj = max(0, min(a.nb, j0 + a.blocks_per_wg) - j0);
+  RecordStream<NCH, REC_K> ks;
+  ks.arena = a.k_arena + (uint64_t)s * a.arena_stride;
+  ks.stride = a.arena_stride;
+  ks.offs.load(a.k_off + (int64_t)s * a.off_stride, j0, nj, lane);
+  ks.nj = nj;
+  ks.lane = lane;
+  RecordStream<NCH, REC_V> vs;
+  vs.arena = a.v_arena + (uint64_t)s * a.arena_stride;
+  vs.stride = a.arena_stride;
+  vs.offs.load(a.v_off + (int64_t)s * a.off_stride, j0, nj, lane);
+  vs.nj = nj;
+  vs.lane = lane;
+  KB kb;
+  kb.init(plane, qs, lane);
+  VB vb;
+  vb.init(dig, lane);
+  bool corrupt = false;
+  const float NEG_INF = -__builtin_huge_valf();
+
+  for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
+    kb.set_queries(a.q, s, a.G, gq0);
+    float m[GT], l[GT], acc[GT][2], pz[GT];
+#pragma unroll
+    for (int g = 0; g < GT; ++g) { m[g] = NEG_INF; l[g] = 0.f; acc[g][0] = acc[g][1] = 0.f; pz[g] = 0.f; }
+
+    // K record of block jj: its scores (times scale * log2 e) in sc, -inf on
+    // slots past n or when the record is unusable; requests V of block jj
+    auto process_k = [&](int jj, u32x4 (&pre)[NCH], float (&sc)[GT][NH]) __attribute__((always_inline)) {
+      const int j = j0 + jj;
+      bool rok;
+      const uint32_t size = ks.size_of(jj, rok);
+      corrupt |= jj < nj && !rok;
+      const int n = jj < nj ? (int)imin64(B, a.n_tokens - (int64_t)j * B) : 0;
+      __syncthreads();
+      store_record<NCH>(rec, size, lane, pre);
+      vs.request(jj, pre);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      float score[GT][NH];
+      const bool ok = kb.run(rec, size, (n + kR - 1) / kR, score) && rok;
+      corrupt |= rok && !ok;
+#pragma unroll
+      for (int g = 0; g < GT; ++g)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          sc[g][h] = ok && h * 64 + lane < n ? score[g][h] * a.scale_log2e : NEG_INF;
+    };
+    // V record of block jj with weights pw; requests K of block jj + 2
+    auto process_v = [&](int jj, u32x4 (&pre)[NCH], const float (&pw)[GT][NH]) __attribute__((always_inline)) {
+      const int j = j0 + jj;
+      bool rok;
+      const uint32_t size = vs.size_of(jj, rok);
+      corrupt |= jj < nj && !rok;
+      const int n = jj < nj ? (int)imin64(B, a.n_tokens - (int64_t)j * B) : 0;
+      __syncthreads();
+      store_record<NCH>(rec, size, lane, pre);
+      ks.request(jj + 2, pre);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      const bool ok = vb.run(rec, size, (n + kR - 1) / kR, rok, pw, acc, pz);
+      corrupt |= rok && !ok;
+    };
+    u32x4 pa[NCH], pb[NCH];
+    ks.request(0, pa);
+    __builtin_amdgcn_sched_barrier(0);
+    ks.request(1, pb);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int jj = 0; jj < nj; jj += 2) {
+      float sa[GT][NH], sb[GT][NH];
+      process_k(jj, pa, sa);
+      process_k(jj + 1, pb, sb);
+      // running-max softmax update over the pair
+      float wa[GT][NH], wb[GT][NH];
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        float mx = fmaxf(sa[g][0], sb[g][0]);
+#pragma unroll
+        for (int h = 1; h < NH; ++h) mx = fmaxf(mx, fmaxf(sa[g][h], sb[g][h]));
+        const float mn = fmaxf(m[g], wave_max_f(mx));
+        const float alpha = mn == NEG_INF ? 1.f : fast_exp2(m[g] - mn);
+        acc[g][0] *= alpha;
+        acc[g][1] *= alpha;
+        pz[g] *= alpha;
+        l[g] *= alpha;
+        m[g] = mn;
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          wa[g][h] = mn == NEG_INF ? 0.f : fast_exp2(sa[g][h] - mn);
+          wb[g][h] = mn == NEG_INF ? 0.f : fast_exp2(sb[g][h] - mn);
+          l[g] += wa[g][h] + wb[g][h];
+        }
+      }
+      process_v(jj, pa, wa);
+      process_v(jj + 1, pb, wb);
+    }
+    // this split's partial: out sums, max, weight sum
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      const float z = wave_sum(pz[g]);
+      const float lsum = wave_sum(l[g]);
+      if (gq0 + g < a.G) {
+        float* dst = a.ws + (((int64_t)s * a.G + gq0 + g) * a.splits + split) * kAttnPartial;
+        store_partial(dst + lane, acc[g][0] + z);
+        store_partial(dst + lane + 64, acc[g][1] + z);
+        if (lane == 0) {
+          store_partial(dst + kD, m[g]);
+          store_partial(dst + kD + 1, lsum);
+        }
+      }
+    }
+  }
+  if (corrupt && lane == 0) latch(a.status, PACKKV_ECORRUPT);
+  if (!last_to_arrive(&a.tickets[s], a.splits, lane)) return;
+  for (int g = 0; g < a.G; ++g) {
+    const float* src = a.ws + ((int64_t)s * a.G + g) * a.splits * kAttnPartial;
+    float M = NEG_INF, L = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int i = 0; i < a.splits; ++i) {
+      const float* part = src + (int64_t)i * kAttnPartial;
+      const float mi = load_partial(part + kD), li = load_partial(part + kD + 1);
+      const float a0 = load_partial(part + lane), a1 = load_partial(part + lane + 64);
+      const float mn = fmaxf(M, mi);
+      if (mn == NEG_INF) continue;                 // nothing valid yet
+      const float fo = fast_exp2(M - mn), fi = fast_exp2(mi - mn);
+      L = L * fo + li * fi;
+      o0 = o0 * fo + a0 * fi;
+      o1 = o1 * fo + a1 * fi;
+      M = mn;
+    }
+    float* dst = a.out + ((int64_t)s * a.G + g) * kD;
+    dst[lane] = o0 / L;
+    dst[lane + 64] = o1 / L;
+  }
+  reset_ticket(&a.tickets[s], lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -819,6 +1099,24 @@ hipError_t launch_pv(const GemvArgs& a, int B, int n_streams, hipStream_t st) {
     case 128 * 8 + 2: pv_launch<128, 2>(a, grid, st); break;
     case 128 * 8 + 3: pv_launch<128, 3>(a, grid, st); break;
     default: pv_launch<128, 4>(a, grid, st); break;
+  }
+  return hipGetLastError();
+}
+
+template <int B, int BITS>
+static void attn_launch(const AttnArgs& a, dim3 grid, hipStream_t st) {
+  if (a.G == 1) hipLaunchKernelGGL((k_attn_decode<B, BITS, 1>), grid, dim3(64), 0, st, a);
+  else hipLaunchKernelGGL((k_attn_decode<B, BITS, 4>), grid, dim3(64), 0, st, a);
+}
+hipError_t launch_attention(const AttnArgs& a, int B, int n_streams, hipStream_t st) {
+  const dim3 grid(n_streams * a.splits);
+  switch (B * 8 + a.bits) {
+    case 64 * 8 + 2: attn_launch<64, 2>(a, grid, st); break;
+    case 64 * 8 + 3: attn_launch<64, 3>(a, grid, st); break;
+    case 64 * 8 + 4: attn_launch<64, 4>(a, grid, st); break;
+    case 128 * 8 + 2: attn_launch<128, 2>(a, grid, st); break;
+    case 128 * 8 + 3: attn_launch<128, 3>(a, grid, st); break;
+    default: attn_launch<128, 4>(a, grid, st); break;
   }
   return hipGetLastError();
 }

@@ -49,6 +49,29 @@ struct GemvArgs {
 };
 
 
+// Fused decode attention over both packed caches of a cache object.
+struct AttnArgs {
+  const uint8_t* k_arena;
+  const uint8_t* v_arena;
+  uint64_t arena_stride;
+  const uint32_t* k_off;
+  const uint32_t* v_off;
+  int64_t off_stride;
+  int64_t n_tokens;
+  int32_t nb;
+  int32_t bits;
+  int32_t blocks_per_wg;
+  int32_t splits;
+  int32_t G;
+  float scale_log2e;     // softmax scale times log2(e)
+  const uint16_t* q;     // [S][G][D] fp16
+  float* ws;             // partials [S][G][splits][kAttnPartial]
+  uint32_t* tickets;     // per-stream arrival counters, zero between calls
+  float* out;            // [S][G][D]
+  int32_t* status;
+};
+constexpr int kAttnPartial = 132;   // D partial sums, running max, weight sum, 2 pad
+
 hipError_t launch_encode(const EncArgs& a, int n_streams, int n_blocks, hipStream_t st);
 hipError_t launch_scan_offsets(uint32_t* k_off, uint32_t* v_off, int64_t off_stride,
                                int n_streams, int nb, hipStream_t st);
@@ -57,6 +80,7 @@ hipError_t launch_stage_tail(const uint16_t* k, const uint16_t* v, int64_t src_s
                              int n_streams, hipStream_t st);
 hipError_t launch_qk(const GemvArgs& a, int B, int n_streams, hipStream_t st);
 hipError_t launch_pv(const GemvArgs& a, int B, int n_streams, hipStream_t st);
+hipError_t launch_attention(const AttnArgs& a, int B, int n_streams, hipStream_t st);
 hipError_t launch_decompress(const GemvArgs& a, int B, bool is_v, int n_streams, const uint8_t* perm,
                              int64_t perm_stride, int mode, void* out, hipStream_t st);
 hipError_t launch_stats(const GemvArgs& a, int B, bool is_v, int n_streams, unsigned long long* out,

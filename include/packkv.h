@@ -184,6 +184,32 @@ int packkv_pv_gemv(const packkv_cache_t* cache, const float* p, int64_t ld, int3
                    float* out, void* workspace, uint64_t ws_bytes, void* stream);
 
 /*
+ * packkv_attention_decode - decode attention in one pass over both packed
+ * caches: out[s][g] = sum_t softmax_t(scale * q[s][g] . K_hat[s][t]) *
+ * V_hat[s][t] over the stream's n_tokens slots (Fig. 1 caption: scores,
+ * softmax, weighted sum of V; TL;DR: decompression fused into the products so
+ * that nothing decompressed is written back).  It is the K GEMV, the softmax
+ * and the V GEMV fused: no scores or weights reach memory.
+ *   q_f16:     device fp16 [S][group][D].
+ *   scale:     softmax scale (e.g. 1/sqrt(D)), finite and > 0.
+ *   out:       device fp32 [S][group][D].
+ *   workspace: device memory of at least
+ *              packkv_attention_workspace_bytes(cache, group) bytes
+ *              (ws_bytes), caller-owned: per split partial sums with their
+ *              running max and weight sum, then one counter per stream,
+ *              which must be zero when a workspace is first used (allocate
+ *              it zero-filled); every call leaves them zero.  Calls that
+ *              share a workspace must not run concurrently.
+ * The splits are merged in a fixed order, so results are bitwise
+ * reproducible.  Single kernel launch.  Errors as for the GEMVs.
+ */
+int packkv_attention_decode(const packkv_cache_t* cache, const void* q_f16, int32_t group, float scale,
+                            float* out, void* workspace, uint64_t ws_bytes, void* stream);
+
+/* Bytes of workspace packkv_attention_decode needs for `group` queries. */
+uint64_t packkv_attention_workspace_bytes(const packkv_cache_t* cache, int32_t group);
+
+/*
  * packkv_decompress - decode the cache (test and debug path).
  *   which: 0 = K, 1 = V.
  *   mode 0: out is uint8 [S][n_tokens][D], the quantised ints q in SLOT order.

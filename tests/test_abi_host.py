@@ -81,6 +81,15 @@ def test_invalid_arguments_fail_before_any_launch(lib):
     assert lib.packkv_append_tokens(ctypes.byref(c3), fake, fake, 51, None) == _lib.ECAPACITY
     assert lib.packkv_decompress(ctypes.byref(c3), 2, 0, fake, None) == _lib.EINVAL
     assert lib.packkv_pv_gemv(ctypes.byref(c3), fake, 50, 1, fake, fake, 0, None) == _lib.EINVAL
+    need = lib.packkv_attention_workspace_bytes(ctypes.byref(c3), 1)
+    assert need > 0
+    assert lib.packkv_attention_decode(ctypes.byref(c3), None, 1, 0.1, fake, fake, need, None) == _lib.EINVAL
+    assert lib.packkv_attention_decode(ctypes.byref(c3), fake, 0, 0.1, fake, fake, need, None) == _lib.EINVAL
+    assert lib.packkv_attention_decode(ctypes.byref(c3), fake, 1, 0.0, fake, fake, need, None) == _lib.EINVAL
+    assert lib.packkv_attention_decode(ctypes.byref(c3), fake, 1, float("nan"), fake, fake, need, None) == _lib.EINVAL
+    assert lib.packkv_attention_decode(ctypes.byref(c3), fake, 1, 0.1, fake, fake, need - 1, None) == _lib.EINVAL
+    c3.n_tokens = 0
+    assert lib.packkv_attention_decode(ctypes.byref(c3), fake, 1, 0.1, fake, fake, need, None) == _lib.ESTATE
 
 
 def test_status_strings(lib):

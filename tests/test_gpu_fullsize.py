@@ -129,6 +129,14 @@ def test_fullsize_workload(torch_dev, name):
     assert rel_l2(scores[s], ref_sc) <= TOL, (rel_l2(scores[s], ref_sc), worst_row_rel(scores[s], ref_sc))
     ref_out = attention.pv(p[s].astype(np.float64), vh)
     assert rel_l2(out[s], ref_out) <= TOL, (rel_l2(out[s], ref_out), worst_row_rel(out[s], ref_out))
+    say("fullsize fused attention", name)
+    fused = c.attention(torch.from_numpy(q).to(dev)).cpu().numpy()
+    assert c.check() == 0
+    assert np.all(np.isfinite(fused))
+    ref_att = attention.pv(attention.softmax(ref_sc, D), vh)
+    assert rel_l2(fused[s], ref_att) <= TOL, (rel_l2(fused[s], ref_att), worst_row_rel(fused[s], ref_att))
+    # every stream: the fused path agrees with GEMV -> softmax -> GEMV
+    assert rel_l2(fused, out) <= TOL, rel_l2(fused, out)
 
 
 def test_fullsize_streaming_append(torch_dev):
@@ -169,5 +177,10 @@ def test_fullsize_streaming_append(torch_dev):
         p = p_d.cpu().numpy()
         assert np.all(np.isfinite(scores)) and np.all(np.isfinite(out))
         kh, vh, _, _ = ostream.decode_stream(ref)
-        assert rel_l2(scores[s], attention.qk(q[s], kh)) <= TOL
+        ref_sc = attention.qk(q[s], kh)
+        assert rel_l2(scores[s], ref_sc) <= TOL
         assert rel_l2(out[s], attention.pv(p[s].astype(np.float64), vh)) <= TOL
+        fused = c.attention(torch.from_numpy(q).to(dev)).cpu().numpy()
+        assert c.check() == 0
+        assert rel_l2(fused[s], attention.pv(attention.softmax(ref_sc, D), vh)) <= TOL
+        assert rel_l2(fused, out) <= TOL

@@ -228,3 +228,40 @@ def test_pv_weight_laws(torch_dev, law):
     assert c.check() == 0
     ref = np.stack([attention.pv(p[s].astype(np.float64), ostream.decode_stream(refs[s])[1]) for s in range(S)])
     assert rel_l2(out, ref) <= TOL, (rel_l2(out, ref), worst_row_rel(out, ref))
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("G", [1, 3, 4])
+def test_fused_attention_within_tolerance(torch_dev, case, G):
+    """Fused K GEMV + softmax + V GEMV against the fp64 oracle's three steps."""
+    torch, dev = torch_dev
+    cid, bits, block, S, T, permute, law = case
+    K, V = make_kv(law, S, T, block)
+    refs = oracle_streams(K, V, bits, block, permute)
+    c = gpu_cache(torch, dev, K, V, bits, block, permute)
+    rng = np.random.default_rng(100 + G)
+    q = (rng.standard_normal((S, G, 128)) * 2).astype(np.float16)
+    say("attention", cid, "G", G)
+    out = c.attention(torch.from_numpy(q).to(dev)).cpu().numpy()
+    assert c.check() == 0
+    ref = []
+    for s in range(S):
+        kh, vh, _, _ = ostream.decode_stream(refs[s])
+        ref.append(attention.pv(attention.softmax(attention.qk(q[s], kh), 128), vh))
+    ref = np.stack(ref)
+    assert rel_l2(out, ref) <= TOL, (rel_l2(out, ref), worst_row_rel(out, ref))
+
+
+def test_fused_attention_is_bitwise_reproducible_and_reuses_its_workspace(torch_dev):
+    torch, dev = torch_dev
+    K, V = make_kv("gauss", 2, 1000, 64)
+    c = gpu_cache(torch, dev, K, V, 4, 64, True)
+    q = torch.from_numpy(np.random.default_rng(5).standard_normal((2, 4, 128)).astype(np.float16)).to(dev)
+    say("attention determinism")
+    a = c.attention(q).clone()
+    b = c.attention(q).clone()
+    assert torch.equal(a, b)
+    # the per-stream counters are back at zero after every call
+    ws = c.attention_workspace(4)
+    tail = ws[-256:].view(torch.int32)[:2].cpu().numpy()
+    assert np.all(tail == 0)
