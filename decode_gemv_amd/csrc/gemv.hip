@@ -727,14 +727,14 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
 //   out[g] = sum_t softmax_t(scale * q_g . K_hat[t]) V_hat[t]
 //
 // in one pass over both packed caches, with no scores or weights in HBM.
-// A workgroup takes J consecutive blocks of one stream and walks them in
-// pairs: the K records of blocks jj and jj+1 give their scores (KBlock), a
-// running-max softmax update turns them into weights exp(s - m) (earlier
-// sums are rescaled when m grows), and the V records of the same two blocks
-// take those weights (VBlock).  The record stream alternates K, K, V, V
-// through the same two register sets, two records in flight.  Each split
-// leaves (partial out[D], its max m, its weight sum l); the last workgroup of
-// the stream merges the splits in split order with the usual rescaling.
+// A workgroup takes J consecutive blocks of one stream.  For each block the
+// K record gives the scores (KBlock), a running-max softmax update turns
+// them into weights exp(s - m) (earlier sums are rescaled when m grows), and
+// the V record of the same block takes those weights (VBlock).  The record
+// stream alternates K, V, K, V with the next record always in flight.  Each
+// split leaves (partial out[D], its max m, its weight sum l); the last
+// workgroup of the stream merges the splits in split order with the usual
+// rescaling.
 __device__ __forceinline__ float wave_max_f(float v) {
   // DPP with bound_ctrl off: lanes without a source keep their own value
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x111, 0xF, 0xF, false)));
@@ -794,59 +794,43 @@ __global__ __launch_bounds__(64) void k_attn_decode(AttnArgs a) {
 #pragma unroll
     for (int g = 0; g < GT; ++g) { m[g] = NEG_INF; l[g] = 0.f; acc[g][0] = acc[g][1] = 0.f; pz[g] = 0.f; }
 
-    // K record of block jj: its scores (times scale * log2 e) in sc, -inf on
-    // slots past n or when the record is unusable; requests V of block jj
-    auto process_k = [&](int jj, u32x4 (&pre)[NCH], float (&sc)[GT][NH]) __attribute__((always_inline)) {
+    // One record in flight: K of block jj requests V of block jj, which
+    // requests K of block jj + 1 (a second register set would push the
+    // kernel past 128 VGPRs and halve its occupancy).
+    u32x4 pre[NCH];
+    ks.request(0, pre);
+    for (int jj = 0; jj < nj; ++jj) {
       const int j = j0 + jj;
-      bool rok;
-      const uint32_t size = ks.size_of(jj, rok);
-      corrupt |= jj < nj && !rok;
-      const int n = jj < nj ? (int)imin64(B, a.n_tokens - (int64_t)j * B) : 0;
-      __syncthreads();
-      store_record<NCH>(rec, size, lane, pre);
-      vs.request(jj, pre);
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      float score[GT][NH];
-      const bool ok = kb.run(rec, size, (n + kR - 1) / kR, score) && rok;
-      corrupt |= rok && !ok;
+      const int n = (int)imin64(B, a.n_tokens - (int64_t)j * B);
+      const int nr = (n + kR - 1) / kR;
+      // K: scores of the block, times scale * log2(e); -inf past n or when
+      // the record is unusable
+      float sc[GT][NH];
+      {
+        bool rok;
+        const uint32_t size = ks.size_of(jj, rok);
+        corrupt |= !rok;
+        __syncthreads();
+        store_record<NCH>(rec, size, lane, pre);
+        vs.request(jj, pre);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        float score[GT][NH];
+        const bool ok = kb.run(rec, size, nr, score) && rok;
+        corrupt |= rok && !ok;
 #pragma unroll
-      for (int g = 0; g < GT; ++g)
+        for (int g = 0; g < GT; ++g)
 #pragma unroll
-        for (int h = 0; h < NH; ++h)
-          sc[g][h] = ok && h * 64 + lane < n ? score[g][h] * a.scale_log2e : NEG_INF;
-    };
-    // V record of block jj with weights pw; requests K of block jj + 2
-    auto process_v = [&](int jj, u32x4 (&pre)[NCH], const float (&pw)[GT][NH]) __attribute__((always_inline)) {
-      const int j = j0 + jj;
-      bool rok;
-      const uint32_t size = vs.size_of(jj, rok);
-      corrupt |= jj < nj && !rok;
-      const int n = jj < nj ? (int)imin64(B, a.n_tokens - (int64_t)j * B) : 0;
-      __syncthreads();
-      store_record<NCH>(rec, size, lane, pre);
-      ks.request(jj + 2, pre);
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      const bool ok = vb.run(rec, size, (n + kR - 1) / kR, rok, pw, acc, pz);
-      corrupt |= rok && !ok;
-    };
-    u32x4 pa[NCH], pb[NCH];
-    ks.request(0, pa);
-    __builtin_amdgcn_sched_barrier(0);
-    ks.request(1, pb);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int jj = 0; jj < nj; jj += 2) {
-      float sa[GT][NH], sb[GT][NH];
-      process_k(jj, pa, sa);
-      process_k(jj + 1, pb, sb);
-      // running-max softmax update over the pair
-      float wa[GT][NH], wb[GT][NH];
+          for (int h = 0; h < NH; ++h)
+            sc[g][h] = ok && h * 64 + lane < n ? score[g][h] * a.scale_log2e : NEG_INF;
+      }
+      // running-max softmax update: weights exp(s - m), earlier sums rescaled
+      float w[GT][NH];
 #pragma unroll
       for (int g = 0; g < GT; ++g) {
-        float mx = fmaxf(sa[g][0], sb[g][0]);
+        float mx = sc[g][0];
 #pragma unroll
-        for (int h = 1; h < NH; ++h) mx = fmaxf(mx, fmaxf(sa[g][h], sb[g][h]));
+        for (int h = 1; h < NH; ++h) mx = fmaxf(mx, sc[g][h]);
         const float mn = fmaxf(m[g], wave_max_f(mx));
         const float alpha = mn == NEG_INF ? 1.f : fast_exp2(m[g] - mn);
         acc[g][0] *= alpha;
@@ -856,13 +840,23 @@ __global__ __launch_bounds__(64) void k_attn_decode(AttnArgs a) {
         m[g] = mn;
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
-          wa[g][h] = mn == NEG_INF ? 0.f : fast_exp2(sa[g][h] - mn);
-          wb[g][h] = mn == NEG_INF ? 0.f : fast_exp2(sb[g][h] - mn);
-          l[g] += wa[g][h] + wb[g][h];
+          w[g][h] = mn == NEG_INF ? 0.f : fast_exp2(sc[g][h] - mn);
+          l[g] += w[g][h];
         }
       }
-      process_v(jj, pa, wa);
-      process_v(jj + 1, pb, wb);
+      // V: the weighted sum of the block's values
+      {
+        bool rok;
+        const uint32_t size = vs.size_of(jj, rok);
+        corrupt |= !rok;
+        __syncthreads();
+        store_record<NCH>(rec, size, lane, pre);
+        ks.request(jj + 1, pre);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        const bool ok = vb.run(rec, size, nr, rok, w, acc, pz);
+        corrupt |= rok && !ok;
+      }
     }
     // this split's partial: out sums, max, weight sum
 #pragma unroll
