@@ -267,16 +267,20 @@ struct KBlock {
   static constexpr int NRL = Dec::NRL;
   static constexpr int NH = B / 64;
   static constexpr int ROWW = kD + 8;
-  static constexpr int PLANE_WORDS = (B / 8) * ROWW;
+  static constexpr int PLANE_BYTES = (B / 8) * ROWW * 4;
   static constexpr int RED_BYTES = GT * 64 * 9 * 4;   // channel-group reduction
+  // The plane and the reduction buffer live in the record's staging buffer:
+  // once a record is decoded into registers its bytes are dead.  With two
+  // 64-slot halves the first half's reduction must not overwrite the second
+  // half's plane rows, so it goes after the plane.
+  static constexpr int SCRATCH_BYTES =
+      NH == 1 ? (PLANE_BYTES > RED_BYTES ? PLANE_BYTES : RED_BYTES) : PLANE_BYTES + RED_BYTES;
 
-  uint32_t* plane;
   float* qs;                                          // [GT][D] q' of the block
   int lane, g8, cg;
   float qa[GT], qb[GT], qau[GT], qbu[GT];             // queries at channels lane, lane + 64
 
-  __device__ __forceinline__ void init(uint32_t* plane_, float* qs_, int lane_) {
-    plane = plane_;
+  __device__ __forceinline__ void init(float* qs_, int lane_) {
     qs = qs_;
     lane = lane_;
     g8 = lane & 7;
@@ -295,18 +299,11 @@ struct KBlock {
     }
   }
 
-  // rec: the staged record (size bytes, nr runs); afterwards it serves as the
-  // reduction buffer.  Returns whether the record decoded consistently.
+  // rec: the staged record (size bytes, nr runs); it is overwritten by the
+  // plane and the reduction.  Returns whether the record decoded
+  // consistently.
   __device__ __forceinline__ bool run(uint8_t* rec, uint32_t size, int nr, float (&score)[GT][NH]) {
-    uint32_t nib[NRL][4];
-    const bool ok = Dec::decode(rec, size, nr, lane, nib);
-#pragma unroll
-    for (int k = 0; k < NRL; ++k) {
-      const int r = k >> 1, c = lane + 64 * (k & 1);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) plane[(r * 4 + kk) * ROWW + c] = nib[k][kk];
-    }
-    // q' = q * scale (per channel), beta = q . zero
+    // q' = q * scale (per channel) and beta = q . zero, before the bytes go
     float beta[GT];
     {
       const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec);
@@ -319,8 +316,18 @@ struct KBlock {
         beta[g] = wave_sum(fmaf(qa[g], za, qb[g] * zb));
       }
     }
+    uint32_t nib[NRL][4];
+    const bool ok = Dec::decode(rec, size, nr, lane, nib);
+    __syncthreads();                                  // every lane has read the record
+    uint32_t* plane = reinterpret_cast<uint32_t*>(rec);
+    float* red = reinterpret_cast<float*>(rec + (NH == 1 ? 0 : PLANE_BYTES));
+#pragma unroll
+    for (int k = 0; k < NRL; ++k) {
+      const int r = k >> 1, c = lane + 64 * (k & 1);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) plane[(r * 4 + kk) * ROWW + c] = nib[k][kk];
+    }
     __syncthreads();
-    float* red = reinterpret_cast<float*>(rec);
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       float acc[GT][8];
@@ -331,6 +338,8 @@ struct KBlock {
       const int row = h * 8 + g8;
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
+        // rotate the quad order per channel group: with the 136-word row
+        // pitch, 16 lanes of a 16-byte read then cover all 64 banks once
         const int c0 = cg * 16 + ((i4 + cg) & 3) * 4;
         const u32x4 nw = *reinterpret_cast<const u32x4*>(&plane[row * ROWW + c0]);
         const uint32_t words[4] = {nw.x, nw.y, nw.z, nw.w};
@@ -526,9 +535,8 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
   constexpr int NH = KB::NH;
   constexpr int REC = max_record_bytes(false, B, 4);
   constexpr int NCH = (REC + 1023) / 1024;
-  constexpr int BUF = (REC + 16) > KB::RED_BYTES ? (REC + 16) : KB::RED_BYTES;
+  constexpr int BUF = (REC + 16) > KB::SCRATCH_BYTES ? (REC + 16) : KB::SCRATCH_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t rec[BUF];
-  __shared__ __attribute__((aligned(16))) uint32_t plane[KB::PLANE_WORDS];
   __shared__ __attribute__((aligned(16))) float qs[GT * kD];
 
   const int lane = threadIdx.x;
@@ -543,7 +551,7 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
   rs.nj = nj;
   rs.lane = lane;
   KB kb;
-  kb.init(plane, qs, lane);
+  kb.init(qs, lane);
   bool corrupt = false;
 
   for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
@@ -758,9 +766,8 @@ __global__ __launch_bounds__(64) void k_attn_decode(AttnArgs a) {
   constexpr int REC_V = max_record_bytes(true, B, 4);
   constexpr int REC = REC_K > REC_V ? REC_K : REC_V;
   constexpr int NCH = (REC + 1023) / 1024;
-  constexpr int BUF = (REC + 16) > KB::RED_BYTES ? (REC + 16) : KB::RED_BYTES;
+  constexpr int BUF = (REC + 16) > KB::SCRATCH_BYTES ? (REC + 16) : KB::SCRATCH_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t rec[BUF];
-  __shared__ __attribute__((aligned(16))) uint32_t plane[KB::PLANE_WORDS];
   __shared__ __attribute__((aligned(16))) float qs[GT * kD];
   __shared__ __attribute__((aligned(16))) uint32_t dig[VB::DIG_WORDS];
 
@@ -782,7 +789,7 @@ __global__ __launch_bounds__(64) void k_attn_decode(AttnArgs a) {
   vs.nj = nj;
   vs.lane = lane;
   KB kb;
-  kb.init(plane, qs, lane);
+  kb.init(qs, lane);
   VB vb;
   vb.init(dig, lane);
   bool corrupt = false;
