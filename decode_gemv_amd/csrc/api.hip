@@ -152,6 +152,7 @@ int packkv_compress_block(packkv_cache_t* c, const void* k_f16, const void* v_f1
   int e = check_cache(c);
   if (e) return e;
   if (!k_f16 || !v_f16 || n_tokens < 1) return PACKKV_EINVAL;
+  if (((uintptr_t)k_f16 | (uintptr_t)v_f16) & 15u) return PACKKV_EINVAL;   // read with 16-byte loads
   if (c->n_tokens != 0) return PACKKV_ESTATE;
   if (n_tokens > c->max_tokens) return PACKKV_ECAPACITY;
   hipStream_t st = (hipStream_t)stream;

@@ -35,45 +35,69 @@ __device__ uint32_t min_f16_step(double d, int L) {
   return h;
 }
 
-__device__ __forceinline__ bool f16_less(uint32_t a, uint32_t b) {
-  return f16_bits_to_double(a) < f16_bits_to_double(b);
+// Order-preserving integer key of an fp16 value (not NaN): -0 and +0 share
+// key 0, so comparing keys is comparing values.
+__device__ __forceinline__ int f16_key(uint32_t h) {
+  return (h & 0x8000u) ? -(int)(h & 0x7FFFu) : (int)(h & 0x7FFFu);
+}
+__device__ __forceinline__ uint32_t f16_of_key(int k) {
+  return k < 0 ? (0x8000u | (uint32_t)(-k)) : (uint32_t)k;   // key 0 -> +0
 }
 
-// Quantise one group of `cnt` fp16 values (stride `st` in `src`) into q[i*qs].
-__device__ void quant_group(const uint16_t* src, int cnt, int st, int L,
-                            uint8_t* q, int qs, uint16_t* scale_out, uint16_t* zero_out) {
-  uint32_t mnb = src[0], mxb = src[0];
-  for (int i = 1; i < cnt; ++i) {
-    uint32_t x = src[(int64_t)i * st];
-    if (f16_less(x, mnb)) mnb = x;
-    if (f16_less(mxb, x)) mxb = x;
-  }
-  const double mn = f16_bits_to_double(mnb), mx = f16_bits_to_double(mxb);
-  const double d = mx - mn;
-  const uint32_t hb = d > 0.0 ? min_f16_step(d, L) : 0u;
-  const double h = f16_bits_to_double(hb);
-  *scale_out = (uint16_t)hb;
-  *zero_out = (uint16_t)(mn == 0.0 ? 0u : mnb);
-  for (int i = 0; i < cnt; ++i) {
-    uint32_t qq = 0;
-    if (hb) {
-      double r = rint((f16_bits_to_double(src[(int64_t)i * st]) - mn) / h);
-      r = r < 0.0 ? 0.0 : (r > (double)L ? (double)L : r);
-      qq = (uint32_t)r;
-    }
-    q[i * qs] = (uint8_t)qq;
+// Step and zero of a group from its min and max keys (the oracle's rule).
+struct QuantParams {
+  double mn, h;
+  uint32_t hb, zero;
+};
+__device__ __forceinline__ QuantParams quant_params(int kmin, int kmax, int L) {
+  QuantParams p;
+  const uint32_t mnb = f16_of_key(kmin), mxb = f16_of_key(kmax);
+  p.mn = f16_bits_to_double(mnb);
+  const double d = f16_bits_to_double(mxb) - p.mn;
+  p.hb = d > 0.0 ? min_f16_step(d, L) : 0u;
+  p.h = f16_bits_to_double(p.hb);
+  p.zero = mnb;                                      // +0 for a zero minimum
+  return p;
+}
+// Level of one value: round half to even of the exact quotient (the fp64
+// subtraction is exact and the division correctly rounded), clamped to [0, L].
+__device__ __forceinline__ uint32_t quant_level(uint32_t x, const QuantParams& p, int L) {
+  if (!p.hb) return 0u;
+  double r = rint((f16_bits_to_double(x) - p.mn) / p.h);
+  r = r < 0.0 ? 0.0 : (r > (double)L ? (double)L : r);
+  return (uint32_t)r;
+}
+
+// The ints of run r, channel c in slot order: v[i] = q[order[r*32 + i]][c]
+// (0 past the n slots).  The run's 32 order bytes are read first as eight
+// words, so the 32 value reads do not wait on one another.
+__device__ __forceinline__ void run_values(const uint8_t* q, const uint8_t* order, int r, int c, int n,
+                                           uint32_t v[kR]) {
+  const int s0 = r * kR;
+  const uint32_t* o4 = reinterpret_cast<const uint32_t*>(order + s0);
+  uint32_t ow[kR / 4];
+#pragma unroll
+  for (int k = 0; k < kR / 4; ++k) ow[k] = o4[k];
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    const uint32_t t = (ow[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+    v[i] = s0 + i < n ? (uint32_t)q[t * kD + c] : 0u;
   }
 }
 
 // Min and width of run r, channel c of the slot-ordered ints q[order[slot]][c].
 __device__ __forceinline__ void run_stats(const uint8_t* q, const uint8_t* order, int r, int c,
                                           int n, uint32_t& m, uint32_t& w) {
-  const int s0 = r * kR, s1 = min(n, s0 + kR);
+  uint32_t v[kR];
+  run_values(q, order, r, c, n, v);
+  const int cnt = min(kR, n - r * kR);
   uint32_t lo = 255, hi = 0;
-  for (int sl = s0; sl < s1; ++sl) {
-    uint32_t x = q[order[sl] * kD + c];
-    lo = min(lo, x);
-    hi = max(hi, x);
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    if (i < cnt) {
+      lo = min(lo, v[i]);
+      hi = max(hi, v[i]);
+    }
   }
   m = lo;
   w = 32u - __clz(hi - lo);
@@ -101,7 +125,9 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
   __shared__ uint8_t qk[128 * kD];
   __shared__ uint8_t qv[128 * kD];
   __shared__ uint16_t ksc[kD], kze[kD], vsc[128], vze[128];
-  __shared__ uint8_t order[128], ident[128], alive[128];
+  __shared__ __attribute__((aligned(16))) uint8_t order[128];
+  __shared__ __attribute__((aligned(16))) uint8_t ident[128];
+  __shared__ uint8_t alive[128];
   __shared__ uint32_t key[128];
   __shared__ uint8_t wk[4 * kD], mk[4 * kD], wv[4 * kD], mv[4 * kD];
   __shared__ uint32_t scan_sh[NT];
@@ -118,12 +144,80 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
   const uint16_t* ks = a.k + s * a.src_stream + (a.mode == kTail ? 0 : j * a.src_block);
   const uint16_t* vs = a.v + s * a.src_stream + (a.mode == kTail ? 0 : j * a.src_block);
 
-  // (1) quantise: K per channel over the block's tokens, V per token.
+  // (1) quantise.  K per channel over the block's tokens: thread c walks its
+  // channel in batches of 16 independent loads (one memory latency per
+  // batch), once for the range and once for the levels.
   if (tid < kD) {
-    quant_group(ks + tid, n, kD, L, qk + tid, kD, &ksc[tid], &kze[tid]);
-  } else if (tid - kD < n) {
-    const int t = tid - kD;
-    quant_group(vs + (int64_t)t * kD, kD, 1, L, qv + t * kD, 1, &vsc[t], &vze[t]);
+    constexpr int KB = 16;
+    int kmin = 0x7FFF, kmax = -0x7FFF;
+    for (int t0 = 0; t0 < n; t0 += KB) {
+      uint32_t x[KB];
+#pragma unroll
+      for (int i = 0; i < KB; ++i) x[i] = ks[(int64_t)min(t0 + i, n - 1) * kD + tid];
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        const int k = f16_key(x[i]);
+        kmin = min(kmin, k);
+        kmax = max(kmax, k);
+      }
+    }
+    const QuantParams qp = quant_params(kmin, kmax, L);
+    ksc[tid] = (uint16_t)qp.hb;
+    kze[tid] = (uint16_t)qp.zero;
+    for (int t0 = 0; t0 < n; t0 += KB) {
+      uint32_t x[KB];
+#pragma unroll
+      for (int i = 0; i < KB; ++i) x[i] = ks[(int64_t)min(t0 + i, n - 1) * kD + tid];
+#pragma unroll
+      for (int i = 0; i < KB; ++i)
+        if (t0 + i < n) qk[(t0 + i) * kD + tid] = (uint8_t)quant_level(x[i], qp, L);
+    }
+  }
+  // V per token: the 128 channels of token t are split over TPT neighbouring
+  // threads, each loading its CPT values with 16-byte loads; min and max are
+  // combined across the TPT threads.
+  {
+    const int TPT = NT / B;                          // 4 (B = 64) or 2 (B = 128)
+    const int CPT = kD / TPT;                        // 32 or 64 channels per thread
+    const int t = tid / TPT, part = tid % TPT;
+    const bool on = t < n;
+    uint32_t w[32];                                  // up to 64 fp16, two per word
+    const uint4* src = reinterpret_cast<const uint4*>(vs + (int64_t)(on ? t : 0) * kD + part * CPT);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < CPT / 8) {
+        const uint4 u = src[i];
+        w[4 * i] = u.x; w[4 * i + 1] = u.y; w[4 * i + 2] = u.z; w[4 * i + 3] = u.w;
+      }
+    }
+    int kmin = 0x7FFF, kmax = -0x7FFF;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i < CPT / 2) {
+        const int a0 = f16_key(w[i] & 0xFFFFu), a1 = f16_key(w[i] >> 16);
+        kmin = min(kmin, min(a0, a1));
+        kmax = max(kmax, max(a0, a1));
+      }
+    }
+    for (int o = 1; o < TPT; o <<= 1) {
+      kmin = min(kmin, __shfl_xor(kmin, o, TPT));
+      kmax = max(kmax, __shfl_xor(kmax, o, TPT));
+    }
+    if (on) {
+      const QuantParams qp = quant_params(kmin, kmax, L);
+      if (part == 0) {
+        vsc[t] = (uint16_t)qp.hb;
+        vze[t] = (uint16_t)qp.zero;
+      }
+      uint8_t* dst = qv + t * kD + part * CPT;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (i < CPT / 2) {
+          dst[2 * i] = (uint8_t)quant_level(w[i] & 0xFFFFu, qp, L);
+          dst[2 * i + 1] = (uint8_t)quant_level(w[i] >> 16, qp, L);
+        }
+      }
+    }
   }
   if (tid < 128) ident[tid] = (uint8_t)tid;
   __syncthreads();
@@ -141,11 +235,9 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
       for (int r = 0; r < nr; ++r) {
         const int base = r * kR;
         // seed = smallest remaining token index
-        if (tid == 0) {
-          int sd = 0;
-          while (!alive[sd]) ++sd;
-          red[0] = (uint32_t)sd;
-        }
+        if (tid == 0) red[0] = 0xFFu;
+        __syncthreads();
+        if (tid < n && alive[tid]) atomicMin(&red[0], (uint32_t)tid);
         __syncthreads();
         const int sd = (int)red[0];
         if (tid < n) {
@@ -288,10 +380,12 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
     const uint32_t woff = (is_v ? v_ex : k_ex) + ((e & 1) ? (is_v ? v_a : k_a) : 0u);
     if (w == 0) continue;
     const int r = rc / kD, c = rc % kD;
+    uint32_t v[kR];
+    run_values(q, order, r, c, n, v);
     uint64_t lo = 0, hi = 0;          // the run's 128-bit string
     for (int i = 0; i < kR; ++i) {
       const int sl = r * kR + i;
-      const uint64_t u = sl < n ? (uint64_t)(q[order[sl] * kD + c] - m) : 0ull;
+      const uint64_t u = sl < n ? (uint64_t)(v[i] - m) : 0ull;
       const int p = i * (int)w;
       if (p < 64) {
         lo |= u << p;

@@ -130,7 +130,8 @@ uint64_t packkv_pv_workspace_bytes(const packkv_cache_t* cache, int32_t group);
  * packkv_compress_block - encode n_tokens tokens of every stream at once
  * (prefill).  Abstract: PackKV compresses the KV cache; Fig. 2 caption and
  * TL;DR: quantise, reorder, then bit-pack losslessly in channel direction.
- *   k_f16, v_f16: device fp16 [S][n_tokens][D], token order, contiguous.
+ *   k_f16, v_f16: device fp16 [S][n_tokens][D], token order, contiguous,
+ *                 16-byte aligned (else PACKKV_EINVAL).
  * The cache must be empty (n_tokens == 0, else PACKKV_ESTATE) and
  * 1 <= n_tokens <= max_tokens (else EINVAL / ECAPACITY).  Writes every
  * record, k_off/v_off[0 .. nb], perm, and the raw tail staging (the last,
