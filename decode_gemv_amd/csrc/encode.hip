@@ -85,6 +85,20 @@ __device__ __forceinline__ void run_values(const uint8_t* q, const uint8_t* orde
   }
 }
 
+// The w-bit string of a run: slot i's value in bits [i*w, i*w + w) of four
+// little-endian words (only the first w are used).  W is a compile-time
+// width, so every bit position is a constant.
+template <int W>
+__device__ __forceinline__ void pack_run(const uint32_t u[kR], uint32_t out[4]) {
+  out[0] = out[1] = out[2] = out[3] = 0u;
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    const int p = i * W, wd = p >> 5, sh = p & 31;
+    out[wd] |= u[i] << sh;
+    if (sh + W > 32) out[wd + 1] |= u[i] >> (32 - sh);
+  }
+}
+
 // Min and width of run r, channel c of the slot-ordered ints q[order[slot]][c].
 __device__ __forceinline__ void run_stats(const uint8_t* q, const uint8_t* order, int r, int c,
                                           int n, uint32_t& m, uint32_t& w) {
@@ -120,10 +134,12 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh /*[256]*/, uint32_t
   return incl - v;
 }
 
+template <int B>
 __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
   constexpr int NT = 256;
-  __shared__ uint8_t qk[128 * kD];
-  __shared__ uint8_t qv[128 * kD];
+  __shared__ __attribute__((aligned(16))) uint8_t qk[B * kD];
+  __shared__ __attribute__((aligned(16))) uint8_t qv[B * kD];
+  __shared__ __attribute__((aligned(16))) uint16_t rawk[B * kD];
   __shared__ uint16_t ksc[kD], kze[kD], vsc[128], vze[128];
   __shared__ __attribute__((aligned(16))) uint8_t order[128];
   __shared__ __attribute__((aligned(16))) uint8_t ident[128];
@@ -134,7 +150,7 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
   __shared__ uint32_t red[4];
 
   const int tid = threadIdx.x;
-  const int B = a.B, L = (1 << a.bits) - 1;
+  const int L = (1 << a.bits) - 1;
   const int s = blockIdx.y;
   const int j = a.mode == kTail ? a.block0 : blockIdx.x;
   const int64_t t0 = (int64_t)j * B;
@@ -144,34 +160,26 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
   const uint16_t* ks = a.k + s * a.src_stream + (a.mode == kTail ? 0 : j * a.src_block);
   const uint16_t* vs = a.v + s * a.src_stream + (a.mode == kTail ? 0 : j * a.src_block);
 
-  // (1) quantise.  K per channel over the block's tokens: thread c walks its
-  // channel in batches of 16 independent loads (one memory latency per
-  // batch), once for the range and once for the levels.
+  // (1) quantise.  K per channel over the block's tokens: the block's raw K
+  // is staged through LDS with 16-byte loads by every thread (one memory
+  // latency), then thread c reads its channel from there.
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(ks);
+    uint4* dst = reinterpret_cast<uint4*>(rawk);
+    for (int i = tid; i < n * (kD / 8); i += NT) dst[i] = src[i];
+  }
+  __syncthreads();
   if (tid < kD) {
-    constexpr int KB = 16;
     int kmin = 0x7FFF, kmax = -0x7FFF;
-    for (int t0 = 0; t0 < n; t0 += KB) {
-      uint32_t x[KB];
-#pragma unroll
-      for (int i = 0; i < KB; ++i) x[i] = ks[(int64_t)min(t0 + i, n - 1) * kD + tid];
-#pragma unroll
-      for (int i = 0; i < KB; ++i) {
-        const int k = f16_key(x[i]);
-        kmin = min(kmin, k);
-        kmax = max(kmax, k);
-      }
+    for (int t = 0; t < n; ++t) {
+      const int k = f16_key(rawk[t * kD + tid]);
+      kmin = min(kmin, k);
+      kmax = max(kmax, k);
     }
     const QuantParams qp = quant_params(kmin, kmax, L);
     ksc[tid] = (uint16_t)qp.hb;
     kze[tid] = (uint16_t)qp.zero;
-    for (int t0 = 0; t0 < n; t0 += KB) {
-      uint32_t x[KB];
-#pragma unroll
-      for (int i = 0; i < KB; ++i) x[i] = ks[(int64_t)min(t0 + i, n - 1) * kD + tid];
-#pragma unroll
-      for (int i = 0; i < KB; ++i)
-        if (t0 + i < n) qk[(t0 + i) * kD + tid] = (uint8_t)quant_level(x[i], qp, L);
-    }
+    for (int t = 0; t < n; ++t) qk[t * kD + tid] = (uint8_t)quant_level(rawk[t * kD + tid], qp, L);
   }
   // V per token: the 128 channels of token t are split over TPT neighbouring
   // threads, each loading its CPT values with 16-byte loads; min and max are
@@ -271,16 +279,25 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
       // identity fallback: keep the grouping only if the payload shrinks.
       if (tid < 2) red[tid] = 0;
       __syncthreads();
+      // The statistics of both orders are kept in registers (at most 4
+      // (run, channel) entries per thread), and those of the chosen order
+      // become the record's widths and minima.
+      constexpr int EPT = 2 * (B / kR) * kD / NT;    // entries per thread: 2 or 4
+      uint32_t gm[EPT], gw[EPT], im[EPT], iw[EPT];
       uint32_t sum_g = 0, sum_i = 0;
-      for (int it = tid; it < 2 * nr * kD; it += NT) {
-        const bool is_v = it >= nr * kD;
-        const int rc = is_v ? it - nr * kD : it;
-        const uint8_t* q = is_v ? qv : qk;
-        uint32_t m, w;
-        run_stats(q, order, rc / kD, rc % kD, n, m, w);
-        sum_g += w;
-        run_stats(q, ident, rc / kD, rc % kD, n, m, w);
-        sum_i += w;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int it = tid + e * NT;
+        gm[e] = gw[e] = im[e] = iw[e] = 0u;
+        if (it < 2 * nr * kD) {
+          const bool is_v = it >= nr * kD;
+          const int rc = is_v ? it - nr * kD : it;
+          const uint8_t* q = is_v ? qv : qk;
+          run_stats(q, order, rc / kD, rc % kD, n, gm[e], gw[e]);
+          run_stats(q, ident, rc / kD, rc % kD, n, im[e], iw[e]);
+          sum_g += gw[e];
+          sum_i += iw[e];
+        }
       }
       atomicAdd(&red[0], sum_g);
       atomicAdd(&red[1], sum_i);
@@ -288,22 +305,42 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
       const bool keep = red[0] < red[1];
       __syncthreads();
       if (!keep && tid < 128) order[tid] = (uint8_t)tid;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int it = tid + e * NT;
+        if (it < 2 * nr * kD) {
+          const bool is_v = it >= nr * kD;
+          const int rc = is_v ? it - nr * kD : it;
+          (is_v ? wv : wk)[rc] = (uint8_t)(keep ? gw[e] : iw[e]);
+          (is_v ? mv : mk)[rc] = (uint8_t)(keep ? gm[e] : im[e]);
+        }
+      }
       __syncthreads();
     } else {
+      // (3') identity order: per-run minima and widths
+      for (int it = tid; it < 2 * nr * kD; it += NT) {
+        const bool is_v = it >= nr * kD;
+        const int rc = is_v ? it - nr * kD : it;
+        uint32_t m, w;
+        run_stats(is_v ? qv : qk, order, rc / kD, rc % kD, n, m, w);
+        (is_v ? wv : wk)[rc] = (uint8_t)w;
+        (is_v ? mv : mk)[rc] = (uint8_t)m;
+      }
       __syncthreads();
     }
   }
-
-  // (3) per-run minima and widths in the chosen order.
-  for (int it = tid; it < 2 * nr * kD; it += NT) {
-    const bool is_v = it >= nr * kD;
-    const int rc = is_v ? it - nr * kD : it;
-    uint32_t m, w;
-    run_stats(is_v ? qv : qk, order, rc / kD, rc % kD, n, m, w);
-    (is_v ? wv : wk)[rc] = (uint8_t)w;
-    (is_v ? mv : mk)[rc] = (uint8_t)m;
+  if (a.mode == kPass2) {
+    // (3) per-run minima and widths in the stored order
+    for (int it = tid; it < 2 * nr * kD; it += NT) {
+      const bool is_v = it >= nr * kD;
+      const int rc = is_v ? it - nr * kD : it;
+      uint32_t m, w;
+      run_stats(is_v ? qv : qk, order, rc / kD, rc % kD, n, m, w);
+      (is_v ? wv : wk)[rc] = (uint8_t)w;
+      (is_v ? mv : mk)[rc] = (uint8_t)m;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // payload word offsets of every (run, channel), run-major: up to 512 per
   // tensor, two per thread.
@@ -382,20 +419,16 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
     const int r = rc / kD, c = rc % kD;
     uint32_t v[kR];
     run_values(q, order, r, c, n, v);
-    uint64_t lo = 0, hi = 0;          // the run's 128-bit string
-    for (int i = 0; i < kR; ++i) {
-      const int sl = r * kR + i;
-      const uint64_t u = sl < n ? (uint64_t)(v[i] - m) : 0ull;
-      const int p = i * (int)w;
-      if (p < 64) {
-        lo |= u << p;
-        if (p + (int)w > 64) hi |= u >> (64 - p);
-      } else {
-        hi |= u << (p - 64);
-      }
+#pragma unroll
+    for (int i = 0; i < kR; ++i) v[i] = r * kR + i < n ? v[i] - m : 0u;
+    uint32_t words[4];
+    switch (w) {
+      case 1: pack_run<1>(v, words); break;
+      case 2: pack_run<2>(v, words); break;
+      case 3: pack_run<3>(v, words); break;
+      default: pack_run<4>(v, words); break;
     }
     uint32_t* dst = reinterpret_cast<uint32_t*>((is_v ? vrec + v_pay : krec + k_pay)) + woff;
-    const uint32_t words[4] = {(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
     for (uint32_t i = 0; i < w; ++i) dst[i] = words[i];
   }
   // zero padding after the payload
@@ -453,7 +486,8 @@ namespace packkv {
 
 hipError_t launch_encode(const EncArgs& a, int n_streams, int n_blocks, hipStream_t st) {
   dim3 grid(a.mode == kTail ? 1 : n_blocks, n_streams);
-  hipLaunchKernelGGL(k_encode, grid, dim3(256), 0, st, a);
+  if (a.B == 64) hipLaunchKernelGGL(k_encode<64>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_encode<128>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
