@@ -54,20 +54,27 @@ int check_cache(const packkv_cache_t* c) {
 
 // Blocks per workgroup for the GEMVs: enough workgroups to fill 256 CUs
 // several times over, at most 64 blocks each.
-int gemv_blocks_per_wg(int64_t n_streams, int nb) {
-  static int env = -1;
-  if (env < 0) {
-    const char* s = getenv("PACKKV_BLOCKS_PER_WG");
-    env = s ? atoi(s) : 0;
-  }
-  if (env > 0) return env > 64 ? 64 : (env < 4 ? 4 : env);
-  // about two rounds of one-wave workgroups over the chip's resident slots
-  // (16 per CU), each workgroup taking an even number of blocks: the GEMVs
-  // process blocks in pairs
-  int64_t total = n_streams * (int64_t)nb;
-  int64_t j = (total + 7679) / 7680;
+// Blocks per workgroup.  The V GEMV and fused attention keep about two
+// rounds of one-wave workgroups over the chip's resident slots (16 per CU):
+// their workgroups end with a partial sum that the last one of the stream
+// merges, so fewer, longer workgroups pay less for it.  The K GEMV has no
+// merge and is fastest with many short workgroups (better balance at the
+// kernel's end).  Always even: the GEMVs take blocks in pairs.
+static int env_int(const char* name) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : 0;
+}
+int gemv_blocks_per_wg(int64_t n_streams, int nb, bool split_merge) {
+  static const int env_all = env_int("PACKKV_BLOCKS_PER_WG");
+  static const int env_qk = env_int("PACKKV_QK_BLOCKS_PER_WG");
+  int64_t j;
+  if (!split_merge && env_qk > 0) j = env_qk;
+  else if (env_all > 0) j = env_all;
+  else if (!split_merge) j = 4;
+  else j = (n_streams * (int64_t)nb + 7679) / 7680;
   j += j & 1;
-  if (j < 4) j = 4;
+  const int lo = split_merge ? 4 : 2;   // the V workspace assumes at least 4
+  if (j < lo) j = lo;
   if (j > 64) j = 64;
   return (int)j;
 }
@@ -84,7 +91,7 @@ GemvArgs gemv_args(const packkv_cache_t* c, bool is_v) {
   a.n_tokens = c->n_tokens;
   a.nb = (int)((c->n_tokens + c->cfg.block_tokens - 1) / c->cfg.block_tokens);
   a.bits = c->cfg.bits;
-  a.blocks_per_wg = gemv_blocks_per_wg(c->n_streams, a.nb);
+  a.blocks_per_wg = gemv_blocks_per_wg(c->n_streams, a.nb, is_v);
   a.splits = (a.nb + a.blocks_per_wg - 1) / a.blocks_per_wg;
   a.status = c->status;
   return a;
@@ -267,7 +274,7 @@ int packkv_attention_decode(const packkv_cache_t* c, const void* q_f16, int32_t 
   if (!q_f16 || !out || !workspace || group < 1 || !(scale > 0.f) || !std::isfinite(scale)) return PACKKV_EINVAL;
   if (c->n_tokens < 1) return PACKKV_ESTATE;
   if (ws_bytes < packkv_attention_workspace_bytes(c, group)) return PACKKV_EINVAL;
-  const GemvArgs g = gemv_args(c, false);
+  const GemvArgs g = gemv_args(c, true);      // the split-merge work division
   AttnArgs a;
   memset(&a, 0, sizeof(a));
   a.k_arena = c->k_arena;
