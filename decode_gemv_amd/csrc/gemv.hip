@@ -469,19 +469,17 @@ struct VBlock {
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         if (r >= nr) break;
-        uint32_t W[ND][4];
 #pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          const u32x4 t = *reinterpret_cast<const u32x4*>(&dig[(g * ND + d) * NG + 4 * r]);
-          W[d][0] = t.x; W[d][1] = t.y; W[d][2] = t.z; W[d][3] = t.w;
-        }
+        for (int kk = 0; kk < 4; ++kk) {
+          uint32_t W[ND];                             // digit words of slots 8(4r+kk) ...
 #pragma unroll
-        for (int ch = 0; ch < 2; ++ch)
+          for (int d = 0; d < ND; ++d) W[d] = dig[(g * ND + d) * NG + 4 * r + kk];
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
+          for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
             for (int d = 0; d < ND; ++d)
-              sd[ch][d] = __builtin_amdgcn_udot8(nib[2 * r + ch][kk], W[d][kk], sd[ch][d], false);
+              sd[ch][d] = __builtin_amdgcn_udot8(nib[2 * r + ch][kk], W[d], sd[ch][d], false);
+        }
       }
       const float unit = ldexpf(1.0f, -E[g]);
 #pragma unroll
@@ -685,22 +683,17 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
       for (int g = 0; g < GT; ++g)
 #pragma unroll
         for (int h = 0; h < NH; ++h) pw[g][h] = pv[g][h];
-      request(jj + 2, pre, pv);
+      request(jj + 1, pre, pv);
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
       const bool ok = vb.run(rec, size, (n + kR - 1) / kR, rok, pw, acc, pz);
       corrupt |= rok && !ok;
     };
-    u32x4 pa[NCH], pb[NCH];
-    float va[GT][NH], vb2[GT][NH];
-    request(0, pa, va);
-    __builtin_amdgcn_sched_barrier(0);
-    request(1, pb, vb2);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int jj = 0; jj < nj; jj += 2) {
-      process(jj, pa, va);
-      process(jj + 1, pb, vb2);
-    }
+    // one record (and its weights) in flight
+    u32x4 pre[NCH];
+    float pv[GT][NH];
+    request(0, pre, pv);
+    for (int jj = 0; jj < nj; ++jj) process(jj, pre, pv);
     // partial result of this split
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
