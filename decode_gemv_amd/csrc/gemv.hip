@@ -562,7 +562,7 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
       const int n = jj < nj ? (int)imin64(B, a.n_tokens - (int64_t)j * B) : 0;
       __syncthreads();
       store_record<NCH>(rec, size, lane, pre);
-      rs.request(jj + 2, pre);
+      rs.request(jj + 1, pre);
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
       float score[GT][NH];
@@ -582,15 +582,9 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
         }
       }
     };
-    u32x4 pa[NCH], pb[NCH];
-    rs.request(0, pa);
-    __builtin_amdgcn_sched_barrier(0);
-    rs.request(1, pb);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int jj = 0; jj < nj; jj += 2) {
-      process(jj, pa);
-      process(jj + 1, pb);
-    }
+    u32x4 pre[NCH];
+    rs.request(0, pre);
+    for (int jj = 0; jj < nj; ++jj) process(jj, pre);
   }
   if (corrupt && lane == 0) latch(a.status, PACKKV_ECORRUPT);
 }
