@@ -28,6 +28,17 @@ namespace packkv {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// LDS ordering inside one wave: wait for the wave's LDS accesses and keep
+// the compiler from moving memory operations across.  Unlike __syncthreads
+// it involves no other wave, so waves of one workgroup may run different
+// code between their workgroup barriers.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 
 __device__ __forceinline__ float fp8_unit() {
   // value of the e4m3 byte 0x01; every byte n <= 15 converts to exactly n * unit
@@ -58,6 +69,7 @@ __device__ __forceinline__ bool record_ok(uint32_t o, uint32_t size, uint64_t st
 // the compiler can count outstanding loads exactly instead of draining them.
 constexpr int kBufferFormat = 0x00020000;          // 32-bit data format
 constexpr int kNonTemporal = 2;
+constexpr int kCoherent = 16;     // sc1: agent-coherent, as relaxed agent-scope atomics
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFormat);
 }
@@ -318,7 +330,7 @@ struct KBlock {
     }
     uint32_t nib[NRL][4];
     const bool ok = Dec::decode(rec, size, nr, lane, nib);
-    __syncthreads();                                  // every lane has read the record
+    wave_sync();                                  // every lane has read the record
     uint32_t* plane = reinterpret_cast<uint32_t*>(rec);
     float* red = reinterpret_cast<float*>(rec + (NH == 1 ? 0 : PLANE_BYTES));
 #pragma unroll
@@ -327,7 +339,7 @@ struct KBlock {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) plane[(r * 4 + kk) * ROWW + c] = nib[k][kk];
     }
-    __syncthreads();
+    wave_sync();
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       float acc[GT][8];
@@ -360,12 +372,12 @@ struct KBlock {
         }
       }
       // reduce the 8 channel groups: red[g][slot][cg], slot = g8*8 + i
-      __syncthreads();
+      wave_sync();
 #pragma unroll
       for (int g = 0; g < GT; ++g)
 #pragma unroll
         for (int i = 0; i < 8; ++i) red[(g * 64 + g8 * 8 + i) * 9 + cg] = acc[g][i];
-      __syncthreads();
+      wave_sync();
 #pragma unroll
       for (int g = 0; g < GT; ++g) {
         float sum = beta[g];
@@ -457,7 +469,7 @@ struct VBlock {
     }
     uint32_t nib[NRL][4];
     const bool ok = Dec::decode(rec, size, nr, lane, nib) && use;
-    __syncthreads();
+    wave_sync();
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       if (!ok || !live[g]) continue;
@@ -560,11 +572,11 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
       const uint32_t size = rs.size_of(jj, rok);
       corrupt |= jj < nj && !rok;
       const int n = jj < nj ? (int)imin64(B, a.n_tokens - (int64_t)j * B) : 0;
-      __syncthreads();
+      wave_sync();
       store_record<NCH>(rec, size, lane, pre);
       rs.request(jj + 1, pre);
       __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
+      wave_sync();
       float score[GT][NH];
       const bool ok = kb.run(rec, size, (n + kR - 1) / kR, score) && rok;
       corrupt |= rok && !ok;
@@ -670,7 +682,7 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
       const uint32_t size = rs.size_of(jj, rok);
       corrupt |= jj < nj && !rok;
       const int n = jj < nj ? (int)imin64(B, a.n_tokens - (int64_t)j * B) : 0;
-      __syncthreads();
+      wave_sync();
       store_record<NCH>(rec, size, lane, pre);
       float pw[GT][NH];
 #pragma unroll
@@ -679,7 +691,7 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
         for (int h = 0; h < NH; ++h) pw[g][h] = pv[g][h];
       request(jj + 1, pre, pv);
       __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
+      wave_sync();
       const bool ok = vb.run(rec, size, (n + kR - 1) / kR, rok, pw, acc, pz);
       corrupt |= rok && !ok;
     };
@@ -745,149 +757,179 @@ __device__ __forceinline__ float wave_max_f(float v) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int B, int BITS, int GT>
-__global__ __launch_bounds__(64) void k_attn_decode(AttnArgs a) {
+__global__ __launch_bounds__(128) void k_attn_decode(AttnArgs a) {
   using KB = KBlock<B, BITS, GT>;
   using VB = VBlock<B, BITS, GT>;
   constexpr int NH = B / 64;
   constexpr int REC_K = max_record_bytes(false, B, 4);
   constexpr int REC_V = max_record_bytes(true, B, 4);
-  constexpr int REC = REC_K > REC_V ? REC_K : REC_V;
-  constexpr int NCH = (REC + 1023) / 1024;
-  constexpr int BUF = (REC + 16) > KB::SCRATCH_BYTES ? (REC + 16) : KB::SCRATCH_BYTES;
-  __shared__ __attribute__((aligned(16))) uint8_t rec[BUF];
+  constexpr int NCH_K = (REC_K + 1023) / 1024;
+  constexpr int NCH_V = (REC_V + 1023) / 1024;
+  constexpr int BUF_K = (REC_K + 16) > KB::SCRATCH_BYTES ? (REC_K + 16) : KB::SCRATCH_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t rec_k[BUF_K];
+  __shared__ __attribute__((aligned(16))) uint8_t rec_v[REC_V + 16];
   __shared__ __attribute__((aligned(16))) float qs[GT * kD];
   __shared__ __attribute__((aligned(16))) uint32_t dig[VB::DIG_WORDS];
+  __shared__ __attribute__((aligned(16))) float ring[2][GT][B];   // scores of blocks jj & 1
 
-  const int lane = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
+  const int lane = threadIdx.x & 63;
   const int s = blockIdx.x / a.splits;
   const int split = blockIdx.x % a.splits;
   const int j0 = split * a.blocks_per_wg;
   const int nj = max(0, min(a.nb, j0 + a.blocks_per_wg) - j0);
-  RecordStream<NCH, REC_K> ks;
-  ks.arena = a.k_arena + (uint64_t)s * a.arena_stride;
-  ks.stride = a.arena_stride;
-  ks.offs.load(a.k_off + (int64_t)s * a.off_stride, j0, nj, lane);
-  ks.nj = nj;
-  ks.lane = lane;
-  RecordStream<NCH, REC_V> vs;
-  vs.arena = a.v_arena + (uint64_t)s * a.arena_stride;
-  vs.stride = a.arena_stride;
-  vs.offs.load(a.v_off + (int64_t)s * a.off_stride, j0, nj, lane);
-  vs.nj = nj;
-  vs.lane = lane;
-  KB kb;
-  kb.init(qs, lane);
-  VB vb;
-  vb.init(dig, lane);
   bool corrupt = false;
   const float NEG_INF = -__builtin_huge_valf();
 
-  for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
-    kb.set_queries(a.q, s, a.G, gq0);
-    float m[GT], l[GT], acc[GT][2], pz[GT];
-#pragma unroll
-    for (int g = 0; g < GT; ++g) { m[g] = NEG_INF; l[g] = 0.f; acc[g][0] = acc[g][1] = 0.f; pz[g] = 0.f; }
-
-    // One record in flight: K of block jj requests V of block jj, which
-    // requests K of block jj + 1 (a second register set would push the
-    // kernel past 128 VGPRs and halve its occupancy).
-    u32x4 pre[NCH];
-    ks.request(0, pre);
-    for (int jj = 0; jj < nj; ++jj) {
-      const int j = j0 + jj;
-      const int n = (int)imin64(B, a.n_tokens - (int64_t)j * B);
-      const int nr = (n + kR - 1) / kR;
-      // K: scores of the block, times scale * log2(e); -inf past n or when
-      // the record is unusable
-      float sc[GT][NH];
-      {
+  // Both waves pass the same barriers: one per block and one per query group.
+  if (wave == 0) {
+    for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
+      // K wave: the scores of every block, handed over through the ring
+      // with one workgroup barrier per block
+      RecordStream<NCH_K, REC_K> ks;
+      ks.arena = a.k_arena + (uint64_t)s * a.arena_stride;
+      ks.stride = a.arena_stride;
+      ks.offs.load(a.k_off + (int64_t)s * a.off_stride, j0, nj, lane);
+      ks.nj = nj;
+      ks.lane = lane;
+      KB kb;
+      kb.init(qs, lane);
+      kb.set_queries(a.q, s, a.G, gq0);
+      u32x4 pre[NCH_K];
+      ks.request(0, pre);
+      for (int jj = 0; jj < nj; ++jj) {
+        const int n = (int)imin64(B, a.n_tokens - (int64_t)(j0 + jj) * B);
         bool rok;
         const uint32_t size = ks.size_of(jj, rok);
         corrupt |= !rok;
-        __syncthreads();
-        store_record<NCH>(rec, size, lane, pre);
-        vs.request(jj, pre);
+        wave_sync();
+        store_record<NCH_K>(rec_k, size, lane, pre);
+        ks.request(jj + 1, pre);
         __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
+        wave_sync();
         float score[GT][NH];
-        const bool ok = kb.run(rec, size, nr, score) && rok;
+        const bool ok = kb.run(rec_k, size, (n + kR - 1) / kR, score) && rok;
         corrupt |= rok && !ok;
 #pragma unroll
         for (int g = 0; g < GT; ++g)
 #pragma unroll
           for (int h = 0; h < NH; ++h)
-            sc[g][h] = ok && h * 64 + lane < n ? score[g][h] * a.scale_log2e : NEG_INF;
+            ring[jj & 1][g][h * 64 + lane] = ok && h * 64 + lane < n ? score[g][h] * a.scale_log2e : NEG_INF;
+        __syncthreads();                            // block jj goes to the V wave
       }
-      // running-max softmax update: weights exp(s - m), earlier sums rescaled
-      float w[GT][NH];
+      __syncthreads();                              // the ring is reused
+    }
+  } else {
+    for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
+      // V wave: running-max softmax over the scores, weighted sum of V
+      RecordStream<NCH_V, REC_V> vs;
+      vs.arena = a.v_arena + (uint64_t)s * a.arena_stride;
+      vs.stride = a.arena_stride;
+      vs.offs.load(a.v_off + (int64_t)s * a.off_stride, j0, nj, lane);
+      vs.nj = nj;
+      vs.lane = lane;
+      VB vb;
+      vb.init(dig, lane);
+      float m[GT], l[GT], acc[GT][2], pz[GT];
 #pragma unroll
-      for (int g = 0; g < GT; ++g) {
-        float mx = sc[g][0];
+      for (int g = 0; g < GT; ++g) { m[g] = NEG_INF; l[g] = 0.f; acc[g][0] = acc[g][1] = 0.f; pz[g] = 0.f; }
+      u32x4 pre[NCH_V];
+      vs.request(0, pre);
+      for (int jj = 0; jj < nj; ++jj) {
+        const int n = (int)imin64(B, a.n_tokens - (int64_t)(j0 + jj) * B);
+        __syncthreads();                            // block jj's scores are in the ring
+        // weights exp(s - m); earlier sums rescaled when m grows
+        float w[GT][NH];
 #pragma unroll
-        for (int h = 1; h < NH; ++h) mx = fmaxf(mx, sc[g][h]);
-        const float mn = fmaxf(m[g], wave_max_f(mx));
-        const float alpha = mn == NEG_INF ? 1.f : fast_exp2(m[g] - mn);
-        acc[g][0] *= alpha;
-        acc[g][1] *= alpha;
-        pz[g] *= alpha;
-        l[g] *= alpha;
-        m[g] = mn;
+        for (int g = 0; g < GT; ++g) {
+          float sc[NH];
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          w[g][h] = mn == NEG_INF ? 0.f : fast_exp2(sc[g][h] - mn);
-          l[g] += w[g][h];
+          for (int h = 0; h < NH; ++h) sc[h] = ring[jj & 1][g][h * 64 + lane];
+          float mx = sc[0];
+#pragma unroll
+          for (int h = 1; h < NH; ++h) mx = fmaxf(mx, sc[h]);
+          const float mn = fmaxf(m[g], wave_max_f(mx));
+          const float alpha = mn == NEG_INF ? 1.f : fast_exp2(m[g] - mn);
+          acc[g][0] *= alpha;
+          acc[g][1] *= alpha;
+          pz[g] *= alpha;
+          l[g] *= alpha;
+          m[g] = mn;
+#pragma unroll
+          for (int h = 0; h < NH; ++h) {
+            w[g][h] = mn == NEG_INF ? 0.f : fast_exp2(sc[h] - mn);
+            l[g] += w[g][h];
+          }
         }
-      }
-      // V: the weighted sum of the block's values
-      {
         bool rok;
         const uint32_t size = vs.size_of(jj, rok);
         corrupt |= !rok;
-        __syncthreads();
-        store_record<NCH>(rec, size, lane, pre);
-        ks.request(jj + 1, pre);
+        wave_sync();
+        store_record<NCH_V>(rec_v, size, lane, pre);
+        vs.request(jj + 1, pre);
         __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-        const bool ok = vb.run(rec, size, nr, rok, w, acc, pz);
+        wave_sync();
+        const bool ok = vb.run(rec_v, size, (n + kR - 1) / kR, rok, w, acc, pz);
         corrupt |= rok && !ok;
       }
-    }
-    // this split's partial: out sums, max, weight sum
+      // this split's partial: out sums, max, weight sum
 #pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      const float z = wave_sum(pz[g]);
-      const float lsum = wave_sum(l[g]);
-      if (gq0 + g < a.G) {
-        float* dst = a.ws + (((int64_t)s * a.G + gq0 + g) * a.splits + split) * kAttnPartial;
-        store_partial(dst + lane, acc[g][0] + z);
-        store_partial(dst + lane + 64, acc[g][1] + z);
-        if (lane == 0) {
-          store_partial(dst + kD, m[g]);
-          store_partial(dst + kD + 1, lsum);
+      for (int g = 0; g < GT; ++g) {
+        const float z = wave_sum(pz[g]);
+        const float lsum = wave_sum(l[g]);
+        if (gq0 + g < a.G) {
+          float* dst = a.ws + (((int64_t)s * a.G + gq0 + g) * a.splits + split) * kAttnPartial;
+          store_partial(dst + lane, acc[g][0] + z);
+          store_partial(dst + lane + 64, acc[g][1] + z);
+          if (lane == 0) {
+            store_partial(dst + kD, m[g]);
+            store_partial(dst + kD + 1, lsum);
+          }
         }
       }
+      __syncthreads();                              // the ring is reused
     }
   }
   if (corrupt && lane == 0) latch(a.status, PACKKV_ECORRUPT);
-  if (!last_to_arrive(&a.tickets[s], a.splits, lane)) return;
+  if (wave != 1 || !last_to_arrive(&a.tickets[s], a.splits, lane)) return;
+  // Merge: the largest split max M first (lanes across splits), then each
+  // split's sums scaled by 2^(m_i - M).  A half-wave takes every other split
+  // (in split order) and a lane four of the outputs; the loads of four splits
+  // per half-wave are issued together.
+  const int half = lane >> 5, d4 = (lane & 31) * 4;
+  constexpr uint32_t PB = kAttnPartial * 4;         // bytes per partial
   for (int g = 0; g < a.G; ++g) {
     const float* src = a.ws + ((int64_t)s * a.G + g) * a.splits * kAttnPartial;
-    float M = NEG_INF, L = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int i = 0; i < a.splits; ++i) {
-      const float* part = src + (int64_t)i * kAttnPartial;
-      const float mi = load_partial(part + kD), li = load_partial(part + kD + 1);
-      const float a0 = load_partial(part + lane), a1 = load_partial(part + lane + 64);
-      const float mn = fmaxf(M, mi);
-      if (mn == NEG_INF) continue;                 // nothing valid yet
-      const float fo = fast_exp2(M - mn), fi = fast_exp2(mi - mn);
-      L = L * fo + li * fi;
-      o0 = o0 * fo + a0 * fi;
-      o1 = o1 * fo + a1 * fi;
-      M = mn;
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(src, (uint32_t)a.splits * PB);
+    float M = NEG_INF;
+    for (int i = lane; i < a.splits; i += 64) M = fmaxf(M, load_partial(src + (int64_t)i * kAttnPartial + kD));
+    M = wave_max_f(M);
+    float L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i0 = 0; i0 < a.splits; i0 += 8) {
+      u32x4 v[4];
+      u32x2 ml[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t off = (uint32_t)(i0 + 2 * u + half) * PB;   // past the end reads zeros
+        v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * d4, 0, kCoherent));
+        ml[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * kD, 0, kCoherent));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool in = i0 + 2 * u + half < a.splits && M != NEG_INF;
+        const float f = in ? fast_exp2(__uint_as_float(ml[u].x) - M) : 0.f;
+        L = fmaf(__uint_as_float(ml[u].y), f, L);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = fmaf(__uint_as_float(v[u][k]), f, o[k]);
+      }
     }
-    float* dst = a.out + ((int64_t)s * a.G + g) * kD;
-    dst[lane] = o0 / L;
-    dst[lane + 64] = o1 / L;
+    L += __shfl_xor(L, 32, kWave);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] += __shfl_xor(o[k], 32, kWave);
+    if (half == 0) {
+      float4 res = {o[0] / L, o[1] / L, o[2] / L, o[3] / L};
+      *reinterpret_cast<float4*>(a.out + ((int64_t)s * a.G + g) * kD + d4) = res;
+    }
   }
   reset_ticket(&a.tickets[s], lane);
 }
@@ -1093,8 +1135,8 @@ hipError_t launch_pv(const GemvArgs& a, int B, int n_streams, hipStream_t st) {
 
 template <int B, int BITS>
 static void attn_launch(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  if (a.G == 1) hipLaunchKernelGGL((k_attn_decode<B, BITS, 1>), grid, dim3(64), 0, st, a);
-  else hipLaunchKernelGGL((k_attn_decode<B, BITS, 4>), grid, dim3(64), 0, st, a);
+  if (a.G == 1) hipLaunchKernelGGL((k_attn_decode<B, BITS, 1>), grid, dim3(128), 0, st, a);
+  else hipLaunchKernelGGL((k_attn_decode<B, BITS, 4>), grid, dim3(128), 0, st, a);
 }
 hipError_t launch_attention(const AttnArgs& a, int B, int n_streams, hipStream_t st) {
   const dim3 grid(n_streams * a.splits);
