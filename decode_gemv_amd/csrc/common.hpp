@@ -86,29 +86,30 @@ __device__ __forceinline__ uint32_t nibble_splat(uint32_t m) {
 // nibble words: word k holds q = m + u of slots 8k .. 8k+7 (nibble i = slot
 // 8k+i).  Valid for m + 2^w - 1 <= 15.  `wd` holds the run's first four
 // payload words (words past the run are ignored).
+template <int WMAX = 4>
 __device__ __forceinline__ void run_to_nibbles(int w, uint32_t m, const uint32_t wd[4], uint32_t out[4]) {
   const uint32_t a = wd[0], b = wd[1], c = wd[2], d = wd[3];
-  switch (w) {
-    case 4: out[0] = a; out[1] = b; out[2] = c; out[3] = d; break;
-    case 3:
-      out[0] = spread3to4(bits_at<0>(a, b, c, d));
-      out[1] = spread3to4(bits_at<24>(a, b, c, d));
-      out[2] = spread3to4(bits_at<48>(a, b, c, d));
-      out[3] = spread3to4(bits_at<72>(a, b, c, d));
-      break;
-    case 2:
-      out[0] = spread2to4(a);
-      out[1] = spread2to4(a >> 16);
-      out[2] = spread2to4(b);
-      out[3] = spread2to4(b >> 16);
-      break;
-    case 1:
-      out[0] = spread1to4(a);
-      out[1] = spread1to4(a >> 8);
-      out[2] = spread1to4(a >> 16);
-      out[3] = spread1to4(a >> 24);
-      break;
-    default: out[0] = out[1] = out[2] = out[3] = 0u; break;
+  // widths above WMAX do not occur at the call site; the widest one that
+  // does is tested first
+  if (WMAX >= 4 && w == 4) {
+    out[0] = a; out[1] = b; out[2] = c; out[3] = d;
+  } else if (WMAX >= 3 && w == 3) {
+    out[0] = spread3to4(bits_at<0>(a, b, c, d));
+    out[1] = spread3to4(bits_at<24>(a, b, c, d));
+    out[2] = spread3to4(bits_at<48>(a, b, c, d));
+    out[3] = spread3to4(bits_at<72>(a, b, c, d));
+  } else if (WMAX >= 2 && w == 2) {
+    out[0] = spread2to4(a);
+    out[1] = spread2to4(a >> 16);
+    out[2] = spread2to4(b);
+    out[3] = spread2to4(b >> 16);
+  } else if (w == 1) {
+    out[0] = spread1to4(a);
+    out[1] = spread1to4(a >> 8);
+    out[2] = spread1to4(a >> 16);
+    out[3] = spread1to4(a >> 24);
+  } else {
+    out[0] = out[1] = out[2] = out[3] = 0u;
   }
   const uint32_t mm = nibble_splat(m);   // m in every nibble; no carries
   out[0] += mm; out[1] += mm; out[2] += mm; out[3] += mm;

@@ -75,7 +75,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 }
 
 // Record staging: chunks of 16 bytes, lane l takes chunks l, l+64, ...
-// Chunks past `bytes` (a multiple of 16) read as zero and are not stored.
+// Chunks past `bytes` (a multiple of 16) read as zero.
 template <int NCH>
 __device__ __forceinline__ void load_record(const uint8_t* g, uint32_t bytes, int lane, u32x4 pre[NCH]) {
   const __amdgpu_buffer_rsrc_t r = buffer_rsrc(g, bytes);
@@ -84,14 +84,16 @@ __device__ __forceinline__ void load_record(const uint8_t* g, uint32_t bytes, in
     pre[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (lane + 64 * k), 0, kNonTemporal));
 }
 template <int NCH>
-__device__ __forceinline__ void store_record(uint8_t* lds, uint32_t bytes, int lane, const u32x4 pre[NCH]) {
+__device__ __forceinline__ void store_record(uint8_t* lds, const u32x4 pre[NCH], int lane) {
   u32x4* dst = reinterpret_cast<u32x4*>(lds);
-  const int nch = (int)(bytes >> 4);
 #pragma unroll
-  for (int k = 0; k < NCH; ++k) {
-    const int c = lane + 64 * k;
-    if (c < nch) dst[c] = pre[k];
-  }
+  for (int k = 0; k < NCH; ++k) dst[lane + 64 * k] = pre[k];
+}
+// LDS staging for records of at most rec bytes: every chunk a load can bring
+// (NCH x 1 KiB, stored without a bounds test) plus 16 bytes of slack that the
+// decoder may read past the record's end.
+__host__ __device__ constexpr int staging_bytes(int rec) {
+  return ((rec + 1023) / 1024) * 1024 > rec + 16 ? ((rec + 1023) / 1024) * 1024 : rec + 16;
 }
 
 // Header decode + width scan for the lane's runs (NRL runs per lane, run
@@ -203,43 +205,67 @@ struct BlockDecoder {
       total -= running;
     }
     const bool ok = __ballot(bad) == 0 && (uint32_t)pad16(pay + 4 * (int)total) == size;
-    uint32_t wd[NRL][4];
-    if (all_full && BITS != 3) {
-      // runs of 4 (2) words at a 16 (8) byte aligned lane stride: one wide
-      // LDS read per run instead of 4 (2) dword reads that would hit the
-      // same banks
+    // container words: all reads are issued first.  At 4 bits a run's words
+    // are its container words; narrower full widths are converted after.
+    auto read_run = [&](int k) __attribute__((always_inline)) -> u32x4 {
+      if (all_full && BITS != 3) {
+        // runs of 4 (2) words at a 16 (8) byte aligned lane stride: one wide
+        // LDS read per run instead of 4 (2) dword reads that would hit the
+        // same banks
+        if (BITS == 4) return reinterpret_cast<const u32x4*>(rec + pay)[ok ? lane + 64 * k : 0];
+        const uint2 t = reinterpret_cast<const uint2*>(rec + pay)[ok ? lane + 64 * k : 0];
+        return u32x4{t.x, t.y, 0u, 0u};
+      }
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + pay) + (ok ? off[k] : 0u);
+      return u32x4{p[0], BITS > 1 ? p[1] : 0u, BITS > 2 ? p[2] : 0u, BITS > 3 ? p[3] : 0u};
+    };
+    if constexpr (BITS == 4) {
 #pragma unroll
       for (int k = 0; k < NRL; ++k) {
-        if (BITS == 4) {
-          const u32x4 t = reinterpret_cast<const u32x4*>(rec + pay)[ok ? lane + 64 * k : 0];
-          wd[k][0] = t.x; wd[k][1] = t.y; wd[k][2] = t.z; wd[k][3] = t.w;
-        } else {
-          const uint2 t = reinterpret_cast<const uint2*>(rec + pay)[ok ? lane + 64 * k : 0];
-          wd[k][0] = t.x; wd[k][1] = t.y; wd[k][2] = wd[k][3] = 0u;
-        }
+        const u32x4 t = read_run(k);
+        nib[k][0] = t.x; nib[k][1] = t.y; nib[k][2] = t.z; nib[k][3] = t.w;
+      }
+#pragma unroll
+      for (int k = 0; k < NRL; ++k) {
+        const uint32_t mm = nibble_splat(h[k]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) nib[k][kk] += mm;
       }
     } else {
+      u32x4 t[NRL];
+#pragma unroll
+      for (int k = 0; k < NRL; ++k) t[k] = read_run(k);
 #pragma unroll
       for (int k = 0; k < NRL; ++k) {
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + pay) + (ok ? off[k] : 0u);
+        const uint32_t wd[4] = {t[k].x, t[k].y, t[k].z, t[k].w};
+        full_to_nibbles<BITS>(wd, nib[k]);
+        const uint32_t mm = nibble_splat(h[k]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wd[k][i] = i < BITS ? p[i] : 0u;
+        for (int kk = 0; kk < 4; ++kk) nib[k][kk] += mm;
       }
     }
-#pragma unroll
-    for (int k = 0; k < NRL; ++k) {
-      full_to_nibbles<BITS>(wd[k], nib[k]);
-      const uint32_t mm = nibble_splat(h[k]);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) nib[k][kk] += mm;
-    }
     if (!all_full && ok) {
+      // narrower runs: read their words again and decode at their width
 #pragma unroll
       for (int k = 0; k < NRL; ++k) {
         const int w = (int)(h[k] >> 4);
         if (w != BITS) {
-          if ((k >> 1) < nr) run_to_nibbles(w, h[k] & 15u, wd[k], nib[k]);
-          else nib[k][0] = nib[k][1] = nib[k][2] = nib[k][3] = 0u;
+          if ((k >> 1) < nr) {
+            uint32_t wd[4];
+            if constexpr (BITS == 4) {
+              // the words read are nib - m in every nibble (mod 2^32)
+              const uint32_t mm = nibble_splat(h[k]);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) wd[i] = nib[k][i] - mm;
+            } else {
+              const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + pay) + off[k];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) wd[i] = i < BITS - 1 ? p[i] : 0u;
+            }
+            run_to_nibbles<BITS - 1>(w, h[k] & 15u, wd, nib[k]);
+          } else {
+            nib[k][0] = nib[k][1] = nib[k][2] = nib[k][3] = 0u;
+          }
         }
       }
     }
@@ -545,7 +571,7 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
   constexpr int NH = KB::NH;
   constexpr int REC = max_record_bytes(false, B, 4);
   constexpr int NCH = (REC + 1023) / 1024;
-  constexpr int BUF = (REC + 16) > KB::SCRATCH_BYTES ? (REC + 16) : KB::SCRATCH_BYTES;
+  constexpr int BUF = staging_bytes(REC) > KB::SCRATCH_BYTES ? staging_bytes(REC) : KB::SCRATCH_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t rec[BUF];
   __shared__ __attribute__((aligned(16))) float qs[GT * kD];
 
@@ -573,7 +599,7 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
       corrupt |= jj < nj && !rok;
       const int n = jj < nj ? (int)imin64(B, a.n_tokens - (int64_t)j * B) : 0;
       wave_sync();
-      store_record<NCH>(rec, size, lane, pre);
+      store_record<NCH>(rec, pre, lane);
       rs.request(jj + 1, pre);
       __builtin_amdgcn_sched_barrier(0);
       wave_sync();
@@ -627,13 +653,20 @@ __device__ __forceinline__ void reset_ticket(uint32_t* ticket, int lane) {
   if (lane == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 64-token blocks with one query fit 96 VGPRs (5 waves per SIMD); asking for
+// that occupancy costs at most a couple of values kept in scratch outside the
+// block loop
+template <int B, int GT>
+constexpr int pv_waves_per_eu() { return B == 64 && GT == 1 ? 5 : 1; }
+
 template <int B, int BITS, int GT>
-__global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(pv_waves_per_eu<B, GT>())))
+void k_pv_gemv(GemvArgs a) {
   using VB = VBlock<B, BITS, GT>;
   constexpr int NH = VB::NH;
   constexpr int REC = max_record_bytes(true, B, 4);
   constexpr int NCH = (REC + 1023) / 1024;
-  __shared__ __attribute__((aligned(16))) uint8_t rec[REC + 16];
+  __shared__ __attribute__((aligned(16))) uint8_t rec[staging_bytes(REC)];
   __shared__ __attribute__((aligned(16))) uint32_t dig[VB::DIG_WORDS];
 
   const int lane = threadIdx.x;
@@ -683,7 +716,7 @@ __global__ __launch_bounds__(64) void k_pv_gemv(GemvArgs a) {
       corrupt |= jj < nj && !rok;
       const int n = jj < nj ? (int)imin64(B, a.n_tokens - (int64_t)j * B) : 0;
       wave_sync();
-      store_record<NCH>(rec, size, lane, pre);
+      store_record<NCH>(rec, pre, lane);
       float pw[GT][NH];
 #pragma unroll
       for (int g = 0; g < GT; ++g)
@@ -765,9 +798,9 @@ __global__ __launch_bounds__(128) void k_attn_decode(AttnArgs a) {
   constexpr int REC_V = max_record_bytes(true, B, 4);
   constexpr int NCH_K = (REC_K + 1023) / 1024;
   constexpr int NCH_V = (REC_V + 1023) / 1024;
-  constexpr int BUF_K = (REC_K + 16) > KB::SCRATCH_BYTES ? (REC_K + 16) : KB::SCRATCH_BYTES;
+  constexpr int BUF_K = staging_bytes(REC_K) > KB::SCRATCH_BYTES ? staging_bytes(REC_K) : KB::SCRATCH_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t rec_k[BUF_K];
-  __shared__ __attribute__((aligned(16))) uint8_t rec_v[REC_V + 16];
+  __shared__ __attribute__((aligned(16))) uint8_t rec_v[staging_bytes(REC_V)];
   __shared__ __attribute__((aligned(16))) float qs[GT * kD];
   __shared__ __attribute__((aligned(16))) uint32_t dig[VB::DIG_WORDS];
   __shared__ __attribute__((aligned(16))) float ring[2][GT][B];   // scores of blocks jj & 1
@@ -803,7 +836,7 @@ __global__ __launch_bounds__(128) void k_attn_decode(AttnArgs a) {
         const uint32_t size = ks.size_of(jj, rok);
         corrupt |= !rok;
         wave_sync();
-        store_record<NCH_K>(rec_k, size, lane, pre);
+        store_record<NCH_K>(rec_k, pre, lane);
         ks.request(jj + 1, pre);
         __builtin_amdgcn_sched_barrier(0);
         wave_sync();
@@ -865,7 +898,7 @@ __global__ __launch_bounds__(128) void k_attn_decode(AttnArgs a) {
         const uint32_t size = vs.size_of(jj, rok);
         corrupt |= !rok;
         wave_sync();
-        store_record<NCH_V>(rec_v, size, lane, pre);
+        store_record<NCH_V>(rec_v, pre, lane);
         vs.request(jj + 1, pre);
         __builtin_amdgcn_sched_barrier(0);
         wave_sync();
@@ -945,7 +978,7 @@ __global__ __launch_bounds__(64) void k_decompress(GemvArgs a, const uint8_t* pe
   constexpr int REC = max_record_bytes(IS_V, B, 4);
   constexpr int NCH = (REC + 1023) / 1024;
   constexpr int HDR = hdr_offset(IS_V, B);
-  __shared__ __attribute__((aligned(16))) uint8_t rec[REC + 16];
+  __shared__ __attribute__((aligned(16))) uint8_t rec[staging_bytes(REC)];
   const int lane = threadIdx.x;
   const int s = blockIdx.y, j = blockIdx.x;
   const uint8_t* arena = a.arena + (uint64_t)s * a.arena_stride;
@@ -959,7 +992,7 @@ __global__ __launch_bounds__(64) void k_decompress(GemvArgs a, const uint8_t* pe
   }
   u32x4 pre[NCH];
   load_record<NCH>(arena + o, size, lane, pre);
-  store_record<NCH>(rec, size, lane, pre);
+  store_record<NCH>(rec, pre, lane);
   __syncthreads();
   const int pay = payload_offset(IS_V, B, nr);
   int w[NRL];
