@@ -306,17 +306,17 @@ struct KBlock {
   static constexpr int NH = B / 64;
   static constexpr int ROWW = kD + 8;
   static constexpr int PLANE_BYTES = (B / 8) * ROWW * 4;
-  static constexpr int RED_BYTES = GT * 64 * 9 * 4;   // channel-group reduction
-  // The plane and the reduction buffer live in the record's staging buffer:
-  // once a record is decoded into registers its bytes are dead.  With two
-  // 64-slot halves the first half's reduction must not overwrite the second
-  // half's plane rows, so it goes after the plane.
-  static constexpr int SCRATCH_BYTES =
-      NH == 1 ? (PLANE_BYTES > RED_BYTES ? PLANE_BYTES : RED_BYTES) : PLANE_BYTES + RED_BYTES;
+  static constexpr int RED_BYTES = 64 * 9 * 4;        // channel-group reduction, one query
+  // The plane and the reduction live in the record's staging buffer: once a
+  // record is decoded into registers its bytes are dead.  Each half's
+  // reduction reuses that half's plane rows, one query at a time.
+  static constexpr int HALF_BYTES = 8 * ROWW * 4;
+  static_assert(RED_BYTES <= HALF_BYTES, "reduction must fit a half's plane rows");
+  static constexpr int SCRATCH_BYTES = PLANE_BYTES;
 
   float* qs;                                          // [GT][D] q' of the block
   int lane, g8, cg;
-  float qa[GT], qb[GT], qau[GT], qbu[GT];             // queries at channels lane, lane + 64
+  float qau[GT], qbu[GT];                             // queries / unit at channels lane, lane + 64
 
   __device__ __forceinline__ void init(float* qs_, int lane_) {
     qs = qs_;
@@ -330,17 +330,18 @@ struct KBlock {
     for (int g = 0; g < GT; ++g) {
       const bool ok = gq0 + g < G;
       const uint16_t* qp = q + (s * G + gq0 + g) * kD;
-      qa[g] = ok ? f16_bits_to_float(qp[lane]) : 0.f;
-      qb[g] = ok ? f16_bits_to_float(qp[lane + 64]) : 0.f;
-      qau[g] = qa[g] * unit_inv;
-      qbu[g] = qb[g] * unit_inv;
+      qau[g] = (ok ? f16_bits_to_float(qp[lane]) : 0.f) * unit_inv;       // exact: a power of two
+      qbu[g] = (ok ? f16_bits_to_float(qp[lane + 64]) : 0.f) * unit_inv;
     }
   }
 
   // rec: the staged record (size bytes, nr runs); it is overwritten by the
-  // plane and the reduction.  Returns whether the record decoded
-  // consistently.
-  __device__ __forceinline__ bool run(uint8_t* rec, uint32_t size, int nr, float (&score)[GT][NH]) {
+  // plane and the reduction.  sink(g, h, score, ok) takes query g's score of
+  // slot h*64 + lane as soon as it is reduced; ok: the record decoded
+  // consistently (the scores of one that did not are meaningless).  Returns
+  // ok.
+  template <class Sink>
+  __device__ __forceinline__ bool run(uint8_t* rec, uint32_t size, int nr, Sink&& sink) {
     // q' = q * scale (per channel) and beta = q . zero, before the bytes go
     float beta[GT];
     {
@@ -351,14 +352,13 @@ struct KBlock {
       for (int g = 0; g < GT; ++g) {
         qs[g * kD + lane] = qau[g] * sa;
         qs[g * kD + lane + 64] = qbu[g] * sb;
-        beta[g] = wave_sum(fmaf(qa[g], za, qb[g] * zb));
+        beta[g] = wave_sum(fmaf(qau[g], za, qbu[g] * zb)) * fp8_unit();
       }
     }
     uint32_t nib[NRL][4];
     const bool ok = Dec::decode(rec, size, nr, lane, nib);
     wave_sync();                                  // every lane has read the record
     uint32_t* plane = reinterpret_cast<uint32_t*>(rec);
-    float* red = reinterpret_cast<float*>(rec + (NH == 1 ? 0 : PLANE_BYTES));
 #pragma unroll
     for (int k = 0; k < NRL; ++k) {
       const int r = k >> 1, c = lane + 64 * (k & 1);
@@ -397,19 +397,19 @@ struct KBlock {
             for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(qq[g][cc], f[i], acc[g][i]);
         }
       }
-      // reduce the 8 channel groups: red[g][slot][cg], slot = g8*8 + i
-      wave_sync();
-#pragma unroll
-      for (int g = 0; g < GT; ++g)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) red[(g * 64 + g8 * 8 + i) * 9 + cg] = acc[g][i];
-      wave_sync();
+      // reduce the 8 channel groups, one query at a time, in this half's
+      // (now dead) plane rows: red[slot][cg], slot = g8*8 + i
+      float* red = reinterpret_cast<float*>(rec + h * HALF_BYTES);
 #pragma unroll
       for (int g = 0; g < GT; ++g) {
+        wave_sync();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) red[(g8 * 8 + i) * 9 + cg] = acc[g][i];
+        wave_sync();
         float sum = beta[g];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) sum += red[(g * 64 + lane) * 9 + u];
-        score[g][h] = sum;
+        for (int u = 0; u < 8; ++u) sum += red[lane * 9 + u];
+        sink(g, h, sum, ok);
       }
     }
     return ok;
@@ -568,7 +568,6 @@ struct RecordStream {
 template <int B, int BITS, int GT>
 __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
   using KB = KBlock<B, BITS, GT>;
-  constexpr int NH = KB::NH;
   constexpr int REC = max_record_bytes(false, B, 4);
   constexpr int NCH = (REC + 1023) / 1024;
   constexpr int BUF = staging_bytes(REC) > KB::SCRATCH_BYTES ? staging_bytes(REC) : KB::SCRATCH_BYTES;
@@ -603,22 +602,16 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
       rs.request(jj + 1, pre);
       __builtin_amdgcn_sched_barrier(0);
       wave_sync();
-      float score[GT][NH];
-      const bool ok = kb.run(rec, size, (n + kR - 1) / kR, score) && rok;
-      corrupt |= rok && !ok;
       // range-checked stores: slots past n, absent queries and corrupt
       // records write nothing
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        const uint32_t valid = ok ? (uint32_t)max(0, min(64, n - h * 64)) : 0u;
-#pragma unroll
-        for (int g = 0; g < GT; ++g) {
-          const bool gok = gq0 + g < a.G;
-          float* row0 = a.scores + ((int64_t)s * a.G + (gok ? gq0 + g : 0)) * a.ld + (int64_t)j * B + h * 64;
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score[g][h]),
-                                                buffer_rsrc(row0, gok ? 4u * valid : 0u), 4 * lane, 0, 0);
-        }
-      }
+      const bool ok = kb.run(rec, size, (n + kR - 1) / kR, [&](int g, int h, float v, bool dok) {
+        const uint32_t valid = dok && rok ? (uint32_t)max(0, min(64, n - h * 64)) : 0u;
+        const bool gok = gq0 + g < a.G;
+        float* row0 = a.scores + ((int64_t)s * a.G + (gok ? gq0 + g : 0)) * a.ld + (int64_t)j * B + h * 64;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), buffer_rsrc(row0, gok ? 4u * valid : 0u),
+                                              4 * lane, 0, 0);
+      }) && rok;
+      corrupt |= rok && !ok;
     };
     u32x4 pre[NCH];
     rs.request(0, pre);
@@ -653,11 +646,11 @@ __device__ __forceinline__ void reset_ticket(uint32_t* ticket, int lane) {
   if (lane == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// 64-token blocks with one query fit 96 VGPRs (5 waves per SIMD); asking for
-// that occupancy costs at most a couple of values kept in scratch outside the
-// block loop
+// Occupancy asked of the register allocator: 64-token blocks with one query
+// fit 96 VGPRs (5 waves per SIMD), 128-token blocks 168 (3 waves); either
+// costs at most a few values kept in scratch outside the block loop
 template <int B, int GT>
-constexpr int pv_waves_per_eu() { return B == 64 && GT == 1 ? 5 : 1; }
+constexpr int pv_waves_per_eu() { return B == 64 && GT == 1 ? 5 : B == 128 ? 3 : 1; }
 
 template <int B, int BITS, int GT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(pv_waves_per_eu<B, GT>())))
@@ -789,8 +782,15 @@ __device__ __forceinline__ float wave_max_f(float v) {
 // result that underflows is a weight of 0
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Occupancy asked of the register allocator: 3 waves per SIMD (168 VGPRs)
+// for 128-token blocks, where the few values it has to spill are read once
+// per query group; the other shapes keep every value in registers.
 template <int B, int BITS, int GT>
-__global__ __launch_bounds__(128) void k_attn_decode(AttnArgs a) {
+constexpr int attn_waves_per_eu() { return B == 128 ? 3 : 1; }
+
+template <int B, int BITS, int GT>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<B, BITS, GT>())))
+void k_attn_decode(AttnArgs a) {
   using KB = KBlock<B, BITS, GT>;
   using VB = VBlock<B, BITS, GT>;
   constexpr int NH = B / 64;
@@ -840,14 +840,10 @@ __global__ __launch_bounds__(128) void k_attn_decode(AttnArgs a) {
         ks.request(jj + 1, pre);
         __builtin_amdgcn_sched_barrier(0);
         wave_sync();
-        float score[GT][NH];
-        const bool ok = kb.run(rec_k, size, (n + kR - 1) / kR, score) && rok;
+        const bool ok = kb.run(rec_k, size, (n + kR - 1) / kR, [&](int g, int h, float v, bool dok) {
+          ring[jj & 1][g][h * 64 + lane] = dok && rok && h * 64 + lane < n ? v * a.scale_log2e : NEG_INF;
+        }) && rok;
         corrupt |= rok && !ok;
-#pragma unroll
-        for (int g = 0; g < GT; ++g)
-#pragma unroll
-          for (int h = 0; h < NH; ++h)
-            ring[jj & 1][g][h * 64 + lane] = ok && h * 64 + lane < n ? score[g][h] * a.scale_log2e : NEG_INF;
         __syncthreads();                            // block jj goes to the V wave
       }
       __syncthreads();                              // the ring is reused
