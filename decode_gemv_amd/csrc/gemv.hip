@@ -783,10 +783,12 @@ __device__ __forceinline__ float wave_max_f(float v) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Occupancy asked of the register allocator: 3 waves per SIMD (168 VGPRs)
-// for 128-token blocks, where the few values it has to spill are read once
-// per query group; the other shapes keep every value in registers.
+// for 128-token blocks and 5 (96 VGPRs) for 2-bit 64-token blocks with one
+// query, where the few values it has to spill are read once per query group
+// (measured: 2-bit 266 -> 249 us; at 4 bits 5 waves gain nothing).  The
+// other shapes keep every value in registers.
 template <int B, int BITS, int GT>
-constexpr int attn_waves_per_eu() { return B == 128 ? 3 : 1; }
+constexpr int attn_waves_per_eu() { return B == 128 ? 3 : B == 64 && BITS == 2 && GT == 1 ? 5 : 1; }
 
 template <int B, int BITS, int GT>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<B, BITS, GT>())))
