@@ -17,7 +17,7 @@ class Config:
     bits: int = 4
     block: int = 64
     run: int = 32
-    permute: bool = True
+    permute: int = 1          # 0 identity, 1 greedy grouping, 2 sort key (oracle.perm)
 
     def __post_init__(self):
         assert self.bits in (2, 3, 4), "b must be 2, 3 or 4"
@@ -25,6 +25,7 @@ class Config:
         assert self.run == 32, "R must be 32"
         assert self.block % self.run == 0
         assert self.head_dim == 128, "D must be 128"
+        assert int(self.permute) in (0, 1, 2), "permute must be 0, 1 or 2"
 
     @property
     def levels(self) -> int:

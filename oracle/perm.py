@@ -20,6 +20,19 @@ Slot i of the block then holds token perm[i].  If this order does not make
 the block's packed payload strictly smaller than the identity order (summed
 over K and V, every run counted at its full R slots), the identity is used.
 Everything here is integer and deterministic.
+
+A second, cheaper rule (this build's, offered as a variant of the same
+rearrangement step) sorts the tokens by one integer key:
+
+    s[t] = sum_c qK[t,c] + sum_c qV[t,c]
+    order = tokens ascending by (s[t], t)
+
+with the same identity fallback.  It costs one pass over the ints and one
+sort instead of a distance pass per run, and it groups tokens whose
+quantised vectors have clearly different totals (a clustered block whose
+centroids differ) but not tokens that merely share a total.
+
+Modes: 0 identity, 1 greedy grouping, 2 sort key.
 """
 
 from __future__ import annotations
@@ -47,6 +60,12 @@ def greedy_order(qk: np.ndarray, qv: np.ndarray, run: int) -> List[int]:
     return order
 
 
+def sort_key_order(qk: np.ndarray, qv: np.ndarray) -> List[int]:
+    """The sort-key order (before the identity fallback)."""
+    total = np.asarray(qk, np.int64).sum(axis=1) + np.asarray(qv, np.int64).sum(axis=1)
+    return sorted(range(qk.shape[0]), key=lambda t: (int(total[t]), t))
+
+
 def payload_words(qk: np.ndarray, qv: np.ndarray, order, run: int) -> int:
     """Packed payload size in 32-bit words of K plus V under slot order ``order``.
 
@@ -58,13 +77,15 @@ def payload_words(qk: np.ndarray, qv: np.ndarray, order, run: int) -> int:
     return int(wk.sum() + wv.sum())
 
 
-def block_permutation(qk: np.ndarray, qv: np.ndarray, run: int, permute: bool = True) -> np.ndarray:
-    """Slot -> token index for one block (greedy order or the identity)."""
+def block_permutation(qk: np.ndarray, qv: np.ndarray, run: int, permute: int = 1) -> np.ndarray:
+    """Slot -> token index for one block: the mode's order if it makes the
+    payload strictly smaller, else the identity (mode 0: always identity)."""
     n = qk.shape[0]
     ident = list(range(n))
-    if not permute or n <= 1:
+    mode = int(permute)
+    if mode == 0 or n <= 1:
         return np.array(ident, dtype=np.int64)
-    order = greedy_order(qk, qv, run)
+    order = greedy_order(qk, qv, run) if mode == 1 else sort_key_order(qk, qv)
     if payload_words(qk, qv, order, run) < payload_words(qk, qv, ident, run):
         return np.array(order, dtype=np.int64)
     return np.array(ident, dtype=np.int64)

@@ -34,7 +34,7 @@ def cfg(bits=4, block=64, D=128, R=32, permute=1):
 
 @pytest.mark.parametrize("bad,code", [
     (dict(D=64), _lib.EUNSUPPORTED), (dict(bits=5), _lib.EUNSUPPORTED), (dict(bits=1), _lib.EUNSUPPORTED),
-    (dict(block=32), _lib.EUNSUPPORTED), (dict(R=16), _lib.EUNSUPPORTED), (dict(permute=2), _lib.EINVAL),
+    (dict(block=32), _lib.EUNSUPPORTED), (dict(R=16), _lib.EUNSUPPORTED), (dict(permute=3), _lib.EINVAL),
 ])
 def test_unsupported_configs_are_rejected(lib, bad, code):
     s = _lib.Sizes()

@@ -72,21 +72,67 @@ def test_grouping_recovers_clusters():
     assert record.run_widths(code.qk_slots, 32)[0].max() == 0
 
 
+def test_sort_key_order_against_exhaustive_search():
+    """Among all orders of a tiny block, exactly one has strictly increasing
+    (total, index) pairs; the sort-key order must be that one."""
+    rng = np.random.default_rng(11)
+    for trial in range(40):
+        n = int(rng.integers(1, 7))
+        qk = rng.integers(0, 3, (n, 3))          # small values: many equal totals
+        qv = rng.integers(0, 3, (n, 2))
+        tot = [int(qk[t].sum() + qv[t].sum()) for t in range(n)]
+        inc = [list(o) for o in itertools.permutations(range(n))
+               if all((tot[o[i]], o[i]) < (tot[o[i + 1]], o[i + 1]) for i in range(n - 1))]
+        assert len(inc) == 1
+        assert perm.sort_key_order(qk, qv) == inc[0]
+
+
+def test_sort_key_groups_clusters_with_distinct_totals():
+    """Shuffled clusters whose quantised totals differ: sorting by the total
+    puts each cluster in one run, every run has width 0, and the order is kept."""
+    k, v = kvsynth.structured_kv(64, 128, 64, 32, seed=4, noise=0.0)
+    cfg = Config(bits=4, block=64, permute=2)
+    code = stream.encode_block(k, v, cfg)
+    tot = code.qk_slots.sum(axis=1).astype(np.int64) + code.qv_slots.sum(axis=1)
+    assert tot[0] != tot[32], "the two clusters must have different totals for this pin"
+    rows = k[code.perm].astype(np.float64)
+    for g in (0, 32):
+        assert np.all(rows[g:g + 32] == rows[g])
+    assert record.run_widths(code.qk_slots, 32)[0].max() == 0
+    assert record.run_widths(code.qv_slots, 32)[0].max() == 0
+    assert list(code.perm) != list(range(64))
+
+
+def test_sort_key_falls_back_to_identity():
+    """Identical tokens: no order is strictly smaller, so the identity stays;
+    iid blocks: whatever is chosen is never larger than the identity."""
+    qk = np.full((64, 128), 5)
+    qv = np.full((64, 128), 9)
+    assert list(perm.block_permutation(qk, qv, 32, 2)) == list(range(64))
+    rng = np.random.default_rng(5)
+    qk = rng.integers(0, 16, (64, 128))
+    qv = rng.integers(0, 16, (64, 128))
+    p = perm.block_permutation(qk, qv, 32, 2)
+    assert perm.payload_words(qk, qv, p, 32) <= perm.payload_words(qk, qv, list(range(64)), 32)
+
+
 def test_attention_is_unchanged_by_the_permutation():
     k, v = kvsynth.structured_kv(300, 128, 64, 32, seed=7)
     q = np.random.default_rng(2).standard_normal((2, 128)).astype(np.float16)
     outs = []
-    for p in (True, False):
+    for p in (1, 2, 0):
         c = stream.compress(k, v, Config(bits=4, block=64, permute=p))
         kh, vh, _, _ = stream.decode_stream(c)
         s = attention.qk(q, kh)
         outs.append(attention.pv(attention.softmax(s, 128), vh))
         # the dequantised rows are the same multiset: equal after un-permuting
-        if p:
-            kt, vt = stream.token_order(c, kh), stream.token_order(c, vh)
+        kt, vt = stream.token_order(c, kh), stream.token_order(c, vh)
+        if p == 1:
+            k1, v1 = kt, vt
         else:
-            assert np.array_equal(kt, kh) and np.array_equal(vt, vh)
+            assert np.array_equal(kt, k1) and np.array_equal(vt, v1)
     assert attention.rel_l2(outs[0], outs[1]) < 1e-12
+    assert attention.rel_l2(outs[0], outs[2]) < 1e-12
 
 
 def test_gemv_definitions_against_loops():
