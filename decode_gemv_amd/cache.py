@@ -33,9 +33,10 @@ class PackedKVCache:
     """
 
     def __init__(self, n_streams: int, max_tokens: int, bits: int = 4, block: int = 64,
-                 permute: bool = True, device: str = "cuda"):
+                 permute: int = 1, device: str = "cuda"):
+        # permute: 0 identity, 1 greedy grouping, 2 sort key (True/False = 1/0)
         lib = _lib.load()
-        self.cfg = _lib.Config(D, bits, block, 32, int(bool(permute)))
+        self.cfg = _lib.Config(D, bits, block, 32, int(permute))
         sz = _lib.Sizes()
         _lib.check(lib.packkv_cache_sizes(ctypes.byref(self.cfg), n_streams, max_tokens, ctypes.byref(sz)),
                    "packkv_cache_sizes")

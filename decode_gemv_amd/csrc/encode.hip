@@ -8,7 +8,8 @@
 //     comparisons on fp16 values), 0 for a constant group;
 //   * q = rint((x - min) / scale) in fp64 (exact subtraction, IEEE division,
 //     round half to even), clamped to [0, L];
-//   * permutation = greedy L1 grouping with key (distance, index), identity
+//   * permutation = greedy L1 grouping with key (distance, index), or (mode
+//     2) the tokens sorted by (total of their K and V ints, index); identity
 //     unless the payload shrinks strictly;
 //   * run width = bit_length(max - min), u = q - min packed LSB-first.
 // This file must be built without fast-math flags.
@@ -237,7 +238,29 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
     __syncthreads();
   } else {
     if (tid < 128) order[tid] = (uint8_t)tid;
-    if (a.permute && n > 1) {
+    if (a.permute == 2 && n > 1) {
+      // sort key: the total of the token's K and V ints (at most
+      // 2 * 128 * 15 < 2^12), ties by index; the slot is the key's rank
+      if (tid < n) {
+        const uint32_t* rt = reinterpret_cast<const uint32_t*>(qk + tid * kD);
+        const uint32_t* vt = reinterpret_cast<const uint32_t*>(qv + tid * kD);
+        uint32_t total = 0;
+        for (int i = 0; i < kD / 4; ++i) {
+          total = __builtin_amdgcn_sad_u8(rt[i], 0u, total);
+          total = __builtin_amdgcn_sad_u8(vt[i], 0u, total);
+        }
+        key[tid] = (total << 8) | (uint32_t)tid;
+      }
+      __syncthreads();
+      if (tid < n) {
+        const uint32_t mine = key[tid];
+        int rank = 0;
+        for (int u = 0; u < n; ++u) rank += key[u] < mine;
+        order[rank] = (uint8_t)tid;
+      }
+      __syncthreads();
+    }
+    if (a.permute == 1 && n > 1) {
       if (tid < 128) alive[tid] = tid < n;
       __syncthreads();
       for (int r = 0; r < nr; ++r) {
@@ -276,7 +299,9 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
         }
         __syncthreads();
       }
-      // identity fallback: keep the grouping only if the payload shrinks.
+    }
+    if (a.permute && n > 1) {
+      // identity fallback: keep the new order only if the payload shrinks.
       if (tid < 2) red[tid] = 0;
       __syncthreads();
       // The statistics of both orders are kept in registers (at most 4

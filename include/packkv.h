@@ -73,7 +73,11 @@ typedef struct {
   int32_t bits;         /* b: 2, 3 or 4                                      */
   int32_t block_tokens; /* B: 64 or 128                                      */
   int32_t run_tokens;   /* R: must be 32                                     */
-  int32_t permute;      /* 1: greedy grouping inside blocks, 0: identity     */
+  int32_t permute;      /* token order inside blocks (Fig. 2 caption, step   */
+                        /* (1)): 0 identity, 1 greedy L1 grouping, 2 sorted  */
+                        /* by the total of the token's K and V ints; modes   */
+                        /* 1 and 2 fall back to the identity unless the      */
+                        /* block's payload shrinks.  Other values: EINVAL    */
 } packkv_config_t;
 
 /*

@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-4
 
 CASES = [
-    # id, bits, block, S, T, permute, law
+    # id, bits, block, S, T, permute (0 identity, 1 greedy, 2 sort key), law
     ("b4B64-gauss", 4, 64, 3, 200, True, "gauss"),
     ("b4B64-struct", 4, 64, 2, 331, True, "struct"),
     ("b4B64-mixed", 4, 64, 2, 256, True, "mixed"),
@@ -27,6 +27,10 @@ CASES = [
     ("b3B128-struct", 3, 128, 2, 390, True, "struct"),
     ("b2B128-mixed", 2, 128, 2, 129, True, "mixed"),
     ("b4B64-identity", 4, 64, 2, 150, False, "struct"),
+    ("b4B64-sortkey-struct", 4, 64, 2, 331, 2, "struct"),
+    ("b4B64-sortkey-gauss", 4, 64, 2, 200, 2, "gauss"),
+    ("b3B128-sortkey-struct", 3, 128, 2, 390, 2, "struct"),
+    ("b2B64-sortkey-mixed", 2, 64, 2, 190, 2, "mixed"),
     ("b4B64-one-token", 4, 64, 1, 1, True, "gauss"),
     ("b4B64-grid", 4, 64, 2, 64, True, "grid"),
     ("b3B64-subnormal", 3, 64, 2, 100, True, "subnormal"),
@@ -137,15 +141,17 @@ def test_softmax_helper(torch_dev):
     assert np.all(np.abs(p.sum(1) - 1) < 1e-5)
 
 
-@pytest.mark.parametrize("bits,block,t0,steps", [(3, 64, 60, 70), (4, 128, 0, 130), (2, 64, 64, 1)])
-def test_append_matches_one_shot(torch_dev, bits, block, t0, steps):
+@pytest.mark.parametrize("bits,block,t0,steps,law,permute", [
+    (3, 64, 60, 70, "gauss", 1), (4, 128, 0, 130, "gauss", 1), (2, 64, 64, 1, "gauss", 1),
+    (4, 64, 30, 100, "struct", 2)])
+def test_append_matches_one_shot(torch_dev, bits, block, t0, steps, law, permute):
     torch, dev = torch_dev
     from decode_gemv_amd import PackedKVCache
     S = 2
-    K, V = make_kv("gauss", S, t0 + steps + 5, block, seed=3)
-    c = PackedKVCache(S, t0 + steps + 10, bits=bits, block=block, device=str(dev))
+    K, V = make_kv(law, S, t0 + steps + 5, block, seed=3)
+    c = PackedKVCache(S, t0 + steps + 10, bits=bits, block=block, permute=permute, device=str(dev))
     Kd, Vd = torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev)
-    say("append", bits, block, t0, steps)
+    say("append", bits, block, t0, steps, law, permute)
     if t0:
         c.compress(Kd[:, :t0].contiguous(), Vd[:, :t0].contiguous())
     for t in range(t0, t0 + steps):
@@ -153,7 +159,7 @@ def test_append_matches_one_shot(torch_dev, bits, block, t0, steps):
     # a multi-token append crossing a block boundary
     c.append(Kd[:, t0 + steps:].contiguous(), Vd[:, t0 + steps:].contiguous())
     assert c.check() == 0
-    refs = oracle_streams(K, V, bits, block)
+    refs = oracle_streams(K, V, bits, block, permute)
     assert c.n_tokens == K.shape[1]
     assert_state_equal(c, refs)
 
