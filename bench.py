@@ -65,12 +65,12 @@ def generate(w: kvsynth.Workload, torch, dev):
     return K, V
 
 
-def cpu_baseline(w: kvsynth.Workload, n_streams: int, n_steps: int) -> dict:
+def cpu_baseline(w: kvsynth.Workload, n_streams: int, n_steps: int, permute: int = 1) -> dict:
     """The fp64 oracle's decode steps on a sample of streams, single-threaded."""
     from threadpoolctl import threadpool_limits
     import oracle
     from oracle import stream as ostream, attention
-    cfg = oracle.Config(bits=w.bits, block=w.block)
+    cfg = oracle.Config(bits=w.bits, block=w.block, permute=permute)
     with threadpool_limits(limits=1):
         caches = []
         for s in range(n_streams):
@@ -229,6 +229,8 @@ def main():
     ap.add_argument("--cpu-streams", type=int, default=4, help="streams in the oracle's timed sample")
     ap.add_argument("--cpu-steps", type=int, default=30, help="decode steps per sampled stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--permute", type=int, default=1, choices=(0, 1, 2),
+                    help="token order inside blocks: 0 identity, 1 greedy grouping, 2 sort key")
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
                     help="size of a plain device copy run after timing (counter calibration)")
     ap.add_argument("--summarize", metavar="DIR",
@@ -255,7 +257,7 @@ def main():
     t = time.perf_counter()
     K, V = generate(w, torch, dev)
     log(f"inputs generated in {time.perf_counter() - t:.1f} s")
-    cache = PackedKVCache(S, T_max, bits=w.bits, block=w.block, device="cuda:0")
+    cache = PackedKVCache(S, T_max, bits=w.bits, block=w.block, permute=args.permute, device="cuda:0")
     torch.cuda.synchronize()
     t = time.perf_counter()
     cache.compress(K, V)
@@ -387,7 +389,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
-        cpu = cpu_baseline(w, args.cpu_streams, args.cpu_steps)
+        cpu = cpu_baseline(w, args.cpu_streams, args.cpu_steps, args.permute)
 
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -396,7 +398,7 @@ def main():
         "data": "synthetic (seeded kvsynth generator; stands in for the pages' models and benchmarks)",
         "config": {"workload": w.key, "batch": w.batch, "kv_heads": w.kv_heads, "group": G,
                    "tokens": T0, "head_dim": D, "bits": w.bits, "block": w.block, "run": 32,
-                   "append_per_step": 1, "parallelism": "single-gpu"},
+                   "append_per_step": 1, "permute": args.permute, "parallelism": "single-gpu"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "kernels_ms": {"append": round(t_app, 4), "attention": round(t_attn, 4), "qk_gemv": round(t_qk, 4),
                        "softmax": round(t_sm, 4), "pv_gemv": round(t_pv, 4)},

@@ -54,7 +54,7 @@ class Workload:
     head_dim: int       # D
     bits: int           # quantisation bits (b)
     block: int          # token block (B)
-    v_law: str          # "gauss" or "bimodal"
+    v_law: str          # "gauss", "bimodal" or "struct" (clustered K and V)
     append_steps: int = 0
 
     @property
@@ -81,6 +81,9 @@ WORKLOADS: Dict[str, Workload] = {
     # prefill 64K then 256 single-token appends
     "append-64k": Workload("append-64k", 32, 8, 1, 65536, 128, 3, 64, "gauss",
                            append_steps=256),
+    # the llama7b-32k shape on clustered data (structured_kv), where the
+    # token order inside a block decides the run widths
+    "struct-32k": Workload("struct-32k", 8, 32, 1, 32768, 128, 4, 64, "struct"),
 }
 
 
@@ -93,6 +96,8 @@ def outlier_channels(head: int, head_dim: int = 128, seed: int = 0) -> np.ndarra
 def _draw_v(rng: np.random.Generator, shape, law: str) -> np.ndarray:
     if law == "gauss":
         return rng.standard_normal(shape, dtype=np.float32)
+    if law == "struct":                 # appended tokens of the clustered workload
+        return rng.standard_normal(shape, dtype=np.float32)
     if law == "bimodal":
         sign = rng.choice(np.array([-1.0, 1.0], dtype=np.float32), size=shape)
         return sign + np.float32(0.3) * rng.standard_normal(shape, dtype=np.float32)
@@ -104,6 +109,8 @@ def stream_kv(w: Workload, s: int, seed: int = 0,
     """fp16 K and V of stream ``s``, each [tokens, D] (token order)."""
     T = w.tokens if tokens is None else tokens
     D = w.head_dim
+    if w.v_law == "struct":
+        return structured_kv(T, D, w.block, 32, seed=(seed << 20) + s)
     rng = np.random.default_rng([seed, 2, s])
     k = rng.standard_normal((T, D), dtype=np.float32)
     k[:, outlier_channels(s % w.kv_heads, D, seed)] *= np.float32(OUTLIER_GAIN)
