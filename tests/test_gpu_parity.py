@@ -105,7 +105,7 @@ def test_encoder_and_decoder_bit_exact(torch_dev, case):
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-@pytest.mark.parametrize("G", [1, 3, 4])
+@pytest.mark.parametrize("G", [1, 3, 4, 9])
 def test_gemvs_within_tolerance(torch_dev, case, G):
     torch, dev = torch_dev
     cid, bits, block, S, T, permute, law = case
@@ -237,7 +237,7 @@ def test_pv_weight_laws(torch_dev, law):
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-@pytest.mark.parametrize("G", [1, 3, 4])
+@pytest.mark.parametrize("G", [1, 3, 4, 9])
 def test_fused_attention_within_tolerance(torch_dev, case, G):
     """Fused K GEMV + softmax + V GEMV against the fp64 oracle's three steps."""
     torch, dev = torch_dev
