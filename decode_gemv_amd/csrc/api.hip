@@ -208,10 +208,11 @@ int packkv_append_tokens(packkv_cache_t* c, const void* k_f16, const void* v_f16
     const int64_t T = c->n_tokens;
     const int n_tail = (int)(T % B);
     const int cnt = (n_new - done) < (B - n_tail) ? (n_new - done) : (B - n_tail);
-    e = hip_status(launch_stage_tail((const uint16_t*)k_f16 + (int64_t)done * kD,
-                                     (const uint16_t*)v_f16 + (int64_t)done * kD, (int64_t)n_new * kD,
-                                     c->tail_k, c->tail_v, B, n_tail, cnt, c->n_streams, st));
-    if (e) return e;
+    // the encoder reads the new tokens from the caller and stages them itself
+    a.new_k = (const uint16_t*)k_f16 + (int64_t)done * kD;
+    a.new_v = (const uint16_t*)v_f16 + (int64_t)done * kD;
+    a.new_stream = (int64_t)n_new * kD;
+    a.new_at = n_tail;
     a.block0 = (int)(T / B);
     a.n_tokens = T + cnt;
     if ((e = hip_status(launch_encode(a, c->n_streams, 1, st)))) return e;

@@ -164,10 +164,21 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
   // (1) quantise.  K per channel over the block's tokens: the block's raw K
   // is staged through LDS with 16-byte loads by every thread (one memory
   // latency), then thread c reads its channel from there.
+  const bool fresh = a.mode == kTail && a.new_k != nullptr;
   {
     const uint4* src = reinterpret_cast<const uint4*>(ks);
     uint4* dst = reinterpret_cast<uint4*>(rawk);
-    for (int i = tid; i < n * (kD / 8); i += NT) dst[i] = src[i];
+    for (int i = tid; i < n * (kD / 8); i += NT) {
+      const int t = i / (kD / 8);
+      if (fresh && t >= a.new_at) {
+        // an appended token: read it from the caller and keep it in the staging
+        const uint4 u = reinterpret_cast<const uint4*>(a.new_k + s * a.new_stream + (int64_t)(t - a.new_at) * kD)[i % (kD / 8)];
+        const_cast<uint4*>(src)[i] = u;
+        dst[i] = u;
+      } else {
+        dst[i] = src[i];
+      }
+    }
   }
   __syncthreads();
   if (tid < kD) {
@@ -190,12 +201,17 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
     const int CPT = kD / TPT;                        // 32 or 64 channels per thread
     const int t = tid / TPT, part = tid % TPT;
     const bool on = t < n;
+    const bool appended = fresh && on && t >= a.new_at;
     uint32_t w[32];                                  // up to 64 fp16, two per word
-    const uint4* src = reinterpret_cast<const uint4*>(vs + (int64_t)(on ? t : 0) * kD + part * CPT);
+    uint4* stage = reinterpret_cast<uint4*>(const_cast<uint16_t*>(vs) + (int64_t)(on ? t : 0) * kD + part * CPT);
+    const uint4* src = appended
+        ? reinterpret_cast<const uint4*>(a.new_v + s * a.new_stream + (int64_t)(t - a.new_at) * kD + part * CPT)
+        : stage;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (i < CPT / 8) {
         const uint4 u = src[i];
+        if (appended) stage[i] = u;                  // keep it in the staging
         w[4 * i] = u.x; w[4 * i + 1] = u.y; w[4 * i + 2] = u.z; w[4 * i + 3] = u.w;
       }
     }

@@ -15,6 +15,14 @@ struct EncArgs {
   int64_t n_tokens;         // total tokens per stream after this call
   int32_t bits, B, permute, mode;
   int32_t block0;           // kTail: index of the block being (re)encoded
+  // kTail: tokens appended by this call, [S][new_cnt][D] fp16 (new_stream
+  // elements apart), at positions new_at.. of the open block; they are read
+  // from here and copied into the raw tail staging (k, v) as they are read.
+  // Null: every token comes from the staging.
+  const uint16_t* new_k;
+  const uint16_t* new_v;
+  int64_t new_stream;
+  int32_t new_at;
   uint8_t* k_arena;
   uint8_t* v_arena;
   uint64_t arena_limit;     // usable bytes per stream region
