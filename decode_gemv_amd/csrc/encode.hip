@@ -281,10 +281,13 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
       __syncthreads();
       for (int r = 0; r < nr; ++r) {
         const int base = r * kR;
-        // seed = smallest remaining token index
+        // seed = smallest remaining token index (one LDS atomic per wave)
         if (tid == 0) red[0] = 0xFFu;
         __syncthreads();
-        if (tid < n && alive[tid]) atomicMin(&red[0], (uint32_t)tid);
+        {
+          const uint64_t b = __ballot(tid < n && alive[tid]);
+          if ((tid & 63) == 0 && b != 0) atomicMin(&red[0], (uint32_t)(tid + __builtin_ctzll(b)));
+        }
         __syncthreads();
         const int sd = (int)red[0];
         if (tid < n) {
@@ -340,8 +343,12 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
           sum_i += iw[e];
         }
       }
-      atomicAdd(&red[0], sum_g);
-      atomicAdd(&red[1], sum_i);
+      // one LDS atomic per wave, not per thread (they serialise on one word)
+      const uint32_t wave_g = (uint32_t)wave_sum_i((int)sum_g), wave_i = (uint32_t)wave_sum_i((int)sum_i);
+      if ((tid & 63) == 0) {
+        atomicAdd(&red[0], wave_g);
+        atomicAdd(&red[1], wave_i);
+      }
       __syncthreads();
       const bool keep = red[0] < red[1];
       __syncthreads();
