@@ -535,16 +535,16 @@ struct VBlock {
 };
 
 // ---------------------------------------------------------------------------
-// Streaming skeleton shared by the GEMVs.  A workgroup (one wave) takes J
-// consecutive blocks of one stream.  Records are staged into LDS from
-// registers; two are in flight, alternating between the register sets of a
-// pair: block jj + 2 is requested while block jj is processed.  A scheduling
-// barrier keeps each request's loads together, so the wait for one record
-// never has to drain the other.  The loop body has no exits: a missing block
-// (jj >= nj) is requested as zero bytes, and a missing or corrupt block
-// contributes nothing (an exit inside the body would give the wait-count
-// analysis a path on which only one register set has loads in flight, and
-// it would then drain both at every block).
+// Streaming skeleton shared by the GEMVs and by each wave of fused
+// attention: a wave walks J consecutive blocks of one stream.  Records are
+// staged into LDS from registers with one record in flight: block jj + 1 is
+// requested into the registers that block jj has just left for LDS, while
+// block jj is processed.  A scheduling barrier keeps the request's loads
+// together.  The loop body has no exits: a missing block (jj >= nj) is
+// requested as zero bytes, and a missing or corrupt block contributes
+// nothing (an exit inside the body would give the wait-count analysis a path
+// with a different set of loads in flight, and it would then drain the load
+// queue at every block).
 template <int NCH, int REC>
 struct RecordStream {
   const uint8_t* arena;
@@ -760,14 +760,15 @@ void k_pv_gemv(GemvArgs a) {
 //   out[g] = sum_t softmax_t(scale * q_g . K_hat[t]) V_hat[t]
 //
 // in one pass over both packed caches, with no scores or weights in HBM.
-// A workgroup takes J consecutive blocks of one stream.  For each block the
-// K record gives the scores (KBlock), a running-max softmax update turns
-// them into weights exp(s - m) (earlier sums are rescaled when m grows), and
-// the V record of the same block takes those weights (VBlock).  The record
-// stream alternates K, V, K, V with the next record always in flight.  Each
-// split leaves (partial out[D], its max m, its weight sum l); the last
-// workgroup of the stream merges the splits in split order with the usual
-// rescaling.
+// A workgroup of two waves takes J consecutive blocks of one stream.  Wave 0
+// streams the K records: for each block the K block code gives the scores,
+// which go to an LDS slot (block jj & 1).  Wave 1 streams the V records: a
+// running-max softmax update turns block jj's scores into weights exp(s - m)
+// (earlier sums are rescaled when m grows), and the V block code takes them
+// with the V record of the same block.  One workgroup barrier per block hands
+// the scores over, so wave 0 scores block jj + 1 while wave 1 finishes block
+// jj.  Each split leaves (partial out[D], its max m, its weight sum l); the
+// last workgroup of the stream merges the splits with the usual rescaling.
 __device__ __forceinline__ float wave_max_f(float v) {
   // DPP with bound_ctrl off: lanes without a source keep their own value
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x111, 0xF, 0xF, false)));
