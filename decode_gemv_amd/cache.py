@@ -187,6 +187,34 @@ class PackedKVCache:
                 "k_words": o[12], "v_words": o[13], "k_runs": o[14], "v_runs": o[15]}
 
 
+def attention_multi_workspace(caches, group: int) -> torch.Tensor:
+    """A zero-filled workspace for attention_multi over `caches` (reusable)."""
+    need = int(_lib.load().packkv_attention_multi_workspace_bytes(ctypes.byref(caches[0]._c), group, len(caches)))
+    return torch.zeros(max(need, 16), dtype=torch.uint8, device=caches[0].k_arena.device)
+
+
+def attention_multi(caches, q: torch.Tensor, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """PackedKVCache.attention for several caches of one shape (e.g. a
+    model's layers) in one launch: q fp16 [L][S][G][D] -> out fp32 [L][S][G][D]."""
+    L, S, G, d = q.shape
+    if L != len(caches) or L < 1:
+        raise ValueError("q must have one [S][G][D] slice per cache")
+    if q.dtype != torch.float16 or d != D or not q.is_contiguous():
+        raise ValueError("q must be contiguous fp16 [L][S][G][D]")
+    if out is None:
+        out = torch.empty(L, S, G, D, dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (L, S, G, D) or not out.is_contiguous():
+        raise ValueError("out must be contiguous fp32 [L][S][G][D]")
+    ws = attention_multi_workspace(caches, G) if workspace is None else workspace
+    sc = D ** -0.5 if scale is None else float(scale)
+    arr = (ctypes.POINTER(_lib.CacheT) * L)(*[ctypes.pointer(c._c) for c in caches])
+    _lib.check(_lib.load().packkv_attention_decode_multi(arr, L, _ptr(q), G, sc, _ptr(out), _ptr(ws),
+                                                         ws.numel() * ws.element_size(), _stream()),
+               "packkv_attention_decode_multi")
+    return out
+
+
 def softmax_rows(scores: torch.Tensor, T: int, scale: float, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """p = softmax(scores * scale) over the first T entries of each row ([..., ld] fp32)."""
     if scores.dtype != torch.float32 or not scores.is_contiguous():

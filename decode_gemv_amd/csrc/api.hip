@@ -268,21 +268,30 @@ uint64_t packkv_attention_workspace_bytes(const packkv_cache_t* c, int32_t group
   return attn_partial_bytes(c, group) + (((uint64_t)c->n_streams * 4u + 255u) & ~(uint64_t)255u);
 }
 
-int packkv_attention_decode(const packkv_cache_t* c, const void* q_f16, int32_t group, float scale, float* out,
-                            void* workspace, uint64_t ws_bytes, void* stream) {
+// Decode attention over n caches of one shape, in launches of up to
+// kAttnMaxCaches caches.
+static int attention_decode(const packkv_cache_t* const* cs, int32_t n, const void* q_f16, int32_t group,
+                            float scale, float* out, void* workspace, uint64_t ws_bytes, void* stream) {
+  if (!cs || n < 1) return PACKKV_EINVAL;
+  const packkv_cache_t* c = cs[0];
   int e = check_cache(c);
   if (e) return e;
+  for (int32_t i = 1; i < n; ++i) {
+    const packkv_cache_t* d = cs[i];
+    if ((e = check_cache(d))) return e;
+    if (d->cfg.bits != c->cfg.bits || d->cfg.block_tokens != c->cfg.block_tokens ||
+        d->n_streams != c->n_streams || d->max_tokens != c->max_tokens || d->n_tokens != c->n_tokens ||
+        d->arena_stride != c->arena_stride)
+      return PACKKV_EINVAL;
+  }
   if (!q_f16 || !out || !workspace || group < 1 || !(scale > 0.f) || !std::isfinite(scale)) return PACKKV_EINVAL;
   if (c->n_tokens < 1) return PACKKV_ESTATE;
-  if (ws_bytes < packkv_attention_workspace_bytes(c, group)) return PACKKV_EINVAL;
+  const uint64_t per_cache = packkv_attention_workspace_bytes(c, group);
+  if (ws_bytes < per_cache * (uint64_t)n) return PACKKV_EINVAL;
   const GemvArgs g = gemv_args(c, true);      // the split-merge work division
   AttnArgs a;
   memset(&a, 0, sizeof(a));
-  a.k_arena = c->k_arena;
-  a.v_arena = c->v_arena;
   a.arena_stride = c->arena_stride;
-  a.k_off = c->k_off;
-  a.v_off = c->v_off;
   a.off_stride = g.off_stride;
   a.n_tokens = c->n_tokens;
   a.nb = g.nb;
@@ -291,12 +300,37 @@ int packkv_attention_decode(const packkv_cache_t* c, const void* q_f16, int32_t 
   a.splits = g.splits;
   a.G = group;
   a.scale_log2e = scale * 1.4426950408889634f;
-  a.q = (const uint16_t*)q_f16;
-  a.ws = (float*)workspace;
-  a.tickets = (uint32_t*)((uint8_t*)workspace + attn_partial_bytes(c, group));
-  a.out = out;
-  a.status = c->status;
-  return hip_status(launch_attention(a, c->cfg.block_tokens, c->n_streams, (hipStream_t)stream));
+  a.qo_stride = (int64_t)c->n_streams * group * kD;
+  a.ws_stride = per_cache;
+  a.partial_bytes = attn_partial_bytes(c, group);
+  for (int32_t i0 = 0; i0 < n; i0 += kAttnMaxCaches) {
+    const int32_t m = n - i0 < kAttnMaxCaches ? n - i0 : kAttnMaxCaches;
+    for (int32_t i = 0; i < m; ++i) {
+      const packkv_cache_t* d = cs[i0 + i];
+      a.cache[i] = AttnCache{d->k_arena, d->v_arena, d->k_off, d->v_off, d->status};
+    }
+    a.q = (const uint16_t*)q_f16 + i0 * a.qo_stride;
+    a.out = out + i0 * a.qo_stride;
+    a.ws = (uint8_t*)workspace + (uint64_t)i0 * per_cache;
+    if ((e = hip_status(launch_attention(a, c->cfg.block_tokens, c->n_streams, m, (hipStream_t)stream)))) return e;
+  }
+  return PACKKV_OK;
+}
+
+int packkv_attention_decode(const packkv_cache_t* c, const void* q_f16, int32_t group, float scale, float* out,
+                            void* workspace, uint64_t ws_bytes, void* stream) {
+  return attention_decode(&c, 1, q_f16, group, scale, out, workspace, ws_bytes, stream);
+}
+
+int packkv_attention_decode_multi(const packkv_cache_t* const* caches, int32_t n_caches, const void* q_f16,
+                                  int32_t group, float scale, float* out, void* workspace, uint64_t ws_bytes,
+                                  void* stream) {
+  return attention_decode(caches, n_caches, q_f16, group, scale, out, workspace, ws_bytes, stream);
+}
+
+uint64_t packkv_attention_multi_workspace_bytes(const packkv_cache_t* c, int32_t group, int32_t n_caches) {
+  if (n_caches < 1) return 0;
+  return packkv_attention_workspace_bytes(c, group) * (uint64_t)n_caches;
 }
 
 int packkv_decompress(const packkv_cache_t* c, int32_t which, int32_t mode, void* out, void* stream) {

@@ -810,6 +810,12 @@ void k_attn_decode(AttnArgs a) {
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int lane = threadIdx.x & 63;
+  // this workgroup's cache (blockIdx.y) and its slices of q, out and the workspace
+  const AttnCache& cache = a.cache[blockIdx.y];
+  const uint16_t* q = a.q + blockIdx.y * a.qo_stride;
+  float* out = a.out + blockIdx.y * a.qo_stride;
+  float* ws = reinterpret_cast<float*>(a.ws + blockIdx.y * a.ws_stride);
+  uint32_t* tickets = reinterpret_cast<uint32_t*>(a.ws + blockIdx.y * a.ws_stride + a.partial_bytes);
   const int s = blockIdx.x / a.splits;
   const int split = blockIdx.x % a.splits;
   const int j0 = split * a.blocks_per_wg;
@@ -823,14 +829,14 @@ void k_attn_decode(AttnArgs a) {
       // K wave: the scores of every block, handed over through the ring
       // with one workgroup barrier per block
       RecordStream<NCH_K, REC_K> ks;
-      ks.arena = a.k_arena + (uint64_t)s * a.arena_stride;
+      ks.arena = cache.k_arena + (uint64_t)s * a.arena_stride;
       ks.stride = a.arena_stride;
-      ks.offs.load(a.k_off + (int64_t)s * a.off_stride, j0, nj, lane);
+      ks.offs.load(cache.k_off + (int64_t)s * a.off_stride, j0, nj, lane);
       ks.nj = nj;
       ks.lane = lane;
       KB kb;
       kb.init(qs, lane);
-      kb.set_queries(a.q, s, a.G, gq0);
+      kb.set_queries(q, s, a.G, gq0);
       u32x4 pre[NCH_K];
       ks.request(0, pre);
       for (int jj = 0; jj < nj; ++jj) {
@@ -855,9 +861,9 @@ void k_attn_decode(AttnArgs a) {
     for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
       // V wave: running-max softmax over the scores, weighted sum of V
       RecordStream<NCH_V, REC_V> vs;
-      vs.arena = a.v_arena + (uint64_t)s * a.arena_stride;
+      vs.arena = cache.v_arena + (uint64_t)s * a.arena_stride;
       vs.stride = a.arena_stride;
-      vs.offs.load(a.v_off + (int64_t)s * a.off_stride, j0, nj, lane);
+      vs.offs.load(cache.v_off + (int64_t)s * a.off_stride, j0, nj, lane);
       vs.nj = nj;
       vs.lane = lane;
       VB vb;
@@ -910,7 +916,7 @@ void k_attn_decode(AttnArgs a) {
         const float z = wave_sum(pz[g]);
         const float lsum = wave_sum(l[g]);
         if (gq0 + g < a.G) {
-          float* dst = a.ws + (((int64_t)s * a.G + gq0 + g) * a.splits + split) * kAttnPartial;
+          float* dst = ws + (((int64_t)s * a.G + gq0 + g) * a.splits + split) * kAttnPartial;
           store_partial(dst + lane, acc[g][0] + z);
           store_partial(dst + lane + 64, acc[g][1] + z);
           if (lane == 0) {
@@ -922,8 +928,8 @@ void k_attn_decode(AttnArgs a) {
       __syncthreads();                              // the ring is reused
     }
   }
-  if (corrupt && lane == 0) latch(a.status, PACKKV_ECORRUPT);
-  if (wave != 1 || !last_to_arrive(&a.tickets[s], a.splits, lane)) return;
+  if (corrupt && lane == 0) latch(cache.status, PACKKV_ECORRUPT);
+  if (wave != 1 || !last_to_arrive(&tickets[s], a.splits, lane)) return;
   // Merge: the largest split max M first (lanes across splits), then each
   // split's sums scaled by 2^(m_i - M).  A half-wave takes every other split
   // (in split order) and a lane four of the outputs; the loads of four splits
@@ -931,7 +937,7 @@ void k_attn_decode(AttnArgs a) {
   const int half = lane >> 5, d4 = (lane & 31) * 4;
   constexpr uint32_t PB = kAttnPartial * 4;         // bytes per partial
   for (int g = 0; g < a.G; ++g) {
-    const float* src = a.ws + ((int64_t)s * a.G + g) * a.splits * kAttnPartial;
+    const float* src = ws + ((int64_t)s * a.G + g) * a.splits * kAttnPartial;
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(src, (uint32_t)a.splits * PB);
     float M = NEG_INF;
     for (int i = lane; i < a.splits; i += 64) M = fmaxf(M, load_partial(src + (int64_t)i * kAttnPartial + kD));
@@ -960,10 +966,10 @@ void k_attn_decode(AttnArgs a) {
     for (int k = 0; k < 4; ++k) o[k] += __shfl_xor(o[k], 32, kWave);
     if (half == 0) {
       float4 res = {o[0] / L, o[1] / L, o[2] / L, o[3] / L};
-      *reinterpret_cast<float4*>(a.out + ((int64_t)s * a.G + g) * kD + d4) = res;
+      *reinterpret_cast<float4*>(out + ((int64_t)s * a.G + g) * kD + d4) = res;
     }
   }
-  reset_ticket(&a.tickets[s], lane);
+  reset_ticket(&tickets[s], lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1170,8 +1176,8 @@ static void attn_launch(const AttnArgs& a, dim3 grid, hipStream_t st) {
   if (a.G == 1) hipLaunchKernelGGL((k_attn_decode<B, BITS, 1>), grid, dim3(128), 0, st, a);
   else hipLaunchKernelGGL((k_attn_decode<B, BITS, 4>), grid, dim3(128), 0, st, a);
 }
-hipError_t launch_attention(const AttnArgs& a, int B, int n_streams, hipStream_t st) {
-  const dim3 grid(n_streams * a.splits);
+hipError_t launch_attention(const AttnArgs& a, int B, int n_streams, int n_caches, hipStream_t st) {
+  const dim3 grid(n_streams * a.splits, n_caches);
   switch (B * 8 + a.bits) {
     case 64 * 8 + 2: attn_launch<64, 2>(a, grid, st); break;
     case 64 * 8 + 3: attn_launch<64, 3>(a, grid, st); break;

@@ -58,12 +58,19 @@ struct GemvArgs {
 
 
 // Fused decode attention over both packed caches of a cache object.
-struct AttnArgs {
+// Fused attention over up to kAttnMaxCaches caches of one shape (the layers
+// of a model) in one launch: blockIdx.y picks the cache.
+constexpr int kAttnMaxCaches = 32;
+struct AttnCache {
   const uint8_t* k_arena;
   const uint8_t* v_arena;
-  uint64_t arena_stride;
   const uint32_t* k_off;
   const uint32_t* v_off;
+  int32_t* status;
+};
+struct AttnArgs {
+  AttnCache cache[kAttnMaxCaches];
+  uint64_t arena_stride;
   int64_t off_stride;
   int64_t n_tokens;
   int32_t nb;
@@ -72,11 +79,12 @@ struct AttnArgs {
   int32_t splits;
   int32_t G;
   float scale_log2e;     // softmax scale times log2(e)
-  const uint16_t* q;     // [S][G][D] fp16
-  float* ws;             // partials [S][G][splits][kAttnPartial]
-  uint32_t* tickets;     // per-stream arrival counters, zero between calls
-  float* out;            // [S][G][D]
-  int32_t* status;
+  const uint16_t* q;     // [caches][S][G][D] fp16
+  float* out;            // [caches][S][G][D]
+  int64_t qo_stride;     // elements per cache in q and out: S * G * D
+  uint8_t* ws;           // per cache ws_stride bytes: partials [S][G][splits][kAttnPartial],
+  uint64_t ws_stride;    //   then per-stream arrival counters (zero between calls)
+  uint64_t partial_bytes;
 };
 constexpr int kAttnPartial = 132;   // D partial sums, running max, weight sum, 2 pad
 
@@ -88,7 +96,7 @@ hipError_t launch_stage_tail(const uint16_t* k, const uint16_t* v, int64_t src_s
                              int n_streams, hipStream_t st);
 hipError_t launch_qk(const GemvArgs& a, int B, int n_streams, hipStream_t st);
 hipError_t launch_pv(const GemvArgs& a, int B, int n_streams, hipStream_t st);
-hipError_t launch_attention(const AttnArgs& a, int B, int n_streams, hipStream_t st);
+hipError_t launch_attention(const AttnArgs& a, int B, int n_streams, int n_caches, hipStream_t st);
 hipError_t launch_decompress(const GemvArgs& a, int B, bool is_v, int n_streams, const uint8_t* perm,
                              int64_t perm_stride, int mode, void* out, hipStream_t st);
 hipError_t launch_stats(const GemvArgs& a, int B, bool is_v, int n_streams, unsigned long long* out,

@@ -215,6 +215,29 @@ int packkv_attention_decode(const packkv_cache_t* cache, const void* q_f16, int3
 uint64_t packkv_attention_workspace_bytes(const packkv_cache_t* cache, int32_t group);
 
 /*
+ * packkv_attention_decode_multi - packkv_attention_decode for n_caches
+ * caches of one shape (typically the layers of a model at one decode step),
+ * in one kernel launch per 32 caches instead of one per cache.  Same
+ * arithmetic as n_caches separate calls, with the same results bit for bit.
+ *   caches:    host array of n_caches >= 1 caches with equal cfg.bits,
+ *              cfg.block_tokens, n_streams, max_tokens, n_tokens and
+ *              arena_stride (else PACKKV_EINVAL).
+ *   q_f16:     device fp16 [n_caches][S][group][D].
+ *   out:       device fp32 [n_caches][S][group][D].
+ *   workspace: at least packkv_attention_multi_workspace_bytes(caches[0],
+ *              group, n_caches) bytes: one packkv_attention_decode
+ *              workspace per cache, back to back, with the same rules
+ *              (counters zero before first use, left zero, no concurrent
+ *              calls on one workspace).
+ */
+int packkv_attention_decode_multi(const packkv_cache_t* const* caches, int32_t n_caches, const void* q_f16,
+                                  int32_t group, float scale, float* out, void* workspace, uint64_t ws_bytes,
+                                  void* stream);
+
+/* Bytes of workspace packkv_attention_decode_multi needs (0 if n_caches < 1). */
+uint64_t packkv_attention_multi_workspace_bytes(const packkv_cache_t* cache, int32_t group, int32_t n_caches);
+
+/*
  * packkv_decompress - decode the cache (test and debug path).
  *   which: 0 = K, 1 = V.
  *   mode 0: out is uint8 [S][n_tokens][D], the quantised ints q in SLOT order.

@@ -92,6 +92,31 @@ def test_invalid_arguments_fail_before_any_launch(lib):
     assert lib.packkv_attention_decode(ctypes.byref(c3), fake, 1, 0.1, fake, fake, need, None) == _lib.ESTATE
 
 
+def test_multi_cache_attention_checks_before_any_launch(lib):
+    fake = 4096
+    s = _lib.Sizes()
+    lib.packkv_cache_sizes(ctypes.byref(cfg()), 2, 100, ctypes.byref(s))
+    mk = lambda n_tokens=50, S=2, max_tokens=100: _lib.CacheT(cfg(), S, max_tokens, n_tokens, s.arena_stride,
+                                                               fake, fake, fake, fake, fake, fake, fake, fake)
+    a, b = mk(), mk()
+    one = lib.packkv_attention_workspace_bytes(ctypes.byref(a), 1)
+    assert lib.packkv_attention_multi_workspace_bytes(ctypes.byref(a), 1, 3) == 3 * one
+    assert lib.packkv_attention_multi_workspace_bytes(ctypes.byref(a), 1, 0) == 0
+    P = ctypes.POINTER(_lib.CacheT)
+    arr = lambda *cs: (P * len(cs))(*[ctypes.pointer(c) for c in cs])
+    ok2 = arr(a, b)
+    assert lib.packkv_attention_decode_multi(None, 2, fake, 1, 0.1, fake, fake, 2 * one, None) == _lib.EINVAL
+    assert lib.packkv_attention_decode_multi(ok2, 0, fake, 1, 0.1, fake, fake, 2 * one, None) == _lib.EINVAL
+    assert lib.packkv_attention_decode_multi(ok2, 2, fake, 1, 0.1, fake, fake, 2 * one - 1, None) == _lib.EINVAL
+    assert lib.packkv_attention_decode_multi(ok2, 2, None, 1, 0.1, fake, fake, 2 * one, None) == _lib.EINVAL
+    # caches that differ in length, stream count or capacity
+    for other in (mk(n_tokens=49), mk(S=3), mk(max_tokens=99)):
+        assert lib.packkv_attention_decode_multi(arr(a, other), 2, fake, 1, 0.1, fake, fake, 4 * one,
+                                                 None) == _lib.EINVAL
+    empty = arr(mk(n_tokens=0), mk(n_tokens=0))
+    assert lib.packkv_attention_decode_multi(empty, 2, fake, 1, 0.1, fake, fake, 2 * one, None) == _lib.ESTATE
+
+
 def test_status_strings(lib):
     for code in range(7):
         assert lib.packkv_status_str(code)

@@ -271,3 +271,34 @@ def test_fused_attention_is_bitwise_reproducible_and_reuses_its_workspace(torch_
     ws = c.attention_workspace(4)
     tail = ws[-256:].view(torch.int32)[:2].cpu().numpy()
     assert np.all(tail == 0)
+
+
+@pytest.mark.parametrize("bits,block,G,L", [(4, 64, 1, 3), (3, 128, 4, 2), (2, 64, 3, 35)])
+def test_multi_cache_attention_matches_single_calls(torch_dev, bits, block, G, L):
+    """One launch over L caches (35 takes two launches of at most 32) gives
+    each cache's single-call result bit for bit, twice on one workspace; the
+    first cache is also checked against the oracle."""
+    torch, dev = torch_dev
+    from decode_gemv_amd import attention_multi, attention_multi_workspace
+    S, T = 2, 150
+    caches, kvs = [], []
+    for layer in range(L):
+        K, V = make_kv("gauss", S, T, block, seed=100 + layer)
+        kvs.append((K, V))
+        caches.append(gpu_cache(torch, dev, K, V, bits, block, 1))
+    rng = np.random.default_rng(L)
+    q = rng.standard_normal((L, S, G, 128)).astype(np.float16)
+    qd = torch.from_numpy(q).to(dev)
+    say("attention multi", bits, block, G, L)
+    ws = attention_multi_workspace(caches, G)
+    single = torch.stack([c.attention(qd[i].contiguous()) for i, c in enumerate(caches)])
+    for rep in range(2):
+        out = attention_multi(caches, qd, workspace=ws)
+        for c in caches:
+            assert c.check() == 0
+        assert torch.equal(out, single), f"repeat {rep}"
+    refs = oracle_streams(*kvs[0], bits, block, 1)
+    for s in range(S):
+        kh, vh, _, _ = ostream.decode_stream(refs[s])
+        ref = attention.pv(attention.softmax(attention.qk(q[0, s], kh), 128), vh)
+        assert rel_l2(out[0, s].cpu().numpy(), ref) <= TOL
