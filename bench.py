@@ -229,6 +229,9 @@ def main():
     ap.add_argument("--cpu-streams", type=int, default=4, help="streams in the oracle's timed sample")
     ap.add_argument("--cpu-steps", type=int, default=30, help="decode steps per sampled stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="also time decode attention over this many caches of the workload's shape "
+                         "(a model's layers): one multi-cache launch against one launch per cache")
     ap.add_argument("--permute", type=int, default=1, choices=(0, 1, 2),
                     help="token order inside blocks: 0 identity, 1 greedy grouping, 2 sort key")
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
@@ -245,7 +248,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from decode_gemv_amd import PackedKVCache, softmax_rows
+    from decode_gemv_amd import PackedKVCache, attention_multi, attention_multi_workspace, softmax_rows
 
     w = kvsynth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -264,6 +267,11 @@ def main():
     torch.cuda.synchronize()
     prefill_s = time.perf_counter() - t
     assert cache.check() == 0
+    layer_caches = [cache]
+    for _ in range(args.layers - 1):            # the other layers hold the same tokens
+        c2 = PackedKVCache(S, T_max, bits=w.bits, block=w.block, permute=args.permute, device="cuda:0")
+        c2.compress(K, V)
+        layer_caches.append(c2)
     del K, V
     torch.cuda.empty_cache()
 
@@ -331,6 +339,48 @@ def main():
         for _ in range(20):
             cache.attention(qn[0], scale, out=fout, workspace=aws)
         torch.cuda.synchronize()
+
+    multi = None
+    if args.layers > 1:
+        # decode attention over every layer at one step: one launch per
+        # layer, then the multi-cache launch (up to 32 caches per launch)
+        L = args.layers
+        qm = qn[0].unsqueeze(0).expand(L, S, G, D).contiguous()
+        outm = torch.empty((L, S, G, D), dtype=torch.float32, device=dev)
+        wsm = attention_multi_workspace(layer_caches, G)
+        ws1 = [c.attention_workspace(G) for c in layer_caches]
+        reps = 20
+
+        def per_layer():
+            for i, c in enumerate(layer_caches):
+                c.attention(qm[i], scale, out=outm[i], workspace=ws1[i])
+
+        def one_launch():
+            attention_multi(layer_caches, qm, scale, out=outm, workspace=wsm)
+
+        res_ms = {}
+        for name, fn in (("per_layer", per_layer), ("multi", one_launch)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            res_ms[name] = e0.elapsed_time(e1) / reps
+        for c in layer_caches:
+            assert c.check() == 0
+        kbl, vbl, nbl = used_bytes()
+        layer_bytes = kbl + vbl + 2 * 4 * S * (nbl + 1)
+        multi = {"layers": L, "per_layer_launches_ms": round(res_ms["per_layer"], 4),
+                 "multi_launch_ms": round(res_ms["multi"], 4),
+                 "multi_GBps": round(L * layer_bytes / (res_ms["multi"] * 1e-3) / 1e9, 1),
+                 "note": "decode attention over L caches of this shape at the prefill length"}
+        log(f"{L} layers: {res_ms['per_layer']:.3f} ms as {L} launches, {res_ms['multi']:.3f} ms as one")
+        del layer_caches[1:], wsm, ws1, outm, qm
+        torch.cuda.empty_cache()
 
     ms_step, fev = timed_loop(fused_step, 3)
     kb1, vb1, nb1 = used_bytes()
@@ -413,6 +463,7 @@ def main():
         "prefill_ms": round(prefill_s * 1e3, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "multi_layer": multi,
         "alg_bytes_per_launch": {"attn": int(attn_alg), "qk": int(qk_alg), "pv": int(pv_alg)},
         "kernel_source": kernel_source_hash(),
     }
