@@ -39,7 +39,7 @@ METRIC = "fused decompress-GEMV effective GB/s & % of HBM peak; K/V compression 
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "decode_gemv_amd", "csrc", f)
-                  for f in ("gemv.hip", "common.hpp", "kernels.hpp")]
+                  for f in ("gemv.hip", "common.hpp", "kernels.hpp", "api.hip")]   # kernels and their launch shapes
 
 
 def log(*a):
