@@ -302,6 +302,11 @@ def main():
     ws = cache.workspace(G)
     scale = 1.0 / float(np.sqrt(D))
 
+    def status_ok(where):
+        code = cache.check()
+        if code:
+            raise RuntimeError(f"cache status {code} after {where}")
+
     def timed_loop(launch, n_ev):
         """W untimed + K timed steps; returns (ms per step, per-step HIP events)."""
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(n_steps)]
@@ -314,7 +319,7 @@ def main():
             launch(i, ev[i])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        assert cache.check() == 0
+        status_ok(launch.__name__)
         return wall / args.steps * 1e3, ev[args.warmup:]
 
     def avg_ms(evs, a, b):
@@ -339,6 +344,7 @@ def main():
         for _ in range(20):
             cache.attention(qn[0], scale, out=fout, workspace=aws)
         torch.cuda.synchronize()
+    status_ok("the clock warm-up")
 
     multi = None
     if args.layers > 1:
