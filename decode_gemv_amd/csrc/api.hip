@@ -305,6 +305,13 @@ static int attention_decode(const packkv_cache_t* const* cs, int32_t n, const vo
   a.bits = c->cfg.bits;
   a.blocks_per_wg = g.blocks_per_wg;
   a.splits = g.splits;
+  {
+    static const int env_splits = env_int("PACKKV_ATTN_SPLITS");
+    if (env_splits > 0) {
+      const int lo = (a.nb + 63) / 64, hi = (a.nb + 3) / 4;
+      a.splits = env_splits < lo ? lo : (env_splits > hi ? hi : env_splits);
+    }
+  }
   a.G = group;
   a.scale_log2e = scale * 1.4426950408889634f;
   a.qo_stride = (int64_t)c->n_streams * group * kD;

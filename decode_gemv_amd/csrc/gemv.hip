@@ -818,8 +818,9 @@ void k_attn_decode(AttnArgs a) {
   uint32_t* tickets = reinterpret_cast<uint32_t*>(a.ws + blockIdx.y * a.ws_stride + a.partial_bytes);
   const int s = blockIdx.x / a.splits;
   const int split = blockIdx.x % a.splits;
-  const int j0 = split * a.blocks_per_wg;
-  const int nj = max(0, min(a.nb, j0 + a.blocks_per_wg) - j0);
+  // the splits divide the blocks evenly: floor or ceil of nb / splits each
+  const int j0 = (int)((int64_t)split * a.nb / a.splits);
+  const int nj = (int)((int64_t)(split + 1) * a.nb / a.splits) - j0;
   bool corrupt = false;
   const float NEG_INF = -__builtin_huge_valf();
 
