@@ -37,6 +37,19 @@ class Sizes(ctypes.Structure):
                 ("perm_bytes", c_uint64), ("tail_bytes", c_uint64), ("max_blocks", c_int64)]
 
 
+class PagedT(ctypes.Structure):
+    _fields_ = [("cfg", Config), ("n_streams", c_int32), ("n_pages", c_int32), ("max_tokens", c_int64),
+                ("page_bytes", c_uint64), ("pool", c_void_p), ("k_table", c_void_p), ("v_table", c_void_p),
+                ("lengths", c_void_p), ("alloc", c_void_p), ("perm", c_void_p), ("tail_k", c_void_p),
+                ("tail_v", c_void_p), ("status", c_void_p), ("host_lengths", c_void_p)]
+
+
+class PagedSizes(ctypes.Structure):
+    _fields_ = [("pool_bytes", c_uint64), ("table_bytes", c_uint64), ("alloc_bytes", c_uint64),
+                ("lengths_bytes", c_uint64), ("perm_bytes", c_uint64), ("tail_bytes", c_uint64),
+                ("slot_bytes", c_uint64), ("min_page_bytes", c_uint64), ("max_blocks", c_int64)]
+
+
 class PackKVError(RuntimeError):
     def __init__(self, code: int, what: str = ""):
         self.code = code
@@ -65,6 +78,17 @@ _SIGS = {
     "packkv_check": (c_int32, [ctypes.POINTER(CacheT), c_void_p]),
     "packkv_stats": (c_int32, [ctypes.POINTER(CacheT), c_void_p, c_void_p]),
     "packkv_status_str": (ctypes.c_char_p, [c_int32]),
+    "packkv_paged_sizes": (c_int32, [ctypes.POINTER(Config), c_int32, c_int64, c_int32, c_uint64,
+                                     ctypes.POINTER(PagedSizes)]),
+    "packkv_paged_init": (c_int32, [ctypes.POINTER(PagedT), c_void_p]),
+    "packkv_paged_prefill": (c_int32, [ctypes.POINTER(PagedT), c_int32, c_int32, c_void_p, c_void_p, c_int64,
+                                       c_void_p]),
+    "packkv_paged_append": (c_int32, [ctypes.POINTER(PagedT), c_void_p, c_void_p, c_void_p]),
+    "packkv_paged_release": (c_int32, [ctypes.POINTER(PagedT), c_int32, c_void_p]),
+    "packkv_paged_attention_workspace_bytes": (c_uint64, [ctypes.POINTER(PagedT), c_int32]),
+    "packkv_paged_attention": (c_int32, [ctypes.POINTER(PagedT), c_void_p, c_int32, ctypes.c_float, c_void_p,
+                                         c_void_p, c_uint64, c_void_p]),
+    "packkv_paged_check": (c_int32, [ctypes.POINTER(PagedT), c_void_p]),
 }
 
 _lib = None

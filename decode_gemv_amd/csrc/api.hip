@@ -405,4 +405,230 @@ const char* packkv_status_str(int s) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Paged cache.
+
+namespace {
+
+uint64_t paged_slot_bytes(const packkv_config_t* c) {
+  const int B = c->block_tokens;
+  const uint64_t rk = (uint64_t)max_record_bytes(false, B, c->bits);
+  const uint64_t rv = (uint64_t)max_record_bytes(true, B, c->bits);
+  return ((rk > rv ? rk : rv) + 15) & ~(uint64_t)15;
+}
+uint64_t paged_min_page(const packkv_config_t* c) { return (paged_slot_bytes(c) + 255) & ~(uint64_t)255; }
+uint64_t paged_pool_bytes(const packkv_config_t* c, int32_t n_streams, int32_t n_pages, uint64_t page_bytes) {
+  return (uint64_t)n_pages * page_bytes + (uint64_t)n_streams * 2u * paged_slot_bytes(c) + 256u;
+}
+
+int check_paged(const packkv_paged_t* c) {
+  if (!c) return PACKKV_EINVAL;
+  int e = check_cfg(&c->cfg);
+  if (e) return e;
+  if (c->n_streams < 1 || c->n_pages < 1 || c->max_tokens < 1) return PACKKV_EINVAL;
+  if (c->page_bytes % 256 || c->page_bytes < paged_min_page(&c->cfg)) return PACKKV_EINVAL;
+  if (paged_pool_bytes(&c->cfg, c->n_streams, c->n_pages, c->page_bytes) >= (1ull << 36)) return PACKKV_EINVAL;
+  if (max_blocks_of(&c->cfg, c->max_tokens) >= (1ll << 31)) return PACKKV_EINVAL;
+  if (!c->pool || !c->k_table || !c->v_table || !c->lengths || !c->alloc || !c->perm || !c->tail_k ||
+      !c->tail_v || !c->status || !c->host_lengths)
+    return PACKKV_EINVAL;
+  return PACKKV_OK;
+}
+
+PageAlloc page_alloc_of(const packkv_paged_t* c) {
+  PageAlloc p;
+  p.state = c->alloc;
+  p.n_streams = c->n_streams;
+  p.n_pages = (uint32_t)c->n_pages;
+  p.page16 = (uint32_t)(c->page_bytes / 16);
+  p.tail16 = (uint32_t)((uint64_t)c->n_pages * c->page_bytes / 16);
+  p.slot16 = (uint32_t)(paged_slot_bytes(&c->cfg) / 16);
+  return p;
+}
+
+EncArgs paged_enc_args(const packkv_paged_t* c) {
+  EncArgs a;
+  memset(&a, 0, sizeof(a));
+  const int64_t mb = max_blocks_of(&c->cfg, c->max_tokens);
+  a.bits = c->cfg.bits;
+  a.B = c->cfg.block_tokens;
+  a.permute = c->cfg.permute;
+  a.k_arena = c->pool;
+  a.v_arena = c->pool;
+  a.arena_limit = paged_pool_bytes(&c->cfg, c->n_streams, c->n_pages, c->page_bytes);
+  a.off_stride = mb;
+  a.perm = c->perm;
+  a.perm_stride = mb * c->cfg.block_tokens;
+  a.status = c->status;
+  a.paged = 1;
+  a.k_tab = reinterpret_cast<uint2*>(c->k_table);
+  a.v_tab = reinterpret_cast<uint2*>(c->v_table);
+  a.lengths = c->lengths;
+  a.pages = page_alloc_of(c);
+  return a;
+}
+
+uint64_t paged_partial_bytes(const packkv_paged_t* c, int32_t group) {
+  const int64_t mb = max_blocks_of(&c->cfg, c->max_tokens);
+  const int64_t splits = (mb + 3) / 4;     // blocks per workgroup is at least 4
+  return (uint64_t)c->n_streams * (uint64_t)group * (uint64_t)splits * kAttnPartial * sizeof(float);
+}
+
+}  // namespace
+
+int packkv_paged_sizes(const packkv_config_t* cfg, int32_t n_streams, int64_t max_tokens, int32_t n_pages,
+                       uint64_t page_bytes, packkv_paged_sizes_t* out) {
+  int e = check_cfg(cfg);
+  if (e) return e;
+  if (!out || n_streams < 1 || max_tokens < 1 || n_pages < 1) return PACKKV_EINVAL;
+  const int64_t mb = max_blocks_of(cfg, max_tokens);
+  out->max_blocks = mb;
+  out->slot_bytes = paged_slot_bytes(cfg);
+  out->min_page_bytes = paged_min_page(cfg);
+  if (page_bytes % 256 || page_bytes < out->min_page_bytes) return PACKKV_EINVAL;
+  out->pool_bytes = paged_pool_bytes(cfg, n_streams, n_pages, page_bytes);
+  if (out->pool_bytes >= (1ull << 36) || mb >= (1ll << 31)) return PACKKV_EINVAL;   // 32-bit 16-byte units
+  out->table_bytes = (uint64_t)n_streams * (uint64_t)mb * 8;
+  out->alloc_bytes = (2u + 2u * (uint64_t)n_streams + (uint64_t)n_pages) * 4;
+  out->lengths_bytes = (uint64_t)n_streams * 4;
+  out->perm_bytes = (uint64_t)n_streams * (uint64_t)mb * (uint64_t)cfg->block_tokens;
+  out->tail_bytes = (uint64_t)n_streams * (uint64_t)cfg->block_tokens * kD * 2;
+  return PACKKV_OK;
+}
+
+int packkv_paged_init(packkv_paged_t* c, void* stream) {
+  int e = check_paged(c);
+  if (e) return e;
+  if ((e = hip_status(launch_paged_init(page_alloc_of(c), c->lengths, c->status, (hipStream_t)stream)))) return e;
+  memset(c->host_lengths, 0, sizeof(int32_t) * (size_t)c->n_streams);
+  return PACKKV_OK;
+}
+
+int packkv_paged_prefill(packkv_paged_t* c, int32_t stream0, int32_t n, const void* k_f16, const void* v_f16,
+                         int64_t n_tokens, void* stream) {
+  int e = check_paged(c);
+  if (e) return e;
+  if (!k_f16 || !v_f16 || n < 1 || stream0 < 0 || (int64_t)stream0 + n > c->n_streams || n_tokens < 1)
+    return PACKKV_EINVAL;
+  if (((uintptr_t)k_f16 | (uintptr_t)v_f16) & 15u) return PACKKV_EINVAL;   // read with 16-byte loads
+  if (n_tokens > c->max_tokens) return PACKKV_ECAPACITY;
+  for (int32_t s = stream0; s < stream0 + n; ++s)
+    if (c->host_lengths[s] != 0) return PACKKV_ESTATE;
+  hipStream_t st = (hipStream_t)stream;
+  const int B = c->cfg.block_tokens;
+  const int nb = (int)((n_tokens + B - 1) / B);
+  EncArgs a = paged_enc_args(c);
+  a.stream0 = stream0;
+  a.k = (const uint16_t*)k_f16;
+  a.v = (const uint16_t*)v_f16;
+  a.src_stream = n_tokens * kD;
+  a.src_block = (int64_t)B * kD;
+  a.n_tokens = n_tokens;
+  a.mode = kPass1;
+  if ((e = hip_status(launch_encode(a, n, nb, st)))) return e;
+  if ((e = hip_status(launch_paged_alloc(a, n, n_tokens, st)))) return e;
+  a.mode = kPass2;
+  if ((e = hip_status(launch_encode(a, n, nb, st)))) return e;
+  const int64_t nfull = n_tokens / B;
+  const int rem = (int)(n_tokens - nfull * B);
+  if (rem) {
+    const int64_t t0 = (int64_t)stream0 * B * kD;
+    e = hip_status(launch_stage_tail((const uint16_t*)k_f16 + nfull * B * kD,
+                                     (const uint16_t*)v_f16 + nfull * B * kD, n_tokens * kD, c->tail_k + t0,
+                                     c->tail_v + t0, B, 0, rem, n, st));
+    if (e) return e;
+  }
+  for (int32_t s = stream0; s < stream0 + n; ++s) c->host_lengths[s] = (int32_t)n_tokens;
+  return PACKKV_OK;
+}
+
+int packkv_paged_append(packkv_paged_t* c, const void* k_f16, const void* v_f16, void* stream) {
+  int e = check_paged(c);
+  if (e) return e;
+  if (!k_f16 || !v_f16) return PACKKV_EINVAL;
+  if (((uintptr_t)k_f16 | (uintptr_t)v_f16) & 15u) return PACKKV_EINVAL;
+  for (int32_t s = 0; s < c->n_streams; ++s)
+    if ((int64_t)c->host_lengths[s] + 1 > c->max_tokens) return PACKKV_ECAPACITY;
+  const int B = c->cfg.block_tokens;
+  EncArgs a = paged_enc_args(c);
+  a.k = c->tail_k;                // the raw staging of each open block
+  a.v = c->tail_v;
+  a.src_stream = (int64_t)B * kD;
+  a.mode = kTail;
+  a.new_k = (const uint16_t*)k_f16;
+  a.new_v = (const uint16_t*)v_f16;
+  a.new_stream = kD;              // one token per stream
+  if ((e = hip_status(launch_encode(a, c->n_streams, 1, (hipStream_t)stream)))) return e;
+  for (int32_t s = 0; s < c->n_streams; ++s) c->host_lengths[s] += 1;
+  return PACKKV_OK;
+}
+
+int packkv_paged_release(packkv_paged_t* c, int32_t s, void* stream) {
+  int e = check_paged(c);
+  if (e) return e;
+  if (s < 0 || s >= c->n_streams) return PACKKV_EINVAL;
+  e = hip_status(launch_paged_release(page_alloc_of(c), reinterpret_cast<const uint2*>(c->k_table),
+                                      reinterpret_cast<const uint2*>(c->v_table),
+                                      max_blocks_of(&c->cfg, c->max_tokens), c->lengths, c->cfg.block_tokens, s,
+                                      (hipStream_t)stream));
+  if (e) return e;
+  c->host_lengths[s] = 0;
+  return PACKKV_OK;
+}
+
+uint64_t packkv_paged_attention_workspace_bytes(const packkv_paged_t* c, int32_t group) {
+  if (check_paged(c) || group < 1) return 0;
+  return paged_partial_bytes(c, group) + (((uint64_t)c->n_streams * 4u + 255u) & ~(uint64_t)255u);
+}
+
+int packkv_paged_attention(const packkv_paged_t* c, const void* q_f16, int32_t group, float scale, float* out,
+                           void* workspace, uint64_t ws_bytes, void* stream) {
+  int e = check_paged(c);
+  if (e) return e;
+  if (!q_f16 || !out || !workspace || group < 1 || !(scale > 0.f) || !std::isfinite(scale))
+    return PACKKV_EINVAL;
+  const uint64_t need = packkv_paged_attention_workspace_bytes(c, group);
+  if (ws_bytes < need) return PACKKV_EINVAL;
+  int64_t longest = 0;
+  for (int32_t s = 0; s < c->n_streams; ++s) longest = c->host_lengths[s] > longest ? c->host_lengths[s] : longest;
+  if (longest < 1) return PACKKV_ESTATE;
+  const int B = c->cfg.block_tokens;
+  // the launch is divided for the longest stream; every stream spreads its
+  // own blocks evenly over the same splits
+  const int nb = (int)((longest + B - 1) / B);
+  const int J = gemv_blocks_per_wg(c->n_streams, nb, true, group);
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.cache[0] = AttnCache{c->pool, c->pool, nullptr, nullptr, c->status,
+                         reinterpret_cast<const uint2*>(c->k_table), reinterpret_cast<const uint2*>(c->v_table),
+                         c->lengths};
+  a.arena_stride = paged_pool_bytes(&c->cfg, c->n_streams, c->n_pages, c->page_bytes);
+  a.off_stride = max_blocks_of(&c->cfg, c->max_tokens);
+  a.bits = c->cfg.bits;
+  a.blocks_per_wg = J;
+  a.splits = (nb + J - 1) / J;
+  a.G = group;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  a.q = (const uint16_t*)q_f16;
+  a.out = out;
+  a.qo_stride = (int64_t)c->n_streams * group * kD;
+  a.ws = (uint8_t*)workspace;
+  a.ws_stride = need;
+  a.partial_bytes = paged_partial_bytes(c, group);
+  return hip_status(launch_attention(a, B, c->n_streams, 1, (hipStream_t)stream, true));
+}
+
+int packkv_paged_check(const packkv_paged_t* c, void* stream) {
+  if (!c || !c->status) return PACKKV_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipStreamSynchronize(st) != hipSuccess) return PACKKV_EHIP;
+  int32_t v = 0;
+  if (hipMemcpy(&v, c->status, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return PACKKV_EHIP;
+  if (v) {
+    const int32_t zero = 0;
+    if (hipMemcpy(c->status, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return PACKKV_EHIP;
+  }
+  return v;
+}
+
 }  // extern "C"

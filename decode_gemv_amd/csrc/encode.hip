@@ -17,6 +17,8 @@
 
 namespace packkv {
 
+__device__ bool page_take(const PageAlloc& p, int s, uint32_t need16, uint32_t& start16);
+
 // Smallest positive fp16 pattern h with value(h) * L >= d, for d > 0.
 __device__ uint32_t min_f16_step(double d, int L) {
   double y = d / (double)L;
@@ -152,14 +154,29 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
 
   const int tid = threadIdx.x;
   const int L = (1 << a.bits) - 1;
-  const int s = blockIdx.y;
-  const int j = a.mode == kTail ? a.block0 : blockIdx.x;
+  const int s = a.stream0 + (int)blockIdx.y;
+  int j = a.mode == kTail ? a.block0 : (int)blockIdx.x;
+  int64_t n_tok = a.n_tokens;
+  int new_at = a.new_at;
+  int32_t len0 = 0;
+  if (a.paged) {
+    len0 = a.lengths[s];
+    if (a.mode == kTail) {
+      // one token per stream, at the stream's own position
+      j = len0 / B;
+      new_at = len0 % B;
+      n_tok = (int64_t)len0 + 1;
+    } else if (a.mode == kPass2 && len0 != a.n_tokens) {
+      return;                                        // its pages were not allocated
+    }
+  }
   const int64_t t0 = (int64_t)j * B;
-  if (t0 >= a.n_tokens) return;
-  const int n = (int)imin64(B, a.n_tokens - t0);
+  if (t0 >= n_tok) return;
+  const int n = (int)imin64(B, n_tok - t0);
   const int nr = (n + kR - 1) / kR;
-  const uint16_t* ks = a.k + s * a.src_stream + (a.mode == kTail ? 0 : j * a.src_block);
-  const uint16_t* vs = a.v + s * a.src_stream + (a.mode == kTail ? 0 : j * a.src_block);
+  // the source holds the launch's streams only
+  const uint16_t* ks = a.k + (s - a.stream0) * a.src_stream + (a.mode == kTail ? 0 : j * a.src_block);
+  const uint16_t* vs = a.v + (s - a.stream0) * a.src_stream + (a.mode == kTail ? 0 : j * a.src_block);
 
   // (1) quantise.  K per channel over the block's tokens: the block's raw K
   // is staged through LDS with 16-byte loads by every thread (one memory
@@ -170,9 +187,9 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
     uint4* dst = reinterpret_cast<uint4*>(rawk);
     for (int i = tid; i < n * (kD / 8); i += NT) {
       const int t = i / (kD / 8);
-      if (fresh && t >= a.new_at) {
+      if (fresh && t >= new_at) {
         // an appended token: read it from the caller and keep it in the staging
-        const uint4 u = reinterpret_cast<const uint4*>(a.new_k + s * a.new_stream + (int64_t)(t - a.new_at) * kD)[i % (kD / 8)];
+        const uint4 u = reinterpret_cast<const uint4*>(a.new_k + s * a.new_stream + (int64_t)(t - new_at) * kD)[i % (kD / 8)];
         const_cast<uint4*>(src)[i] = u;
         dst[i] = u;
       } else {
@@ -201,11 +218,11 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
     const int CPT = kD / TPT;                        // 32 or 64 channels per thread
     const int t = tid / TPT, part = tid % TPT;
     const bool on = t < n;
-    const bool appended = fresh && on && t >= a.new_at;
+    const bool appended = fresh && on && t >= new_at;
     uint32_t w[32];                                  // up to 64 fp16, two per word
     uint4* stage = reinterpret_cast<uint4*>(const_cast<uint16_t*>(vs) + (int64_t)(on ? t : 0) * kD + part * CPT);
     const uint4* src = appended
-        ? reinterpret_cast<const uint4*>(a.new_v + s * a.new_stream + (int64_t)(t - a.new_at) * kD + part * CPT)
+        ? reinterpret_cast<const uint4*>(a.new_v + s * a.new_stream + (int64_t)(t - new_at) * kD + part * CPT)
         : stage;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -405,36 +422,76 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
   const uint32_t v_size = v_pay + (uint32_t)pad16(4 * (int)totv);
   uint32_t* koff = a.k_off + s * a.off_stride;
   uint32_t* voff = a.v_off + s * a.off_stride;
+  uint2* ktab = a.k_tab + s * a.off_stride;
+  uint2* vtab = a.v_tab + s * a.off_stride;
 
   if (a.mode == kPass1) {
     if (tid < B) perm_g[tid] = tid < n ? order[tid] : (uint8_t)0xFF;
     if (tid == 0) {
-      koff[j + 1] = k_size;       // sizes; a later scan turns them into offsets
-      voff[j + 1] = v_size;
+      if (a.paged) {
+        ktab[j].y = k_size;       // sizes; the allocator then places the records
+        vtab[j].y = v_size;
+      } else {
+        koff[j + 1] = k_size;     // sizes; a later scan turns them into offsets
+        voff[j + 1] = v_size;
+      }
     }
     return;
   }
 
   // (4) write the records.
-  uint32_t kbase, vbase;
-  if (a.mode == kTail) {
-    if (j == 0) {
-      kbase = 0u;
-      vbase = 0u;
+  uint64_t kbase, vbase;
+  uint8_t* krec;
+  uint8_t* vrec;
+  if (a.paged) {
+    __shared__ uint32_t base_sh[2];
+    if (a.mode == kTail) {
+      // a block that this token fills moves to the stream's pages; an open
+      // one stays in the stream's tail slots
+      if (tid == 0) {
+        uint32_t k16 = a.pages.tail16 + 2u * (uint32_t)s * a.pages.slot16, v16 = k16 + a.pages.slot16;
+        if (n == B && !(page_take(a.pages, s, k_size >> 4, k16) && page_take(a.pages, s, v_size >> 4, v16)))
+          k16 = kNoPage;
+        base_sh[0] = k16;
+        base_sh[1] = v16;
+      }
+      __syncthreads();
+      if (base_sh[0] == kNoPage) {
+        if (tid == 0) latch(a.status, PACKKV_ECAPACITY);
+        return;
+      }
+      kbase = (uint64_t)base_sh[0] << 4;
+      vbase = (uint64_t)base_sh[1] << 4;
+    } else {
+      kbase = (uint64_t)ktab[j].x << 4;
+      vbase = (uint64_t)vtab[j].x << 4;
+    }
+    if (kbase + k_size > a.arena_limit || vbase + v_size > a.arena_limit) {
+      if (tid == 0) latch(a.status, PACKKV_ECORRUPT);
+      return;
+    }
+    krec = a.k_arena + kbase;
+    vrec = a.v_arena + vbase;
+  } else {
+    if (a.mode == kTail) {
+      if (j == 0) {
+        kbase = 0u;
+        vbase = 0u;
+      } else {
+        kbase = koff[j];
+        vbase = voff[j];
+      }
     } else {
       kbase = koff[j];
       vbase = voff[j];
     }
-  } else {
-    kbase = koff[j];
-    vbase = voff[j];
+    if (kbase + k_size > a.arena_limit || vbase + v_size > a.arena_limit) {
+      if (tid == 0) latch(a.status, PACKKV_ECAPACITY);
+      return;
+    }
+    krec = a.k_arena + s * a.arena_stride + kbase;
+    vrec = a.v_arena + s * a.arena_stride + vbase;
   }
-  if ((uint64_t)kbase + k_size > a.arena_limit || (uint64_t)vbase + v_size > a.arena_limit) {
-    if (tid == 0) latch(a.status, PACKKV_ECAPACITY);
-    return;
-  }
-  uint8_t* krec = a.k_arena + s * a.arena_stride + kbase;
-  uint8_t* vrec = a.v_arena + s * a.arena_stride + vbase;
 
   // params
   if (tid < kD) {
@@ -489,14 +546,112 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
   if (a.mode == kTail) {
     if (tid < B) perm_g[tid] = tid < n ? order[tid] : (uint8_t)0xFF;
     if (tid == 0) {
-      if (j == 0) {
-        koff[0] = 0u;
-        voff[0] = 0u;
+      if (a.paged) {
+        ktab[j] = make_uint2((uint32_t)(kbase >> 4), k_size);
+        vtab[j] = make_uint2((uint32_t)(vbase >> 4), v_size);
+        a.lengths[s] = len0 + 1;
+      } else {
+        if (j == 0) {
+          koff[0] = 0u;
+          voff[0] = 0u;
+        }
+        koff[j + 1] = (uint32_t)kbase + k_size;
+        voff[j + 1] = (uint32_t)vbase + v_size;
       }
-      koff[j + 1] = kbase + k_size;
-      voff[j + 1] = vbase + v_size;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Paged cache: page allocation, set-up and release.
+
+// Place a record of need16 16-byte units in stream s's current page, or at
+// the start of a page taken from the free stack; false if none is left.
+// Called by one thread per stream at a time.
+__device__ bool page_take(const PageAlloc& p, int s, uint32_t need16, uint32_t& start16) {
+  uint32_t* st = p.state + 2 + 2 * s;
+  uint32_t page = st[0], fill = st[1];
+  if (page == kNoPage || fill + need16 > p.page16) {
+    const int old = atomicSub(reinterpret_cast<int*>(p.state), 1);
+    if (old <= 0) {
+      atomicAdd(reinterpret_cast<int*>(p.state), 1);
+      return false;
+    }
+    page = p.state[2 + 2 * p.n_streams + old - 1];
+    fill = 0;
+  }
+  start16 = page * p.page16 + fill;
+  st[0] = page;
+  st[1] = fill + need16;
+  return true;
+}
+
+// Prefill of n_streams streams from stream0 on, after pass 1 wrote the
+// sizes: one thread per stream places the closed blocks' records (K then V,
+// block order), points the open block at the tail slots and sets the length.
+__global__ __launch_bounds__(64) void k_paged_alloc(EncArgs a, int n_streams, int64_t n_tokens) {
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  if (i >= n_streams) return;
+  const int s = a.stream0 + i;
+  const int nfull = (int)(n_tokens / a.B), nb = (int)((n_tokens + a.B - 1) / a.B);
+  uint2* kt = a.k_tab + s * a.off_stride;
+  uint2* vt = a.v_tab + s * a.off_stride;
+  for (int j = 0; j < nfull; ++j) {
+    uint32_t k16, v16;
+    if (!page_take(a.pages, s, kt[j].y >> 4, k16) || !page_take(a.pages, s, vt[j].y >> 4, v16)) {
+      latch(a.status, PACKKV_ECAPACITY);
+      return;                                        // length stays 0: pass 2 writes nothing
+    }
+    kt[j].x = k16;
+    vt[j].x = v16;
+  }
+  if (nb > nfull) {
+    kt[nfull].x = a.pages.tail16 + 2u * (uint32_t)s * a.pages.slot16;
+    vt[nfull].x = kt[nfull].x + a.pages.slot16;
+  }
+  a.lengths[s] = (int32_t)n_tokens;
+}
+
+// Every page free, every stream empty, the status clear.
+__global__ __launch_bounds__(256) void k_paged_init(PageAlloc p, int32_t* lengths, int32_t* status) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i == 0) {
+    p.state[0] = p.n_pages;
+    p.state[1] = 0u;
+    *status = 0;
+  }
+  if (i < p.n_streams) {
+    p.state[2 + 2 * i] = kNoPage;
+    p.state[3 + 2 * i] = 0u;
+    lengths[i] = 0;
+  }
+  if (i < (int64_t)p.n_pages) p.state[2 + 2 * p.n_streams + i] = p.n_pages - 1u - (uint32_t)i;
+}
+
+// Stream s back to empty: its pages go back on the stack.  Its records were
+// placed in page order (K then V of each closed block), so each page shows
+// up in one run of consecutive records.
+__global__ __launch_bounds__(64) void k_paged_release(PageAlloc p, const uint2* k_tab, const uint2* v_tab,
+                                                      int64_t tab_stride, int32_t* lengths, int B, int s) {
+  if (threadIdx.x != 0) return;
+  const int nfull = lengths[s] / B;
+  const uint2* kt = k_tab + s * tab_stride;
+  const uint2* vt = v_tab + s * tab_stride;
+  uint32_t last = kNoPage;
+  for (int j = 0; j < nfull; ++j) {
+    const uint32_t pk = kt[j].x / p.page16, pv = vt[j].x / p.page16;
+    if (pk != last) {
+      p.state[2 + 2 * p.n_streams + atomicAdd(reinterpret_cast<int*>(p.state), 1)] = pk;
+      last = pk;
+    }
+    if (pv != last) {
+      p.state[2 + 2 * p.n_streams + atomicAdd(reinterpret_cast<int*>(p.state), 1)] = pv;
+      last = pv;
+    }
+  }
+  p.state[2 + 2 * s] = kNoPage;
+  p.state[3 + 2 * s] = 0u;
+  lengths[s] = 0;
 }
 
 // Per stream: sizes in off[1..nb] -> byte offsets (off[0] = 0).
@@ -536,6 +691,24 @@ hipError_t launch_encode(const EncArgs& a, int n_streams, int n_blocks, hipStrea
   dim3 grid(a.mode == kTail ? 1 : n_blocks, n_streams);
   if (a.B == 64) hipLaunchKernelGGL(k_encode<64>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(k_encode<128>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_alloc(const EncArgs& a, int n_streams, int64_t n_tokens, hipStream_t st) {
+  hipLaunchKernelGGL(k_paged_alloc, dim3((n_streams + 63) / 64), dim3(64), 0, st, a, n_streams, n_tokens);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_init(const PageAlloc& p, int32_t* lengths, int32_t* status, hipStream_t st) {
+  const int64_t n = p.n_pages > (uint32_t)p.n_streams ? (int64_t)p.n_pages : (int64_t)p.n_streams;
+  hipLaunchKernelGGL(k_paged_init, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, lengths, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_release(const PageAlloc& p, const uint2* k_tab, const uint2* v_tab,
+                                int64_t tab_stride, int32_t* lengths, int B, int stream, hipStream_t st) {
+  hipLaunchKernelGGL(k_paged_release, dim3(1), dim3(64), 0, st, p, k_tab, v_tab, tab_stride, lengths, B,
+                     stream);
   return hipGetLastError();
 }
 

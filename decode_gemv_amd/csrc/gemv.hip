@@ -22,6 +22,8 @@
 // Integers become floats through v_cvt_pk_f32_fp8 (two per instruction): a
 // byte n <= 15 read as an fp8 e4m3 number is exactly n * c for a power of two
 // c, and 1/c is folded into the dense operand.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace packkv {
@@ -59,8 +61,8 @@ __device__ __forceinline__ void nibbles_to_f32(uint32_t w, float f[8]) {
 
 // A record is usable only if it lies inside its stream region and fits the
 // staging buffer; corrupt offsets must never turn into wild loads.
-__device__ __forceinline__ bool record_ok(uint32_t o, uint32_t size, uint64_t stride, int rec_max) {
-  return size >= 16u && size <= (uint32_t)rec_max && (uint64_t)o + size <= stride;
+__device__ __forceinline__ bool record_ok(uint64_t o, uint32_t size, uint64_t stride, int rec_max) {
+  return size >= 16u && size <= (uint32_t)rec_max && o + size <= stride;
 }
 
 // Raw buffer resource over [base, base + bytes): the hardware range check
@@ -285,6 +287,23 @@ struct RecordOffsets {
   __device__ __forceinline__ uint32_t operator()(int i) const {
     return i < 64 ? readlane_u32(lo, i) : readlane_u32(hi, i - 64);
   }
+  // block i of the window: byte offset in the stream region and size
+  __device__ __forceinline__ uint64_t start(int i) const { return (*this)(i); }
+  __device__ __forceinline__ uint32_t size(int i) const { return (*this)(i + 1) - (*this)(i); }
+};
+
+// The same window read from a paged cache's block table: entry j holds the
+// record's start in 16-byte units of the pool and its size in bytes.  Lane l
+// keeps entry j0 + l (windows of at most 64 blocks).
+struct RecordTable {
+  uint32_t st, sz;
+  __device__ __forceinline__ void load(const uint2* tab, int j0, int nj, int lane) {
+    const uint2 e = lane < nj ? tab[j0 + lane] : make_uint2(0u, 0u);
+    st = e.x;
+    sz = e.y;
+  }
+  __device__ __forceinline__ uint64_t start(int i) const { return (uint64_t)readlane_u32(st, i) << 4; }
+  __device__ __forceinline__ uint32_t size(int i) const { return readlane_u32(sz, i); }
 };
 
 // ---------------------------------------------------------------------------
@@ -545,21 +564,23 @@ struct VBlock {
 // nothing (an exit inside the body would give the wait-count analysis a path
 // with a different set of loads in flight, and it would then drain the load
 // queue at every block).
-template <int NCH, int REC>
+template <int NCH, int REC, class Loc = RecordOffsets>
 struct RecordStream {
   const uint8_t* arena;
   uint64_t stride;
-  RecordOffsets offs;
+  Loc offs;
   int nj, lane;
   __device__ __forceinline__ void request(int jj, u32x4 (&pre)[NCH]) const {
     const bool in = jj < nj;
-    const uint32_t o = in ? offs(jj) : 0u, size = in ? offs(jj + 1) - o : 0u;
+    const uint64_t o = in ? offs.start(jj) : 0u;
+    const uint32_t size = in ? offs.size(jj) : 0u;
     load_record<NCH>(arena + o, record_ok(o, size, stride, REC) ? size : 0u, lane, pre);
   }
   // size of block jj's record, 0 if jj is missing; rok: in range and sane
   __device__ __forceinline__ uint32_t size_of(int jj, bool& rok) const {
     const bool in = jj < nj;
-    const uint32_t o = in ? offs(jj) : 0u, size = in ? offs(jj + 1) - o : 0u;
+    const uint64_t o = in ? offs.start(jj) : 0u;
+    const uint32_t size = in ? offs.size(jj) : 0u;
     rok = record_ok(o, size, stride, REC);
     return rok ? size : 0u;
   }
@@ -791,7 +812,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 template <int B, int BITS, int GT>
 constexpr int attn_waves_per_eu() { return B == 128 ? 3 : B == 64 && BITS == 2 && GT == 1 ? 5 : 1; }
 
-template <int B, int BITS, int GT>
+template <int B, int BITS, int GT, bool PAGED>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<B, BITS, GT>())))
 void k_attn_decode(AttnArgs a) {
   using KB = KBlock<B, BITS, GT>;
@@ -818,10 +839,22 @@ void k_attn_decode(AttnArgs a) {
   uint32_t* tickets = reinterpret_cast<uint32_t*>(a.ws + blockIdx.y * a.ws_stride + a.partial_bytes);
   const int s = blockIdx.x / a.splits;
   const int split = blockIdx.x % a.splits;
+  // the stream's length: one for the cache, or (paged) the stream's own
+  int64_t n_tokens = a.n_tokens;
+  int nb = a.nb;
+  if constexpr (PAGED) {
+    n_tokens = __builtin_amdgcn_readfirstlane(cache.lengths[s]);
+    nb = (int)((n_tokens + B - 1) / B);
+  }
   // the splits divide the blocks evenly: floor or ceil of nb / splits each
-  const int j0 = (int)((int64_t)split * a.nb / a.splits);
-  const int nj = (int)((int64_t)(split + 1) * a.nb / a.splits) - j0;
+  const int j0 = (int)((int64_t)split * nb / a.splits);
+  int nj = (int)((int64_t)(split + 1) * nb / a.splits) - j0;
   bool corrupt = false;
+  if (PAGED && nj > 64) {                           // a length the launch was not sized for
+    nj = 64;
+    corrupt = true;
+  }
+  using Loc = std::conditional_t<PAGED, RecordTable, RecordOffsets>;
   const float NEG_INF = -__builtin_huge_valf();
 
   // Both waves pass the same barriers: one per block and one per query group.
@@ -829,10 +862,15 @@ void k_attn_decode(AttnArgs a) {
     for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
       // K wave: the scores of every block, handed over through the ring
       // with one workgroup barrier per block
-      RecordStream<NCH_K, REC_K> ks;
-      ks.arena = cache.k_arena + (uint64_t)s * a.arena_stride;
+      RecordStream<NCH_K, REC_K, Loc> ks;
+      if constexpr (PAGED) {
+        ks.arena = cache.k_arena;
+        ks.offs.load(cache.k_tab + (int64_t)s * a.off_stride, j0, nj, lane);
+      } else {
+        ks.arena = cache.k_arena + (uint64_t)s * a.arena_stride;
+        ks.offs.load(cache.k_off + (int64_t)s * a.off_stride, j0, nj, lane);
+      }
       ks.stride = a.arena_stride;
-      ks.offs.load(cache.k_off + (int64_t)s * a.off_stride, j0, nj, lane);
       ks.nj = nj;
       ks.lane = lane;
       KB kb;
@@ -841,7 +879,7 @@ void k_attn_decode(AttnArgs a) {
       u32x4 pre[NCH_K];
       ks.request(0, pre);
       for (int jj = 0; jj < nj; ++jj) {
-        const int n = (int)imin64(B, a.n_tokens - (int64_t)(j0 + jj) * B);
+        const int n = (int)imin64(B, n_tokens - (int64_t)(j0 + jj) * B);
         bool rok;
         const uint32_t size = ks.size_of(jj, rok);
         corrupt |= !rok;
@@ -861,10 +899,15 @@ void k_attn_decode(AttnArgs a) {
   } else {
     for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
       // V wave: running-max softmax over the scores, weighted sum of V
-      RecordStream<NCH_V, REC_V> vs;
-      vs.arena = cache.v_arena + (uint64_t)s * a.arena_stride;
+      RecordStream<NCH_V, REC_V, Loc> vs;
+      if constexpr (PAGED) {
+        vs.arena = cache.v_arena;
+        vs.offs.load(cache.v_tab + (int64_t)s * a.off_stride, j0, nj, lane);
+      } else {
+        vs.arena = cache.v_arena + (uint64_t)s * a.arena_stride;
+        vs.offs.load(cache.v_off + (int64_t)s * a.off_stride, j0, nj, lane);
+      }
       vs.stride = a.arena_stride;
-      vs.offs.load(cache.v_off + (int64_t)s * a.off_stride, j0, nj, lane);
       vs.nj = nj;
       vs.lane = lane;
       VB vb;
@@ -875,7 +918,7 @@ void k_attn_decode(AttnArgs a) {
       u32x4 pre[NCH_V];
       vs.request(0, pre);
       for (int jj = 0; jj < nj; ++jj) {
-        const int n = (int)imin64(B, a.n_tokens - (int64_t)(j0 + jj) * B);
+        const int n = (int)imin64(B, n_tokens - (int64_t)(j0 + jj) * B);
         __syncthreads();                            // block jj's scores are in the ring
         // weights exp(s - m); earlier sums rescaled when m grows
         float w[GT][NH];
@@ -966,7 +1009,9 @@ void k_attn_decode(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) o[k] += __shfl_xor(o[k], 32, kWave);
     if (half == 0) {
-      float4 res = {o[0] / L, o[1] / L, o[2] / L, o[3] / L};
+      // an empty stream (paged) has no weights: its output is zero
+      float4 res = {L > 0.f ? o[0] / L : 0.f, L > 0.f ? o[1] / L : 0.f, L > 0.f ? o[2] / L : 0.f,
+                    L > 0.f ? o[3] / L : 0.f};
       *reinterpret_cast<float4*>(out + ((int64_t)s * a.G + g) * kD + d4) = res;
     }
   }
@@ -1172,21 +1217,27 @@ hipError_t launch_pv(const GemvArgs& a, int B, int n_streams, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int B, int BITS>
+template <int B, int BITS, bool PAGED>
 static void attn_launch(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  if (a.G == 1) hipLaunchKernelGGL((k_attn_decode<B, BITS, 1>), grid, dim3(128), 0, st, a);
-  else hipLaunchKernelGGL((k_attn_decode<B, BITS, 4>), grid, dim3(128), 0, st, a);
+  if (a.G == 1) hipLaunchKernelGGL((k_attn_decode<B, BITS, 1, PAGED>), grid, dim3(128), 0, st, a);
+  else hipLaunchKernelGGL((k_attn_decode<B, BITS, 4, PAGED>), grid, dim3(128), 0, st, a);
 }
-hipError_t launch_attention(const AttnArgs& a, int B, int n_streams, int n_caches, hipStream_t st) {
-  const dim3 grid(n_streams * a.splits, n_caches);
+template <bool PAGED>
+static void attn_dispatch(const AttnArgs& a, int B, dim3 grid, hipStream_t st) {
   switch (B * 8 + a.bits) {
-    case 64 * 8 + 2: attn_launch<64, 2>(a, grid, st); break;
-    case 64 * 8 + 3: attn_launch<64, 3>(a, grid, st); break;
-    case 64 * 8 + 4: attn_launch<64, 4>(a, grid, st); break;
-    case 128 * 8 + 2: attn_launch<128, 2>(a, grid, st); break;
-    case 128 * 8 + 3: attn_launch<128, 3>(a, grid, st); break;
-    default: attn_launch<128, 4>(a, grid, st); break;
+    case 64 * 8 + 2: attn_launch<64, 2, PAGED>(a, grid, st); break;
+    case 64 * 8 + 3: attn_launch<64, 3, PAGED>(a, grid, st); break;
+    case 64 * 8 + 4: attn_launch<64, 4, PAGED>(a, grid, st); break;
+    case 128 * 8 + 2: attn_launch<128, 2, PAGED>(a, grid, st); break;
+    case 128 * 8 + 3: attn_launch<128, 3, PAGED>(a, grid, st); break;
+    default: attn_launch<128, 4, PAGED>(a, grid, st); break;
   }
+}
+hipError_t launch_attention(const AttnArgs& a, int B, int n_streams, int n_caches, hipStream_t st,
+                            bool paged) {
+  const dim3 grid(n_streams * a.splits, n_caches);
+  if (paged) attn_dispatch<true>(a, B, grid, st);
+  else attn_dispatch<false>(a, B, grid, st);
   return hipGetLastError();
 }
 

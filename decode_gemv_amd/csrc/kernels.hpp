@@ -7,6 +7,24 @@ namespace packkv {
 
 enum EncMode : int { kPass1 = 0, kPass2 = 1, kTail = 2 };
 
+// Page allocator state of a paged cache, in one device array of u32:
+//   [0] free pages, [1] 0, [2 + 2s] stream s's current page (kNoPage: none),
+//   [3 + 2s] its fill in 16-byte units, then the stack of free page indices.
+// A stream's records (K then V of each closed block, in block order) are
+// placed one after another in its current page; a record that does not fit
+// takes a new page from the stack, so no record straddles two pages.  The
+// open block's K and V records live in two fixed tail slots per stream past
+// the pages.
+constexpr uint32_t kNoPage = 0xFFFFFFFFu;
+struct PageAlloc {
+  uint32_t* state;
+  int32_t n_streams;
+  uint32_t n_pages;
+  uint32_t page16;          // page size in 16-byte units
+  uint32_t tail16;          // start of the tail slots in 16-byte units
+  uint32_t slot16;          // one tail slot in 16-byte units
+};
+
 struct EncArgs {
   const uint16_t* k;        // raw fp16 source of token 0 of stream 0
   const uint16_t* v;
@@ -33,6 +51,17 @@ struct EncArgs {
   uint8_t* perm;
   int64_t perm_stride;      // max_blocks * B
   int32_t* status;
+  // Paged cache (k_arena = v_arena = the pool, paged != 0): record j of
+  // stream s starts 16 * k_tab[s * off_stride + j].x bytes into the pool and
+  // is .y bytes long; the stream's length is lengths[s] (kTail appends one
+  // token per stream and reads its position from there).  Streams of the
+  // launch are stream0 + blockIdx.y.
+  int32_t paged;
+  int32_t stream0;
+  uint2* k_tab;
+  uint2* v_tab;
+  int32_t* lengths;
+  PageAlloc pages;
 };
 
 struct GemvArgs {
@@ -62,17 +91,20 @@ struct GemvArgs {
 // of a model) in one launch: blockIdx.y picks the cache.
 constexpr int kAttnMaxCaches = 32;
 struct AttnCache {
-  const uint8_t* k_arena;
+  const uint8_t* k_arena;   // paged: the pool
   const uint8_t* v_arena;
   const uint32_t* k_off;
   const uint32_t* v_off;
   int32_t* status;
+  const uint2* k_tab;       // paged: block tables [S][off_stride] and lengths [S]
+  const uint2* v_tab;
+  const int32_t* lengths;
 };
 struct AttnArgs {
   AttnCache cache[kAttnMaxCaches];
-  uint64_t arena_stride;
-  int64_t off_stride;
-  int64_t n_tokens;
+  uint64_t arena_stride;    // paged: the pool's size in bytes
+  int64_t off_stride;       // paged: block-table entries per stream
+  int64_t n_tokens;         // paged: unused (lengths[s] per stream)
   int32_t nb;
   int32_t bits;
   int32_t blocks_per_wg;
@@ -96,7 +128,12 @@ hipError_t launch_stage_tail(const uint16_t* k, const uint16_t* v, int64_t src_s
                              int n_streams, hipStream_t st);
 hipError_t launch_qk(const GemvArgs& a, int B, int n_streams, hipStream_t st);
 hipError_t launch_pv(const GemvArgs& a, int B, int n_streams, hipStream_t st);
-hipError_t launch_attention(const AttnArgs& a, int B, int n_streams, int n_caches, hipStream_t st);
+hipError_t launch_attention(const AttnArgs& a, int B, int n_streams, int n_caches, hipStream_t st,
+                            bool paged = false);
+hipError_t launch_paged_alloc(const EncArgs& a, int n_streams, int64_t n_tokens, hipStream_t st);
+hipError_t launch_paged_init(const PageAlloc& p, int32_t* lengths, int32_t* status, hipStream_t st);
+hipError_t launch_paged_release(const PageAlloc& p, const uint2* k_tab, const uint2* v_tab,
+                                int64_t tab_stride, int32_t* lengths, int B, int stream, hipStream_t st);
 hipError_t launch_decompress(const GemvArgs& a, int B, bool is_v, int n_streams, const uint8_t* perm,
                              int64_t perm_stride, int mode, void* out, hipStream_t st);
 hipError_t launch_stats(const GemvArgs& a, int B, bool is_v, int n_streams, unsigned long long* out,

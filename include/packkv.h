@@ -271,6 +271,111 @@ int packkv_stats(const packkv_cache_t* cache, uint64_t* out, void* stream);
 /* Static text for a status code. */
 const char* packkv_status_str(int status);
 
+/* ------------------------------------------------------------------------
+ * Paged cache.  The pages list PagedAttention among the prior work and name
+ * paging as a running cost of custom packed formats; this is the form of it
+ * for variable-size records.  The records of every stream share one pool of
+ * fixed-size pages and are found through per-stream block tables, and each
+ * stream holds its own number of tokens.
+ *
+ *   - A stream's closed blocks are placed one after another in its current
+ *     page, K record then V record, in block order.  A record that does not
+ *     fit takes a new page from a free-page stack on the device, so no
+ *     record straddles two pages and a page belongs to one stream.
+ *   - The open (partial) block's K and V records live in two fixed tail
+ *     slots of the stream, past the pages, and are re-encoded there by every
+ *     append; the append that fills the block writes it into the pages.
+ *   - Releasing a stream returns its pages to the stack.
+ *   - Every record is byte-identical to the one packkv_cache_t holds for the
+ *     same tokens; only where it lives differs.
+ *
+ * Same conventions as packkv_cache_t (caller-owned device memory, one HIP
+ * stream per call, host checks before any launch, device-only failures
+ * latched in *status).  Device-side failures: no free page left
+ * (PACKKV_ECAPACITY; the pool is then in an undefined state and must be set
+ * up again with packkv_paged_init) and inconsistent table entries
+ * (PACKKV_ECORRUPT).
+ */
+typedef struct {
+  packkv_config_t cfg;
+  int32_t n_streams;      /* S >= 1                                           */
+  int32_t n_pages;        /* pages in the pool, >= 1                          */
+  int64_t max_tokens;     /* capacity of each stream (sizes the block tables) */
+  uint64_t page_bytes;    /* multiple of 256 and >= min_page_bytes            */
+  uint8_t* pool;          /* [pool_bytes]: n_pages pages, then the tail slots */
+  uint64_t* k_table;      /* [S][max_blocks]: bits 0-31 the record's start in
+                             16-byte units of the pool, bits 32-63 its size
+                             in bytes; valid for blocks < ceil(length / B)    */
+  uint64_t* v_table;      /* [S][max_blocks]                                  */
+  int32_t* lengths;       /* [S] tokens held by each stream                   */
+  uint32_t* alloc;        /* [alloc_bytes / 4] allocator state: [0] free pages,
+                             [1] 0, [2 + 2s] stream s's current page
+                             (0xFFFFFFFF: none) and [3 + 2s] its fill in
+                             16-byte units, then the stack of free pages      */
+  uint8_t* perm;          /* [S][max_blocks][B], as in packkv_cache_t         */
+  uint16_t* tail_k;       /* [S][B][D] fp16 raw tokens of each open block     */
+  uint16_t* tail_v;       /* [S][B][D]                                        */
+  int32_t* status;        /* [1] device error latch                           */
+  int32_t* host_lengths;  /* HOST memory [S]: the library keeps it equal to
+                             `lengths` (it sizes launches from it)            */
+} packkv_paged_t;
+
+typedef struct {
+  uint64_t pool_bytes;     /* n_pages * page_bytes + S * 2 * slot_bytes       */
+  uint64_t table_bytes;    /* S * max_blocks * 8, for each of k_table, v_table */
+  uint64_t alloc_bytes;    /* (2 + 2 * S + n_pages) * 4                       */
+  uint64_t lengths_bytes;  /* S * 4                                           */
+  uint64_t perm_bytes;     /* S * max_blocks * B                              */
+  uint64_t tail_bytes;     /* S * B * D * 2, for each of tail_k, tail_v       */
+  uint64_t slot_bytes;     /* one tail slot: the largest K or V record        */
+  uint64_t min_page_bytes; /* slot_bytes rounded up to 256                    */
+  int64_t max_blocks;      /* ceil(max_tokens / B)                            */
+} packkv_paged_sizes_t;
+
+/* Validate and report the sizes of a paged cache.  Host only.  EINVAL when
+ * page_bytes is not a multiple of 256 or below min_page_bytes, n_pages < 1,
+ * or the pool would not be addressable in 16-byte units by 32 bits. */
+int packkv_paged_sizes(const packkv_config_t* cfg, int32_t n_streams, int64_t max_tokens, int32_t n_pages,
+                       uint64_t page_bytes, packkv_paged_sizes_t* out);
+
+/* Every page free, every stream empty, the status clear (device and host). */
+int packkv_paged_init(packkv_paged_t* cache, void* stream);
+
+/*
+ * packkv_paged_prefill - packkv_compress_block for streams stream0 ..
+ * stream0 + n - 1, which must be empty (else ESTATE).  k_f16, v_f16: device
+ * fp16 [n][n_tokens][D], contiguous, 16-byte aligned; 1 <= n_tokens <=
+ * max_tokens.  Pages are taken as the records are placed; without enough
+ * free pages the streams stay empty and ECAPACITY is latched.
+ */
+int packkv_paged_prefill(packkv_paged_t* cache, int32_t stream0, int32_t n, const void* k_f16,
+                         const void* v_f16, int64_t n_tokens, void* stream);
+
+/*
+ * packkv_paged_append - one decode step: token k_f16[s], v_f16[s] (device
+ * fp16 [S][1][D]) is appended to every stream s at its own position, with
+ * the open-block re-encode of packkv_append_tokens.  ECAPACITY (before any
+ * launch) if a stream is full.
+ */
+int packkv_paged_append(packkv_paged_t* cache, const void* k_f16, const void* v_f16, void* stream);
+
+/* Stream s back to empty; its pages return to the free stack. */
+int packkv_paged_release(packkv_paged_t* cache, int32_t s, void* stream);
+
+/* Workspace of packkv_paged_attention for `group` queries per stream. */
+uint64_t packkv_paged_attention_workspace_bytes(const packkv_paged_t* cache, int32_t group);
+
+/*
+ * packkv_paged_attention - packkv_attention_decode over the paged cache,
+ * each stream over its own length; an empty stream's output is zero.  ESTATE
+ * if every stream is empty.
+ */
+int packkv_paged_attention(const packkv_paged_t* cache, const void* q_f16, int32_t group, float scale,
+                           float* out, void* workspace, uint64_t ws_bytes, void* stream);
+
+/* packkv_check for a paged cache. */
+int packkv_paged_check(const packkv_paged_t* cache, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

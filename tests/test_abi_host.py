@@ -121,3 +121,74 @@ def test_status_strings(lib):
     for code in range(7):
         assert lib.packkv_status_str(code)
     assert lib.packkv_status_str(99) == b"unknown status"
+
+
+def paged_cfg(lib, S=3, max_tokens=1000, n_pages=8, page=None, bits=4, block=64):
+    s = _lib.PagedSizes()
+    c = cfg(bits, block)
+    assert lib.packkv_paged_sizes(ctypes.byref(c), S, max_tokens, n_pages, 1 << 20, ctypes.byref(s)) == 0
+    page = page or s.min_page_bytes
+    fake = 4096
+    host = (ctypes.c_int32 * S)()
+    p = _lib.PagedT(c, S, n_pages, max_tokens, page, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                    ctypes.addressof(host))
+    return p, host, s
+
+
+@pytest.mark.parametrize("bits,block", [(2, 64), (4, 64), (3, 128), (4, 128)])
+def test_paged_sizes(lib, bits, block):
+    s = _lib.PagedSizes()
+    c = cfg(bits, block)
+    assert lib.packkv_paged_sizes(ctypes.byref(c), 3, 1000, 10, 1 << 16, ctypes.byref(s)) == 0
+    nr = block // 32
+    krec = -(-(512 + nr * 128) // 16) * 16 + 4 * nr * 128 * bits
+    vrec = -(-(4 * block + nr * 128) // 16) * 16 + 4 * nr * 128 * bits
+    assert s.slot_bytes == max(krec, vrec)
+    assert s.min_page_bytes % 256 == 0 and s.slot_bytes <= s.min_page_bytes < s.slot_bytes + 256
+    assert s.pool_bytes == 10 * (1 << 16) + 3 * 2 * s.slot_bytes + 256
+    mb = -(-1000 // block)
+    assert s.max_blocks == mb and s.table_bytes == 3 * mb * 8
+    assert s.alloc_bytes == (2 + 2 * 3 + 10) * 4 and s.lengths_bytes == 12
+    assert s.perm_bytes == 3 * mb * block and s.tail_bytes == 3 * block * 128 * 2
+    bad = lambda **kw: lib.packkv_paged_sizes(ctypes.byref(c), kw.get("S", 3), 1000, kw.get("n", 10),
+                                              kw.get("page", 1 << 16), ctypes.byref(s))
+    assert bad(page=s.min_page_bytes + 128) == _lib.EINVAL          # not a multiple of 256
+    assert bad(page=s.min_page_bytes - 256) == _lib.EINVAL          # below one record
+    assert bad(n=0) == _lib.EINVAL
+    assert bad(n=(1 << 36) // (1 << 16)) == _lib.EINVAL            # pool past 2^32 16-byte units
+    assert bad(S=0) == _lib.EINVAL
+
+
+def test_paged_calls_check_before_any_launch(lib):
+    p, host, s = paged_cfg(lib)
+    fake = 4096
+    P = ctypes.byref(p)
+    need = lib.packkv_paged_attention_workspace_bytes(P, 1)
+    assert need > 0
+    # every stream empty: nothing to attend to
+    assert lib.packkv_paged_attention(P, fake, 1, 0.1, fake, fake, need, None) == _lib.ESTATE
+    host[1] = 10
+    assert lib.packkv_paged_attention(P, fake, 1, 0.1, fake, fake, need - 1, None) == _lib.EINVAL
+    assert lib.packkv_paged_attention(P, None, 1, 0.1, fake, fake, need, None) == _lib.EINVAL
+    assert lib.packkv_paged_attention(P, fake, 0, 0.1, fake, fake, need, None) == _lib.EINVAL
+    assert lib.packkv_paged_attention(P, fake, 1, float("inf"), fake, fake, need, None) == _lib.EINVAL
+    # prefill: a stream that holds tokens, a range past S, too many tokens, misalignment
+    assert lib.packkv_paged_prefill(P, 1, 1, fake, fake, 10, None) == _lib.ESTATE
+    assert lib.packkv_paged_prefill(P, 0, 2, fake, fake, 10, None) == _lib.ESTATE
+    assert lib.packkv_paged_prefill(P, 2, 2, fake, fake, 10, None) == _lib.EINVAL
+    assert lib.packkv_paged_prefill(P, 0, 1, fake, fake, 1001, None) == _lib.ECAPACITY
+    assert lib.packkv_paged_prefill(P, 0, 1, fake + 2, fake, 10, None) == _lib.EINVAL
+    assert lib.packkv_paged_prefill(P, 0, 1, fake, fake, 0, None) == _lib.EINVAL
+    # append: one full stream stops the step
+    host[2] = 1000
+    assert lib.packkv_paged_append(P, fake, fake, None) == _lib.ECAPACITY
+    assert lib.packkv_paged_append(P, None, fake, None) == _lib.EINVAL
+    assert list(host) == [0, 10, 1000]                             # nothing changed
+    assert lib.packkv_paged_release(P, 3, None) == _lib.EINVAL
+    assert lib.packkv_paged_release(P, -1, None) == _lib.EINVAL
+    # a page below one record, or a missing array
+    p.page_bytes = s.min_page_bytes - 256
+    assert lib.packkv_paged_release(P, 0, None) == _lib.EINVAL
+    p.page_bytes = s.min_page_bytes
+    p.host_lengths = None
+    assert lib.packkv_paged_release(P, 0, None) == _lib.EINVAL
