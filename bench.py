@@ -5,9 +5,11 @@ One step is one decode-attention pass over the packed cache of every stream:
 append one new token per stream (open-tail re-encode: quantise, reorder,
 pack), then the K decompress-GEMV, softmax and the V decompress-GEMV, run as
 one fused launch.  The same steps are timed again with the three kernels
-launched separately (scores and weights through HBM).  The cache is
-prefilled (bulk compress) before the timed region, so every input is
-resident in HBM when timing starts.
+launched separately (scores and weights through HBM), and on paged copies
+of the cache (one page pool behind per-stream block tables), once with every
+stream at the workload's length and once with lengths spread from T to T/4.
+The caches are prefilled (bulk compress) before the timed region, so every
+input is resident in HBM when timing starts.
 
 value = compressed bytes the step reads (K and V records plus their offset
 tables) / wall time per step, in GB/s (1e9 B/s).  The per-kernel split, each
@@ -229,6 +231,8 @@ def main():
     ap.add_argument("--cpu-streams", type=int, default=4, help="streams in the oracle's timed sample")
     ap.add_argument("--cpu-steps", type=int, default=30, help="decode steps per sampled stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache measurement")
+    ap.add_argument("--page-kib", type=int, default=64, help="page size of the paged cache")
     ap.add_argument("--layers", type=int, default=1,
                     help="also time decode attention over this many caches of the workload's shape "
                          "(a model's layers): one multi-cache launch against one launch per cache")
@@ -272,6 +276,29 @@ def main():
         c2 = PackedKVCache(S, T_max, bits=w.bits, block=w.block, permute=args.permute, device="cuda:0")
         c2.compress(K, V)
         layer_caches.append(c2)
+    # the same tokens in paged caches: every stream at T0, and streams spread
+    # linearly from T0 down to T0/4 (ragged lengths)
+    paged = {}
+    if not args.no_paged:
+        from decode_gemv_amd import PagedKVCache
+        ko = cache.offsets("K").cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+        vo = cache.offsets("V").cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+        nb0 = -(-T0 // w.block)
+        per_token = (ko[:, nb0].sum() + vo[:, nb0].sum()) / (S * T0)
+        page = args.page_kib << 10
+        for kind in ("uniform", "ragged"):
+            lens = [T0] * S if kind == "uniform" else [T0 - (3 * T0 // 4) * s // S for s in range(S)]
+            n_pages = sum(int(np.ceil(1.1 * (L + n_steps) * per_token / page)) + 1 for L in lens) + 16
+            pc = PagedKVCache(S, T0 + n_steps + 8, n_pages, page_bytes=page, bits=w.bits, block=w.block,
+                              permute=args.permute, device="cuda:0")
+            if kind == "uniform":
+                pc.prefill(0, K, V)
+            else:
+                for s_, L in enumerate(lens):
+                    pc.prefill(s_, K[s_:s_ + 1, :L].contiguous(), V[s_:s_ + 1, :L].contiguous())
+            if pc.check() != 0:
+                raise RuntimeError(f"paged prefill ({kind}) failed")
+            paged[kind] = pc
     del K, V
     torch.cuda.empty_cache()
 
@@ -434,6 +461,58 @@ def main():
                 "traffic": tr.get("attn") if tr else None,
                 "kernel": "k_attn_decode", "bytes_per_launch": int(attn_alg), "launch_ms": round(t_attn, 4)}
 
+    # the step on the paged caches: append, then fused attention through the
+    # block tables
+    paged_res = None
+    if paged:
+        paged_res = {"page_bytes": args.page_kib << 10,
+                     "contiguous_arenas_MiB": round(2 * cache.sizes.arena_bytes / 2**20, 1)}
+        pout = torch.empty((S, G, D), dtype=torch.float32, device=dev)
+        for kind, pc in paged.items():
+            pws = pc.attention_workspace(G)
+
+            def alg_bytes():
+                (ks_, kz_), (vs_, vz_) = pc.tables()
+                tot = 0
+                for s_, L in enumerate(pc.lengths):
+                    nb_ = -(-L // w.block)
+                    tot += int(kz_[s_, :nb_].sum() + vz_[s_, :nb_].sum()) + 16 * nb_
+                return tot + S * G * D * 2 + S * G * D * 4
+
+            a0 = alg_bytes()
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_steps)]
+            torch.cuda.synchronize()
+            for i in range(n_steps):
+                if i == args.warmup:
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                ev[i][0].record()
+                pc.append(kn[i], vn[i])
+                ev[i][1].record()
+                pc.attention(qn[i], scale, out=pout, workspace=pws)
+                ev[i][2].record()
+            torch.cuda.synchronize()
+            wall = (time.perf_counter() - t0) / args.steps * 1e3
+            code = pc.check()
+            if code:
+                raise RuntimeError(f"paged cache status {code} after the {kind} loop")
+            a1 = alg_bytes()
+            t_pa = avg_ms(ev[args.warmup:], 1, 2)
+            used_pages = pc.n_pages - pc.free_pages()
+            lens = pc.lengths
+            paged_res[kind] = {
+                "attention_ms": round(t_pa, 4), "GBps": round((a0 + a1) / 2 / (t_pa * 1e-3) / 1e9, 1),
+                "append_ms": round(avg_ms(ev[args.warmup:], 0, 1), 4), "ms_per_step": round(wall, 4),
+                "tokens_min": min(lens), "tokens_max": max(lens), "tokens_mean": round(float(np.mean(lens)), 1),
+                "pages_used": used_pages,
+                "pool_used_MiB": round((used_pages * pc.page_bytes + 2 * S * pc.sizes.slot_bytes) / 2**20, 1),
+                "record_MiB": round(((a0 + a1) / 2 - S * G * D * 6) / 2**20, 1)}
+            log(f"paged {kind}: attention {t_pa:.4f} ms, {paged_res[kind]['GBps']} GB/s, "
+                f"{used_pages} pages")
+        paged_res["note"] = ("append then fused attention per step through the block tables; ragged: "
+                             "stream lengths spread linearly from T to T/4")
+        del paged
+
     # a plain device copy of known size, for counter calibration runs
     if args.copy_probe_mib > 0:
         a = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
@@ -470,6 +549,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "multi_layer": multi,
+        "paged": paged_res,
         "alg_bytes_per_launch": {"attn": int(attn_alg), "qk": int(qk_alg), "pv": int(pv_alg)},
         "kernel_source": kernel_source_hash(),
     }
