@@ -288,7 +288,7 @@ def main():
         page = args.page_kib << 10
         for kind in ("uniform", "ragged"):
             lens = [T0] * S if kind == "uniform" else [T0 - (3 * T0 // 4) * s // S for s in range(S)]
-            n_pages = sum(int(np.ceil(1.1 * (L + n_steps) * per_token / page)) + 1 for L in lens) + 16
+            n_pages = sum(int(np.ceil(1.1 * (L + n_steps) * per_token / page)) + 2 for L in lens) + 16
             pc = PagedKVCache(S, T0 + n_steps + 8, n_pages, page_bytes=page, bits=w.bits, block=w.block,
                               permute=args.permute, device="cuda:0")
             if kind == "uniform":
@@ -480,7 +480,7 @@ def main():
                 return tot + S * G * D * 2 + S * G * D * 4
 
             a0 = alg_bytes()
-            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_steps)]
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_steps)]
             torch.cuda.synchronize()
             for i in range(n_steps):
                 if i == args.warmup:
@@ -489,24 +489,43 @@ def main():
                 ev[i][0].record()
                 pc.append(kn[i], vn[i])
                 ev[i][1].record()
+                if kind == "uniform" and i % 2:
+                    # paired control: the contiguous cache's launch in the same
+                    # loop, before the paged one on odd steps and after on even
+                    cache.attention(qn[i], scale, out=fout, workspace=aws)
+                    ev[i][2].record()
                 pc.attention(qn[i], scale, out=pout, workspace=pws)
-                ev[i][2].record()
+                ev[i][3 if kind == "uniform" and i % 2 else 2].record()
+                if kind == "uniform" and i % 2 == 0:
+                    cache.attention(qn[i], scale, out=fout, workspace=aws)
+                    ev[i][3].record()
             torch.cuda.synchronize()
             wall = (time.perf_counter() - t0) / args.steps * 1e3
             code = pc.check()
             if code:
                 raise RuntimeError(f"paged cache status {code} after the {kind} loop")
             a1 = alg_bytes()
-            t_pa = avg_ms(ev[args.warmup:], 1, 2)
+            evs = ev[args.warmup:]
+            if kind == "uniform":
+                steps_i = range(args.warmup, n_steps)
+                t_pa = float(np.mean([ev[i][2].elapsed_time(ev[i][3]) if i % 2 else ev[i][1].elapsed_time(ev[i][2])
+                                      for i in steps_i]))
+                t_ctl = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) if i % 2 else ev[i][2].elapsed_time(ev[i][3])
+                                       for i in steps_i]))
+            else:
+                t_pa = avg_ms(evs, 1, 2)
             used_pages = pc.n_pages - pc.free_pages()
             lens = pc.lengths
             paged_res[kind] = {
                 "attention_ms": round(t_pa, 4), "GBps": round((a0 + a1) / 2 / (t_pa * 1e-3) / 1e9, 1),
-                "append_ms": round(avg_ms(ev[args.warmup:], 0, 1), 4), "ms_per_step": round(wall, 4),
+                "append_ms": round(avg_ms(evs, 0, 1), 4), "ms_per_step": round(wall, 4),
                 "tokens_min": min(lens), "tokens_max": max(lens), "tokens_mean": round(float(np.mean(lens)), 1),
                 "pages_used": used_pages,
                 "pool_used_MiB": round((used_pages * pc.page_bytes + 2 * S * pc.sizes.slot_bytes) / 2**20, 1),
                 "record_MiB": round(((a0 + a1) / 2 - S * G * D * 6) / 2**20, 1)}
+            if kind == "uniform":
+                paged_res[kind]["contiguous_attention_ms"] = round(t_ctl, 4)
+                paged_res[kind]["ms_per_step"] = None          # the loop also ran the control
             log(f"paged {kind}: attention {t_pa:.4f} ms, {paged_res[kind]['GBps']} GB/s, "
                 f"{used_pages} pages")
         paged_res["note"] = ("append then fused attention per step through the block tables; ragged: "

@@ -489,7 +489,7 @@ int packkv_paged_sizes(const packkv_config_t* cfg, int32_t n_streams, int64_t ma
   out->pool_bytes = paged_pool_bytes(cfg, n_streams, n_pages, page_bytes);
   if (out->pool_bytes >= (1ull << 36) || mb >= (1ll << 31)) return PACKKV_EINVAL;   // 32-bit 16-byte units
   out->table_bytes = (uint64_t)n_streams * (uint64_t)mb * 8;
-  out->alloc_bytes = (2u + 2u * (uint64_t)n_streams + (uint64_t)n_pages) * 4;
+  out->alloc_bytes = (2u + 4u * (uint64_t)n_streams + (uint64_t)n_pages) * 4;
   out->lengths_bytes = (uint64_t)n_streams * 4;
   out->perm_bytes = (uint64_t)n_streams * (uint64_t)mb * (uint64_t)cfg->block_tokens;
   out->tail_bytes = (uint64_t)n_streams * (uint64_t)cfg->block_tokens * kD * 2;
@@ -593,8 +593,8 @@ int packkv_paged_attention(const packkv_paged_t* c, const void* q_f16, int32_t g
   for (int32_t s = 0; s < c->n_streams; ++s) longest = c->host_lengths[s] > longest ? c->host_lengths[s] : longest;
   if (longest < 1) return PACKKV_ESTATE;
   const int B = c->cfg.block_tokens;
-  // the launch is divided for the longest stream; every stream spreads its
-  // own blocks evenly over the same splits
+  // the launch is sized for the longest stream; every stream spreads its
+  // own blocks evenly over the same splits (at most J each)
   const int nb = (int)((longest + B - 1) / B);
   const int J = gemv_blocks_per_wg(c->n_streams, nb, true, group);
   AttnArgs a;

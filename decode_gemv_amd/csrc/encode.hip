@@ -17,7 +17,7 @@
 
 namespace packkv {
 
-__device__ bool page_take(const PageAlloc& p, int s, uint32_t need16, uint32_t& start16);
+__device__ bool page_take(const PageAlloc& p, int s, int which, uint32_t need16, uint32_t& start16);
 
 // Smallest positive fp16 pattern h with value(h) * L >= d, for d > 0.
 __device__ uint32_t min_f16_step(double d, int L) {
@@ -450,7 +450,7 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
       // one stays in the stream's tail slots
       if (tid == 0) {
         uint32_t k16 = a.pages.tail16 + 2u * (uint32_t)s * a.pages.slot16, v16 = k16 + a.pages.slot16;
-        if (n == B && !(page_take(a.pages, s, k_size >> 4, k16) && page_take(a.pages, s, v_size >> 4, v16)))
+        if (n == B && !(page_take(a.pages, s, 0, k_size >> 4, k16) && page_take(a.pages, s, 1, v_size >> 4, v16)))
           k16 = kNoPage;
         base_sh[0] = k16;
         base_sh[1] = v16;
@@ -565,11 +565,12 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
 // ---------------------------------------------------------------------------
 // Paged cache: page allocation, set-up and release.
 
-// Place a record of need16 16-byte units in stream s's current page, or at
-// the start of a page taken from the free stack; false if none is left.
-// Called by one thread per stream at a time.
-__device__ bool page_take(const PageAlloc& p, int s, uint32_t need16, uint32_t& start16) {
-  uint32_t* st = p.state + 2 + 2 * s;
+// Place a K (which = 0) or V (1) record of need16 16-byte units in stream
+// s's current page of that kind, or at the start of a page taken from the
+// free stack; false if none is left.  Called by one thread per stream at a
+// time.
+__device__ bool page_take(const PageAlloc& p, int s, int which, uint32_t need16, uint32_t& start16) {
+  uint32_t* st = p.state + 2 + 4 * s + 2 * which;
   uint32_t page = st[0], fill = st[1];
   if (page == kNoPage || fill + need16 > p.page16) {
     const int old = atomicSub(reinterpret_cast<int*>(p.state), 1);
@@ -577,7 +578,7 @@ __device__ bool page_take(const PageAlloc& p, int s, uint32_t need16, uint32_t& 
       atomicAdd(reinterpret_cast<int*>(p.state), 1);
       return false;
     }
-    page = p.state[2 + 2 * p.n_streams + old - 1];
+    page = p.state[2 + 4 * p.n_streams + old - 1];
     fill = 0;
   }
   start16 = page * p.page16 + fill;
@@ -587,8 +588,9 @@ __device__ bool page_take(const PageAlloc& p, int s, uint32_t need16, uint32_t& 
 }
 
 // Prefill of n_streams streams from stream0 on, after pass 1 wrote the
-// sizes: one thread per stream places the closed blocks' records (K then V,
-// block order), points the open block at the tail slots and sets the length.
+// sizes: one thread per stream places the closed blocks' records (block
+// order, K and V in pages of their own), points the open block at the tail
+// slots and sets the length.
 __global__ __launch_bounds__(64) void k_paged_alloc(EncArgs a, int n_streams, int64_t n_tokens) {
   const int i = blockIdx.x * 64 + threadIdx.x;
   if (i >= n_streams) return;
@@ -598,7 +600,7 @@ __global__ __launch_bounds__(64) void k_paged_alloc(EncArgs a, int n_streams, in
   uint2* vt = a.v_tab + s * a.off_stride;
   for (int j = 0; j < nfull; ++j) {
     uint32_t k16, v16;
-    if (!page_take(a.pages, s, kt[j].y >> 4, k16) || !page_take(a.pages, s, vt[j].y >> 4, v16)) {
+    if (!page_take(a.pages, s, 0, kt[j].y >> 4, k16) || !page_take(a.pages, s, 1, vt[j].y >> 4, v16)) {
       latch(a.status, PACKKV_ECAPACITY);
       return;                                        // length stays 0: pass 2 writes nothing
     }
@@ -621,36 +623,35 @@ __global__ __launch_bounds__(256) void k_paged_init(PageAlloc p, int32_t* length
     *status = 0;
   }
   if (i < p.n_streams) {
-    p.state[2 + 2 * i] = kNoPage;
-    p.state[3 + 2 * i] = 0u;
+    for (int k = 0; k < 4; k += 2) {
+      p.state[2 + 4 * i + k] = kNoPage;
+      p.state[3 + 4 * i + k] = 0u;
+    }
     lengths[i] = 0;
   }
-  if (i < (int64_t)p.n_pages) p.state[2 + 2 * p.n_streams + i] = p.n_pages - 1u - (uint32_t)i;
+  if (i < (int64_t)p.n_pages) p.state[2 + 4 * p.n_streams + i] = p.n_pages - 1u - (uint32_t)i;
 }
 
-// Stream s back to empty: its pages go back on the stack.  Its records were
-// placed in page order (K then V of each closed block), so each page shows
-// up in one run of consecutive records.
+// Stream s back to empty: its pages go back on the stack.  Its K records
+// fill its K pages in block order (and likewise V), so each page shows up
+// in one run of consecutive records of its kind.
 __global__ __launch_bounds__(64) void k_paged_release(PageAlloc p, const uint2* k_tab, const uint2* v_tab,
                                                       int64_t tab_stride, int32_t* lengths, int B, int s) {
   if (threadIdx.x != 0) return;
   const int nfull = lengths[s] / B;
-  const uint2* kt = k_tab + s * tab_stride;
-  const uint2* vt = v_tab + s * tab_stride;
-  uint32_t last = kNoPage;
-  for (int j = 0; j < nfull; ++j) {
-    const uint32_t pk = kt[j].x / p.page16, pv = vt[j].x / p.page16;
-    if (pk != last) {
-      p.state[2 + 2 * p.n_streams + atomicAdd(reinterpret_cast<int*>(p.state), 1)] = pk;
-      last = pk;
+  for (int which = 0; which < 2; ++which) {
+    const uint2* t = (which ? v_tab : k_tab) + s * tab_stride;
+    uint32_t last = kNoPage;
+    for (int j = 0; j < nfull; ++j) {
+      const uint32_t pg = t[j].x / p.page16;
+      if (pg != last) {
+        p.state[2 + 4 * p.n_streams + atomicAdd(reinterpret_cast<int*>(p.state), 1)] = pg;
+        last = pg;
+      }
     }
-    if (pv != last) {
-      p.state[2 + 2 * p.n_streams + atomicAdd(reinterpret_cast<int*>(p.state), 1)] = pv;
-      last = pv;
-    }
+    p.state[2 + 4 * s + 2 * which] = kNoPage;
+    p.state[3 + 4 * s + 2 * which] = 0u;
   }
-  p.state[2 + 2 * s] = kNoPage;
-  p.state[3 + 2 * s] = 0u;
   lengths[s] = 0;
 }
 

@@ -278,18 +278,19 @@ struct BlockDecoder {
 // ---------------------------------------------------------------------------
 // Offsets of a workgroup's records: lane i holds off[j0 + i] and
 // off[j0 + 64 + i] (up to 128 blocks), read back with readlane.
+// A window of at most 64 consecutive blocks (the work division never gives
+// a workgroup more): lane l keeps block j0 + l's record offset in the
+// stream region and its size, so a block's record costs one readlane each.
 struct RecordOffsets {
-  uint32_t lo, hi;
+  uint32_t st, sz;
   __device__ __forceinline__ void load(const uint32_t* offs, int j0, int nj, int lane) {
-    lo = lane <= nj ? offs[j0 + lane] : 0u;
-    hi = lane + 64 <= nj ? offs[j0 + 64 + lane] : 0u;
+    const uint32_t a = lane < nj ? offs[j0 + lane] : 0u;
+    const uint32_t b = lane < nj ? offs[j0 + lane + 1] : 0u;
+    st = a;
+    sz = b - a;
   }
-  __device__ __forceinline__ uint32_t operator()(int i) const {
-    return i < 64 ? readlane_u32(lo, i) : readlane_u32(hi, i - 64);
-  }
-  // block i of the window: byte offset in the stream region and size
-  __device__ __forceinline__ uint64_t start(int i) const { return (*this)(i); }
-  __device__ __forceinline__ uint32_t size(int i) const { return (*this)(i + 1) - (*this)(i); }
+  __device__ __forceinline__ uint64_t start(int i) const { return readlane_u32(st, i); }
+  __device__ __forceinline__ uint32_t size(int i) const { return readlane_u32(sz, i); }
 };
 
 // The same window read from a paged cache's block table: entry j holds the

@@ -8,13 +8,15 @@ namespace packkv {
 enum EncMode : int { kPass1 = 0, kPass2 = 1, kTail = 2 };
 
 // Page allocator state of a paged cache, in one device array of u32:
-//   [0] free pages, [1] 0, [2 + 2s] stream s's current page (kNoPage: none),
-//   [3 + 2s] its fill in 16-byte units, then the stack of free page indices.
-// A stream's records (K then V of each closed block, in block order) are
-// placed one after another in its current page; a record that does not fit
-// takes a new page from the stack, so no record straddles two pages.  The
-// open block's K and V records live in two fixed tail slots per stream past
-// the pages.
+//   [0] free pages, [1] 0, [2 + 4s] stream s's current K page (kNoPage:
+//   none), [3 + 4s] its fill in 16-byte units, [4 + 4s], [5 + 4s] the same
+//   for V, then the stack of free page indices.
+// A stream's K records of closed blocks are placed one after another, in
+// block order, in its current K page (V records in its V page), so each
+// wave of the attention kernel still reads one sequential run per page; a
+// record that does not fit takes a new page from the stack, so no record
+// straddles two pages.  The open block's K and V records live in two fixed
+// tail slots per stream past the pages.
 constexpr uint32_t kNoPage = 0xFFFFFFFFu;
 struct PageAlloc {
   uint32_t* state;

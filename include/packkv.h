@@ -278,10 +278,11 @@ const char* packkv_status_str(int status);
  * fixed-size pages and are found through per-stream block tables, and each
  * stream holds its own number of tokens.
  *
- *   - A stream's closed blocks are placed one after another in its current
- *     page, K record then V record, in block order.  A record that does not
- *     fit takes a new page from a free-page stack on the device, so no
- *     record straddles two pages and a page belongs to one stream.
+ *   - A stream's closed blocks are placed in block order, the K records one
+ *     after another in its current K page and the V records in its current V
+ *     page.  A record that does not fit takes a new page from a free-page
+ *     stack on the device, so no record straddles two pages and a page
+ *     belongs to one stream and one of K, V.
  *   - The open (partial) block's K and V records live in two fixed tail
  *     slots of the stream, past the pages, and are re-encoded there by every
  *     append; the append that fills the block writes it into the pages.
@@ -309,9 +310,10 @@ typedef struct {
   uint64_t* v_table;      /* [S][max_blocks]                                  */
   int32_t* lengths;       /* [S] tokens held by each stream                   */
   uint32_t* alloc;        /* [alloc_bytes / 4] allocator state: [0] free pages,
-                             [1] 0, [2 + 2s] stream s's current page
-                             (0xFFFFFFFF: none) and [3 + 2s] its fill in
-                             16-byte units, then the stack of free pages      */
+                             [1] 0, [2 + 4s] stream s's current K page
+                             (0xFFFFFFFF: none) and [3 + 4s] its fill in
+                             16-byte units, [4 + 4s], [5 + 4s] the same for
+                             V, then the stack of free pages                  */
   uint8_t* perm;          /* [S][max_blocks][B], as in packkv_cache_t         */
   uint16_t* tail_k;       /* [S][B][D] fp16 raw tokens of each open block     */
   uint16_t* tail_v;       /* [S][B][D]                                        */
@@ -323,7 +325,7 @@ typedef struct {
 typedef struct {
   uint64_t pool_bytes;     /* n_pages * page_bytes + S * 2 * slot_bytes       */
   uint64_t table_bytes;    /* S * max_blocks * 8, for each of k_table, v_table */
-  uint64_t alloc_bytes;    /* (2 + 2 * S + n_pages) * 4                       */
+  uint64_t alloc_bytes;    /* (2 + 4 * S + n_pages) * 4                       */
   uint64_t lengths_bytes;  /* S * 4                                           */
   uint64_t perm_bytes;     /* S * max_blocks * B                              */
   uint64_t tail_bytes;     /* S * B * D * 2, for each of tail_k, tail_v       */

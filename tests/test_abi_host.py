@@ -148,7 +148,7 @@ def test_paged_sizes(lib, bits, block):
     assert s.pool_bytes == 10 * (1 << 16) + 3 * 2 * s.slot_bytes + 256
     mb = -(-1000 // block)
     assert s.max_blocks == mb and s.table_bytes == 3 * mb * 8
-    assert s.alloc_bytes == (2 + 2 * 3 + 10) * 4 and s.lengths_bytes == 12
+    assert s.alloc_bytes == (2 + 4 * 3 + 10) * 4 and s.lengths_bytes == 12
     assert s.perm_bytes == 3 * mb * block and s.tail_bytes == 3 * block * 128 * 2
     bad = lambda **kw: lib.packkv_paged_sizes(ctypes.byref(c), kw.get("S", 3), 1000, kw.get("n", 10),
                                               kw.get("page", 1 << 16), ctypes.byref(s))

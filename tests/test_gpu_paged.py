@@ -43,9 +43,10 @@ def paged(torch, dev, S, max_tokens, n_pages, page_records, bits, block, permute
 
 
 def check_placement(c):
-    """Every record of a closed block lies inside one page; pages belong to one
-    stream; open blocks sit in their stream's tail slots; nothing overlaps;
-    the free count is what the streams do not hold."""
+    """Every record of a closed block lies inside one page; a page belongs to
+    one stream and holds only K or only V records; open blocks sit in their
+    stream's tail slots; nothing overlaps; the free count is what the streams
+    do not hold."""
     (ks, kz), (vs, vz) = c.tables()
     slot, page = int(c.sizes.slot_bytes), c.page_bytes
     tail0 = c.n_pages * page
@@ -58,7 +59,7 @@ def check_placement(c):
                 if j < nfull:
                     p = st // page
                     assert p < c.n_pages and (st + sz - 1) // page == p, f"record straddles a page, stream {s}"
-                    assert owner.setdefault(p, s) == s, f"page {p} shared by two streams"
+                    assert owner.setdefault(p, (s, which)) == (s, which), f"page {p} shared"
                 else:
                     assert st == tail0 + (2 * s + which) * slot, f"open block not in its tail slot, stream {s}"
                     assert sz <= slot
@@ -163,7 +164,7 @@ def test_release_returns_pages_and_the_stream_is_reused(torch_dev, bits, block):
     c.prefill(0, torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev))
     assert c.check() == 0
     owner = check_placement(c)
-    held = sum(1 for s in owner.values() if s == 1)
+    held = sum(1 for s, _ in owner.values() if s == 1)
     free0 = c.free_pages()
     c.release(1)
     assert c.check() == 0
