@@ -17,6 +17,9 @@ from __future__ import annotations
 
 import numpy as np
 
+from .perm import block_permutation
+from .quant import quantize_k_block, quantize_v_tokens
+from .record import run_widths
 from .stream import StreamCache
 from .unpack import decode_record
 
@@ -53,3 +56,42 @@ def closed_form_full_width(which: str, bits: int, block: int, run: int, D: int) 
     16 / (b + 8/R + 32/D) for V (per-value bit cost of payload, header, params)."""
     per = block if which == "K" else D
     return 16.0 / (bits + 8.0 / run + 32.0 / per)
+
+
+def run_length_bits(k16: np.ndarray, v16: np.ndarray, bits: int, block: int, permute: int, run: int):
+    """Ideal bits of the K and of the V records of one stream if the packing
+    run were ``run`` slots instead of the format's 32 (a study of the pages'
+    open choice of run length; nothing is stored in this form).
+
+    Every block is quantised as the format does, ordered by the permutation
+    rule with groups of ``run`` tokens (and its identity fallback judged at
+    that run length), and counted like ``ratios``' ideal figure: ``run * w``
+    payload bits and 8 header bits per (run, channel), plus the parameters
+    (K: 32 bits per channel per block, V: 32 per token).
+    """
+    n_tok, D = k16.shape
+    kb = vb = 0
+    for j0 in range(0, n_tok, block):
+        k, v = k16[j0:j0 + block], v16[j0:j0 + block]
+        n = k.shape[0]
+        qk = quantize_k_block(k, bits)[0]
+        qv = quantize_v_tokens(v, bits)[0]
+        perm = block_permutation(qk, qv, run, permute)
+        wk, _ = run_widths(qk[perm], run)
+        wv, _ = run_widths(qv[perm], run)
+        kb += run * int(wk.sum()) + 8 * wk.size + 32 * D
+        vb += run * int(wv.sum()) + 8 * wv.size + 32 * n
+    return kb, vb
+
+
+def run_length_study(streams, bits: int, block: int, permute: int, runs=(16, 32, 64)) -> dict:
+    """CR (ideal) of K and V over ``streams`` [(k16, v16), ...] for each run length."""
+    out = {}
+    for r in runs:
+        kb = vb = raw = 0
+        for k16, v16 in streams:
+            a, b = run_length_bits(k16, v16, bits, block, permute, r)
+            kb, vb, raw = kb + a, vb + b, raw + 16 * k16.size
+        out[r] = (raw / kb, raw / vb)
+    return out
+
