@@ -289,8 +289,15 @@ struct RecordOffsets {
     st = a;
     sz = b - a;
   }
-  __device__ __forceinline__ uint64_t start(int i) const { return readlane_u32(st, i); }
-  __device__ __forceinline__ uint32_t size(int i) const { return readlane_u32(sz, i); }
+  // block i (any i: lane i & 63 is read, the caller discards i >= nj): byte
+  // offset o and size, and whether [o, o + size) lies in a region of
+  // `limit` bytes (32-bit arithmetic, exact)
+  __device__ __forceinline__ void at(int i, uint32_t limit, uint64_t& o, uint32_t& size, bool& fits) const {
+    const uint32_t so = readlane_u32(st, i & 63);
+    size = readlane_u32(sz, i & 63);
+    o = so;
+    fits = so <= limit && size <= limit - so;
+  }
 };
 
 // The same window read from a paged cache's block table: entry j holds the
@@ -303,8 +310,15 @@ struct RecordTable {
     st = e.x;
     sz = e.y;
   }
-  __device__ __forceinline__ uint64_t start(int i) const { return (uint64_t)readlane_u32(st, i) << 4; }
-  __device__ __forceinline__ uint32_t size(int i) const { return readlane_u32(sz, i); }
+  // as RecordOffsets::at, with `limit` the pool's size in 16-byte units; a
+  // size that is not a multiple of 16 may reach 15 bytes past that, into
+  // the pool's slack
+  __device__ __forceinline__ void at(int i, uint32_t limit, uint64_t& o, uint32_t& size, bool& fits) const {
+    const uint32_t s16 = readlane_u32(st, i & 63);
+    size = readlane_u32(sz, i & 63);
+    o = (uint64_t)s16 << 4;
+    fits = s16 <= limit && (size >> 4) <= limit - s16;
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -568,21 +582,26 @@ struct VBlock {
 template <int NCH, int REC, class Loc = RecordOffsets>
 struct RecordStream {
   const uint8_t* arena;
-  uint64_t stride;
+  uint32_t limit;        // the region's bytes (RecordOffsets) or the pool's 16-byte units (RecordTable)
   Loc offs;
   int nj, lane;
-  __device__ __forceinline__ void request(int jj, u32x4 (&pre)[NCH]) const {
-    const bool in = jj < nj;
-    const uint64_t o = in ? offs.start(jj) : 0u;
-    const uint32_t size = in ? offs.size(jj) : 0u;
-    load_record<NCH>(arena + o, record_ok(o, size, stride, REC) ? size : 0u, lane, pre);
+  // block jj's record: present (jj < nj), in range and of a sane size
+  __device__ __forceinline__ bool locate(int jj, uint64_t& o, uint32_t& size) const {
+    bool fits;
+    offs.at(jj, limit, o, size, fits);
+    return jj < nj && fits && size >= 16u && size <= (uint32_t)REC;
   }
-  // size of block jj's record, 0 if jj is missing; rok: in range and sane
+  __device__ __forceinline__ void request(int jj, u32x4 (&pre)[NCH]) const {
+    uint64_t o;
+    uint32_t size;
+    const bool ok = locate(jj, o, size);
+    load_record<NCH>(arena + o, ok ? size : 0u, lane, pre);
+  }
+  // size of block jj's record, 0 if jj is missing; rok: present, in range and sane
   __device__ __forceinline__ uint32_t size_of(int jj, bool& rok) const {
-    const bool in = jj < nj;
-    const uint64_t o = in ? offs.start(jj) : 0u;
-    const uint32_t size = in ? offs.size(jj) : 0u;
-    rok = record_ok(o, size, stride, REC);
+    uint64_t o;
+    uint32_t size;
+    rok = locate(jj, o, size);
     return rok ? size : 0u;
   }
 };
@@ -603,8 +622,10 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
   const int nj = max(0, min(a.nb, j0 + a.blocks_per_wg) - j0);
   RecordStream<NCH, REC> rs;
   rs.arena = a.arena + (uint64_t)s * a.arena_stride;
-  rs.stride = a.arena_stride;
+  rs.limit = (uint32_t)a.arena_stride;
   rs.offs.load(a.off + (int64_t)s * a.off_stride, j0, nj, lane);
+  // tokens from the window's first block on (at most nj * B)
+  const int rem = (int)max((int64_t)0, imin64(a.n_tokens - (int64_t)j0 * B, (int64_t)nj * B));
   rs.nj = nj;
   rs.lane = lane;
   KB kb;
@@ -618,7 +639,7 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
       bool rok;
       const uint32_t size = rs.size_of(jj, rok);
       corrupt |= jj < nj && !rok;
-      const int n = jj < nj ? (int)imin64(B, a.n_tokens - (int64_t)j * B) : 0;
+      const int n = jj < nj ? min(B, rem - jj * B) : 0;
       wave_sync();
       store_record<NCH>(rec, pre, lane);
       rs.request(jj + 1, pre);
@@ -691,8 +712,10 @@ void k_pv_gemv(GemvArgs a) {
   const int nj = max(0, min(a.nb, j0 + a.blocks_per_wg) - j0);
   RecordStream<NCH, REC> rs;
   rs.arena = a.arena + (uint64_t)s * a.arena_stride;
-  rs.stride = a.arena_stride;
+  rs.limit = (uint32_t)a.arena_stride;
   rs.offs.load(a.off + (int64_t)s * a.off_stride, j0, nj, lane);
+  // tokens from the window's first block on (at most nj * B)
+  const int rem = (int)max((int64_t)0, imin64(a.n_tokens - (int64_t)j0 * B, (int64_t)nj * B));
   rs.nj = nj;
   rs.lane = lane;
   VB vb;
@@ -708,8 +731,8 @@ void k_pv_gemv(GemvArgs a) {
     // the valid slots, for absent queries and missing blocks
     auto load_p = [&](int jj, float (&pv)[GT][NH]) __attribute__((always_inline)) {
       const bool in = jj < nj;
-      const int64_t left = a.n_tokens - (int64_t)(j0 + jj) * B;
-      const uint32_t nbytes = in && left > 0 ? 4u * (uint32_t)imin64(B, left) : 0u;
+      const int left = rem - jj * B;
+      const uint32_t nbytes = in && left > 0 ? 4u * (uint32_t)min(B, left) : 0u;
 #pragma unroll
       for (int g = 0; g < GT; ++g) {
         const bool gok = gq0 + g < a.G;
@@ -729,7 +752,7 @@ void k_pv_gemv(GemvArgs a) {
       bool rok;
       const uint32_t size = rs.size_of(jj, rok);
       corrupt |= jj < nj && !rok;
-      const int n = jj < nj ? (int)imin64(B, a.n_tokens - (int64_t)j * B) : 0;
+      const int n = jj < nj ? min(B, rem - jj * B) : 0;
       wave_sync();
       store_record<NCH>(rec, pre, lane);
       float pw[GT][NH];
@@ -856,6 +879,9 @@ void k_attn_decode(AttnArgs a) {
     corrupt = true;
   }
   using Loc = std::conditional_t<PAGED, RecordTable, RecordOffsets>;
+  const uint32_t limit = (uint32_t)(PAGED ? a.arena_stride >> 4 : a.arena_stride);
+  // tokens from the window's first block on (at most nj * B)
+  const int rem = (int)max((int64_t)0, imin64(n_tokens - (int64_t)j0 * B, (int64_t)nj * B));
   const float NEG_INF = -__builtin_huge_valf();
 
   // Both waves pass the same barriers: one per block and one per query group.
@@ -871,7 +897,7 @@ void k_attn_decode(AttnArgs a) {
         ks.arena = cache.k_arena + (uint64_t)s * a.arena_stride;
         ks.offs.load(cache.k_off + (int64_t)s * a.off_stride, j0, nj, lane);
       }
-      ks.stride = a.arena_stride;
+      ks.limit = limit;
       ks.nj = nj;
       ks.lane = lane;
       KB kb;
@@ -880,7 +906,7 @@ void k_attn_decode(AttnArgs a) {
       u32x4 pre[NCH_K];
       ks.request(0, pre);
       for (int jj = 0; jj < nj; ++jj) {
-        const int n = (int)imin64(B, n_tokens - (int64_t)(j0 + jj) * B);
+        const int n = min(B, rem - jj * B);
         bool rok;
         const uint32_t size = ks.size_of(jj, rok);
         corrupt |= !rok;
@@ -908,7 +934,7 @@ void k_attn_decode(AttnArgs a) {
         vs.arena = cache.v_arena + (uint64_t)s * a.arena_stride;
         vs.offs.load(cache.v_off + (int64_t)s * a.off_stride, j0, nj, lane);
       }
-      vs.stride = a.arena_stride;
+      vs.limit = limit;
       vs.nj = nj;
       vs.lane = lane;
       VB vb;
@@ -919,7 +945,7 @@ void k_attn_decode(AttnArgs a) {
       u32x4 pre[NCH_V];
       vs.request(0, pre);
       for (int jj = 0; jj < nj; ++jj) {
-        const int n = (int)imin64(B, n_tokens - (int64_t)(j0 + jj) * B);
+        const int n = min(B, rem - jj * B);
         __syncthreads();                            // block jj's scores are in the ring
         // weights exp(s - m); earlier sums rescaled when m grows
         float w[GT][NH];
