@@ -176,7 +176,13 @@ struct BlockDecoder {
     const int nruns = nr * kD;
     uint32_t h[NRL];
 #pragma unroll
-    for (int k = 0; k < NRL; ++k) h[k] = (k >> 1) < nr ? rec[HDR + lane + 64 * k] : 0u;
+    for (int k = 0; k < NRL; ++k) {
+      // read unconditionally (the staging always holds a full-size header)
+      // and select, instead of a branch around each read
+      uint32_t hv = rec[HDR + lane + 64 * k];
+      asm volatile("" : "+v"(hv));
+      h[k] = (k >> 1) < nr ? hv : 0u;
+    }
     bool all_full = false;
     if (nr == NR) {
       bool ok = true;
@@ -515,7 +521,9 @@ struct VBlock {
         for (int h = 1; h < NH; ++h) mx = fmaxf(mx, pp[g][h]);
         const float M = wave_max_nonneg(mx);
         live[g] = M > 0.f;
-        E[g] = live[g] ? 19 - ilogbf(M) : 0;          // M * 2^E in [2^19, 2^20)
+        // M * 2^E in [2^19, 2^20): M = f * 2^e with f in [0.5, 1), so
+        // ilogb(M) = e - 1
+        E[g] = live[g] ? 20 - __builtin_amdgcn_frexp_expf(M) : 0;
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
           const uint32_t P = min((uint32_t)(ldexpf(pp[g][h], E[g]) + 0.5f), 0xFFFFFu);
