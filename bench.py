@@ -162,7 +162,7 @@ def summarize_profile(pdir: str, workload: str) -> None:
             return None
         return int(c["FETCH_SIZE"] * 1024 * f_fetch + c["WRITE_SIZE"] * 1024 * f_write)
 
-    gemvs = {"attn": next((k for k in stats if k.startswith("k_attn_decode")), None),
+    gemvs = {"attn": next((k for k in stats if k.startswith("k_attn_decode") and "true" not in k), None),
              "qk": next((k for k in stats if k.startswith("k_qk_gemv")), None),
              "pv": next((k for k in stats if k.startswith("k_pv_gemv")), None)}
     if not bench_line:
