@@ -532,6 +532,27 @@ def main():
                              "stream lengths spread linearly from T to T/4")
         del paged
 
+    # the box's streaming-read ceiling, measured like the fused launch: the
+    # library's read probe over as many bytes as one launch reads, averaged
+    # over back-to-back launches
+    from decode_gemv_amd import stream_read
+    rbytes = (int(attn_alg) + 255) // 256 * 256
+    rbuf = torch.ones(rbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    for _ in range(5):
+        stream_read(rbuf, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        stream_read(rbuf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    read_ceiling = rbytes / (e0.elapsed_time(e1) / 20 * 1e-3) / 1e9
+    del rbuf
+    roofline["read_ceiling_GBps"] = round(read_ceiling, 1)
+    roofline["frac_of_read_ceiling"] = round(attn_gbps / read_ceiling, 4)
+    log(f"streaming-read ceiling {read_ceiling:.0f} GB/s")
+
     # a plain device copy of known size, for counter calibration runs
     if args.copy_probe_mib > 0:
         a = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)

@@ -76,6 +76,7 @@ _SIGS = {
     "packkv_softmax_rows": (c_int32, [c_void_p, c_void_p, c_int32, c_int64, c_int64, ctypes.c_float,
                                       c_void_p]),
     "packkv_check": (c_int32, [ctypes.POINTER(CacheT), c_void_p]),
+    "packkv_stream_read": (c_int32, [c_void_p, c_uint64, c_void_p, c_void_p]),
     "packkv_stats": (c_int32, [ctypes.POINTER(CacheT), c_void_p, c_void_p]),
     "packkv_status_str": (ctypes.c_char_p, [c_int32]),
     "packkv_paged_sizes": (c_int32, [ctypes.POINTER(Config), c_int32, c_int64, c_int32, c_uint64,

@@ -187,6 +187,16 @@ class PackedKVCache:
                 "k_words": o[12], "v_words": o[13], "k_runs": o[14], "v_runs": o[15]}
 
 
+def stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """The streaming-read ceiling probe: read a 16-byte-aligned device buffer
+    once; sink (int32 [4096], on the device) receives the XOR of each
+    workgroup's words, so folding a zero-filled sink gives the buffer's XOR."""
+    if sink.dtype != torch.int32 or sink.numel() < 4096 or not sink.is_contiguous():
+        raise ValueError("sink must be a contiguous int32 tensor of at least 4096 words")
+    nbytes = buf.numel() * buf.element_size()
+    _lib.check(_lib.load().packkv_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream()), "packkv_stream_read")
+
+
 def attention_multi_workspace(caches, group: int) -> torch.Tensor:
     """A zero-filled workspace for attention_multi over `caches` (reusable)."""
     need = int(_lib.load().packkv_attention_multi_workspace_bytes(ctypes.byref(caches[0]._c), group, len(caches)))

@@ -364,6 +364,11 @@ int packkv_softmax_rows(const float* scores, float* p, int32_t rows, int64_t T, 
   return hip_status(launch_softmax(scores, p, rows, T, ld, scale, (hipStream_t)stream));
 }
 
+int packkv_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || bytes < 16 || bytes % 16 || ((uintptr_t)buf & 15u)) return PACKKV_EINVAL;
+  return hip_status(launch_stream_read(buf, bytes, sink, (hipStream_t)stream));
+}
+
 int packkv_check(const packkv_cache_t* c, void* stream) {
   if (!c || !c->status) return PACKKV_EINVAL;
   hipStream_t st = (hipStream_t)stream;

@@ -1338,6 +1338,44 @@ hipError_t launch_stats(const GemvArgs& a, int B, bool is_v, int n_streams, unsi
   return hipGetLastError();
 }
 
+// Streaming-read ceiling (a measurement helper, not part of the method):
+// a grid-stride read of the buffer, 16 bytes per thread and step in
+// 1024-thread workgroups (the steadiest of the shapes measured on 1.24 GB:
+// 7.1 TB/s at every grid from 1024 to 16384 workgroups, where contiguous
+// shares per workgroup and deeper unrolling ranged 5.7-7.3 TB/s).  Each
+// workgroup folds its words with XOR, so the loads cannot be dropped, and
+// stores the result to sink[w].  No atomics: thousands of them on one word
+// would serialise at the end of the launch and time themselves instead of
+// the reads.
+constexpr int kReadGroups = 4096;
+__global__ __launch_bounds__(1024) void k_stream_read(const u32x4* buf, uint64_t n16, uint32_t* sink) {
+  __shared__ uint32_t part[16];
+  const uint64_t stride = (uint64_t)gridDim.x * 1024;
+  uint32_t x = 0;
+  for (uint64_t i = (uint64_t)blockIdx.x * 1024 + threadIdx.x; i < n16; i += stride) {
+    const u32x4 a = __builtin_nontemporal_load(&buf[i]);
+    x ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+  }
+  for (int o = 32; o > 0; o >>= 1) x ^= (uint32_t)__shfl_xor((int)x, o, kWave);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t y = 0;
+    for (int k = 0; k < 16; ++k) y ^= part[k];
+    sink[blockIdx.x] = y;
+  }
+}
+
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t st) {
+  const uint64_t n16 = bytes / 16;
+  uint64_t blocks = (n16 + 1023) / 1024;
+  if (blocks > kReadGroups) blocks = kReadGroups;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_stream_read, dim3((unsigned)blocks), dim3(1024), 0, st, reinterpret_cast<const u32x4*>(buf),
+                     n16, sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_softmax(const float* scores, float* p, int rows, int64_t T, int64_t ld, float scale,
                           hipStream_t st) {
   hipLaunchKernelGGL(k_softmax, dim3(rows), dim3(1024), 0, st, scores, p, T, ld, scale);

@@ -142,5 +142,6 @@ hipError_t launch_stats(const GemvArgs& a, int B, bool is_v, int n_streams, unsi
                         hipStream_t st);
 hipError_t launch_softmax(const float* scores, float* p, int rows, int64_t T, int64_t ld, float scale,
                           hipStream_t st);
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t st);
 
 }  // namespace packkv

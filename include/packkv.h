@@ -260,6 +260,20 @@ int packkv_softmax_rows(const float* scores, float* p, int32_t rows, int64_t T,
 int packkv_check(const packkv_cache_t* cache, void* stream);
 
 /*
+ * packkv_stream_read - a measurement helper, not a step of the method: reads
+ * every 16-byte chunk of the device buffer buf[0 .. bytes) once (grid-stride
+ * over up to 4096 workgroups of 1024 threads) and stores the XOR of the
+ * 32-bit words workgroup w read to the device
+ * word sink[w] (sink holds 4096 words; the words of workgroups the launch
+ * does not use are left untouched, so the XOR of a zero-filled sink is the
+ * XOR of the whole buffer).  Timed over as many bytes as a decode launch
+ * reads, it is the streaming-read ceiling of the box that the kernels'
+ * bandwidth is compared with.  EINVAL if buf or sink is null, buf is not
+ * 16-byte aligned, or bytes is not a positive multiple of 16.
+ */
+int packkv_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* stream);
+
+/*
  * packkv_stats - width histogram and byte counts of the cache, into device
  * memory out[32] (uint64): out[0..4] K runs with w = 0..4, out[5..9] the
  * same for V, out[10] K record bytes, out[11] V record bytes, out[12] K

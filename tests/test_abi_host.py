@@ -192,3 +192,12 @@ def test_paged_calls_check_before_any_launch(lib):
     p.page_bytes = s.min_page_bytes
     p.host_lengths = None
     assert lib.packkv_paged_release(P, 0, None) == _lib.EINVAL
+
+
+def test_stream_read_checks_its_arguments(lib):
+    fake = 4096
+    assert lib.packkv_stream_read(None, 64, fake, None) == _lib.EINVAL
+    assert lib.packkv_stream_read(fake, 64, None, None) == _lib.EINVAL
+    assert lib.packkv_stream_read(fake + 8, 64, fake, None) == _lib.EINVAL     # not 16-byte aligned
+    assert lib.packkv_stream_read(fake, 60, fake, None) == _lib.EINVAL         # not a multiple of 16
+    assert lib.packkv_stream_read(fake, 0, fake, None) == _lib.EINVAL

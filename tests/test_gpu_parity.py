@@ -302,3 +302,18 @@ def test_multi_cache_attention_matches_single_calls(torch_dev, bits, block, G, L
         kh, vh, _, _ = ostream.decode_stream(refs[s])
         ref = attention.pv(attention.softmax(attention.qk(q[0, s], kh), 128), vh)
         assert rel_l2(out[0, s].cpu().numpy(), ref) <= TOL
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 16, 10 * 2**20 + 48, 70 * 2**20])
+def test_stream_read_folds_every_word(torch_dev, nbytes):
+    """The read-ceiling probe reads every word once: its XOR fold equals numpy's."""
+    torch, dev = torch_dev
+    from decode_gemv_amd import stream_read
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 2**32, nbytes // 4, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).to(dev)
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    say("stream read", nbytes)
+    stream_read(buf, sink)
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert int(got) == int(np.bitwise_xor.reduce(host))
