@@ -60,3 +60,32 @@ def worst_row_rel(y, ref):
     num = np.linalg.norm(y - ref, axis=1)
     den = np.maximum(np.linalg.norm(ref, axis=1), 1e-300)
     return float((num / den).max())
+
+
+def check_placement(c):
+    """Every record of a closed block lies inside one page; a page belongs to
+    one stream and holds only K or only V records; open blocks sit in their
+    stream's tail slots; nothing overlaps; the free count is what the streams
+    do not hold."""
+    (ks, kz), (vs, vz) = c.tables()
+    slot, page = int(c.sizes.slot_bytes), c.page_bytes
+    tail0 = c.n_pages * page
+    spans, owner = [], {}
+    for s, n in enumerate(c.lengths):
+        nfull, nb = n // c.block, -(-n // c.block)
+        for j in range(nb):
+            for st, sz, which in ((ks[s, j], kz[s, j], 0), (vs[s, j], vz[s, j], 1)):
+                assert sz >= 16 and sz % 16 == 0
+                if j < nfull:
+                    p = st // page
+                    assert p < c.n_pages and (st + sz - 1) // page == p, f"record straddles a page, stream {s}"
+                    assert owner.setdefault(p, (s, which)) == (s, which), f"page {p} shared"
+                else:
+                    assert st == tail0 + (2 * s + which) * slot, f"open block not in its tail slot, stream {s}"
+                    assert sz <= slot
+                spans.append((st, st + sz))
+    spans.sort()
+    for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+        assert a1 <= b0, "records overlap"
+    assert c.free_pages() == c.n_pages - len(owner)
+    return owner

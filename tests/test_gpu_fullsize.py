@@ -184,3 +184,78 @@ def test_fullsize_streaming_append(torch_dev):
         assert c.check() == 0
         assert rel_l2(fused[s], attention.pv(attention.softmax(ref_sc, D), vh)) <= TOL
         assert rel_l2(fused, out) <= TOL
+
+
+def test_fullsize_paged_ragged(torch_dev):
+    """The paged cache at the llama7b-32k shape with stream lengths spread from
+    T down to T/4 (64 KiB pages, as bench.py times it): placement holds on
+    every stream, one random closed block of every stream equals the oracle's
+    encoding of that block alone, and the shortest stream is checked
+    completely (records, permutation, tail, fused attention)."""
+    torch, dev = torch_dev
+    from decode_gemv_amd import PagedKVCache
+    from gpu_common import check_placement
+    w = kvsynth.WORKLOADS["llama7b-32k"]
+    S, T, D, B = w.streams, w.tokens, w.head_dim, w.block
+    cfg = oracle.Config(bits=w.bits, block=B)
+    lens = [T - (3 * T // 4) * s // S for s in range(S)]
+    say("fullsize paged ragged", S, T)
+    K, V = host_streams(w, T)
+    n_pages = sum(-(-L * 160 // 65536) + 3 for L in lens) + 16     # 148 B of records per token
+    pc = PagedKVCache(S, T + 8, n_pages, page_bytes=65536, bits=w.bits, block=B, device=str(dev))
+    Kd, Vd = torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev)
+    for s, L in enumerate(lens):
+        pc.prefill(s, Kd[s:s + 1, :L].contiguous(), Vd[s:s + 1, :L].contiguous())
+    del Kd, Vd
+    assert pc.check() == 0 and pc.lengths == lens
+    check_placement(pc)
+    say("fullsize paged sampled blocks")
+    pool = pc.pool.cpu().numpy()
+    (ks, kz), (vs, vz) = pc.tables()
+    rng = np.random.default_rng(11)
+    for s, L in enumerate(lens):
+        j = int(rng.integers(L // B))
+        code = ostream.encode_block(K[s, j * B:(j + 1) * B], V[s, j * B:(j + 1) * B], cfg)
+        assert pool[ks[s, j]:ks[s, j] + kz[s, j]].tobytes() == code.k_record, f"K record ({s}, {j})"
+        assert pool[vs[s, j]:vs[s, j] + vz[s, j]].tobytes() == code.v_record, f"V record ({s}, {j})"
+    s = S - 1
+    say("fullsize paged oracle stream", s, lens[s])
+    ref = ostream.compress(K[s, :lens[s]], V[s, :lens[s]], cfg)
+    ko, vo = ref.offsets("K"), ref.offsets("V")
+    ka, va = ref.arena("K"), ref.arena("V")
+    for j in range(len(ko) - 1):
+        assert pool[ks[s, j]:ks[s, j] + kz[s, j]].tobytes() == ka[ko[j]:ko[j + 1]], f"K record {j}"
+        assert pool[vs[s, j]:vs[s, j] + vz[s, j]].tobytes() == va[vo[j]:vo[j + 1]], f"V record {j}"
+    nb = len(ko) - 1
+    assert np.array_equal(pc.perm_table()[s, :nb].cpu().numpy(), ref.perm_table())
+    q = np.stack([kvsynth.stream_q(w, i) for i in range(S)])
+    fused = pc.attention(torch.from_numpy(q).to(dev)).cpu().numpy()
+    assert pc.check() == 0
+    assert np.all(np.isfinite(fused))
+    kh, vh, _, _ = ostream.decode_stream(ref)
+    want = attention.pv(attention.softmax(attention.qk(q[s], kh), D), vh)
+    assert rel_l2(fused[s], want) <= TOL, rel_l2(fused[s], want)
+
+
+def test_fullsize_paged_equals_contiguous(torch_dev):
+    """Every stream at T tokens in both layouts at the llama7b-32k shape: fused
+    attention through the block tables equals the contiguous cache's bit for
+    bit on all 256 streams."""
+    torch, dev = torch_dev
+    from decode_gemv_amd import PackedKVCache, PagedKVCache
+    w = kvsynth.WORKLOADS["llama7b-32k"]
+    S, T = w.streams, w.tokens
+    say("fullsize paged vs contiguous", S, T)
+    K, V = host_streams(w, T)
+    Kd, Vd = torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev)
+    c = PackedKVCache(S, T + 8, bits=w.bits, block=w.block, device=str(dev))
+    c.compress(Kd, Vd)
+    pc = PagedKVCache(S, T + 8, S * (-(-T * 160 // 65536) + 3) + 16, page_bytes=65536, bits=w.bits,
+                      block=w.block, device=str(dev))
+    pc.prefill(0, Kd, Vd)
+    del Kd, Vd
+    assert c.check() == 0 and pc.check() == 0
+    q = torch.from_numpy(np.stack([kvsynth.stream_q(w, i) for i in range(S)])).to(dev)
+    x, y = c.attention(q), pc.attention(q)
+    assert c.check() == 0 and pc.check() == 0
+    assert torch.equal(x, y)
