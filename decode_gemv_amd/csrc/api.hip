@@ -70,7 +70,7 @@ int gemv_blocks_per_wg(int64_t n_streams, int nb, bool split_merge, int group) {
   int64_t j;
   if (!split_merge && env_qk > 0) j = env_qk;
   else if (env_all > 0) j = env_all;
-  else if (!split_merge) j = 4;
+  else if (!split_merge) j = 2;
   else {
     j = (n_streams * (int64_t)nb + 7679) / 7680;
     j += j & 1;
