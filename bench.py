@@ -134,6 +134,15 @@ def summarize_profile(pdir: str, workload: str) -> None:
         for r in csv.DictReader(f):
             stats[short(r["Name"])] = (int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
                                        float(r["MaxNs"]) / 1e3)
+    # median duration per kernel from the per-dispatch trace: unlike the mean
+    # it is not pulled up by the launches made while the clock still ramps
+    durs = {}
+    trace = os.path.join(pdir, "kt", "run_kernel_trace.csv")
+    if os.path.exists(trace):
+        for r in csv.DictReader(open(trace)):
+            durs.setdefault(short(r["Kernel_Name"]), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    med = {k: float(np.median(v)) for k, v in durs.items()}
     bench_line = None
     for line in open(os.path.join(pdir, "kt.log")):
         if line.startswith("{") and '"metric"' in line:
@@ -192,9 +201,10 @@ def summarize_profile(pdir: str, workload: str) -> None:
              "SQ_INSTS_VALU_FMA_F32 SQ_INSTS_VALU_INT32.", "",
              f"Kernel source hash: `{entry['kernel_source']}`", "",
              "## Kernel durations (rocprofv3 --stats)", "",
-             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+             "| kernel | calls | avg us | median us | min us | max us |", "|---|---|---|---|---|---|"]
     for k, (n, avg, mn, mx) in sorted(stats.items(), key=lambda x: -x[1][0] * x[1][1]):
-        lines.append(f"| {k} | {n} | {avg:.1f} | {mn:.1f} | {mx:.1f} |")
+        m = f"{med[k]:.1f}" if k in med else "-"
+        lines.append(f"| {k} | {n} | {avg:.1f} | {m} | {mn:.1f} | {mx:.1f} |")
     lines += ["", "## HBM traffic per launch", "",
               f"1 GiB device copy: FETCH_SIZE {copy.get('FETCH_SIZE', 0):.0f} KiB, WRITE_SIZE "
               f"{copy.get('WRITE_SIZE', 0):.0f} KiB, so fetch factor {f_fetch and round(f_fetch, 4)}, "
