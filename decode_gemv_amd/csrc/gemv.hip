@@ -31,6 +31,7 @@ namespace packkv {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 // LDS ordering inside one wave: wait for the wave's LDS accesses and keep
 // the compiler from moving memory operations across.  Unlike __syncthreads
@@ -353,13 +354,14 @@ struct KBlock {
   static constexpr int HALF_BYTES = 8 * ROWW * 4;
   static_assert(RED_BYTES <= HALF_BYTES, "reduction must fit a half's plane rows");
   static constexpr int SCRATCH_BYTES = PLANE_BYTES;
+  static constexpr int QS_BYTES = GT * kD * 4;
 
   float* qs;                                          // [GT][D] q' of the block
   int lane, g8, cg;
   float qau[GT], qbu[GT];                             // queries / unit at channels lane, lane + 64
 
-  __device__ __forceinline__ void init(float* qs_, int lane_) {
-    qs = qs_;
+  __device__ __forceinline__ void init(uint8_t* qs_, int lane_) {
+    qs = reinterpret_cast<float*>(qs_);
     lane = lane_;
     g8 = lane & 7;
     cg = lane >> 3;
@@ -455,6 +457,207 @@ struct KBlock {
     return ok;
   }
 };
+
+// ---------------------------------------------------------------------------
+// K side on the matrix cores, one staged block.
+//
+//   scores[g][t] = beta_g + sum_c q'_g[c] u[t][c],   q' = q * scale (per channel)
+//
+// The channel sum is a (queries x channels) by (channels x tokens) product,
+// and v_mfma_i32_16x16x64_i8 takes 16 tokens x 64 channels of it at a time,
+// which moves the multiply-adds off the vector ALU.  Per block and query, q'
+// is written in fixed point, Q = rint(q' 2^E) with |Q| < 2^24 (E from the
+// block's largest |q'|), and split into four 7-bit digits, the last one
+// signed, so every product and sum is an exact integer; row 4g + d of the
+// operand is digit d of query g.  The ints come from the LDS plane [slot
+// group][channel] of 4-bit containers: each lane transposes 8 x 8 nibble
+// tiles (8 channels x 8 slots; a 16-bit, an 8-bit and a 4-bit exchange stage,
+// with v_perm and v_bfi) into a token-major plane [slot][channel / 8], from
+// which an MFMA lane reads 16 channels of one token and spreads the nibbles to
+// bytes: even nibbles first, then odd.  The digit rows store the channels in
+// that same order (opos), since A and B of the MFMA pair byte b of lane l with
+// the same k.  Each lane (g, token) adds up its query's four digit sums,
+// scales by 2^-E and adds beta.
+template <int B, int BITS, int GT>
+struct KBlockM {
+  using Dec = BlockDecoder<B, BITS, false>;
+  static constexpr int NRL = Dec::NRL;
+  static constexpr int NH = B / 64;
+  static constexpr int NT = B / 16;                   // token tiles of the MFMA
+  static constexpr int ROWW = kD + 8;                 // plane row pitch (words)
+  static constexpr int PLANE_BYTES = (B / 8) * ROWW * 4;
+  static constexpr int TP = 18;                       // token-major pitch: 16 octets + 2 (no bank conflicts)
+  static constexpr int TPLANE_BYTES = B * TP * 4;
+  static constexpr int SCRATCH_BYTES = PLANE_BYTES > TPLANE_BYTES ? PLANE_BYTES : TPLANE_BYTES;
+  static constexpr int QS_BYTES = 16 * kD;            // digit rows [16][128]
+  static constexpr int NTILE_LANE = (B / 8) * 16 / 64;   // 8x8 tiles per lane
+  static_assert(GT * B * 4 <= SCRATCH_BYTES, "the scores reuse the scratch");
+  static_assert(4 * GT <= 16, "one operand row per (query, digit)");
+
+  uint8_t* dig;
+  int lane;
+  float qa[GT], qb[GT];                               // queries at channels lane, lane + 64
+
+  __device__ __forceinline__ void init(uint8_t* qs_, int lane_) {
+    dig = qs_;
+    lane = lane_;
+  }
+  __device__ __forceinline__ void set_queries(const uint16_t* q, int64_t s, int G, int gq0) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      const bool ok = gq0 + g < G;
+      const uint16_t* qp = q + (s * G + gq0 + g) * kD;
+      qa[g] = ok ? f16_bits_to_float(qp[lane]) : 0.f;
+      qb[g] = ok ? f16_bits_to_float(qp[lane + 64]) : 0.f;
+    }
+    // the rows past the queries' digits stay zero
+    constexpr int ZW = (16 - 4 * GT) * kD / 16;
+    for (int i = lane; i < ZW; i += 64) reinterpret_cast<u32x4*>(dig + 4 * GT * kD)[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  // byte position of channel c inside a digit row (the operand order)
+  __device__ __forceinline__ static int opos(int c) {
+    const int o = c >> 3, n = c & 7;
+    return 64 * (o >> 3) + 16 * ((o & 7) >> 1) + 8 * (o & 1) + 4 * (n & 1) + (n >> 1);
+  }
+  // in place: W[i] nibble j  ->  W[j] nibble i
+  __device__ __forceinline__ static void transpose8(uint32_t (&W)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {                     // 16-bit halves of words i, i + 4
+      const uint32_t a = W[i], b = W[i + 4];
+      W[i] = __builtin_amdgcn_perm(b, a, 0x05040100u);
+      W[i + 4] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+    }
+#pragma unroll
+    for (int i0 = 0; i0 < 8; i0 += 4)                 // bytes of words i, i + 2
+#pragma unroll
+      for (int i = i0; i < i0 + 2; ++i) {
+        const uint32_t a = W[i], b = W[i + 2];
+        W[i] = __builtin_amdgcn_perm(b, a, 0x06020400u);
+        W[i + 2] = __builtin_amdgcn_perm(b, a, 0x07030501u);
+      }
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {                  // nibbles of words i, i + 1
+      const uint32_t a = W[i], b = W[i + 1];
+      W[i] = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
+      W[i + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+    }
+  }
+
+  // As KBlock::run: rec is overwritten; sink(g, h, score, ok) takes query g's
+  // score of slot h*64 + lane.
+  template <class Sink>
+  __device__ __forceinline__ bool run(uint8_t* rec, uint32_t size, int nr, Sink&& sink) {
+    float beta[GT];
+    int E[GT];
+    {
+      const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec);
+      const float sa = f16_bits_to_float(sc[lane]), sb = f16_bits_to_float(sc[lane + 64]);
+      const float za = f16_bits_to_float(sc[kD + lane]), zb = f16_bits_to_float(sc[kD + lane + 64]);
+      const int pa = opos(lane), pb = opos(lane + 64);
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        beta[g] = wave_sum(fmaf(qa[g], za, qb[g] * zb));
+        const float xa = qa[g] * sa, xb = qb[g] * sb;
+        const float M = wave_max_nonneg(fmaxf(fabsf(xa), fabsf(xb)));
+        E[g] = M > 0.f ? 24 - __builtin_amdgcn_frexp_expf(M) : 0;    // M 2^E in [2^23, 2^24)
+        const int Qa = (int)rintf(ldexpf(xa, E[g])), Qb = (int)rintf(ldexpf(xb, E[g]));
+        uint8_t* row = dig + 4 * g * kD;
+        row[pa] = (uint8_t)(Qa & 127);
+        row[kD + pa] = (uint8_t)((Qa >> 7) & 127);
+        row[2 * kD + pa] = (uint8_t)((Qa >> 14) & 127);
+        row[3 * kD + pa] = (uint8_t)(Qa >> 21);
+        row[pb] = (uint8_t)(Qb & 127);
+        row[kD + pb] = (uint8_t)((Qb >> 7) & 127);
+        row[2 * kD + pb] = (uint8_t)((Qb >> 14) & 127);
+        row[3 * kD + pb] = (uint8_t)(Qb >> 21);
+      }
+    }
+    uint32_t nib[NRL][4];
+    const bool ok = Dec::decode(rec, size, nr, lane, nib);
+    wave_sync();                                  // every lane has read the record
+    uint32_t* plane = reinterpret_cast<uint32_t*>(rec);
+#pragma unroll
+    for (int k = 0; k < NRL; ++k) {
+      const int r = k >> 1, c = lane + 64 * (k & 1);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) plane[(r * 4 + kk) * ROWW + c] = nib[k][kk];
+    }
+    wave_sync();
+    // tiles (slot group, octet): the lane's 8 words of 8 channels, transposed
+    // to 8 words of 8 slots
+    uint32_t T[NTILE_LANE][8];
+#pragma unroll
+    for (int it = 0; it < NTILE_LANE; ++it) {
+      const int tile = it * 64 + lane, sg = tile >> 4, o = tile & 15;
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(&plane[sg * ROWW + 8 * o]);
+      const u32x4 w1 = *reinterpret_cast<const u32x4*>(&plane[sg * ROWW + 8 * o + 4]);
+      uint32_t W[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+      transpose8(W);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) T[it][j] = W[j];
+    }
+    wave_sync();                                  // the plane is read: the token-major plane replaces it
+    uint32_t* tpl = plane;
+#pragma unroll
+    for (int it = 0; it < NTILE_LANE; ++it) {
+      const int tile = it * 64 + lane, sg = tile >> 4, o = tile & 15;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) tpl[(8 * sg + j) * TP + o] = T[it][j];
+    }
+    wave_sync();
+    i32x4 A[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      A[s] = *reinterpret_cast<const i32x4*>(dig + (lane & 15) * kD + 64 * s + 16 * (lane >> 4));
+    i32x4 C[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      C[tt] = i32x4{0, 0, 0, 0};
+      const int t = 16 * tt + (lane & 15);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint2 w = *reinterpret_cast<const uint2*>(&tpl[t * TP + 8 * s + 2 * (lane >> 4)]);
+        const i32x4 Bv = {(int)(w.x & 0x0F0F0F0Fu), (int)((w.x >> 4) & 0x0F0F0F0Fu), (int)(w.y & 0x0F0F0F0Fu),
+                          (int)((w.y >> 4) & 0x0F0F0F0Fu)};
+        C[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[s], Bv, C[tt], 0, 0, 0);
+      }
+    }
+    // lane (g, token): the four digit sums of query g
+    const int g = lane >> 4;
+    float bsel = beta[0];
+    int esel = E[0];
+#pragma unroll
+    for (int k = 1; k < GT; ++k) {
+      bsel = g == k ? beta[k] : bsel;
+      esel = g == k ? E[k] : esel;
+    }
+    wave_sync();                                  // the token-major plane is read
+    float* scs = reinterpret_cast<float*>(rec);
+    if (g < GT) {
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        const float v = fmaf(2097152.f, (float)C[tt][3],
+                             fmaf(16384.f, (float)C[tt][2], fmaf(128.f, (float)C[tt][1], (float)C[tt][0])));
+        scs[g * B + 16 * tt + (lane & 15)] = ldexpf(v, -esel) + bsel;
+      }
+    }
+    wave_sync();
+#pragma unroll
+    for (int gg = 0; gg < GT; ++gg)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) sink(gg, h, scs[gg * B + h * 64 + lane], ok);
+    return ok;
+  }
+};
+
+// The K block code the kernels use: on the matrix cores (KBlockM) for a tile
+// of four queries, with vector FMAs (KBlock) for one.  Measured (A/B in one
+// process): with four queries, 128-token blocks, fused attention 295 -> 264 us
+// and the K GEMV 128 -> 117 us; with one query the matrix version is slower
+// (K GEMV +9-10 %, one wave less occupancy; fused attention +1-3 %), as its
+// transposes and LDS round trips are not repaid by 32 FMAs per packed word.
+template <int B, int BITS, int GT>
+using KSel = std::conditional_t<(GT > 1), KBlockM<B, BITS, GT>, KBlock<B, BITS, GT>>;
 
 // ---------------------------------------------------------------------------
 // V side, one staged block.
@@ -652,12 +855,12 @@ struct RecordStream {
 
 template <int B, int BITS, int GT>
 __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
-  using KB = KBlock<B, BITS, GT>;
+  using KB = KSel<B, BITS, GT>;
   constexpr int REC = max_record_bytes(false, B, 4);
   constexpr int NCH = (REC + 1023) / 1024;
   constexpr int BUF = staging_bytes(REC) > KB::SCRATCH_BYTES ? staging_bytes(REC) : KB::SCRATCH_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t rec[BUF];
-  __shared__ __attribute__((aligned(16))) float qs[GT * kD];
+  __shared__ __attribute__((aligned(16))) uint8_t qs[KB::QS_BYTES];
 
   const int lane = threadIdx.x;
   const int s = blockIdx.x / a.splits;
@@ -883,7 +1086,7 @@ constexpr int attn_waves_per_eu() { return B == 128 ? 3 : B == 64 && BITS == 2 &
 template <int B, int BITS, int GT, bool PAGED>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<B, BITS, GT>())))
 void k_attn_decode(AttnArgs a) {
-  using KB = KBlock<B, BITS, GT>;
+  using KB = KSel<B, BITS, GT>;
   using VB = VBlock<B, BITS, GT, false>;
   constexpr int NH = B / 64;
   constexpr int REC_K = max_record_bytes(false, B, 4);
@@ -893,7 +1096,7 @@ void k_attn_decode(AttnArgs a) {
   constexpr int BUF_K = staging_bytes(REC_K) > KB::SCRATCH_BYTES ? staging_bytes(REC_K) : KB::SCRATCH_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t rec_k[BUF_K];
   __shared__ __attribute__((aligned(16))) uint8_t rec_v[staging_bytes(REC_V)];
-  __shared__ __attribute__((aligned(16))) float qs[GT * kD];
+  __shared__ __attribute__((aligned(16))) uint8_t qs[KB::QS_BYTES];
   __shared__ __attribute__((aligned(16))) uint32_t dig[VB::LDS_WORDS];
   __shared__ __attribute__((aligned(16))) float ring[2][GT][B];   // scores of blocks jj & 1
 
