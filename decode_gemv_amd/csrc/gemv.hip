@@ -340,6 +340,28 @@ struct RecordTable {
 // v_cvt_pk_f32_fp8 (a byte n <= 15 read as e4m3 is exactly n * 2^-9; 2^9 is
 // folded into q'), one FMA per element, and an LDS transpose sums the 8
 // channel groups.  Lane l ends with the scores of slots h*64 + l.
+// v[g] for a lane-dependent g, as a chain of selects.  Each candidate is made
+// opaque first: the compiler otherwise recognises the chain as v[g] and
+// indexes a copy of v in scratch memory.
+template <class T, int N>
+__device__ __forceinline__ T lane_pick(const T (&v)[N], int g) {
+  T r = v[0];
+#pragma unroll
+  for (int k = 1; k < N; ++k) {
+    T c = v[k];
+    asm volatile("" : "+v"(c));
+    r = g == k ? c : r;
+  }
+  return r;
+}
+
+// A split's partial sum goes to the workspace with a relaxed agent-scope
+// store: it lands in the device-coherent level, so the workgroup that merges
+// the splits can read it on any XCD.
+__device__ __forceinline__ void store_partial(float* dst, float v) {
+  __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int B, int BITS, int GT>
 struct KBlock {
   using Dec = BlockDecoder<B, BITS, false>;
@@ -624,13 +646,8 @@ struct KBlockM {
     }
     // lane (g, token): the four digit sums of query g
     const int g = lane >> 4;
-    float bsel = beta[0];
-    int esel = E[0];
-#pragma unroll
-    for (int k = 1; k < GT; ++k) {
-      bsel = g == k ? beta[k] : bsel;
-      esel = g == k ? E[k] : esel;
-    }
+    const float bsel = lane_pick(beta, g);
+    const int esel = lane_pick(E, g);
     wave_sync();                                  // the token-major plane is read
     float* scs = reinterpret_cast<float*>(rec);
     if (g < GT) {
@@ -699,6 +716,27 @@ struct VBlock {
     pst = lds + DIG_WORDS;
     lane = lane_;
     nib_shift = 4 * (lane & 7);
+  }
+
+  // acc[g][0], acc[g][1]: query g at channels lane, lane + 64
+  __device__ __forceinline__ void rescale(float (&acc)[GT][2], const float (&alpha)[GT]) const {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      acc[g][0] *= alpha[g];
+      acc[g][1] *= alpha[g];
+    }
+  }
+  // dst(g): query g's partial sums (nullptr for an absent query)
+  template <class Dst>
+  __device__ __forceinline__ void store(const float (&acc)[GT][2], const float (&z)[GT], Dst&& dst) const {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      float* d = dst(g);
+      if (d) {
+        store_partial(d + lane, acc[g][0] + z[g]);
+        store_partial(d + lane + 64, acc[g][1] + z[g]);
+      }
+    }
   }
 
   // pw[g][h]: weight of slot h*64 + lane (0 past the valid slots).  use:
@@ -816,6 +854,146 @@ struct VBlock {
 };
 
 // ---------------------------------------------------------------------------
+// V side on the matrix cores, one staged block, for a tile of four queries.
+//
+//   out[g][c] = sum_t p_t zero_t + sum_t p'_g[t] u[t][c]
+//
+// The second sum is a (queries x tokens) by (tokens x channels) product, and
+// the payload already packs each channel's tokens together, so no transpose
+// is needed: the decoded container words go to an LDS plane [channel][slot
+// group], and each lane of v_mfma_i32_16x16x64_i8 reads 16 tokens of one
+// channel and spreads the nibbles to bytes (even nibbles first).  The
+// weights are the same 20-bit fixed point as VBlock's (P = round(p' 2^E) per
+// block and query), split into three 7-bit digits; operand row 4g + d holds
+// digit d of query g in the token order of the spread (tpos), row 4g + 3 is
+// zero.  Eight MFMAs cover the 128 channels; lane l then holds query l / 16
+// at channels 16j + l % 16 (acc[j / 2][j % 2]) and adds its three digit sums
+// scaled by 2^-E.
+template <int B, int BITS, int GT>
+struct VBlockM {
+  using Dec = BlockDecoder<B, BITS, true>;
+  static constexpr int NRL = Dec::NRL;
+  static constexpr int NH = B / 64;
+  static constexpr int KS = B / 64;                   // 64-token steps of the MFMA
+  static constexpr int VP = B / 8 + 2;                // plane pitch per channel (words)
+  static constexpr int LDS_WORDS = 16 * B / 4;        // digit rows [16][B] bytes
+  static_assert(GT == 4, "operand rows are (query, digit) for four queries");
+  static_assert(kD * VP * 4 <= staging_bytes(max_record_bytes(true, B, 4)), "the plane reuses the staging");
+
+  uint8_t* dig;
+  int lane;
+
+  __device__ __forceinline__ void init(uint32_t* lds, int lane_) {
+    dig = reinterpret_cast<uint8_t*>(lds);
+    lane = lane_;
+    // the rows 4g + 3 are never written: zero
+#pragma unroll
+    for (int g = 0; g < GT; ++g)
+      for (int i = lane; i < B / 16; i += 64) reinterpret_cast<u32x4*>(dig + (4 * g + 3) * B)[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  // position of token t of the block inside a digit row (the operand order)
+  __device__ __forceinline__ static int tpos(int t) {
+    const int rs = t & 15, n = rs & 7;
+    return 64 * (t >> 6) + 16 * ((t >> 4) & 3) + 8 * (rs >> 3) + 4 * (n & 1) + (n >> 1);
+  }
+  __device__ __forceinline__ void rescale(float (&acc)[GT][2], const float (&alpha)[GT]) const {
+    const float f = lane_pick(alpha, lane >> 4);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j >> 1][j & 1] *= f;
+  }
+  template <class Dst>
+  __device__ __forceinline__ void store(const float (&acc)[GT][2], const float (&z)[GT], Dst&& dst) const {
+    const int g = lane >> 4;
+    const float zg = lane_pick(z, g);
+    float* d = dst(g);
+    if (d) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) store_partial(d + 16 * j + (lane & 15), acc[j >> 1][j & 1] + zg);
+    }
+  }
+
+  // As VBlock::run; rec is overwritten by the plane.
+  __device__ __forceinline__ bool run(uint8_t* rec, uint32_t size, int nr, bool use,
+                                      const float (&pw)[GT][NH], float (&acc)[GT][2], float (&pz)[GT]) {
+    int E[GT];
+    float pzb[GT];
+    {
+      const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec);
+      float pp[GT][NH];
+#pragma unroll
+      for (int g = 0; g < GT; ++g) pzb[g] = 0.f;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const int sl = h * 64 + lane;
+        const float scl = f16_bits_to_float(sc[sl]), zer = f16_bits_to_float(sc[B + sl]);
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+          pp[g][h] = pw[g][h] * scl;
+          pzb[g] = fmaf(pw[g][h], zer, pzb[g]);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        float mx = pp[g][0];
+#pragma unroll
+        for (int h = 1; h < NH; ++h) mx = fmaxf(mx, pp[g][h]);
+        const float M = wave_max_nonneg(mx);
+        E[g] = M > 0.f ? 20 - __builtin_amdgcn_frexp_expf(M) : 0;    // M 2^E in [2^19, 2^20)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          const uint32_t P = min((uint32_t)(ldexpf(pp[g][h], E[g]) + 0.5f), 0xFFFFFu);
+          const int p = tpos(h * 64 + lane);
+          dig[(4 * g) * B + p] = (uint8_t)(P & 127u);
+          dig[(4 * g + 1) * B + p] = (uint8_t)((P >> 7) & 127u);
+          dig[(4 * g + 2) * B + p] = (uint8_t)(P >> 14);
+        }
+      }
+    }
+    uint32_t nib[NRL][4];
+    const bool ok = Dec::decode(rec, size, nr, lane, nib) && use;
+    wave_sync();                                  // every lane has read the record
+    uint32_t* vpl = reinterpret_cast<uint32_t*>(rec);
+#pragma unroll
+    for (int k = 0; k < NRL; ++k) {
+      const int r = k >> 1, c = lane + 64 * (k & 1);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) vpl[c * VP + 4 * r + kk] = nib[k][kk];
+    }
+    wave_sync();
+    i32x4 A[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      A[s] = *reinterpret_cast<const i32x4*>(dig + (lane & 15) * B + 64 * s + 16 * (lane >> 4));
+    const float unit = ldexpf(1.0f, -lane_pick(E, lane >> 4));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      i32x4 C = {0, 0, 0, 0};
+      const int ch = 16 * j + (lane & 15);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const uint2 w = *reinterpret_cast<const uint2*>(&vpl[ch * VP + 8 * s + 2 * (lane >> 4)]);
+        const i32x4 Bv = {(int)(w.x & 0x0F0F0F0Fu), (int)((w.x >> 4) & 0x0F0F0F0Fu), (int)(w.y & 0x0F0F0F0Fu),
+                          (int)((w.y >> 4) & 0x0F0F0F0Fu)};
+        C = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[s], Bv, C, 0, 0, 0);
+      }
+      if (ok) {
+        const float x = fmaf(16384.f, (float)C[2], fmaf(128.f, (float)C[1], (float)C[0]));
+        acc[j >> 1][j & 1] = fmaf(x, unit, acc[j >> 1][j & 1]);
+      }
+    }
+#pragma unroll
+    for (int gg = 0; gg < GT; ++gg)
+      if (ok) pz[gg] += pzb[gg];
+    return ok;
+  }
+};
+
+// The V block code the kernels use: on the matrix cores (VBlockM) for a tile
+// of four queries, with v_dot8 (VBlock) for one.
+template <int B, int BITS, int GT, bool STAGED = true>
+using VSel = std::conditional_t<(GT > 1), VBlockM<B, BITS, GT>, VBlock<B, BITS, GT, STAGED>>;
+
+// ---------------------------------------------------------------------------
 // Streaming skeleton shared by the GEMVs and by each wave of fused
 // attention: a wave walks J consecutive blocks of one stream.  Records are
 // staged into LDS from registers with one record in flight: block jj + 1 is
@@ -919,9 +1097,6 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
 // the counter back to zero for the next call.  No cache write-back or
 // invalidation is needed; a release fence in every workgroup (an L2
 // write-back on this multi-XCD part) made the V GEMV three times slower.
-__device__ __forceinline__ void store_partial(float* dst, float v) {
-  __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ float load_partial(const float* src) {
   return __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -945,7 +1120,7 @@ constexpr int pv_waves_per_eu() { return B == 64 && GT == 1 ? 5 : B == 128 ? 3 :
 template <int B, int BITS, int GT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(pv_waves_per_eu<B, GT>())))
 void k_pv_gemv(GemvArgs a) {
-  using VB = VBlock<B, BITS, GT>;
+  using VB = VSel<B, BITS, GT>;
   constexpr int NH = VB::NH;
   constexpr int REC = max_record_bytes(true, B, 4);
   constexpr int NCH = (REC + 1023) / 1024;
@@ -1019,15 +1194,12 @@ void k_pv_gemv(GemvArgs a) {
     request(0, pre, pv);
     for (int jj = 0; jj < nj; ++jj) process(jj, pre, pv);
     // partial result of this split
+    float z[GT];
 #pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      const float z = wave_sum(pz[g]);
-      if (gq0 + g < a.G) {
-        float* dst = a.ws + (((int64_t)s * a.G + gq0 + g) * a.splits + split) * kD;
-        store_partial(dst + lane, acc[g][0] + z);
-        store_partial(dst + lane + 64, acc[g][1] + z);
-      }
-    }
+    for (int g = 0; g < GT; ++g) z[g] = wave_sum(pz[g]);
+    vb.store(acc, z, [&](int g) -> float* {
+      return gq0 + g < a.G ? a.ws + (((int64_t)s * a.G + gq0 + g) * a.splits + split) * kD : nullptr;
+    });
   }
   if (corrupt && lane == 0) latch(a.status, PACKKV_ECORRUPT);
   if (!last_to_arrive(&a.tickets[s], a.splits, lane)) return;
@@ -1087,7 +1259,7 @@ template <int B, int BITS, int GT, bool PAGED>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<B, BITS, GT>())))
 void k_attn_decode(AttnArgs a) {
   using KB = KSel<B, BITS, GT>;
-  using VB = VBlock<B, BITS, GT, false>;
+  using VB = VSel<B, BITS, GT, false>;
   constexpr int NH = B / 64;
   constexpr int REC_K = max_record_bytes(false, B, 4);
   constexpr int REC_V = max_record_bytes(true, B, 4);
@@ -1195,7 +1367,7 @@ void k_attn_decode(AttnArgs a) {
         const int n = min(B, rem - jj * B);
         __syncthreads();                            // block jj's scores are in the ring
         // weights exp(s - m); earlier sums rescaled when m grows
-        float w[GT][NH];
+        float w[GT][NH], al[GT];
 #pragma unroll
         for (int g = 0; g < GT; ++g) {
           float sc[NH];
@@ -1206,8 +1378,7 @@ void k_attn_decode(AttnArgs a) {
           for (int h = 1; h < NH; ++h) mx = fmaxf(mx, sc[h]);
           const float mn = fmaxf(m[g], wave_max_f(mx));
           const float alpha = mn == NEG_INF ? 1.f : fast_exp2(m[g] - mn);
-          acc[g][0] *= alpha;
-          acc[g][1] *= alpha;
+          al[g] = alpha;
           pz[g] *= alpha;
           l[g] *= alpha;
           m[g] = mn;
@@ -1217,6 +1388,7 @@ void k_attn_decode(AttnArgs a) {
             l[g] += w[g][h];
           }
         }
+        vb.rescale(acc, al);
         bool rok;
         const uint32_t size = vs.size_of(jj, rok);
         corrupt |= !rok;
@@ -1229,20 +1401,20 @@ void k_attn_decode(AttnArgs a) {
         corrupt |= rok && !ok;
       }
       // this split's partial: out sums, max, weight sum
+      float z[GT];
 #pragma unroll
       for (int g = 0; g < GT; ++g) {
-        const float z = wave_sum(pz[g]);
+        z[g] = wave_sum(pz[g]);
         const float lsum = wave_sum(l[g]);
-        if (gq0 + g < a.G) {
+        if (gq0 + g < a.G && lane == 0) {
           float* dst = ws + (((int64_t)s * a.G + gq0 + g) * a.splits + split) * kAttnPartial;
-          store_partial(dst + lane, acc[g][0] + z);
-          store_partial(dst + lane + 64, acc[g][1] + z);
-          if (lane == 0) {
-            store_partial(dst + kD, m[g]);
-            store_partial(dst + kD + 1, lsum);
-          }
+          store_partial(dst + kD, m[g]);
+          store_partial(dst + kD + 1, lsum);
         }
       }
+      vb.store(acc, z, [&](int g) -> float* {
+        return gq0 + g < a.G ? ws + (((int64_t)s * a.G + gq0 + g) * a.splits + split) * kAttnPartial : nullptr;
+      });
       __syncthreads();                              // the ring is reused
     }
   }
