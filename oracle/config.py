@@ -1,9 +1,13 @@
 """Format parameters of the packed cache (oracle side).
 
-Reading adopted (the pages name no sizes): head_dim D = 128, b in {2, 3, 4}
+Reading adopted (the pages name no sizes): head_dim D = 128, b in {2, ..., 8}
 bits, token block B in {64, 128}, pack run R = 32 tokens with R dividing B.
 The run is the unit that gets its own width and offset; the block is the unit
-of quantisation (K), permutation and append.
+of quantisation (K), permutation and append.  A run's header entry holds its
+width w (0..b) and minimum m (0..2^b - 1): one byte (w << 4 | m) up to b = 4,
+two bytes (little-endian w << 8 | m) for b = 5..8, where m no longer fits a
+nibble.  The pages give no header encoding; this one is the plainest that
+holds both fields.
 """
 
 from __future__ import annotations
@@ -20,7 +24,7 @@ class Config:
     permute: int = 1          # 0 identity, 1 greedy grouping, 2 sort key (oracle.perm)
 
     def __post_init__(self):
-        assert self.bits in (2, 3, 4), "b must be 2, 3 or 4"
+        assert 2 <= self.bits <= 8, "b must be 2 .. 8"
         assert self.block in (64, 128), "B must be 64 or 128"
         assert self.run == 32, "R must be 32"
         assert self.block % self.run == 0
@@ -31,6 +35,11 @@ class Config:
     def levels(self) -> int:
         """L = 2^b - 1, the largest quantised value."""
         return (1 << self.bits) - 1
+
+    @property
+    def header_bytes(self) -> int:
+        """Bytes of one (run, channel) header entry: 1 up to b = 4, else 2."""
+        return 1 if self.bits <= 4 else 2
 
     def runs(self, n: int) -> int:
         """Number of runs in a block holding n tokens: ceil(n / R)."""

@@ -6,6 +6,7 @@ the compression ratio CR = fp16 bytes / compressed bytes, three ways, plus
 the same ratio for plain b-bit quantisation with the same fp16 parameters:
 
 * ideal    - payload bits (each run at R * w) + 8 header bits per run
+             (16 for b > 4, where an entry takes two bytes)
              + parameter bits (K: 32 per channel per block; V: 32 per token);
 * physical - the record bytes as stored, 16-byte padding included;
 * full     - physical plus the one-byte-per-token permutation table.
@@ -34,9 +35,9 @@ def ratios(cache: StreamCache, which: str) -> dict:
     off = cache.offsets(which)
     for j in range(len(cache.blocks)):
         n = cache.block_tokens(j)
-        d = decode_record(which, arena[off[j]:off[j + 1]], n, D, cfg.block, R)
+        d = decode_record(which, arena[off[j]:off[j + 1]], n, D, cfg.block, R, cfg.header_bytes)
         par = 32 * D if which == "K" else 32 * n
-        ideal += R * int(d.w.sum()) + 8 * d.w.size + par
+        ideal += R * int(d.w.sum()) + 8 * cfg.header_bytes * d.w.size + par
         params += par
     phys = 8 * len(arena)
     full = phys + 8 * cache.n_tokens
@@ -52,10 +53,12 @@ def ratios(cache: StreamCache, which: str) -> dict:
 
 
 def closed_form_full_width(which: str, bits: int, block: int, run: int, D: int) -> float:
-    """CR when every run needs the full b bits: 16 / (b + 8/R + 32/B) for K,
-    16 / (b + 8/R + 32/D) for V (per-value bit cost of payload, header, params)."""
+    """CR when every run needs the full b bits: 16 / (b + 8h/R + 32/B) for K,
+    16 / (b + 8h/R + 32/D) for V (per-value bit cost of payload, header,
+    params; h = 1 header byte per run up to b = 4, 2 above)."""
     per = block if which == "K" else D
-    return 16.0 / (bits + 8.0 / run + 32.0 / per)
+    h = 1 if bits <= 4 else 2
+    return 16.0 / (bits + 8.0 * h / run + 32.0 / per)
 
 
 def run_length_bits(k16: np.ndarray, v16: np.ndarray, bits: int, block: int, permute: int, run: int):
@@ -66,7 +69,7 @@ def run_length_bits(k16: np.ndarray, v16: np.ndarray, bits: int, block: int, per
     Every block is quantised as the format does, ordered by the permutation
     rule with groups of ``run`` tokens (and its identity fallback judged at
     that run length), and counted like ``ratios``' ideal figure: ``run * w``
-    payload bits and 8 header bits per (run, channel), plus the parameters
+    payload bits and 8 (b > 4: 16) header bits per (run, channel), plus the parameters
     (K: 32 bits per channel per block, V: 32 per token).
     """
     n_tok, D = k16.shape
@@ -79,8 +82,9 @@ def run_length_bits(k16: np.ndarray, v16: np.ndarray, bits: int, block: int, per
         perm = block_permutation(qk, qv, run, permute)
         wk, _ = run_widths(qk[perm], run)
         wv, _ = run_widths(qv[perm], run)
-        kb += run * int(wk.sum()) + 8 * wk.size + 32 * D
-        vb += run * int(wv.sum()) + 8 * wv.size + 32 * n
+        hbits = 8 if bits <= 4 else 16
+        kb += run * int(wk.sum()) + hbits * wk.size + 32 * D
+        vb += run * int(wv.sum()) + hbits * wv.size + 32 * n
     return kb, vb
 
 

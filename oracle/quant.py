@@ -65,5 +65,5 @@ def quantize_v_tokens(v16: np.ndarray, bits: int):
 
 
 def dequantize(q, scale, zero, axis: int) -> np.ndarray:
-    """x_hat = zero + scale * q, exact in fp64 (fp16 * int <= 15 plus fp16)."""
+    """x_hat = zero + scale * q, exact in fp64 (fp16 * int <= 255 plus fp16)."""
     return np.expand_dims(zero, axis) + np.expand_dims(scale, axis) * np.asarray(q, np.float64)

@@ -9,16 +9,18 @@ channel over consecutive tokens.  Readings adopted:
   a block holding n tokens covers slots r*R .. min(r*R + R, n) - 1;
 * each (run, channel) is stored at its own minimal width
   w = bit_length(max - min) (0 <= w <= b) relative to its minimum m, as
-  u = q - m; the header byte of the run is (w << 4) | m;
+  u = q - m; the header entry of the run is the byte (w << 4) | m for
+  b <= 4 and the little-endian u16 (w << 8) | m for b = 5..8 (hb = 1 or 2
+  bytes per entry);
 * the R slots of a run fill exactly w little-endian 32-bit words, slot i in
   bits [i*w, i*w + w) of the run's 32*w-bit string; slots past n hold u = 0.
 
 Record of one block (all integers little-endian, every section contiguous):
 
-    K:  scale[D] fp16 | zero[D] fp16 | hdr[nr][D] u8 | 0-pad to 16 B |
+    K:  scale[D] fp16 | zero[D] fp16 | hdr[nr][D] (hb B each) | 0-pad to 16 B |
         payload | 0-pad to 16 B
     V:  scale[B] fp16 | zero[B] fp16 (slot order; slots >= n hold 0) |
-        hdr[nr][D] u8 | 0-pad to 16 B | payload | 0-pad to 16 B
+        hdr[nr][D] (hb B each) | 0-pad to 16 B | payload | 0-pad to 16 B
 
 payload = for r in 0..nr-1, for c in 0..D-1: the w words of run (r, c).
 """
@@ -74,12 +76,17 @@ def pack_payload(q_slots: np.ndarray, w: np.ndarray, m: np.ndarray, run: int) ->
     return bytes(out)
 
 
-def header_bytes(w: np.ndarray, m: np.ndarray) -> bytes:
-    assert np.all(w <= 4) and np.all(m <= 15) and np.all(m >= 0)
-    return ((w << 4) | m).astype(np.uint8).tobytes()
+def header_bytes(w: np.ndarray, m: np.ndarray, hb: int = 1) -> bytes:
+    """The header entries [nr][D], hb bytes each (1: w << 4 | m, 2: w << 8 | m)."""
+    w, m = np.asarray(w, np.int64), np.asarray(m, np.int64)
+    if hb == 1:
+        assert np.all(w <= 4) and np.all(m <= 15) and np.all(m >= 0)
+        return ((w << 4) | m).astype(np.uint8).tobytes()
+    assert hb == 2 and np.all(w <= 8) and np.all(m <= 255) and np.all(m >= 0)
+    return ((w << 8) | m).astype("<u2").tobytes()
 
 
-def build_record(kind: str, q_slots, scale, zero, block: int, run: int) -> bytes:
+def build_record(kind: str, q_slots, scale, zero, block: int, run: int, hb: int = 1) -> bytes:
     """Assemble the record bytes of one block.
 
     kind 'K': scale/zero have D entries (per channel).
@@ -100,15 +107,15 @@ def build_record(kind: str, q_slots, scale, zero, block: int, run: int) -> bytes
         raise ValueError(kind)
     w, m = run_widths(q, run)
     head = f16_bits(sc).astype("<u2").tobytes() + f16_bits(ze).astype("<u2").tobytes()
-    head += header_bytes(w, m)
+    head += header_bytes(w, m, hb)
     head += bytes(_pad16(len(head)) - len(head))
     body = pack_payload(q, w, m, run)
     body += bytes(_pad16(len(body)) - len(body))
     return head + body
 
 
-def record_size(kind: str, w: np.ndarray, D: int, block: int) -> int:
+def record_size(kind: str, w: np.ndarray, D: int, block: int, hb: int = 1) -> int:
     """Closed-form record size in bytes from the run widths."""
     nr = w.shape[0]
     params = 4 * (D if kind == "K" else block)
-    return _pad16(params + nr * D) + _pad16(4 * int(w.sum()))
+    return _pad16(params + hb * nr * D) + _pad16(4 * int(w.sum()))

@@ -24,16 +24,20 @@ class Decoded:
     size: int             # bytes consumed (the record length)
 
 
-def decode_record(kind: str, buf: bytes, n: int, D: int, block: int, run: int) -> Decoded:
+def decode_record(kind: str, buf: bytes, n: int, D: int, block: int, run: int, hb: int = 1) -> Decoded:
+    """Decode one record; hb is the header entry size (1 byte up to b = 4, 2 above)."""
     nr = -(-n // run)
     b = np.frombuffer(buf, dtype=np.uint8)
     n_par = D if kind == "K" else block
     sc = f16_from_bits(b[0:2 * n_par].view("<u2"))
     ze = f16_from_bits(b[2 * n_par:4 * n_par].view("<u2"))
-    hdr = b[4 * n_par:4 * n_par + nr * D].astype(np.int64).reshape(nr, D)
-    w = hdr >> 4
-    m = hdr & 15
-    p0 = (4 * n_par + nr * D + 15) // 16 * 16
+    if hb == 1:
+        hdr = b[4 * n_par:4 * n_par + nr * D].astype(np.int64).reshape(nr, D)
+        w, m = hdr >> 4, hdr & 15
+    else:
+        hdr = b[4 * n_par:4 * n_par + 2 * nr * D].view("<u2").astype(np.int64).reshape(nr, D)
+        w, m = hdr >> 8, hdr & 255
+    p0 = (4 * n_par + hb * nr * D + 15) // 16 * 16
     nwords = int(w.sum())
     words = np.frombuffer(buf[p0:p0 + 4 * nwords], dtype="<u4").astype(np.uint64)
     words = np.concatenate([words, np.zeros(1, np.uint64)])       # window guard

@@ -37,7 +37,7 @@ def test_run_of_one_slot_has_no_payload():
     assert vb == 8 * n * D + 32 * n
 
 
-@pytest.mark.parametrize("bits,block", [(4, 64), (2, 128)])
+@pytest.mark.parametrize("bits,block", [(4, 64), (2, 128), (6, 64)])
 def test_run_of_a_whole_block_is_the_full_width_closed_form(bits, block):
     # K is quantised per channel over the block, so a run spanning the block
     # holds both 0 and 2^b - 1 in every non-constant channel: width b

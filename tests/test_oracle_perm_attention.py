@@ -164,7 +164,7 @@ def test_softmax_properties():
     assert np.all(one == 0.5)
 
 
-@pytest.mark.parametrize("bits,block", [(4, 64), (2, 64), (3, 64), (4, 128)])
+@pytest.mark.parametrize("bits,block", [(4, 64), (2, 64), (3, 64), (4, 128), (5, 128), (8, 64)])
 def test_cr_matches_closed_form_when_every_run_is_full_width(bits, block):
     """Construct blocks whose every run spans 0..L in every channel."""
     L = (1 << bits) - 1
@@ -188,6 +188,8 @@ def test_cr_matches_closed_form_when_every_run_is_full_width(bits, block):
         assert abs(r["cr_ideal"] - cf) < 1e-12
         assert abs(r["cr_phys"] - cf) < 1e-12     # all sections 16-byte aligned here
     assert abs(cr.closed_form_full_width("K", 4, 64, 32, 128) - 1024 / 304) < 1e-15
+    # b = 8: 8 payload bits, 16/32 header bits (two-byte entries), 32/64 parameter bits
+    assert abs(cr.closed_form_full_width("K", 8, 64, 32, 128) - 16 / 9) < 1e-15
 
 
 def test_cr_counts_the_bits_the_packer_writes():

@@ -43,7 +43,7 @@ def check_group(x16, bits):
     assert Fraction(float(ze[0])) == bmn
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 def test_random_groups_match_brute_force(bits):
     rng = np.random.default_rng(11)
     for trial in range(40):
@@ -53,7 +53,7 @@ def test_random_groups_match_brute_force(bits):
         check_group(x, bits)
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 def test_exact_ties_round_to_even(bits):
     """Values exactly halfway between two levels go to the even level."""
     L = (1 << bits) - 1
@@ -71,7 +71,7 @@ def test_exact_ties_round_to_even(bits):
 @settings(max_examples=60, deadline=None)
 @given(st.lists(st.integers(min_value=0, max_value=0x7BFF), min_size=1, max_size=9),
        st.lists(st.booleans(), min_size=9, max_size=9),
-       st.sampled_from([2, 3, 4]))
+       st.sampled_from([2, 3, 4, 5, 6, 7, 8]))
 def test_hypothesis_groups(mags, signs, bits):
     bits_arr = np.array(mags, np.uint16) | (np.array(signs[:len(mags)], np.uint16) << 15)
     x = bits_arr.view(np.float16)
@@ -90,7 +90,7 @@ def test_negative_zero_minimum_is_stored_as_plus_zero():
     assert fp16bits.f16_bits(ze)[0] == 0
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 def test_error_bound_and_scale_minimality(bits):
     """|x - x_hat| <= scale/2 exactly; the scale is the smallest fp16 that covers the range."""
     L = (1 << bits) - 1
@@ -123,7 +123,7 @@ def test_k_is_per_channel_and_v_per_token():
     assert sv.shape == (n,) and np.array_equal(zv, x.astype(np.float64).min(1) + 0.0)
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 def test_k_block_channel_hits_both_extremes(bits):
     """With a normal-range step, each K (block, channel) has min q = 0 and max q = L."""
     rng = np.random.default_rng(3)

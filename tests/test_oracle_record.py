@@ -13,16 +13,20 @@ import kvsynth
 from oracle import Config, record, unpack, stream, quant
 
 
-def bitstring_decode(kind, buf, n, D, B, R):
+def bitstring_decode(kind, buf, n, D, B, R, hb=1):
     nr = -(-n // R)
     npar = D if kind == "K" else B
-    hdr = list(buf[4 * npar:4 * npar + nr * D])
-    p0 = -(-(4 * npar + nr * D) // 16) * 16
+    raw = list(buf[4 * npar:4 * npar + hb * nr * D])
+    # entries: one byte (w in the high nibble) or two little-endian bytes
+    # (w in the high byte), read here byte by byte
+    hdr = raw if hb == 1 else [raw[2 * i] + 256 * raw[2 * i + 1] for i in range(nr * D)]
+    wsh, mmask = (4, 15) if hb == 1 else (8, 255)
+    p0 = -(-(4 * npar + hb * nr * D) // 16) * 16
     q = np.zeros((nr * R, D), np.int64)
     pos = p0
     for r in range(nr):
         for c in range(D):
-            w, m = hdr[r * D + c] >> 4, hdr[r * D + c] & 15
+            w, m = hdr[r * D + c] >> wsh, hdr[r * D + c] & mmask
             words = buf[pos:pos + 4 * w]
             pos += 4 * w
             # bit k of the run = bit (k % 32) of word k // 32
@@ -35,7 +39,7 @@ def bitstring_decode(kind, buf, n, D, B, R):
 
 
 def test_width_is_minimal():
-    for span in range(0, 16):
+    for span in range(0, 256):
         w = int(span).bit_length()
         assert (1 << w) > span and (w == 0 or (1 << (w - 1)) <= span)
         qs = np.array([[3], [3 + span]])
@@ -43,7 +47,8 @@ def test_width_is_minimal():
         assert ww[0, 0] == w and mm[0, 0] == 3
 
 
-@pytest.mark.parametrize("bits,block", [(2, 64), (3, 64), (4, 64), (4, 128), (3, 128)])
+@pytest.mark.parametrize("bits,block", [(2, 64), (3, 64), (4, 64), (4, 128), (3, 128), (5, 64), (6, 128),
+                                        (7, 64), (8, 64), (8, 128)])
 @pytest.mark.parametrize("n", [1, 5, 31, 32, 33, 63, 64, 100, 128])
 def test_record_roundtrip_and_layout(bits, block, n):
     if n > block:
@@ -57,15 +62,18 @@ def test_record_roundtrip_and_layout(bits, block, n):
         v = rng.standard_normal((n, 128)).astype(np.float16)
     code = stream.encode_block(k, v, cfg)
     for kind, rec, qs in (("K", code.k_record, code.qk_slots), ("V", code.v_record, code.qv_slots)):
-        d = unpack.decode_record(kind, rec, n, 128, block, 32)
+        hb = cfg.header_bytes
+        assert hb == (1 if bits <= 4 else 2)
+        d = unpack.decode_record(kind, rec, n, 128, block, 32, hb)
         assert np.array_equal(d.q, qs)
-        bq, end = bitstring_decode(kind, rec, n, 128, block, 32)
+        assert qs.max() <= (1 << bits) - 1
+        bq, end = bitstring_decode(kind, rec, n, 128, block, 32, hb)
         assert np.array_equal(bq, qs)
-        assert len(rec) == d.size == record.record_size(kind, d.w, 128, block)
+        assert len(rec) == d.size == record.record_size(kind, d.w, 128, block, hb)
         assert len(rec) % 16 == 0
         assert not any(rec[end:])                         # tail padding is zero
         npar = 128 if kind == "K" else block
-        hdr_end = 4 * npar + d.w.size
+        hdr_end = 4 * npar + hb * d.w.size
         p0 = -(-hdr_end // 16) * 16
         assert not any(rec[hdr_end:p0])                   # header padding is zero
         assert np.all(d.w <= bits)
@@ -85,7 +93,7 @@ def test_v_params_are_slot_ordered_and_zero_padded():
 
 
 @settings(max_examples=40, deadline=None)
-@given(st.integers(1, 64), st.sampled_from([2, 3, 4]), st.integers(0, 2**31 - 1))
+@given(st.integers(1, 64), st.sampled_from([2, 3, 4, 5, 6, 7, 8]), st.integers(0, 2**31 - 1))
 def test_hypothesis_roundtrip(n, bits, seed):
     rng = np.random.default_rng(seed)
     cfg = Config(bits=bits, block=64)
@@ -96,8 +104,33 @@ def test_hypothesis_roundtrip(n, bits, seed):
     v = rng.standard_normal((n, 128)).astype(np.float16)
     code = stream.encode_block(k, v, cfg)
     for kind, rec, qs in (("K", code.k_record, code.qk_slots), ("V", code.v_record, code.qv_slots)):
-        d = unpack.decode_record(kind, rec, n, 128, 64, 32)
+        d = unpack.decode_record(kind, rec, n, 128, 64, 32, cfg.header_bytes)
         assert np.array_equal(d.q, qs)
+
+
+@pytest.mark.parametrize("bits", [5, 8])
+def test_wide_header_entries_by_hand(bits):
+    """Two-byte entries: a run with every value equal has w = 0 and its
+    minimum in the low byte; a run spanning 0..L has w = b and m = 0; a
+    minimum above 15 (beyond a nibble) survives the round trip."""
+    L = (1 << bits) - 1
+    q = np.zeros((64, 128), np.int64)
+    q[:, 0] = 0
+    q[:32, 1] = np.arange(32) % (L + 1)
+    q[32:, 1] = L
+    q[:32, 2] = 200 if bits == 8 else 20
+    q[32:, 2] = (200 if bits == 8 else 20) + 3
+    q[:, 3] = np.arange(64) % 2 + 17
+    rec = record.build_record("K", q, np.ones(128), np.zeros(128), 64, 32, hb=2)
+    h = np.frombuffer(rec[512:512 + 2 * 2 * 128], "<u2").reshape(2, 128)
+    assert h[0, 0] == 0 and h[1, 0] == 0
+    assert h[0, 1] == (5 << 8) | 0 and h[1, 1] == (0 << 8) | L
+    m2 = 200 if bits == 8 else 20
+    assert h[0, 2] == m2 and h[1, 2] == m2 + 3
+    assert h[0, 3] == (1 << 8) | 17 and h[1, 3] == (1 << 8) | 17
+    d = unpack.decode_record("K", rec, 64, 128, 64, 32, 2)
+    assert np.array_equal(d.q, q)
+    assert np.array_equal(bitstring_decode("K", rec, 64, 128, 64, 32, 2)[0], q)
 
 
 def test_lossless_grid_values_are_reproduced_exactly():
