@@ -183,8 +183,11 @@ class PackedKVCache:
         out = torch.zeros(32, dtype=torch.int64, device=self.k_arena.device)
         _lib.check(_lib.load().packkv_stats(ctypes.byref(self._c), _ptr(out), _stream()), "packkv_stats")
         o = out.cpu().tolist()
-        return {"k_width_hist": o[0:5], "v_width_hist": o[5:10], "k_bytes": o[10], "v_bytes": o[11],
-                "k_words": o[12], "v_words": o[13], "k_runs": o[14], "v_runs": o[15]}
+        # widths 0..4 then 5..8 (the latter only at b > 4)
+        nw = self.bits + 1
+        return {"k_width_hist": (o[0:5] + o[16:20])[:max(5, nw)], "v_width_hist": (o[5:10] + o[20:24])[:max(5, nw)],
+                "k_bytes": o[10], "v_bytes": o[11], "k_words": o[12], "v_words": o[13], "k_runs": o[14],
+                "v_runs": o[15]}
 
 
 def stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:

@@ -17,7 +17,7 @@ constexpr uint64_t kArenaSlack = 64;   // over-read room for 16-byte vector load
 int check_cfg(const packkv_config_t* c) {
   if (!c) return PACKKV_EINVAL;
   if (c->head_dim != kD || c->run_tokens != kR) return PACKKV_EUNSUPPORTED;
-  if (c->bits < 2 || c->bits > 4) return PACKKV_EUNSUPPORTED;
+  if (c->bits < 2 || c->bits > 8) return PACKKV_EUNSUPPORTED;
   if (c->block_tokens != 64 && c->block_tokens != 128) return PACKKV_EUNSUPPORTED;
   if (c->permute < 0 || c->permute > 2) return PACKKV_EINVAL;
   return PACKKV_OK;

@@ -3,10 +3,12 @@
 // Record layout (one block of B tokens of one stream), from the PackKV
 // pipeline of quantise -> reorder tokens -> lossless channel-direction
 // bit-packing (Fig. 2 caption; TL;DR):
-//   K: scale[D] f16 | zero[D] f16 | hdr[nr][D] u8 | pad16 | payload | pad16
-//   V: scale[B] f16 | zero[B] f16 | hdr[nr][D] u8 | pad16 | payload | pad16
-// hdr = (w << 4) | m per (run, channel); payload = for run r, channel c: w
-// little-endian u32 words, slot i of the run in bits [i*w, i*w + w).
+//   K: scale[D] f16 | zero[D] f16 | hdr[nr][D] | pad16 | payload | pad16
+//   V: scale[B] f16 | zero[B] f16 | hdr[nr][D] | pad16 | payload | pad16
+// hdr per (run, channel): the byte (w << 4) | m for b <= 4, the
+// little-endian u16 (w << 8) | m for b = 5..8 (m needs the whole byte);
+// payload = for run r, channel c: w little-endian u32 words, slot i of the
+// run in bits [i*w, i*w + w).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -26,11 +28,12 @@ __host__ __device__ constexpr int64_t imin64(int64_t a, int64_t b) { return a < 
 // Geometry of a record holding n tokens (nr runs) of a block of B tokens.
 __host__ __device__ constexpr int n_params(bool is_v, int B) { return is_v ? B : kD; }
 __host__ __device__ constexpr int hdr_offset(bool is_v, int B) { return 4 * n_params(is_v, B); }
-__host__ __device__ constexpr int payload_offset(bool is_v, int B, int nr) {
-  return pad16(4 * n_params(is_v, B) + nr * kD);
+__host__ __device__ constexpr int hdr_entry_bytes(int bits) { return bits > 4 ? 2 : 1; }
+__host__ __device__ constexpr int payload_offset(bool is_v, int B, int nr, int hb = 1) {
+  return pad16(4 * n_params(is_v, B) + hb * nr * kD);
 }
 __host__ __device__ constexpr int max_record_bytes(bool is_v, int B, int bits) {
-  return payload_offset(is_v, B, B / kR) + 4 * (B / kR) * kD * bits;
+  return payload_offset(is_v, B, B / kR, hdr_entry_bytes(bits)) + 4 * (B / kR) * kD * bits;
 }
 
 // ---------------------------------------------------------------------------

@@ -88,12 +88,13 @@ __device__ __forceinline__ void run_values(const uint8_t* q, const uint8_t* orde
   }
 }
 
-// The w-bit string of a run: slot i's value in bits [i*w, i*w + w) of four
+// The w-bit string of a run: slot i's value in bits [i*w, i*w + w) of eight
 // little-endian words (only the first w are used).  W is a compile-time
 // width, so every bit position is a constant.
 template <int W>
-__device__ __forceinline__ void pack_run(const uint32_t u[kR], uint32_t out[4]) {
-  out[0] = out[1] = out[2] = out[3] = 0u;
+__device__ __forceinline__ void pack_run(const uint32_t u[kR], uint32_t out[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) out[k] = 0u;
 #pragma unroll
   for (int i = 0; i < kR; ++i) {
     const int p = i * W, wd = p >> 5, sh = p & 31;
@@ -416,8 +417,9 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
   const uint32_t k_ex = block_excl_scan(k_a + k_b, scan_sh, &totk);
   const uint32_t v_ex = block_excl_scan(v_a + v_b, scan_sh, &totv);
 
-  const uint32_t k_pay = (uint32_t)payload_offset(false, B, nr);
-  const uint32_t v_pay = (uint32_t)payload_offset(true, B, nr);
+  const int hb = hdr_entry_bytes(a.bits);
+  const uint32_t k_pay = (uint32_t)payload_offset(false, B, nr, hb);
+  const uint32_t v_pay = (uint32_t)payload_offset(true, B, nr, hb);
   const uint32_t k_size = k_pay + (uint32_t)pad16(4 * (int)totk);
   const uint32_t v_size = v_pay + (uint32_t)pad16(4 * (int)totv);
   uint32_t* koff = a.k_off + s * a.off_stride;
@@ -506,10 +508,17 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
   // headers and the zero padding up to the payload
   {
     const uint32_t kh = (uint32_t)hdr_offset(false, B), vh = (uint32_t)hdr_offset(true, B);
-    for (uint32_t i = tid; i < k_pay - kh; i += NT)
-      krec[kh + i] = i < (uint32_t)nrc ? (uint8_t)((wk[i] << 4) | mk[i]) : (uint8_t)0;
-    for (uint32_t i = tid; i < v_pay - vh; i += NT)
-      vrec[vh + i] = i < (uint32_t)nrc ? (uint8_t)((wv[i] << 4) | mv[i]) : (uint8_t)0;
+    // byte i of the header area: entry i / hb, byte i % hb of it
+    for (uint32_t i = tid; i < k_pay - kh; i += NT) {
+      const uint32_t e = hb == 2 ? i >> 1 : i;
+      const uint32_t h = e < (uint32_t)nrc ? (hb == 2 ? ((uint32_t)wk[e] << 8) | mk[e] : ((uint32_t)wk[e] << 4) | mk[e]) : 0u;
+      krec[kh + i] = (uint8_t)(hb == 2 && (i & 1u) ? h >> 8 : h);
+    }
+    for (uint32_t i = tid; i < v_pay - vh; i += NT) {
+      const uint32_t e = hb == 2 ? i >> 1 : i;
+      const uint32_t h = e < (uint32_t)nrc ? (hb == 2 ? ((uint32_t)wv[e] << 8) | mv[e] : ((uint32_t)wv[e] << 4) | mv[e]) : 0u;
+      vrec[vh + i] = (uint8_t)(hb == 2 && (i & 1u) ? h >> 8 : h);
+    }
   }
   // payload: each thread packs its two (run, channel) entries of K and of V
   for (int e = 0; e < 4; ++e) {
@@ -526,12 +535,16 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
     run_values(q, order, r, c, n, v);
 #pragma unroll
     for (int i = 0; i < kR; ++i) v[i] = r * kR + i < n ? v[i] - m : 0u;
-    uint32_t words[4];
+    uint32_t words[8];
     switch (w) {
       case 1: pack_run<1>(v, words); break;
       case 2: pack_run<2>(v, words); break;
       case 3: pack_run<3>(v, words); break;
-      default: pack_run<4>(v, words); break;
+      case 4: pack_run<4>(v, words); break;
+      case 5: pack_run<5>(v, words); break;
+      case 6: pack_run<6>(v, words); break;
+      case 7: pack_run<7>(v, words); break;
+      default: pack_run<8>(v, words); break;
     }
     uint32_t* dst = reinterpret_cast<uint32_t*>((is_v ? vrec + v_pay : krec + k_pay)) + woff;
     for (uint32_t i = 0; i < w; ++i) dst[i] = words[i];

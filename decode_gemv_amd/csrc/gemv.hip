@@ -103,7 +103,7 @@ __host__ __device__ constexpr int staging_bytes(int rec) {
 // index l + 64k).  Returns false if the record is inconsistent.  When every
 // run is at full width the offsets are implicit and no scan is needed;
 // `aligned` then reports that every run starts on a 16-byte boundary.
-template <int NRL>
+template <int NRL, int HB = 1>
 __device__ __forceinline__ bool scan_runs(const uint8_t* rec, int hdr_off, int pay_off, uint32_t size,
                                           int nruns, int bits, int lane,
                                           int w[NRL], uint32_t m[NRL], uint32_t off[NRL], bool& full) {
@@ -112,11 +112,12 @@ __device__ __forceinline__ bool scan_runs(const uint8_t* rec, int hdr_off, int p
 #pragma unroll
   for (int k = 0; k < NRL; ++k) {
     const int ri = lane + 64 * k;
-    const uint32_t h = ri < nruns ? rec[hdr_off + ri] : 0u;
-    w[k] = (int)(h >> 4);
-    m[k] = h & 15u;
+    uint32_t h = 0u;
+    if (ri < nruns) h = HB == 2 ? reinterpret_cast<const uint16_t*>(rec + hdr_off)[ri] : rec[hdr_off + ri];
+    w[k] = (int)(HB == 2 ? h >> 8 : h >> 4);
+    m[k] = HB == 2 ? h & 255u : h & 15u;
     // a valid run has max - m in [2^(w-1), 2^w - 1] and max <= L
-    bad |= (w[k] > bits) | ((int)m[k] > L) | (w[k] > 0 && (int)m[k] + (1 << (w[k] - 1)) > L);
+    bad |= w[k] > bits || (int)m[k] > L || (w[k] > 0 && (int)m[k] + (1 << (w[k] - 1)) > L);
     narrow |= w[k] != bits;
   }
   if (__ballot(bad)) return false;
@@ -667,14 +668,6 @@ struct KBlockM {
   }
 };
 
-// The K block code the kernels use: on the matrix cores (KBlockM) for a tile
-// of four queries, with vector FMAs (KBlock) for one.  Measured (A/B in one
-// process): with four queries, 128-token blocks, fused attention 295 -> 264 us
-// and the K GEMV 128 -> 117 us; with one query the matrix version is slower
-// (K GEMV +9-10 %, one wave less occupancy; fused attention +1-3 %), as its
-// transposes and LDS round trips are not repaid by 32 FMAs per packed word.
-template <int B, int BITS, int GT>
-using KSel = std::conditional_t<(GT > 1), KBlockM<B, BITS, GT>, KBlock<B, BITS, GT>>;
 
 // ---------------------------------------------------------------------------
 // V side, one staged block.
@@ -988,10 +981,353 @@ struct VBlockM {
   }
 };
 
-// The V block code the kernels use: on the matrix cores (VBlockM) for a tile
-// of four queries, with v_dot8 (VBlock) for one.
+// ---------------------------------------------------------------------------
+// Wide widths, b = 5..8: two-byte header entries (w << 8 | m) and byte
+// containers.  The block code is the plain form of the 4-bit path: every
+// run is decoded with a prefix sum of its widths (no full-width shortcut),
+// K converts bytes with v_cvt_f32_ubyte and V takes the 20-bit weights as
+// three byte digits with v_dot4_u32_u8.
+
+// Decode of one staged record: lane l holds runs l + 64k (k < NRL) as eight
+// words of byte containers, word i = q of slots 4i .. 4i+3 (byte j = slot
+// 4i + j), q = m + u.  Returns false if the record is inconsistent (a width
+// above bits, a minimum that leaves no room for its width, or widths that do
+// not add up to the record size); the containers are then zero.
+template <int B, bool IS_V>
+struct DecW {
+  static constexpr int NR = B / kR;
+  static constexpr int NRL = NR * kD / 64;
+  static constexpr int HDR = hdr_offset(IS_V, B);
+
+  // the R fields of width W of a run's W words, spread to bytes
+  template <int W>
+  __device__ __forceinline__ static void spread(const uint32_t (&wd)[8], uint32_t (&out)[8]) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) out[k] = 0u;
+    if constexpr (W > 0) {
+#pragma unroll
+      for (int i = 0; i < kR; ++i) {
+        const int p = i * W, wi = p >> 5, sh = p & 31;
+        uint32_t v = wd[wi] >> sh;
+        if (sh + W > 32) v |= wd[wi + 1] << (32 - sh);
+        out[i >> 2] |= (v & ((1u << W) - 1u)) << (8 * (i & 3));
+      }
+    }
+  }
+
+  __device__ __forceinline__ static bool decode(const uint8_t* rec, uint32_t size, int nr, int lane, int bits,
+                                                uint32_t (&cont)[NRL][8]) {
+    const int pay = payload_offset(IS_V, B, nr, 2);
+    const int nruns = nr * kD;
+    const int L = (1 << bits) - 1;
+    const uint16_t* hd = reinterpret_cast<const uint16_t*>(rec + HDR);
+    int w[NRL];
+    uint32_t m[NRL], off[NRL];
+    bool bad = false;
+    uint32_t base = 0;
+#pragma unroll
+    for (int k = 0; k < NRL; ++k) {
+      const int ri = lane + 64 * k;
+      const uint32_t h = ri < nruns ? hd[ri] : 0u;
+      w[k] = (int)(h >> 8);
+      m[k] = h & 255u;
+      // a valid run has max - m in [2^(w-1), 2^w - 1] and max <= L
+      bad |= w[k] > bits || (int)m[k] > L || (w[k] > 0 && (int)m[k] + (1 << (w[k] - 1)) > L);
+      const int incl = wave_incl_scan(w[k]);
+      off[k] = base + (uint32_t)(incl - w[k]);
+      base += (uint32_t)__builtin_amdgcn_readlane(incl, 63);
+    }
+    const bool ok = __ballot(bad) == 0 && (uint32_t)pad16(pay + 4 * (int)base) == size;
+    const uint32_t* pw = reinterpret_cast<const uint32_t*>(rec + pay);
+#pragma unroll
+    for (int k = 0; k < NRL; ++k) {
+      // a consistent record keeps every run's words inside it
+      const int wr = ok ? w[k] : 0;
+      uint32_t wd[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wd[i] = i < wr ? pw[off[k] + i] : 0u;
+      switch (wr) {
+        case 0: spread<0>(wd, cont[k]); break;
+        case 1: spread<1>(wd, cont[k]); break;
+        case 2: spread<2>(wd, cont[k]); break;
+        case 3: spread<3>(wd, cont[k]); break;
+        case 4: spread<4>(wd, cont[k]); break;
+        case 5: spread<5>(wd, cont[k]); break;
+        case 6: spread<6>(wd, cont[k]); break;
+        case 7: spread<7>(wd, cont[k]); break;
+        default: spread<8>(wd, cont[k]); break;
+      }
+      const uint32_t mm = (ok ? m[k] : 0u) * 0x01010101u;   // m + u <= 255: no carries
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cont[k][i] += mm;
+    }
+    return ok;
+  }
+};
+
+// K side, wide widths, one staged block (the interface of KBlock).  The
+// containers go to an LDS plane [slot quad][channel]; lane (g8, cg) then
+// takes slots 8 g8 .. 8 g8 + 7 of 16 channels, converts the bytes exactly
+// and multiply-adds q' = q * scale, and the 8 channel groups are reduced
+// through LDS as in KBlock.
+template <int B, int GT>
+struct KBlockW {
+  using Dec = DecW<B, false>;
+  static constexpr int NRL = Dec::NRL;
+  static constexpr int NH = B / 64;
+  static constexpr int ROWW = kD + 8;
+  static constexpr int PLANE_BYTES = (B / 4) * ROWW * 4;
+  static constexpr int RED_BYTES = 64 * 9 * 4;
+  static constexpr int HALF_BYTES = 16 * ROWW * 4;    // the quad rows of 64 slots
+  static_assert(RED_BYTES <= HALF_BYTES, "reduction must fit a half's plane rows");
+  static constexpr int SCRATCH_BYTES = PLANE_BYTES;
+  static constexpr int QS_BYTES = GT * kD * 4;
+
+  float* qs;
+  int lane, g8, cg, bits = 8;
+  float qa[GT], qb[GT];                               // queries at channels lane, lane + 64
+
+  __device__ __forceinline__ void init(uint8_t* qs_, int lane_) {
+    qs = reinterpret_cast<float*>(qs_);
+    lane = lane_;
+    g8 = lane & 7;
+    cg = lane >> 3;
+  }
+  __device__ __forceinline__ void set_queries(const uint16_t* q, int64_t s, int G, int gq0) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      const bool ok = gq0 + g < G;
+      const uint16_t* qp = q + (s * G + gq0 + g) * kD;
+      qa[g] = ok ? f16_bits_to_float(qp[lane]) : 0.f;
+      qb[g] = ok ? f16_bits_to_float(qp[lane + 64]) : 0.f;
+    }
+  }
+
+  template <class Sink>
+  __device__ __forceinline__ bool run(uint8_t* rec, uint32_t size, int nr, Sink&& sink) {
+    float beta[GT];
+    {
+      const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec);
+      const float sa = f16_bits_to_float(sc[lane]), sb = f16_bits_to_float(sc[lane + 64]);
+      const float za = f16_bits_to_float(sc[kD + lane]), zb = f16_bits_to_float(sc[kD + lane + 64]);
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        qs[g * kD + lane] = qa[g] * sa;
+        qs[g * kD + lane + 64] = qb[g] * sb;
+        beta[g] = wave_sum(fmaf(qa[g], za, qb[g] * zb));
+      }
+    }
+    uint32_t cont[NRL][8];
+    const bool ok = Dec::decode(rec, size, nr, lane, bits, cont);
+    wave_sync();                                  // every lane has read the record
+    uint32_t* plane = reinterpret_cast<uint32_t*>(rec);
+#pragma unroll
+    for (int k = 0; k < NRL; ++k) {
+      const int r = k >> 1, c = lane + 64 * (k & 1);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) plane[(r * 8 + kk) * ROWW + c] = cont[k][kk];
+    }
+    wave_sync();
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      float acc[GT][8];
+#pragma unroll
+      for (int g = 0; g < GT; ++g)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
+      const int row = h * 16 + 2 * g8;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int c0 = cg * 16 + ((i4 + cg) & 3) * 4;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(&plane[row * ROWW + c0]);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(&plane[(row + 1) * ROWW + c0]);
+        float qq[GT][4];
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+          const float4 t = *reinterpret_cast<const float4*>(&qs[g * kD + c0]);
+          qq[g][0] = t.x; qq[g][1] = t.y; qq[g][2] = t.z; qq[g][3] = t.w;
+        }
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          float f[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f[i] = (float)((lo[cc] >> (8 * i)) & 255u);
+            f[4 + i] = (float)((hi[cc] >> (8 * i)) & 255u);
+          }
+#pragma unroll
+          for (int g = 0; g < GT; ++g)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(qq[g][cc], f[i], acc[g][i]);
+        }
+      }
+      float* red = reinterpret_cast<float*>(rec + h * HALF_BYTES);
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        wave_sync();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) red[(g8 * 8 + i) * 9 + cg] = acc[g][i];
+        wave_sync();
+        float sum = beta[g];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += red[lane * 9 + u];
+        sink(g, h, sum, ok);
+      }
+    }
+    return ok;
+  }
+};
+
+// V side, wide widths, one staged block (the interface of VBlock).  The
+// weights are VBlock's 20-bit fixed point per block and query, split into
+// three byte digits; v_dot4_u32_u8 takes 4 slots of one channel per
+// instruction.  Each digit sum is at most B * 255 * 255 < 2^24, so the three
+// are exact in fp32 and are combined there.
+template <int B, int GT>
+struct VBlockW {
+  using Dec = DecW<B, true>;
+  static constexpr int NR = B / kR;
+  static constexpr int NRL = Dec::NRL;
+  static constexpr int NH = B / 64;
+  static constexpr int NQ = B / 4;                    // 4-slot groups per block
+  static constexpr int ND = 3;                        // byte digits of p'
+  static constexpr int DIG_WORDS = GT * ND * NQ;
+  static constexpr int LDS_WORDS = DIG_WORDS + GT * B;
+
+  uint32_t* dig;                                      // [GT][ND][NQ]
+  uint32_t* pst;                                      // [GT][B] fixed-point weights
+  int lane, bits = 8;
+
+  __device__ __forceinline__ void init(uint32_t* lds, int lane_) {
+    dig = lds;
+    pst = lds + DIG_WORDS;
+    lane = lane_;
+  }
+  __device__ __forceinline__ void rescale(float (&acc)[GT][2], const float (&alpha)[GT]) const {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      acc[g][0] *= alpha[g];
+      acc[g][1] *= alpha[g];
+    }
+  }
+  template <class Dst>
+  __device__ __forceinline__ void store(const float (&acc)[GT][2], const float (&z)[GT], Dst&& dst) const {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      float* d = dst(g);
+      if (d) {
+        store_partial(d + lane, acc[g][0] + z[g]);
+        store_partial(d + lane + 64, acc[g][1] + z[g]);
+      }
+    }
+  }
+
+  __device__ __forceinline__ bool run(const uint8_t* rec, uint32_t size, int nr, bool use,
+                                      const float (&pw)[GT][NH], float (&acc)[GT][2], float (&pz)[GT]) {
+    int E[GT];
+    bool live[GT];
+    float pzb[GT];
+    {
+      const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec);
+      float pp[GT][NH];
+#pragma unroll
+      for (int g = 0; g < GT; ++g) pzb[g] = 0.f;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const int sl = h * 64 + lane;
+        const float scl = f16_bits_to_float(sc[sl]), zer = f16_bits_to_float(sc[B + sl]);
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+          pp[g][h] = pw[g][h] * scl;
+          pzb[g] = fmaf(pw[g][h], zer, pzb[g]);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        float mx = pp[g][0];
+#pragma unroll
+        for (int h = 1; h < NH; ++h) mx = fmaxf(mx, pp[g][h]);
+        const float M = wave_max_nonneg(mx);
+        live[g] = M > 0.f;
+        E[g] = live[g] ? 20 - __builtin_amdgcn_frexp_expf(M) : 0;   // M 2^E in [2^19, 2^20)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          pst[g * B + h * 64 + lane] = min((uint32_t)(ldexpf(pp[g][h], E[g]) + 0.5f), 0xFFFFFu);
+      }
+    }
+    wave_sync();
+    // digit word (g, d, q): byte d of the weights of slots 4q .. 4q+3, slot
+    // 4q + j in byte j; one word per lane and pass
+#pragma unroll
+    for (int i0 = 0; i0 < DIG_WORDS; i0 += 64) {
+      const int i = i0 + lane;
+      if (DIG_WORDS % 64 == 0 || i < DIG_WORDS) {
+        const int g = i / (ND * NQ), d = (i / NQ) % ND, q = i % NQ;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(pst + g * B + 4 * q);
+        const uint32_t sh = 8u * (uint32_t)d;
+        dig[i] = __builtin_amdgcn_ubfe(a[0], sh, 8) | (__builtin_amdgcn_ubfe(a[1], sh, 8) << 8) |
+                 (__builtin_amdgcn_ubfe(a[2], sh, 8) << 16) | (__builtin_amdgcn_ubfe(a[3], sh, 8) << 24);
+      }
+    }
+    uint32_t cont[NRL][8];
+    const bool ok = Dec::decode(rec, size, nr, lane, bits, cont) && use;
+    wave_sync();
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      if (!ok || !live[g]) continue;
+      uint32_t sd[2][ND];
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+        for (int d = 0; d < ND; ++d) sd[ch][d] = 0u;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        if (r >= nr) break;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          uint32_t W[ND];                             // digit words of slots 4(8r+kk) ...
+#pragma unroll
+          for (int d = 0; d < ND; ++d) W[d] = dig[(g * ND + d) * NQ + 8 * r + kk];
+#pragma unroll
+          for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+              sd[ch][d] = __builtin_amdgcn_udot4(cont[2 * r + ch][kk], W[d], sd[ch][d], false);
+        }
+      }
+      const float unit = ldexpf(1.0f, -E[g]);
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        const float x = fmaf(65536.f, (float)sd[ch][2], fmaf(256.f, (float)sd[ch][1], (float)sd[ch][0]));
+        acc[g][ch] = fmaf(x, unit, acc[g][ch]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < GT; ++g)
+      if (ok) pz[g] += pzb[g];
+    return ok;
+  }
+};
+
+// The K block code the kernels use: wide widths (b > 4) take KBlockW; at
+// b <= 4 the matrix cores (KBlockM) for a tile of four queries, vector FMAs
+// (KBlock) for one.  Measured (A/B in one process): with four queries,
+// 128-token blocks, fused attention 295 -> 264 us and the K GEMV 128 -> 117
+// us; with one query the matrix version is slower (K GEMV +9-10 %, one wave
+// less occupancy; fused attention +1-3 %), as its transposes and LDS round
+// trips are not repaid by 32 FMAs per packed word.
+template <int B, int BITS, int GT>
+using KSel = std::conditional_t<(BITS > 4), KBlockW<B, GT>,
+                                std::conditional_t<(GT > 1), KBlockM<B, BITS, GT>, KBlock<B, BITS, GT>>>;
+
+// The V block code the kernels use: wide widths take VBlockW; at b <= 4 the
+// matrix cores (VBlockM) for a tile of four queries, v_dot8 (VBlock) for one.
 template <int B, int BITS, int GT, bool STAGED = true>
-using VSel = std::conditional_t<(GT > 1), VBlockM<B, BITS, GT>, VBlock<B, BITS, GT, STAGED>>;
+using VSel = std::conditional_t<(BITS > 4), VBlockW<B, GT>,
+                                std::conditional_t<(GT > 1), VBlockM<B, BITS, GT>, VBlock<B, BITS, GT, STAGED>>>;
+
+// The largest record the kernels of a width class stage: b <= 4 or b = 5..8.
+__host__ __device__ constexpr int class_bits(int bits) { return bits > 4 ? 8 : 4; }
 
 // ---------------------------------------------------------------------------
 // Streaming skeleton shared by the GEMVs and by each wave of fused
@@ -1034,7 +1370,7 @@ struct RecordStream {
 template <int B, int BITS, int GT>
 __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
   using KB = KSel<B, BITS, GT>;
-  constexpr int REC = max_record_bytes(false, B, 4);
+  constexpr int REC = max_record_bytes(false, B, class_bits(BITS));
   constexpr int NCH = (REC + 1023) / 1024;
   constexpr int BUF = staging_bytes(REC) > KB::SCRATCH_BYTES ? staging_bytes(REC) : KB::SCRATCH_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t rec[BUF];
@@ -1055,6 +1391,7 @@ __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
   rs.lane = lane;
   KB kb;
   kb.init(qs, lane);
+  if constexpr (BITS > 4) kb.bits = a.bits;
   bool corrupt = false;
 
   for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
@@ -1122,7 +1459,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(pv_waves_per
 void k_pv_gemv(GemvArgs a) {
   using VB = VSel<B, BITS, GT>;
   constexpr int NH = VB::NH;
-  constexpr int REC = max_record_bytes(true, B, 4);
+  constexpr int REC = max_record_bytes(true, B, class_bits(BITS));
   constexpr int NCH = (REC + 1023) / 1024;
   __shared__ __attribute__((aligned(16))) uint8_t rec[staging_bytes(REC)];
   __shared__ __attribute__((aligned(16))) uint32_t dig[VB::LDS_WORDS];
@@ -1142,6 +1479,7 @@ void k_pv_gemv(GemvArgs a) {
   rs.lane = lane;
   VB vb;
   vb.init(dig, lane);
+  if constexpr (BITS > 4) vb.bits = a.bits;
   bool corrupt = false;
 
   for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
@@ -1261,8 +1599,8 @@ void k_attn_decode(AttnArgs a) {
   using KB = KSel<B, BITS, GT>;
   using VB = VSel<B, BITS, GT, false>;
   constexpr int NH = B / 64;
-  constexpr int REC_K = max_record_bytes(false, B, 4);
-  constexpr int REC_V = max_record_bytes(true, B, 4);
+  constexpr int REC_K = max_record_bytes(false, B, class_bits(BITS));
+  constexpr int REC_V = max_record_bytes(true, B, class_bits(BITS));
   constexpr int NCH_K = (REC_K + 1023) / 1024;
   constexpr int NCH_V = (REC_V + 1023) / 1024;
   constexpr int BUF_K = staging_bytes(REC_K) > KB::SCRATCH_BYTES ? staging_bytes(REC_K) : KB::SCRATCH_BYTES;
@@ -1321,6 +1659,7 @@ void k_attn_decode(AttnArgs a) {
       ks.lane = lane;
       KB kb;
       kb.init(qs, lane);
+      if constexpr (BITS > 4) kb.bits = a.bits;
       kb.set_queries(q, s, a.G, gq0);
       u32x4 pre[NCH_K];
       ks.request(0, pre);
@@ -1358,6 +1697,7 @@ void k_attn_decode(AttnArgs a) {
       vs.lane = lane;
       VB vb;
       vb.init(dig, lane);
+      if constexpr (BITS > 4) vb.bits = a.bits;
       float m[GT], l[GT], acc[GT][2], pz[GT];
 #pragma unroll
       for (int g = 0; g < GT; ++g) { m[g] = NEG_INF; l[g] = 0.f; acc[g][0] = acc[g][1] = 0.f; pz[g] = 0.f; }
@@ -1467,12 +1807,13 @@ void k_attn_decode(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // Decompress (test path): mode 0 -> u8 q in slot order, mode 1 -> fp32 x_hat
 // in token order.
-template <int B, bool IS_V>
+template <int B, bool IS_V, bool WIDE>
 __global__ __launch_bounds__(64) void k_decompress(GemvArgs a, const uint8_t* perm, int64_t perm_stride,
                                                    int mode, void* out) {
   constexpr int NR = B / kR;
   constexpr int NRL = NR * kD / 64;
-  constexpr int REC = max_record_bytes(IS_V, B, 4);
+  constexpr int HB = WIDE ? 2 : 1;
+  constexpr int REC = max_record_bytes(IS_V, B, WIDE ? 8 : 4);
   constexpr int NCH = (REC + 1023) / 1024;
   constexpr int HDR = hdr_offset(IS_V, B);
   __shared__ __attribute__((aligned(16))) uint8_t rec[staging_bytes(REC)];
@@ -1491,11 +1832,11 @@ __global__ __launch_bounds__(64) void k_decompress(GemvArgs a, const uint8_t* pe
   load_record<NCH>(arena + o, size, lane, pre);
   store_record<NCH>(rec, pre, lane);
   __syncthreads();
-  const int pay = payload_offset(IS_V, B, nr);
+  const int pay = payload_offset(IS_V, B, nr, HB);
   int w[NRL];
   uint32_t m[NRL], ro[NRL];
   bool full;
-  if (!scan_runs<NRL>(rec, HDR, pay, size, nr * kD, a.bits, lane, w, m, ro, full)) {
+  if (!scan_runs<NRL, HB>(rec, HDR, pay, size, nr * kD, a.bits, lane, w, m, ro, full)) {
     if (lane == 0) latch(a.status, PACKKV_ECORRUPT);
     return;
   }
@@ -1507,12 +1848,29 @@ __global__ __launch_bounds__(64) void k_decompress(GemvArgs a, const uint8_t* pe
     const int r = ri / kD, c = ri % kD;
     if (r >= nr) continue;
     uint32_t wd[4], nib[4];
-    run_words(rec, pay, ro[k], false, wd);
-    run_to_nibbles(w[k], m[k], wd, nib);
+    if constexpr (!WIDE) {
+      run_words(rec, pay, ro[k], false, wd);
+      run_to_nibbles(w[k], m[k], wd, nib);
+    }
+    // wide: field i of the run's w words, read from the staged record
+    const uint32_t* pw = reinterpret_cast<const uint32_t*>(rec + pay) + ro[k];
+    const int wk = w[k];
     for (int i = 0; i < kR; ++i) {
       const int sl = r * kR + i;
       if (sl >= n) break;
-      const uint32_t qv = (nib[i >> 3] >> (4 * (i & 7))) & 15u;
+      uint32_t qv;
+      if constexpr (WIDE) {
+        uint32_t u = 0u;
+        if (wk > 0) {
+          const int p = i * wk, wi = p >> 5, sh = p & 31;
+          uint32_t v = pw[wi] >> sh;
+          if (sh + wk > 32) v |= pw[wi + 1] << (32 - sh);
+          u = v & ((1u << wk) - 1u);
+        }
+        qv = m[k] + u;
+      } else {
+        qv = (nib[i >> 3] >> (4 * (i & 7))) & 15u;
+      }
       if (mode == 0) {
         uint8_t* o8 = reinterpret_cast<uint8_t*>(out);
         o8[(((int64_t)s * a.n_tokens) + (int64_t)j * B + sl) * kD + c] = (uint8_t)qv;
@@ -1533,7 +1891,7 @@ __global__ __launch_bounds__(64) void k_decompress(GemvArgs a, const uint8_t* pe
 }
 
 // Width histogram and byte counts.
-template <int B, bool IS_V>
+template <int B, bool IS_V, bool WIDE>
 __global__ __launch_bounds__(64) void k_stats(GemvArgs a, unsigned long long* out) {
   constexpr int NR = B / kR;
   const int lane = threadIdx.x;
@@ -1543,21 +1901,22 @@ __global__ __launch_bounds__(64) void k_stats(GemvArgs a, unsigned long long* ou
   const uint32_t o = offs[j], size = offs[j + 1] - o;
   const int n = (int)imin64(B, a.n_tokens - (int64_t)j * B);
   const int nr = (n + kR - 1) / kR;
-  if (!record_ok(o, size, a.arena_stride, max_record_bytes(IS_V, B, 4))) {
+  if (!record_ok(o, size, a.arena_stride, max_record_bytes(IS_V, B, WIDE ? 8 : 4))) {
     if (lane == 0) latch(a.status, PACKKV_ECORRUPT);
     return;
   }
   const uint8_t* hdr = arena + o + hdr_offset(IS_V, B);
-  unsigned long long hist[5] = {0, 0, 0, 0, 0};
+  unsigned long long hist[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
   unsigned long long words = 0;
   for (int ri = lane; ri < nr * kD; ri += 64) {
-    const int w = hdr[ri] >> 4;
-    if (w <= 4) hist[w]++;
+    const int w = WIDE ? reinterpret_cast<const uint16_t*>(hdr)[ri] >> 8 : hdr[ri] >> 4;
+    if (w <= 8) hist[w]++;
     words += (unsigned long long)w;
   }
-  const int base = IS_V ? 5 : 0;
-  for (int i = 0; i < 5; ++i)
-    if (hist[i]) atomicAdd(&out[base + i], hist[i]);
+  // widths 0..4 at out[0..4] (K) and out[5..9] (V); 5..8 at out[16..19]
+  // (K) and out[20..23] (V)
+  for (int i = 0; i < 9; ++i)
+    if (hist[i]) atomicAdd(&out[i < 5 ? (IS_V ? 5 : 0) + i : (IS_V ? 20 : 16) + i - 5], hist[i]);
   if (words) atomicAdd(&out[IS_V ? 13 : 12], words);
   if (lane == 0) {
     atomicAdd(&out[IS_V ? 11 : 10], (unsigned long long)size);
@@ -1626,7 +1985,9 @@ __global__ __launch_bounds__(1024) void k_softmax(const float* scores, float* p,
 }
 
 // ---------------------------------------------------------------------------
-// Launchers.
+// Launchers.  Widths 5..8 share one kernel per shape (BITS = 8), which checks
+// the record's widths against the configured b at run time.
+static inline int class_bits_or_narrow(int bits) { return bits > 4 ? 8 : bits; }
 template <int B, int BITS>
 static void qk_launch(const GemvArgs& a, dim3 grid, hipStream_t st) {
   if (a.G == 1) hipLaunchKernelGGL((k_qk_gemv<B, BITS, 1>), grid, dim3(64), 0, st, a);
@@ -1639,26 +2000,30 @@ static void pv_launch(const GemvArgs& a, dim3 grid, hipStream_t st) {
 }
 hipError_t launch_qk(const GemvArgs& a, int B, int n_streams, hipStream_t st) {
   const dim3 grid(n_streams * a.splits);
-  switch (B * 8 + a.bits) {
+  switch (B * 8 + class_bits_or_narrow(a.bits)) {
     case 64 * 8 + 2: qk_launch<64, 2>(a, grid, st); break;
     case 64 * 8 + 3: qk_launch<64, 3>(a, grid, st); break;
     case 64 * 8 + 4: qk_launch<64, 4>(a, grid, st); break;
     case 128 * 8 + 2: qk_launch<128, 2>(a, grid, st); break;
     case 128 * 8 + 3: qk_launch<128, 3>(a, grid, st); break;
-    default: qk_launch<128, 4>(a, grid, st); break;
+    case 128 * 8 + 4: qk_launch<128, 4>(a, grid, st); break;
+    case 64 * 8 + 8: qk_launch<64, 8>(a, grid, st); break;
+    default: qk_launch<128, 8>(a, grid, st); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_pv(const GemvArgs& a, int B, int n_streams, hipStream_t st) {
   const dim3 grid(n_streams * a.splits);
-  switch (B * 8 + a.bits) {
+  switch (B * 8 + class_bits_or_narrow(a.bits)) {
     case 64 * 8 + 2: pv_launch<64, 2>(a, grid, st); break;
     case 64 * 8 + 3: pv_launch<64, 3>(a, grid, st); break;
     case 64 * 8 + 4: pv_launch<64, 4>(a, grid, st); break;
     case 128 * 8 + 2: pv_launch<128, 2>(a, grid, st); break;
     case 128 * 8 + 3: pv_launch<128, 3>(a, grid, st); break;
-    default: pv_launch<128, 4>(a, grid, st); break;
+    case 128 * 8 + 4: pv_launch<128, 4>(a, grid, st); break;
+    case 64 * 8 + 8: pv_launch<64, 8>(a, grid, st); break;
+    default: pv_launch<128, 8>(a, grid, st); break;
   }
   return hipGetLastError();
 }
@@ -1670,13 +2035,15 @@ static void attn_launch(const AttnArgs& a, dim3 grid, hipStream_t st) {
 }
 template <bool PAGED>
 static void attn_dispatch(const AttnArgs& a, int B, dim3 grid, hipStream_t st) {
-  switch (B * 8 + a.bits) {
+  switch (B * 8 + class_bits_or_narrow(a.bits)) {
     case 64 * 8 + 2: attn_launch<64, 2, PAGED>(a, grid, st); break;
     case 64 * 8 + 3: attn_launch<64, 3, PAGED>(a, grid, st); break;
     case 64 * 8 + 4: attn_launch<64, 4, PAGED>(a, grid, st); break;
     case 128 * 8 + 2: attn_launch<128, 2, PAGED>(a, grid, st); break;
     case 128 * 8 + 3: attn_launch<128, 3, PAGED>(a, grid, st); break;
-    default: attn_launch<128, 4, PAGED>(a, grid, st); break;
+    case 128 * 8 + 4: attn_launch<128, 4, PAGED>(a, grid, st); break;
+    case 64 * 8 + 8: attn_launch<64, 8, PAGED>(a, grid, st); break;
+    default: attn_launch<128, 8, PAGED>(a, grid, st); break;
   }
 }
 hipError_t launch_attention(const AttnArgs& a, int B, int n_streams, int n_caches, hipStream_t st,
@@ -1690,12 +2057,14 @@ hipError_t launch_attention(const AttnArgs& a, int B, int n_streams, int n_cache
 hipError_t launch_decompress(const GemvArgs& a, int B, bool is_v, int n_streams, const uint8_t* perm,
                              int64_t perm_stride, int mode, void* out, hipStream_t st) {
   dim3 grid(a.nb, n_streams), block(64);
-  if (B == 64) {
-    if (is_v) hipLaunchKernelGGL((k_decompress<64, true>), grid, block, 0, st, a, perm, perm_stride, mode, out);
-    else hipLaunchKernelGGL((k_decompress<64, false>), grid, block, 0, st, a, perm, perm_stride, mode, out);
-  } else {
-    if (is_v) hipLaunchKernelGGL((k_decompress<128, true>), grid, block, 0, st, a, perm, perm_stride, mode, out);
-    else hipLaunchKernelGGL((k_decompress<128, false>), grid, block, 0, st, a, perm, perm_stride, mode, out);
+  const int sel = (B == 64 ? 0 : 4) + (is_v ? 2 : 0) + (a.bits > 4 ? 1 : 0);
+  switch (sel) {
+#define PACKKV_DEC(S, BB, V, W) \
+    case S: hipLaunchKernelGGL((k_decompress<BB, V, W>), grid, block, 0, st, a, perm, perm_stride, mode, out); break;
+    PACKKV_DEC(0, 64, false, false) PACKKV_DEC(1, 64, false, true) PACKKV_DEC(2, 64, true, false)
+    PACKKV_DEC(3, 64, true, true) PACKKV_DEC(4, 128, false, false) PACKKV_DEC(5, 128, false, true)
+    PACKKV_DEC(6, 128, true, false) PACKKV_DEC(7, 128, true, true)
+#undef PACKKV_DEC
   }
   return hipGetLastError();
 }
@@ -1703,12 +2072,14 @@ hipError_t launch_decompress(const GemvArgs& a, int B, bool is_v, int n_streams,
 hipError_t launch_stats(const GemvArgs& a, int B, bool is_v, int n_streams, unsigned long long* out,
                         hipStream_t st) {
   dim3 grid(a.nb, n_streams), block(64);
-  if (B == 64) {
-    if (is_v) hipLaunchKernelGGL((k_stats<64, true>), grid, block, 0, st, a, out);
-    else hipLaunchKernelGGL((k_stats<64, false>), grid, block, 0, st, a, out);
-  } else {
-    if (is_v) hipLaunchKernelGGL((k_stats<128, true>), grid, block, 0, st, a, out);
-    else hipLaunchKernelGGL((k_stats<128, false>), grid, block, 0, st, a, out);
+  const int sel = (B == 64 ? 0 : 4) + (is_v ? 2 : 0) + (a.bits > 4 ? 1 : 0);
+  switch (sel) {
+#define PACKKV_STATS(S, BB, V, W) \
+    case S: hipLaunchKernelGGL((k_stats<BB, V, W>), grid, block, 0, st, a, out); break;
+    PACKKV_STATS(0, 64, false, false) PACKKV_STATS(1, 64, false, true) PACKKV_STATS(2, 64, true, false)
+    PACKKV_STATS(3, 64, true, true) PACKKV_STATS(4, 128, false, false) PACKKV_STATS(5, 128, false, true)
+    PACKKV_STATS(6, 128, true, false) PACKKV_STATS(7, 128, true, true)
+#undef PACKKV_STATS
   }
   return hipGetLastError();
 }

@@ -12,11 +12,12 @@
  *
  * Packed format (one record per block of B tokens of one stream; integers
  * little-endian):
- *   K record: scale[D] fp16 | zero[D] fp16 | hdr[nr][D] u8 | 0-pad to 16 B |
+ *   K record: scale[D] fp16 | zero[D] fp16 | hdr[nr][D] | 0-pad to 16 B |
  *             payload | 0-pad to 16 B
  *   V record: scale[B] fp16 | zero[B] fp16 (slot order, 0 past n) |
- *             hdr[nr][D] u8 | 0-pad to 16 B | payload | 0-pad to 16 B
- *   nr = ceil(n / R) runs of R = 32 slots; hdr = (w << 4) | m for the run's
+ *             hdr[nr][D] | 0-pad to 16 B | payload | 0-pad to 16 B
+ *   nr = ceil(n / R) runs of R = 32 slots; hdr = the byte (w << 4) | m for
+ *   b <= 4, the little-endian u16 (w << 8) | m for b = 5..8, for the run's
  *   width w = bit_length(max - min) and minimum m; payload = for each run r,
  *   for each channel c, w u32 words holding u = q - m of slot i in bits
  *   [i*w, i*w + w).  Quantisation: K per channel over the block's tokens, V
@@ -70,7 +71,7 @@ enum {
 /* Format parameters. */
 typedef struct {
   int32_t head_dim;     /* D: must be 128                                    */
-  int32_t bits;         /* b: 2, 3 or 4                                      */
+  int32_t bits;         /* b: 2 .. 8 (5..8: two-byte header entries)         */
   int32_t block_tokens; /* B: 64 or 128                                      */
   int32_t run_tokens;   /* R: must be 32                                     */
   int32_t permute;      /* token order inside blocks (Fig. 2 caption, step   */
@@ -277,8 +278,9 @@ int packkv_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* st
  * packkv_stats - width histogram and byte counts of the cache, into device
  * memory out[32] (uint64): out[0..4] K runs with w = 0..4, out[5..9] the
  * same for V, out[10] K record bytes, out[11] V record bytes, out[12] K
- * payload words, out[13] V payload words, out[14] K runs, out[15] V runs.
- * out must be zeroed by the caller.
+ * payload words, out[13] V payload words, out[14] K runs, out[15] V runs,
+ * out[16..19] K runs with w = 5..8, out[20..23] the same for V (zero for
+ * b <= 4).  out must be zeroed by the caller.
  */
 int packkv_stats(const packkv_cache_t* cache, uint64_t* out, void* stream);
 

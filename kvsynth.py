@@ -84,6 +84,8 @@ WORKLOADS: Dict[str, Workload] = {
     # the llama7b-32k shape on clustered data (structured_kv), where the
     # token order inside a block decides the run widths
     "struct-32k": Workload("struct-32k", 8, 32, 1, 32768, 128, 4, 64, "struct"),
+    # the llama7b shape at 8 bits (two-byte run headers, byte containers)
+    "8bit-16k": Workload("8bit-16k", 8, 32, 1, 16384, 128, 8, 64, "gauss"),
 }
 
 

@@ -33,7 +33,7 @@ def cfg(bits=4, block=64, D=128, R=32, permute=1):
 
 
 @pytest.mark.parametrize("bad,code", [
-    (dict(D=64), _lib.EUNSUPPORTED), (dict(bits=5), _lib.EUNSUPPORTED), (dict(bits=1), _lib.EUNSUPPORTED),
+    (dict(D=64), _lib.EUNSUPPORTED), (dict(bits=9), _lib.EUNSUPPORTED), (dict(bits=1), _lib.EUNSUPPORTED),
     (dict(block=32), _lib.EUNSUPPORTED), (dict(R=16), _lib.EUNSUPPORTED), (dict(permute=3), _lib.EINVAL),
 ])
 def test_unsupported_configs_are_rejected(lib, bad, code):
@@ -42,14 +42,15 @@ def test_unsupported_configs_are_rejected(lib, bad, code):
     assert lib.packkv_arena_stride_bytes(ctypes.byref(cfg(**bad)), 1000) == 0
 
 
-@pytest.mark.parametrize("bits,block", [(2, 64), (3, 64), (4, 64), (4, 128), (3, 128)])
+@pytest.mark.parametrize("bits,block", [(2, 64), (3, 64), (4, 64), (4, 128), (3, 128), (5, 64), (8, 128)])
 def test_sizes_follow_the_worst_case_record(lib, bits, block):
     s = _lib.Sizes()
     assert lib.packkv_cache_sizes(ctypes.byref(cfg(bits, block)), 3, 1000, ctypes.byref(s)) == 0
     nb = -(-1000 // block)
     nr = block // 32
-    krec = -(-(512 + nr * 128) // 16) * 16 + 4 * nr * 128 * bits
-    vrec = -(-(4 * block + nr * 128) // 16) * 16 + 4 * nr * 128 * bits
+    hb = 1 if bits <= 4 else 2                    # header entry bytes
+    krec = -(-(512 + hb * nr * 128) // 16) * 16 + 4 * nr * 128 * bits
+    vrec = -(-(4 * block + hb * nr * 128) // 16) * 16 + 4 * nr * 128 * bits
     assert s.max_blocks == nb
     assert s.arena_stride % 256 == 0 and s.arena_stride >= nb * max(krec, vrec) + 64
     assert s.arena_bytes == 3 * s.arena_stride

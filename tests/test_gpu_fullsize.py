@@ -68,8 +68,9 @@ def check_offsets_all_streams(c, cfg):
         assert np.all(offs[:, 0] == 0)
         sizes = np.diff(offs, axis=1)
         params = 4 * 128 if which == "K" else 4 * B
-        lo = params + nr_full * 128                        # header only (narrowest runs)
-        hi = params + nr_full * 128 + 16 + nr_full * 128 * 4 * cfg.bits
+        hdr = cfg.header_bytes * nr_full * 128             # one entry per (run, channel)
+        lo = params + hdr                                  # header only (narrowest runs)
+        hi = params + hdr + 16 + nr_full * 128 * 4 * cfg.bits
         assert np.all(sizes[:, :-1] >= lo) and np.all(sizes <= hi), f"{which} record sizes out of range"
 
 
@@ -95,7 +96,7 @@ def sampled_blocks(c, w, K, V, cfg, scores, rng):
     assert worst <= TOL, worst
 
 
-@pytest.mark.parametrize("name", ["single-head-4k", "llama7b-32k", "gqa-128k", "2bit-16k"])
+@pytest.mark.parametrize("name", ["single-head-4k", "llama7b-32k", "gqa-128k", "2bit-16k", "8bit-16k"])
 def test_fullsize_workload(torch_dev, name):
     torch, dev = torch_dev
     from decode_gemv_amd import PackedKVCache, softmax_rows

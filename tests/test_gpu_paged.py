@@ -20,6 +20,8 @@ CASES = [
     ("b3B128-struct", 3, 128, 1, "struct", 3),
     ("b2B64-mixed-sortkey", 2, 64, 2, "mixed", 5),
     ("b4B64-identity", 4, 64, 0, "struct", 1),
+    ("b8B64-gauss", 8, 64, 1, "gauss", 2),
+    ("b6B128-struct", 6, 128, 2, "struct", 3),
 ]
 
 

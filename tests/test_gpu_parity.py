@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 
 from gpu_common import say, make_kv, oracle_streams, rel_l2, worst_row_rel
-from oracle import stream as ostream, attention
+import oracle
+from oracle import stream as ostream, attention, unpack as ounpack
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-4
@@ -34,6 +35,15 @@ CASES = [
     ("b4B64-one-token", 4, 64, 1, 1, True, "gauss"),
     ("b4B64-grid", 4, 64, 2, 64, True, "grid"),
     ("b3B64-subnormal", 3, 64, 2, 100, True, "subnormal"),
+    # wide widths: two-byte header entries and byte containers
+    ("b8B64-gauss", 8, 64, 3, 200, True, "gauss"),
+    ("b5B64-struct", 5, 64, 2, 331, True, "struct"),
+    ("b6B128-mixed", 6, 128, 2, 256, True, "mixed"),
+    ("b7B64-sortkey-gauss", 7, 64, 2, 150, 2, "gauss"),
+    ("b8B128-struct", 8, 128, 2, 300, True, "struct"),
+    ("b5B64-identity-grid", 5, 64, 2, 97, False, "grid"),
+    ("b6B64-subnormal", 6, 64, 2, 100, True, "subnormal"),
+    ("b8B64-one-token", 8, 64, 1, 1, True, "gauss"),
 ]
 
 
@@ -141,9 +151,38 @@ def test_softmax_helper(torch_dev):
     assert np.all(np.abs(p.sum(1) - 1) < 1e-5)
 
 
+@pytest.mark.parametrize("bits,block,law", [(4, 64, "mixed"), (2, 128, "struct"), (8, 64, "gauss"), (6, 128, "mixed")])
+def test_stats_match_the_oracle_widths(torch_dev, bits, block, law):
+    """Width histogram, payload words, runs and record bytes of the device
+    cache equal those of the oracle's records."""
+    torch, dev = torch_dev
+    K, V = make_kv(law, 2, 3 * block + 17, block, seed=4)
+    refs = oracle_streams(K, V, bits, block, True)
+    c = gpu_cache(torch, dev, K, V, bits, block, True)
+    say("stats", bits, block, law)
+    st = c.stats()
+    assert c.check() == 0
+    cfg = oracle.Config(bits=bits, block=block)
+    for which in "KV":
+        hist = np.zeros(max(5, bits + 1), np.int64)
+        words = runs = nbytes = 0
+        for ref in refs:
+            arena, off = ref.arena(which), ref.offsets(which)
+            nbytes += int(off[-1])
+            for j in range(len(off) - 1):
+                n = ref.block_tokens(j)
+                d = ounpack.decode_record(which, arena[off[j]:off[j + 1]], n, 128, block, 32, cfg.header_bytes)
+                hist += np.bincount(d.w.ravel(), minlength=len(hist))[:len(hist)]
+                words += int(d.w.sum())
+                runs += d.w.size
+        key = which.lower()
+        assert st[f"{key}_width_hist"] == hist.tolist(), which
+        assert st[f"{key}_words"] == words and st[f"{key}_runs"] == runs and st[f"{key}_bytes"] == nbytes
+
+
 @pytest.mark.parametrize("bits,block,t0,steps,law,permute", [
     (3, 64, 60, 70, "gauss", 1), (4, 128, 0, 130, "gauss", 1), (2, 64, 64, 1, "gauss", 1),
-    (4, 64, 30, 100, "struct", 2)])
+    (4, 64, 30, 100, "struct", 2), (6, 64, 30, 70, "gauss", 1), (8, 128, 64, 65, "struct", 2)])
 def test_append_matches_one_shot(torch_dev, bits, block, t0, steps, law, permute):
     torch, dev = torch_dev
     from decode_gemv_amd import PackedKVCache
