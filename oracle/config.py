@@ -1,6 +1,6 @@
 """Format parameters of the packed cache (oracle side).
 
-Reading adopted (the pages name no sizes): head_dim D = 128, b in {2, ..., 8}
+Reading adopted (the pages name no sizes): head_dim D in {64, 128, 256}, b in {2, ..., 8}
 bits, token block B in {64, 128}, pack run R = 32 tokens with R dividing B.
 The run is the unit that gets its own width and offset; the block is the unit
 of quantisation (K), permutation and append.  A run's header entry holds its
@@ -28,7 +28,7 @@ class Config:
         assert self.block in (64, 128), "B must be 64 or 128"
         assert self.run == 32, "R must be 32"
         assert self.block % self.run == 0
-        assert self.head_dim == 128, "D must be 128"
+        assert self.head_dim in (64, 128, 256), "D must be 64, 128 or 256"
         assert int(self.permute) in (0, 1, 2), "permute must be 0, 1 or 2"
 
     @property

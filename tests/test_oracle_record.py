@@ -81,6 +81,27 @@ def test_record_roundtrip_and_layout(bits, block, n):
         assert record.pack_payload(qs, d.w, d.m, 32) == rec[p0:p0 + 4 * int(d.w.sum())]
 
 
+@pytest.mark.parametrize("D,bits,block", [(64, 4, 64), (64, 7, 128), (256, 3, 64), (256, 8, 128)])
+@pytest.mark.parametrize("n", [1, 33, 64])
+def test_other_head_dims_roundtrip_and_layout(D, bits, block, n):
+    """The record layout with D channels in place of 128: the oracle's decoder
+    and the bit-string reader agree with the quantised ints, and the size is
+    the closed form."""
+    cfg = Config(head_dim=D, bits=bits, block=block)
+    rng = np.random.default_rng([D, bits, n])
+    k = (rng.standard_normal((n, D)) * np.where(rng.random(D) < 0.3, 0.01, 1.0)).astype(np.float16)
+    v = rng.standard_normal((n, D)).astype(np.float16)
+    code = stream.encode_block(k, v, cfg)
+    hb = cfg.header_bytes
+    for kind, rec, qs in (("K", code.k_record, code.qk_slots), ("V", code.v_record, code.qv_slots)):
+        assert qs.shape == (n, D)
+        d = unpack.decode_record(kind, rec, n, D, block, 32, hb)
+        assert np.array_equal(d.q, qs) and d.w.shape == (-(-n // 32), D)
+        assert np.array_equal(bitstring_decode(kind, rec, n, D, block, 32, hb)[0], qs)
+        assert len(rec) == record.record_size(kind, d.w, D, block, hb)
+        assert len(d.scale) == (D if kind == "K" else n)
+
+
 def test_v_params_are_slot_ordered_and_zero_padded():
     cfg = Config(bits=4, block=64)
     k, v = kvsynth.structured_kv(40, 128, 64, 32, seed=2)
