@@ -53,10 +53,14 @@ __device__ __forceinline__ uint32_t spread3to4(uint32_t x) {
   uint32_t b = (a & 0x003F003Fu) | ((a & 0x0FC00FC0u) << 2);
   return (b & 0x07070707u) | ((b & 0x38383838u) << 1);
 }
+// 2-bit fields: the 8 fields of bytes 2H and 2H+1 of x.  v_perm puts the
+// two bytes in bytes 0 and 2, then two shift-or-mask steps split each byte
+// into its nibbles and each nibble into its two fields.
+template <int H>
 __device__ __forceinline__ uint32_t spread2to4(uint32_t x) {
-  uint32_t a = (x & 0xFFu) | ((x & 0xFF00u) << 8);
-  uint32_t b = (a & 0x000F000Fu) | ((a & 0x00F000F0u) << 4);
-  return (b & 0x03030303u) | ((b & 0x0C0C0C0Cu) << 2);
+  const uint32_t a = __builtin_amdgcn_perm(0u, x, H ? 0x0c030c02u : 0x0c010c00u);
+  const uint32_t b = (a | (a << 4)) & 0x0F0F0F0Fu;
+  return (b | (b << 2)) & 0x33333333u;
 }
 __device__ __forceinline__ uint32_t spread1to4(uint32_t x) {
   uint32_t a = (x & 0xFu) | ((x & 0xF0u) << 12);
@@ -102,10 +106,10 @@ __device__ __forceinline__ void run_to_nibbles(int w, uint32_t m, const uint32_t
     out[2] = spread3to4(bits_at<48>(a, b, c, d));
     out[3] = spread3to4(bits_at<72>(a, b, c, d));
   } else if (WMAX >= 2 && w == 2) {
-    out[0] = spread2to4(a);
-    out[1] = spread2to4(a >> 16);
-    out[2] = spread2to4(b);
-    out[3] = spread2to4(b >> 16);
+    out[0] = spread2to4<0>(a);
+    out[1] = spread2to4<1>(a);
+    out[2] = spread2to4<0>(b);
+    out[3] = spread2to4<1>(b);
   } else if (w == 1) {
     out[0] = spread1to4(a);
     out[1] = spread1to4(a >> 8);
@@ -129,10 +133,10 @@ __device__ __forceinline__ void full_to_nibbles(const uint32_t wd[4], uint32_t o
     out[2] = spread3to4(bits_at<48>(wd[0], wd[1], wd[2], 0u));
     out[3] = spread3to4(bits_at<72>(wd[0], wd[1], wd[2], 0u));
   } else {
-    out[0] = spread2to4(wd[0]);
-    out[1] = spread2to4(wd[0] >> 16);
-    out[2] = spread2to4(wd[1]);
-    out[3] = spread2to4(wd[1] >> 16);
+    out[0] = spread2to4<0>(wd[0]);
+    out[1] = spread2to4<1>(wd[0]);
+    out[2] = spread2to4<0>(wd[1]);
+    out[3] = spread2to4<1>(wd[1]);
   }
 }
 
