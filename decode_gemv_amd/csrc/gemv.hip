@@ -2046,6 +2046,40 @@ static void attn_dispatch(const AttnArgs& a, int B, dim3 grid, hipStream_t st) {
     default: attn_launch<128, 8, PAGED>(a, grid, st); break;
   }
 }
+// Workgroups of the (contiguous-cache) fused attention kernel for this shape
+// that are resident on the current device at once: occupancy per compute
+// unit times the compute units; 0 if the runtime cannot say.  Asked once per
+// shape.
+template <int B, int BITS, int GT>
+static int resident_wgs_of() {
+  int per_cu = 0, dev = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_decode<B, BITS, GT, false>, 128, 0) !=
+          hipSuccess ||
+      hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return per_cu * cus;
+}
+int attention_resident_wgs(int B, int bits, int G) {
+  static int known[2][9][2];                          // [B == 128][bits class][G > 1], 0 = not asked yet
+  const int cb = class_bits_or_narrow(bits), b1 = B == 128, g1 = G > 1;
+  int& r = known[b1][cb][g1];
+  if (r == 0) {
+    int v = 0;
+    switch ((B * 8 + cb) * 2 + g1) {
+#define PACKKV_RES(BB, BI)                                   \
+      case (BB * 8 + BI) * 2: v = resident_wgs_of<BB, BI, 1>(); break; \
+      case (BB * 8 + BI) * 2 + 1: v = resident_wgs_of<BB, BI, 4>(); break;
+      PACKKV_RES(64, 2) PACKKV_RES(64, 3) PACKKV_RES(64, 4) PACKKV_RES(64, 8)
+      PACKKV_RES(128, 2) PACKKV_RES(128, 3) PACKKV_RES(128, 4) PACKKV_RES(128, 8)
+#undef PACKKV_RES
+      default: break;
+    }
+    r = v > 0 ? v : -1;
+  }
+  return r > 0 ? r : 0;
+}
+
 hipError_t launch_attention(const AttnArgs& a, int B, int n_streams, int n_caches, hipStream_t st,
                             bool paged) {
   const dim3 grid(n_streams * a.splits, n_caches);

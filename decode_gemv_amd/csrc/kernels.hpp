@@ -132,6 +132,7 @@ hipError_t launch_qk(const GemvArgs& a, int B, int n_streams, hipStream_t st);
 hipError_t launch_pv(const GemvArgs& a, int B, int n_streams, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, int B, int n_streams, int n_caches, hipStream_t st,
                             bool paged = false);
+int attention_resident_wgs(int B, int bits, int G);
 hipError_t launch_paged_alloc(const EncArgs& a, int n_streams, int64_t n_tokens, hipStream_t st);
 hipError_t launch_paged_init(const PageAlloc& p, int32_t* lengths, int32_t* status, hipStream_t st);
 hipError_t launch_paged_release(const PageAlloc& p, const uint2* k_tab, const uint2* v_tab,
