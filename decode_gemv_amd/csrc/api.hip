@@ -64,13 +64,20 @@ static int env_int(const char* name) {
   const char* v = getenv(name);
   return v ? atoi(v) : 0;
 }
-int gemv_blocks_per_wg(int64_t n_streams, int nb, bool split_merge, int group) {
+int gemv_blocks_per_wg(int64_t n_streams, int nb, bool split_merge, int group, int bits) {
   static const int env_all = env_int("PACKKV_BLOCKS_PER_WG");
   static const int env_qk = env_int("PACKKV_QK_BLOCKS_PER_WG");
   int64_t j;
   if (!split_merge && env_qk > 0) j = env_qk;
   else if (env_all > 0) j = env_all;
-  else if (!split_merge) j = 2;
+  else if (!split_merge) {
+    // K GEMV (no merge): short workgroups keep many blocks in flight; at 2
+    // bits, where the decode is the heaviest per byte, 4 blocks repay the
+    // per-workgroup set-up.  Measured (K GEMV, A/B in one process): 2 bits
+    // 127.7 -> 123.9 us with 4 blocks; at 4 and 8 bits 4 blocks are 2-4 %
+    // slower, and with four queries 8 blocks are no faster
+    j = bits == 2 && group == 1 ? 4 : 2;
+  }
   else {
     j = (n_streams * (int64_t)nb + 7679) / 7680;
     j += j & 1;
@@ -115,7 +122,7 @@ GemvArgs gemv_args(const packkv_cache_t* c, bool is_v, int group = 1) {
   a.n_tokens = c->n_tokens;
   a.nb = (int)((c->n_tokens + c->cfg.block_tokens - 1) / c->cfg.block_tokens);
   a.bits = c->cfg.bits;
-  a.blocks_per_wg = gemv_blocks_per_wg(c->n_streams, a.nb, is_v, group);
+  a.blocks_per_wg = gemv_blocks_per_wg(c->n_streams, a.nb, is_v, group, c->cfg.bits);
   a.splits = (a.nb + a.blocks_per_wg - 1) / a.blocks_per_wg;
   a.status = c->status;
   return a;
@@ -619,7 +626,7 @@ int packkv_paged_attention(const packkv_paged_t* c, const void* q_f16, int32_t g
   // the launch is sized for the longest stream; every stream spreads its
   // own blocks evenly over the same splits (at most J each)
   const int nb = (int)((longest + B - 1) / B);
-  const int J = gemv_blocks_per_wg(c->n_streams, nb, true, group);
+  const int J = gemv_blocks_per_wg(c->n_streams, nb, true, group, c->cfg.bits);
   AttnArgs a;
   memset(&a, 0, sizeof(a));
   a.cache[0] = AttnCache{c->pool, c->pool, nullptr, nullptr, c->status,
