@@ -243,6 +243,32 @@ def test_corrupt_header_is_reported_not_used(torch_dev):
     assert c.check() == 0               # the latch was cleared
 
 
+@pytest.mark.parametrize("entry", [(7, None), (6, 40)], ids=["width-above-b", "minimum-leaves-no-room"])
+def test_corrupt_wide_header_is_reported_not_used(torch_dev, entry):
+    """b = 6 (two-byte entries): a width above b, or a minimum that leaves no
+    room for its width (m + 2^(w-1) > 2^b - 1), latches ECORRUPT; the K
+    GEMV writes nothing for that block and fused attention reports it."""
+    torch, dev = torch_dev
+    from decode_gemv_amd import _lib
+    K, V = make_kv("gauss", 1, 128, 64)
+    c = gpu_cache(torch, dev, K, V, 6, 64, True)
+    w, m = entry
+    arena = c.arena("K")
+    arena[0, 512 + 2 * 5 + 1] = w                 # entry 5 of block 0: high byte w
+    if m is not None:
+        arena[0, 512 + 2 * 5] = m                 # low byte m
+    q = torch.ones(1, 1, 128, dtype=torch.float16, device=dev)
+    sc = torch.full((1, 1, 128), float("nan"), device=dev)
+    say("corrupt wide header", w, m)
+    c.qk(q, sc)
+    assert c.check() == _lib.ECORRUPT
+    s = sc.cpu().numpy()
+    assert np.all(np.isnan(s[0, 0, :64])) and np.all(np.isfinite(s[0, 0, 64:]))
+    c.attention(q)
+    assert c.check() == _lib.ECORRUPT
+    assert c.check() == 0
+
+
 @pytest.mark.parametrize("law", ["uniform", "one-hot", "peaked", "sparse-blocks", "wide-range"])
 def test_pv_weight_laws(torch_dev, law):
     """V GEMV precision across weight distributions (fp64 oracle, rel-L2 <= 1e-4)."""
