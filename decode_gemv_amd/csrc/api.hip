@@ -72,11 +72,12 @@ int gemv_blocks_per_wg(int64_t n_streams, int nb, bool split_merge, int group, i
   else if (env_all > 0) j = env_all;
   else if (!split_merge) {
     // K GEMV (no merge): short workgroups keep many blocks in flight; at 2
-    // bits, where the decode is the heaviest per byte, 4 blocks repay the
-    // per-workgroup set-up.  Measured (K GEMV, A/B in one process): 2 bits
-    // 127.7 -> 123.9 us with 4 blocks; at 4 and 8 bits 4 blocks are 2-4 %
-    // slower, and with four queries 8 blocks are no faster
-    j = bits == 2 && group == 1 ? 4 : 2;
+    // and 3 bits, where the decode is the heaviest per byte, 4 blocks repay
+    // the per-workgroup set-up.  Measured (K GEMV): 2 bits 127.7 -> 123.9 us
+    // and 3 bits (append-64k) 258.9 -> 252.8 us (A/B in one process); at 4 and
+    // 8 bits 4 blocks are 2-4 % slower, and with four queries 8 blocks are
+    // no faster
+    j = bits <= 3 && group == 1 ? 4 : 2;
   }
   else {
     j = (n_streams * (int64_t)nb + 7679) / 7680;
