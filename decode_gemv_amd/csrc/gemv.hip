@@ -22,6 +22,7 @@
 // Integers become floats through v_cvt_pk_f32_fp8 (two per instruction): a
 // byte n <= 15 read as an fp8 e4m3 number is exactly n * c for a power of two
 // c, and 1/c is folded into the dense operand.
+#include <atomic>
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -2061,9 +2062,12 @@ static int resident_wgs_of() {
   return per_cu * cus;
 }
 int attention_resident_wgs(int B, int bits, int G) {
-  static int known[2][9][2];                          // [B == 128][bits class][G > 1], 0 = not asked yet
+  // [B == 128][bits class][G > 1]: 0 = not asked yet, -1 = unknown.  Host
+  // threads may race to fill an entry; they store the same value.
+  static std::atomic<int> known[2][9][2];
   const int cb = class_bits_or_narrow(bits), b1 = B == 128, g1 = G > 1;
-  int& r = known[b1][cb][g1];
+  std::atomic<int>& slot = known[b1][cb][g1];
+  int r = slot.load(std::memory_order_relaxed);
   if (r == 0) {
     int v = 0;
     switch ((B * 8 + cb) * 2 + g1) {
@@ -2076,6 +2080,7 @@ int attention_resident_wgs(int B, int bits, int G) {
       default: break;
     }
     r = v > 0 ? v : -1;
+    slot.store(r, std::memory_order_relaxed);
   }
   return r > 0 ? r : 0;
 }
