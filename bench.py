@@ -542,7 +542,7 @@ def main():
                              "stream lengths spread linearly from T to T/4")
         del paged
 
-    # the box's streaming-read ceiling, measured like the fused launch: the
+    # the device's streaming-read ceiling, measured like the fused launch: the
     # library's read probe over as many bytes as one launch reads, averaged
     # over back-to-back launches
     from decode_gemv_amd import stream_read

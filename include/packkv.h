@@ -268,7 +268,7 @@ int packkv_check(const packkv_cache_t* cache, void* stream);
  * word sink[w] (sink holds 4096 words; the words of workgroups the launch
  * does not use are left untouched, so the XOR of a zero-filled sink is the
  * XOR of the whole buffer).  Timed over as many bytes as a decode launch
- * reads, it is the streaming-read ceiling of the box that the kernels'
+ * reads, it is the streaming-read ceiling of the device that the kernels'
  * bandwidth is compared with.  EINVAL if buf or sink is null, buf is not
  * 16-byte aligned, or bytes is not a positive multiple of 16.
  */
