@@ -12,10 +12,17 @@ The caches are prefilled (bulk compress) before the timed region, so every
 input is resident in HBM when timing starts.
 
 value = compressed bytes the step reads (K and V records plus their offset
-tables) / wall time per step, in GB/s (1e9 B/s).  The per-kernel split, each
-GEMV's effective bandwidth, the roofline of the dominant kernel (bytes per
-launch over its HIP-event duration) and the oracle's CPU throughput are
-reported beside.
+tables) / time per step, in GB/s (1e9 B/s).  Each step is timed with HIP
+events on the launch stream; before every step a 512 MiB write evicts the
+device's 256 MB memory-side cache (MALL), outside the step's events, so no
+step reads records a previous one left cached.  The per-kernel split (event
+medians and means), each GEMV's effective bandwidth, the roofline of the
+dominant kernel (bytes per launch over its mean HIP-event duration), the
+compression ratios (ideal, physical, full, and plain b-bit quantisation) and
+the oracle's CPU throughput are reported beside.
+
+The default workload is append-64k, the largest: 256 streams of 65536
+tokens at 3 bits, one appended token per stream and step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -91,10 +98,53 @@ def cpu_baseline(w: kvsynth.Workload, n_streams: int, n_steps: int, permute: int
                 attention.pv(p, vh)
                 nbytes += len(c.arena("K")) + len(c.arena("V")) + 2 * 4 * (len(c.blocks) + 1)
         dt = time.perf_counter() - t0
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle", "host": host_cpu(),
             "sample": f"{n_streams} of {w.streams} streams at {w.tokens}+ tokens, {n_steps} decode steps each "
                       f"(tail re-encode, unpack, fp64 dequantise, K GEMV, softmax, V GEMV), {dt:.1f} s of "
                       f"single-threaded CPU time; value = compressed bytes (records + offsets) decoded per second"}
+
+
+def compression_ratios(st: dict, S: int, T: int, D: int, bits: int, nb: int) -> dict:
+    """Compression ratios of the cache after prefill, from the library's
+    width statistics: fp16 bytes over compressed bytes, counted three ways
+    (ideal: payload bits + header bits + fp16 parameters; physical: the stored
+    records, padding included; full: physical plus the one-byte-per-token
+    permutation), next to plain b-bit quantisation with the same parameters
+    (T*D*b bits + parameters), and PackKV's gain over it (CR / CR_plain - 1)."""
+    raw = 16 * S * T * D
+    hb = 1 if bits <= 4 else 2
+    res = {}
+    for side, params in (("k", 32 * D * nb * S), ("v", 32 * T * S)):
+        ideal = 32 * st[f"{side}_words"] + 8 * hb * st[f"{side}_runs"] + params
+        phys = 8 * st[f"{side}_bytes"]
+        full = phys + 8 * S * T
+        plain = S * T * D * bits + params
+        res[side] = {"ideal": round(raw / ideal, 4), "physical": round(raw / phys, 4), "full": round(raw / full, 4),
+                     "plain_quant": round(raw / plain, 4),
+                     "pct_vs_plain_quant": {k: round(100 * (raw / b_ / (raw / plain) - 1), 2)
+                                            for k, b_ in (("ideal", ideal), ("physical", phys), ("full", full))}}
+    res["note"] = ("fp16 bytes / compressed bytes at the prefill length; pct_vs_plain_quant = CR / CR of plain "
+                   "b-bit quantisation - 1 (the pages' 'higher memory reduction' is stated against "
+                   "quantisation baselines); negative on data without token structure, where the run "
+                   "headers cost more than the narrower runs save")
+    return res
+
+
+def host_cpu() -> dict:
+    """The host the oracle runs on: CPU model, logical CPUs, CPUs this process may use."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except Exception:
+        usable = None
+    return {"cpu_model": model, "cpu_count": os.cpu_count(), "cpus_usable": usable}
 
 
 def load_traffic(workload: str):
@@ -237,9 +287,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama7b-32k", choices=sorted(kvsynth.WORKLOADS))
+    ap.add_argument("--workload", default="append-64k", choices=sorted(kvsynth.WORKLOADS))
     ap.add_argument("--cpu-streams", type=int, default=4, help="streams in the oracle's timed sample")
-    ap.add_argument("--cpu-steps", type=int, default=30, help="decode steps per sampled stream")
+    ap.add_argument("--cpu-steps", type=int, default=None,
+                    help="decode steps per sampled stream (default: about 12 s of oracle work)")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="bytes written before every timed step to evict the memory-side cache (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache measurement")
     ap.add_argument("--page-kib", type=int, default=64, help="page size of the paged cache")
@@ -318,10 +371,10 @@ def main():
         nb = -(-cache.n_tokens // w.block)
         return int(ko[:, nb].sum()), int(vo[:, nb].sum()), nb
 
-    kb0, vb0, _ = used_bytes()
+    kb0, vb0, nb0 = used_bytes()
     st = cache.stats()
-    raw = 2 * S * T0 * D
-    log(f"prefill {prefill_s * 1e3:.1f} ms; CR K {raw / kb0:.3f} V {raw / vb0:.3f}")
+    cr = compression_ratios(st, S, T0, D, w.bits, nb0)
+    log(f"prefill {prefill_s * 1e3:.1f} ms; CR (physical) K {cr['k']['physical']:.3f} V {cr['v']['physical']:.3f}")
 
     # per-step inputs, generated before timing
     kn = torch.empty((n_steps, S, 1, D), dtype=torch.float16)
@@ -344,8 +397,18 @@ def main():
         if code:
             raise RuntimeError(f"cache status {code} after {where}")
 
+    # a write of twice the 256 MB memory-side cache before every step (outside
+    # the step's events), so no step finds records a previous one left there
+    flush_buf = torch.empty(max(args.flush_mib, 1) << 20, dtype=torch.uint8, device=dev)
+
+    def flush(i):
+        if args.flush_mib > 0:
+            flush_buf.fill_(i & 0xFF)
+
     def timed_loop(launch, n_ev):
-        """W untimed + K timed steps; returns (ms per step, per-step HIP events)."""
+        """W untimed + K timed steps, each after a cache flush.  Returns (mean
+        and median ms per step from the HIP events around each step, wall ms
+        per step over the K steps with their flushes, per-step events)."""
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(n_steps)]
         torch.cuda.synchronize()
         t0 = None
@@ -353,14 +416,20 @@ def main():
             if i == args.warmup:
                 torch.cuda.synchronize()
                 t0 = time.perf_counter()
+            flush(i)
             launch(i, ev[i])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         status_ok(launch.__name__)
-        return wall / args.steps * 1e3, ev[args.warmup:]
+        evs = ev[args.warmup:]
+        per = [x[0].elapsed_time(x[-1]) for x in evs]
+        return float(np.mean(per)), float(np.median(per)), wall / args.steps * 1e3, evs
 
     def avg_ms(evs, a, b):
         return float(np.mean([x[a].elapsed_time(x[b]) for x in evs]))
+
+    def med_ms(evs, a, b):
+        return float(np.median([x[a].elapsed_time(x[b]) for x in evs]))
 
     # the step: append one token per stream, then decode attention in one
     # launch (K GEMV, softmax and V GEMV fused)
@@ -425,9 +494,10 @@ def main():
         del layer_caches[1:], wsm, ws1, outm, qm
         torch.cuda.empty_cache()
 
-    ms_step, fev = timed_loop(fused_step, 3)
+    ms_step, ms_step_med, wall_step, fev = timed_loop(fused_step, 3)
     kb1, vb1, nb1 = used_bytes()
     t_app, t_attn = avg_ms(fev, 0, 1), avg_ms(fev, 1, 2)
+    m_app, m_attn = med_ms(fev, 0, 1), med_ms(fev, 1, 2)
 
     # the same steps with the three kernels of the path launched separately
     # (scores and weights go through HBM); the appends continue the cache
@@ -442,9 +512,10 @@ def main():
         cache.pv(p, out, workspace=ws)
         e[4].record()
 
-    sep_ms_step, sev = timed_loop(separate_step, 5)
+    sep_ms_step, _, _, sev = timed_loop(separate_step, 5)
     kb2, vb2, nb2 = used_bytes()
     t_qk, t_sm, t_pv = avg_ms(sev, 1, 2), avg_ms(sev, 2, 3), avg_ms(sev, 3, 4)
+    m_qk, m_sm, m_pv = med_ms(sev, 1, 2), med_ms(sev, 2, 3), med_ms(sev, 3, 4)
 
     # compressed bytes read per step (records + offset tables), mean over each loop
     k_bytes = (kb0 + kb1) / 2 + 4 * S * (nb1 + 1)
@@ -469,7 +540,9 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
                 "traffic": tr.get("attn") if tr else None,
-                "kernel": "k_attn_decode", "bytes_per_launch": int(attn_alg), "launch_ms": round(t_attn, 4)}
+                "kernel": "k_attn_decode", "bytes_per_launch": int(attn_alg), "launch_ms": round(t_attn, 4),
+                "launch_ms_median": round(m_attn, 4),
+                "frac_at_median": round(attn_alg / (m_attn * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
     # the step on the paged caches: append, then fused attention through the
     # block tables
@@ -496,6 +569,7 @@ def main():
                 if i == args.warmup:
                     torch.cuda.synchronize()
                     t0 = time.perf_counter()
+                flush(i)
                 ev[i][0].record()
                 pc.append(kn[i], vn[i])
                 ev[i][1].record()
@@ -574,26 +648,42 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
-        cpu = cpu_baseline(w, args.cpu_streams, args.cpu_steps, args.permute)
+        # about 12 s of single-threaded oracle work: one decode step of a
+        # stream costs the oracle ~3 us per cached token
+        steps = args.cpu_steps or max(3, int(12.0 / (args.cpu_streams * 3e-6 * T0)))
+        cpu = cpu_baseline(w, args.cpu_streams, steps, args.permute)
 
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32 acc; V weights 20-bit fixed point x u4/u8 ints",
+        "arithmetic": ("K GEMV: fp32 FMA of q*scale with the exact 4-bit containers (one query per "
+                       "stream) or int8 matrix cores on q*scale in 24-bit fixed point (four queries); "
+                       "V GEMV: weights*scale in 20-bit fixed point per block times the ints by integer "
+                       "dot products (v_dot8 / v_dot4 / int8 matrix cores), exact integer sums, fp32 "
+                       "accumulation; softmax fp32; encoder fp64 (bit-exact with the oracle)"),
         "data": "synthetic (seeded kvsynth generator; stands in for the pages' models and benchmarks)",
         "config": {"workload": w.key, "batch": w.batch, "kv_heads": w.kv_heads, "group": G,
                    "tokens": T0, "head_dim": D, "bits": w.bits, "block": w.block, "run": 32,
                    "append_per_step": 1, "permute": args.permute, "parallelism": "single-gpu"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "kernels_ms": {"append": round(t_app, 4), "attention": round(t_attn, 4), "qk_gemv": round(t_qk, 4),
-                       "softmax": round(t_sm, 4), "pv_gemv": round(t_pv, 4)},
+        "ms_per_step_median": round(ms_step_med, 4),
+        "wall_ms_per_step": round(wall_step, 4),
+        "kernels_ms": {"append": round(m_app, 4), "attention": round(m_attn, 4), "qk_gemv": round(m_qk, 4),
+                       "softmax": round(m_sm, 4), "pv_gemv": round(m_pv, 4), "stat": "median"},
+        "kernels_ms_mean": {"append": round(t_app, 4), "attention": round(t_attn, 4), "qk_gemv": round(t_qk, 4),
+                            "softmax": round(t_sm, 4), "pv_gemv": round(t_pv, 4)},
+        "timing": (f"HIP events on the launch stream around each step and kernel; a {args.flush_mib} MiB "
+                   "write before every step evicts the memory-side cache (not timed); ms_per_step and "
+                   "value from the mean step time, wall_ms_per_step includes the flushes"),
         "kernel_GBps": {"attention": round(attn_gbps, 1), "qk_gemv": round(qk_gbps, 1),
                         "pv_gemv": round(pv_gbps, 1)},
         "gemv_effective_GBps": {"qk": round(k_bytes2 / (t_qk * 1e-3) / 1e9, 1),
                                 "pv": round(v_bytes2 / (t_pv * 1e-3) / 1e9, 1)},
         "separate_path": {"ms_per_step": round(sep_ms_step, 4), "value": round(sep_value, 1),
                           "note": "append, K GEMV, softmax, V GEMV as four launches"},
-        "cr": {"k": round(2 * S * T0 * D / kb0, 4), "v": round(2 * S * T0 * D / vb0, 4)},
+        "cr": cr,
         "width_hist": {"k": st["k_width_hist"], "v": st["v_width_hist"]},
         "prefill_ms": round(prefill_s * 1e3, 2),
         "roofline": roofline,

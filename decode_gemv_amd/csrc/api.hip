@@ -1,7 +1,6 @@
 // C ABI of the packkv library: argument validation, work decomposition and
 // kernel launches on the caller's stream.  No device memory is allocated
 // here; every buffer belongs to the caller.
-#include <stdlib.h>
 #include <string.h>
 
 #include <cmath>
@@ -52,25 +51,16 @@ int check_cache(const packkv_cache_t* c) {
   return PACKKV_OK;
 }
 
-// Blocks per workgroup for the GEMVs: enough workgroups to fill 256 CUs
-// several times over, at most 64 blocks each.
 // Blocks per workgroup.  The V GEMV and fused attention keep about two
 // rounds of one-wave workgroups over the chip's resident slots (16 per CU):
 // their workgroups end with a partial sum that the last one of the stream
 // merges, so fewer, longer workgroups pay less for it.  The K GEMV has no
 // merge and is fastest with many short workgroups (better balance at the
-// kernel's end).  Always even: the GEMVs take blocks in pairs.
-static int env_int(const char* name) {
-  const char* v = getenv(name);
-  return v ? atoi(v) : 0;
-}
+// kernel's end).  Always even, at most 64.  The division depends only on the
+// cache's shape, so results are the same from run to run.
 int gemv_blocks_per_wg(int64_t n_streams, int nb, bool split_merge, int group, int bits) {
-  static const int env_all = env_int("PACKKV_BLOCKS_PER_WG");
-  static const int env_qk = env_int("PACKKV_QK_BLOCKS_PER_WG");
   int64_t j;
-  if (!split_merge && env_qk > 0) j = env_qk;
-  else if (env_all > 0) j = env_all;
-  else if (!split_merge) {
+  if (!split_merge) {
     // K GEMV (no merge): short workgroups keep many blocks in flight; at 2
     // and 3 bits, where the decode is the heaviest per byte, 4 blocks repay
     // the per-workgroup set-up.  Measured (K GEMV): 2 bits 127.7 -> 123.9 us
@@ -226,6 +216,7 @@ int packkv_append_tokens(packkv_cache_t* c, const void* k_f16, const void* v_f16
   int e = check_cache(c);
   if (e) return e;
   if (!k_f16 || !v_f16 || n_new < 1) return PACKKV_EINVAL;
+  if (((uintptr_t)k_f16 | (uintptr_t)v_f16) & 15u) return PACKKV_EINVAL;   // read with 16-byte loads
   if (c->n_tokens + n_new > c->max_tokens) return PACKKV_ECAPACITY;
   hipStream_t st = (hipStream_t)stream;
   const int B = c->cfg.block_tokens;
@@ -331,13 +322,6 @@ static int attention_decode(const packkv_cache_t* const* cs, int32_t n, const vo
   a.blocks_per_wg = g.blocks_per_wg;
   a.splits = attention_splits((int64_t)c->n_streams * (n < kAttnMaxCaches ? n : kAttnMaxCaches), g.splits, g.nb,
                               c->cfg.block_tokens, c->cfg.bits, group);
-  {
-    static const int env_splits = env_int("PACKKV_ATTN_SPLITS");
-    if (env_splits > 0) {
-      const int lo = (a.nb + 63) / 64, hi = (a.nb + 3) / 4;
-      a.splits = env_splits < lo ? lo : (env_splits > hi ? hi : env_splits);
-    }
-  }
   a.G = group;
   a.scale_log2e = scale * 1.4426950408889634f;
   a.qo_stride = (int64_t)c->n_streams * group * kD;

@@ -199,10 +199,15 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
     }
   }
   __syncthreads();
+  // an infinite or NaN input (exponent field all ones) is outside the
+  // method: it latches EINVAL; the records stay well-formed
+  bool nonfinite = false;
   if (tid < kD) {
     int kmin = 0x7FFF, kmax = -0x7FFF;
     for (int t = 0; t < n; ++t) {
-      const int k = f16_key(rawk[t * kD + tid]);
+      const uint32_t x = rawk[t * kD + tid];
+      nonfinite |= (x & 0x7C00u) == 0x7C00u;
+      const int k = f16_key(x);
       kmin = min(kmin, k);
       kmax = max(kmax, k);
     }
@@ -237,6 +242,7 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       if (i < CPT / 2) {
+        nonfinite |= on && (((w[i] & 0x7C00u) == 0x7C00u) || ((w[i] & 0x7C000000u) == 0x7C000000u));
         const int a0 = f16_key(w[i] & 0xFFFFu), a1 = f16_key(w[i] >> 16);
         kmin = min(kmin, min(a0, a1));
         kmax = max(kmax, max(a0, a1));
@@ -262,6 +268,7 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
       }
     }
   }
+  if (__ballot(nonfinite) != 0 && (tid & 63) == 0) latch(a.status, PACKKV_EINVAL);
   if (tid < 128) ident[tid] = (uint8_t)tid;
   __syncthreads();
 

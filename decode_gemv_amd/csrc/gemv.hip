@@ -168,7 +168,8 @@ struct BlockDecoder {
 
   // Decode the lane's runs of the staged record into container words
   // nib[k][0..3] (run l + 64k).  Returns false if the record is inconsistent
-  // (a width above BITS, or widths that do not add up to the record size).
+  // (a width above BITS, a minimum that leaves no room for its width, or
+  // widths that do not add up to the record size).
   // One code path for every block: offsets start from the full-width layout;
   // a block holding narrower runs (or a partial block) corrects them with
   // the width deficit of earlier runs, and its narrow runs are re-decoded at
@@ -200,11 +201,14 @@ struct BlockDecoder {
     uint32_t total = (uint32_t)(nruns * BITS);
     bool bad = false;
     if (!all_full) {
+      constexpr int L = (1 << BITS) - 1;
       uint32_t running = 0;                            // deficit of earlier groups
 #pragma unroll
       for (int k = 0; k < NRL; ++k) {
-        const int w = (int)(h[k] >> 4);
-        bad |= w > BITS;
+        const int w = (int)(h[k] >> 4), m = (int)(h[k] & 15u);
+        // as scan_runs: a valid run has max - m in [2^(w-1), 2^w - 1] and
+        // max <= L, so its containers m + u never carry into the next slot
+        bad |= w > BITS || m > L || (w > 0 && m + (1 << (w - 1)) > L);
         const int d = (lane + 64 * k) < nruns ? BITS - w : 0;
         off[k] -= running;
         if (__ballot(d != 0) != 0) {
@@ -1481,7 +1485,7 @@ void k_pv_gemv(GemvArgs a) {
   VB vb;
   vb.init(dig, lane);
   if constexpr (BITS > 4) vb.bits = a.bits;
-  bool corrupt = false;
+  bool corrupt = false, invalid = false;
 
   for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
     float acc[GT][2];
@@ -1521,11 +1525,20 @@ void k_pv_gemv(GemvArgs a) {
       for (int g = 0; g < GT; ++g)
 #pragma unroll
         for (int h = 0; h < NH; ++h) pw[g][h] = pv[g][h];
+      // the fixed-point weights need p >= 0 and finite (softmax weights); a
+      // block holding any other weight takes no part and latches EINVAL
+      bool badp = false;
+#pragma unroll
+      for (int g = 0; g < GT; ++g)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) badp |= !(pw[g][h] >= 0.f && pw[g][h] <= __FLT_MAX__);
+      const bool pok = __ballot(badp) == 0;
+      invalid |= !pok;
       request(jj + 1, pre, pv);
       __builtin_amdgcn_sched_barrier(0);
       wave_sync();
-      const bool ok = vb.run(rec, size, (n + kR - 1) / kR, rok, pw, acc, pz);
-      corrupt |= rok && !ok;
+      const bool ok = vb.run(rec, size, (n + kR - 1) / kR, rok && pok, pw, acc, pz);
+      corrupt |= rok && pok && !ok;
     };
     // one record (and its weights) in flight
     u32x4 pre[NCH];
@@ -1541,6 +1554,7 @@ void k_pv_gemv(GemvArgs a) {
     });
   }
   if (corrupt && lane == 0) latch(a.status, PACKKV_ECORRUPT);
+  if (invalid && lane == 0) latch(a.status, PACKKV_EINVAL);
   if (!last_to_arrive(&a.tickets[s], a.splits, lane)) return;
   for (int g = 0; g < a.G; ++g) {
     const float* src = a.ws + ((int64_t)s * a.G + g) * a.splits * kD;

@@ -30,8 +30,11 @@
  * Conventions for every entry point
  *   - Every pointer inside packkv_cache_t and every tensor argument is DEVICE
  *     memory owned by the caller (e.g. allocated with torch on ROCm).  The
- *     library never allocates or frees device memory and keeps no global
- *     mutable state; calls on different caches are independent.
+ *     library never allocates or frees device memory, and all state of a
+ *     cache lives in the caller's buffers; calls on different caches are
+ *     independent.  The only process-wide state is a table of per-shape
+ *     occupancy figures (resident workgroups per device), asked from the
+ *     runtime once per kernel shape and read-only after that.
  *   - `stream` is a hipStream_t passed as void*.  Every call only enqueues
  *     work on that stream and returns without synchronising, except
  *     packkv_check, which synchronises the stream.
@@ -60,8 +63,11 @@ extern "C" {
 /* Status codes. */
 enum {
   PACKKV_OK = 0,
-  PACKKV_EINVAL = 1,       /* bad argument (null pointer, size, stride)        */
-  PACKKV_EUNSUPPORTED = 2, /* configuration outside D=128, b 2..4, B 64/128, R 32 */
+  PACKKV_EINVAL = 1,       /* bad argument (null pointer, size, stride), or, as
+                              a device latch, an input value outside the
+                              method's domain (non-finite K/V, a V-GEMV weight
+                              that is negative or non-finite)                 */
+  PACKKV_EUNSUPPORTED = 2, /* configuration outside D 128, b 2..8, B 64/128, R 32 */
   PACKKV_ECAPACITY = 3,    /* tokens over max_tokens, or arena region overflow */
   PACKKV_ECORRUPT = 4,     /* a record header is inconsistent                  */
   PACKKV_EHIP = 5,         /* a HIP runtime call or kernel launch failed       */
@@ -140,7 +146,10 @@ uint64_t packkv_pv_workspace_bytes(const packkv_cache_t* cache, int32_t group);
  * The cache must be empty (n_tokens == 0, else PACKKV_ESTATE) and
  * 1 <= n_tokens <= max_tokens (else EINVAL / ECAPACITY).  Writes every
  * record, k_off/v_off[0 .. nb], perm, and the raw tail staging (the last,
- * partial block's tokens).  Sets cache->n_tokens on success.
+ * partial block's tokens).  Sets cache->n_tokens on success.  An infinite
+ * or NaN input value latches PACKKV_EINVAL in *status (the method quantises
+ * finite values only); the records stay well-formed, with unspecified
+ * contents for the blocks holding such values.
  */
 int packkv_compress_block(packkv_cache_t* cache, const void* k_f16, const void* v_f16,
                           int64_t n_tokens, void* stream);
@@ -151,9 +160,11 @@ int packkv_compress_block(packkv_cache_t* cache, const void* k_f16, const void* 
  * The open tail block is kept as raw fp16 and re-encoded in full on every
  * call; closed blocks never change, so appending gives exactly the bytes a
  * one-shot compress of all tokens gives.
- *   k_f16, v_f16: device fp16 [S][n_new][D].
+ *   k_f16, v_f16: device fp16 [S][n_new][D], contiguous, 16-byte aligned
+ *                 (else PACKKV_EINVAL).
  * n_new >= 1 and n_tokens + n_new <= max_tokens (else EINVAL / ECAPACITY).
- * Updates cache->n_tokens on success.
+ * Updates cache->n_tokens on success.  Non-finite values latch EINVAL as in
+ * packkv_compress_block.
  */
 int packkv_append_tokens(packkv_cache_t* cache, const void* k_f16, const void* v_f16,
                          int32_t n_new, void* stream);
@@ -172,7 +183,11 @@ int packkv_qk_gemv(const packkv_cache_t* cache, const void* q_f16, int32_t group
 /*
  * packkv_pv_gemv - fused V decompress + GEMV with a split-T partial-sum
  * reduction in a fixed order (Fig. 1 caption: weighted V vectors summed).
- *   p:         device fp32 [S][group][ld], slot order (as scores).
+ *   p:         device fp32 [S][group][ld], slot order (as scores); every
+ *              weight >= 0 and finite (softmax weights: the V block code
+ *              turns them into fixed point relative to each block's largest
+ *              weight).  A block holding any other weight contributes
+ *              nothing and latches PACKKV_EINVAL in *status.
  *   out:       device fp32 [S][group][D]; out[s][g][c] =
  *              sum_t p[s][g][t] * V_hat[s][t][c].
  *   workspace: device memory of at least packkv_pv_workspace_bytes(cache,
@@ -239,7 +254,10 @@ int packkv_attention_decode_multi(const packkv_cache_t* const* caches, int32_t n
 uint64_t packkv_attention_multi_workspace_bytes(const packkv_cache_t* cache, int32_t group, int32_t n_caches);
 
 /*
- * packkv_decompress - decode the cache (test and debug path).
+ * packkv_decompress - decode the cache.  Not a step of the method (the
+ * pages fuse decompression into the products so that nothing decompressed
+ * is written, TL;DR); a test and debug path that writes the quantised ints
+ * or the dequantised values out so they can be compared bit for bit.
  *   which: 0 = K, 1 = V.
  *   mode 0: out is uint8 [S][n_tokens][D], the quantised ints q in SLOT order.
  *   mode 1: out is fp32 [S][n_tokens][D], x_hat = zero + scale * q rounded

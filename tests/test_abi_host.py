@@ -77,6 +77,11 @@ def test_invalid_arguments_fail_before_any_launch(lib):
     assert lib.packkv_qk_gemv(ctypes.byref(c3), fake, 1, fake, 10, None) == _lib.ESTATE
     c3.n_tokens = 50
     assert lib.packkv_compress_block(ctypes.byref(c3), fake, fake, 10, None) == _lib.ESTATE
+    # the encoder reads appended tokens with 16-byte loads: misaligned input
+    # is refused before any launch
+    assert lib.packkv_append_tokens(ctypes.byref(c3), fake + 2, fake, 1, None) == _lib.EINVAL
+    assert lib.packkv_append_tokens(ctypes.byref(c3), fake, fake + 8, 1, None) == _lib.EINVAL
+    assert lib.packkv_compress_block(ctypes.byref(c3), fake + 4, fake, 10, None) == _lib.EINVAL
     assert lib.packkv_qk_gemv(ctypes.byref(c3), fake, 0, fake, 50, None) == _lib.EINVAL
     assert lib.packkv_qk_gemv(ctypes.byref(c3), fake, 1, fake, 49, None) == _lib.EINVAL
     assert lib.packkv_append_tokens(ctypes.byref(c3), fake, fake, 51, None) == _lib.ECAPACITY

@@ -3,11 +3,14 @@ launch configuration bench.py times.
 
 The oracle cannot follow a whole 256-stream cache in seconds, so each test
 checks (1) one sampled stream completely - every record byte, the offsets,
-the permutation and the tail, and its K-GEMV scores and V-GEMV output within
-rel-L2 1e-4 of the fp64 oracle - and (2) one sampled block of every stream,
-re-encoded by the oracle on its own (a closed block depends only on its own
-tokens): its K and V record bytes and its scores.  Every row also has to
-satisfy what holds at any size (finite outputs, softmax rows summing to 1).
+the permutation and the tail, and its K-GEMV scores, V-GEMV output and fused
+attention within rel-L2 1e-4 of the fp64 oracle (tensor and worst row) - and
+(2) one sampled block of every stream, re-encoded by the oracle on its own (a
+closed block depends only on its own tokens): its K and V record bytes, its
+scores, and the stream's V-GEMV output for weights that are zero outside that
+block (so the output is the block's product alone).  Every row also has to
+satisfy what holds at any size (finite outputs, softmax rows summing to 1,
+fused attention equal to the separate K GEMV -> softmax -> V GEMV).
 """
 
 import concurrent.futures as cf
@@ -74,26 +77,42 @@ def check_offsets_all_streams(c, cfg):
         assert np.all(sizes[:, :-1] >= lo) and np.all(sizes <= hi), f"{which} record sizes out of range"
 
 
-def sampled_blocks(c, w, K, V, cfg, scores, rng):
-    """One random closed block per stream, re-encoded by the oracle alone."""
+def sampled_blocks(torch, dev, c, w, block_kv, cfg, scores, q, rng, closed=None):
+    """One random closed block per stream, re-encoded by the oracle alone:
+    its K and V record bytes, its scores, and the V GEMV of every stream
+    against the oracle, with weights that are zero outside the stream's
+    sampled block (the output is then that block's product alone).
+    block_kv(s, j) gives the fp16 K, V of block j of stream s; closed: the
+    blocks to sample from (default: every closed block)."""
     B = w.block
-    nb_closed = c.n_tokens // B
+    S, G, T = w.streams, w.group, c.n_tokens
+    closed = closed or range(T // B)
     ka = c.arena("K").cpu().numpy()
     va = c.arena("V").cpu().numpy()
     ko = c.offsets("K").cpu().numpy().astype(np.int64) & 0xFFFFFFFF
     vo = c.offsets("V").cpu().numpy().astype(np.int64) & 0xFFFFFFFF
-    worst = 0.0
-    for s in range(w.streams):
-        j = int(rng.integers(nb_closed))
-        code = ostream.encode_block(K[s, j * B:(j + 1) * B], V[s, j * B:(j + 1) * B], cfg)
+    pick = [int(closed[int(rng.integers(len(closed)))]) for _ in range(S)]
+    pw = rng.random((S, G, B)).astype(np.float32)
+    p = np.zeros((S, G, T), np.float32)
+    for s, j in enumerate(pick):
+        p[s, :, j * B:(j + 1) * B] = pw[s]
+    out = c.pv(torch.from_numpy(p).to(dev)).cpu().numpy()
+    assert c.check() == 0
+    worst_sc = worst_out = 0.0
+    for s, j in enumerate(pick):
+        kb, vb = block_kv(s, j)
+        code = ostream.encode_block(kb, vb, cfg)
         assert ka[s, ko[s, j]:ko[s, j + 1]].tobytes() == code.k_record, f"K record ({s}, {j})"
         assert va[s, vo[s, j]:vo[s, j + 1]].tobytes() == code.v_record, f"V record ({s}, {j})"
-        one = ostream.StreamCache(cfg, [code], B, K[s, :0], V[s, :0])
-        kh = ostream.decode_stream(one)[0]
-        q = kvsynth.stream_q(w, s)
-        ref = attention.qk(q, kh)
-        worst = max(worst, rel_l2(scores[s, :, j * B:(j + 1) * B], ref))
-    assert worst <= TOL, worst
+        one = ostream.StreamCache(cfg, [code], B, kb[:0], vb[:0])
+        kh, vh, _, _ = ostream.decode_stream(one)
+        ref = attention.qk(q[s], kh)
+        got = scores[s, :, j * B:(j + 1) * B]
+        worst_sc = max(worst_sc, rel_l2(got, ref), worst_row_rel(got, ref))
+        ref_o = attention.pv(pw[s].astype(np.float64), vh)
+        worst_out = max(worst_out, rel_l2(out[s], ref_o), worst_row_rel(out[s], ref_o))
+    assert worst_sc <= TOL, worst_sc
+    assert worst_out <= TOL, worst_out
 
 
 @pytest.mark.parametrize("name", ["single-head-4k", "llama7b-32k", "gqa-128k", "2bit-16k", "8bit-16k"])
@@ -120,24 +139,31 @@ def test_fullsize_workload(torch_dev, name):
     assert np.all(np.isfinite(scores)) and np.all(np.isfinite(out))
     assert np.all(np.abs(p.sum(-1) - 1.0) < 1e-4)
     say("fullsize sampled blocks", name)
-    sampled_blocks(c, w, K, V, cfg, scores, np.random.default_rng(7))
+    sampled_blocks(torch, dev, c, w, lambda s_, j: (K[s_, j * w.block:(j + 1) * w.block],
+                                                    V[s_, j * w.block:(j + 1) * w.block]),
+                   cfg, scores, q, np.random.default_rng(7))
     s = S - 1                                   # the stream at the far end of the arenas
     say("fullsize oracle stream", name, s)
     ref = ostream.compress(K[s], V[s], cfg)
     stream_state_equal(c, ref, s)
     kh, vh, _, _ = ostream.decode_stream(ref)
     ref_sc = attention.qk(q[s], kh)
-    assert rel_l2(scores[s], ref_sc) <= TOL, (rel_l2(scores[s], ref_sc), worst_row_rel(scores[s], ref_sc))
+    assert rel_l2(scores[s], ref_sc) <= TOL and worst_row_rel(scores[s], ref_sc) <= TOL, \
+        (rel_l2(scores[s], ref_sc), worst_row_rel(scores[s], ref_sc))
     ref_out = attention.pv(p[s].astype(np.float64), vh)
-    assert rel_l2(out[s], ref_out) <= TOL, (rel_l2(out[s], ref_out), worst_row_rel(out[s], ref_out))
+    assert rel_l2(out[s], ref_out) <= TOL and worst_row_rel(out[s], ref_out) <= TOL, \
+        (rel_l2(out[s], ref_out), worst_row_rel(out[s], ref_out))
     say("fullsize fused attention", name)
     fused = c.attention(torch.from_numpy(q).to(dev)).cpu().numpy()
     assert c.check() == 0
     assert np.all(np.isfinite(fused))
     ref_att = attention.pv(attention.softmax(ref_sc, D), vh)
-    assert rel_l2(fused[s], ref_att) <= TOL, (rel_l2(fused[s], ref_att), worst_row_rel(fused[s], ref_att))
-    # every stream: the fused path agrees with GEMV -> softmax -> GEMV
-    assert rel_l2(fused, out) <= TOL, rel_l2(fused, out)
+    assert rel_l2(fused[s], ref_att) <= TOL and worst_row_rel(fused[s], ref_att) <= TOL, \
+        (rel_l2(fused[s], ref_att), worst_row_rel(fused[s], ref_att))
+    # every stream: the fused path agrees with GEMV -> softmax -> GEMV, whose
+    # K and V products were checked on every stream above
+    assert rel_l2(fused, out) <= TOL and worst_row_rel(fused, out) <= TOL, (rel_l2(fused, out),
+                                                                           worst_row_rel(fused, out))
 
 
 def test_fullsize_streaming_append(torch_dev):
@@ -157,8 +183,12 @@ def test_fullsize_streaming_append(torch_dev):
     s = S - 1
     ref = ostream.compress(K[s], V[s], cfg)
     del K, V
+    app_k = np.empty((S, n_app, D), np.float16)
+    app_v = np.empty_like(app_k)
     for step in range(1, n_app + 1):
         new = [kvsynth.append_kv(w, i, step - 1) for i in range(S)]
+        for i, (a_, b_) in enumerate(new):
+            app_k[i, step - 1], app_v[i, step - 1] = a_[0], b_[0]
         kn = torch.from_numpy(np.stack([a for a, _ in new])).to(dev)
         vn = torch.from_numpy(np.stack([b for _, b in new])).to(dev)
         c.append(kn, vn)
@@ -179,12 +209,24 @@ def test_fullsize_streaming_append(torch_dev):
         assert np.all(np.isfinite(scores)) and np.all(np.isfinite(out))
         kh, vh, _, _ = ostream.decode_stream(ref)
         ref_sc = attention.qk(q[s], kh)
-        assert rel_l2(scores[s], ref_sc) <= TOL
-        assert rel_l2(out[s], attention.pv(p[s].astype(np.float64), vh)) <= TOL
+        ref_out = attention.pv(p[s].astype(np.float64), vh)
+        assert rel_l2(scores[s], ref_sc) <= TOL and worst_row_rel(scores[s], ref_sc) <= TOL
+        assert rel_l2(out[s], ref_out) <= TOL and worst_row_rel(out[s], ref_out) <= TOL
         fused = c.attention(torch.from_numpy(q).to(dev)).cpu().numpy()
         assert c.check() == 0
-        assert rel_l2(fused[s], attention.pv(attention.softmax(ref_sc, D), vh)) <= TOL
-        assert rel_l2(fused, out) <= TOL
+        ref_att = attention.pv(attention.softmax(ref_sc, D), vh)
+        assert rel_l2(fused[s], ref_att) <= TOL and worst_row_rel(fused[s], ref_att) <= TOL
+        assert rel_l2(fused, out) <= TOL and worst_row_rel(fused, out) <= TOL
+        if step == n_app:
+            # every stream: one block closed by the appends, re-encoded by the
+            # oracle from the appended tokens alone, with its scores and V GEMV
+            say("append sampled blocks", step)
+            B = w.block
+            j0 = T0 // B
+            sampled_blocks(torch, dev, c, w,
+                           lambda s_, j: (app_k[s_, (j - j0) * B:(j - j0 + 1) * B],
+                                          app_v[s_, (j - j0) * B:(j - j0 + 1) * B]),
+                           cfg, scores, q, np.random.default_rng(step), closed=list(range(j0, T // B)))
 
 
 def test_fullsize_paged_ragged(torch_dev):

@@ -8,7 +8,7 @@ cache bit for bit.
 import numpy as np
 import pytest
 
-from gpu_common import say, make_kv, oracle_streams, rel_l2, check_placement
+from gpu_common import say, make_kv, oracle_streams, rel_l2, worst_row_rel, check_placement
 from oracle import stream as ostream, attention
 
 pytestmark = pytest.mark.gpu
@@ -79,7 +79,8 @@ def check_attention(torch, dev, c, refs, lengths, G, seed):
             continue
         kh, vh, _, _ = ostream.decode_stream(ref)
         want = attention.pv(attention.softmax(attention.qk(q[s], kh), 128), vh)
-        assert rel_l2(got[s], want) <= TOL, (s, rel_l2(got[s], want))
+        assert rel_l2(got[s], want) <= TOL and worst_row_rel(got[s], want) <= TOL, \
+            (s, rel_l2(got[s], want), worst_row_rel(got[s], want))
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])

@@ -128,7 +128,7 @@ def test_gemvs_within_tolerance(torch_dev, case, G):
     scores = c.qk(torch.from_numpy(q).to(dev)).cpu().numpy()
     assert c.check() == 0
     ref_s = np.stack([attention.qk(q[s], ostream.decode_stream(refs[s])[0]) for s in range(S)])
-    assert rel_l2(scores, ref_s) <= TOL, (rel_l2(scores, ref_s), worst_row_rel(scores, ref_s))
+    assert rel_l2(scores, ref_s) <= TOL and worst_row_rel(scores, ref_s) <= TOL, (rel_l2(scores, ref_s), worst_row_rel(scores, ref_s))
     # p: a softmax of the oracle scores, rounded to fp32 - the same input to both sides
     p = np.stack([attention.softmax(ref_s[s], 128) for s in range(S)]).astype(np.float32)
     say("pv", cid, "G", G)
@@ -136,7 +136,7 @@ def test_gemvs_within_tolerance(torch_dev, case, G):
     assert c.check() == 0
     ref_o = np.stack([attention.pv(p[s].astype(np.float64), ostream.decode_stream(refs[s])[1])
                       for s in range(S)])
-    assert rel_l2(out, ref_o) <= TOL, (rel_l2(out, ref_o), worst_row_rel(out, ref_o))
+    assert rel_l2(out, ref_o) <= TOL and worst_row_rel(out, ref_o) <= TOL, (rel_l2(out, ref_o), worst_row_rel(out, ref_o))
 
 
 def test_softmax_helper(torch_dev):
@@ -147,7 +147,7 @@ def test_softmax_helper(torch_dev):
     say("softmax")
     p = softmax_rows(torch.from_numpy(x).to(dev), 1000, 0.125).cpu().numpy()
     ref = np.stack([attention.softmax(r.astype(np.float64) * 0.125 * np.sqrt(128), 128) for r in x])
-    assert rel_l2(p, ref) <= TOL
+    assert rel_l2(p, ref) <= TOL and worst_row_rel(p, ref) <= TOL
     assert np.all(np.abs(p.sum(1) - 1) < 1e-5)
 
 
@@ -243,6 +243,45 @@ def test_corrupt_header_is_reported_not_used(torch_dev):
     assert c.check() == 0               # the latch was cleared
 
 
+@pytest.mark.parametrize("bits,w,m", [(2, 2, 2), (2, 1, 3), (3, 3, 4), (3, 2, 9), (4, 4, 8), (4, 1, 15)],
+                         ids=["b2-w2-m2", "b2-w1-m3", "b3-w3-m4", "b3-m-above-L", "b4-w4-m8", "b4-w1-m15"])
+def test_corrupt_minimum_is_reported_not_used(torch_dev, bits, w, m):
+    """One-byte header entries whose minimum leaves no room for the width
+    (m + 2^(w-1) > 2^b - 1, or m > 2^b - 1): packkv_decompress rejects
+    them, and so do the K GEMV, the V GEMV and fused attention - each
+    latches ECORRUPT and takes nothing from that block."""
+    torch, dev = torch_dev
+    from decode_gemv_amd import _lib
+    K, V = make_kv("gauss", 1, 128, 64)
+    c = gpu_cache(torch, dev, K, V, bits, 64, True)
+    rng = np.random.default_rng(bits)
+    q = torch.from_numpy(rng.standard_normal((1, 1, 128)).astype(np.float16)).to(dev)
+    p = torch.from_numpy(rng.random((1, 1, 128)).astype(np.float32)).to(dev)
+    p0 = p.clone()
+    p0[:, :, :64] = 0.0
+    want_pv = c.pv(p0).clone()                   # block 0 weighted by zero
+    assert c.check() == 0
+    entry = (w << 4) | m
+    say("corrupt minimum", bits, w, m)
+    c.arena("K")[0, 512 + 5] = entry             # K header entry 5 of block 0
+    sc = torch.full((1, 1, 128), float("nan"), device=dev)
+    c.qk(q, sc)
+    assert c.check() == _lib.ECORRUPT
+    s = sc.cpu().numpy()
+    assert np.all(np.isnan(s[0, 0, :64])) and np.all(np.isfinite(s[0, 0, 64:]))
+    out = c.attention(q)
+    assert c.check() == _lib.ECORRUPT
+    assert torch.all(torch.isfinite(out))
+    for which, mode in (("K", 0), ("K", 1)):
+        c.decompress(which, mode)
+        assert c.check() == _lib.ECORRUPT
+    c.arena("V")[0, 256 + 5] = entry             # V header entry 5 of block 0
+    got = c.pv(p)
+    assert c.check() == _lib.ECORRUPT
+    assert torch.equal(got, want_pv)
+    assert c.check() == 0
+
+
 @pytest.mark.parametrize("entry", [(7, None), (6, 40)], ids=["width-above-b", "minimum-leaves-no-room"])
 def test_corrupt_wide_header_is_reported_not_used(torch_dev, entry):
     """b = 6 (two-byte entries): a width above b, or a minimum that leaves no
@@ -266,6 +305,57 @@ def test_corrupt_wide_header_is_reported_not_used(torch_dev, entry):
     assert np.all(np.isnan(s[0, 0, :64])) and np.all(np.isfinite(s[0, 0, 64:]))
     c.attention(q)
     assert c.check() == _lib.ECORRUPT
+    assert c.check() == 0
+
+
+@pytest.mark.parametrize("bad", ["negative", "nan", "inf"])
+@pytest.mark.parametrize("bits,G", [(4, 1), (3, 4), (8, 1)])
+def test_pv_rejects_weights_outside_its_domain(torch_dev, bad, bits, G):
+    """The V GEMV takes p >= 0 and finite (softmax weights, which its 20-bit
+    fixed point assumes): a block holding any other weight latches EINVAL
+    and contributes nothing, so the output is that of p with the block's
+    weights zeroed."""
+    torch, dev = torch_dev
+    from decode_gemv_amd import _lib
+    K, V = make_kv("gauss", 2, 200, 64)
+    c = gpu_cache(torch, dev, K, V, bits, 64, True)
+    rng = np.random.default_rng(3)
+    p = rng.random((2, G, 200)).astype(np.float32)
+    p0 = p.copy()
+    p0[1, :, 64:128] = 0.0                       # stream 1, block 1 zeroed
+    p[1, G - 1, 70] = {"negative": -0.25, "nan": np.nan, "inf": np.inf}[bad]
+    say("pv domain", bad, bits, G)
+    want = c.pv(torch.from_numpy(p0).to(dev)).clone()
+    assert c.check() == 0
+    got = c.pv(torch.from_numpy(p).to(dev))
+    assert c.check() == _lib.EINVAL
+    assert torch.equal(got, want)
+    assert c.check() == 0
+
+
+@pytest.mark.parametrize("bad", [0x7C00, 0xFC00, 0x7E00])
+def test_non_finite_input_latches_einval(torch_dev, bad):
+    """Infinite or NaN fp16 inputs are outside the method: compress and
+    append latch EINVAL; the other blocks' records are still exact."""
+    torch, dev = torch_dev
+    from decode_gemv_amd import _lib, PackedKVCache
+    K, V = make_kv("gauss", 2, 150, 64)
+    refs = oracle_streams(K[:, :128], V[:, :128], 4, 64)
+    Kb, Vb = K.copy(), V.copy()
+    Kb.view(np.uint16)[0, 140, 3] = bad          # in the partial last block
+    say("non-finite", hex(bad))
+    c = PackedKVCache(2, 300, bits=4, block=64, device=str(dev))
+    c.compress(torch.from_numpy(Kb).to(dev), torch.from_numpy(Vb).to(dev))
+    assert c.check() == _lib.EINVAL
+    ko = c.offsets("K").cpu().numpy().astype(np.int64)
+    for s, ref in enumerate(refs):                # the two closed blocks are untouched
+        ro = ref.offsets("K")
+        assert np.array_equal(ko[s, :3], ro)
+        assert c.arena("K")[s, :int(ro[-1])].cpu().numpy().tobytes() == ref.arena("K")
+    vnew = np.zeros((2, 1, 128), np.float16)
+    vnew.view(np.uint16)[1, 0, 7] = bad
+    c.append(torch.zeros(2, 1, 128, dtype=torch.float16, device=dev), torch.from_numpy(vnew).to(dev))
+    assert c.check() == _lib.EINVAL
     assert c.check() == 0
 
 
@@ -298,7 +388,7 @@ def test_pv_weight_laws(torch_dev, law):
     out = c.pv(torch.from_numpy(p).to(dev)).cpu().numpy()
     assert c.check() == 0
     ref = np.stack([attention.pv(p[s].astype(np.float64), ostream.decode_stream(refs[s])[1]) for s in range(S)])
-    assert rel_l2(out, ref) <= TOL, (rel_l2(out, ref), worst_row_rel(out, ref))
+    assert rel_l2(out, ref) <= TOL and worst_row_rel(out, ref) <= TOL, (rel_l2(out, ref), worst_row_rel(out, ref))
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
@@ -320,7 +410,7 @@ def test_fused_attention_within_tolerance(torch_dev, case, G):
         kh, vh, _, _ = ostream.decode_stream(refs[s])
         ref.append(attention.pv(attention.softmax(attention.qk(q[s], kh), 128), vh))
     ref = np.stack(ref)
-    assert rel_l2(out, ref) <= TOL, (rel_l2(out, ref), worst_row_rel(out, ref))
+    assert rel_l2(out, ref) <= TOL and worst_row_rel(out, ref) <= TOL, (rel_l2(out, ref), worst_row_rel(out, ref))
 
 
 def test_fused_attention_is_bitwise_reproducible_and_reuses_its_workspace(torch_dev):
@@ -366,7 +456,8 @@ def test_multi_cache_attention_matches_single_calls(torch_dev, bits, block, G, L
     for s in range(S):
         kh, vh, _, _ = ostream.decode_stream(refs[s])
         ref = attention.pv(attention.softmax(attention.qk(q[0, s], kh), 128), vh)
-        assert rel_l2(out[0, s].cpu().numpy(), ref) <= TOL
+        got = out[0, s].cpu().numpy()
+        assert rel_l2(got, ref) <= TOL and worst_row_rel(got, ref) <= TOL
 
 
 @pytest.mark.parametrize("nbytes", [16, 4096 + 16, 10 * 2**20 + 48, 70 * 2**20])

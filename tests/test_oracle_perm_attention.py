@@ -164,6 +164,17 @@ def test_softmax_properties():
     assert np.all(one == 0.5)
 
 
+@pytest.mark.parametrize("D,ratio", [(128, 2.0), (64, 3.0), (256, 5.0)])
+def test_softmax_temperature_is_one_over_sqrt_head_dim(D, ratio):
+    """Closed form: scores (0, sqrt(D) ln r) give weights 1/(1+r) and r/(1+r)
+    exactly when the temperature is 1/sqrt(D); 1/D, no scaling or a fixed
+    1/sqrt(128) would give other weights."""
+    s = np.array([[0.0, np.sqrt(D) * np.log(ratio)]])
+    p = attention.softmax(s, D)
+    assert abs(p[0, 0] - 1.0 / (1.0 + ratio)) < 1e-14
+    assert abs(p[0, 1] - ratio / (1.0 + ratio)) < 1e-14
+
+
 @pytest.mark.parametrize("bits,block", [(4, 64), (2, 64), (3, 64), (4, 128), (5, 128), (8, 64)])
 def test_cr_matches_closed_form_when_every_run_is_full_width(bits, block):
     """Construct blocks whose every run spans 0..L in every channel."""
@@ -190,6 +201,55 @@ def test_cr_matches_closed_form_when_every_run_is_full_width(bits, block):
     assert abs(cr.closed_form_full_width("K", 4, 64, 32, 128) - 1024 / 304) < 1e-15
     # b = 8: 8 payload bits, 16/32 header bits (two-byte entries), 32/64 parameter bits
     assert abs(cr.closed_form_full_width("K", 8, 64, 32, 128) - 16 / 9) < 1e-15
+
+
+@pytest.mark.parametrize("bits,block,k_rec,v_rec", [(4, 64, 4864, 4608), (3, 64, 3840, 3584),
+                                                    (2, 64, 2816, 2560), (4, 128, 9216, 9216)])
+def test_full_and_plain_quant_ratios_by_record_geometry(bits, block, k_rec, v_rec):
+    """CR_full adds one permutation byte per token to the stored records, and
+    plain b-bit quantisation stores T*D*b bits plus the same fp16 parameters.
+    Blocks whose every run is at full width have records of the sizes the
+    format's geometry gives (params + one header byte per run and channel +
+    b words per run and channel): 4864 / 4608 bytes at b = 4, B = 64, etc.
+    Both ratios are checked against those byte counts and against the
+    printed plain-quantisation ratios 16 / (b + 32/B) (K) and 16 / (b + 32/D)
+    (V): 3.556 / 3.765 at b = 4, B = 64; 6.400 / 7.111 at b = 2."""
+    L = (1 << bits) - 1
+    nb = 3
+    T = nb * block
+    t = np.arange(T)[:, None]
+    c = np.arange(128)[None, :]
+    # checkerboard of the two extremes: every K (block, channel) and every V
+    # token spans 0..L, and every run holds both in every channel
+    grid = np.where((t + c) % 2 == 0, 0.0, float(L)).astype(np.float16)
+    cache = stream.compress(grid, grid, Config(bits=bits, block=block, permute=False))
+    raw = 2 * T * 128
+    for which, rec in (("K", k_rec), ("V", v_rec)):
+        r = cr.ratios(cache, which)
+        assert r["phys_bytes"] == nb * rec
+        assert abs(r["cr_full"] - raw / (nb * rec + T)) < 1e-12
+        params = 32 * 128 * nb if which == "K" else 32 * T
+        assert abs(r["cr_plain_quant"] - 16 * T * 128 / (T * 128 * bits + params)) < 1e-12
+    printed = {(4, 64): (3.556, 3.765), (3, 64): (4.571, 4.923), (2, 64): (6.400, 7.111), (4, 128): (3.765, 3.765)}
+    pk, pv = printed[(bits, block)]
+    assert abs(cr.ratios(cache, "K")["cr_plain_quant"] - pk) < 5e-4
+    assert abs(cr.ratios(cache, "V")["cr_plain_quant"] - pv) < 5e-4
+
+
+def test_plain_quant_ratio_does_not_depend_on_the_data():
+    """Plain quantisation has no per-run width: its ratio depends only on T,
+    D, b and the parameter count, whatever the values (ragged last block)."""
+    w = kvsynth.WORKLOADS["llama7b-32k"]
+    k, v = kvsynth.stream_kv(w, 5, tokens=200)
+    c1 = stream.compress(k, v, Config(bits=4, block=64))
+    ks, vs = kvsynth.structured_kv(200, 128, 64, 32, seed=9)
+    c2 = stream.compress(ks, vs, Config(bits=4, block=64))
+    for which in "KV":
+        a, b = cr.ratios(c1, which)["cr_plain_quant"], cr.ratios(c2, which)["cr_plain_quant"]
+        assert a == b
+    # 4 blocks (the last holds 8 tokens): K params 4 * 128 * 32 bits, V 200 * 32
+    assert abs(cr.ratios(c1, "K")["cr_plain_quant"] - 16 * 200 * 128 / (200 * 128 * 4 + 4 * 128 * 32)) < 1e-12
+    assert abs(cr.ratios(c1, "V")["cr_plain_quant"] - 16 * 200 * 128 / (200 * 128 * 4 + 200 * 32)) < 1e-12
 
 
 def test_cr_counts_the_bits_the_packer_writes():
