@@ -67,6 +67,8 @@ _SIGS = {
                                                 c_int32, ctypes.c_float, c_void_p, c_void_p, c_uint64,
                                                 c_void_p]),
     "packkv_attention_multi_workspace_bytes": (c_uint64, [ctypes.POINTER(CacheT), c_int32, c_int32]),
+    "packkv_attention_decode_noalloc": (c_int32, [ctypes.POINTER(CacheT), c_void_p, c_int32, ctypes.c_float,
+                                                  c_void_p, c_void_p]),
     "packkv_compress_block": (c_int32, [ctypes.POINTER(CacheT), c_void_p, c_void_p, c_int64, c_void_p]),
     "packkv_append_tokens": (c_int32, [ctypes.POINTER(CacheT), c_void_p, c_void_p, c_int32, c_void_p]),
     "packkv_qk_gemv": (c_int32, [ctypes.POINTER(CacheT), c_void_p, c_int32, c_void_p, c_int64, c_void_p]),

@@ -166,6 +166,20 @@ class PackedKVCache:
                    "packkv_attention_decode")
         return out
 
+    def attention_noalloc(self, q: torch.Tensor, out: torch.Tensor, scale: Optional[float] = None) -> torch.Tensor:
+        """attention() through packkv_attention_decode_noalloc: no workspace,
+        the library's own per-GPU scratch array instead (the caller passes
+        out, fp32 [S][G][D]); bit-identical results."""
+        S, G, d = q.shape
+        if q.dtype != torch.float16 or S != self.n_streams or d != D or not q.is_contiguous():
+            raise ValueError("q must be contiguous fp16 [S][G][D]")
+        if out.dtype != torch.float32 or tuple(out.shape) != (S, G, D) or not out.is_contiguous():
+            raise ValueError("out must be contiguous fp32 [S][G][D]")
+        sc = D ** -0.5 if scale is None else float(scale)
+        _lib.check(_lib.load().packkv_attention_decode_noalloc(ctypes.byref(self._c), _ptr(q), G, sc, _ptr(out),
+                                                               _stream()), "packkv_attention_decode_noalloc")
+        return out
+
     def decompress(self, which: str, mode: int) -> torch.Tensor:
         """mode 0: uint8 q [S][T][D] slot order; mode 1: fp32 x_hat [S][T][D] token order."""
         T = self.n_tokens

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "kernels.hpp"
 
@@ -291,6 +292,27 @@ uint64_t packkv_attention_workspace_bytes(const packkv_cache_t* c, int32_t group
   return attn_partial_bytes(c, group) + (((uint64_t)c->n_streams * 4u + 255u) & ~(uint64_t)255u);
 }
 
+// Launch arguments of fused attention over caches of c's shape (n per
+// launch at most kAttnMaxCaches): the split-merge work division, the scale,
+// q/out strides.  Workspace pointers are left to the caller.
+static AttnArgs attention_args(const packkv_cache_t* c, int32_t n, int32_t group, float scale) {
+  const GemvArgs g = gemv_args(c, true, group);   // the split-merge work division
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.arena_stride = c->arena_stride;
+  a.off_stride = g.off_stride;
+  a.n_tokens = c->n_tokens;
+  a.nb = g.nb;
+  a.bits = c->cfg.bits;
+  a.blocks_per_wg = g.blocks_per_wg;
+  a.splits = attention_splits((int64_t)c->n_streams * (n < kAttnMaxCaches ? n : kAttnMaxCaches), g.splits, g.nb,
+                              c->cfg.block_tokens, c->cfg.bits, group);
+  a.G = group;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  a.qo_stride = (int64_t)c->n_streams * group * kD;
+  return a;
+}
+
 // Decode attention over n caches of one shape, in launches of up to
 // kAttnMaxCaches caches.
 static int attention_decode(const packkv_cache_t* const* cs, int32_t n, const void* q_f16, int32_t group,
@@ -311,22 +333,9 @@ static int attention_decode(const packkv_cache_t* const* cs, int32_t n, const vo
   if (c->n_tokens < 1) return PACKKV_ESTATE;
   const uint64_t per_cache = packkv_attention_workspace_bytes(c, group);
   if (ws_bytes < per_cache * (uint64_t)n) return PACKKV_EINVAL;
-  const GemvArgs g = gemv_args(c, true, group);   // the split-merge work division
-  AttnArgs a;
-  memset(&a, 0, sizeof(a));
-  a.arena_stride = c->arena_stride;
-  a.off_stride = g.off_stride;
-  a.n_tokens = c->n_tokens;
-  a.nb = g.nb;
-  a.bits = c->cfg.bits;
-  a.blocks_per_wg = g.blocks_per_wg;
-  a.splits = attention_splits((int64_t)c->n_streams * (n < kAttnMaxCaches ? n : kAttnMaxCaches), g.splits, g.nb,
-                              c->cfg.block_tokens, c->cfg.bits, group);
-  a.G = group;
-  a.scale_log2e = scale * 1.4426950408889634f;
-  a.qo_stride = (int64_t)c->n_streams * group * kD;
+  AttnArgs a = attention_args(c, n, group, scale);
   a.ws_stride = per_cache;
-  a.partial_bytes = attn_partial_bytes(c, group);
+  a.tk_stride = per_cache;
   for (int32_t i0 = 0; i0 < n; i0 += kAttnMaxCaches) {
     const int32_t m = n - i0 < kAttnMaxCaches ? n - i0 : kAttnMaxCaches;
     for (int32_t i = 0; i < m; ++i) {
@@ -336,6 +345,7 @@ static int attention_decode(const packkv_cache_t* const* cs, int32_t n, const vo
     a.q = (const uint16_t*)q_f16 + i0 * a.qo_stride;
     a.out = out + i0 * a.qo_stride;
     a.ws = (uint8_t*)workspace + (uint64_t)i0 * per_cache;
+    a.tk = a.ws + attn_partial_bytes(c, group);
     if ((e = hip_status(launch_attention(a, c->cfg.block_tokens, c->n_streams, m, (hipStream_t)stream)))) return e;
   }
   return PACKKV_OK;
@@ -350,6 +360,77 @@ int packkv_attention_decode_multi(const packkv_cache_t* const* caches, int32_t n
                                   int32_t group, float scale, float* out, void* workspace, uint64_t ws_bytes,
                                   void* stream) {
   return attention_decode(caches, n_caches, q_f16, group, scale, out, workspace, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Fused attention with the library's own scratch memory, for callers that
+// cannot allocate.  The split partials and the per-stream arrival counters
+// live in one file-scope device array per GPU: counters first, at fixed
+// places (so a call of any shape finds them where the previous call, of any
+// shape, left them at zero), then the partials of the current call.
+namespace {
+
+constexpr uint64_t kScratchBytes = 16ull << 20;
+constexpr int32_t kScratchStreams = 16384;
+constexpr uint64_t kScratchCounterBytes = (uint64_t)kScratchStreams * 4;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// The counters the kernel relies on start at zero: cleared with a kernel
+// (not a memset, which graph capture would record as a memset node) on the
+// call's stream before the attention launch.
+__global__ __launch_bounds__(256) void k_clear_counters(uint32_t* counters, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) counters[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+uint8_t* scratch_dev[kMaxDevices];   // device address of `scratch` on each GPU, once asked
+
+// The device address of the current device's scratch array (each GPU holds
+// its own copy at its own address; the array's name is only a host-side
+// handle, so host code passes this address to kernels, never the name).
+int scratch_of_current_device(uint8_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PACKKV_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return PACKKV_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PACKKV_EHIP;
+    scratch_dev[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = scratch_dev[dev];
+  return PACKKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int packkv_attention_decode_noalloc(const packkv_cache_t* c, const void* q_f16, int32_t group, float scale,
+                                    float* out, void* stream) {
+  int e = check_cache(c);
+  if (e) return e;
+  if (!q_f16 || !out || group < 1 || !(scale > 0.f) || !std::isfinite(scale)) return PACKKV_EINVAL;
+  if (c->n_tokens < 1) return PACKKV_ESTATE;
+  AttnArgs a = attention_args(c, 1, group, scale);
+  const uint64_t partials = (uint64_t)c->n_streams * (uint64_t)group * (uint64_t)a.splits * kAttnPartial * 4u;
+  if (c->n_streams > kScratchStreams || partials > kScratchBytes - kScratchCounterBytes) return PACKKV_ECAPACITY;
+  uint8_t* base = nullptr;
+  if ((e = scratch_of_current_device(&base))) return e;
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(k_clear_counters, dim3((c->n_streams + 255) / 256), dim3(256), 0, st,
+                     reinterpret_cast<uint32_t*>(base), c->n_streams);
+  if ((e = hip_status(hipGetLastError()))) return e;
+  a.cache[0] = AttnCache{c->k_arena, c->v_arena, c->k_off, c->v_off, c->status};
+  a.q = (const uint16_t*)q_f16;
+  a.out = out;
+  a.tk = base;
+  a.ws = base + kScratchCounterBytes;
+  return hip_status(launch_attention(a, c->cfg.block_tokens, c->n_streams, 1, st));
 }
 
 uint64_t packkv_attention_multi_workspace_bytes(const packkv_cache_t* c, int32_t group, int32_t n_caches) {
@@ -630,7 +711,8 @@ int packkv_paged_attention(const packkv_paged_t* c, const void* q_f16, int32_t g
   a.qo_stride = (int64_t)c->n_streams * group * kD;
   a.ws = (uint8_t*)workspace;
   a.ws_stride = need;
-  a.partial_bytes = paged_partial_bytes(c, group);
+  a.tk = a.ws + paged_partial_bytes(c, group);
+  a.tk_stride = need;
   return hip_status(launch_attention(a, B, c->n_streams, 1, (hipStream_t)stream, true));
 }
 

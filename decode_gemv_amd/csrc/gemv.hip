@@ -1632,7 +1632,7 @@ void k_attn_decode(AttnArgs a) {
   const uint16_t* q = a.q + blockIdx.y * a.qo_stride;
   float* out = a.out + blockIdx.y * a.qo_stride;
   float* ws = reinterpret_cast<float*>(a.ws + blockIdx.y * a.ws_stride);
-  uint32_t* tickets = reinterpret_cast<uint32_t*>(a.ws + blockIdx.y * a.ws_stride + a.partial_bytes);
+  uint32_t* tickets = reinterpret_cast<uint32_t*>(a.tk + blockIdx.y * a.tk_stride);
   const int s = blockIdx.x / a.splits;
   const int split = blockIdx.x % a.splits;
   // the stream's length: one for the cache, or (paged) the stream's own

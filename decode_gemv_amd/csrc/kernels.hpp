@@ -116,9 +116,10 @@ struct AttnArgs {
   const uint16_t* q;     // [caches][S][G][D] fp16
   float* out;            // [caches][S][G][D]
   int64_t qo_stride;     // elements per cache in q and out: S * G * D
-  uint8_t* ws;           // per cache ws_stride bytes: partials [S][G][splits][kAttnPartial],
-  uint64_t ws_stride;    //   then per-stream arrival counters (zero between calls)
-  uint64_t partial_bytes;
+  uint8_t* ws;           // per cache ws_stride bytes of partials [S][G][splits][kAttnPartial]
+  uint64_t ws_stride;
+  uint8_t* tk;           // per cache tk_stride bytes: per-stream arrival counters
+  uint64_t tk_stride;    //   (u32 [S], zero between calls)
 };
 constexpr int kAttnPartial = 132;   // D partial sums, running max, weight sum, 2 pad
 

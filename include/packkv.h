@@ -34,7 +34,8 @@
  *     cache lives in the caller's buffers; calls on different caches are
  *     independent.  The only process-wide state is a table of per-shape
  *     occupancy figures (resident workgroups per device), asked from the
- *     runtime once per kernel shape and read-only after that.
+ *     runtime once per kernel shape and read-only after that, and the
+ *     scratch array of packkv_attention_decode_noalloc (one per GPU).
  *   - `stream` is a hipStream_t passed as void*.  Every call only enqueues
  *     work on that stream and returns without synchronising, except
  *     packkv_check, which synchronises the stream.
@@ -249,6 +250,24 @@ uint64_t packkv_attention_workspace_bytes(const packkv_cache_t* cache, int32_t g
 int packkv_attention_decode_multi(const packkv_cache_t* const* caches, int32_t n_caches, const void* q_f16,
                                   int32_t group, float scale, float* out, void* workspace, uint64_t ws_bytes,
                                   void* stream);
+
+/*
+ * packkv_attention_decode_noalloc - packkv_attention_decode without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same kernels, same work division and the same results bit
+ * for bit.  It allocates nothing: the split partials and the per-stream
+ * arrival counters live in a file-scope device array of the library, 16 MiB
+ * per GPU, held from the library's load until the process ends.  Limits:
+ * at most 16384 streams and at most 16 MiB - 64 KiB of partials
+ * (n_streams * group * splits * 528 bytes; a few MiB at the shapes measured
+ * here), else PACKKV_ECAPACITY before any launch.  Each call first clears
+ * the counters of its streams with a small kernel on `stream`.  Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (different
+ * streams, or host threads) race and must not be issued.
+ */
+int packkv_attention_decode_noalloc(const packkv_cache_t* cache, const void* q_f16, int32_t group, float scale,
+                                    float* out, void* stream);
 
 /* Bytes of workspace packkv_attention_decode_multi needs (0 if n_caches < 1). */
 uint64_t packkv_attention_multi_workspace_bytes(const packkv_cache_t* cache, int32_t group, int32_t n_caches);
