@@ -74,8 +74,9 @@ def generate(w: kvsynth.Workload, torch, dev):
     return K, V
 
 
-def cpu_baseline(w: kvsynth.Workload, n_streams: int, n_steps: int, permute: int = 1) -> dict:
-    """The fp64 oracle's decode steps on a sample of streams, single-threaded."""
+def cpu_baseline(w: kvsynth.Workload, n_streams: int, budget_s: float, permute: int = 1) -> dict:
+    """The fp64 oracle's decode steps on a sample of streams, single-threaded,
+    for about budget_s seconds (whole steps over the sample, at least one)."""
     from threadpoolctl import threadpool_limits
     import oracle
     from oracle import stream as ostream, attention
@@ -85,19 +86,22 @@ def cpu_baseline(w: kvsynth.Workload, n_streams: int, n_steps: int, permute: int
         for s in range(n_streams):
             k, v = kvsynth.stream_kv(w, s)
             caches.append(ostream.compress(k, v, cfg))          # prefill: not timed
-        steps = [[(kvsynth.stream_q(w, s, step=i), kvsynth.append_kv(w, s, i)) for s in range(n_streams)]
-                 for i in range(n_steps)]
         nbytes = 0
-        t0 = time.perf_counter()
-        for i in range(n_steps):
+        n_steps = 0
+        dt = 0.0
+        while n_steps == 0 or dt < budget_s:
+            inputs = [(kvsynth.stream_q(w, s, step=n_steps), kvsynth.append_kv(w, s, n_steps))
+                      for s in range(n_streams)]
+            t0 = time.perf_counter()
             for s in range(n_streams):
-                q, kv_new = steps[i][s]
+                q, kv_new = inputs[s]
                 caches[s] = c = ostream.append(caches[s], *kv_new)   # tail re-encode
                 kh, vh, _, _ = ostream.decode_stream(c)                # unpack + fp64 dequant
                 p = attention.softmax(attention.qk(q, kh), w.head_dim)
                 attention.pv(p, vh)
                 nbytes += len(c.arena("K")) + len(c.arena("V")) + 2 * 4 * (len(c.blocks) + 1)
-        dt = time.perf_counter() - t0
+            dt += time.perf_counter() - t0
+            n_steps += 1
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle", "host": host_cpu(),
             "sample": f"{n_streams} of {w.streams} streams at {w.tokens}+ tokens, {n_steps} decode steps each "
                       f"(tail re-encode, unpack, fp64 dequantise, K GEMV, softmax, V GEMV), {dt:.1f} s of "
@@ -289,8 +293,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="append-64k", choices=sorted(kvsynth.WORKLOADS))
     ap.add_argument("--cpu-streams", type=int, default=4, help="streams in the oracle's timed sample")
-    ap.add_argument("--cpu-steps", type=int, default=None,
-                    help="decode steps per sampled stream (default: about 12 s of oracle work)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="timed oracle work (whole decode steps over the sampled streams)")
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="bytes written before every timed step to evict the memory-side cache (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -648,10 +652,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
-        # about 12 s of single-threaded oracle work: one decode step of a
-        # stream costs the oracle ~3 us per cached token
-        steps = args.cpu_steps or max(3, int(12.0 / (args.cpu_streams * 3e-6 * T0)))
-        cpu = cpu_baseline(w, args.cpu_streams, steps, args.permute)
+        cpu = cpu_baseline(w, args.cpu_streams, args.cpu_seconds, args.permute)
 
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,

@@ -7,8 +7,8 @@
 //   V: scale[B] f16 | zero[B] f16 | hdr[nr][D] | pad16 | payload | pad16
 // hdr per (run, channel): the byte (w << 4) | m for b <= 4, the
 // little-endian u16 (w << 8) | m for b = 5..8 (m needs the whole byte);
-// payload = for run r, channel c: w little-endian u32 words, slot i of the
-// run in bits [i*w, i*w + w).
+// payload = for run r, channel c: w little-endian u32 words in the sliced
+// order described below (sliced_to_nibbles / sliced_to_bytes).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -46,37 +46,68 @@ __device__ __forceinline__ double f16_bits_to_double(uint32_t h) {
 }
 
 // ---------------------------------------------------------------------------
-// Spread the fields of one 8-slot group into eight 4-bit nibbles.
-// Input: the group's 8*w bits at the bottom of x.  Output: nibble i = field i.
-__device__ __forceinline__ uint32_t spread3to4(uint32_t x) {
-  uint32_t a = (x & 0xFFFu) | ((x & 0xFFF000u) << 4);
-  uint32_t b = (a & 0x003F003Fu) | ((a & 0x0FC00FC0u) << 2);
-  return (b & 0x07070707u) | ((b & 0x38383838u) << 1);
-}
-// 2-bit fields: the 8 fields of bytes 2H and 2H+1 of x.  v_perm puts the
-// two bytes in bytes 0 and 2, then two shift-or-mask steps split each byte
-// into its nibbles and each nibble into its two fields.
-template <int H>
-__device__ __forceinline__ uint32_t spread2to4(uint32_t x) {
-  const uint32_t a = __builtin_amdgcn_perm(0u, x, H ? 0x0c030c02u : 0x0c010c00u);
-  const uint32_t b = (a | (a << 4)) & 0x0F0F0F0Fu;
-  return (b | (b << 2)) & 0x33333333u;
-}
-__device__ __forceinline__ uint32_t spread1to4(uint32_t x) {
-  uint32_t a = (x & 0xFu) | ((x & 0xF0u) << 12);
-  uint32_t b = (a & 0x00030003u) | ((a & 0x000C000Cu) << 6);
-  return (b & 0x01010101u) | ((b & 0x02020202u) << 3);
+// Run payload -> container words.  A run's u = q - m values (32 slots, w
+// bits each) are stored in w words laid out for these decoders: with c-bit
+// containers (c = 4 for b <= 4, 8 for b = 5..8), slot i belongs to
+// container word k = i / (32/c), field j = i % (32/c), and bit p of its u
+// sits in run word W at bit c*j + Q, where W = k / g, Q = w*(k % g) + p if
+// w divides c (g = c/w), else W = k, Q = p for k < w and W = p, Q = k for
+// k >= w.  Rebuilding the container words (every slot's u in its own field,
+// upper bits zero) then takes only shifts and masks.
+
+// Nibble containers: out[k] holds u of slots 8k .. 8k+7 (nibble j = slot
+// 8k + j), from the run's first W words wd[0 .. W-1].
+template <int W>
+__device__ __forceinline__ void sliced_to_nibbles(const uint32_t wd[4], uint32_t out[4]) {
+  if constexpr (W == 4) {
+    out[0] = wd[0]; out[1] = wd[1]; out[2] = wd[2]; out[3] = wd[3];
+  } else if constexpr (W == 3) {
+    // containers 0..2 in the low 3 bits of words 0..2; bit p of container
+    // 3 in bit 3 of every nibble of word p
+    out[0] = wd[0] & 0x77777777u;
+    out[1] = wd[1] & 0x77777777u;
+    out[2] = wd[2] & 0x77777777u;
+    out[3] = ((wd[0] >> 3) & 0x11111111u) | ((wd[1] >> 2) & 0x22222222u) | ((wd[2] >> 1) & 0x44444444u);
+  } else if constexpr (W == 2) {
+    out[0] = wd[0] & 0x33333333u;
+    out[1] = (wd[0] >> 2) & 0x33333333u;
+    out[2] = wd[1] & 0x33333333u;
+    out[3] = (wd[1] >> 2) & 0x33333333u;
+  } else if constexpr (W == 1) {
+    out[0] = wd[0] & 0x11111111u;
+    out[1] = (wd[0] >> 1) & 0x11111111u;
+    out[2] = (wd[0] >> 2) & 0x11111111u;
+    out[3] = (wd[0] >> 3) & 0x11111111u;
+  } else {
+    out[0] = out[1] = out[2] = out[3] = 0u;
+  }
 }
 
-// 32 bits of the run's bit string starting at bit p (p a compile-time
-// multiple of 8 inside a switch), from its words w0..w3.
-template <int P>
-__device__ __forceinline__ uint32_t bits_at(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
-  constexpr int wi = P >> 5, sh = P & 31;
-  uint32_t lo = wi == 0 ? w0 : wi == 1 ? w1 : wi == 2 ? w2 : w3;
-  uint32_t hi = wi == 0 ? w1 : wi == 1 ? w2 : wi == 2 ? w3 : 0u;
-  if constexpr (sh == 0) return lo;
-  else return __builtin_amdgcn_alignbit(hi, lo, sh);
+// Byte containers: out[k] holds u of slots 4k .. 4k+3 (byte j = slot 4k + j),
+// from the run's first W words wd[0 .. W-1].
+template <int W>
+__device__ __forceinline__ void sliced_to_bytes(const uint32_t (&wd)[8], uint32_t (&out)[8]) {
+  constexpr uint32_t rep = 0x01010101u;
+  if constexpr (W == 0) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) out[k] = 0u;
+  } else if constexpr (8 % W == 0) {
+    constexpr int g = 8 / W;
+    constexpr uint32_t low = W == 8 ? 0xFFFFFFFFu : ((1u << W) - 1u) * rep;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) out[k] = (wd[k / g] >> (W * (k % g))) & low;
+  } else {
+    constexpr uint32_t low = ((1u << W) - 1u) * rep;
+#pragma unroll
+    for (int k = 0; k < W; ++k) out[k] = wd[k] & low;
+#pragma unroll
+    for (int k = W; k < 8; ++k) {
+      uint32_t x = 0u;
+#pragma unroll
+      for (int p = 0; p < W; ++p) x |= (wd[p] >> (k - p)) & (rep << p);
+      out[k] = x;
+    }
+  }
 }
 
 // m (0..15) in all eight nibbles of a word: one shift-or and a byte broadcast
@@ -89,35 +120,19 @@ __device__ __forceinline__ uint32_t nibble_splat(uint32_t m) {
   return r;
 }
 
-// Decode one run (R = 32 slots) stored at width w with minimum m into four
-// nibble words: word k holds q = m + u of slots 8k .. 8k+7 (nibble i = slot
-// 8k+i).  Valid for m + 2^w - 1 <= 15.  `wd` holds the run's first four
-// payload words (words past the run are ignored).
+// Decode one run (R = 32 slots) stored at width w (0 .. WMAX) with minimum m
+// into four nibble words: word k holds q = m + u of slots 8k .. 8k+7
+// (nibble i = slot 8k+i).  Valid for m + 2^w - 1 <= 15.  `wd` holds the
+// run's first four payload words (words past the run are ignored).
 template <int WMAX = 4>
 __device__ __forceinline__ void run_to_nibbles(int w, uint32_t m, const uint32_t wd[4], uint32_t out[4]) {
-  const uint32_t a = wd[0], b = wd[1], c = wd[2], d = wd[3];
   // widths above WMAX do not occur at the call site; the widest one that
   // does is tested first
-  if (WMAX >= 4 && w == 4) {
-    out[0] = a; out[1] = b; out[2] = c; out[3] = d;
-  } else if (WMAX >= 3 && w == 3) {
-    out[0] = spread3to4(bits_at<0>(a, b, c, d));
-    out[1] = spread3to4(bits_at<24>(a, b, c, d));
-    out[2] = spread3to4(bits_at<48>(a, b, c, d));
-    out[3] = spread3to4(bits_at<72>(a, b, c, d));
-  } else if (WMAX >= 2 && w == 2) {
-    out[0] = spread2to4<0>(a);
-    out[1] = spread2to4<1>(a);
-    out[2] = spread2to4<0>(b);
-    out[3] = spread2to4<1>(b);
-  } else if (w == 1) {
-    out[0] = spread1to4(a);
-    out[1] = spread1to4(a >> 8);
-    out[2] = spread1to4(a >> 16);
-    out[3] = spread1to4(a >> 24);
-  } else {
-    out[0] = out[1] = out[2] = out[3] = 0u;
-  }
+  if (WMAX >= 4 && w == 4) sliced_to_nibbles<4>(wd, out);
+  else if (WMAX >= 3 && w == 3) sliced_to_nibbles<3>(wd, out);
+  else if (WMAX >= 2 && w == 2) sliced_to_nibbles<2>(wd, out);
+  else if (w == 1) sliced_to_nibbles<1>(wd, out);
+  else sliced_to_nibbles<0>(wd, out);
   const uint32_t mm = nibble_splat(m);   // m in every nibble; no carries
   out[0] += mm; out[1] += mm; out[2] += mm; out[3] += mm;
 }
@@ -125,19 +140,7 @@ __device__ __forceinline__ void run_to_nibbles(int w, uint32_t m, const uint32_t
 // A run stored at the full width BITS: its BITS words -> four container words.
 template <int BITS>
 __device__ __forceinline__ void full_to_nibbles(const uint32_t wd[4], uint32_t out[4]) {
-  if constexpr (BITS == 4) {
-    out[0] = wd[0]; out[1] = wd[1]; out[2] = wd[2]; out[3] = wd[3];
-  } else if constexpr (BITS == 3) {
-    out[0] = spread3to4(bits_at<0>(wd[0], wd[1], wd[2], 0u));
-    out[1] = spread3to4(bits_at<24>(wd[0], wd[1], wd[2], 0u));
-    out[2] = spread3to4(bits_at<48>(wd[0], wd[1], wd[2], 0u));
-    out[3] = spread3to4(bits_at<72>(wd[0], wd[1], wd[2], 0u));
-  } else {
-    out[0] = spread2to4<0>(wd[0]);
-    out[1] = spread2to4<1>(wd[0]);
-    out[2] = spread2to4<0>(wd[1]);
-    out[3] = spread2to4<1>(wd[1]);
-  }
+  sliced_to_nibbles<BITS>(wd, out);
 }
 
 // Four header bytes (w << 4 | m) of runs that are all at the full width BITS

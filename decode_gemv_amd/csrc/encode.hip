@@ -11,7 +11,8 @@
 //   * permutation = greedy L1 grouping with key (distance, index), or (mode
 //     2) the tokens sorted by (total of their K and V ints, index); identity
 //     unless the payload shrinks strictly;
-//   * run width = bit_length(max - min), u = q - min packed LSB-first.
+//   * run width = bit_length(max - min), u = q - min packed in the sliced
+//     order of pack_run below.
 // This file must be built without fast-math flags.
 #include "kernels.hpp"
 
@@ -88,18 +89,38 @@ __device__ __forceinline__ void run_values(const uint8_t* q, const uint8_t* orde
   }
 }
 
-// The w-bit string of a run: slot i's value in bits [i*w, i*w + w) of eight
-// little-endian words (only the first w are used).  W is a compile-time
-// width, so every bit position is a constant.
-template <int W>
+// The W words of a run (out[0 .. W-1]; W = 1 .. CB) in the sliced order the
+// decoders read: with CB-bit containers (4 for b <= 4, 8 for b = 5..8), the
+// container word k holds slots k*(32/CB) + j in field j; if W divides CB,
+// g = CB/W containers share word k/g, container k shifted left by
+// W*(k % g); otherwise container k < W is word k's low W bits per field and
+// bit p of container k >= W goes to bit k of every field of word p.  u[i]
+// < 2^W for every slot.
+template <int W, int CB>
 __device__ __forceinline__ void pack_run(const uint32_t u[kR], uint32_t out[8]) {
+  constexpr int PER = 32 / CB;                       // slots per container word
+  constexpr uint32_t rep = CB == 4 ? 0x11111111u : 0x01010101u;
+  uint32_t C[CB];
+#pragma unroll
+  for (int k = 0; k < CB; ++k) {
+    uint32_t x = 0u;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) x |= u[k * PER + j] << (CB * j);
+    C[k] = x;
+  }
 #pragma unroll
   for (int k = 0; k < 8; ++k) out[k] = 0u;
+  if constexpr (CB % W == 0) {
+    constexpr int g = CB / W;
 #pragma unroll
-  for (int i = 0; i < kR; ++i) {
-    const int p = i * W, wd = p >> 5, sh = p & 31;
-    out[wd] |= u[i] << sh;
-    if (sh + W > 32) out[wd + 1] |= u[i] >> (32 - sh);
+    for (int k = 0; k < CB; ++k) out[k / g] |= C[k] << (W * (k % g));
+  } else {
+#pragma unroll
+    for (int p = 0; p < W; ++p) out[p] = C[p];
+#pragma unroll
+    for (int k = W; k < CB; ++k)
+#pragma unroll
+      for (int p = 0; p < W; ++p) out[p] |= ((C[k] >> p) & rep) << k;
   }
 }
 
@@ -543,15 +564,24 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
 #pragma unroll
     for (int i = 0; i < kR; ++i) v[i] = r * kR + i < n ? v[i] - m : 0u;
     uint32_t words[8];
-    switch (w) {
-      case 1: pack_run<1>(v, words); break;
-      case 2: pack_run<2>(v, words); break;
-      case 3: pack_run<3>(v, words); break;
-      case 4: pack_run<4>(v, words); break;
-      case 5: pack_run<5>(v, words); break;
-      case 6: pack_run<6>(v, words); break;
-      case 7: pack_run<7>(v, words); break;
-      default: pack_run<8>(v, words); break;
+    if (hb == 1) {                                   // nibble containers (b <= 4)
+      switch (w) {
+        case 1: pack_run<1, 4>(v, words); break;
+        case 2: pack_run<2, 4>(v, words); break;
+        case 3: pack_run<3, 4>(v, words); break;
+        default: pack_run<4, 4>(v, words); break;
+      }
+    } else {                                         // byte containers (b = 5..8)
+      switch (w) {
+        case 1: pack_run<1, 8>(v, words); break;
+        case 2: pack_run<2, 8>(v, words); break;
+        case 3: pack_run<3, 8>(v, words); break;
+        case 4: pack_run<4, 8>(v, words); break;
+        case 5: pack_run<5, 8>(v, words); break;
+        case 6: pack_run<6, 8>(v, words); break;
+        case 7: pack_run<7, 8>(v, words); break;
+        default: pack_run<8, 8>(v, words); break;
+      }
     }
     uint32_t* dst = reinterpret_cast<uint32_t*>((is_v ? vrec + v_pay : krec + k_pay)) + woff;
     for (uint32_t i = 0; i < w; ++i) dst[i] = words[i];

@@ -1004,20 +1004,10 @@ struct DecW {
   static constexpr int NRL = NR * kD / 64;
   static constexpr int HDR = hdr_offset(IS_V, B);
 
-  // the R fields of width W of a run's W words, spread to bytes
+  // the R fields of width W of a run's W words, as byte containers
   template <int W>
   __device__ __forceinline__ static void spread(const uint32_t (&wd)[8], uint32_t (&out)[8]) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) out[k] = 0u;
-    if constexpr (W > 0) {
-#pragma unroll
-      for (int i = 0; i < kR; ++i) {
-        const int p = i * W, wi = p >> 5, sh = p & 31;
-        uint32_t v = wd[wi] >> sh;
-        if (sh + W > 32) v |= wd[wi + 1] << (32 - sh);
-        out[i >> 2] |= (v & ((1u << W) - 1u)) << (8 * (i & 3));
-      }
-    }
+    sliced_to_bytes<W>(wd, out);
   }
 
   __device__ __forceinline__ static bool decode(const uint8_t* rec, uint32_t size, int nr, int lane, int bits,
@@ -1862,27 +1852,36 @@ __global__ __launch_bounds__(64) void k_decompress(GemvArgs a, const uint8_t* pe
     const int ri = lane + 64 * k;
     const int r = ri / kD, c = ri % kD;
     if (r >= nr) continue;
-    uint32_t wd[4], nib[4];
+    // the run's containers: nibbles holding q (b <= 4) or bytes holding u
+    uint32_t nib[4], byt[8];
     if constexpr (!WIDE) {
+      uint32_t wd[4];
       run_words(rec, pay, ro[k], false, wd);
       run_to_nibbles(w[k], m[k], wd, nib);
+    } else {
+      // a consistent record keeps the run's w words inside the staging
+      const uint32_t* pw = reinterpret_cast<const uint32_t*>(rec + pay) + ro[k];
+      uint32_t wd[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wd[i] = i < w[k] ? pw[i] : 0u;
+      switch (w[k]) {
+        case 0: sliced_to_bytes<0>(wd, byt); break;
+        case 1: sliced_to_bytes<1>(wd, byt); break;
+        case 2: sliced_to_bytes<2>(wd, byt); break;
+        case 3: sliced_to_bytes<3>(wd, byt); break;
+        case 4: sliced_to_bytes<4>(wd, byt); break;
+        case 5: sliced_to_bytes<5>(wd, byt); break;
+        case 6: sliced_to_bytes<6>(wd, byt); break;
+        case 7: sliced_to_bytes<7>(wd, byt); break;
+        default: sliced_to_bytes<8>(wd, byt); break;
+      }
     }
-    // wide: field i of the run's w words, read from the staged record
-    const uint32_t* pw = reinterpret_cast<const uint32_t*>(rec + pay) + ro[k];
-    const int wk = w[k];
     for (int i = 0; i < kR; ++i) {
       const int sl = r * kR + i;
       if (sl >= n) break;
       uint32_t qv;
       if constexpr (WIDE) {
-        uint32_t u = 0u;
-        if (wk > 0) {
-          const int p = i * wk, wi = p >> 5, sh = p & 31;
-          uint32_t v = pw[wi] >> sh;
-          if (sh + wk > 32) v |= pw[wi + 1] << (32 - sh);
-          u = v & ((1u << wk) - 1u);
-        }
-        qv = m[k] + u;
+        qv = m[k] + ((byt[i >> 2] >> (8 * (i & 3))) & 255u);
       } else {
         qv = (nib[i >> 3] >> (4 * (i & 7))) & 15u;
       }

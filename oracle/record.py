@@ -12,8 +12,20 @@ channel over consecutive tokens.  Readings adopted:
   u = q - m; the header entry of the run is the byte (w << 4) | m for
   b <= 4 and the little-endian u16 (w << 8) | m for b = 5..8 (hb = 1 or 2
   bytes per entry);
-* the R slots of a run fill exactly w little-endian 32-bit words, slot i in
-  bits [i*w, i*w + w) of the run's 32*w-bit string; slots past n hold u = 0.
+* the R slots of a run fill exactly w little-endian 32-bit words; slots
+  past n hold u = 0.  The bits are laid out for a decoder that works on
+  "container" words: with c-bit containers (c = 4 for b <= 4, c = 8 for
+  b = 5..8), slot i belongs to container word k = i // (32/c), field
+  j = i % (32/c), and bit p (p < w) of its u is stored in run word W at
+  bit c*j + Q, where
+    - if w divides c (g = c/w containers share a word): W = k // g,
+      Q = w*(k % g) + p;
+    - otherwise, if k < w: W = k, Q = p (the container's low w bits);
+    - otherwise: W = p, Q = k (the spare high bits of every word).
+  The pages fix no bit order; they only ask that the packed layout suit
+  the GPU that consumes it (explainer page, "PackKV as a staged dataflow").
+  With this order a decoder rebuilds each container word (every slot's u in
+  its own c-bit field) from the run words with a few shifts and masks.
 
 Record of one block (all integers little-endian, every section contiguous):
 
@@ -56,8 +68,24 @@ def run_widths(q_slots: np.ndarray, run: int):
     return w, m
 
 
-def pack_payload(q_slots: np.ndarray, w: np.ndarray, m: np.ndarray, run: int) -> bytes:
-    """The payload words of all (run, channel) pairs, run-major then channel."""
+def bit_place(i: int, p: int, w: int, cont: int):
+    """(word, bit) of bit p of slot i's u in a run stored at width w, for
+    cont-bit containers (the layout rule in the module docstring)."""
+    k, j = divmod(i, 32 // cont)
+    if cont % w == 0:
+        g = cont // w
+        word, q = k // g, w * (k % g) + p
+    elif k < w:
+        word, q = k, p
+    else:
+        word, q = p, k
+    return word, cont * j + q
+
+
+def pack_payload(q_slots: np.ndarray, w: np.ndarray, m: np.ndarray, run: int, cont: int = 4) -> bytes:
+    """The payload words of all (run, channel) pairs, run-major then channel;
+    cont = container bits (4 for b <= 4, 8 for b = 5..8)."""
+    assert run == 32 and cont in (4, 8)
     q = np.asarray(q_slots, dtype=np.int64)
     n, D = q.shape
     out = bytearray()
@@ -66,12 +94,15 @@ def pack_payload(q_slots: np.ndarray, w: np.ndarray, m: np.ndarray, run: int) ->
             wr = int(w[r, c])
             if wr == 0:
                 continue
+            assert wr <= cont
             bits = 0
             for i in range(run):
                 t = r * run + i
                 u = int(q[t, c] - m[r, c]) if t < n else 0
                 assert 0 <= u < (1 << wr)
-                bits |= u << (i * wr)
+                for p in range(wr):
+                    word, pos = bit_place(i, p, wr, cont)
+                    bits |= ((u >> p) & 1) << (32 * word + pos)
             out += bits.to_bytes(4 * wr, "little")
     return bytes(out)
 
@@ -109,7 +140,7 @@ def build_record(kind: str, q_slots, scale, zero, block: int, run: int, hb: int 
     head = f16_bits(sc).astype("<u2").tobytes() + f16_bits(ze).astype("<u2").tobytes()
     head += header_bytes(w, m, hb)
     head += bytes(_pad16(len(head)) - len(head))
-    body = pack_payload(q, w, m, run)
+    body = pack_payload(q, w, m, run, 4 * hb)
     body += bytes(_pad16(len(body)) - len(body))
     return head + body
 

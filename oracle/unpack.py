@@ -1,8 +1,15 @@
 """Record bytes -> quantised integers (oracle decoder).
 
-A second implementation of the record layout described in ``record``:
-vectorised 64-bit window reads here, against per-run big-integer assembly
-there, so a shared misreading of the bit order would have to be made twice.
+A second implementation of the record layout described in ``record``: the
+encoder there places every bit of every slot; here each run's container
+words (one c-bit field per slot) are rebuilt from its w words with shifts
+and masks, so a shared misreading of the bit order would have to be made
+twice:
+
+* w divides c (g = c/w containers per word): container k is word k // g
+  shifted right by w*(k % g), masked to w bits per field;
+* otherwise container k < w is word k masked to its low w bits per field,
+  and container k >= w collects bit k of every field of word p as its bit p.
 """
 
 from __future__ import annotations
@@ -39,16 +46,33 @@ def decode_record(kind: str, buf: bytes, n: int, D: int, block: int, run: int, h
         w, m = hdr >> 8, hdr & 255
     p0 = (4 * n_par + hb * nr * D + 15) // 16 * 16
     nwords = int(w.sum())
-    words = np.frombuffer(buf[p0:p0 + 4 * nwords], dtype="<u4").astype(np.uint64)
-    words = np.concatenate([words, np.zeros(1, np.uint64)])       # window guard
+    words = np.frombuffer(buf[p0:p0 + 4 * nwords], dtype="<u4").astype(np.int64)
     start = np.concatenate([[0], np.cumsum(w.ravel())[:-1]]).reshape(nr, D)
-    i = np.arange(run)
-    bitpos = i[None, None, :] * w[:, :, None]                          # [nr, D, R]
-    widx = start[:, :, None] + (bitpos >> 5)
-    window = words[widx] | (words[np.minimum(widx + 1, nwords)] << np.uint64(32))
-    mask = (np.uint64(1) << w[:, :, None].astype(np.uint64)) - np.uint64(1)
-    u = ((window >> (bitpos & 31).astype(np.uint64)) & mask).astype(np.int64)
-    q_runs = u + m[:, :, None]                                          # [nr, D, R]
+    cb = 4 * hb                                   # container bits
+    per = 32 // cb                                # slots per container word
+    rep1 = sum(1 << (cb * j) for j in range(per))  # bit 0 of every field
+    assert run == 32
+    u = np.zeros((nr * D, run), np.int64)
+    wf, sf = w.ravel(), start.ravel()
+    for wr in range(1, cb + 1):                   # all runs of one width at once
+        idx = np.nonzero(wf == wr)[0]
+        if idx.size == 0:
+            continue
+        P = words[sf[idx][:, None] + np.arange(wr)[None, :]]           # [runs, wr]
+        low = ((1 << wr) - 1) * rep1
+        C = np.zeros((idx.size, cb), np.int64)                          # container words
+        for k in range(cb):
+            if cb % wr == 0:
+                g = cb // wr
+                C[:, k] = (P[:, k // g] >> (wr * (k % g))) & low
+            elif k < wr:
+                C[:, k] = P[:, k] & low
+            else:
+                for pb in range(wr):
+                    C[:, k] |= ((P[:, pb] >> k) & rep1) << pb
+        fields = (C[:, :, None] >> (cb * np.arange(per))[None, None, :]) & ((1 << cb) - 1)
+        u[idx] = fields.reshape(idx.size, run)                         # slot k*per + j
+    q_runs = u.reshape(nr, D, run) + m[:, :, None]                      # [nr, D, R]
     q = q_runs.transpose(0, 2, 1).reshape(nr * run, D)[:n]
     size = p0 + (4 * nwords + 15) // 16 * 16
     if kind == "V":

@@ -262,7 +262,7 @@ def test_cr_counts_the_bits_the_packer_writes():
             rec = b.k_record if which == "K" else b.v_record
             qs = b.qk_slots if which == "K" else b.qv_slots
             w, m = record.run_widths(qs, 32)
-            payload = record.pack_payload(qs, w, m, 32)
+            payload = record.pack_payload(qs, w, m, 32, 4)
             par = 32 * 128 if which == "K" else 32 * len(b.perm)
             total += 8 * len(payload) + 8 * w.size + par
         assert r["ideal_bits"] == total

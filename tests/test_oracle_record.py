@@ -24,6 +24,7 @@ def bitstring_decode(kind, buf, n, D, B, R, hb=1):
     p0 = -(-(4 * npar + hb * nr * D) // 16) * 16
     q = np.zeros((nr * R, D), np.int64)
     pos = p0
+    cb = 4 * hb                    # container field bits: 4 (b <= 4) or 8
     for r in range(nr):
         for c in range(D):
             w, m = hdr[r * D + c] >> wsh, hdr[r * D + c] & mmask
@@ -33,9 +34,62 @@ def bitstring_decode(kind, buf, n, D, B, R, hb=1):
             s = "".join(format(words[4 * j + (k // 8) % 4], "08b")[::-1][k % 8]
                         for j in range(w) for k in range(32))
             for i in range(R):
-                u = int(s[i * w:(i + 1) * w][::-1], 2) if w else 0
+                # slot i sits in field f of container t; its bit p is in word
+                # (t*w) // cb at cb*f + (t*w) % cb + p when w divides cb, else
+                # in word t at cb*f + p (t < w) or in word p at cb*f + t
+                t, f = i // (32 // cb), i % (32 // cb)
+                u = 0
+                for p in range(w):
+                    if cb % w == 0:
+                        word, bit = (t * w) // cb, cb * f + (t * w) % cb + p
+                    elif t < w:
+                        word, bit = t, cb * f + p
+                    else:
+                        word, bit = p, cb * f + t
+                    u |= int(s[32 * word + bit]) << p
                 q[r * R + i, c] = m + u
     return q[:n], pos
+
+
+# Run words worked out by hand from the layout rule: (container bits, u of
+# slots 0..31, expected run words).
+HAND_RUNS = [
+    # w = 4, nibbles: slot 8k + j in nibble j of word k (the plain order)
+    (4, [i % 16 for i in range(32)], [0x76543210, 0xFEDCBA98, 0x76543210, 0xFEDCBA98]),
+    # w = 3, nibbles: containers 0..2 in the low 3 bits of words 0..2; bit p
+    # of container 3 (slots 24..31, u = j) in bit 3 of nibble j of word p
+    (4, [i % 8 for i in range(32)], [0xF6D4B290, 0xFE54BA10, 0xFEDC3210]),
+    # w = 2: word 0 = container 0 | container 1 << 2, word 1 = 2 | 3 << 2
+    (4, [i % 4 for i in range(32)], [0xFA50FA50, 0xFA50FA50]),
+    # w = 1: word 0 = sum of container k << k; slots 8..15 and 24..31 are 1
+    (4, [(i >> 3) & 1 for i in range(32)], [0xAAAAAAAA]),
+    # w = 5, bytes: containers 0..4 (slots 0..19) in the low 5 bits of words
+    # 0..4; bit p of containers 5, 6, 7 (slots 20..31) in bits 5, 6, 7 of
+    # byte j of word p
+    (8, list(range(32)), [0xE302E100, 0xE7E60504, 0xABAAA9A8, 0xCFCECDCC, 0xF3F2F1F0]),
+    # w = 4, bytes: word i = container 2i | container 2i+1 << 4
+    (8, [i % 16 for i in range(32)], [0x73625140, 0xFBEAD9C8, 0x73625140, 0xFBEAD9C8]),
+]
+
+
+@pytest.mark.parametrize("cb,u,words", HAND_RUNS)
+def test_run_layout_by_hand(cb, u, words):
+    """The payload words of one run, built by hand from the layout rule, are
+    what the encoder writes, and both readers recover the values."""
+    w = max(u).bit_length()
+    assert w == len(words)
+    q = np.zeros((32, 128), np.int64)
+    q[:, 5] = u
+    q[0, :] = np.maximum(q[0, :], 0)
+    wr, mr = record.run_widths(q, 32)
+    assert wr[0, 5] == w and mr[0, 5] == 0
+    pay = record.pack_payload(q, wr, mr, 32, cb)
+    got = np.frombuffer(pay, "<u4")                       # only channel 5 has w > 0
+    assert [int(x) for x in got] == words
+    hb = cb // 4
+    rec = record.build_record("K", q, np.ones(128), np.zeros(128), 64, 32, hb=hb)
+    assert np.array_equal(unpack.decode_record("K", rec, 32, 128, 64, 32, hb).q, q)
+    assert np.array_equal(bitstring_decode("K", rec, 32, 128, 64, 32, hb)[0], q)
 
 
 def test_width_is_minimal():
@@ -78,7 +132,7 @@ def test_record_roundtrip_and_layout(bits, block, n):
         assert not any(rec[hdr_end:p0])                   # header padding is zero
         assert np.all(d.w <= bits)
         # padding slots of a partial last run are zero bits: re-pack check
-        assert record.pack_payload(qs, d.w, d.m, 32) == rec[p0:p0 + 4 * int(d.w.sum())]
+        assert record.pack_payload(qs, d.w, d.m, 32, 4 * hb) == rec[p0:p0 + 4 * int(d.w.sum())]
 
 
 @pytest.mark.parametrize("D,bits,block", [(64, 4, 64), (64, 7, 128), (256, 3, 64), (256, 8, 128)])
