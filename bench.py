@@ -246,7 +246,7 @@ def summarize_profile(pdir: str, workload: str) -> None:
              f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/kt -o run -- "
              f"python bench.py --workload {workload} --steps 20 --warmup 5 --no-cpu-baseline > <dir>/kt.log",
              f"rocprofv3 --pmc <counters> --output-format csv -d <dir>/p<i> -o run -- "
-             f"python bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline",
+             f"python bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline --no-paged",
              f"python bench.py --summarize <dir> --workload {workload}", "```", "",
              "Counter passes: (1) SQ_WAVES SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU SQ_INSTS_VMEM_RD "
              "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_LDS; (2) SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS "
