@@ -21,7 +21,7 @@ ARCH = "gfx950"
 SOURCES = ["encode.hip", "gemv.hip", "api.hip"]
 
 COMMON = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
     # packed fp32 instructions stay off on this hardware
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", f"-I{INCLUDE}",

@@ -14,6 +14,7 @@ import torch
 
 from . import _lib
 
+# head_dim of the paged cache (the contiguous cache takes 64, 128 or 256)
 D = 128
 
 
@@ -33,10 +34,11 @@ class PackedKVCache:
     """
 
     def __init__(self, n_streams: int, max_tokens: int, bits: int = 4, block: int = 64,
-                 permute: int = 1, device: str = "cuda"):
+                 permute: int = 1, device: str = "cuda", head_dim: int = 128):
         # permute: 0 identity, 1 greedy grouping, 2 sort key (True/False = 1/0)
         lib = _lib.load()
-        self.cfg = _lib.Config(D, bits, block, 32, int(permute))
+        self.head_dim = head_dim
+        self.cfg = _lib.Config(head_dim, bits, block, 32, int(permute))
         sz = _lib.Sizes()
         _lib.check(lib.packkv_cache_sizes(ctypes.byref(self.cfg), n_streams, max_tokens, ctypes.byref(sz)),
                    "packkv_cache_sizes")
@@ -49,7 +51,7 @@ class PackedKVCache:
         self.k_off = torch.zeros(n_streams * (sz.max_blocks + 1), dtype=torch.int32, device=dev)
         self.v_off = torch.zeros_like(self.k_off)
         self.perm = torch.full((sz.perm_bytes,), 0xFF, dtype=torch.uint8, device=dev)
-        self.tail_k = torch.zeros(n_streams * block * D, dtype=torch.float16, device=dev)
+        self.tail_k = torch.zeros(n_streams * block * self.head_dim, dtype=torch.float16, device=dev)
         self.tail_v = torch.zeros_like(self.tail_k)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         self._c = _lib.CacheT(self.cfg, n_streams, max_tokens, 0, sz.arena_stride,
@@ -94,14 +96,14 @@ class PackedKVCache:
     def _check_kv(self, k, v):
         if k.dtype != torch.float16 or v.dtype != torch.float16 or not k.is_contiguous() or \
                 not v.is_contiguous() or k.shape != v.shape or k.dim() != 3 or \
-                k.shape[0] != self.n_streams or k.shape[2] != D or not k.is_cuda:
+                k.shape[0] != self.n_streams or k.shape[2] != self.head_dim or not k.is_cuda:
             raise ValueError("k and v must be contiguous fp16 CUDA tensors [S][T][D]")
 
     # ------------------------------------------------------------- decoding
     def qk(self, q: torch.Tensor, scores: Optional[torch.Tensor] = None) -> torch.Tensor:
         """scores[s][g][t] = q[s][g] . K_hat[s][t] (slot order); q fp16 [S][G][D]."""
         S, G, d = q.shape
-        if q.dtype != torch.float16 or S != self.n_streams or d != D or not q.is_contiguous():
+        if q.dtype != torch.float16 or S != self.n_streams or d != self.head_dim or not q.is_contiguous():
             raise ValueError("q must be contiguous fp16 [S][G][D]")
         T = self.n_tokens
         if scores is None:
@@ -131,7 +133,7 @@ class PackedKVCache:
         if p.dtype != torch.float32 or S != self.n_streams or not p.is_contiguous():
             raise ValueError("p must be contiguous fp32 [S][G][ld]")
         if out is None:
-            out = torch.empty(S, G, D, dtype=torch.float32, device=p.device)
+            out = torch.empty(S, G, self.head_dim, dtype=torch.float32, device=p.device)
         ws = self.workspace(G) if workspace is None else workspace
         _lib.check(_lib.load().packkv_pv_gemv(ctypes.byref(self._c), _ptr(p), ld, G, _ptr(out), _ptr(ws),
                                               ws.numel() * ws.element_size(), _stream()),
@@ -153,14 +155,14 @@ class PackedKVCache:
         """out[s][g] = softmax(scale * q[s][g] . K_hat[s]^T) V_hat[s] in one launch;
         q fp16 [S][G][D], scale defaults to 1/sqrt(D)."""
         S, G, d = q.shape
-        if q.dtype != torch.float16 or S != self.n_streams or d != D or not q.is_contiguous():
+        if q.dtype != torch.float16 or S != self.n_streams or d != self.head_dim or not q.is_contiguous():
             raise ValueError("q must be contiguous fp16 [S][G][D]")
         if out is None:
-            out = torch.empty(S, G, D, dtype=torch.float32, device=q.device)
-        if out.dtype != torch.float32 or tuple(out.shape) != (S, G, D) or not out.is_contiguous():
+            out = torch.empty(S, G, self.head_dim, dtype=torch.float32, device=q.device)
+        if out.dtype != torch.float32 or tuple(out.shape) != (S, G, self.head_dim) or not out.is_contiguous():
             raise ValueError("out must be contiguous fp32 [S][G][D]")
         ws = self.attention_workspace(G) if workspace is None else workspace
-        sc = D ** -0.5 if scale is None else float(scale)
+        sc = self.head_dim ** -0.5 if scale is None else float(scale)
         _lib.check(_lib.load().packkv_attention_decode(ctypes.byref(self._c), _ptr(q), G, sc, _ptr(out), _ptr(ws),
                                                        ws.numel() * ws.element_size(), _stream()),
                    "packkv_attention_decode")
@@ -171,11 +173,11 @@ class PackedKVCache:
         the library's own per-GPU scratch array instead (the caller passes
         out, fp32 [S][G][D]); bit-identical results."""
         S, G, d = q.shape
-        if q.dtype != torch.float16 or S != self.n_streams or d != D or not q.is_contiguous():
+        if q.dtype != torch.float16 or S != self.n_streams or d != self.head_dim or not q.is_contiguous():
             raise ValueError("q must be contiguous fp16 [S][G][D]")
-        if out.dtype != torch.float32 or tuple(out.shape) != (S, G, D) or not out.is_contiguous():
+        if out.dtype != torch.float32 or tuple(out.shape) != (S, G, self.head_dim) or not out.is_contiguous():
             raise ValueError("out must be contiguous fp32 [S][G][D]")
-        sc = D ** -0.5 if scale is None else float(scale)
+        sc = self.head_dim ** -0.5 if scale is None else float(scale)
         _lib.check(_lib.load().packkv_attention_decode_noalloc(ctypes.byref(self._c), _ptr(q), G, sc, _ptr(out),
                                                                _stream()), "packkv_attention_decode_noalloc")
         return out
@@ -184,7 +186,7 @@ class PackedKVCache:
         """mode 0: uint8 q [S][T][D] slot order; mode 1: fp32 x_hat [S][T][D] token order."""
         T = self.n_tokens
         dt = torch.uint8 if mode == 0 else torch.float32
-        out = torch.zeros(self.n_streams, T, D, dtype=dt, device=self.k_arena.device)
+        out = torch.zeros(self.n_streams, T, self.head_dim, dtype=dt, device=self.k_arena.device)
         _lib.check(_lib.load().packkv_decompress(ctypes.byref(self._c), 0 if which == "K" else 1, mode,
                                                  _ptr(out), _stream()), "packkv_decompress")
         return out
@@ -227,6 +229,7 @@ def attention_multi(caches, q: torch.Tensor, scale: Optional[float] = None, out:
     L, S, G, d = q.shape
     if L != len(caches) or L < 1:
         raise ValueError("q must have one [S][G][D] slice per cache")
+    D = caches[0].head_dim
     if q.dtype != torch.float16 or d != D or not q.is_contiguous():
         raise ValueError("q must be contiguous fp16 [L][S][G][D]")
     if out is None:

@@ -16,7 +16,7 @@ constexpr uint64_t kArenaSlack = 64;   // over-read room for 16-byte vector load
 
 int check_cfg(const packkv_config_t* c) {
   if (!c) return PACKKV_EINVAL;
-  if (c->head_dim != kD || c->run_tokens != kR) return PACKKV_EUNSUPPORTED;
+  if (!head_dim_ok(c->head_dim) || c->run_tokens != kR) return PACKKV_EUNSUPPORTED;
   if (c->bits < 2 || c->bits > 8) return PACKKV_EUNSUPPORTED;
   if (c->block_tokens != 64 && c->block_tokens != 128) return PACKKV_EUNSUPPORTED;
   if (c->permute < 0 || c->permute > 2) return PACKKV_EINVAL;
@@ -29,8 +29,8 @@ int64_t max_blocks_of(const packkv_config_t* c, int64_t max_tokens) {
 
 uint64_t stride_bytes(const packkv_config_t* c, int64_t max_tokens) {
   const int B = c->block_tokens;
-  const uint64_t rk = (uint64_t)max_record_bytes(false, B, c->bits);
-  const uint64_t rv = (uint64_t)max_record_bytes(true, B, c->bits);
+  const uint64_t rk = (uint64_t)max_record_bytes(false, B, c->bits, c->head_dim);
+  const uint64_t rv = (uint64_t)max_record_bytes(true, B, c->bits, c->head_dim);
   const uint64_t per = rk > rv ? rk : rv;
   const uint64_t need = (uint64_t)max_blocks_of(c, max_tokens) * per + kArenaSlack;
   return (need + 255) & ~(uint64_t)255;
@@ -96,8 +96,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? PACKKV_OK : PACKKV_EHIP;
 // 32 streams of 131072 tokens, four queries per stream: 86 -> 48 splits,
 // fused attention 204 -> 178 us; with hundreds of streams (three or more
 // rounds) one round measured slower and the default stays.
-int attention_splits(int64_t units, int splits, int nb, int B, int bits, int G) {
-  const int64_t R = attention_resident_wgs(B, bits, G);
+int attention_splits(int64_t units, int splits, int nb, int B, int bits, int G, int D) {
+  const int64_t R = attention_resident_wgs(B, bits, G, D);
   if (R <= 0 || units <= 0 || units * splits > 2 * R) return splits;
   const int64_t sp = R / units;
   if (sp < 1 || sp >= splits || (nb + sp - 1) / sp > 64) return splits;
@@ -114,6 +114,7 @@ GemvArgs gemv_args(const packkv_cache_t* c, bool is_v, int group = 1) {
   a.n_tokens = c->n_tokens;
   a.nb = (int)((c->n_tokens + c->cfg.block_tokens - 1) / c->cfg.block_tokens);
   a.bits = c->cfg.bits;
+  a.D = c->cfg.head_dim;
   a.blocks_per_wg = gemv_blocks_per_wg(c->n_streams, a.nb, is_v, group, c->cfg.bits);
   a.splits = (a.nb + a.blocks_per_wg - 1) / a.blocks_per_wg;
   a.status = c->status;
@@ -125,6 +126,7 @@ EncArgs enc_args(const packkv_cache_t* c) {
   memset(&a, 0, sizeof(a));
   a.bits = c->cfg.bits;
   a.B = c->cfg.block_tokens;
+  a.D = c->cfg.head_dim;
   a.permute = c->cfg.permute;
   a.k_arena = c->k_arena;
   a.v_arena = c->v_arena;
@@ -155,7 +157,7 @@ int packkv_cache_sizes(const packkv_config_t* cfg, int32_t n_streams, int64_t ma
   out->arena_bytes = (uint64_t)n_streams * out->arena_stride;
   out->off_bytes = (uint64_t)n_streams * (uint64_t)(mb + 1) * 4;
   out->perm_bytes = (uint64_t)n_streams * (uint64_t)mb * (uint64_t)cfg->block_tokens;
-  out->tail_bytes = (uint64_t)n_streams * (uint64_t)cfg->block_tokens * kD * 2;
+  out->tail_bytes = (uint64_t)n_streams * (uint64_t)cfg->block_tokens * (uint64_t)cfg->head_dim * 2;
   return PACKKV_OK;
 }
 
@@ -169,7 +171,7 @@ uint64_t packkv_arena_stride_bytes(const packkv_config_t* cfg, int64_t max_token
 static uint64_t pv_partial_bytes(const packkv_cache_t* c, int32_t group) {
   const int64_t mb = max_blocks_of(&c->cfg, c->max_tokens);
   const int64_t splits = (mb + 3) / 4;     // blocks per workgroup is at least 4
-  return (uint64_t)c->n_streams * (uint64_t)group * (uint64_t)splits * kD * sizeof(float);
+  return (uint64_t)c->n_streams * (uint64_t)group * (uint64_t)splits * (uint64_t)c->cfg.head_dim * sizeof(float);
 }
 
 uint64_t packkv_pv_workspace_bytes(const packkv_cache_t* c, int32_t group) {
@@ -186,13 +188,13 @@ int packkv_compress_block(packkv_cache_t* c, const void* k_f16, const void* v_f1
   if (c->n_tokens != 0) return PACKKV_ESTATE;
   if (n_tokens > c->max_tokens) return PACKKV_ECAPACITY;
   hipStream_t st = (hipStream_t)stream;
-  const int B = c->cfg.block_tokens;
+  const int B = c->cfg.block_tokens, D = c->cfg.head_dim;
   const int nb = (int)((n_tokens + B - 1) / B);
   EncArgs a = enc_args(c);
   a.k = (const uint16_t*)k_f16;
   a.v = (const uint16_t*)v_f16;
-  a.src_stream = n_tokens * kD;
-  a.src_block = (int64_t)B * kD;
+  a.src_stream = n_tokens * D;
+  a.src_block = (int64_t)B * D;
   a.n_tokens = n_tokens;
   a.mode = kPass1;
   if ((e = hip_status(launch_encode(a, c->n_streams, nb, st)))) return e;
@@ -203,9 +205,9 @@ int packkv_compress_block(packkv_cache_t* c, const void* k_f16, const void* v_f1
   const int64_t nfull = n_tokens / B;
   const int rem = (int)(n_tokens - nfull * B);
   if (rem) {
-    e = hip_status(launch_stage_tail((const uint16_t*)k_f16 + nfull * B * kD,
-                                     (const uint16_t*)v_f16 + nfull * B * kD, n_tokens * kD, c->tail_k,
-                                     c->tail_v, B, 0, rem, c->n_streams, st));
+    e = hip_status(launch_stage_tail((const uint16_t*)k_f16 + nfull * B * D,
+                                     (const uint16_t*)v_f16 + nfull * B * D, n_tokens * D, c->tail_k,
+                                     c->tail_v, B, D, 0, rem, c->n_streams, st));
     if (e) return e;
   }
   c->n_tokens = n_tokens;
@@ -220,11 +222,11 @@ int packkv_append_tokens(packkv_cache_t* c, const void* k_f16, const void* v_f16
   if (((uintptr_t)k_f16 | (uintptr_t)v_f16) & 15u) return PACKKV_EINVAL;   // read with 16-byte loads
   if (c->n_tokens + n_new > c->max_tokens) return PACKKV_ECAPACITY;
   hipStream_t st = (hipStream_t)stream;
-  const int B = c->cfg.block_tokens;
+  const int B = c->cfg.block_tokens, D = c->cfg.head_dim;
   EncArgs a = enc_args(c);
   a.k = c->tail_k;
   a.v = c->tail_v;
-  a.src_stream = (int64_t)B * kD;
+  a.src_stream = (int64_t)B * D;
   a.src_block = 0;
   a.mode = kTail;
   int done = 0;
@@ -233,9 +235,9 @@ int packkv_append_tokens(packkv_cache_t* c, const void* k_f16, const void* v_f16
     const int n_tail = (int)(T % B);
     const int cnt = (n_new - done) < (B - n_tail) ? (n_new - done) : (B - n_tail);
     // the encoder reads the new tokens from the caller and stages them itself
-    a.new_k = (const uint16_t*)k_f16 + (int64_t)done * kD;
-    a.new_v = (const uint16_t*)v_f16 + (int64_t)done * kD;
-    a.new_stream = (int64_t)n_new * kD;
+    a.new_k = (const uint16_t*)k_f16 + (int64_t)done * D;
+    a.new_v = (const uint16_t*)v_f16 + (int64_t)done * D;
+    a.new_stream = (int64_t)n_new * D;
     a.new_at = n_tail;
     a.block0 = (int)(T / B);
     a.n_tokens = T + cnt;
@@ -279,12 +281,13 @@ int packkv_pv_gemv(const packkv_cache_t* c, const float* p, int64_t ld, int32_t 
   return hip_status(launch_pv(a, c->cfg.block_tokens, c->n_streams, (hipStream_t)stream));
 }
 
-// Attention workspace: per (stream, query, split) kAttnPartial floats, then
+// Attention workspace: per (stream, query, split) D + 4 floats, then
 // one u32 arrival counter per stream.
 static uint64_t attn_partial_bytes(const packkv_cache_t* c, int32_t group) {
   const int64_t mb = max_blocks_of(&c->cfg, c->max_tokens);
   const int64_t splits = (mb + 3) / 4;     // blocks per workgroup is at least 4
-  return (uint64_t)c->n_streams * (uint64_t)group * (uint64_t)splits * kAttnPartial * sizeof(float);
+  return (uint64_t)c->n_streams * (uint64_t)group * (uint64_t)splits * attn_partial_floats(c->cfg.head_dim) *
+         sizeof(float);
 }
 
 uint64_t packkv_attention_workspace_bytes(const packkv_cache_t* c, int32_t group) {
@@ -306,10 +309,11 @@ static AttnArgs attention_args(const packkv_cache_t* c, int32_t n, int32_t group
   a.bits = c->cfg.bits;
   a.blocks_per_wg = g.blocks_per_wg;
   a.splits = attention_splits((int64_t)c->n_streams * (n < kAttnMaxCaches ? n : kAttnMaxCaches), g.splits, g.nb,
-                              c->cfg.block_tokens, c->cfg.bits, group);
+                              c->cfg.block_tokens, c->cfg.bits, group, c->cfg.head_dim);
   a.G = group;
   a.scale_log2e = scale * 1.4426950408889634f;
-  a.qo_stride = (int64_t)c->n_streams * group * kD;
+  a.qo_stride = (int64_t)c->n_streams * group * c->cfg.head_dim;
+  a.D = c->cfg.head_dim;
   return a;
 }
 
@@ -324,7 +328,7 @@ static int attention_decode(const packkv_cache_t* const* cs, int32_t n, const vo
   for (int32_t i = 1; i < n; ++i) {
     const packkv_cache_t* d = cs[i];
     if ((e = check_cache(d))) return e;
-    if (d->cfg.bits != c->cfg.bits || d->cfg.block_tokens != c->cfg.block_tokens ||
+    if (d->cfg.bits != c->cfg.bits || d->cfg.block_tokens != c->cfg.block_tokens || d->cfg.head_dim != c->cfg.head_dim ||
         d->n_streams != c->n_streams || d->max_tokens != c->max_tokens || d->n_tokens != c->n_tokens ||
         d->arena_stride != c->arena_stride)
       return PACKKV_EINVAL;
@@ -417,7 +421,8 @@ int packkv_attention_decode_noalloc(const packkv_cache_t* c, const void* q_f16, 
   if (!q_f16 || !out || group < 1 || !(scale > 0.f) || !std::isfinite(scale)) return PACKKV_EINVAL;
   if (c->n_tokens < 1) return PACKKV_ESTATE;
   AttnArgs a = attention_args(c, 1, group, scale);
-  const uint64_t partials = (uint64_t)c->n_streams * (uint64_t)group * (uint64_t)a.splits * kAttnPartial * 4u;
+  const uint64_t partials =
+      (uint64_t)c->n_streams * (uint64_t)group * (uint64_t)a.splits * attn_partial_floats(c->cfg.head_dim) * 4u;
   if (c->n_streams > kScratchStreams || partials > kScratchBytes - kScratchCounterBytes) return PACKKV_ECAPACITY;
   uint8_t* base = nullptr;
   if ((e = scratch_of_current_device(&base))) return e;
@@ -506,10 +511,12 @@ const char* packkv_status_str(int s) {
 
 namespace {
 
+constexpr int kPagedD = 128;   // head_dim of the paged cache
+
 uint64_t paged_slot_bytes(const packkv_config_t* c) {
   const int B = c->block_tokens;
-  const uint64_t rk = (uint64_t)max_record_bytes(false, B, c->bits);
-  const uint64_t rv = (uint64_t)max_record_bytes(true, B, c->bits);
+  const uint64_t rk = (uint64_t)max_record_bytes(false, B, c->bits, kPagedD);
+  const uint64_t rv = (uint64_t)max_record_bytes(true, B, c->bits, kPagedD);
   return ((rk > rv ? rk : rv) + 15) & ~(uint64_t)15;
 }
 uint64_t paged_min_page(const packkv_config_t* c) { return (paged_slot_bytes(c) + 255) & ~(uint64_t)255; }
@@ -521,6 +528,7 @@ int check_paged(const packkv_paged_t* c) {
   if (!c) return PACKKV_EINVAL;
   int e = check_cfg(&c->cfg);
   if (e) return e;
+  if (c->cfg.head_dim != kPagedD) return PACKKV_EUNSUPPORTED;
   if (c->n_streams < 1 || c->n_pages < 1 || c->max_tokens < 1) return PACKKV_EINVAL;
   if (c->page_bytes % 256 || c->page_bytes < paged_min_page(&c->cfg)) return PACKKV_EINVAL;
   if (paged_pool_bytes(&c->cfg, c->n_streams, c->n_pages, c->page_bytes) >= (1ull << 36)) return PACKKV_EINVAL;
@@ -548,6 +556,7 @@ EncArgs paged_enc_args(const packkv_paged_t* c) {
   const int64_t mb = max_blocks_of(&c->cfg, c->max_tokens);
   a.bits = c->cfg.bits;
   a.B = c->cfg.block_tokens;
+  a.D = kPagedD;
   a.permute = c->cfg.permute;
   a.k_arena = c->pool;
   a.v_arena = c->pool;
@@ -567,7 +576,7 @@ EncArgs paged_enc_args(const packkv_paged_t* c) {
 uint64_t paged_partial_bytes(const packkv_paged_t* c, int32_t group) {
   const int64_t mb = max_blocks_of(&c->cfg, c->max_tokens);
   const int64_t splits = (mb + 3) / 4;     // blocks per workgroup is at least 4
-  return (uint64_t)c->n_streams * (uint64_t)group * (uint64_t)splits * kAttnPartial * sizeof(float);
+  return (uint64_t)c->n_streams * (uint64_t)group * (uint64_t)splits * attn_partial_floats(kPagedD) * sizeof(float);
 }
 
 }  // namespace
@@ -576,6 +585,7 @@ int packkv_paged_sizes(const packkv_config_t* cfg, int32_t n_streams, int64_t ma
                        uint64_t page_bytes, packkv_paged_sizes_t* out) {
   int e = check_cfg(cfg);
   if (e) return e;
+  if (cfg->head_dim != kPagedD) return PACKKV_EUNSUPPORTED;
   if (!out || n_streams < 1 || max_tokens < 1 || n_pages < 1) return PACKKV_EINVAL;
   const int64_t mb = max_blocks_of(cfg, max_tokens);
   out->max_blocks = mb;
@@ -588,7 +598,7 @@ int packkv_paged_sizes(const packkv_config_t* cfg, int32_t n_streams, int64_t ma
   out->alloc_bytes = (2u + 4u * (uint64_t)n_streams + (uint64_t)n_pages) * 4;
   out->lengths_bytes = (uint64_t)n_streams * 4;
   out->perm_bytes = (uint64_t)n_streams * (uint64_t)mb * (uint64_t)cfg->block_tokens;
-  out->tail_bytes = (uint64_t)n_streams * (uint64_t)cfg->block_tokens * kD * 2;
+  out->tail_bytes = (uint64_t)n_streams * (uint64_t)cfg->block_tokens * kPagedD * 2;
   return PACKKV_OK;
 }
 
@@ -617,8 +627,8 @@ int packkv_paged_prefill(packkv_paged_t* c, int32_t stream0, int32_t n, const vo
   a.stream0 = stream0;
   a.k = (const uint16_t*)k_f16;
   a.v = (const uint16_t*)v_f16;
-  a.src_stream = n_tokens * kD;
-  a.src_block = (int64_t)B * kD;
+  a.src_stream = n_tokens * kPagedD;
+  a.src_block = (int64_t)B * kPagedD;
   a.n_tokens = n_tokens;
   a.mode = kPass1;
   if ((e = hip_status(launch_encode(a, n, nb, st)))) return e;
@@ -628,10 +638,10 @@ int packkv_paged_prefill(packkv_paged_t* c, int32_t stream0, int32_t n, const vo
   const int64_t nfull = n_tokens / B;
   const int rem = (int)(n_tokens - nfull * B);
   if (rem) {
-    const int64_t t0 = (int64_t)stream0 * B * kD;
-    e = hip_status(launch_stage_tail((const uint16_t*)k_f16 + nfull * B * kD,
-                                     (const uint16_t*)v_f16 + nfull * B * kD, n_tokens * kD, c->tail_k + t0,
-                                     c->tail_v + t0, B, 0, rem, n, st));
+    const int64_t t0 = (int64_t)stream0 * B * kPagedD;
+    e = hip_status(launch_stage_tail((const uint16_t*)k_f16 + nfull * B * kPagedD,
+                                     (const uint16_t*)v_f16 + nfull * B * kPagedD, n_tokens * kPagedD, c->tail_k + t0,
+                                     c->tail_v + t0, B, kPagedD, 0, rem, n, st));
     if (e) return e;
   }
   for (int32_t s = stream0; s < stream0 + n; ++s) c->host_lengths[s] = (int32_t)n_tokens;
@@ -649,11 +659,11 @@ int packkv_paged_append(packkv_paged_t* c, const void* k_f16, const void* v_f16,
   EncArgs a = paged_enc_args(c);
   a.k = c->tail_k;                // the raw staging of each open block
   a.v = c->tail_v;
-  a.src_stream = (int64_t)B * kD;
+  a.src_stream = (int64_t)B * kPagedD;
   a.mode = kTail;
   a.new_k = (const uint16_t*)k_f16;
   a.new_v = (const uint16_t*)v_f16;
-  a.new_stream = kD;              // one token per stream
+  a.new_stream = kPagedD;              // one token per stream
   if ((e = hip_status(launch_encode(a, c->n_streams, 1, (hipStream_t)stream)))) return e;
   for (int32_t s = 0; s < c->n_streams; ++s) c->host_lengths[s] += 1;
   return PACKKV_OK;
@@ -703,12 +713,13 @@ int packkv_paged_attention(const packkv_paged_t* c, const void* q_f16, int32_t g
   a.bits = c->cfg.bits;
   a.blocks_per_wg = J;
   // the same division as the contiguous cache for the same lengths
-  a.splits = attention_splits(c->n_streams, (nb + J - 1) / J, nb, B, c->cfg.bits, group);
+  a.splits = attention_splits(c->n_streams, (nb + J - 1) / J, nb, B, c->cfg.bits, group, kPagedD);
+  a.D = kPagedD;
   a.G = group;
   a.scale_log2e = scale * 1.4426950408889634f;
   a.q = (const uint16_t*)q_f16;
   a.out = out;
-  a.qo_stride = (int64_t)c->n_streams * group * kD;
+  a.qo_stride = (int64_t)c->n_streams * group * kPagedD;
   a.ws = (uint8_t*)workspace;
   a.ws_stride = need;
   a.tk = a.ws + paged_partial_bytes(c, group);

@@ -18,23 +18,29 @@
 
 namespace packkv {
 
-constexpr int kD = 128;        // head_dim
 constexpr int kR = 32;         // run length (slots)
 constexpr int kWave = 64;      // CDNA wavefront
+
+// head_dim D is 64, 128 or 256 (a template parameter of every kernel)
+__host__ __device__ constexpr bool head_dim_ok(int D) { return D == 64 || D == 128 || D == 256; }
 
 __host__ __device__ constexpr int pad16(int x) { return (x + 15) & ~15; }
 __host__ __device__ constexpr int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
 
-// Geometry of a record holding n tokens (nr runs) of a block of B tokens.
-__host__ __device__ constexpr int n_params(bool is_v, int B) { return is_v ? B : kD; }
-__host__ __device__ constexpr int hdr_offset(bool is_v, int B) { return 4 * n_params(is_v, B); }
+// Geometry of a record holding n tokens (nr runs) of a block of B tokens of
+// D channels.
+__host__ __device__ constexpr int n_params(bool is_v, int B, int D) { return is_v ? B : D; }
+__host__ __device__ constexpr int hdr_offset(bool is_v, int B, int D) { return 4 * n_params(is_v, B, D); }
 __host__ __device__ constexpr int hdr_entry_bytes(int bits) { return bits > 4 ? 2 : 1; }
-__host__ __device__ constexpr int payload_offset(bool is_v, int B, int nr, int hb = 1) {
-  return pad16(4 * n_params(is_v, B) + hb * nr * kD);
+__host__ __device__ constexpr int payload_offset(bool is_v, int B, int nr, int hb, int D) {
+  return pad16(4 * n_params(is_v, B, D) + hb * nr * D);
 }
-__host__ __device__ constexpr int max_record_bytes(bool is_v, int B, int bits) {
-  return payload_offset(is_v, B, B / kR, hdr_entry_bytes(bits)) + 4 * (B / kR) * kD * bits;
+__host__ __device__ constexpr int max_record_bytes(bool is_v, int B, int bits, int D) {
+  return payload_offset(is_v, B, B / kR, hdr_entry_bytes(bits), D) + 4 * (B / kR) * D * bits;
 }
+// Fused attention's partial result per (stream, query, split): D partial
+// sums, running max, weight sum, 2 pad
+__host__ __device__ constexpr int attn_partial_floats(int D) { return D + 4; }
 
 // ---------------------------------------------------------------------------
 // fp16 bit helpers (exact).

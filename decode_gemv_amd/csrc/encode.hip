@@ -75,6 +75,7 @@ __device__ __forceinline__ uint32_t quant_level(uint32_t x, const QuantParams& p
 // The ints of run r, channel c in slot order: v[i] = q[order[r*32 + i]][c]
 // (0 past the n slots).  The run's 32 order bytes are read first as eight
 // words, so the 32 value reads do not wait on one another.
+template <int D>
 __device__ __forceinline__ void run_values(const uint8_t* q, const uint8_t* order, int r, int c, int n,
                                            uint32_t v[kR]) {
   const int s0 = r * kR;
@@ -85,7 +86,7 @@ __device__ __forceinline__ void run_values(const uint8_t* q, const uint8_t* orde
 #pragma unroll
   for (int i = 0; i < kR; ++i) {
     const uint32_t t = (ow[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-    v[i] = s0 + i < n ? (uint32_t)q[t * kD + c] : 0u;
+    v[i] = s0 + i < n ? (uint32_t)q[t * D + c] : 0u;
   }
 }
 
@@ -125,10 +126,11 @@ __device__ __forceinline__ void pack_run(const uint32_t u[kR], uint32_t out[8]) 
 }
 
 // Min and width of run r, channel c of the slot-ordered ints q[order[slot]][c].
+template <int D>
 __device__ __forceinline__ void run_stats(const uint8_t* q, const uint8_t* order, int r, int c,
                                           int n, uint32_t& m, uint32_t& w) {
   uint32_t v[kR];
-  run_values(q, order, r, c, n, v);
+  run_values<D>(q, order, r, c, n, v);
   const int cnt = min(kR, n - r * kR);
   uint32_t lo = 255, hi = 0;
 #pragma unroll
@@ -159,18 +161,19 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh /*[256]*/, uint32_t
   return incl - v;
 }
 
-template <int B>
+template <int B, int D>
 __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
+  constexpr int NR = B / kR;
   constexpr int NT = 256;
-  __shared__ __attribute__((aligned(16))) uint8_t qk[B * kD];
-  __shared__ __attribute__((aligned(16))) uint8_t qv[B * kD];
-  __shared__ __attribute__((aligned(16))) uint16_t rawk[B * kD];
-  __shared__ uint16_t ksc[kD], kze[kD], vsc[128], vze[128];
+  __shared__ __attribute__((aligned(16))) uint8_t qk[B * D];
+  __shared__ __attribute__((aligned(16))) uint8_t qv[B * D];
+  __shared__ __attribute__((aligned(16))) uint16_t rawk[B * D];
+  __shared__ uint16_t ksc[D], kze[D], vsc[128], vze[128];
   __shared__ __attribute__((aligned(16))) uint8_t order[128];
   __shared__ __attribute__((aligned(16))) uint8_t ident[128];
   __shared__ uint8_t alive[128];
   __shared__ uint32_t key[128];
-  __shared__ uint8_t wk[4 * kD], mk[4 * kD], wv[4 * kD], mv[4 * kD];
+  __shared__ uint8_t wk[4 * D], mk[4 * D], wv[4 * D], mv[4 * D];
   __shared__ uint32_t scan_sh[NT];
   __shared__ uint32_t red[4];
 
@@ -207,11 +210,11 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
   {
     const uint4* src = reinterpret_cast<const uint4*>(ks);
     uint4* dst = reinterpret_cast<uint4*>(rawk);
-    for (int i = tid; i < n * (kD / 8); i += NT) {
-      const int t = i / (kD / 8);
+    for (int i = tid; i < n * (D / 8); i += NT) {
+      const int t = i / (D / 8);
       if (fresh && t >= new_at) {
         // an appended token: read it from the caller and keep it in the staging
-        const uint4 u = reinterpret_cast<const uint4*>(a.new_k + s * a.new_stream + (int64_t)(t - new_at) * kD)[i % (kD / 8)];
+        const uint4 u = reinterpret_cast<const uint4*>(a.new_k + s * a.new_stream + (int64_t)(t - new_at) * D)[i % (D / 8)];
         const_cast<uint4*>(src)[i] = u;
         dst[i] = u;
       } else {
@@ -223,10 +226,10 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
   // an infinite or NaN input (exponent field all ones) is outside the
   // method: it latches EINVAL; the records stay well-formed
   bool nonfinite = false;
-  if (tid < kD) {
+  if (tid < D) {
     int kmin = 0x7FFF, kmax = -0x7FFF;
     for (int t = 0; t < n; ++t) {
-      const uint32_t x = rawk[t * kD + tid];
+      const uint32_t x = rawk[t * D + tid];
       nonfinite |= (x & 0x7C00u) == 0x7C00u;
       const int k = f16_key(x);
       kmin = min(kmin, k);
@@ -235,25 +238,25 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
     const QuantParams qp = quant_params(kmin, kmax, L);
     ksc[tid] = (uint16_t)qp.hb;
     kze[tid] = (uint16_t)qp.zero;
-    for (int t = 0; t < n; ++t) qk[t * kD + tid] = (uint8_t)quant_level(rawk[t * kD + tid], qp, L);
+    for (int t = 0; t < n; ++t) qk[t * D + tid] = (uint8_t)quant_level(rawk[t * D + tid], qp, L);
   }
-  // V per token: the 128 channels of token t are split over TPT neighbouring
+  // V per token: the D channels of token t are split over TPT neighbouring
   // threads, each loading its CPT values with 16-byte loads; min and max are
   // combined across the TPT threads.
   {
-    const int TPT = NT / B;                          // 4 (B = 64) or 2 (B = 128)
-    const int CPT = kD / TPT;                        // 32 or 64 channels per thread
+    constexpr int TPT = NT / B;                      // 4 (B = 64) or 2 (B = 128)
+    constexpr int CPT = D / TPT;                     // 16 .. 128 channels per thread
     const int t = tid / TPT, part = tid % TPT;
     const bool on = t < n;
     const bool appended = fresh && on && t >= new_at;
-    uint32_t w[32];                                  // up to 64 fp16, two per word
-    uint4* stage = reinterpret_cast<uint4*>(const_cast<uint16_t*>(vs) + (int64_t)(on ? t : 0) * kD + part * CPT);
+    uint32_t w[CPT / 2];                             // CPT fp16, two per word
+    uint4* stage = reinterpret_cast<uint4*>(const_cast<uint16_t*>(vs) + (int64_t)(on ? t : 0) * D + part * CPT);
     const uint4* src = appended
-        ? reinterpret_cast<const uint4*>(a.new_v + s * a.new_stream + (int64_t)(t - new_at) * kD + part * CPT)
+        ? reinterpret_cast<const uint4*>(a.new_v + s * a.new_stream + (int64_t)(t - new_at) * D + part * CPT)
         : stage;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i < CPT / 8) {
+    for (int i = 0; i < CPT / 8; ++i) {
+      {
         const uint4 u = src[i];
         if (appended) stage[i] = u;                  // keep it in the staging
         w[4 * i] = u.x; w[4 * i + 1] = u.y; w[4 * i + 2] = u.z; w[4 * i + 3] = u.w;
@@ -261,8 +264,8 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
     }
     int kmin = 0x7FFF, kmax = -0x7FFF;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if (i < CPT / 2) {
+    for (int i = 0; i < CPT / 2; ++i) {
+      {
         nonfinite |= on && (((w[i] & 0x7C00u) == 0x7C00u) || ((w[i] & 0x7C000000u) == 0x7C000000u));
         const int a0 = f16_key(w[i] & 0xFFFFu), a1 = f16_key(w[i] >> 16);
         kmin = min(kmin, min(a0, a1));
@@ -279,10 +282,10 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
         vsc[t] = (uint16_t)qp.hb;
         vze[t] = (uint16_t)qp.zero;
       }
-      uint8_t* dst = qv + t * kD + part * CPT;
+      uint8_t* dst = qv + t * D + part * CPT;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (i < CPT / 2) {
+      for (int i = 0; i < CPT / 2; ++i) {
+        {
           dst[2 * i] = (uint8_t)quant_level(w[i] & 0xFFFFu, qp, L);
           dst[2 * i + 1] = (uint8_t)quant_level(w[i] >> 16, qp, L);
         }
@@ -304,10 +307,10 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
       // sort key: the total of the token's K and V ints (at most
       // 2 * 128 * 15 < 2^12), ties by index; the slot is the key's rank
       if (tid < n) {
-        const uint32_t* rt = reinterpret_cast<const uint32_t*>(qk + tid * kD);
-        const uint32_t* vt = reinterpret_cast<const uint32_t*>(qv + tid * kD);
+        const uint32_t* rt = reinterpret_cast<const uint32_t*>(qk + tid * D);
+        const uint32_t* vt = reinterpret_cast<const uint32_t*>(qv + tid * D);
         uint32_t total = 0;
-        for (int i = 0; i < kD / 4; ++i) {
+        for (int i = 0; i < D / 4; ++i) {
           total = __builtin_amdgcn_sad_u8(rt[i], 0u, total);
           total = __builtin_amdgcn_sad_u8(vt[i], 0u, total);
         }
@@ -339,12 +342,12 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
         if (tid < n) {
           uint32_t k0 = 0xFFFFFFFFu;
           if (alive[tid]) {
-            const uint32_t* rt = reinterpret_cast<const uint32_t*>(qk + tid * kD);
-            const uint32_t* rs = reinterpret_cast<const uint32_t*>(qk + sd * kD);
-            const uint32_t* vt = reinterpret_cast<const uint32_t*>(qv + tid * kD);
-            const uint32_t* vd = reinterpret_cast<const uint32_t*>(qv + sd * kD);
+            const uint32_t* rt = reinterpret_cast<const uint32_t*>(qk + tid * D);
+            const uint32_t* rs = reinterpret_cast<const uint32_t*>(qk + sd * D);
+            const uint32_t* vt = reinterpret_cast<const uint32_t*>(qv + tid * D);
+            const uint32_t* vd = reinterpret_cast<const uint32_t*>(qv + sd * D);
             uint32_t dist = 0;
-            for (int i = 0; i < kD / 4; ++i) {
+            for (int i = 0; i < D / 4; ++i) {
               dist = __builtin_amdgcn_sad_u8(rt[i], rs[i], dist);
               dist = __builtin_amdgcn_sad_u8(vt[i], vd[i], dist);
             }
@@ -372,19 +375,19 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
       // The statistics of both orders are kept in registers (at most 4
       // (run, channel) entries per thread), and those of the chosen order
       // become the record's widths and minima.
-      constexpr int EPT = 2 * (B / kR) * kD / NT;    // entries per thread: 2 or 4
+      constexpr int EPT = 2 * NR * D / NT;           // entries per thread: 1 .. 8
       uint32_t gm[EPT], gw[EPT], im[EPT], iw[EPT];
       uint32_t sum_g = 0, sum_i = 0;
 #pragma unroll
       for (int e = 0; e < EPT; ++e) {
         const int it = tid + e * NT;
         gm[e] = gw[e] = im[e] = iw[e] = 0u;
-        if (it < 2 * nr * kD) {
-          const bool is_v = it >= nr * kD;
-          const int rc = is_v ? it - nr * kD : it;
+        if (it < 2 * nr * D) {
+          const bool is_v = it >= nr * D;
+          const int rc = is_v ? it - nr * D : it;
           const uint8_t* q = is_v ? qv : qk;
-          run_stats(q, order, rc / kD, rc % kD, n, gm[e], gw[e]);
-          run_stats(q, ident, rc / kD, rc % kD, n, im[e], iw[e]);
+          run_stats<D>(q, order, rc / D, rc % D, n, gm[e], gw[e]);
+          run_stats<D>(q, ident, rc / D, rc % D, n, im[e], iw[e]);
           sum_g += gw[e];
           sum_i += iw[e];
         }
@@ -402,9 +405,9 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
 #pragma unroll
       for (int e = 0; e < EPT; ++e) {
         const int it = tid + e * NT;
-        if (it < 2 * nr * kD) {
-          const bool is_v = it >= nr * kD;
-          const int rc = is_v ? it - nr * kD : it;
+        if (it < 2 * nr * D) {
+          const bool is_v = it >= nr * D;
+          const int rc = is_v ? it - nr * D : it;
           (is_v ? wv : wk)[rc] = (uint8_t)(keep ? gw[e] : iw[e]);
           (is_v ? mv : mk)[rc] = (uint8_t)(keep ? gm[e] : im[e]);
         }
@@ -412,11 +415,11 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
       __syncthreads();
     } else {
       // (3') identity order: per-run minima and widths
-      for (int it = tid; it < 2 * nr * kD; it += NT) {
-        const bool is_v = it >= nr * kD;
-        const int rc = is_v ? it - nr * kD : it;
+      for (int it = tid; it < 2 * nr * D; it += NT) {
+        const bool is_v = it >= nr * D;
+        const int rc = is_v ? it - nr * D : it;
         uint32_t m, w;
-        run_stats(is_v ? qv : qk, order, rc / kD, rc % kD, n, m, w);
+        run_stats<D>(is_v ? qv : qk, order, rc / D, rc % D, n, m, w);
         (is_v ? wv : wk)[rc] = (uint8_t)w;
         (is_v ? mv : mk)[rc] = (uint8_t)m;
       }
@@ -425,29 +428,37 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
   }
   if (a.mode == kPass2) {
     // (3) per-run minima and widths in the stored order
-    for (int it = tid; it < 2 * nr * kD; it += NT) {
-      const bool is_v = it >= nr * kD;
-      const int rc = is_v ? it - nr * kD : it;
+    for (int it = tid; it < 2 * nr * D; it += NT) {
+      const bool is_v = it >= nr * D;
+      const int rc = is_v ? it - nr * D : it;
       uint32_t m, w;
-      run_stats(is_v ? qv : qk, order, rc / kD, rc % kD, n, m, w);
+      run_stats<D>(is_v ? qv : qk, order, rc / D, rc % D, n, m, w);
       (is_v ? wv : wk)[rc] = (uint8_t)w;
       (is_v ? mv : mk)[rc] = (uint8_t)m;
     }
     __syncthreads();
   }
 
-  // payload word offsets of every (run, channel), run-major: up to 512 per
-  // tensor, two per thread.
+  // payload word offsets of every (run, channel), run-major: up to NR * D
+  // per tensor, PT consecutive entries per thread.
+  constexpr int PT = (NR * D + NT - 1) / NT;         // 1 .. 4
   uint32_t totk, totv;
-  const int nrc = nr * kD;
-  uint32_t k_a = 2 * tid < nrc ? wk[2 * tid] : 0u, k_b = 2 * tid + 1 < nrc ? wk[2 * tid + 1] : 0u;
-  uint32_t v_a = 2 * tid < nrc ? wv[2 * tid] : 0u, v_b = 2 * tid + 1 < nrc ? wv[2 * tid + 1] : 0u;
-  const uint32_t k_ex = block_excl_scan(k_a + k_b, scan_sh, &totk);
-  const uint32_t v_ex = block_excl_scan(v_a + v_b, scan_sh, &totv);
+  const int nrc = nr * D;
+  uint32_t k_in[PT], v_in[PT], k_sum = 0, v_sum = 0;  // exclusive sums inside the thread
+#pragma unroll
+  for (int e = 0; e < PT; ++e) {
+    const int rc = PT * tid + e;
+    k_in[e] = k_sum;
+    v_in[e] = v_sum;
+    k_sum += rc < nrc ? wk[rc] : 0u;
+    v_sum += rc < nrc ? wv[rc] : 0u;
+  }
+  const uint32_t k_ex = block_excl_scan(k_sum, scan_sh, &totk);
+  const uint32_t v_ex = block_excl_scan(v_sum, scan_sh, &totv);
 
   const int hb = hdr_entry_bytes(a.bits);
-  const uint32_t k_pay = (uint32_t)payload_offset(false, B, nr, hb);
-  const uint32_t v_pay = (uint32_t)payload_offset(true, B, nr, hb);
+  const uint32_t k_pay = (uint32_t)payload_offset(false, B, nr, hb, D);
+  const uint32_t v_pay = (uint32_t)payload_offset(true, B, nr, hb, D);
   const uint32_t k_size = k_pay + (uint32_t)pad16(4 * (int)totk);
   const uint32_t v_size = v_pay + (uint32_t)pad16(4 * (int)totv);
   uint32_t* koff = a.k_off + s * a.off_stride;
@@ -524,9 +535,9 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
   }
 
   // params
-  if (tid < kD) {
+  if (tid < D) {
     reinterpret_cast<uint16_t*>(krec)[tid] = ksc[tid];
-    reinterpret_cast<uint16_t*>(krec)[kD + tid] = kze[tid];
+    reinterpret_cast<uint16_t*>(krec)[D + tid] = kze[tid];
   }
   if (tid < B) {
     const bool ok = tid < n;
@@ -535,7 +546,7 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
   }
   // headers and the zero padding up to the payload
   {
-    const uint32_t kh = (uint32_t)hdr_offset(false, B), vh = (uint32_t)hdr_offset(true, B);
+    const uint32_t kh = (uint32_t)hdr_offset(false, B, D), vh = (uint32_t)hdr_offset(true, B, D);
     // byte i of the header area: entry i / hb, byte i % hb of it
     for (uint32_t i = tid; i < k_pay - kh; i += NT) {
       const uint32_t e = hb == 2 ? i >> 1 : i;
@@ -548,19 +559,20 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
       vrec[vh + i] = (uint8_t)(hb == 2 && (i & 1u) ? h >> 8 : h);
     }
   }
-  // payload: each thread packs its two (run, channel) entries of K and of V
-  for (int e = 0; e < 4; ++e) {
-    const bool is_v = e >= 2;
-    const int rc = 2 * tid + (e & 1);
+  // payload: each thread packs its PT (run, channel) entries of K and of V
+  for (int e = 0; e < 2 * PT; ++e) {
+    const bool is_v = e >= PT;
+    const int ei = is_v ? e - PT : e;
+    const int rc = PT * tid + ei;
     if (rc >= nrc) continue;
     const uint8_t* q = is_v ? qv : qk;
     const uint32_t w = (is_v ? wv : wk)[rc];
     const uint32_t m = (is_v ? mv : mk)[rc];
-    const uint32_t woff = (is_v ? v_ex : k_ex) + ((e & 1) ? (is_v ? v_a : k_a) : 0u);
+    const uint32_t woff = is_v ? v_ex + v_in[ei] : k_ex + k_in[ei];
     if (w == 0) continue;
-    const int r = rc / kD, c = rc % kD;
+    const int r = rc / D, c = rc % D;
     uint32_t v[kR];
-    run_values(q, order, r, c, n, v);
+    run_values<D>(q, order, r, c, n, v);
 #pragma unroll
     for (int i = 0; i < kR; ++i) v[i] = r * kR + i < n ? v[i] - m : 0u;
     uint32_t words[8];
@@ -724,11 +736,11 @@ __global__ __launch_bounds__(256) void k_scan_offsets(uint32_t* k_off, uint32_t*
 
 // Copy `cnt` tokens [S][cnt][D] fp16 into the tail staging at token `at`.
 __global__ void k_stage_tail(const uint16_t* k, const uint16_t* v, int64_t src_stream,
-                             uint16_t* tk, uint16_t* tv, int B, int at, int cnt) {
+                             uint16_t* tk, uint16_t* tv, int B, int D, int at, int cnt) {
   const int s = blockIdx.x;
-  for (int i = threadIdx.x; i < cnt * kD; i += blockDim.x) {
-    tk[(int64_t)s * B * kD + (int64_t)at * kD + i] = k[s * src_stream + i];
-    tv[(int64_t)s * B * kD + (int64_t)at * kD + i] = v[s * src_stream + i];
+  for (int i = threadIdx.x; i < cnt * D; i += blockDim.x) {
+    tk[(int64_t)s * B * D + (int64_t)at * D + i] = k[s * src_stream + i];
+    tv[(int64_t)s * B * D + (int64_t)at * D + i] = v[s * src_stream + i];
   }
 }
 
@@ -740,8 +752,14 @@ namespace packkv {
 
 hipError_t launch_encode(const EncArgs& a, int n_streams, int n_blocks, hipStream_t st) {
   dim3 grid(a.mode == kTail ? 1 : n_blocks, n_streams);
-  if (a.B == 64) hipLaunchKernelGGL(k_encode<64>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(k_encode<128>, grid, dim3(256), 0, st, a);
+  switch ((a.B == 64 ? 0 : 3) + (a.D == 64 ? 0 : a.D == 128 ? 1 : 2)) {
+    case 0: hipLaunchKernelGGL((k_encode<64, 64>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_encode<64, 128>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_encode<64, 256>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_encode<128, 64>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_encode<128, 128>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((k_encode<128, 256>), grid, dim3(256), 0, st, a); break;
+  }
   return hipGetLastError();
 }
 
@@ -771,10 +789,10 @@ hipError_t launch_scan_offsets(uint32_t* k_off, uint32_t* v_off, int64_t off_str
 }
 
 hipError_t launch_stage_tail(const uint16_t* k, const uint16_t* v, int64_t src_stream,
-                             uint16_t* tk, uint16_t* tv, int B, int at, int cnt,
+                             uint16_t* tk, uint16_t* tv, int B, int D, int at, int cnt,
                              int n_streams, hipStream_t st) {
   hipLaunchKernelGGL(k_stage_tail, dim3(n_streams), dim3(256), 0, st, k, v, src_stream, tk, tv,
-                     B, at, cnt);
+                     B, D, at, cnt);
   return hipGetLastError();
 }
 

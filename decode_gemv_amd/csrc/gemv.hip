@@ -160,11 +160,13 @@ __device__ __forceinline__ void run_words(const uint8_t* rec, int pay_off, uint3
 // BITS with a consistent minimum; offsets are then implicit and each run is
 // BITS words at (run index) * BITS.  Otherwise the headers are validated one
 // by one and a wave prefix sum gives the offsets.
-template <int B, int BITS, bool IS_V>
+template <int B, int BITS, bool IS_V, int D>
 struct BlockDecoder {
   static constexpr int NR = B / kR;
-  static constexpr int NRL = NR * kD / 64;          // runs per lane: run l + 64k, r = k/2
-  static constexpr int HDR = hdr_offset(IS_V, B);
+  static constexpr int DL = D / 64;                 // runs of one block run per lane
+  static constexpr int NRL = NR * DL;               // runs per lane: run l + 64k, r = k / DL
+  static constexpr int HDR = hdr_offset(IS_V, B, D);
+  static constexpr int HW = NR * D / 4;             // header dwords of a full block
 
   // Decode the lane's runs of the staged record into container words
   // nib[k][0..3] (run l + 64k).  Returns false if the record is inconsistent
@@ -176,8 +178,8 @@ struct BlockDecoder {
   // the end.  Both corrections are uniform branches taken by few blocks.
   __device__ __forceinline__ static bool decode(const uint8_t* rec, uint32_t size, int nr, int lane,
                                                 uint32_t nib[NRL][4]) {
-    const int pay = payload_offset(IS_V, B, nr);
-    const int nruns = nr * kD;
+    const int pay = payload_offset(IS_V, B, nr, 1, D);
+    const int nruns = nr * D;
     uint32_t h[NRL];
 #pragma unroll
     for (int k = 0; k < NRL; ++k) {
@@ -185,14 +187,15 @@ struct BlockDecoder {
       // and select, instead of a branch around each read
       uint32_t hv = rec[HDR + lane + 64 * k];
       asm volatile("" : "+v"(hv));
-      h[k] = (k >> 1) < nr ? hv : 0u;
+      h[k] = k / DL < nr ? hv : 0u;
     }
     bool all_full = false;
     if (nr == NR) {
       bool ok = true;
 #pragma unroll
-      for (int i = 0; i < NR / 2; ++i)                // header dwords lane + 64i
-        ok &= hdr4_full<BITS>(reinterpret_cast<const uint32_t*>(rec + HDR)[lane + 64 * i]);
+      for (int i = 0; i < (HW + 63) / 64; ++i)        // header dwords lane + 64i
+        if (HW % 64 == 0 || lane + 64 * i < HW)
+          ok &= hdr4_full<BITS>(reinterpret_cast<const uint32_t*>(rec + HDR)[lane + 64 * i]);
       all_full = __ballot(!ok) == 0;
     }
     uint32_t off[NRL];
@@ -265,7 +268,7 @@ struct BlockDecoder {
       for (int k = 0; k < NRL; ++k) {
         const int w = (int)(h[k] >> 4);
         if (w != BITS) {
-          if ((k >> 1) < nr) {
+          if (k / DL < nr) {
             uint32_t wd[4];
             if constexpr (BITS == 4) {
               // the words read are nib - m in every nibble (mod 2^32)
@@ -340,9 +343,9 @@ struct RecordTable {
 //   scores[g][t] = beta_g + sum_c q'_g[c] (m + u)[t][c],   q' = q * scale
 //
 // The record's containers go to an LDS plane [slot group][channel] (row
-// pitch 136 words; the quad order rotates per channel group, so 16 lanes of a
-// 16-byte read cover the 64 banks once).  Lane (g8, cg) then covers 8 slots
-// x 16 channels: each container word becomes 8 floats through 4
+// pitch D + 8 words; the quad order rotates per channel group).  Lane (g8,
+// cg) then covers 8 slots x D/8 channels: each container word becomes 8
+// floats through 4
 // v_cvt_pk_f32_fp8 (a byte n <= 15 read as e4m3 is exactly n * 2^-9; 2^9 is
 // folded into q'), one FMA per element, and an LDS transpose sums the 8
 // channel groups.  Lane l ends with the scores of slots h*64 + l.
@@ -368,12 +371,15 @@ __device__ __forceinline__ void store_partial(float* dst, float v) {
   __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int B, int BITS, int GT>
+template <int B, int BITS, int GT, int D>
 struct KBlock {
-  using Dec = BlockDecoder<B, BITS, false>;
+  using Dec = BlockDecoder<B, BITS, false, D>;
   static constexpr int NRL = Dec::NRL;
+  static constexpr int DL = D / 64;                   // channels per lane: lane + 64j
+  static constexpr int CW = D / 8;                    // channels per channel group
+  static constexpr int NQ = CW / 4;                   // 16-byte quads per channel group
   static constexpr int NH = B / 64;
-  static constexpr int ROWW = kD + 8;
+  static constexpr int ROWW = D + 8;
   static constexpr int PLANE_BYTES = (B / 8) * ROWW * 4;
   static constexpr int RED_BYTES = 64 * 9 * 4;        // channel-group reduction, one query
   // The plane and the reduction live in the record's staging buffer: once a
@@ -382,11 +388,11 @@ struct KBlock {
   static constexpr int HALF_BYTES = 8 * ROWW * 4;
   static_assert(RED_BYTES <= HALF_BYTES, "reduction must fit a half's plane rows");
   static constexpr int SCRATCH_BYTES = PLANE_BYTES;
-  static constexpr int QS_BYTES = GT * kD * 4;
+  static constexpr int QS_BYTES = GT * D * 4;
 
   float* qs;                                          // [GT][D] q' of the block
   int lane, g8, cg;
-  float qau[GT], qbu[GT];                             // queries / unit at channels lane, lane + 64
+  float qu[GT][DL];                                   // queries / unit at channels lane + 64j
 
   __device__ __forceinline__ void init(uint8_t* qs_, int lane_) {
     qs = reinterpret_cast<float*>(qs_);
@@ -399,9 +405,10 @@ struct KBlock {
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       const bool ok = gq0 + g < G;
-      const uint16_t* qp = q + (s * G + gq0 + g) * kD;
-      qau[g] = (ok ? f16_bits_to_float(qp[lane]) : 0.f) * unit_inv;       // exact: a power of two
-      qbu[g] = (ok ? f16_bits_to_float(qp[lane + 64]) : 0.f) * unit_inv;
+      const uint16_t* qp = q + (s * G + gq0 + g) * D;
+#pragma unroll
+      for (int j = 0; j < DL; ++j)                    // exact: unit is a power of two
+        qu[g][j] = (ok ? f16_bits_to_float(qp[lane + 64 * j]) : 0.f) * unit_inv;
     }
   }
 
@@ -416,13 +423,21 @@ struct KBlock {
     float beta[GT];
     {
       const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec);
-      const float sa = f16_bits_to_float(sc[lane]), sb = f16_bits_to_float(sc[lane + 64]);
-      const float za = f16_bits_to_float(sc[kD + lane]), zb = f16_bits_to_float(sc[kD + lane + 64]);
+      float sv[DL], zv[DL];
+#pragma unroll
+      for (int j = 0; j < DL; ++j) {
+        sv[j] = f16_bits_to_float(sc[lane + 64 * j]);
+        zv[j] = f16_bits_to_float(sc[D + lane + 64 * j]);
+      }
 #pragma unroll
       for (int g = 0; g < GT; ++g) {
-        qs[g * kD + lane] = qau[g] * sa;
-        qs[g * kD + lane + 64] = qbu[g] * sb;
-        beta[g] = wave_sum(fmaf(qau[g], za, qbu[g] * zb)) * fp8_unit();
+        float bz = 0.f;
+#pragma unroll
+        for (int j = 0; j < DL; ++j) {
+          qs[g * D + lane + 64 * j] = qu[g][j] * sv[j];
+          bz = fmaf(qu[g][j], zv[j], bz);
+        }
+        beta[g] = wave_sum(bz) * fp8_unit();
       }
     }
     uint32_t nib[NRL][4];
@@ -431,7 +446,7 @@ struct KBlock {
     uint32_t* plane = reinterpret_cast<uint32_t*>(rec);
 #pragma unroll
     for (int k = 0; k < NRL; ++k) {
-      const int r = k >> 1, c = lane + 64 * (k & 1);
+      const int r = k / DL, c = lane + 64 * (k % DL);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) plane[(r * 4 + kk) * ROWW + c] = nib[k][kk];
     }
@@ -445,16 +460,16 @@ struct KBlock {
         for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
       const int row = h * 8 + g8;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        // rotate the quad order per channel group: with the 136-word row
-        // pitch, 16 lanes of a 16-byte read then cover all 64 banks once
-        const int c0 = cg * 16 + ((i4 + cg) & 3) * 4;
+      for (int i4 = 0; i4 < NQ; ++i4) {
+        // the quad order rotates per channel group, so the lanes of one
+        // 16-byte read spread over more banks
+        const int c0 = cg * CW + ((i4 + cg) % NQ) * 4;
         const u32x4 nw = *reinterpret_cast<const u32x4*>(&plane[row * ROWW + c0]);
         const uint32_t words[4] = {nw.x, nw.y, nw.z, nw.w};
         float qq[GT][4];
 #pragma unroll
         for (int g = 0; g < GT; ++g) {
-          const float4 t = *reinterpret_cast<const float4*>(&qs[g * kD + c0]);
+          const float4 t = *reinterpret_cast<const float4*>(&qs[g * D + c0]);
           qq[g][0] = t.x; qq[g][1] = t.y; qq[g][2] = t.z; qq[g][3] = t.w;
         }
 #pragma unroll
@@ -508,7 +523,8 @@ struct KBlock {
 // scales by 2^-E and adds beta.
 template <int B, int BITS, int GT>
 struct KBlockM {
-  using Dec = BlockDecoder<B, BITS, false>;
+  static constexpr int kD = 128;                      // the matrix-core tiles are laid out for D = 128
+  using Dec = BlockDecoder<B, BITS, false, kD>;
   static constexpr int NRL = Dec::NRL;
   static constexpr int NH = B / 64;
   static constexpr int NT = B / 16;                   // token tiles of the MFMA
@@ -687,18 +703,19 @@ struct KBlockM {
 // LDS.  One v_dot8_u32_u4 then multiplies a container word by a digit word:
 // 5 instructions per 8 elements, with exact integer sums that are scaled by
 // 2^-E once per block and channel.  Per element the weight error is at most
-// 2^-21 of the block's largest weight.  Lane l accumulates channels l and
-// l + 64.
+// 2^-21 of the block's largest weight.  Lane l accumulates channels l + 64j.
 // STAGED: the weights' digit words are assembled from weights staged in
 // LDS (one word per lane and pass) rather than by an OR across each group of
 // 8 lanes per digit.  Measured: the V GEMV 2-9 % faster staged; fused
 // attention unchanged with one query and 5 % slower with four, where the
 // extra LDS round trip sits on the V wave's path between two barriers.
-template <int B, int BITS, int GT, bool STAGED = true>
+template <int B, int BITS, int GT, int D, bool STAGED = true>
 struct VBlock {
-  using Dec = BlockDecoder<B, BITS, true>;
+  using Dec = BlockDecoder<B, BITS, true, D>;
   static constexpr int NR = Dec::NR;
-  static constexpr int NRL = Dec::NRL;                // run l + 64k: r = k/2, channel l + 64(k&1)
+  static constexpr int NRL = Dec::NRL;                // run l + 64k: r = k / DL, channel l + 64 (k % DL)
+  static constexpr int DL = D / 64;
+  static constexpr int NA = DL;                       // accumulators per query: channels lane + 64j
   static constexpr int NH = B / 64;                   // slots per lane
   static constexpr int NG = B / 8;                    // 8-slot groups per block
   static constexpr int ND = 5;                        // 4-bit digits of p'
@@ -716,23 +733,23 @@ struct VBlock {
     nib_shift = 4 * (lane & 7);
   }
 
-  // acc[g][0], acc[g][1]: query g at channels lane, lane + 64
-  __device__ __forceinline__ void rescale(float (&acc)[GT][2], const float (&alpha)[GT]) const {
+  // acc[g][j]: query g at channel lane + 64j
+  __device__ __forceinline__ void rescale(float (&acc)[GT][NA], const float (&alpha)[GT]) const {
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
-      acc[g][0] *= alpha[g];
-      acc[g][1] *= alpha[g];
+#pragma unroll
+      for (int j = 0; j < NA; ++j) acc[g][j] *= alpha[g];
     }
   }
   // dst(g): query g's partial sums (nullptr for an absent query)
   template <class Dst>
-  __device__ __forceinline__ void store(const float (&acc)[GT][2], const float (&z)[GT], Dst&& dst) const {
+  __device__ __forceinline__ void store(const float (&acc)[GT][NA], const float (&z)[GT], Dst&& dst) const {
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       float* d = dst(g);
       if (d) {
-        store_partial(d + lane, acc[g][0] + z[g]);
-        store_partial(d + lane + 64, acc[g][1] + z[g]);
+#pragma unroll
+        for (int j = 0; j < NA; ++j) store_partial(d + lane + 64 * j, acc[g][j] + z[g]);
       }
     }
   }
@@ -742,7 +759,7 @@ struct VBlock {
   // whether the record decoded consistently; a block that does not adds
   // nothing.
   __device__ __forceinline__ bool run(const uint8_t* rec, uint32_t size, int nr, bool use,
-                                      const float (&pw)[GT][NH], float (&acc)[GT][2], float (&pz)[GT]) {
+                                      const float (&pw)[GT][NH], float (&acc)[GT][NA], float (&pz)[GT]) {
     int E[GT];
     bool live[GT];
     float pzb[GT];
@@ -816,9 +833,9 @@ struct VBlock {
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       if (!ok || !live[g]) continue;
-      uint32_t sd[2][ND];
+      uint32_t sd[DL][ND];
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch)
+      for (int ch = 0; ch < DL; ++ch)
 #pragma unroll
         for (int d = 0; d < ND; ++d) sd[ch][d] = 0u;
 #pragma unroll
@@ -830,15 +847,15 @@ struct VBlock {
 #pragma unroll
           for (int d = 0; d < ND; ++d) W[d] = dig[(g * ND + d) * NG + 4 * r + kk];
 #pragma unroll
-          for (int ch = 0; ch < 2; ++ch)
+          for (int ch = 0; ch < DL; ++ch)
 #pragma unroll
             for (int d = 0; d < ND; ++d)
-              sd[ch][d] = __builtin_amdgcn_udot8(nib[2 * r + ch][kk], W[d], sd[ch][d], false);
+              sd[ch][d] = __builtin_amdgcn_udot8(nib[DL * r + ch][kk], W[d], sd[ch][d], false);
         }
       }
       const float unit = ldexpf(1.0f, -E[g]);
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
+      for (int ch = 0; ch < DL; ++ch) {
         // each digit sum is <= NR*32*15*15 < 2^15, so the total stays below 2^32
         const uint32_t x = sd[ch][0] + (sd[ch][1] << 4) + (sd[ch][2] << 8) + (sd[ch][3] << 12) + (sd[ch][4] << 16);
         acc[g][ch] = fmaf((float)x, unit, acc[g][ch]);
@@ -869,14 +886,16 @@ struct VBlock {
 // scaled by 2^-E.
 template <int B, int BITS, int GT>
 struct VBlockM {
-  using Dec = BlockDecoder<B, BITS, true>;
+  static constexpr int kD = 128;                      // the matrix-core tiles are laid out for D = 128
+  using Dec = BlockDecoder<B, BITS, true, kD>;
   static constexpr int NRL = Dec::NRL;
+  static constexpr int NA = 2;                        // accumulators: channels 16j + l % 16 as [j / 2][j % 2]
   static constexpr int NH = B / 64;
   static constexpr int KS = B / 64;                   // 64-token steps of the MFMA
   static constexpr int VP = B / 8 + 2;                // plane pitch per channel (words)
   static constexpr int LDS_WORDS = 16 * B / 4;        // digit rows [16][B] bytes
   static_assert(GT == 4, "operand rows are (query, digit) for four queries");
-  static_assert(kD * VP * 4 <= staging_bytes(max_record_bytes(true, B, 4)), "the plane reuses the staging");
+  static_assert(kD * VP * 4 <= staging_bytes(max_record_bytes(true, B, 4, kD)), "the plane reuses the staging");
 
   uint8_t* dig;
   int lane;
@@ -894,13 +913,13 @@ struct VBlockM {
     const int rs = t & 15, n = rs & 7;
     return 64 * (t >> 6) + 16 * ((t >> 4) & 3) + 8 * (rs >> 3) + 4 * (n & 1) + (n >> 1);
   }
-  __device__ __forceinline__ void rescale(float (&acc)[GT][2], const float (&alpha)[GT]) const {
+  __device__ __forceinline__ void rescale(float (&acc)[GT][NA], const float (&alpha)[GT]) const {
     const float f = lane_pick(alpha, lane >> 4);
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j >> 1][j & 1] *= f;
   }
   template <class Dst>
-  __device__ __forceinline__ void store(const float (&acc)[GT][2], const float (&z)[GT], Dst&& dst) const {
+  __device__ __forceinline__ void store(const float (&acc)[GT][NA], const float (&z)[GT], Dst&& dst) const {
     const int g = lane >> 4;
     const float zg = lane_pick(z, g);
     float* d = dst(g);
@@ -912,7 +931,7 @@ struct VBlockM {
 
   // As VBlock::run; rec is overwritten by the plane.
   __device__ __forceinline__ bool run(uint8_t* rec, uint32_t size, int nr, bool use,
-                                      const float (&pw)[GT][NH], float (&acc)[GT][2], float (&pz)[GT]) {
+                                      const float (&pw)[GT][NH], float (&acc)[GT][NA], float (&pz)[GT]) {
     int E[GT];
     float pzb[GT];
     {
@@ -998,11 +1017,11 @@ struct VBlockM {
 // 4i + j), q = m + u.  Returns false if the record is inconsistent (a width
 // above bits, a minimum that leaves no room for its width, or widths that do
 // not add up to the record size); the containers are then zero.
-template <int B, bool IS_V>
+template <int B, bool IS_V, int D>
 struct DecW {
   static constexpr int NR = B / kR;
-  static constexpr int NRL = NR * kD / 64;
-  static constexpr int HDR = hdr_offset(IS_V, B);
+  static constexpr int NRL = NR * D / 64;
+  static constexpr int HDR = hdr_offset(IS_V, B, D);
 
   // the R fields of width W of a run's W words, as byte containers
   template <int W>
@@ -1012,8 +1031,8 @@ struct DecW {
 
   __device__ __forceinline__ static bool decode(const uint8_t* rec, uint32_t size, int nr, int lane, int bits,
                                                 uint32_t (&cont)[NRL][8]) {
-    const int pay = payload_offset(IS_V, B, nr, 2);
-    const int nruns = nr * kD;
+    const int pay = payload_offset(IS_V, B, nr, 2, D);
+    const int nruns = nr * D;
     const int L = (1 << bits) - 1;
     const uint16_t* hd = reinterpret_cast<const uint16_t*>(rec + HDR);
     int w[NRL];
@@ -1065,22 +1084,25 @@ struct DecW {
 // takes slots 8 g8 .. 8 g8 + 7 of 16 channels, converts the bytes exactly
 // and multiply-adds q' = q * scale, and the 8 channel groups are reduced
 // through LDS as in KBlock.
-template <int B, int GT>
+template <int B, int GT, int D>
 struct KBlockW {
-  using Dec = DecW<B, false>;
+  using Dec = DecW<B, false, D>;
   static constexpr int NRL = Dec::NRL;
+  static constexpr int DL = D / 64;                   // channels per lane: lane + 64j
+  static constexpr int CW = D / 8;                    // channels per channel group
+  static constexpr int NQ = CW / 4;                   // 16-byte quads per channel group
   static constexpr int NH = B / 64;
-  static constexpr int ROWW = kD + 8;
+  static constexpr int ROWW = D + 8;
   static constexpr int PLANE_BYTES = (B / 4) * ROWW * 4;
   static constexpr int RED_BYTES = 64 * 9 * 4;
   static constexpr int HALF_BYTES = 16 * ROWW * 4;    // the quad rows of 64 slots
   static_assert(RED_BYTES <= HALF_BYTES, "reduction must fit a half's plane rows");
   static constexpr int SCRATCH_BYTES = PLANE_BYTES;
-  static constexpr int QS_BYTES = GT * kD * 4;
+  static constexpr int QS_BYTES = GT * D * 4;
 
   float* qs;
   int lane, g8, cg, bits = 8;
-  float qa[GT], qb[GT];                               // queries at channels lane, lane + 64
+  float qv[GT][DL];                                   // queries at channels lane + 64j
 
   __device__ __forceinline__ void init(uint8_t* qs_, int lane_) {
     qs = reinterpret_cast<float*>(qs_);
@@ -1092,9 +1114,9 @@ struct KBlockW {
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       const bool ok = gq0 + g < G;
-      const uint16_t* qp = q + (s * G + gq0 + g) * kD;
-      qa[g] = ok ? f16_bits_to_float(qp[lane]) : 0.f;
-      qb[g] = ok ? f16_bits_to_float(qp[lane + 64]) : 0.f;
+      const uint16_t* qp = q + (s * G + gq0 + g) * D;
+#pragma unroll
+      for (int j = 0; j < DL; ++j) qv[g][j] = ok ? f16_bits_to_float(qp[lane + 64 * j]) : 0.f;
     }
   }
 
@@ -1103,13 +1125,21 @@ struct KBlockW {
     float beta[GT];
     {
       const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec);
-      const float sa = f16_bits_to_float(sc[lane]), sb = f16_bits_to_float(sc[lane + 64]);
-      const float za = f16_bits_to_float(sc[kD + lane]), zb = f16_bits_to_float(sc[kD + lane + 64]);
+      float sv[DL], zv[DL];
+#pragma unroll
+      for (int j = 0; j < DL; ++j) {
+        sv[j] = f16_bits_to_float(sc[lane + 64 * j]);
+        zv[j] = f16_bits_to_float(sc[D + lane + 64 * j]);
+      }
 #pragma unroll
       for (int g = 0; g < GT; ++g) {
-        qs[g * kD + lane] = qa[g] * sa;
-        qs[g * kD + lane + 64] = qb[g] * sb;
-        beta[g] = wave_sum(fmaf(qa[g], za, qb[g] * zb));
+        float bz = 0.f;
+#pragma unroll
+        for (int j = 0; j < DL; ++j) {
+          qs[g * D + lane + 64 * j] = qv[g][j] * sv[j];
+          bz = fmaf(qv[g][j], zv[j], bz);
+        }
+        beta[g] = wave_sum(bz);
       }
     }
     uint32_t cont[NRL][8];
@@ -1118,7 +1148,7 @@ struct KBlockW {
     uint32_t* plane = reinterpret_cast<uint32_t*>(rec);
 #pragma unroll
     for (int k = 0; k < NRL; ++k) {
-      const int r = k >> 1, c = lane + 64 * (k & 1);
+      const int r = k / DL, c = lane + 64 * (k % DL);
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) plane[(r * 8 + kk) * ROWW + c] = cont[k][kk];
     }
@@ -1132,14 +1162,14 @@ struct KBlockW {
         for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
       const int row = h * 16 + 2 * g8;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int c0 = cg * 16 + ((i4 + cg) & 3) * 4;
+      for (int i4 = 0; i4 < NQ; ++i4) {
+        const int c0 = cg * CW + ((i4 + cg) % NQ) * 4;
         const u32x4 lo = *reinterpret_cast<const u32x4*>(&plane[row * ROWW + c0]);
         const u32x4 hi = *reinterpret_cast<const u32x4*>(&plane[(row + 1) * ROWW + c0]);
         float qq[GT][4];
 #pragma unroll
         for (int g = 0; g < GT; ++g) {
-          const float4 t = *reinterpret_cast<const float4*>(&qs[g * kD + c0]);
+          const float4 t = *reinterpret_cast<const float4*>(&qs[g * D + c0]);
           qq[g][0] = t.x; qq[g][1] = t.y; qq[g][2] = t.z; qq[g][3] = t.w;
         }
 #pragma unroll
@@ -1178,11 +1208,13 @@ struct KBlockW {
 // three byte digits; v_dot4_u32_u8 takes 4 slots of one channel per
 // instruction.  Each digit sum is at most B * 255 * 255 < 2^24, so the three
 // are exact in fp32 and are combined there.
-template <int B, int GT>
+template <int B, int GT, int D>
 struct VBlockW {
-  using Dec = DecW<B, true>;
+  using Dec = DecW<B, true, D>;
   static constexpr int NR = B / kR;
   static constexpr int NRL = Dec::NRL;
+  static constexpr int DL = D / 64;
+  static constexpr int NA = DL;                       // accumulators per query: channels lane + 64j
   static constexpr int NH = B / 64;
   static constexpr int NQ = B / 4;                    // 4-slot groups per block
   static constexpr int ND = 3;                        // byte digits of p'
@@ -1198,27 +1230,27 @@ struct VBlockW {
     pst = lds + DIG_WORDS;
     lane = lane_;
   }
-  __device__ __forceinline__ void rescale(float (&acc)[GT][2], const float (&alpha)[GT]) const {
+  __device__ __forceinline__ void rescale(float (&acc)[GT][NA], const float (&alpha)[GT]) const {
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
-      acc[g][0] *= alpha[g];
-      acc[g][1] *= alpha[g];
+#pragma unroll
+      for (int j = 0; j < NA; ++j) acc[g][j] *= alpha[g];
     }
   }
   template <class Dst>
-  __device__ __forceinline__ void store(const float (&acc)[GT][2], const float (&z)[GT], Dst&& dst) const {
+  __device__ __forceinline__ void store(const float (&acc)[GT][NA], const float (&z)[GT], Dst&& dst) const {
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       float* d = dst(g);
       if (d) {
-        store_partial(d + lane, acc[g][0] + z[g]);
-        store_partial(d + lane + 64, acc[g][1] + z[g]);
+#pragma unroll
+        for (int j = 0; j < NA; ++j) store_partial(d + lane + 64 * j, acc[g][j] + z[g]);
       }
     }
   }
 
   __device__ __forceinline__ bool run(const uint8_t* rec, uint32_t size, int nr, bool use,
-                                      const float (&pw)[GT][NH], float (&acc)[GT][2], float (&pz)[GT]) {
+                                      const float (&pw)[GT][NH], float (&acc)[GT][NA], float (&pz)[GT]) {
     int E[GT];
     bool live[GT];
     float pzb[GT];
@@ -1270,9 +1302,9 @@ struct VBlockW {
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       if (!ok || !live[g]) continue;
-      uint32_t sd[2][ND];
+      uint32_t sd[DL][ND];
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch)
+      for (int ch = 0; ch < DL; ++ch)
 #pragma unroll
         for (int d = 0; d < ND; ++d) sd[ch][d] = 0u;
 #pragma unroll
@@ -1284,15 +1316,15 @@ struct VBlockW {
 #pragma unroll
           for (int d = 0; d < ND; ++d) W[d] = dig[(g * ND + d) * NQ + 8 * r + kk];
 #pragma unroll
-          for (int ch = 0; ch < 2; ++ch)
+          for (int ch = 0; ch < DL; ++ch)
 #pragma unroll
             for (int d = 0; d < ND; ++d)
-              sd[ch][d] = __builtin_amdgcn_udot4(cont[2 * r + ch][kk], W[d], sd[ch][d], false);
+              sd[ch][d] = __builtin_amdgcn_udot4(cont[DL * r + ch][kk], W[d], sd[ch][d], false);
         }
       }
       const float unit = ldexpf(1.0f, -E[g]);
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
+      for (int ch = 0; ch < DL; ++ch) {
         const float x = fmaf(65536.f, (float)sd[ch][2], fmaf(256.f, (float)sd[ch][1], (float)sd[ch][0]));
         acc[g][ch] = fmaf(x, unit, acc[g][ch]);
       }
@@ -1311,15 +1343,19 @@ struct VBlockW {
 // us; with one query the matrix version is slower (K GEMV +9-10 %, one wave
 // less occupancy; fused attention +1-3 %), as its transposes and LDS round
 // trips are not repaid by 32 FMAs per packed word.
-template <int B, int BITS, int GT>
-using KSel = std::conditional_t<(BITS > 4), KBlockW<B, GT>,
-                                std::conditional_t<(GT > 1), KBlockM<B, BITS, GT>, KBlock<B, BITS, GT>>>;
+// The matrix-core tiles are laid out for D = 128; other head_dims take the
+// vector code for every tile.
+template <int B, int BITS, int GT, int D>
+using KSel = std::conditional_t<(BITS > 4), KBlockW<B, GT, D>,
+                                std::conditional_t<(GT > 1 && D == 128), KBlockM<B, BITS, GT>, KBlock<B, BITS, GT, D>>>;
 
 // The V block code the kernels use: wide widths take VBlockW; at b <= 4 the
-// matrix cores (VBlockM) for a tile of four queries, v_dot8 (VBlock) for one.
-template <int B, int BITS, int GT, bool STAGED = true>
-using VSel = std::conditional_t<(BITS > 4), VBlockW<B, GT>,
-                                std::conditional_t<(GT > 1), VBlockM<B, BITS, GT>, VBlock<B, BITS, GT, STAGED>>>;
+// matrix cores (VBlockM) for a tile of four queries (D = 128), v_dot8
+// (VBlock) otherwise.
+template <int B, int BITS, int GT, int D, bool STAGED = true>
+using VSel = std::conditional_t<(BITS > 4), VBlockW<B, GT, D>,
+                                std::conditional_t<(GT > 1 && D == 128), VBlockM<B, BITS, GT>,
+                                                   VBlock<B, BITS, GT, D, STAGED>>>;
 
 // The largest record the kernels of a width class stage: b <= 4 or b = 5..8.
 __host__ __device__ constexpr int class_bits(int bits) { return bits > 4 ? 8 : 4; }
@@ -1362,10 +1398,10 @@ struct RecordStream {
   }
 };
 
-template <int B, int BITS, int GT>
+template <int B, int BITS, int GT, int D>
 __global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
-  using KB = KSel<B, BITS, GT>;
-  constexpr int REC = max_record_bytes(false, B, class_bits(BITS));
+  using KB = KSel<B, BITS, GT, D>;
+  constexpr int REC = max_record_bytes(false, B, class_bits(BITS), D);
   constexpr int NCH = (REC + 1023) / 1024;
   constexpr int BUF = staging_bytes(REC) > KB::SCRATCH_BYTES ? staging_bytes(REC) : KB::SCRATCH_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t rec[BUF];
@@ -1446,15 +1482,17 @@ __device__ __forceinline__ void reset_ticket(uint32_t* ticket, int lane) {
 // Occupancy asked of the register allocator: 64-token blocks with one query
 // fit 96 VGPRs (5 waves per SIMD), 128-token blocks 168 (3 waves); either
 // costs at most a few values kept in scratch outside the block loop
-template <int B, int GT>
-constexpr int pv_waves_per_eu() { return B == 64 && GT == 1 ? 5 : B == 128 ? 3 : 1; }
+// (D = 128; other head_dims leave the allocator free)
+template <int B, int GT, int D>
+constexpr int pv_waves_per_eu() { return D != 128 ? 1 : B == 64 && GT == 1 ? 5 : B == 128 ? 3 : 1; }
 
-template <int B, int BITS, int GT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(pv_waves_per_eu<B, GT>())))
+template <int B, int BITS, int GT, int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(pv_waves_per_eu<B, GT, D>())))
 void k_pv_gemv(GemvArgs a) {
-  using VB = VSel<B, BITS, GT>;
+  using VB = VSel<B, BITS, GT, D>;
   constexpr int NH = VB::NH;
-  constexpr int REC = max_record_bytes(true, B, class_bits(BITS));
+  constexpr int NA = VB::NA;
+  constexpr int REC = max_record_bytes(true, B, class_bits(BITS), D);
   constexpr int NCH = (REC + 1023) / 1024;
   __shared__ __attribute__((aligned(16))) uint8_t rec[staging_bytes(REC)];
   __shared__ __attribute__((aligned(16))) uint32_t dig[VB::LDS_WORDS];
@@ -1478,10 +1516,14 @@ void k_pv_gemv(GemvArgs a) {
   bool corrupt = false, invalid = false;
 
   for (int gq0 = 0; gq0 < a.G; gq0 += GT) {
-    float acc[GT][2];
+    float acc[GT][NA];
     float pz[GT];
 #pragma unroll
-    for (int g = 0; g < GT; ++g) { acc[g][0] = acc[g][1] = 0.f; pz[g] = 0.f; }
+    for (int g = 0; g < GT; ++g) {
+#pragma unroll
+      for (int j = 0; j < NA; ++j) acc[g][j] = 0.f;
+      pz[g] = 0.f;
+    }
     // weights of the lane's slots (slot h*64 + lane) for block jj; zero past
     // the valid slots, for absent queries and missing blocks
     auto load_p = [&](int jj, float (&pv)[GT][NH]) __attribute__((always_inline)) {
@@ -1540,23 +1582,25 @@ void k_pv_gemv(GemvArgs a) {
 #pragma unroll
     for (int g = 0; g < GT; ++g) z[g] = wave_sum(pz[g]);
     vb.store(acc, z, [&](int g) -> float* {
-      return gq0 + g < a.G ? a.ws + (((int64_t)s * a.G + gq0 + g) * a.splits + split) * kD : nullptr;
+      return gq0 + g < a.G ? a.ws + (((int64_t)s * a.G + gq0 + g) * a.splits + split) * D : nullptr;
     });
   }
   if (corrupt && lane == 0) latch(a.status, PACKKV_ECORRUPT);
   if (invalid && lane == 0) latch(a.status, PACKKV_EINVAL);
   if (!last_to_arrive(&a.tickets[s], a.splits, lane)) return;
+  constexpr int DL = D / 64;
   for (int g = 0; g < a.G; ++g) {
-    const float* src = a.ws + ((int64_t)s * a.G + g) * a.splits * kD;
-    float s0 = 0.f, s1 = 0.f;
+    const float* src = a.ws + ((int64_t)s * a.G + g) * a.splits * D;
+    float sum[DL];
+#pragma unroll
+    for (int j = 0; j < DL; ++j) sum[j] = 0.f;
 #pragma unroll 8
-    for (int i = 0; i < a.splits; ++i) {
-      s0 += load_partial(src + (int64_t)i * kD + lane);
-      s1 += load_partial(src + (int64_t)i * kD + lane + 64);
-    }
-    float* dst = a.out + ((int64_t)s * a.G + g) * kD;
-    dst[lane] = s0;
-    dst[lane + 64] = s1;
+    for (int i = 0; i < a.splits; ++i)
+#pragma unroll
+      for (int j = 0; j < DL; ++j) sum[j] += load_partial(src + (int64_t)i * D + lane + 64 * j);
+    float* dst = a.out + ((int64_t)s * a.G + g) * D;
+#pragma unroll
+    for (int j = 0; j < DL; ++j) dst[lane + 64 * j] = sum[j];
   }
   reset_ticket(&a.tickets[s], lane);
 }
@@ -1594,18 +1638,20 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // for 128-token blocks and 5 (96 VGPRs) for 2-bit 64-token blocks with one
 // query, where the few values it has to spill are read once per query group
 // (measured: 2-bit 266 -> 249 us; at 4 bits 5 waves gain nothing).  The
-// other shapes keep every value in registers.
-template <int B, int BITS, int GT>
-constexpr int attn_waves_per_eu() { return B == 128 ? 3 : B == 64 && BITS == 2 && GT == 1 ? 5 : 1; }
+// other shapes keep every value in registers.  (Tuned at D = 128; other
+// head_dims leave the allocator free.)
+template <int B, int BITS, int GT, int D>
+constexpr int attn_waves_per_eu() { return D != 128 ? 1 : B == 128 ? 3 : B == 64 && BITS == 2 && GT == 1 ? 5 : 1; }
 
-template <int B, int BITS, int GT, bool PAGED>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<B, BITS, GT>())))
+template <int B, int BITS, int GT, int D, bool PAGED>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<B, BITS, GT, D>())))
 void k_attn_decode(AttnArgs a) {
-  using KB = KSel<B, BITS, GT>;
-  using VB = VSel<B, BITS, GT, false>;
+  using KB = KSel<B, BITS, GT, D>;
+  using VB = VSel<B, BITS, GT, D, false>;
   constexpr int NH = B / 64;
-  constexpr int REC_K = max_record_bytes(false, B, class_bits(BITS));
-  constexpr int REC_V = max_record_bytes(true, B, class_bits(BITS));
+  constexpr int PF = attn_partial_floats(D);      // floats per split partial
+  constexpr int REC_K = max_record_bytes(false, B, class_bits(BITS), D);
+  constexpr int REC_V = max_record_bytes(true, B, class_bits(BITS), D);
   constexpr int NCH_K = (REC_K + 1023) / 1024;
   constexpr int NCH_V = (REC_V + 1023) / 1024;
   constexpr int BUF_K = staging_bytes(REC_K) > KB::SCRATCH_BYTES ? staging_bytes(REC_K) : KB::SCRATCH_BYTES;
@@ -1703,9 +1749,15 @@ void k_attn_decode(AttnArgs a) {
       VB vb;
       vb.init(dig, lane);
       if constexpr (BITS > 4) vb.bits = a.bits;
-      float m[GT], l[GT], acc[GT][2], pz[GT];
+      float m[GT], l[GT], acc[GT][VB::NA], pz[GT];
 #pragma unroll
-      for (int g = 0; g < GT; ++g) { m[g] = NEG_INF; l[g] = 0.f; acc[g][0] = acc[g][1] = 0.f; pz[g] = 0.f; }
+      for (int g = 0; g < GT; ++g) {
+        m[g] = NEG_INF;
+        l[g] = 0.f;
+        pz[g] = 0.f;
+#pragma unroll
+        for (int j = 0; j < VB::NA; ++j) acc[g][j] = 0.f;
+      }
       u32x4 pre[NCH_V];
       vs.request(0, pre);
       for (int jj = 0; jj < nj; ++jj) {
@@ -1752,13 +1804,13 @@ void k_attn_decode(AttnArgs a) {
         z[g] = wave_sum(pz[g]);
         const float lsum = wave_sum(l[g]);
         if (gq0 + g < a.G && lane == 0) {
-          float* dst = ws + (((int64_t)s * a.G + gq0 + g) * a.splits + split) * kAttnPartial;
-          store_partial(dst + kD, m[g]);
-          store_partial(dst + kD + 1, lsum);
+          float* dst = ws + (((int64_t)s * a.G + gq0 + g) * a.splits + split) * PF;
+          store_partial(dst + D, m[g]);
+          store_partial(dst + D + 1, lsum);
         }
       }
       vb.store(acc, z, [&](int g) -> float* {
-        return gq0 + g < a.G ? ws + (((int64_t)s * a.G + gq0 + g) * a.splits + split) * kAttnPartial : nullptr;
+        return gq0 + g < a.G ? ws + (((int64_t)s * a.G + gq0 + g) * a.splits + split) * PF : nullptr;
       });
       __syncthreads();                              // the ring is reused
     }
@@ -1767,25 +1819,40 @@ void k_attn_decode(AttnArgs a) {
   if (wave != 1 || !last_to_arrive(&tickets[s], a.splits, lane)) return;
   // Merge: the largest split max M first (lanes across splits), then each
   // split's sums scaled by 2^(m_i - M).  A half-wave takes every other split
-  // (in split order) and a lane four of the outputs; the loads of four splits
-  // per half-wave are issued together.
-  const int half = lane >> 5, d4 = (lane & 31) * 4;
-  constexpr uint32_t PB = kAttnPartial * 4;         // bytes per partial
+  // (in split order) and a lane NPL = D/32 of the outputs; the loads of four
+  // splits per half-wave are issued together.
+  constexpr int NPL = D / 32;
+  const int half = lane >> 5, d0 = (lane & 31) * NPL;
+  constexpr uint32_t PB = PF * 4;                   // bytes per partial
   for (int g = 0; g < a.G; ++g) {
-    const float* src = ws + ((int64_t)s * a.G + g) * a.splits * kAttnPartial;
+    const float* src = ws + ((int64_t)s * a.G + g) * a.splits * PF;
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(src, (uint32_t)a.splits * PB);
     float M = NEG_INF;
-    for (int i = lane; i < a.splits; i += 64) M = fmaxf(M, load_partial(src + (int64_t)i * kAttnPartial + kD));
+    for (int i = lane; i < a.splits; i += 64) M = fmaxf(M, load_partial(src + (int64_t)i * PF + D));
     M = wave_max_f(M);
-    float L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+    float L = 0.f, o[NPL];
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) o[k] = 0.f;
     for (int i0 = 0; i0 < a.splits; i0 += 8) {
-      u32x4 v[4];
+      uint32_t v[4][NPL];
       u32x2 ml[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const uint32_t off = (uint32_t)(i0 + 2 * u + half) * PB;   // past the end reads zeros
-        v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * d4, 0, kCoherent));
-        ml[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * kD, 0, kCoherent));
+        if constexpr (NPL == 2) {
+          const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * d0, 0, kCoherent));
+          v[u][0] = t[0];
+          v[u][1] = t[1];
+        } else {
+#pragma unroll
+          for (int c = 0; c < NPL; c += 4) {
+            const u32x4 t =
+                __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * (d0 + c), 0, kCoherent));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[u][c + k] = t[k];
+          }
+        }
+        ml[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * D, 0, kCoherent));
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -1793,17 +1860,18 @@ void k_attn_decode(AttnArgs a) {
         const float f = in ? fast_exp2(__uint_as_float(ml[u].x) - M) : 0.f;
         L = fmaf(__uint_as_float(ml[u].y), f, L);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) o[k] = fmaf(__uint_as_float(v[u][k]), f, o[k]);
+        for (int k = 0; k < NPL; ++k) o[k] = fmaf(__uint_as_float(v[u][k]), f, o[k]);
       }
     }
     L += __shfl_xor(L, 32, kWave);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] += __shfl_xor(o[k], 32, kWave);
+    for (int k = 0; k < NPL; ++k) o[k] += __shfl_xor(o[k], 32, kWave);
     if (half == 0) {
       // an empty stream (paged) has no weights: its output is zero
-      float4 res = {L > 0.f ? o[0] / L : 0.f, L > 0.f ? o[1] / L : 0.f, L > 0.f ? o[2] / L : 0.f,
-                    L > 0.f ? o[3] / L : 0.f};
-      *reinterpret_cast<float4*>(out + ((int64_t)s * a.G + g) * kD + d4) = res;
+      float* dst = out + ((int64_t)s * a.G + g) * D + d0;
+#pragma unroll
+      for (int c = 0; c < NPL; c += 2)
+        *reinterpret_cast<float2*>(dst + c) = float2{L > 0.f ? o[c] / L : 0.f, L > 0.f ? o[c + 1] / L : 0.f};
     }
   }
   reset_ticket(&tickets[s], lane);
@@ -1812,15 +1880,15 @@ void k_attn_decode(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // Decompress (test path): mode 0 -> u8 q in slot order, mode 1 -> fp32 x_hat
 // in token order.
-template <int B, bool IS_V, bool WIDE>
+template <int B, bool IS_V, bool WIDE, int D>
 __global__ __launch_bounds__(64) void k_decompress(GemvArgs a, const uint8_t* perm, int64_t perm_stride,
                                                    int mode, void* out) {
   constexpr int NR = B / kR;
-  constexpr int NRL = NR * kD / 64;
+  constexpr int NRL = NR * D / 64;
   constexpr int HB = WIDE ? 2 : 1;
-  constexpr int REC = max_record_bytes(IS_V, B, WIDE ? 8 : 4);
+  constexpr int REC = max_record_bytes(IS_V, B, WIDE ? 8 : 4, D);
   constexpr int NCH = (REC + 1023) / 1024;
-  constexpr int HDR = hdr_offset(IS_V, B);
+  constexpr int HDR = hdr_offset(IS_V, B, D);
   __shared__ __attribute__((aligned(16))) uint8_t rec[staging_bytes(REC)];
   const int lane = threadIdx.x;
   const int s = blockIdx.y, j = blockIdx.x;
@@ -1833,15 +1901,20 @@ __global__ __launch_bounds__(64) void k_decompress(GemvArgs a, const uint8_t* pe
     if (lane == 0) latch(a.status, PACKKV_ECORRUPT);
     return;
   }
-  u32x4 pre[NCH];
-  load_record<NCH>(arena + o, size, lane, pre);
-  store_record<NCH>(rec, pre, lane);
+  {
+    // chunk by chunk (the largest records would not fit one register batch)
+    const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(arena + o, size);
+    u32x4* dst = reinterpret_cast<u32x4*>(rec);
+    for (int k = 0; k < NCH; ++k)
+      dst[lane + 64 * k] =
+          __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, 16 * (lane + 64 * k), 0, kNonTemporal));
+  }
   __syncthreads();
-  const int pay = payload_offset(IS_V, B, nr, HB);
+  const int pay = payload_offset(IS_V, B, nr, HB, D);
   int w[NRL];
   uint32_t m[NRL], ro[NRL];
   bool full;
-  if (!scan_runs<NRL, HB>(rec, HDR, pay, size, nr * kD, a.bits, lane, w, m, ro, full)) {
+  if (!scan_runs<NRL, HB>(rec, HDR, pay, size, nr * D, a.bits, lane, w, m, ro, full)) {
     if (lane == 0) latch(a.status, PACKKV_ECORRUPT);
     return;
   }
@@ -1850,7 +1923,7 @@ __global__ __launch_bounds__(64) void k_decompress(GemvArgs a, const uint8_t* pe
 #pragma unroll
   for (int k = 0; k < NRL; ++k) {
     const int ri = lane + 64 * k;
-    const int r = ri / kD, c = ri % kD;
+    const int r = ri / D, c = ri % D;
     if (r >= nr) continue;
     // the run's containers: nibbles holding q (b <= 4) or bytes holding u
     uint32_t nib[4], byt[8];
@@ -1887,10 +1960,10 @@ __global__ __launch_bounds__(64) void k_decompress(GemvArgs a, const uint8_t* pe
       }
       if (mode == 0) {
         uint8_t* o8 = reinterpret_cast<uint8_t*>(out);
-        o8[(((int64_t)s * a.n_tokens) + (int64_t)j * B + sl) * kD + c] = (uint8_t)qv;
+        o8[(((int64_t)s * a.n_tokens) + (int64_t)j * B + sl) * D + c] = (uint8_t)qv;
       } else {
         const float scale = f16_bits_to_float(IS_V ? sc[sl] : sc[c]);
-        const float zero = f16_bits_to_float(IS_V ? sc[B + sl] : sc[kD + c]);
+        const float zero = f16_bits_to_float(IS_V ? sc[B + sl] : sc[D + c]);
         float* of = reinterpret_cast<float*>(out);
         const int tok = pm[sl];
         if (tok >= n) {
@@ -1898,16 +1971,16 @@ __global__ __launch_bounds__(64) void k_decompress(GemvArgs a, const uint8_t* pe
           continue;
         }
         const int64_t t = (int64_t)j * B + tok;
-        of[((int64_t)s * a.n_tokens + t) * kD + c] = fmaf(scale, (float)qv, zero);
+        of[((int64_t)s * a.n_tokens + t) * D + c] = fmaf(scale, (float)qv, zero);
       }
     }
   }
 }
 
-// Width histogram and byte counts.
-template <int B, bool IS_V, bool WIDE>
+// Width histogram and byte counts: one wave per record; the lanes' counts
+// are summed over the wave first, so a record costs at most a dozen atomics.
+template <int B, bool IS_V, bool WIDE, int D>
 __global__ __launch_bounds__(64) void k_stats(GemvArgs a, unsigned long long* out) {
-  constexpr int NR = B / kR;
   const int lane = threadIdx.x;
   const int s = blockIdx.y, j = blockIdx.x;
   const uint8_t* arena = a.arena + (uint64_t)s * a.arena_stride;
@@ -1915,28 +1988,32 @@ __global__ __launch_bounds__(64) void k_stats(GemvArgs a, unsigned long long* ou
   const uint32_t o = offs[j], size = offs[j + 1] - o;
   const int n = (int)imin64(B, a.n_tokens - (int64_t)j * B);
   const int nr = (n + kR - 1) / kR;
-  if (!record_ok(o, size, a.arena_stride, max_record_bytes(IS_V, B, WIDE ? 8 : 4))) {
+  if (!record_ok(o, size, a.arena_stride, max_record_bytes(IS_V, B, WIDE ? 8 : 4, D))) {
     if (lane == 0) latch(a.status, PACKKV_ECORRUPT);
     return;
   }
-  const uint8_t* hdr = arena + o + hdr_offset(IS_V, B);
-  unsigned long long hist[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
-  unsigned long long words = 0;
-  for (int ri = lane; ri < nr * kD; ri += 64) {
+  const uint8_t* hdr = arena + o + hdr_offset(IS_V, B, D);
+  int hist[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+  int words = 0;
+  for (int ri = lane; ri < nr * D; ri += 64) {
     const int w = WIDE ? reinterpret_cast<const uint16_t*>(hdr)[ri] >> 8 : hdr[ri] >> 4;
-    if (w <= 8) hist[w]++;
-    words += (unsigned long long)w;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) hist[i] += w == i;
+    words += w;
   }
   // widths 0..4 at out[0..4] (K) and out[5..9] (V); 5..8 at out[16..19]
   // (K) and out[20..23] (V)
-  for (int i = 0; i < 9; ++i)
-    if (hist[i]) atomicAdd(&out[i < 5 ? (IS_V ? 5 : 0) + i : (IS_V ? 20 : 16) + i - 5], hist[i]);
-  if (words) atomicAdd(&out[IS_V ? 13 : 12], words);
-  if (lane == 0) {
-    atomicAdd(&out[IS_V ? 11 : 10], (unsigned long long)size);
-    atomicAdd(&out[IS_V ? 15 : 14], (unsigned long long)(nr * kD));
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    const int h = wave_sum_i(hist[i]);
+    if (lane == 0 && h) atomicAdd(&out[i < 5 ? (IS_V ? 5 : 0) + i : (IS_V ? 20 : 16) + i - 5], (unsigned long long)h);
   }
-  (void)NR;
+  const int wsum = wave_sum_i(words);
+  if (lane == 0) {
+    if (wsum) atomicAdd(&out[IS_V ? 13 : 12], (unsigned long long)wsum);
+    atomicAdd(&out[IS_V ? 11 : 10], (unsigned long long)size);
+    atomicAdd(&out[IS_V ? 15 : 14], (unsigned long long)(nr * D));
+  }
 }
 
 // Softmax over the first T entries of each row: p = exp(s*scale - max)/sum.
@@ -2000,98 +2077,70 @@ __global__ __launch_bounds__(1024) void k_softmax(const float* scores, float* p,
 
 // ---------------------------------------------------------------------------
 // Launchers.  Widths 5..8 share one kernel per shape (BITS = 8), which checks
-// the record's widths against the configured b at run time.
+// the record's widths against the configured b at run time.  Shapes are
+// dispatched as (B, width class, D); the paged cache is D = 128 only.
 static inline int class_bits_or_narrow(int bits) { return bits > 4 ? 8 : bits; }
-template <int B, int BITS>
-static void qk_launch(const GemvArgs& a, dim3 grid, hipStream_t st) {
-  if (a.G == 1) hipLaunchKernelGGL((k_qk_gemv<B, BITS, 1>), grid, dim3(64), 0, st, a);
-  else hipLaunchKernelGGL((k_qk_gemv<B, BITS, 4>), grid, dim3(64), 0, st, a);
+
+// f.template operator()<B, BITS, D>() for the cache's shape
+template <class F>
+static void dispatch_shape(int B, int bits, int D, F&& f) {
+  const int cb = class_bits_or_narrow(bits);
+  const int key = (B == 128 ? 100 : 0) + (D == 64 ? 0 : D == 128 ? 10 : 20) + cb;
+  switch (key) {
+#define PACKKV_SHAPE(BB, DD, BI)     case (BB == 128 ? 100 : 0) + (DD == 64 ? 0 : DD == 128 ? 10 : 20) + BI: f.template operator()<BB, BI, DD>(); break;
+#define PACKKV_SHAPES(BB, DD) PACKKV_SHAPE(BB, DD, 2) PACKKV_SHAPE(BB, DD, 3) PACKKV_SHAPE(BB, DD, 4) PACKKV_SHAPE(BB, DD, 8)
+    PACKKV_SHAPES(64, 64) PACKKV_SHAPES(64, 128) PACKKV_SHAPES(64, 256)
+    PACKKV_SHAPES(128, 64) PACKKV_SHAPES(128, 128) PACKKV_SHAPES(128, 256)
+#undef PACKKV_SHAPES
+#undef PACKKV_SHAPE
+    default: break;
+  }
 }
-template <int B, int BITS>
-static void pv_launch(const GemvArgs& a, dim3 grid, hipStream_t st) {
-  if (a.G == 1) hipLaunchKernelGGL((k_pv_gemv<B, BITS, 1>), grid, dim3(64), 0, st, a);
-  else hipLaunchKernelGGL((k_pv_gemv<B, BITS, 4>), grid, dim3(64), 0, st, a);
-}
+
 hipError_t launch_qk(const GemvArgs& a, int B, int n_streams, hipStream_t st) {
   const dim3 grid(n_streams * a.splits);
-  switch (B * 8 + class_bits_or_narrow(a.bits)) {
-    case 64 * 8 + 2: qk_launch<64, 2>(a, grid, st); break;
-    case 64 * 8 + 3: qk_launch<64, 3>(a, grid, st); break;
-    case 64 * 8 + 4: qk_launch<64, 4>(a, grid, st); break;
-    case 128 * 8 + 2: qk_launch<128, 2>(a, grid, st); break;
-    case 128 * 8 + 3: qk_launch<128, 3>(a, grid, st); break;
-    case 128 * 8 + 4: qk_launch<128, 4>(a, grid, st); break;
-    case 64 * 8 + 8: qk_launch<64, 8>(a, grid, st); break;
-    default: qk_launch<128, 8>(a, grid, st); break;
-  }
+  dispatch_shape(B, a.bits, a.D, [&]<int BB, int BI, int DD>() {
+    if (a.G == 1) hipLaunchKernelGGL((k_qk_gemv<BB, BI, 1, DD>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((k_qk_gemv<BB, BI, 4, DD>), grid, dim3(64), 0, st, a);
+  });
   return hipGetLastError();
 }
 
 hipError_t launch_pv(const GemvArgs& a, int B, int n_streams, hipStream_t st) {
   const dim3 grid(n_streams * a.splits);
-  switch (B * 8 + class_bits_or_narrow(a.bits)) {
-    case 64 * 8 + 2: pv_launch<64, 2>(a, grid, st); break;
-    case 64 * 8 + 3: pv_launch<64, 3>(a, grid, st); break;
-    case 64 * 8 + 4: pv_launch<64, 4>(a, grid, st); break;
-    case 128 * 8 + 2: pv_launch<128, 2>(a, grid, st); break;
-    case 128 * 8 + 3: pv_launch<128, 3>(a, grid, st); break;
-    case 128 * 8 + 4: pv_launch<128, 4>(a, grid, st); break;
-    case 64 * 8 + 8: pv_launch<64, 8>(a, grid, st); break;
-    default: pv_launch<128, 8>(a, grid, st); break;
-  }
+  dispatch_shape(B, a.bits, a.D, [&]<int BB, int BI, int DD>() {
+    if (a.G == 1) hipLaunchKernelGGL((k_pv_gemv<BB, BI, 1, DD>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((k_pv_gemv<BB, BI, 4, DD>), grid, dim3(64), 0, st, a);
+  });
   return hipGetLastError();
 }
 
-template <int B, int BITS, bool PAGED>
-static void attn_launch(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  if (a.G == 1) hipLaunchKernelGGL((k_attn_decode<B, BITS, 1, PAGED>), grid, dim3(128), 0, st, a);
-  else hipLaunchKernelGGL((k_attn_decode<B, BITS, 4, PAGED>), grid, dim3(128), 0, st, a);
-}
-template <bool PAGED>
-static void attn_dispatch(const AttnArgs& a, int B, dim3 grid, hipStream_t st) {
-  switch (B * 8 + class_bits_or_narrow(a.bits)) {
-    case 64 * 8 + 2: attn_launch<64, 2, PAGED>(a, grid, st); break;
-    case 64 * 8 + 3: attn_launch<64, 3, PAGED>(a, grid, st); break;
-    case 64 * 8 + 4: attn_launch<64, 4, PAGED>(a, grid, st); break;
-    case 128 * 8 + 2: attn_launch<128, 2, PAGED>(a, grid, st); break;
-    case 128 * 8 + 3: attn_launch<128, 3, PAGED>(a, grid, st); break;
-    case 128 * 8 + 4: attn_launch<128, 4, PAGED>(a, grid, st); break;
-    case 64 * 8 + 8: attn_launch<64, 8, PAGED>(a, grid, st); break;
-    default: attn_launch<128, 8, PAGED>(a, grid, st); break;
-  }
-}
 // Workgroups of the (contiguous-cache) fused attention kernel for this shape
 // that are resident on the current device at once: occupancy per compute
 // unit times the compute units; 0 if the runtime cannot say.  Asked once per
 // shape.
-template <int B, int BITS, int GT>
+template <int B, int BITS, int GT, int D>
 static int resident_wgs_of() {
   int per_cu = 0, dev = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_decode<B, BITS, GT, false>, 128, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_decode<B, BITS, GT, D, false>, 128, 0) !=
           hipSuccess ||
       hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   return per_cu * cus;
 }
-int attention_resident_wgs(int B, int bits, int G) {
-  // [B == 128][bits class][G > 1]: 0 = not asked yet, -1 = unknown.  Host
-  // threads may race to fill an entry; they store the same value.
-  static std::atomic<int> known[2][9][2];
-  const int cb = class_bits_or_narrow(bits), b1 = B == 128, g1 = G > 1;
-  std::atomic<int>& slot = known[b1][cb][g1];
+int attention_resident_wgs(int B, int bits, int G, int D) {
+  // [B == 128][D index][bits class][G > 1]: 0 = not asked yet, -1 = unknown.
+  // Host threads may race to fill an entry; they store the same value.
+  static std::atomic<int> known[2][3][9][2];
+  const int cb = class_bits_or_narrow(bits), b1 = B == 128, g1 = G > 1, di = D == 64 ? 0 : D == 128 ? 1 : 2;
+  std::atomic<int>& slot = known[b1][di][cb][g1];
   int r = slot.load(std::memory_order_relaxed);
   if (r == 0) {
     int v = 0;
-    switch ((B * 8 + cb) * 2 + g1) {
-#define PACKKV_RES(BB, BI)                                   \
-      case (BB * 8 + BI) * 2: v = resident_wgs_of<BB, BI, 1>(); break; \
-      case (BB * 8 + BI) * 2 + 1: v = resident_wgs_of<BB, BI, 4>(); break;
-      PACKKV_RES(64, 2) PACKKV_RES(64, 3) PACKKV_RES(64, 4) PACKKV_RES(64, 8)
-      PACKKV_RES(128, 2) PACKKV_RES(128, 3) PACKKV_RES(128, 4) PACKKV_RES(128, 8)
-#undef PACKKV_RES
-      default: break;
-    }
+    dispatch_shape(B, bits, D, [&]<int BB, int BI, int DD>() {
+      v = g1 ? resident_wgs_of<BB, BI, 4, DD>() : resident_wgs_of<BB, BI, 1, DD>();
+    });
     r = v > 0 ? v : -1;
     slot.store(r, std::memory_order_relaxed);
   }
@@ -2101,38 +2150,42 @@ int attention_resident_wgs(int B, int bits, int G) {
 hipError_t launch_attention(const AttnArgs& a, int B, int n_streams, int n_caches, hipStream_t st,
                             bool paged) {
   const dim3 grid(n_streams * a.splits, n_caches);
-  if (paged) attn_dispatch<true>(a, B, grid, st);
-  else attn_dispatch<false>(a, B, grid, st);
+  if (paged) {
+    if (a.D != 128) return hipErrorInvalidValue;
+    dispatch_shape(B, a.bits, 128, [&]<int BB, int BI, int DD>() {
+      if constexpr (DD == 128) {
+        if (a.G == 1) hipLaunchKernelGGL((k_attn_decode<BB, BI, 1, DD, true>), grid, dim3(128), 0, st, a);
+        else hipLaunchKernelGGL((k_attn_decode<BB, BI, 4, DD, true>), grid, dim3(128), 0, st, a);
+      }
+    });
+  } else {
+    dispatch_shape(B, a.bits, a.D, [&]<int BB, int BI, int DD>() {
+      if (a.G == 1) hipLaunchKernelGGL((k_attn_decode<BB, BI, 1, DD, false>), grid, dim3(128), 0, st, a);
+      else hipLaunchKernelGGL((k_attn_decode<BB, BI, 4, DD, false>), grid, dim3(128), 0, st, a);
+    });
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_decompress(const GemvArgs& a, int B, bool is_v, int n_streams, const uint8_t* perm,
                              int64_t perm_stride, int mode, void* out, hipStream_t st) {
   dim3 grid(a.nb, n_streams), block(64);
-  const int sel = (B == 64 ? 0 : 4) + (is_v ? 2 : 0) + (a.bits > 4 ? 1 : 0);
-  switch (sel) {
-#define PACKKV_DEC(S, BB, V, W) \
-    case S: hipLaunchKernelGGL((k_decompress<BB, V, W>), grid, block, 0, st, a, perm, perm_stride, mode, out); break;
-    PACKKV_DEC(0, 64, false, false) PACKKV_DEC(1, 64, false, true) PACKKV_DEC(2, 64, true, false)
-    PACKKV_DEC(3, 64, true, true) PACKKV_DEC(4, 128, false, false) PACKKV_DEC(5, 128, false, true)
-    PACKKV_DEC(6, 128, true, false) PACKKV_DEC(7, 128, true, true)
-#undef PACKKV_DEC
-  }
+  dispatch_shape(B, a.bits, a.D, [&]<int BB, int BI, int DD>() {
+    constexpr bool W = BI > 4;
+    if (is_v) hipLaunchKernelGGL((k_decompress<BB, true, W, DD>), grid, block, 0, st, a, perm, perm_stride, mode, out);
+    else hipLaunchKernelGGL((k_decompress<BB, false, W, DD>), grid, block, 0, st, a, perm, perm_stride, mode, out);
+  });
   return hipGetLastError();
 }
 
 hipError_t launch_stats(const GemvArgs& a, int B, bool is_v, int n_streams, unsigned long long* out,
                         hipStream_t st) {
   dim3 grid(a.nb, n_streams), block(64);
-  const int sel = (B == 64 ? 0 : 4) + (is_v ? 2 : 0) + (a.bits > 4 ? 1 : 0);
-  switch (sel) {
-#define PACKKV_STATS(S, BB, V, W) \
-    case S: hipLaunchKernelGGL((k_stats<BB, V, W>), grid, block, 0, st, a, out); break;
-    PACKKV_STATS(0, 64, false, false) PACKKV_STATS(1, 64, false, true) PACKKV_STATS(2, 64, true, false)
-    PACKKV_STATS(3, 64, true, true) PACKKV_STATS(4, 128, false, false) PACKKV_STATS(5, 128, false, true)
-    PACKKV_STATS(6, 128, true, false) PACKKV_STATS(7, 128, true, true)
-#undef PACKKV_STATS
-  }
+  dispatch_shape(B, a.bits, a.D, [&]<int BB, int BI, int DD>() {
+    constexpr bool W = BI > 4;
+    if (is_v) hipLaunchKernelGGL((k_stats<BB, true, W, DD>), grid, block, 0, st, a, out);
+    else hipLaunchKernelGGL((k_stats<BB, false, W, DD>), grid, block, 0, st, a, out);
+  });
   return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ struct EncArgs {
   int64_t src_stream;       // elements between streams in the source
   int64_t src_block;        // elements between blocks in the source
   int64_t n_tokens;         // total tokens per stream after this call
-  int32_t bits, B, permute, mode;
+  int32_t bits, B, D, permute, mode;
   int32_t block0;           // kTail: index of the block being (re)encoded
   // kTail: tokens appended by this call, [S][new_cnt][D] fp16 (new_stream
   // elements apart), at positions new_at.. of the open block; they are read
@@ -74,6 +74,7 @@ struct GemvArgs {
   int64_t n_tokens;
   int32_t nb;            // records per stream = ceil(T / B)
   int32_t bits;
+  int32_t D;             // head_dim: 64, 128 or 256
   int32_t blocks_per_wg;
   int32_t splits;        // workgroups per stream
   int32_t G;
@@ -109,6 +110,7 @@ struct AttnArgs {
   int64_t n_tokens;         // paged: unused (lengths[s] per stream)
   int32_t nb;
   int32_t bits;
+  int32_t D;                // head_dim: 64, 128 or 256 (the paged cache: 128)
   int32_t blocks_per_wg;
   int32_t splits;
   int32_t G;
@@ -116,24 +118,23 @@ struct AttnArgs {
   const uint16_t* q;     // [caches][S][G][D] fp16
   float* out;            // [caches][S][G][D]
   int64_t qo_stride;     // elements per cache in q and out: S * G * D
-  uint8_t* ws;           // per cache ws_stride bytes of partials [S][G][splits][kAttnPartial]
+  uint8_t* ws;           // per cache ws_stride bytes of partials [S][G][splits][D + 4]
   uint64_t ws_stride;
   uint8_t* tk;           // per cache tk_stride bytes: per-stream arrival counters
   uint64_t tk_stride;    //   (u32 [S], zero between calls)
 };
-constexpr int kAttnPartial = 132;   // D partial sums, running max, weight sum, 2 pad
 
 hipError_t launch_encode(const EncArgs& a, int n_streams, int n_blocks, hipStream_t st);
 hipError_t launch_scan_offsets(uint32_t* k_off, uint32_t* v_off, int64_t off_stride,
                                int n_streams, int nb, hipStream_t st);
 hipError_t launch_stage_tail(const uint16_t* k, const uint16_t* v, int64_t src_stream,
-                             uint16_t* tk, uint16_t* tv, int B, int at, int cnt,
+                             uint16_t* tk, uint16_t* tv, int B, int D, int at, int cnt,
                              int n_streams, hipStream_t st);
 hipError_t launch_qk(const GemvArgs& a, int B, int n_streams, hipStream_t st);
 hipError_t launch_pv(const GemvArgs& a, int B, int n_streams, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, int B, int n_streams, int n_caches, hipStream_t st,
                             bool paged = false);
-int attention_resident_wgs(int B, int bits, int G);
+int attention_resident_wgs(int B, int bits, int G, int D);
 hipError_t launch_paged_alloc(const EncArgs& a, int n_streams, int64_t n_tokens, hipStream_t st);
 hipError_t launch_paged_init(const PageAlloc& p, int32_t* lengths, int32_t* status, hipStream_t st);
 hipError_t launch_paged_release(const PageAlloc& p, const uint2* k_tab, const uint2* v_tab,

@@ -19,8 +19,12 @@
  *   nr = ceil(n / R) runs of R = 32 slots; hdr = the byte (w << 4) | m for
  *   b <= 4, the little-endian u16 (w << 8) | m for b = 5..8, for the run's
  *   width w = bit_length(max - min) and minimum m; payload = for each run r,
- *   for each channel c, w u32 words holding u = q - m of slot i in bits
- *   [i*w, i*w + w).  Quantisation: K per channel over the block's tokens, V
+ *   for each channel c, w u32 words holding u = q - m of its 32 slots in the
+ *   sliced order: with c-bit containers (c = 4 for b <= 4, 8 above), slot i
+ *   is field j = i % (32/c) of container k = i / (32/c), and bit p of its u
+ *   is bit c*j + Q of run word W, where W = k / g, Q = w*(k % g) + p if w
+ *   divides c (g = c/w), else W = k, Q = p for k < w and W = p, Q = k for
+ *   k >= w.  Quantisation: K per channel over the block's tokens, V
  *   per token over D channels; zero = group minimum, scale = the smallest
  *   fp16 h with h * (2^b - 1) >= max - min, q = round-half-even((x-min)/h).
  *   Slot i of block j holds token j*B + perm[j][i]; the permutation is the
@@ -68,7 +72,7 @@ enum {
                               a device latch, an input value outside the
                               method's domain (non-finite K/V, a V-GEMV weight
                               that is negative or non-finite)                 */
-  PACKKV_EUNSUPPORTED = 2, /* configuration outside D 128, b 2..8, B 64/128, R 32 */
+  PACKKV_EUNSUPPORTED = 2, /* configuration outside D 64/128/256, b 2..8, B 64/128, R 32 */
   PACKKV_ECAPACITY = 3,    /* tokens over max_tokens, or arena region overflow */
   PACKKV_ECORRUPT = 4,     /* a record header is inconsistent                  */
   PACKKV_EHIP = 5,         /* a HIP runtime call or kernel launch failed       */
@@ -77,7 +81,9 @@ enum {
 
 /* Format parameters. */
 typedef struct {
-  int32_t head_dim;     /* D: must be 128                                    */
+  int32_t head_dim;     /* D: 64, 128 or 256 (Fig. 5 caption: quantisation  */
+                        /* groups along the channel axis; the paged cache  */
+                        /* takes 128 only)                                  */
   int32_t bits;         /* b: 2 .. 8 (5..8: two-byte header entries)         */
   int32_t block_tokens; /* B: 64 or 128                                      */
   int32_t run_tokens;   /* R: must be 32                                     */

@@ -14,26 +14,26 @@ def say(*a):
     sys.stdout.flush()
 
 
-def make_kv(law: str, S: int, T: int, block: int, seed: int = 0):
+def make_kv(law: str, S: int, T: int, block: int, seed: int = 0, D: int = 128):
     """fp16 K, V [S][T][D] for one of the small parity laws."""
     ks, vs = [], []
     for s in range(S):
         if law in ("gauss", "bimodal"):
-            w = kvsynth.Workload("t", 1, S, 1, T, 128, 4, block, law)
+            w = kvsynth.Workload("t", 1, S, 1, T, D, 4, block, law)
             k, v = kvsynth.stream_kv(w, s, seed=seed, tokens=T)
         elif law == "struct":
-            k, v = kvsynth.structured_kv(T, 128, block, 32, seed=seed + s)
+            k, v = kvsynth.structured_kv(T, D, block, 32, seed=seed + s)
         elif law == "mixed":            # half the channels nearly constant: narrow runs
-            k, v = kvsynth.structured_kv(T, 128, block, 32, seed=seed + s, noise=0.3, shuffle=False)
+            k, v = kvsynth.structured_kv(T, D, block, 32, seed=seed + s, noise=0.3, shuffle=False)
         elif law == "grid":             # values on an fp16 grid: exact dequantisation
             rng = np.random.default_rng([seed, s])
-            k = (rng.integers(-60, 60, (T, 128)) * 0.125).astype(np.float16)
-            v = (rng.integers(-60, 60, (T, 128)) * 0.0625).astype(np.float16)
+            k = (rng.integers(-60, 60, (T, D)) * 0.125).astype(np.float16)
+            v = (rng.integers(-60, 60, (T, D)) * 0.0625).astype(np.float16)
         elif law == "subnormal":        # fp16 subnormals, signed zeros, tiny ranges
             rng = np.random.default_rng([seed, s, 7])
-            bits = rng.integers(0, 0x0400, (2, T, 128)).astype(np.uint16)
-            bits |= (rng.random((2, T, 128)) < 0.5).astype(np.uint16) << 15
-            big = rng.random((2, T, 128)) < 0.02           # a few normal values
+            bits = rng.integers(0, 0x0400, (2, T, D)).astype(np.uint16)
+            bits |= (rng.random((2, T, D)) < 0.5).astype(np.uint16) << 15
+            big = rng.random((2, T, D)) < 0.02             # a few normal values
             bits[big] = rng.integers(0x0400, 0x1400, int(big.sum())).astype(np.uint16)
             k, v = bits[0].view(np.float16), bits[1].view(np.float16)
         else:
@@ -44,7 +44,7 @@ def make_kv(law: str, S: int, T: int, block: int, seed: int = 0):
 
 
 def oracle_streams(K, V, bits, block, permute=True):
-    cfg = oracle.Config(bits=bits, block=block, permute=permute)
+    cfg = oracle.Config(head_dim=K.shape[2], bits=bits, block=block, permute=permute)
     return [ostream.compress(K[s], V[s], cfg) for s in range(K.shape[0])]
 
 

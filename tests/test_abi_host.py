@@ -33,7 +33,8 @@ def cfg(bits=4, block=64, D=128, R=32, permute=1):
 
 
 @pytest.mark.parametrize("bad,code", [
-    (dict(D=64), _lib.EUNSUPPORTED), (dict(bits=9), _lib.EUNSUPPORTED), (dict(bits=1), _lib.EUNSUPPORTED),
+    (dict(D=96), _lib.EUNSUPPORTED), (dict(D=512), _lib.EUNSUPPORTED), (dict(bits=9), _lib.EUNSUPPORTED),
+    (dict(bits=1), _lib.EUNSUPPORTED),
     (dict(block=32), _lib.EUNSUPPORTED), (dict(R=16), _lib.EUNSUPPORTED), (dict(permute=3), _lib.EINVAL),
 ])
 def test_unsupported_configs_are_rejected(lib, bad, code):
@@ -57,6 +58,27 @@ def test_sizes_follow_the_worst_case_record(lib, bits, block):
     assert s.off_bytes == 3 * (nb + 1) * 4 and s.perm_bytes == 3 * nb * block
     assert s.tail_bytes == 3 * block * 128 * 2
     assert lib.packkv_arena_stride_bytes(ctypes.byref(cfg(bits, block)), 1000) == s.arena_stride
+
+
+@pytest.mark.parametrize("D,bits,block", [(64, 4, 64), (64, 8, 128), (256, 2, 64), (256, 8, 128)])
+def test_sizes_follow_the_head_dim(lib, D, bits, block):
+    """Records scale with head_dim: K params 4D, V params 4B, one header entry
+    per (run, channel), b words per (run, channel) at full width."""
+    s = _lib.Sizes()
+    assert lib.packkv_cache_sizes(ctypes.byref(cfg(bits, block, D=D)), 2, 1000, ctypes.byref(s)) == 0
+    nb, nr, hb = -(-1000 // block), block // 32, 1 if bits <= 4 else 2
+    krec = -(-(4 * D + hb * nr * D) // 16) * 16 + 4 * nr * D * bits
+    vrec = -(-(4 * block + hb * nr * D) // 16) * 16 + 4 * nr * D * bits
+    assert s.arena_stride >= nb * max(krec, vrec) + 64 and s.arena_stride % 256 == 0
+    assert s.tail_bytes == 2 * block * D * 2
+
+
+def test_paged_cache_takes_head_dim_128_only(lib):
+    s = _lib.PagedSizes()
+    for D in (64, 256):
+        c = cfg(4, 64, D=D)
+        assert lib.packkv_paged_sizes(ctypes.byref(c), 2, 1000, 16, 65536, ctypes.byref(s)) == _lib.EUNSUPPORTED
+    assert lib.packkv_paged_sizes(ctypes.byref(cfg(4, 64)), 2, 1000, 16, 65536, ctypes.byref(s)) == 0
 
 
 def test_invalid_arguments_fail_before_any_launch(lib):

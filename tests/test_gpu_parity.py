@@ -56,8 +56,9 @@ def torch_dev():
 
 def gpu_cache(torch, dev, K, V, bits, block, permute, max_tokens=None):
     from decode_gemv_amd import PackedKVCache
-    S, T, _ = K.shape
-    c = PackedKVCache(S, max_tokens or T + 70, bits=bits, block=block, permute=permute, device=str(dev))
+    S, T, D = K.shape
+    c = PackedKVCache(S, max_tokens or T + 70, bits=bits, block=block, permute=permute, device=str(dev),
+                      head_dim=D)
     c.compress(torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev))
     return c
 
@@ -84,8 +85,8 @@ def assert_state_equal(c, refs):
     for s, ref in enumerate(refs):
         assert np.array_equal(perm[s, :nb], ref.perm_table()), f"perm differs, stream {s}"
         nt = T % B
-        tk = c.tail_k.view(c.n_streams, B, 128)[s, :nt].cpu().numpy()
-        tv = c.tail_v.view(c.n_streams, B, 128)[s, :nt].cpu().numpy()
+        tk = c.tail_k.view(c.n_streams, B, c.head_dim)[s, :nt].cpu().numpy()
+        tv = c.tail_v.view(c.n_streams, B, c.head_dim)[s, :nt].cpu().numpy()
         assert np.array_equal(tk.view(np.uint16), ref.tail_k.view(np.uint16))
         assert np.array_equal(tv.view(np.uint16), ref.tail_v.view(np.uint16))
 
