@@ -158,6 +158,25 @@ __device__ __forceinline__ bool hdr4_full(uint32_t x) {
   return ((x ^ want) & (0xF0F0F0F0u | mbad)) == 0u;
 }
 
+// Four header bytes (w << 4 | m): true if any of them is inconsistent, i.e.
+// its width is above BITS or its minimum leaves no room for the width (a
+// valid run has max - m in [2^(w-1), 2^w - 1] and max <= L = 2^BITS - 1).
+// SWAR: a byte-wise table lookup (v_perm_b32 on w & 7) gives
+// c(w) = 2^(w-1) (0 for w = 0, 16 for w > BITS) plus 127 - L, so that
+// m + c(w) sets bit 7 exactly when m + 2^(w-1) > L; bit 7 of the header
+// byte itself is set for w >= 8.  No byte carries into the next
+// (m + c <= 15 + 16 + 124).
+template <int BITS>
+__device__ __forceinline__ bool hdr4_bad(uint32_t x) {
+  constexpr uint32_t L = (1u << BITS) - 1u;
+  constexpr uint32_t c0 = 127u - L, c1 = 1u + c0, c2 = (BITS >= 2 ? 2u : 16u) + c0,
+                     c3 = (BITS >= 3 ? 4u : 16u) + c0, c4 = (BITS >= 4 ? 8u : 16u) + c0, cx = 16u + c0;
+  constexpr uint32_t lo = c0 | c1 << 8 | c2 << 16 | c3 << 24;
+  constexpr uint32_t hi = c4 | cx << 8 | cx << 16 | cx << 24;
+  const uint32_t c = __builtin_amdgcn_perm(hi, lo, (x >> 4) & 0x07070707u);
+  return (((x & 0x0F0F0F0Fu) + c) | x) & 0x80808080u;
+}
+
 // Latch the first device-side error code.
 __device__ __forceinline__ void latch(int32_t* status, int code) {
   if (status) atomicCAS(status, 0, code);

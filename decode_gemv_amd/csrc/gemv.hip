@@ -189,29 +189,36 @@ struct BlockDecoder {
       asm volatile("" : "+v"(hv));
       h[k] = k / DL < nr ? hv : 0u;
     }
-    bool all_full = false;
-    if (nr == NR) {
-      bool ok = true;
+    // header dwords lane + 64i, four runs each; dwords past the record's
+    // nr rows of runs read as width 0, minimum 0 (consistent, not full)
+    constexpr int HWL = (HW + 63) / 64;
+    uint32_t hx[HWL];
+    bool full = nr == NR;
 #pragma unroll
-      for (int i = 0; i < (HW + 63) / 64; ++i)        // header dwords lane + 64i
-        if (HW % 64 == 0 || lane + 64 * i < HW)
-          ok &= hdr4_full<BITS>(reinterpret_cast<const uint32_t*>(rec + HDR)[lane + 64 * i]);
-      all_full = __ballot(!ok) == 0;
+    for (int i = 0; i < HWL; ++i) {
+      const int di = lane + 64 * i;
+      hx[i] = 0u;
+      if (HW % 64 == 0 || di < HW) {
+        const uint32_t x = reinterpret_cast<const uint32_t*>(rec + HDR)[di];
+        hx[i] = di < nruns / 4 ? x : 0u;
+        full &= hdr4_full<BITS>(hx[i]);
+      }
     }
+    const bool all_full = __ballot(!full) == 0;
     uint32_t off[NRL];
 #pragma unroll
     for (int k = 0; k < NRL; ++k) off[k] = (uint32_t)((lane + 64 * k) * BITS);
     uint32_t total = (uint32_t)(nruns * BITS);
     bool bad = false;
     if (!all_full) {
-      constexpr int L = (1 << BITS) - 1;
+      // as scan_runs: a valid run has max - m in [2^(w-1), 2^w - 1] and
+      // max <= L, so its containers m + u never carry into the next slot
+#pragma unroll
+      for (int i = 0; i < HWL; ++i) bad |= hdr4_bad<BITS>(hx[i]);
       uint32_t running = 0;                            // deficit of earlier groups
 #pragma unroll
       for (int k = 0; k < NRL; ++k) {
-        const int w = (int)(h[k] >> 4), m = (int)(h[k] & 15u);
-        // as scan_runs: a valid run has max - m in [2^(w-1), 2^w - 1] and
-        // max <= L, so its containers m + u never carry into the next slot
-        bad |= w > BITS || m > L || (w > 0 && m + (1 << (w - 1)) > L);
+        const int w = (int)(h[k] >> 4);
         const int d = (lane + 64 * k) < nruns ? BITS - w : 0;
         off[k] -= running;
         if (__ballot(d != 0) != 0) {
@@ -1621,14 +1628,18 @@ void k_pv_gemv(GemvArgs a) {
 // jj.  Each split leaves (partial out[D], its max m, its weight sum l); the
 // last workgroup of the stream merges the splits with the usual rescaling.
 __device__ __forceinline__ float wave_max_f(float v) {
-  // DPP with bound_ctrl off: lanes without a source keep their own value
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x111, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x112, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x114, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x118, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x142, 0xA, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x143, 0xC, 0xF, false)));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  // fp32 order is the unsigned order of the key bits ^ 0x80000000 (x >= 0)
+  // or ~bits (x < 0); a lane without a DPP source reads key 0, the lowest
+  const uint32_t b = __float_as_uint(v);
+  uint32_t k = b ^ ((uint32_t)((int)b >> 31) | 0x80000000u);
+  k = max(k, (uint32_t)dpp_i<0x111>((int)k));
+  k = max(k, (uint32_t)dpp_i<0x112>((int)k));
+  k = max(k, (uint32_t)dpp_i<0x114>((int)k));
+  k = max(k, (uint32_t)dpp_i<0x118>((int)k));
+  k = max(k, (uint32_t)dpp_i<0x142, 0xA>((int)k));
+  k = max(k, (uint32_t)dpp_i<0x143, 0xC>((int)k));
+  const uint32_t r = readlane_u32(k, 63);
+  return __uint_as_float(r ^ (r >> 31 ? 0x80000000u : 0xFFFFFFFFu));
 }
 // 2^x without the range fix-ups of exp2f: arguments here are <= 0 and a
 // result that underflows is a weight of 0
