@@ -143,6 +143,20 @@ __device__ __forceinline__ void run_to_nibbles(int w, uint32_t m, const uint32_t
   out[0] += mm; out[1] += mm; out[2] += mm; out[3] += mm;
 }
 
+// A run of width w = 0, 1 or 2 (below a full width of 2 or 3) from its first
+// two payload words, without a branch on w: both widths divide the 4-bit
+// container, so container k sits in word (k w) / 4 at bit (k w) % 4 of each
+// nibble, under the mask of w low bits per nibble (0 for w = 0).
+__device__ __forceinline__ void narrow_to_nibbles(int w, uint32_t m, uint32_t x0, uint32_t x1, uint32_t out[4]) {
+  const uint32_t mask = (0x11111111u << w) - 0x11111111u;
+  const bool two = w == 2;
+  const uint32_t mm = nibble_splat(m);
+  out[0] = (x0 & mask) + mm;
+  out[1] = ((x0 >> w) & mask) + mm;
+  out[2] = ((two ? x1 : x0 >> 2) & mask) + mm;
+  out[3] = ((two ? x1 >> 2 : x0 >> 3) & mask) + mm;
+}
+
 // A run stored at the full width BITS: its BITS words -> four container words.
 template <int BITS>
 __device__ __forceinline__ void full_to_nibbles(const uint32_t wd[4], uint32_t out[4]) {

@@ -221,10 +221,19 @@ struct BlockDecoder {
         const int w = (int)(h[k] >> 4);
         const int d = (lane + 64 * k) < nruns ? BITS - w : 0;
         off[k] -= running;
-        if (__ballot(d != 0) != 0) {
-          const int incl = wave_incl_scan(d);
-          off[k] -= (uint32_t)(incl - d);
-          running += (uint32_t)__builtin_amdgcn_readlane(incl, 63);
+        const uint64_t short_runs = __ballot(d != 0);
+        if (short_runs != 0) {
+          if (BITS < 4 && __ballot(d > 1) == 0) {
+            // deficits of 0 or 1 (the usual case below 4 bits): count the
+            // lanes below (at 4 bits the extra path costs registers)
+            off[k] -= __builtin_amdgcn_mbcnt_hi((uint32_t)(short_runs >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)short_runs, 0u));
+            running += (uint32_t)__builtin_popcountll(short_runs);
+          } else {
+            const int incl = wave_incl_scan(d);
+            off[k] -= (uint32_t)(incl - d);
+            running += (uint32_t)__builtin_amdgcn_readlane(incl, 63);
+          }
         }
       }
       total -= running;
@@ -276,18 +285,17 @@ struct BlockDecoder {
         const int w = (int)(h[k] >> 4);
         if (w != BITS) {
           if (k / DL < nr) {
-            uint32_t wd[4];
             if constexpr (BITS == 4) {
               // the words read are nib - m in every nibble (mod 2^32)
               const uint32_t mm = nibble_splat(h[k]);
+              uint32_t wd[4];
 #pragma unroll
               for (int i = 0; i < 4; ++i) wd[i] = nib[k][i] - mm;
+              run_to_nibbles<3>(w, h[k] & 15u, wd, nib[k]);
             } else {
               const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + pay) + off[k];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) wd[i] = i < BITS - 1 ? p[i] : 0u;
+              narrow_to_nibbles(w, h[k] & 15u, p[0], BITS == 3 ? p[1] : 0u, nib[k]);
             }
-            run_to_nibbles<BITS - 1>(w, h[k] & 15u, wd, nib[k]);
           } else {
             nib[k][0] = nib[k][1] = nib[k][2] = nib[k][3] = 0u;
           }
