@@ -181,13 +181,15 @@ struct BlockDecoder {
     const int pay = payload_offset(IS_V, B, nr, 1, D);
     const int nruns = nr * D;
     uint32_t h[NRL];
+    // read unconditionally (the staging always holds a full-size header) and
+    // select, instead of a branch around each read; all reads are issued
+    // before the first value is pinned, so they are in flight together
+#pragma unroll
+    for (int k = 0; k < NRL; ++k) h[k] = rec[HDR + lane + 64 * k];
 #pragma unroll
     for (int k = 0; k < NRL; ++k) {
-      // read unconditionally (the staging always holds a full-size header)
-      // and select, instead of a branch around each read
-      uint32_t hv = rec[HDR + lane + 64 * k];
-      asm volatile("" : "+v"(hv));
-      h[k] = k / DL < nr ? hv : 0u;
+      asm volatile("" : "+v"(h[k]));
+      h[k] = k / DL < nr ? h[k] : 0u;
     }
     // header dwords lane + 64i, four runs each; dwords past the record's
     // nr rows of runs read as width 0, minimum 0 (consistent, not full)
