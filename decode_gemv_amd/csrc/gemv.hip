@@ -1415,8 +1415,17 @@ struct RecordStream {
   }
 };
 
+// Occupancy asked of the register allocator for the K GEMV: at 2 and 3 bits
+// with one query and 64-token blocks 6 waves per SIMD (80 VGPRs, a few
+// values kept in scratch outside the block loop; measured 3-4 % faster than
+// 5 waves), at 4 bits the allocator's own choice (6 waves there: 4.5 %
+// slower).  (Tuned at D = 128.)
 template <int B, int BITS, int GT, int D>
-__global__ __launch_bounds__(64) void k_qk_gemv(GemvArgs a) {
+constexpr int qk_waves_per_eu() { return B == 64 && BITS <= 3 && GT == 1 && D == 128 ? 6 : 1; }
+
+template <int B, int BITS, int GT, int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(qk_waves_per_eu<B, BITS, GT, D>())))
+void k_qk_gemv(GemvArgs a) {
   using KB = KSel<B, BITS, GT, D>;
   constexpr int REC = max_record_bytes(false, B, class_bits(BITS), D);
   constexpr int NCH = (REC + 1023) / 1024;
