@@ -1419,9 +1419,13 @@ struct RecordStream {
 // with one query and 64-token blocks 6 waves per SIMD (80 VGPRs, a few
 // values kept in scratch outside the block loop; measured 3-4 % faster than
 // 5 waves), at 4 bits the allocator's own choice (6 waves there: 4.5 %
-// slower).  (Tuned at D = 128.)
+// slower); with four queries on the matrix cores and 128-token blocks 3
+// waves (154 VGPRs instead of 188, no scratch; 17.5 % faster than 2 waves).
+// (Tuned at D = 128.)
 template <int B, int BITS, int GT, int D>
-constexpr int qk_waves_per_eu() { return B == 64 && BITS <= 3 && GT == 1 && D == 128 ? 6 : 1; }
+constexpr int qk_waves_per_eu() {
+  return D != 128 ? 1 : B == 64 && BITS <= 3 && GT == 1 ? 6 : B == 128 && BITS <= 4 && GT > 1 ? 3 : 1;
+}
 
 template <int B, int BITS, int GT, int D>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(qk_waves_per_eu<B, BITS, GT, D>())))
