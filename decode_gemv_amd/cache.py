@@ -80,6 +80,35 @@ class PackedKVCache:
         a = self.k_arena if which == "K" else self.v_arena
         return a.view(self.n_streams, self.arena_stride)
 
+    # ------------------------------------------------------------ checkpoint
+    _STATE = ("k_arena", "v_arena", "k_off", "v_off", "perm", "tail_k", "tail_v")
+
+    def state_dict(self) -> dict:
+        """The cache's whole state as host tensors: both arenas, both offset
+        tables, the permutation, the raw tail staging and the token count.
+        Synchronises the current stream first."""
+        torch.cuda.current_stream().synchronize()
+        st = {name: getattr(self, name).cpu() for name in self._STATE}
+        st["n_tokens"] = self.n_tokens
+        st["config"] = (self.n_streams, self.max_tokens, self.bits, self.block, int(self.cfg.permute),
+                        self.head_dim)
+        return st
+
+    def load_state_dict(self, st: dict) -> None:
+        """Restores a state taken by state_dict from a cache of the same
+        configuration; appends then continue where that cache stopped."""
+        mine = (self.n_streams, self.max_tokens, self.bits, self.block, int(self.cfg.permute), self.head_dim)
+        if tuple(st["config"]) != mine:
+            raise ValueError(f"state of a cache configured {tuple(st['config'])}, this one is {mine}")
+        for name in self._STATE:
+            dst = getattr(self, name)
+            src = st[name]
+            if src.shape != dst.shape or src.dtype != dst.dtype:
+                raise ValueError(f"{name}: shape or dtype differs")
+            dst.copy_(src, non_blocking=False)
+        self._c.n_tokens = int(st["n_tokens"])
+        self.status.zero_()
+
     # ------------------------------------------------------------- encoding
     def compress(self, k: torch.Tensor, v: torch.Tensor) -> None:
         """Prefill: k, v fp16 [S][T][D] contiguous on the device."""
