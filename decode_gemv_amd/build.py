@@ -47,24 +47,37 @@ def _run(cmd, verbose):
         print(errs, file=sys.stderr)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile all sources and link the shared library; returns its path."""
+# AddressSanitizer on the host code only (argument checks, sizes, launches);
+# the device code is built as usual
+HOST_ASAN = "-Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer".split()
+
+
+def build(verbose: bool = False, out: str = LIB, host_asan: bool = False) -> str:
+    """Compile all sources and link the shared library; returns its path.
+    host_asan: instrument the host code with AddressSanitizer (load the
+    library with the sanitizer runtime preloaded)."""
     hipcc = _hipcc()
+    extra = HOST_ASAN if host_asan else []
     with tempfile.TemporaryDirectory(prefix="packkv_build_") as tmp:
         objs = []
         cmds = []
         for src in SOURCES:
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
             objs.append(obj)
-            cmds.append([hipcc, *COMMON, *PER_SOURCE.get(src, []), "-c",
+            cmds.append([hipcc, *COMMON, *extra, *PER_SOURCE.get(src, []), "-c",
                          os.path.join(CSRC, src), "-o", obj])
         with concurrent.futures.ThreadPoolExecutor(len(cmds)) as ex:
             list(ex.map(lambda c: _run(c, verbose), cmds))
-        out_tmp = LIB + ".tmp"
-        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out_tmp], verbose)
-        os.replace(out_tmp, LIB)
-    return LIB
+        out_tmp = out + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra[:2], *objs, "-o", out_tmp], verbose)
+        os.replace(out_tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+    ap = argparse.ArgumentParser(description="build libpackkv.so for gfx950")
+    ap.add_argument("--out", default=LIB, help="library path (default: the in-tree one)")
+    ap.add_argument("--host-asan", action="store_true", help="AddressSanitizer on the host code")
+    args = ap.parse_args()
+    print(build(verbose=True, out=args.out, host_asan=args.host_asan))
