@@ -738,6 +738,7 @@ struct VBlock {
   static constexpr int ND = 5;                        // 4-bit digits of p'
   static constexpr int DIG_WORDS = GT * ND * NG;
   static constexpr int LDS_WORDS = DIG_WORDS + (STAGED ? GT * B : 0);   // digit words, then the weights
+  static constexpr int SCRATCH_BYTES = 0;            // the staged record is only read
 
   uint32_t* dig;                                      // [GT][ND][NG]
   uint32_t* pst;                                      // [GT][B] fixed-point weights
@@ -911,8 +912,8 @@ struct VBlockM {
   static constexpr int KS = B / 64;                   // 64-token steps of the MFMA
   static constexpr int VP = B / 8 + 2;                // plane pitch per channel (words)
   static constexpr int LDS_WORDS = 16 * B / 4;        // digit rows [16][B] bytes
+  static constexpr int SCRATCH_BYTES = kD * VP * 4;   // the plane overwrites the staged record
   static_assert(GT == 4, "operand rows are (query, digit) for four queries");
-  static_assert(kD * VP * 4 <= staging_bytes(max_record_bytes(true, B, 4, kD)), "the plane reuses the staging");
 
   uint8_t* dig;
   int lane;
@@ -1237,6 +1238,7 @@ struct VBlockW {
   static constexpr int ND = 3;                        // byte digits of p'
   static constexpr int DIG_WORDS = GT * ND * NQ;
   static constexpr int LDS_WORDS = DIG_WORDS + GT * B;
+  static constexpr int SCRATCH_BYTES = 0;            // the staged record is only read
 
   uint32_t* dig;                                      // [GT][ND][NQ]
   uint32_t* pst;                                      // [GT][B] fixed-point weights
@@ -1374,8 +1376,6 @@ using VSel = std::conditional_t<(BITS > 4), VBlockW<B, GT, D>,
                                 std::conditional_t<(GT > 1 && D == 128), VBlockM<B, BITS, GT>,
                                                    VBlock<B, BITS, GT, D, STAGED>>>;
 
-// The largest record the kernels of a width class stage: b <= 4 or b = 5..8.
-__host__ __device__ constexpr int class_bits(int bits) { return bits > 4 ? 8 : 4; }
 
 // ---------------------------------------------------------------------------
 // Streaming skeleton shared by the GEMVs and by each wave of fused
@@ -1431,7 +1431,7 @@ template <int B, int BITS, int GT, int D>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(qk_waves_per_eu<B, BITS, GT, D>())))
 void k_qk_gemv(GemvArgs a) {
   using KB = KSel<B, BITS, GT, D>;
-  constexpr int REC = max_record_bytes(false, B, class_bits(BITS), D);
+  constexpr int REC = max_record_bytes(false, B, BITS, D);
   constexpr int NCH = (REC + 1023) / 1024;
   constexpr int BUF = staging_bytes(REC) > KB::SCRATCH_BYTES ? staging_bytes(REC) : KB::SCRATCH_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t rec[BUF];
@@ -1522,9 +1522,10 @@ void k_pv_gemv(GemvArgs a) {
   using VB = VSel<B, BITS, GT, D>;
   constexpr int NH = VB::NH;
   constexpr int NA = VB::NA;
-  constexpr int REC = max_record_bytes(true, B, class_bits(BITS), D);
+  constexpr int REC = max_record_bytes(true, B, BITS, D);
   constexpr int NCH = (REC + 1023) / 1024;
-  __shared__ __attribute__((aligned(16))) uint8_t rec[staging_bytes(REC)];
+  constexpr int BUF = staging_bytes(REC) > VB::SCRATCH_BYTES ? staging_bytes(REC) : VB::SCRATCH_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t rec[BUF];
   __shared__ __attribute__((aligned(16))) uint32_t dig[VB::LDS_WORDS];
 
   const int lane = threadIdx.x;
@@ -1684,13 +1685,14 @@ void k_attn_decode(AttnArgs a) {
   using VB = VSel<B, BITS, GT, D, false>;
   constexpr int NH = B / 64;
   constexpr int PF = attn_partial_floats(D);      // floats per split partial
-  constexpr int REC_K = max_record_bytes(false, B, class_bits(BITS), D);
-  constexpr int REC_V = max_record_bytes(true, B, class_bits(BITS), D);
+  constexpr int REC_K = max_record_bytes(false, B, BITS, D);
+  constexpr int REC_V = max_record_bytes(true, B, BITS, D);
   constexpr int NCH_K = (REC_K + 1023) / 1024;
   constexpr int NCH_V = (REC_V + 1023) / 1024;
   constexpr int BUF_K = staging_bytes(REC_K) > KB::SCRATCH_BYTES ? staging_bytes(REC_K) : KB::SCRATCH_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t rec_k[BUF_K];
-  __shared__ __attribute__((aligned(16))) uint8_t rec_v[staging_bytes(REC_V)];
+  constexpr int BUF_V = staging_bytes(REC_V) > VB::SCRATCH_BYTES ? staging_bytes(REC_V) : VB::SCRATCH_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t rec_v[BUF_V];
   __shared__ __attribute__((aligned(16))) uint8_t qs[KB::QS_BYTES];
   __shared__ __attribute__((aligned(16))) uint32_t dig[VB::LDS_WORDS];
   __shared__ __attribute__((aligned(16))) float ring[2][GT][B];   // scores of blocks jj & 1
