@@ -8,6 +8,13 @@ width w (0..b) and minimum m (0..2^b - 1): one byte (w << 4 | m) up to b = 4,
 two bytes (little-endian w << 8 | m) for b = 5..8, where m no longer fits a
 nibble.  The pages give no header encoding; this one is the plainest that
 holds both fields.
+
+Payload order (a format variant; the explainer page's "Block matrix before
+and after repacking" asks that the packed layout suit the GPU that consumes
+it): 0 stores a record's (run, channel) entries run-major, then by channel;
+1 stores each run row of a K record by decreasing width, ties by increasing
+channel, so that neighbouring entries share a width.  V records and headers
+keep order 0 in both.
 """
 
 from __future__ import annotations
@@ -22,6 +29,7 @@ class Config:
     block: int = 64
     run: int = 32
     permute: int = 1          # 0 identity, 1 greedy grouping, 2 sort key (oracle.perm)
+    payload_order: int = 0    # 0 run-major then channel; 1 K rows by decreasing width
 
     def __post_init__(self):
         assert 2 <= self.bits <= 8, "b must be 2 .. 8"
@@ -30,6 +38,7 @@ class Config:
         assert self.block % self.run == 0
         assert self.head_dim in (64, 128, 256), "D must be 64, 128 or 256"
         assert int(self.permute) in (0, 1, 2), "permute must be 0, 1 or 2"
+        assert self.payload_order in (0, 1), "payload_order must be 0 or 1"
 
     @property
     def levels(self) -> int:

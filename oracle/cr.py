@@ -35,7 +35,8 @@ def ratios(cache: StreamCache, which: str) -> dict:
     off = cache.offsets(which)
     for j in range(len(cache.blocks)):
         n = cache.block_tokens(j)
-        d = decode_record(which, arena[off[j]:off[j + 1]], n, D, cfg.block, R, cfg.header_bytes)
+        d = decode_record(which, arena[off[j]:off[j + 1]], n, D, cfg.block, R, cfg.header_bytes,
+                          cfg.payload_order if which == "K" else 0)
         par = 32 * D if which == "K" else 32 * n
         ideal += R * int(d.w.sum()) + 8 * cfg.header_bytes * d.w.size + par
         params += par

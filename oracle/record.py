@@ -34,7 +34,11 @@ Record of one block (all integers little-endian, every section contiguous):
     V:  scale[B] fp16 | zero[B] fp16 (slot order; slots >= n hold 0) |
         hdr[nr][D] (hb B each) | 0-pad to 16 B | payload | 0-pad to 16 B
 
-payload = for r in 0..nr-1, for c in 0..D-1: the w words of run (r, c).
+payload = for r in 0..nr-1, for c in row_order(r): the w words of run (r, c),
+where row_order is 0, 1, ..., D-1 (payload order 0) or, for a K record in
+payload order 1, the channels sorted by decreasing width w[r, c], equal
+widths by increasing channel.  The header stays in channel order either way,
+so the record's size does not depend on the order.
 """
 
 from __future__ import annotations
@@ -82,15 +86,26 @@ def bit_place(i: int, p: int, w: int, cont: int):
     return word, cont * j + q
 
 
-def pack_payload(q_slots: np.ndarray, w: np.ndarray, m: np.ndarray, run: int, cont: int = 4) -> bytes:
-    """The payload words of all (run, channel) pairs, run-major then channel;
-    cont = container bits (4 for b <= 4, 8 for b = 5..8)."""
+def row_order(w_row, order: int = 0) -> list:
+    """Channels of one run row in payload order: 0 by channel; 1 by
+    decreasing width, equal widths by increasing channel."""
+    D = len(w_row)
+    if order == 0:
+        return list(range(D))
+    assert order == 1
+    return sorted(range(D), key=lambda c: (-int(w_row[c]), c))
+
+
+def pack_payload(q_slots: np.ndarray, w: np.ndarray, m: np.ndarray, run: int, cont: int = 4,
+                 order: int = 0) -> bytes:
+    """The payload words of all (run, channel) pairs, run-major, each row in
+    row_order; cont = container bits (4 for b <= 4, 8 for b = 5..8)."""
     assert run == 32 and cont in (4, 8)
     q = np.asarray(q_slots, dtype=np.int64)
     n, D = q.shape
     out = bytearray()
     for r in range(w.shape[0]):
-        for c in range(D):
+        for c in row_order(w[r], order):
             wr = int(w[r, c])
             if wr == 0:
                 continue
@@ -117,12 +132,15 @@ def header_bytes(w: np.ndarray, m: np.ndarray, hb: int = 1) -> bytes:
     return ((w << 8) | m).astype("<u2").tobytes()
 
 
-def build_record(kind: str, q_slots, scale, zero, block: int, run: int, hb: int = 1) -> bytes:
+def build_record(kind: str, q_slots, scale, zero, block: int, run: int, hb: int = 1,
+                 order: int = 0) -> bytes:
     """Assemble the record bytes of one block.
 
     kind 'K': scale/zero have D entries (per channel).
     kind 'V': scale/zero have n entries in slot order, padded to B with 0.
+    order: payload order (1 is defined for K records only).
     """
+    assert order == 0 or kind == "K"
     q = np.asarray(q_slots, dtype=np.int64)
     n, D = q.shape
     if kind == "K":
@@ -140,7 +158,7 @@ def build_record(kind: str, q_slots, scale, zero, block: int, run: int, hb: int 
     head = f16_bits(sc).astype("<u2").tobytes() + f16_bits(ze).astype("<u2").tobytes()
     head += header_bytes(w, m, hb)
     head += bytes(_pad16(len(head)) - len(head))
-    body = pack_payload(q, w, m, run, 4 * hb)
+    body = pack_payload(q, w, m, run, 4 * hb, order)
     body += bytes(_pad16(len(body)) - len(body))
     return head + body
 

@@ -44,7 +44,7 @@ def encode_block(k16: np.ndarray, v16: np.ndarray, cfg: Config) -> BlockCode:
     qk, sk, zk = quantize_k_block(k16, cfg.bits)
     qv, sv, zv = quantize_v_tokens(v16, cfg.bits)
     perm = block_permutation(qk, qv, cfg.run, cfg.permute)
-    k_rec = build_record("K", qk[perm], sk, zk, cfg.block, cfg.run, cfg.header_bytes)
+    k_rec = build_record("K", qk[perm], sk, zk, cfg.block, cfg.run, cfg.header_bytes, cfg.payload_order)
     v_rec = build_record("V", qv[perm], sv[perm], zv[perm], cfg.block, cfg.run, cfg.header_bytes)
     return BlockCode(k_rec, v_rec, perm, qk[perm], qv[perm])
 
@@ -112,7 +112,8 @@ def decode_stream(cache: StreamCache):
     ko, vo = cache.offsets("K"), cache.offsets("V")
     for j in range(len(cache.blocks)):
         n = cache.block_tokens(j)
-        dk = decode_record("K", ka[ko[j]:ko[j + 1]], n, D, cfg.block, cfg.run, cfg.header_bytes)
+        dk = decode_record("K", ka[ko[j]:ko[j + 1]], n, D, cfg.block, cfg.run, cfg.header_bytes,
+                           cfg.payload_order)
         dv = decode_record("V", va[vo[j]:vo[j + 1]], n, D, cfg.block, cfg.run, cfg.header_bytes)
         assert dk.size == ko[j + 1] - ko[j] and dv.size == vo[j + 1] - vo[j]
         k_hat.append(dequantize(dk.q, dk.scale, dk.zero, axis=0))

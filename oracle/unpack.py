@@ -10,6 +10,10 @@ twice:
   shifted right by w*(k % g), masked to w bits per field;
 * otherwise container k < w is word k masked to its low w bits per field,
   and container k >= w collects bit k of every field of word p as its bit p.
+
+In payload order 1 (K records) a row's entries are stored by decreasing
+width, equal widths by channel; the offsets below walk the rows in that
+order, worked out here from the header without the encoder's helper.
 """
 
 from __future__ import annotations
@@ -31,8 +35,29 @@ class Decoded:
     size: int             # bytes consumed (the record length)
 
 
-def decode_record(kind: str, buf: bytes, n: int, D: int, block: int, run: int, hb: int = 1) -> Decoded:
-    """Decode one record; hb is the header entry size (1 byte up to b = 4, 2 above)."""
+def _entry_starts(w: np.ndarray, order: int) -> np.ndarray:
+    """Word offset of every (run, channel) entry in the payload [nr, D]."""
+    nr, D = w.shape
+    start = np.zeros((nr, D), np.int64)
+    pos = 0
+    for r in range(nr):
+        if order == 0:
+            seq = range(D)
+        else:
+            # widest first; a stable sort on the negated width keeps equal
+            # widths in channel order
+            seq = np.argsort(-w[r], kind="stable")
+        for c in seq:
+            start[r, c] = pos
+            pos += int(w[r, c])
+    return start
+
+
+def decode_record(kind: str, buf: bytes, n: int, D: int, block: int, run: int, hb: int = 1,
+                  order: int = 0) -> Decoded:
+    """Decode one record; hb is the header entry size (1 byte up to b = 4, 2
+    above); order is the payload order (1 only for K records)."""
+    assert order == 0 or kind == "K"
     nr = -(-n // run)
     b = np.frombuffer(buf, dtype=np.uint8)
     n_par = D if kind == "K" else block
@@ -47,7 +72,7 @@ def decode_record(kind: str, buf: bytes, n: int, D: int, block: int, run: int, h
     p0 = (4 * n_par + hb * nr * D + 15) // 16 * 16
     nwords = int(w.sum())
     words = np.frombuffer(buf[p0:p0 + 4 * nwords], dtype="<u4").astype(np.int64)
-    start = np.concatenate([[0], np.cumsum(w.ravel())[:-1]]).reshape(nr, D)
+    start = _entry_starts(w, order)
     cb = 4 * hb                                   # container bits
     per = 32 // cb                                # slots per container word
     rep1 = sum(1 << (cb * j) for j in range(per))  # bit 0 of every field

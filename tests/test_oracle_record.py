@@ -13,7 +13,9 @@ import kvsynth
 from oracle import Config, record, unpack, stream, quant
 
 
-def bitstring_decode(kind, buf, n, D, B, R, hb=1):
+def bitstring_decode(kind, buf, n, D, B, R, hb=1, order=0):
+    """order 1: each run row's payload holds the widest entries first, equal
+    widths by channel; walked here width by width from the largest."""
     nr = -(-n // R)
     npar = D if kind == "K" else B
     raw = list(buf[4 * npar:4 * npar + hb * nr * D])
@@ -26,7 +28,10 @@ def bitstring_decode(kind, buf, n, D, B, R, hb=1):
     pos = p0
     cb = 4 * hb                    # container field bits: 4 (b <= 4) or 8
     for r in range(nr):
-        for c in range(D):
+        row_w = [hdr[r * D + c] >> wsh for c in range(D)]
+        seq = list(range(D)) if order == 0 else [c for wv in range(8, -1, -1) for c in range(D) if row_w[c] == wv]
+        assert sorted(seq) == list(range(D))
+        for c in seq:
             w, m = hdr[r * D + c] >> wsh, hdr[r * D + c] & mmask
             words = buf[pos:pos + 4 * w]
             pos += 4 * w
@@ -232,3 +237,92 @@ def test_lossless_grid_values_are_reproduced_exactly():
     kh, vh, _, _ = stream.decode_stream(c)
     assert np.array_equal(stream.token_order(c, kh), k)
     assert np.array_equal(stream.token_order(c, vh), v)
+
+
+# ---- payload order 1: K rows stored by decreasing width -------------------
+
+def _single_channel_words(u, cb=4):
+    """Run words of one channel's 32 values, from the channel-order layout
+    (pinned by hand above)."""
+    q = np.zeros((32, 128), np.int64)
+    q[:, 0] = u
+    w, m = record.run_widths(q, 32)
+    return np.frombuffer(record.pack_payload(q, w, m, 32, cb), "<u4").tolist()
+
+
+def test_width_sorted_payload_by_hand():
+    """Two rows of a K block with chosen widths: the payload holds, row by
+    row, the widest entries first and equal widths by channel; each entry's
+    words are its channel-order words."""
+    q = np.zeros((64, 128), np.int64)
+    ua = [i % 8 for i in range(32)]                 # w = 3
+    ub = [7 - (i % 8) for i in range(32)]           # w = 3
+    uc = [i % 4 for i in range(32)]                 # w = 2
+    ud = [(i >> 3) & 1 for i in range(32)]          # w = 1
+    q[:32, 9], q[:32, 2], q[:32, 7], q[:32, 5] = ua, ub, uc, ud
+    q[32:, 5], q[32:, 100], q[32:, 3] = ua, uc, uc  # row 1: 5 (w 3), then 3 and 100 (w 2)
+    w, m = record.run_widths(q, 32)
+    assert w[0, 9] == w[0, 2] == 3 and w[0, 7] == 2 and w[0, 5] == 1
+    got = np.frombuffer(record.pack_payload(q, w, m, 32, 4, order=1), "<u4").tolist()
+    want = (_single_channel_words(ub) + _single_channel_words(ua) + _single_channel_words(uc)
+            + _single_channel_words(ud)
+            + _single_channel_words(ua) + _single_channel_words(uc) + _single_channel_words(uc))
+    assert got == want
+    assert _single_channel_words(ua) == [0xF6D4B290, 0xFE54BA10, 0xFEDC3210]
+    rec1 = record.build_record("K", q, np.ones(128), np.zeros(128), 64, 32, order=1)
+    rec0 = record.build_record("K", q, np.ones(128), np.zeros(128), 64, 32)
+    assert len(rec1) == len(rec0) and rec1[:512 + 256] == rec0[:512 + 256]   # params and header
+    assert rec1 != rec0
+    assert np.array_equal(unpack.decode_record("K", rec1, 64, 128, 64, 32, 1, order=1).q, q)
+    assert np.array_equal(bitstring_decode("K", rec1, 64, 128, 64, 32, 1, order=1)[0], q)
+
+
+@pytest.mark.parametrize("bits,block", [(2, 64), (3, 64), (4, 64), (4, 128), (3, 128), (6, 64), (8, 128)])
+@pytest.mark.parametrize("n", [1, 31, 33, 64, 100, 128])
+def test_width_sorted_roundtrip(bits, block, n):
+    """Payload order 1 on data with mixed widths: both readers recover the
+    ints, the size and header match order 0, the payload holds the same run
+    words rearranged, and a row whose widths are all equal is unchanged."""
+    if n > block:
+        pytest.skip("n > B")
+    cfg0 = Config(bits=bits, block=block)
+    cfg1 = Config(bits=bits, block=block, payload_order=1)
+    k, v = kvsynth.structured_kv(n, 128, block, 32, seed=n + bits)
+    c0, c1 = stream.encode_block(k, v, cfg0), stream.encode_block(k, v, cfg1)
+    assert c1.v_record == c0.v_record and np.array_equal(c1.perm, c0.perm)
+    hb = cfg1.header_bytes
+    d1 = unpack.decode_record("K", c1.k_record, n, 128, block, 32, hb, order=1)
+    assert np.array_equal(d1.q, c1.qk_slots)
+    assert np.array_equal(bitstring_decode("K", c1.k_record, n, 128, block, 32, hb, order=1)[0], c1.qk_slots)
+    assert len(c1.k_record) == len(c0.k_record) == d1.size
+    p0 = -(-(4 * 128 + hb * d1.w.size) // 16) * 16
+    assert c1.k_record[:p0] == c0.k_record[:p0]
+    w0 = np.frombuffer(c0.k_record[p0:], "<u4")
+    w1 = np.frombuffer(c1.k_record[p0:], "<u4")
+    assert sorted(w0.tolist()) == sorted(w1.tolist())
+    # the orders coincide exactly where, in every row, the entries that hold
+    # words (w > 0) already fall (weakly) in width from channel 0 to D-1
+    already_sorted = all(np.all(np.diff(row[row > 0]) <= 0) for row in d1.w)
+    assert (c1.k_record == c0.k_record) == already_sorted
+
+
+def test_width_sorted_uniform_rows_equal_channel_order():
+    """When every entry of a row has the same width the two orders coincide."""
+    rng = np.random.default_rng(4)
+    k = rng.standard_normal((64, 128)).astype(np.float16)
+    k[0], k[1], k[32], k[33] = -4, 4, -4, 4          # every run of every channel spans 0..15
+    v = rng.standard_normal((64, 128)).astype(np.float16)
+    c0 = stream.encode_block(k, v, Config(bits=4, block=64, permute=0))
+    c1 = stream.encode_block(k, v, Config(bits=4, block=64, permute=0, payload_order=1))
+    d = unpack.decode_record("K", c0.k_record, 64, 128, 64, 32)
+    assert np.all(d.w == 4)
+    assert c1.k_record == c0.k_record
+
+
+def test_width_sorted_stream_decodes_to_the_same_cache():
+    k, v = kvsynth.structured_kv(300, 128, 64, 32, seed=8)
+    a = stream.compress(k, v, Config(bits=3, block=64))
+    b = stream.compress(k, v, Config(bits=3, block=64, payload_order=1))
+    for x, y in zip(stream.decode_stream(a), stream.decode_stream(b)):
+        assert np.array_equal(x, y)
+    assert a.arena("K") != b.arena("K") and a.arena("V") == b.arena("V")
