@@ -74,13 +74,14 @@ def generate(w: kvsynth.Workload, torch, dev):
     return K, V
 
 
-def cpu_baseline(w: kvsynth.Workload, n_streams: int, budget_s: float, permute: int = 1) -> dict:
+def cpu_baseline(w: kvsynth.Workload, n_streams: int, budget_s: float, permute: int = 1,
+                 payload_order: int = 0) -> dict:
     """The fp64 oracle's decode steps on a sample of streams, single-threaded,
     for about budget_s seconds (whole steps over the sample, at least one)."""
     from threadpoolctl import threadpool_limits
     import oracle
     from oracle import stream as ostream, attention
-    cfg = oracle.Config(bits=w.bits, block=w.block, permute=permute)
+    cfg = oracle.Config(bits=w.bits, block=w.block, permute=permute, payload_order=payload_order)
     with threadpool_limits(limits=1):
         caches = []
         for s in range(n_streams):
@@ -305,6 +306,8 @@ def main():
                          "(a model's layers): one multi-cache launch against one launch per cache")
     ap.add_argument("--permute", type=int, default=1, choices=(0, 1, 2),
                     help="token order inside blocks: 0 identity, 1 greedy grouping, 2 sort key")
+    ap.add_argument("--payload-order", type=int, default=0, choices=(0, 1),
+                    help="K payload order: 0 by channel, 1 each run row by decreasing width (b <= 4)")
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
                     help="size of a plain device copy run after timing (counter calibration)")
     ap.add_argument("--summarize", metavar="DIR",
@@ -331,7 +334,8 @@ def main():
     t = time.perf_counter()
     K, V = generate(w, torch, dev)
     log(f"inputs generated in {time.perf_counter() - t:.1f} s")
-    cache = PackedKVCache(S, T_max, bits=w.bits, block=w.block, permute=args.permute, device="cuda:0")
+    cache = PackedKVCache(S, T_max, bits=w.bits, block=w.block, permute=args.permute, device="cuda:0",
+                         payload_order=args.payload_order)
     torch.cuda.synchronize()
     t = time.perf_counter()
     cache.compress(K, V)
@@ -340,7 +344,8 @@ def main():
     assert cache.check() == 0
     layer_caches = [cache]
     for _ in range(args.layers - 1):            # the other layers hold the same tokens
-        c2 = PackedKVCache(S, T_max, bits=w.bits, block=w.block, permute=args.permute, device="cuda:0")
+        c2 = PackedKVCache(S, T_max, bits=w.bits, block=w.block, permute=args.permute, device="cuda:0",
+                         payload_order=args.payload_order)
         c2.compress(K, V)
         layer_caches.append(c2)
     # the same tokens in paged caches: every stream at T0, and streams spread
@@ -357,7 +362,8 @@ def main():
             lens = [T0] * S if kind == "uniform" else [T0 - (3 * T0 // 4) * s // S for s in range(S)]
             n_pages = sum(int(np.ceil(1.1 * (L + n_steps) * per_token / page)) + 2 for L in lens) + 16
             pc = PagedKVCache(S, T0 + n_steps + 8, n_pages, page_bytes=page, bits=w.bits, block=w.block,
-                              permute=args.permute, device="cuda:0")
+                              permute=args.permute, device="cuda:0",
+                         payload_order=args.payload_order)
             if kind == "uniform":
                 pc.prefill(0, K, V)
             else:
@@ -652,7 +658,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
-        cpu = cpu_baseline(w, args.cpu_streams, args.cpu_seconds, args.permute)
+        cpu = cpu_baseline(w, args.cpu_streams, args.cpu_seconds, args.permute, args.payload_order)
 
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -667,7 +673,8 @@ def main():
         "data": "synthetic (seeded kvsynth generator; stands in for the pages' models and benchmarks)",
         "config": {"workload": w.key, "batch": w.batch, "kv_heads": w.kv_heads, "group": G,
                    "tokens": T0, "head_dim": D, "bits": w.bits, "block": w.block, "run": 32,
-                   "append_per_step": 1, "permute": args.permute, "parallelism": "single-gpu"},
+                   "append_per_step": 1, "permute": args.permute, "payload_order": args.payload_order,
+                   "parallelism": "single-gpu"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "ms_per_step_median": round(ms_step_med, 4),
         "wall_ms_per_step": round(wall_step, 4),

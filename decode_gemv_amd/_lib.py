@@ -21,7 +21,7 @@ c_int32, c_int64, c_uint64, c_void_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_
 
 class Config(ctypes.Structure):
     _fields_ = [("head_dim", c_int32), ("bits", c_int32), ("block_tokens", c_int32),
-                ("run_tokens", c_int32), ("permute", c_int32)]
+                ("run_tokens", c_int32), ("permute", c_int32), ("payload_order", c_int32)]
 
 
 class CacheT(ctypes.Structure):

@@ -34,11 +34,12 @@ class PackedKVCache:
     """
 
     def __init__(self, n_streams: int, max_tokens: int, bits: int = 4, block: int = 64,
-                 permute: int = 1, device: str = "cuda", head_dim: int = 128):
-        # permute: 0 identity, 1 greedy grouping, 2 sort key (True/False = 1/0)
+                 permute: int = 1, device: str = "cuda", head_dim: int = 128, payload_order: int = 0):
+        # permute: 0 identity, 1 greedy grouping, 2 sort key (True/False = 1/0);
+        # payload_order: 0 by channel, 1 K rows by decreasing width (b <= 4)
         lib = _lib.load()
         self.head_dim = head_dim
-        self.cfg = _lib.Config(head_dim, bits, block, 32, int(permute))
+        self.cfg = _lib.Config(head_dim, bits, block, 32, int(permute), int(payload_order))
         sz = _lib.Sizes()
         _lib.check(lib.packkv_cache_sizes(ctypes.byref(self.cfg), n_streams, max_tokens, ctypes.byref(sz)),
                    "packkv_cache_sizes")
@@ -91,13 +92,14 @@ class PackedKVCache:
         st = {name: getattr(self, name).cpu() for name in self._STATE}
         st["n_tokens"] = self.n_tokens
         st["config"] = (self.n_streams, self.max_tokens, self.bits, self.block, int(self.cfg.permute),
-                        self.head_dim)
+                        self.head_dim, int(self.cfg.payload_order))
         return st
 
     def load_state_dict(self, st: dict) -> None:
         """Restores a state taken by state_dict from a cache of the same
         configuration; appends then continue where that cache stopped."""
-        mine = (self.n_streams, self.max_tokens, self.bits, self.block, int(self.cfg.permute), self.head_dim)
+        mine = (self.n_streams, self.max_tokens, self.bits, self.block, int(self.cfg.permute), self.head_dim,
+                int(self.cfg.payload_order))
         if tuple(st["config"]) != mine:
             raise ValueError(f"state of a cache configured {tuple(st['config'])}, this one is {mine}")
         for name in self._STATE:

@@ -20,6 +20,8 @@ int check_cfg(const packkv_config_t* c) {
   if (c->bits < 2 || c->bits > 8) return PACKKV_EUNSUPPORTED;
   if (c->block_tokens != 64 && c->block_tokens != 128) return PACKKV_EUNSUPPORTED;
   if (c->permute < 0 || c->permute > 2) return PACKKV_EINVAL;
+  if (c->payload_order < 0 || c->payload_order > 1) return PACKKV_EINVAL;
+  if (c->payload_order == 1 && c->bits > 4) return PACKKV_EUNSUPPORTED;
   return PACKKV_OK;
 }
 
@@ -117,6 +119,7 @@ GemvArgs gemv_args(const packkv_cache_t* c, bool is_v, int group = 1) {
   a.D = c->cfg.head_dim;
   a.blocks_per_wg = gemv_blocks_per_wg(c->n_streams, a.nb, is_v, group, c->cfg.bits);
   a.splits = (a.nb + a.blocks_per_wg - 1) / a.blocks_per_wg;
+  a.korder = is_v ? 0 : c->cfg.payload_order;
   a.status = c->status;
   return a;
 }
@@ -128,6 +131,7 @@ EncArgs enc_args(const packkv_cache_t* c) {
   a.B = c->cfg.block_tokens;
   a.D = c->cfg.head_dim;
   a.permute = c->cfg.permute;
+  a.korder = c->cfg.payload_order;
   a.k_arena = c->k_arena;
   a.v_arena = c->v_arena;
   a.arena_stride = c->arena_stride;
@@ -311,6 +315,7 @@ static AttnArgs attention_args(const packkv_cache_t* c, int32_t n, int32_t group
   a.splits = attention_splits((int64_t)c->n_streams * (n < kAttnMaxCaches ? n : kAttnMaxCaches), g.splits, g.nb,
                               c->cfg.block_tokens, c->cfg.bits, group, c->cfg.head_dim);
   a.G = group;
+  a.korder = c->cfg.payload_order;
   a.scale_log2e = scale * 1.4426950408889634f;
   a.qo_stride = (int64_t)c->n_streams * group * c->cfg.head_dim;
   a.D = c->cfg.head_dim;
@@ -329,6 +334,7 @@ static int attention_decode(const packkv_cache_t* const* cs, int32_t n, const vo
     const packkv_cache_t* d = cs[i];
     if ((e = check_cache(d))) return e;
     if (d->cfg.bits != c->cfg.bits || d->cfg.block_tokens != c->cfg.block_tokens || d->cfg.head_dim != c->cfg.head_dim ||
+        d->cfg.payload_order != c->cfg.payload_order ||
         d->n_streams != c->n_streams || d->max_tokens != c->max_tokens || d->n_tokens != c->n_tokens ||
         d->arena_stride != c->arena_stride)
       return PACKKV_EINVAL;
@@ -558,6 +564,7 @@ EncArgs paged_enc_args(const packkv_paged_t* c) {
   a.B = c->cfg.block_tokens;
   a.D = kPagedD;
   a.permute = c->cfg.permute;
+  a.korder = c->cfg.payload_order;
   a.k_arena = c->pool;
   a.v_arena = c->pool;
   a.arena_limit = paged_pool_bytes(&c->cfg, c->n_streams, c->n_pages, c->page_bytes);
@@ -716,6 +723,7 @@ int packkv_paged_attention(const packkv_paged_t* c, const void* q_f16, int32_t g
   a.splits = attention_splits(c->n_streams, (nb + J - 1) / J, nb, B, c->cfg.bits, group, kPagedD);
   a.D = kPagedD;
   a.G = group;
+  a.korder = c->cfg.payload_order;
   a.scale_log2e = scale * 1.4426950408889634f;
   a.q = (const uint16_t*)q_f16;
   a.out = out;

@@ -144,6 +144,23 @@ __device__ __forceinline__ void run_stats(const uint8_t* q, const uint8_t* order
   w = 32u - __clz(hi - lo);
 }
 
+// Payload order 1 of a K record: a run row's entries go by decreasing width,
+// equal widths by channel.  The channel-order word offset of entry (r, c)
+// counts the words of the row's channels below c; the sorted one counts
+// those of the wider channels and of the equally wide ones below c.
+// Returns the difference, from the row's widths wrow[D].
+template <int D>
+__device__ int32_t width_sorted_shift(const uint8_t* wrow, int c, uint32_t w) {
+  int32_t d = 0;
+  for (int c2 = 0; c2 < D; ++c2) {
+    const uint32_t w2 = wrow[c2];
+    const int before_sorted = w2 > w || (w2 == w && c2 < c);
+    const int before_channel = c2 < c;
+    d += (before_sorted - before_channel) * (int32_t)w2;
+  }
+  return d;
+}
+
 // Block-wide (256 threads) exclusive scan of one value per thread.
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh /*[256]*/, uint32_t* total) {
   const int t = threadIdx.x;
@@ -568,9 +585,10 @@ __global__ __launch_bounds__(256) void k_encode(EncArgs a) {
     const uint8_t* q = is_v ? qv : qk;
     const uint32_t w = (is_v ? wv : wk)[rc];
     const uint32_t m = (is_v ? mv : mk)[rc];
-    const uint32_t woff = is_v ? v_ex + v_in[ei] : k_ex + k_in[ei];
     if (w == 0) continue;
     const int r = rc / D, c = rc % D;
+    uint32_t woff = is_v ? v_ex + v_in[ei] : k_ex + k_in[ei];
+    if (!is_v && a.korder == 1) woff += (uint32_t)width_sorted_shift<D>(wk + r * D, c, w);
     uint32_t v[kR];
     run_values<D>(q, order, r, c, n, v);
 #pragma unroll

@@ -101,13 +101,15 @@ __host__ __device__ constexpr int staging_bytes(int rec) {
 }
 
 // Header decode + width scan for the lane's runs (NRL runs per lane, run
-// index l + 64k).  Returns false if the record is inconsistent.  When every
-// run is at full width the offsets are implicit and no scan is needed;
-// `aligned` then reports that every run starts on a 16-byte boundary.
-template <int NRL, int HB = 1>
+// index l + 64k, DL of them per run row of D channels).  Returns false if the
+// record is inconsistent.  When every run is at full width the offsets are
+// implicit and no scan is needed.  wsorted: payload order 1 (each run row by
+// decreasing width, equal widths by channel).
+template <int NRL, int HB = 1, int DL = 2>
 __device__ __forceinline__ bool scan_runs(const uint8_t* rec, int hdr_off, int pay_off, uint32_t size,
                                           int nruns, int bits, int lane,
-                                          int w[NRL], uint32_t m[NRL], uint32_t off[NRL], bool& full) {
+                                          int w[NRL], uint32_t m[NRL], uint32_t off[NRL], bool& full,
+                                          bool wsorted = false) {
   const int L = (1 << bits) - 1;
   bool bad = false, narrow = false;
 #pragma unroll
@@ -128,6 +130,25 @@ __device__ __forceinline__ bool scan_runs(const uint8_t* rec, int hdr_off, int p
 #pragma unroll
     for (int k = 0; k < NRL; ++k) off[k] = (uint32_t)((lane + 64 * k) * bits);
     base = (uint32_t)(NRL * 64 * bits);
+  } else if (wsorted) {
+    base = 0;
+    for (int r = 0; r < NRL / DL; ++r) {
+      uint32_t above = 0;                               // words of the row's wider entries
+      for (int j = 0; j < DL; ++j) off[r * DL + j] = base;
+      for (int v = bits; v >= 1; --v) {
+        uint32_t before = 0;                            // width-v entries of lower channel groups
+        for (int j = 0; j < DL; ++j) {
+          const int k = r * DL + j;
+          const uint64_t mk = __ballot(w[k] == v);
+          const uint32_t rank = before + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+          if (w[k] == v) off[k] = base + above + rank * (uint32_t)v;
+          before += (uint32_t)__builtin_popcountll(mk);
+        }
+        above += before * (uint32_t)v;
+      }
+      base += above;
+    }
   } else {
     base = 0;
 #pragma unroll
@@ -168,6 +189,38 @@ struct BlockDecoder {
   static constexpr int HDR = hdr_offset(IS_V, B, D);
   static constexpr int HW = NR * D / 4;             // header dwords of a full block
 
+  // Word offsets of the lane's runs in payload order 1: in run row r the
+  // entries of width v follow every wider entry of the row, in channel
+  // order (run k = r*DL + j holds channel lane + 64j).  Runs of width 0 get
+  // the row's start (they hold no words; the reads there stay inside the
+  // record).  Returns the payload's words.
+  __device__ __forceinline__ static uint32_t sorted_offsets(const uint32_t h[NRL], uint32_t off[NRL]) {
+    uint32_t row_base = 0;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      uint32_t above = 0;                               // words of the row's wider entries
+#pragma unroll
+      for (int j = 0; j < DL; ++j) off[r * DL + j] = row_base;
+#pragma unroll
+      for (int v = BITS; v >= 1; --v) {
+        uint32_t before = 0;                            // width-v entries of lower channel groups
+#pragma unroll
+        for (int j = 0; j < DL; ++j) {
+          const int k = r * DL + j;
+          const bool mine = (int)(h[k] >> 4) == v;
+          const uint64_t m = __ballot(mine);
+          const uint32_t rank =
+              before + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          if (mine) off[k] = row_base + above + rank * (uint32_t)v;
+          before += (uint32_t)__builtin_popcountll(m);
+        }
+        above += before * (uint32_t)v;
+      }
+      row_base += above;
+    }
+    return row_base;
+  }
+
   // Decode the lane's runs of the staged record into container words
   // nib[k][0..3] (run l + 64k).  Returns false if the record is inconsistent
   // (a width above BITS, a minimum that leaves no room for its width, or
@@ -176,8 +229,11 @@ struct BlockDecoder {
   // a block holding narrower runs (or a partial block) corrects them with
   // the width deficit of earlier runs, and its narrow runs are re-decoded at
   // the end.  Both corrections are uniform branches taken by few blocks.
+  // wsorted: the K payload is in order 1 (each run row by decreasing width,
+  // equal widths by channel); a row of equal widths is then laid out as in
+  // order 0, so only the narrow-run branch differs.
   __device__ __forceinline__ static bool decode(const uint8_t* rec, uint32_t size, int nr, int lane,
-                                                uint32_t nib[NRL][4]) {
+                                                uint32_t nib[NRL][4], bool wsorted = false) {
     const int pay = payload_offset(IS_V, B, nr, 1, D);
     const int nruns = nr * D;
     uint32_t h[NRL];
@@ -217,6 +273,9 @@ struct BlockDecoder {
       // max <= L, so its containers m + u never carry into the next slot
 #pragma unroll
       for (int i = 0; i < HWL; ++i) bad |= hdr4_bad<BITS>(hx[i]);
+      if (!IS_V && wsorted) {
+        total = sorted_offsets(h, off);
+      } else {
       uint32_t running = 0;                            // deficit of earlier groups
 #pragma unroll
       for (int k = 0; k < NRL; ++k) {
@@ -239,6 +298,7 @@ struct BlockDecoder {
         }
       }
       total -= running;
+      }
     }
     const bool ok = __ballot(bad) == 0 && (uint32_t)pad16(pay + 4 * (int)total) == size;
     // container words: all reads are issued first.  At 4 bits a run's words
@@ -388,7 +448,8 @@ __device__ __forceinline__ void store_partial(float* dst, float v) {
   __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int B, int BITS, int GT, int D>
+// WS: the records are in payload order 1 (width-sorted rows).
+template <int B, int BITS, int GT, int D, bool WS = false>
 struct KBlock {
   using Dec = BlockDecoder<B, BITS, false, D>;
   static constexpr int NRL = Dec::NRL;
@@ -458,7 +519,7 @@ struct KBlock {
       }
     }
     uint32_t nib[NRL][4];
-    const bool ok = Dec::decode(rec, size, nr, lane, nib);
+    const bool ok = Dec::decode(rec, size, nr, lane, nib, WS);
     wave_sync();                                  // every lane has read the record
     uint32_t* plane = reinterpret_cast<uint32_t*>(rec);
 #pragma unroll
@@ -538,7 +599,7 @@ struct KBlock {
 // that same order (opos), since A and B of the MFMA pair byte b of lane l with
 // the same k.  Each lane (g, token) adds up its query's four digit sums,
 // scales by 2^-E and adds beta.
-template <int B, int BITS, int GT>
+template <int B, int BITS, int GT, bool WS = false>
 struct KBlockM {
   static constexpr int kD = 128;                      // the matrix-core tiles are laid out for D = 128
   using Dec = BlockDecoder<B, BITS, false, kD>;
@@ -634,7 +695,7 @@ struct KBlockM {
       }
     }
     uint32_t nib[NRL][4];
-    const bool ok = Dec::decode(rec, size, nr, lane, nib);
+    const bool ok = Dec::decode(rec, size, nr, lane, nib, WS);
     wave_sync();                                  // every lane has read the record
     uint32_t* plane = reinterpret_cast<uint32_t*>(rec);
 #pragma unroll
@@ -1364,9 +1425,11 @@ struct VBlockW {
 // trips are not repaid by 32 FMAs per packed word.
 // The matrix-core tiles are laid out for D = 128; other head_dims take the
 // vector code for every tile.
-template <int B, int BITS, int GT, int D>
+// WS: payload order 1, taken only up to 4 bits.
+template <int B, int BITS, int GT, int D, bool WS = false>
 using KSel = std::conditional_t<(BITS > 4), KBlockW<B, GT, D>,
-                                std::conditional_t<(GT > 1 && D == 128), KBlockM<B, BITS, GT>, KBlock<B, BITS, GT, D>>>;
+                                std::conditional_t<(GT > 1 && D == 128), KBlockM<B, BITS, GT, WS>,
+                                                   KBlock<B, BITS, GT, D, WS>>>;
 
 // The V block code the kernels use: wide widths take VBlockW; at b <= 4 the
 // matrix cores (VBlockM) for a tile of four queries (D = 128), v_dot8
@@ -1427,10 +1490,12 @@ constexpr int qk_waves_per_eu() {
   return D != 128 ? 1 : B == 64 && BITS <= 3 && GT == 1 ? 6 : B == 128 && BITS <= 4 && GT > 1 ? 3 : 1;
 }
 
-template <int B, int BITS, int GT, int D>
+// WS: the K records are in payload order 1 (a separate instantiation, so
+// that the default one carries none of its code).
+template <int B, int BITS, int GT, int D, bool WS = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(qk_waves_per_eu<B, BITS, GT, D>())))
 void k_qk_gemv(GemvArgs a) {
-  using KB = KSel<B, BITS, GT, D>;
+  using KB = KSel<B, BITS, GT, D, WS>;
   constexpr int REC = max_record_bytes(false, B, BITS, D);
   constexpr int NCH = (REC + 1023) / 1024;
   constexpr int BUF = staging_bytes(REC) > KB::SCRATCH_BYTES ? staging_bytes(REC) : KB::SCRATCH_BYTES;
@@ -1678,10 +1743,10 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 template <int B, int BITS, int GT, int D>
 constexpr int attn_waves_per_eu() { return D != 128 ? 1 : B == 128 ? 3 : B == 64 && BITS == 2 && GT == 1 ? 5 : 1; }
 
-template <int B, int BITS, int GT, int D, bool PAGED>
+template <int B, int BITS, int GT, int D, bool PAGED, bool WS = false>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<B, BITS, GT, D>())))
 void k_attn_decode(AttnArgs a) {
-  using KB = KSel<B, BITS, GT, D>;
+  using KB = KSel<B, BITS, GT, D, WS>;
   using VB = VSel<B, BITS, GT, D, false>;
   constexpr int NH = B / 64;
   constexpr int PF = attn_partial_floats(D);      // floats per split partial
@@ -1955,7 +2020,8 @@ __global__ __launch_bounds__(64) void k_decompress(GemvArgs a, const uint8_t* pe
   int w[NRL];
   uint32_t m[NRL], ro[NRL];
   bool full;
-  if (!scan_runs<NRL, HB>(rec, HDR, pay, size, nr * D, a.bits, lane, w, m, ro, full)) {
+  if (!scan_runs<NRL, HB, D / 64>(rec, HDR, pay, size, nr * D, a.bits, lane, w, m, ro, full,
+                                  a.korder == 1)) {
     if (lane == 0) latch(a.status, PACKKV_ECORRUPT);
     return;
   }
@@ -2141,6 +2207,13 @@ static void dispatch_shape(int B, int bits, int D, F&& f) {
 hipError_t launch_qk(const GemvArgs& a, int B, int n_streams, hipStream_t st) {
   const dim3 grid(n_streams * a.splits);
   dispatch_shape(B, a.bits, a.D, [&]<int BB, int BI, int DD>() {
+    if constexpr (BI <= 4) {
+      if (a.korder == 1) {
+        if (a.G == 1) hipLaunchKernelGGL((k_qk_gemv<BB, BI, 1, DD, true>), grid, dim3(64), 0, st, a);
+        else hipLaunchKernelGGL((k_qk_gemv<BB, BI, 4, DD, true>), grid, dim3(64), 0, st, a);
+        return;
+      }
+    }
     if (a.G == 1) hipLaunchKernelGGL((k_qk_gemv<BB, BI, 1, DD>), grid, dim3(64), 0, st, a);
     else hipLaunchKernelGGL((k_qk_gemv<BB, BI, 4, DD>), grid, dim3(64), 0, st, a);
   });
@@ -2195,12 +2268,26 @@ hipError_t launch_attention(const AttnArgs& a, int B, int n_streams, int n_cache
     if (a.D != 128) return hipErrorInvalidValue;
     dispatch_shape(B, a.bits, 128, [&]<int BB, int BI, int DD>() {
       if constexpr (DD == 128) {
+        if constexpr (BI <= 4) {
+          if (a.korder == 1) {
+            if (a.G == 1) hipLaunchKernelGGL((k_attn_decode<BB, BI, 1, DD, true, true>), grid, dim3(128), 0, st, a);
+            else hipLaunchKernelGGL((k_attn_decode<BB, BI, 4, DD, true, true>), grid, dim3(128), 0, st, a);
+            return;
+          }
+        }
         if (a.G == 1) hipLaunchKernelGGL((k_attn_decode<BB, BI, 1, DD, true>), grid, dim3(128), 0, st, a);
         else hipLaunchKernelGGL((k_attn_decode<BB, BI, 4, DD, true>), grid, dim3(128), 0, st, a);
       }
     });
   } else {
     dispatch_shape(B, a.bits, a.D, [&]<int BB, int BI, int DD>() {
+      if constexpr (BI <= 4) {
+        if (a.korder == 1) {
+          if (a.G == 1) hipLaunchKernelGGL((k_attn_decode<BB, BI, 1, DD, false, true>), grid, dim3(128), 0, st, a);
+          else hipLaunchKernelGGL((k_attn_decode<BB, BI, 4, DD, false, true>), grid, dim3(128), 0, st, a);
+          return;
+        }
+      }
       if (a.G == 1) hipLaunchKernelGGL((k_attn_decode<BB, BI, 1, DD, false>), grid, dim3(128), 0, st, a);
       else hipLaunchKernelGGL((k_attn_decode<BB, BI, 4, DD, false>), grid, dim3(128), 0, st, a);
     });

@@ -34,6 +34,7 @@ struct EncArgs {
   int64_t src_block;        // elements between blocks in the source
   int64_t n_tokens;         // total tokens per stream after this call
   int32_t bits, B, D, permute, mode;
+  int32_t korder;           // payload order of the K records (0 by channel, 1 width-sorted)
   int32_t block0;           // kTail: index of the block being (re)encoded
   // kTail: tokens appended by this call, [S][new_cnt][D] fp16 (new_stream
   // elements apart), at positions new_at.. of the open block; they are read
@@ -78,6 +79,7 @@ struct GemvArgs {
   int32_t blocks_per_wg;
   int32_t splits;        // workgroups per stream
   int32_t G;
+  int32_t korder;        // payload order of K records (0 by channel, 1 width-sorted); 0 for V
   const uint16_t* q;     // K: q [S][G][D] fp16
   const float* p;        // V: p [S][G][ld] fp32
   float* scores;         // K: [S][G][ld]
@@ -114,6 +116,7 @@ struct AttnArgs {
   int32_t blocks_per_wg;
   int32_t splits;
   int32_t G;
+  int32_t korder;        // payload order of the K records (0 by channel, 1 width-sorted)
   float scale_log2e;     // softmax scale times log2(e)
   const uint16_t* q;     // [caches][S][G][D] fp16
   float* out;            // [caches][S][G][D]

@@ -24,9 +24,10 @@ class PagedKVCache:
     tokens each, over a pool of ``n_pages`` pages of ``page_bytes``."""
 
     def __init__(self, n_streams: int, max_tokens: int, n_pages: int, page_bytes: int = 65536,
-                 bits: int = 4, block: int = 64, permute: int = 1, device: str = "cuda"):
+                 bits: int = 4, block: int = 64, permute: int = 1, device: str = "cuda",
+                 payload_order: int = 0):
         lib = _lib.load()
-        self.cfg = _lib.Config(D, bits, block, 32, int(permute))
+        self.cfg = _lib.Config(D, bits, block, 32, int(permute), int(payload_order))
         sz = _lib.PagedSizes()
         _lib.check(lib.packkv_paged_sizes(ctypes.byref(self.cfg), n_streams, max_tokens, n_pages, page_bytes,
                                           ctypes.byref(sz)), "packkv_paged_sizes")

@@ -19,8 +19,9 @@
  *   nr = ceil(n / R) runs of R = 32 slots; hdr = the byte (w << 4) | m for
  *   b <= 4, the little-endian u16 (w << 8) | m for b = 5..8, for the run's
  *   width w = bit_length(max - min) and minimum m; payload = for each run r,
- *   for each channel c, w u32 words holding u = q - m of its 32 slots in the
- *   sliced order: with c-bit containers (c = 4 for b <= 4, 8 above), slot i
+ *   for each channel c (payload_order 0; in order 1 a K record takes the
+ *   channels of each run by decreasing w, equal w by channel), w u32 words
+ *   holding u = q - m of its 32 slots in the sliced order: with c-bit containers (c = 4 for b <= 4, 8 above), slot i
  *   is field j = i % (32/c) of container k = i / (32/c), and bit p of its u
  *   is bit c*j + Q of run word W, where W = k / g, Q = w*(k % g) + p if w
  *   divides c (g = c/w), else W = k, Q = p for k < w and W = p, Q = k for
@@ -72,7 +73,8 @@ enum {
                               a device latch, an input value outside the
                               method's domain (non-finite K/V, a V-GEMV weight
                               that is negative or non-finite)                 */
-  PACKKV_EUNSUPPORTED = 2, /* configuration outside D 64/128/256, b 2..8, B 64/128, R 32 */
+  PACKKV_EUNSUPPORTED = 2, /* configuration outside D 64/128/256, b 2..8, B 64/128, R 32,
+                              or payload order 1 above 4 bits                 */
   PACKKV_ECAPACITY = 3,    /* tokens over max_tokens, or arena region overflow */
   PACKKV_ECORRUPT = 4,     /* a record header is inconsistent                  */
   PACKKV_EHIP = 5,         /* a HIP runtime call or kernel launch failed       */
@@ -92,6 +94,15 @@ typedef struct {
                         /* by the total of the token's K and V ints; modes   */
                         /* 1 and 2 fall back to the identity unless the      */
                         /* block's payload shrinks.  Other values: EINVAL    */
+  int32_t payload_order; /* order of a K record's payload entries (explainer */
+                        /* page, "Block matrix before and after repacking": */
+                        /* a layout that suits the consuming GPU): 0 run-   */
+                        /* major then channel; 1 each run row by decreasing */
+                        /* width, equal widths by channel, so that the      */
+                        /* entries a wave decodes together share a width.   */
+                        /* Headers and V records keep order 0; record sizes */
+                        /* do not change.  1 needs b <= 4 (EUNSUPPORTED     */
+                        /* otherwise); other values: EINVAL                 */
 } packkv_config_t;
 
 /*

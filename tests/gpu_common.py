@@ -43,8 +43,9 @@ def make_kv(law: str, S: int, T: int, block: int, seed: int = 0, D: int = 128):
     return np.stack(ks), np.stack(vs)
 
 
-def oracle_streams(K, V, bits, block, permute=True):
-    cfg = oracle.Config(head_dim=K.shape[2], bits=bits, block=block, permute=permute)
+def oracle_streams(K, V, bits, block, permute=True, payload_order=0):
+    cfg = oracle.Config(head_dim=K.shape[2], bits=bits, block=block, permute=permute,
+                        payload_order=payload_order)
     return [ostream.compress(K[s], V[s], cfg) for s in range(K.shape[0])]
 
 

@@ -28,14 +28,16 @@ def test_every_header_function_is_exported(lib):
     assert set(names) == set(_lib._SIGS), "binding signatures and header disagree"
 
 
-def cfg(bits=4, block=64, D=128, R=32, permute=1):
-    return _lib.Config(D, bits, block, R, permute)
+def cfg(bits=4, block=64, D=128, R=32, permute=1, order=0):
+    return _lib.Config(D, bits, block, R, permute, order)
 
 
 @pytest.mark.parametrize("bad,code", [
     (dict(D=96), _lib.EUNSUPPORTED), (dict(D=512), _lib.EUNSUPPORTED), (dict(bits=9), _lib.EUNSUPPORTED),
     (dict(bits=1), _lib.EUNSUPPORTED),
     (dict(block=32), _lib.EUNSUPPORTED), (dict(R=16), _lib.EUNSUPPORTED), (dict(permute=3), _lib.EINVAL),
+    (dict(order=2), _lib.EINVAL), (dict(order=-1), _lib.EINVAL), (dict(bits=5, order=1), _lib.EUNSUPPORTED),
+    (dict(bits=8, order=1), _lib.EUNSUPPORTED),
 ])
 def test_unsupported_configs_are_rejected(lib, bad, code):
     s = _lib.Sizes()
@@ -229,3 +231,12 @@ def test_stream_read_checks_its_arguments(lib):
     assert lib.packkv_stream_read(fake + 8, 64, fake, None) == _lib.EINVAL     # not 16-byte aligned
     assert lib.packkv_stream_read(fake, 60, fake, None) == _lib.EINVAL         # not a multiple of 16
     assert lib.packkv_stream_read(fake, 0, fake, None) == _lib.EINVAL
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_width_sorted_payload_keeps_the_sizes(lib, bits):
+    """Payload order 1 is accepted up to 4 bits and sizes nothing differently."""
+    a, b = _lib.Sizes(), _lib.Sizes()
+    assert lib.packkv_cache_sizes(ctypes.byref(cfg(bits)), 3, 1000, ctypes.byref(a)) == 0
+    assert lib.packkv_cache_sizes(ctypes.byref(cfg(bits, order=1)), 3, 1000, ctypes.byref(b)) == 0
+    assert bytes(a) == bytes(b)

@@ -22,6 +22,9 @@ CASES = [
     ("b4B64-identity", 4, 64, 0, "struct", 1),
     ("b8B64-gauss", 8, 64, 1, "gauss", 2),
     ("b6B128-struct", 6, 128, 2, "struct", 3),
+    # width-sorted K payload (payload order 1)
+    ("b3B128-struct-wsorted", 3, 128, 1, "struct", 3, 1),
+    ("b4B64-mixed-wsorted", 4, 64, 2, "mixed", 2, 1),
 ]
 
 
@@ -32,16 +35,16 @@ def torch_dev():
     return torch, torch.device("cuda:0")
 
 
-def paged(torch, dev, S, max_tokens, n_pages, page_records, bits, block, permute):
+def paged(torch, dev, S, max_tokens, n_pages, page_records, bits, block, permute, payload_order=0):
     from decode_gemv_amd import PagedKVCache
     from decode_gemv_amd import _lib
     import ctypes
     sz = _lib.PagedSizes()
-    cfg = _lib.Config(128, bits, block, 32, permute)
+    cfg = _lib.Config(128, bits, block, 32, permute, payload_order)
     assert _lib.load().packkv_paged_sizes(ctypes.byref(cfg), S, max_tokens, 1, 1 << 20, ctypes.byref(sz)) == 0
     page = -(-page_records * sz.slot_bytes // 256) * 256
     return PagedKVCache(S, max_tokens, n_pages, page_bytes=page, bits=bits, block=block, permute=permute,
-                        device=str(dev))
+                        device=str(dev), payload_order=payload_order)
 
 
 def check_records(c, refs, lengths):
@@ -89,14 +92,15 @@ def test_ragged_prefill_and_appends_match_oracle(torch_dev, case):
     steps on every stream: records, permutation, tail staging and attention
     equal the oracle's for each stream's tokens at every checkpoint."""
     torch, dev = torch_dev
-    cid, bits, block, permute, law, page_records = case
+    cid, bits, block, permute, law, page_records = case[:6]
+    order = case[6] if len(case) > 6 else 0
     B = block
     start = [0, 1, B, B + 86, 5 * B + 13]
     steps = 70
     S = len(start)
     total = max(start) + steps
     K, V = make_kv(law, S, total, block, seed=3)
-    c = paged(torch, dev, S, total + 4, 64, page_records, bits, block, permute)
+    c = paged(torch, dev, S, total + 4, 64, page_records, bits, block, permute, order)
     for s, n in enumerate(start):
         if n:
             say("paged prefill", cid, s, n)
@@ -106,7 +110,7 @@ def test_ragged_prefill_and_appends_match_oracle(torch_dev, case):
     lengths = list(start)
 
     def refs_now():
-        return [oracle_streams(K[s:s + 1, :n], V[s:s + 1, :n], bits, block, permute)[0] if n else None
+        return [oracle_streams(K[s:s + 1, :n], V[s:s + 1, :n], bits, block, permute, order)[0] if n else None
                 for s, n in enumerate(lengths)]
 
     refs = refs_now()

@@ -54,11 +54,11 @@ def torch_dev():
     return torch, torch.device("cuda:0")
 
 
-def gpu_cache(torch, dev, K, V, bits, block, permute, max_tokens=None):
+def gpu_cache(torch, dev, K, V, bits, block, permute, max_tokens=None, payload_order=0):
     from decode_gemv_amd import PackedKVCache
     S, T, D = K.shape
     c = PackedKVCache(S, max_tokens or T + 70, bits=bits, block=block, permute=permute, device=str(dev),
-                      head_dim=D)
+                      head_dim=D, payload_order=payload_order)
     c.compress(torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev))
     return c
 
