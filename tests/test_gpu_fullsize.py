@@ -115,16 +115,22 @@ def sampled_blocks(torch, dev, c, w, block_kv, cfg, scores, q, rng, closed=None)
     assert worst_out <= TOL, worst_out
 
 
-@pytest.mark.parametrize("name", ["single-head-4k", "llama7b-32k", "gqa-128k", "2bit-16k", "8bit-16k"])
-def test_fullsize_workload(torch_dev, name):
+FULLSIZE = [("single-head-4k", 0), ("llama7b-32k", 0), ("gqa-128k", 0), ("2bit-16k", 0), ("8bit-16k", 0),
+            # clustered tokens in the greedy order, with the K payload by
+            # channel and width-sorted (payload order 1)
+            ("struct-32k", 0), ("struct-32k", 1)]
+
+
+@pytest.mark.parametrize("name,order", FULLSIZE, ids=[f"{n}-order{o}" for n, o in FULLSIZE])
+def test_fullsize_workload(torch_dev, name, order):
     torch, dev = torch_dev
     from decode_gemv_amd import PackedKVCache, softmax_rows
     w = kvsynth.WORKLOADS[name]
     S, G, T, D = w.streams, w.group, w.tokens, w.head_dim
-    cfg = oracle.Config(bits=w.bits, block=w.block)
-    say("fullsize", name, "S", S, "T", T, "G", G)
+    cfg = oracle.Config(bits=w.bits, block=w.block, payload_order=order)
+    say("fullsize", name, "order", order, "S", S, "T", T, "G", G)
     K, V = host_streams(w, T)
-    c = PackedKVCache(S, T + 8, bits=w.bits, block=w.block, device=str(dev))
+    c = PackedKVCache(S, T + 8, bits=w.bits, block=w.block, device=str(dev), payload_order=order)
     c.compress(torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev))
     assert c.check() == 0
     check_offsets_all_streams(c, cfg)
