@@ -2125,7 +2125,8 @@ __global__ __launch_bounds__(64) void k_stats(GemvArgs a, unsigned long long* ou
 
 // Softmax over the first T entries of each row: p = exp(s*scale - max)/sum.
 // One workgroup of 1024 threads per row: an online (max, sum) pass, then the
-// normalising write pass.
+// normalising write pass (k_softmax); few or very long rows are cut into
+// chunks instead (k_softmax_chunk_*, below).
 __device__ __forceinline__ void online_add(float& m, float& sum, float v) {
   if (v > m) {
     sum = sum * __expf(m - v) + 1.0f;
@@ -2141,8 +2142,30 @@ __device__ __forceinline__ void online_merge(float& m, float& sum, float m2, flo
   m = M;
 }
 
+// Four float4 loads per thread are issued before any of them is used (a row
+// is one workgroup, and with few rows the chip's HBM is reached only through
+// loads in flight); the running (max, sum) is updated once per 16 values.
+constexpr int kSoftmaxUnroll = 4;
+
+__device__ __forceinline__ void online_add16(float& m, float& sum, const float4 (&v)[kSoftmaxUnroll], float scale) {
+  float lm = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kSoftmaxUnroll; ++u)
+    lm = fmaxf(lm, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)) * scale);
+  const float M = fmaxf(m, lm);
+  if (M == -INFINITY) return;
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < kSoftmaxUnroll; ++u)
+    s += __expf(v[u].x * scale - M) + __expf(v[u].y * scale - M) + __expf(v[u].z * scale - M) +
+         __expf(v[u].w * scale - M);
+  sum = sum * __expf(m - M) + s;
+  m = M;
+}
+
 __global__ __launch_bounds__(1024) void k_softmax(const float* scores, float* p, int64_t T, int64_t ld,
                                                   float scale) {
+  constexpr int U = kSoftmaxUnroll;
   __shared__ float sm[16], ss[16];
   const float* x = scores + (int64_t)blockIdx.x * ld;
   float* y = p + (int64_t)blockIdx.x * ld;
@@ -2150,15 +2173,23 @@ __global__ __launch_bounds__(1024) void k_softmax(const float* scores, float* p,
   const bool vec = ((ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15) == 0) &&
                    ((reinterpret_cast<uintptr_t>(p) & 15) == 0);
   const int64_t T4 = vec ? (T >> 2) : 0;
+  const float4* x4 = reinterpret_cast<const float4*>(x);
   float m = -INFINITY, sum = 0.f;
-  for (int64_t i = tid; i < T4; i += 1024) {
-    const float4 v = reinterpret_cast<const float4*>(x)[i];
+  int64_t i = tid;
+  for (; i + (U - 1) * 1024 < T4; i += U * 1024) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = x4[i + u * 1024];
+    online_add16(m, sum, v, scale);
+  }
+  for (; i < T4; i += 1024) {
+    const float4 v = x4[i];
     online_add(m, sum, v.x * scale);
     online_add(m, sum, v.y * scale);
     online_add(m, sum, v.z * scale);
     online_add(m, sum, v.w * scale);
   }
-  for (int64_t i = 4 * T4 + tid; i < T; i += 1024) online_add(m, sum, x[i] * scale);
+  for (int64_t k = 4 * T4 + tid; k < T; k += 1024) online_add(m, sum, x[k] * scale);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const float m2 = __shfl_xor(m, o, kWave), s2 = __shfl_xor(sum, o, kWave);
@@ -2168,18 +2199,158 @@ __global__ __launch_bounds__(1024) void k_softmax(const float* scores, float* p,
   __syncthreads();
   m = sm[0];
   sum = ss[0];
-  for (int i = 1; i < 16; ++i) online_merge(m, sum, sm[i], ss[i]);
+  for (int k = 1; k < 16; ++k) online_merge(m, sum, sm[k], ss[k]);
   const float inv = 1.0f / sum;
-  for (int64_t i = tid; i < T4; i += 1024) {
-    const float4 v = reinterpret_cast<const float4*>(x)[i];
+  float4* y4 = reinterpret_cast<float4*>(y);
+  i = tid;
+  for (; i + (U - 1) * 1024 < T4; i += U * 1024) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = x4[i + u * 1024];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float4 r;
+      r.x = __expf(v[u].x * scale - m) * inv;
+      r.y = __expf(v[u].y * scale - m) * inv;
+      r.z = __expf(v[u].z * scale - m) * inv;
+      r.w = __expf(v[u].w * scale - m) * inv;
+      y4[i + u * 1024] = r;
+    }
+  }
+  for (; i < T4; i += 1024) {
+    const float4 v = x4[i];
     float4 r;
     r.x = __expf(v.x * scale - m) * inv;
     r.y = __expf(v.y * scale - m) * inv;
     r.z = __expf(v.z * scale - m) * inv;
     r.w = __expf(v.w * scale - m) * inv;
-    reinterpret_cast<float4*>(y)[i] = r;
+    y4[i] = r;
   }
-  for (int64_t i = 4 * T4 + tid; i < T; i += 1024) y[i] = __expf(x[i] * scale - m) * inv;
+  for (int64_t k = 4 * T4 + tid; k < T; k += 1024) y[k] = __expf(x[k] * scale - m) * inv;
+}
+
+// Chunked softmax for long rows that are too few to fill the chip one
+// workgroup each.  Row r is cut into nchunks chunks of kSoftmaxChunk entries,
+// the last one taking the remainder (so every chunk holds at least two).
+// (1) each chunk's (max, sum) goes to the first two entries of its own range
+// of p; (2) one wave per row merges them and writes the row's (max, 1/sum)
+// over every chunk's pair; (3) each chunk reads its pair, then writes its
+// outputs over the whole range.  p must not alias scores.
+constexpr int kSoftmaxChunk = 8192;
+
+__device__ __forceinline__ void softmax_chunk_range(int c, int nchunks, int64_t T, int64_t& lo, int64_t& hi) {
+  lo = (int64_t)c * kSoftmaxChunk;
+  hi = c == nchunks - 1 ? T : lo + kSoftmaxChunk;
+}
+
+__global__ __launch_bounds__(256) void k_softmax_chunk_stats(const float* scores, float* p, int64_t T, int64_t ld,
+                                                             float scale, int nchunks) {
+  constexpr int U = kSoftmaxUnroll;
+  __shared__ float sm[4], ss[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const float* x = scores + (int64_t)blockIdx.y * ld;
+  int64_t lo, hi;
+  softmax_chunk_range(blockIdx.x, nchunks, T, lo, hi);
+  const bool vec = ((ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15) == 0);
+  // chunk starts are multiples of 4 entries: float4 j covers entries 4j..4j+3
+  const int64_t v0 = vec ? lo / 4 : 0, v1 = vec ? hi / 4 : 0;
+  const float4* x4 = reinterpret_cast<const float4*>(x);
+  float m = -INFINITY, sum = 0.f;
+  int64_t i = v0 + tid;
+  for (; i + (U - 1) * 256 < v1; i += U * 256) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = x4[i + u * 256];
+    online_add16(m, sum, v, scale);
+  }
+  for (; i < v1; i += 256) {
+    const float4 v = x4[i];
+    online_add(m, sum, v.x * scale);
+    online_add(m, sum, v.y * scale);
+    online_add(m, sum, v.z * scale);
+    online_add(m, sum, v.w * scale);
+  }
+  for (int64_t k = (vec ? 4 * v1 : lo) + tid; k < hi; k += 256) online_add(m, sum, x[k] * scale);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, kWave), s2 = __shfl_xor(sum, o, kWave);
+    online_merge(m, sum, m2, s2);
+  }
+  if (lane == 0) { sm[wv] = m; ss[wv] = sum; }
+  __syncthreads();
+  if (tid == 0) {
+    for (int k = 1; k < 4; ++k) online_merge(m, sum, sm[k], ss[k]);
+    float* y = p + (int64_t)blockIdx.y * ld + lo;
+    y[0] = m;
+    y[1] = sum;
+  }
+}
+
+__global__ __launch_bounds__(64) void k_softmax_merge(float* p, int64_t ld, int nchunks) {
+  const int lane = threadIdx.x;
+  float* y = p + (int64_t)blockIdx.x * ld;
+  float m = -INFINITY, sum = 0.f;
+  for (int c = lane; c < nchunks; c += 64) {
+    const int64_t lo = (int64_t)c * kSoftmaxChunk;
+    online_merge(m, sum, y[lo], y[lo + 1]);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, kWave), s2 = __shfl_xor(sum, o, kWave);
+    online_merge(m, sum, m2, s2);
+  }
+  // every lane holds the row's (max, sum) now; the pairs are overwritten
+  // only after all of them were read (one wave, loads before stores)
+  const float inv = 1.0f / sum;
+  for (int c = lane; c < nchunks; c += 64) {
+    const int64_t lo = (int64_t)c * kSoftmaxChunk;
+    y[lo] = m;
+    y[lo + 1] = inv;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_softmax_chunk_norm(const float* scores, float* p, int64_t T, int64_t ld,
+                                                            float scale, int nchunks) {
+  constexpr int U = kSoftmaxUnroll;
+  __shared__ float mi[2];
+  const int tid = threadIdx.x;
+  const float* x = scores + (int64_t)blockIdx.y * ld;
+  float* y = p + (int64_t)blockIdx.y * ld;
+  int64_t lo, hi;
+  softmax_chunk_range(blockIdx.x, nchunks, T, lo, hi);
+  if (tid == 0) { mi[0] = y[lo]; mi[1] = y[lo + 1]; }
+  __syncthreads();                                   // the pair is read before the chunk is written
+  const float m = mi[0], inv = mi[1];
+  const bool vec = ((ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(p) & 15) == 0);
+  const int64_t v0 = vec ? lo / 4 : 0, v1 = vec ? hi / 4 : 0;
+  const float4* x4 = reinterpret_cast<const float4*>(x);
+  float4* y4 = reinterpret_cast<float4*>(y);
+  int64_t i = v0 + tid;
+  for (; i + (U - 1) * 256 < v1; i += U * 256) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = x4[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float4 r;
+      r.x = __expf(v[u].x * scale - m) * inv;
+      r.y = __expf(v[u].y * scale - m) * inv;
+      r.z = __expf(v[u].z * scale - m) * inv;
+      r.w = __expf(v[u].w * scale - m) * inv;
+      y4[i + u * 256] = r;
+    }
+  }
+  for (; i < v1; i += 256) {
+    const float4 v = x4[i];
+    float4 r;
+    r.x = __expf(v.x * scale - m) * inv;
+    r.y = __expf(v.y * scale - m) * inv;
+    r.z = __expf(v.z * scale - m) * inv;
+    r.w = __expf(v.w * scale - m) * inv;
+    y4[i] = r;
+  }
+  for (int64_t k = (vec ? 4 * v1 : lo) + tid; k < hi; k += 256) y[k] = __expf(x[k] * scale - m) * inv;
 }
 
 // ---------------------------------------------------------------------------
@@ -2357,6 +2528,18 @@ hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, h
 
 hipError_t launch_softmax(const float* scores, float* p, int rows, int64_t T, int64_t ld, float scale,
                           hipStream_t st) {
+  // Out of place, with fewer rows than compute units or rows of 64K entries
+  // and more: split every row into chunks (three launches).  Measured:
+  // 128 rows of 131072 entries 96.7 -> 45.4 us, 256 rows of 65792 56.4 ->
+  // 46.2 us; 256 rows of 32768 were slower chunked (31.8 -> 36.2 us).
+  const int64_t nchunks = T / kSoftmaxChunk;
+  if (scores != p && nchunks >= 2 && (rows < 256 || nchunks >= 8) && rows < 1024) {
+    const dim3 grid((unsigned)nchunks, (unsigned)rows);
+    hipLaunchKernelGGL(k_softmax_chunk_stats, grid, dim3(256), 0, st, scores, p, T, ld, scale, (int)nchunks);
+    hipLaunchKernelGGL(k_softmax_merge, dim3(rows), dim3(64), 0, st, p, ld, (int)nchunks);
+    hipLaunchKernelGGL(k_softmax_chunk_norm, grid, dim3(256), 0, st, scores, p, T, ld, scale, (int)nchunks);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_softmax, dim3(rows), dim3(1024), 0, st, scores, p, T, ld, scale);
   return hipGetLastError();
 }

@@ -140,16 +140,32 @@ def test_gemvs_within_tolerance(torch_dev, case, G):
     assert rel_l2(out, ref_o) <= TOL and worst_row_rel(out, ref_o) <= TOL, (rel_l2(out, ref_o), worst_row_rel(out, ref_o))
 
 
-def test_softmax_helper(torch_dev):
+@pytest.mark.parametrize("rows,T,ld", [(5, 1000, 1000), (3, 65537, 65540), (2, 70001, 70003), (1, 4097, 4100)])
+def test_softmax_helper(torch_dev, rows, T, ld):
+    """Rows long enough for the unrolled loads, with a ragged tail, and a
+    leading dimension that rules out vector loads."""
     torch, dev = torch_dev
     from decode_gemv_amd import softmax_rows
-    rng = np.random.default_rng(0)
-    x = (rng.standard_normal((5, 1000)) * 20).astype(np.float32)
-    say("softmax")
-    p = softmax_rows(torch.from_numpy(x).to(dev), 1000, 0.125).cpu().numpy()
-    ref = np.stack([attention.softmax(r.astype(np.float64) * 0.125 * np.sqrt(128), 128) for r in x])
+    rng = np.random.default_rng(T)
+    x = (rng.standard_normal((rows, ld)) * 20).astype(np.float32)
+    say("softmax", rows, T, ld)
+    p = softmax_rows(torch.from_numpy(x).to(dev), T, 0.125).cpu().numpy()[:, :T]
+    ref = np.stack([attention.softmax(r[:T].astype(np.float64) * 0.125 * np.sqrt(128), 128) for r in x])
     assert rel_l2(p, ref) <= TOL and worst_row_rel(p, ref) <= TOL
     assert np.all(np.abs(p.sum(1) - 1) < 1e-5)
+
+
+def test_softmax_helper_in_place(torch_dev):
+    """scores and p may be the same buffer (long rows included)."""
+    torch, dev = torch_dev
+    from decode_gemv_amd import softmax_rows
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((2, 131072)) * 20).astype(np.float32)
+    say("softmax in place")
+    xd = torch.from_numpy(x).to(dev)
+    p = softmax_rows(xd, 131072, 0.125, out=xd).cpu().numpy()
+    ref = np.stack([attention.softmax(r.astype(np.float64) * 0.125 * np.sqrt(128), 128) for r in x])
+    assert rel_l2(p, ref) <= TOL and worst_row_rel(p, ref) <= TOL
 
 
 @pytest.mark.parametrize("bits,block,law", [(4, 64, "mixed"), (2, 128, "struct"), (8, 64, "gauss"), (6, 128, "mixed")])
