@@ -50,15 +50,42 @@ __device__ __forceinline__ float fp8_unit() {
   return v.x;
 }
 
-// 8 slot values of one container word: f[i] = nibble i * unit.
+// Value of one step of the container conversion below.  Up to 3 bits a
+// container nibble holds q <= 3, and the e2m1 (fp4) codes 0..3 are the
+// exact multiples 0, 1, 2, 3 of their smallest subnormal, so a nibble
+// converts as it stands; wider containers go through e4m3 bytes, whose codes
+// 0..15 are likewise exact multiples of theirs.
+template <int BITS>
+__device__ __forceinline__ float container_unit() {
+  if constexpr (BITS <= 2) {
+    f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(1u, 1.0f, 0);
+    return v.x;
+  } else {
+    return fp8_unit();
+  }
+}
+
+// 8 slot values of one container word: f[i] = nibble i * container_unit.
+// At 2 bits each byte (two nibbles) is one fp4 pair conversion; otherwise
+// the nibbles are first spread to bytes for the e4m3 conversion.
+template <int BITS>
 __device__ __forceinline__ void nibbles_to_f32(uint32_t w, float f[8]) {
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-  f[0] = a.x; f[2] = a.y; f[4] = b.x; f[6] = b.y;
-  f[1] = c.x; f[3] = c.y; f[5] = d.x; f[7] = d.y;
+  if constexpr (BITS <= 2) {
+    const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y;
+    f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
+  } else {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+    const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+    const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+    f[0] = a.x; f[2] = a.y; f[4] = b.x; f[6] = b.y;
+    f[1] = c.x; f[3] = c.y; f[5] = d.x; f[7] = d.y;
+  }
 }
 
 // A record is usable only if it lies inside its stream region and fits the
@@ -479,7 +506,7 @@ struct KBlock {
     cg = lane >> 3;
   }
   __device__ __forceinline__ void set_queries(const uint16_t* q, int64_t s, int G, int gq0) {
-    const float unit_inv = 1.0f / fp8_unit();
+    const float unit_inv = 1.0f / container_unit<BITS>();
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       const bool ok = gq0 + g < G;
@@ -515,7 +542,7 @@ struct KBlock {
           qs[g * D + lane + 64 * j] = qu[g][j] * sv[j];
           bz = fmaf(qu[g][j], zv[j], bz);
         }
-        beta[g] = wave_sum(bz) * fp8_unit();
+        beta[g] = wave_sum(bz) * container_unit<BITS>();
       }
     }
     uint32_t nib[NRL][4];
@@ -553,7 +580,7 @@ struct KBlock {
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
           float f[8];
-          nibbles_to_f32(words[cc], f);
+          nibbles_to_f32<BITS>(words[cc], f);
 #pragma unroll
           for (int g = 0; g < GT; ++g)
 #pragma unroll
