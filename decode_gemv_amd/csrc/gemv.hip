@@ -30,6 +30,7 @@
 namespace packkv {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -493,9 +494,15 @@ struct KBlock {
   static constexpr int HALF_BYTES = 8 * ROWW * 4;
   static_assert(RED_BYTES <= HALF_BYTES, "reduction must fit a half's plane rows");
   static constexpr int SCRATCH_BYTES = PLANE_BYTES;
-  static constexpr int QS_BYTES = GT * D * 4;
+  // From 3 bits on a container nibble reaches 7 (15), past the linear fp4
+  // codes.  There the nibbles are masked into the low bits of 16-bit halves
+  // instead: nibble 2i of a half is an fp16 subnormal n * 2^-24, nibble 2i+1
+  // one of 16 n * 2^-24, both exact, and the mixed-precision FMA takes the
+  // half as it stands.  q' is kept twice, the second copy divided by 16.
+  static constexpr bool HALVES = BITS >= 3;
+  static constexpr int QS_BYTES = GT * D * 4 * (HALVES ? 2 : 1);
 
-  float* qs;                                          // [GT][D] q' of the block
+  float* qs;                                          // [GT][D] q' of the block (then [GT][D] q' / 16)
   int lane, g8, cg;
   float qu[GT][DL];                                   // queries / unit at channels lane + 64j
 
@@ -506,7 +513,7 @@ struct KBlock {
     cg = lane >> 3;
   }
   __device__ __forceinline__ void set_queries(const uint16_t* q, int64_t s, int G, int gq0) {
-    const float unit_inv = 1.0f / container_unit<BITS>();
+    const float unit_inv = HALVES ? 0x1p24f : 1.0f / container_unit<BITS>();
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       const bool ok = gq0 + g < G;
@@ -539,10 +546,12 @@ struct KBlock {
         float bz = 0.f;
 #pragma unroll
         for (int j = 0; j < DL; ++j) {
-          qs[g * D + lane + 64 * j] = qu[g][j] * sv[j];
+          const float v = qu[g][j] * sv[j];
+          qs[g * D + lane + 64 * j] = v;
+          if constexpr (HALVES) qs[(GT + g) * D + lane + 64 * j] = v * 0.0625f;   // exact
           bz = fmaf(qu[g][j], zv[j], bz);
         }
-        beta[g] = wave_sum(bz) * container_unit<BITS>();
+        beta[g] = wave_sum(bz) * (HALVES ? 0x1p-24f : container_unit<BITS>());
       }
     }
     uint32_t nib[NRL][4];
@@ -571,20 +580,41 @@ struct KBlock {
         const int c0 = cg * CW + ((i4 + cg) % NQ) * 4;
         const u32x4 nw = *reinterpret_cast<const u32x4*>(&plane[row * ROWW + c0]);
         const uint32_t words[4] = {nw.x, nw.y, nw.z, nw.w};
-        float qq[GT][4];
+        float qq[GT][4], qh[GT][4];
 #pragma unroll
         for (int g = 0; g < GT; ++g) {
           const float4 t = *reinterpret_cast<const float4*>(&qs[g * D + c0]);
           qq[g][0] = t.x; qq[g][1] = t.y; qq[g][2] = t.z; qq[g][3] = t.w;
+          if constexpr (HALVES) {
+            const float4 u = *reinterpret_cast<const float4*>(&qs[(GT + g) * D + c0]);
+            qh[g][0] = u.x; qh[g][1] = u.y; qh[g][2] = u.z; qh[g][3] = u.w;
+          }
         }
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-          float f[8];
-          nibbles_to_f32<BITS>(words[cc], f);
+          if constexpr (HALVES) {
+            // halves k: slots k (low) and k + 4 (high), 16x for odd k
+            const uint32_t x = words[cc], y = x >> 8;
+            const uint32_t hw[4] = {x & 0x000F000Fu, x & 0x00F000F0u, y & 0x000F000Fu, y & 0x00F000F0u};
 #pragma unroll
-          for (int g = 0; g < GT; ++g)
+            for (int k = 0; k < 4; ++k) {
+              const f16x2 hh = __builtin_bit_cast(f16x2, hw[k]);
+              const float lo = (float)hh.x, hi = (float)hh.y;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(qq[g][cc], f[i], acc[g][i]);
+              for (int g = 0; g < GT; ++g) {
+                const float qv = (k & 1) ? qh[g][cc] : qq[g][cc];
+                acc[g][k] = fmaf(qv, lo, acc[g][k]);
+                acc[g][k + 4] = fmaf(qv, hi, acc[g][k + 4]);
+              }
+            }
+          } else {
+            float f[8];
+            nibbles_to_f32<BITS>(words[cc], f);
+#pragma unroll
+            for (int g = 0; g < GT; ++g)
+#pragma unroll
+              for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(qq[g][cc], f[i], acc[g][i]);
+          }
         }
       }
       // reduce the 8 channel groups, one query at a time, in this half's
