@@ -1982,25 +1982,21 @@ void k_attn_decode(AttnArgs a) {
   if (wave != 1 || !last_to_arrive(&tickets[s], a.splits, lane)) return;
   // Merge: the largest split max M first (lanes across splits), then each
   // split's sums scaled by 2^(m_i - M).  A half-wave takes every other split
-  // (in split order) and a lane NPL = D/32 of the outputs; the loads of four
-  // splits per half-wave are issued together.
+  // (in split order) and a lane NPL = D/32 of the outputs; the loads of NU
+  // splits per half-wave are issued together, those of the first NU before
+  // the max is known, so that up to 2 NU splits cost two memory round trips.
   constexpr int NPL = D / 32;
+  constexpr int NU = NPL <= 4 ? 8 : 4;
   const int half = lane >> 5, d0 = (lane & 31) * NPL;
   constexpr uint32_t PB = PF * 4;                   // bytes per partial
   for (int g = 0; g < a.G; ++g) {
     const float* src = ws + ((int64_t)s * a.G + g) * a.splits * PF;
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(src, (uint32_t)a.splits * PB);
-    float M = NEG_INF;
-    for (int i = lane; i < a.splits; i += 64) M = fmaxf(M, load_partial(src + (int64_t)i * PF + D));
-    M = wave_max_f(M);
-    float L = 0.f, o[NPL];
+    uint32_t v[NU][NPL];
+    u32x2 ml[NU];
+    auto load_batch = [&](int i0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < NPL; ++k) o[k] = 0.f;
-    for (int i0 = 0; i0 < a.splits; i0 += 8) {
-      uint32_t v[4][NPL];
-      u32x2 ml[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < NU; ++u) {
         const uint32_t off = (uint32_t)(i0 + 2 * u + half) * PB;   // past the end reads zeros
         if constexpr (NPL == 2) {
           const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * d0, 0, kCoherent));
@@ -2017,8 +2013,18 @@ void k_attn_decode(AttnArgs a) {
         }
         ml[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * D, 0, kCoherent));
       }
+    };
+    load_batch(0);
+    float M = NEG_INF;
+    for (int i = lane; i < a.splits; i += 64) M = fmaxf(M, load_partial(src + (int64_t)i * PF + D));
+    M = wave_max_f(M);
+    float L = 0.f, o[NPL];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+    for (int k = 0; k < NPL; ++k) o[k] = 0.f;
+    for (int i0 = 0; i0 < a.splits; i0 += 2 * NU) {
+      if (i0 > 0) load_batch(i0);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
         const bool in = i0 + 2 * u + half < a.splits && M != NEG_INF;
         const float f = in ? fast_exp2(__uint_as_float(ml[u].x) - M) : 0.f;
         L = fmaf(__uint_as_float(ml[u].y), f, L);
