@@ -45,48 +45,24 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-__device__ __forceinline__ float fp8_unit() {
-  // value of the e4m3 byte 0x01; every byte n <= 15 converts to exactly n * unit
-  f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(1u, false);
+// Value of the e2m1 (fp4) code 1.  Up to 2 bits a container nibble holds
+// at most 4 in any record whose header passes the checks (m + 2^(w-1) <= 3
+// bounds m + 2^w - 1 by 4), and the fp4 codes 0..4 are exactly 0, 1, 2, 3, 4
+// times it, so such a nibble converts as it stands.
+__device__ __forceinline__ float fp4_unit() {
+  f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(1u, 1.0f, 0);
   return v.x;
 }
 
-// Value of one step of the container conversion below.  Up to 3 bits a
-// container nibble holds q <= 3, and the e2m1 (fp4) codes 0..3 are the
-// exact multiples 0, 1, 2, 3 of their smallest subnormal, so a nibble
-// converts as it stands; wider containers go through e4m3 bytes, whose codes
-// 0..15 are likewise exact multiples of theirs.
-template <int BITS>
-__device__ __forceinline__ float container_unit() {
-  if constexpr (BITS <= 2) {
-    f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(1u, 1.0f, 0);
-    return v.x;
-  } else {
-    return fp8_unit();
-  }
-}
-
-// 8 slot values of one container word: f[i] = nibble i * container_unit.
-// At 2 bits each byte (two nibbles) is one fp4 pair conversion; otherwise
-// the nibbles are first spread to bytes for the e4m3 conversion.
-template <int BITS>
-__device__ __forceinline__ void nibbles_to_f32(uint32_t w, float f[8]) {
-  if constexpr (BITS <= 2) {
-    const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-    const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-    const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-    const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-    f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y;
-    f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
-  } else {
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
-    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-    const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-    const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-    f[0] = a.x; f[2] = a.y; f[4] = b.x; f[6] = b.y;
-    f[1] = c.x; f[3] = c.y; f[5] = d.x; f[7] = d.y;
-  }
+// 8 slot values of one container word (2-bit runs): f[i] = nibble i *
+// fp4_unit, each byte (two nibbles) one fp4 pair conversion.
+__device__ __forceinline__ void nibbles_to_f32_fp4(uint32_t w, float f[8]) {
+  const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y;
+  f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
 }
 
 // A record is usable only if it lies inside its stream region and fits the
@@ -494,11 +470,14 @@ struct KBlock {
   static constexpr int HALF_BYTES = 8 * ROWW * 4;
   static_assert(RED_BYTES <= HALF_BYTES, "reduction must fit a half's plane rows");
   static constexpr int SCRATCH_BYTES = PLANE_BYTES;
-  // From 3 bits on a container nibble reaches 7 (15), past the linear fp4
-  // codes.  There the nibbles are masked into the low bits of 16-bit halves
-  // instead: nibble 2i of a half is an fp16 subnormal n * 2^-24, nibble 2i+1
-  // one of 16 n * 2^-24, both exact, and the mixed-precision FMA takes the
-  // half as it stands.  q' is kept twice, the second copy divided by 16.
+  // Slot values for the FMAs.  At 2 bits a container word goes through four
+  // fp4 pair conversions (nibbles_to_f32_fp4).  From 3 bits on a nibble
+  // reaches 7 (15), past the linear fp4 codes; there the nibbles are masked
+  // into the low bits of 16-bit halves: nibble 2i of a half is an fp16
+  // subnormal n * 2^-24, nibble 2i+1 one of 16 n * 2^-24, both exact, and the
+  // mixed-precision FMA takes the half as it stands.  q' is then kept twice,
+  // the second copy divided by 16.
+  static_assert(BITS >= 2 && BITS <= 4, "one-byte headers and 4-bit containers");
   static constexpr bool HALVES = BITS >= 3;
   static constexpr int QS_BYTES = GT * D * 4 * (HALVES ? 2 : 1);
 
@@ -513,7 +492,7 @@ struct KBlock {
     cg = lane >> 3;
   }
   __device__ __forceinline__ void set_queries(const uint16_t* q, int64_t s, int G, int gq0) {
-    const float unit_inv = HALVES ? 0x1p24f : 1.0f / container_unit<BITS>();
+    const float unit_inv = HALVES ? 0x1p24f : 1.0f / fp4_unit();
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       const bool ok = gq0 + g < G;
@@ -551,7 +530,7 @@ struct KBlock {
           if constexpr (HALVES) qs[(GT + g) * D + lane + 64 * j] = v * 0.0625f;   // exact
           bz = fmaf(qu[g][j], zv[j], bz);
         }
-        beta[g] = wave_sum(bz) * (HALVES ? 0x1p-24f : container_unit<BITS>());
+        beta[g] = wave_sum(bz) * (HALVES ? 0x1p-24f : fp4_unit());
       }
     }
     uint32_t nib[NRL][4];
@@ -609,7 +588,7 @@ struct KBlock {
             }
           } else {
             float f[8];
-            nibbles_to_f32<BITS>(words[cc], f);
+            nibbles_to_f32_fp4(words[cc], f);
 #pragma unroll
             for (int g = 0; g < GT; ++g)
 #pragma unroll
