@@ -157,6 +157,21 @@ __device__ __forceinline__ void narrow_to_nibbles(int w, uint32_t m, uint32_t x0
   out[3] = ((two ? x1 >> 2 : x0 >> 3) & mask) + mm;
 }
 
+// A run of width w = 0 .. 3 (below a full width of 4) from its first three
+// payload words, without a branch on w: widths 0, 1 and 2 as in
+// narrow_to_nibbles, width 3 as in sliced_to_nibbles<3>, one of the two
+// chosen per lane.  Where a wave's narrow runs come in several widths this
+// replaces one masked pass per width present.
+__device__ __forceinline__ void narrow4_to_nibbles(int w, uint32_t m, const uint32_t wd[4], uint32_t out[4]) {
+  uint32_t lo[4], w3[4];
+  narrow_to_nibbles(w, m, wd[0], wd[1], lo);
+  sliced_to_nibbles<3>(wd, w3);
+  const uint32_t mm = nibble_splat(m);
+  const bool three = w == 3;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) out[k] = three ? w3[k] + mm : lo[k];
+}
+
 // A run stored at the full width BITS: its BITS words -> four container words.
 template <int BITS>
 __device__ __forceinline__ void full_to_nibbles(const uint32_t wd[4], uint32_t out[4]) {

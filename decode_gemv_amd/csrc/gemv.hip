@@ -357,7 +357,11 @@ struct BlockDecoder {
               uint32_t wd[4];
 #pragma unroll
               for (int i = 0; i < 4; ++i) wd[i] = nib[k][i] - mm;
-              run_to_nibbles<3>(w, h[k] & 15u, wd, nib[k]);
+              // K: one branch-free pass for every width (1-2 % faster on
+              // clustered data); V keeps the pass per width present, whose
+              // registers its block loop can afford
+              if constexpr (!IS_V) narrow4_to_nibbles(w, h[k] & 15u, wd, nib[k]);
+              else run_to_nibbles<3>(w, h[k] & 15u, wd, nib[k]);
             } else {
               const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + pay) + off[k];
               narrow_to_nibbles(w, h[k] & 15u, p[0], BITS == 3 ? p[1] : 0u, nib[k]);
