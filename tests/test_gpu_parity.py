@@ -325,6 +325,53 @@ def test_corrupt_wide_header_is_reported_not_used(torch_dev, entry):
     assert c.check() == 0
 
 
+@pytest.mark.parametrize("payload", ["all-three", "random"])
+def test_two_bit_slot_values_up_to_four(torch_dev, payload):
+    """At 2 bits the K side turns container nibbles into floats as e2m1
+    (fp4) codes, which are exact multiples of one step only up to 4.  A
+    header entry that passes every check (w = 2, m = 1) lets an altered
+    payload hold m + u = 4, the largest value such a record can carry; the K
+    GEMV and fused attention must read those bytes as the oracle's record
+    decoder does (records here are altered bytes, not encoder output)."""
+    torch, dev = torch_dev
+    D, B = 128, 64
+    K, V = make_kv("gauss", 1, B, B)
+    c = gpu_cache(torch, dev, K, V, 2, B, False)
+    hdr = 4 * D                                   # K header after scale and zero
+    pay = (hdr + 2 * D + 15) // 16 * 16           # two run rows of one-byte entries
+    arena = c.arena("K")
+    w_row0 = arena[0, hdr:hdr + D].cpu().numpy() >> 4
+    full = np.nonzero(np.cumprod(w_row0 == 2))[0]  # channels after only full-width runs of row 0
+    assert full.size >= 4, "gauss data at 2 bits: the first runs are at full width"
+    ch = int(full[3])                              # run (0, ch) starts at word 2 * ch
+    arena[0, hdr + ch] = (2 << 4) | 1
+    rng = np.random.default_rng(7)
+    words = np.full(8, 0xFF, np.uint8) if payload == "all-three" else rng.integers(0, 256, 8).astype(np.uint8)
+    arena[0, pay + 8 * ch:pay + 8 * ch + 8] = torch.from_numpy(words).to(dev)
+    koff = c.offsets("K").cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+    voff = c.offsets("V").cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+    kbuf = arena[0, koff[0, 0]:koff[0, 1]].cpu().numpy().tobytes()
+    vbuf = c.arena("V")[0, voff[0, 0]:voff[0, 1]].cpu().numpy().tobytes()
+    dk = ounpack.decode_record("K", kbuf, B, D, B, 32)
+    dv = ounpack.decode_record("V", vbuf, B, D, B, 32)
+    assert dk.q[:, ch].max() == 4 if payload == "all-three" else dk.q[:, ch].max() <= 4
+    k_hat = dk.zero[None, :] + dk.scale[None, :] * dk.q          # slot order, fp64
+    v_hat = dv.zero[:, None] + dv.scale[:, None] * dv.q
+    qn = rng.standard_normal((1, 1, D)).astype(np.float16)
+    q = torch.from_numpy(qn).to(dev)
+    say("two-bit slot values up to four", payload, "channel", ch)
+    sc = c.qk(q)
+    assert c.check() == 0
+    want = attention.qk(qn[0].astype(np.float64), k_hat)
+    got = sc[0, :, :B].cpu().numpy()
+    assert rel_l2(got, want) <= TOL and worst_row_rel(got, want) <= TOL
+    out = c.attention(q)
+    assert c.check() == 0
+    want_o = attention.pv(attention.softmax(want, D), v_hat)
+    got_o = out[0].cpu().numpy()
+    assert rel_l2(got_o, want_o) <= TOL and worst_row_rel(got_o, want_o) <= TOL
+
+
 @pytest.mark.parametrize("bad", ["negative", "nan", "inf"])
 @pytest.mark.parametrize("bits,G", [(4, 1), (3, 4), (8, 1)])
 def test_pv_rejects_weights_outside_its_domain(torch_dev, bad, bits, G):
