@@ -1156,8 +1156,7 @@ struct DecW {
     const uint16_t* hd = reinterpret_cast<const uint16_t*>(rec + HDR);
     int w[NRL];
     uint32_t m[NRL], off[NRL];
-    bool bad = false;
-    uint32_t base = 0;
+    bool bad = false, narrow = nr != NR;
 #pragma unroll
     for (int k = 0; k < NRL; ++k) {
       const int ri = lane + 64 * k;
@@ -1166,19 +1165,44 @@ struct DecW {
       m[k] = h & 255u;
       // a valid run has max - m in [2^(w-1), 2^w - 1] and max <= L
       bad |= w[k] > bits || (int)m[k] > L || (w[k] > 0 && (int)m[k] + (1 << (w[k] - 1)) > L);
-      const int incl = wave_incl_scan(w[k]);
-      off[k] = base + (uint32_t)(incl - w[k]);
-      base += (uint32_t)__builtin_amdgcn_readlane(incl, 63);
+      narrow |= w[k] != bits;
+    }
+    // a full block whose runs are all at the full width has implicit offsets
+    // (run i at word i * bits); otherwise a wave prefix sum of the widths
+    const bool all_full = __ballot(narrow) == 0;
+    uint32_t base = 0;
+    if (all_full) {
+#pragma unroll
+      for (int k = 0; k < NRL; ++k) off[k] = (uint32_t)((lane + 64 * k) * bits);
+      base = (uint32_t)(NRL * 64 * bits);
+    } else {
+#pragma unroll
+      for (int k = 0; k < NRL; ++k) {
+        const int incl = wave_incl_scan(w[k]);
+        off[k] = base + (uint32_t)(incl - w[k]);
+        base += (uint32_t)__builtin_amdgcn_readlane(incl, 63);
+      }
     }
     const bool ok = __ballot(bad) == 0 && (uint32_t)pad16(pay + 4 * (int)base) == size;
     const uint32_t* pw = reinterpret_cast<const uint32_t*>(rec + pay);
+    // at the full width 8 every run is 32 bytes at a 32-byte boundary: two
+    // 16-byte reads instead of eight dword reads 32 bytes apart across the
+    // lanes (which fall in the same banks)
+    const bool wide8 = all_full && bits == 8 && ok;
 #pragma unroll
     for (int k = 0; k < NRL; ++k) {
       // a consistent record keeps every run's words inside it
       const int wr = ok ? w[k] : 0;
       uint32_t wd[8];
+      if (wide8) {
+        const u32x4 a = reinterpret_cast<const u32x4*>(pw + off[k])[0];
+        const u32x4 b = reinterpret_cast<const u32x4*>(pw + off[k])[1];
+        wd[0] = a.x; wd[1] = a.y; wd[2] = a.z; wd[3] = a.w;
+        wd[4] = b.x; wd[5] = b.y; wd[6] = b.z; wd[7] = b.w;
+      } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) wd[i] = i < wr ? pw[off[k] + i] : 0u;
+        for (int i = 0; i < 8; ++i) wd[i] = i < wr ? pw[off[k] + i] : 0u;
+      }
       switch (wr) {
         case 0: spread<0>(wd, cont[k]); break;
         case 1: spread<1>(wd, cont[k]); break;
