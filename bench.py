@@ -198,6 +198,12 @@ def summarize_profile(pdir: str, workload: str) -> None:
             durs.setdefault(short(r["Kernel_Name"]), []).append(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     med = {k: float(np.median(v)) for k, v in durs.items()}
+    # the launches in the order they ran, for the timed-loop figures below
+    seq = []
+    if os.path.exists(trace):
+        rows = sorted(csv.DictReader(open(trace)), key=lambda r: int(r["Start_Timestamp"]))
+        seq = [(short(r["Kernel_Name"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+               for r in rows]
     bench_line = None
     for line in open(os.path.join(pdir, "kt.log")):
         if line.startswith("{") and '"metric"' in line:
@@ -260,6 +266,31 @@ def summarize_profile(pdir: str, workload: str) -> None:
     for k, (n, avg, mn, mx) in sorted(stats.items(), key=lambda x: -x[1][0] * x[1][1]):
         m = f"{med[k]:.1f}" if k in med else "-"
         lines.append(f"| {k} | {n} | {avg:.1f} | {m} | {mn:.1f} | {mx:.1f} |")
+    # The launches the bench line's HIP events time: in the fused loop each
+    # attention launch follows a cache flush and the append; the GEMVs run
+    # in the separate loop only.  Warm-up steps first, then the timed ones.
+    warm, steps = int(bench_line.get("warmup", 0)), int(bench_line.get("steps", 0))
+    timed = {}
+    if seq and gemvs["attn"]:
+        timed["attn"] = [d for i, (n, d) in enumerate(seq) if n == gemvs["attn"] and i >= 2
+                         and seq[i - 1][0].startswith("k_encode")
+                         and "FillFunctor<unsigned char>" in seq[i - 2][0]][warm:warm + steps]
+    for tag in ("qk", "pv"):
+        if seq and gemvs[tag]:
+            timed[tag] = [d for n, d in seq if n == gemvs[tag]][warm:warm + steps]
+    if any(timed.values()):
+        ev = bench_line.get("kernels_ms_mean", {})
+        evk = {"attn": "attention", "qk": "qk_gemv", "pv": "pv_gemv"}
+        lines += ["", "## Launches of the timed loops", "",
+                  "The same launches as the bench line's HIP events (its `kernels_ms_mean`); the table "
+                  "above also counts the clock warm-up and the paged loops.", "",
+                  "| kernel | launches | mean us | median us | HIP events, mean us |", "|---|---|---|---|---|"]
+        for tag, v in timed.items():
+            if v:
+                e = ev.get(evk[tag])
+                lines.append(f"| {gemvs[tag]} | {len(v)} | {np.mean(v):.1f} | {np.median(v):.1f} | "
+                             f"{e * 1e3:.1f} |" if e is not None else
+                             f"| {gemvs[tag]} | {len(v)} | {np.mean(v):.1f} | {np.median(v):.1f} | - |")
     lines += ["", "## HBM traffic per launch", "",
               f"1 GiB device copy: FETCH_SIZE {copy.get('FETCH_SIZE', 0):.0f} KiB, WRITE_SIZE "
               f"{copy.get('WRITE_SIZE', 0):.0f} KiB, so fetch factor {f_fetch and round(f_fetch, 4)}, "
