@@ -152,6 +152,31 @@ def host_cpu() -> dict:
     return {"cpu_model": model, "cpu_count": os.cpu_count(), "cpus_usable": usable}
 
 
+def gpu_info(torch) -> dict:
+    """The device and software measured on: name, architecture, compute
+    units, HIP version, and the engine and memory clocks rocm-smi reports at
+    the call (None where a field cannot be read)."""
+    import re
+    import subprocess
+    pr = torch.cuda.get_device_properties(0)
+    info = {"name": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count,
+            "hip": torch.version.hip, "sclk_mhz": None, "mclk_mhz": None}
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                             timeout=20).stdout
+        for card in json.loads(out).values():
+            for k, v in card.items():
+                m = re.search(r"(\d+)\s*Mhz", str(v), re.I)
+                if m and "sclk" in k.lower() and info["sclk_mhz"] is None:
+                    info["sclk_mhz"] = int(m.group(1))
+                if m and "mclk" in k.lower() and info["mclk_mhz"] is None:
+                    info["mclk_mhz"] = int(m.group(1))
+            break
+    except Exception:
+        pass
+    return info
+
+
 def load_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if current."""
     if not os.path.exists(TRAFFIC_FILE):
@@ -554,6 +579,7 @@ def main():
         e[4].record()
 
     sep_ms_step, _, _, sev = timed_loop(separate_step, 5)
+    gpu = gpu_info(torch)                    # clocks read right after the timed loops
     kb2, vb2, nb2 = used_bytes()
     t_qk, t_sm, t_pv = avg_ms(sev, 1, 2), avg_ms(sev, 2, 3), avg_ms(sev, 3, 4)
     m_qk, m_sm, m_pv = med_ms(sev, 1, 2), med_ms(sev, 2, 3), med_ms(sev, 3, 4)
@@ -730,6 +756,7 @@ def main():
         "multi_layer": multi,
         "paged": paged_res,
         "alg_bytes_per_launch": {"attn": int(attn_alg), "qk": int(qk_alg), "pv": int(pv_alg)},
+        "gpu": gpu,
         "kernel_source": kernel_source_hash(),
     }
     print(json.dumps(res), flush=True)
