@@ -19,9 +19,12 @@
 //   4. K: the containers go to an LDS plane [slot group][channel] and every
 //      lane reduces 16 channels for 8 slots; V: each lane accumulates its own
 //      channels over the run's 32 slots directly from registers.
-// Integers become floats through v_cvt_pk_f32_fp8 (two per instruction): a
-// byte n <= 15 read as an fp8 e4m3 number is exactly n * c for a power of two
-// c, and 1/c is folded into the dense operand.
+// Integers become floats exactly, with the conversion's power of two folded
+// into the dense operand: at 2 bits each byte of a container word goes
+// through one fp4 pair conversion (the e2m1 codes 0..4 are exact multiples
+// of their step); at 3 and 4 bits nibbles masked into 16-bit halves are fp16
+// subnormals that the mixed-precision FMA reads as they stand; bytes of the
+// wide (5..8-bit) containers convert one at a time.
 #include <atomic>
 #include <type_traits>
 
@@ -429,11 +432,10 @@ struct RecordTable {
 //
 // The record's containers go to an LDS plane [slot group][channel] (row
 // pitch D + 8 words; the quad order rotates per channel group).  Lane (g8,
-// cg) then covers 8 slots x D/8 channels: each container word becomes 8
-// floats through 4
-// v_cvt_pk_f32_fp8 (a byte n <= 15 read as e4m3 is exactly n * 2^-9; 2^9 is
-// folded into q'), one FMA per element, and an LDS transpose sums the 8
-// channel groups.  Lane l ends with the scores of slots h*64 + l.
+// cg) then covers 8 slots x D/8 channels: each container word gives the 8
+// slot values exactly (fp4 pair conversions at 2 bits, fp16-subnormal halves
+// at 3 and 4 bits; see HALVES), one FMA per element, and an LDS transpose
+// sums the 8 channel groups.  Lane l ends with the scores of slots h*64 + l.
 // v[g] for a lane-dependent g, as a chain of selects.  Each candidate is made
 // opaque first: the compiler otherwise recognises the chain as v[g] and
 // indexes a copy of v in scratch memory.
