@@ -6,8 +6,9 @@
 //   * zero = group minimum (fp16, -0 stored as +0);
 //   * scale = smallest positive fp16 h with h * L >= max - min (exact fp64
 //     comparisons on fp16 values), 0 for a constant group;
-//   * q = rint((x - min) / scale) in fp64 (exact subtraction, IEEE division,
-//     round half to even), clamped to [0, L];
+//   * q = the level nearest to (x - min) / scale, ties to even (what rint of
+//     the correctly rounded fp64 quotient gives), clamped to [0, L]; found
+//     from a reciprocal and an exact residual (quant_level);
 //   * permutation = greedy L1 grouping with key (distance, index), or (mode
 //     2) the tokens sorted by (total of their K and V ints, index); identity
 //     unless the payload shrinks strictly;
@@ -50,7 +51,7 @@ __device__ __forceinline__ uint32_t f16_of_key(int k) {
 
 // Step and zero of a group from its min and max keys (the oracle's rule).
 struct QuantParams {
-  double mn, h;
+  double mn, h, inv, half;                           // inv = 1/h rounded once, half = h/2 exactly
   uint32_t hb, zero;
 };
 __device__ __forceinline__ QuantParams quant_params(int kmin, int kmax, int L) {
@@ -60,16 +61,28 @@ __device__ __forceinline__ QuantParams quant_params(int kmin, int kmax, int L) {
   const double d = f16_bits_to_double(mxb) - p.mn;
   p.hb = d > 0.0 ? min_f16_step(d, L) : 0u;
   p.h = f16_bits_to_double(p.hb);
+  p.inv = p.hb ? 1.0 / p.h : 0.0;
+  p.half = 0.5 * p.h;
   p.zero = mnb;                                      // +0 for a zero minimum
   return p;
 }
-// Level of one value: round half to even of the exact quotient (the fp64
-// subtraction is exact and the division correctly rounded), clamped to [0, L].
+// Level of one value: the level nearest to the exact quotient d / h
+// (d = x - min, an exact fp64 subtraction), ties to even, clamped to [0, L],
+// without a division per value.  d is a multiple of 2^-24 and h an fp16, so
+// a quotient that is not a tie lies at least 2^-25 / h >= 2^-41 from every
+// half-way point, while d * inv is within 2^-44 of it (the quotient is at
+// most 255): rint(d * inv) is then the nearest level.  At a tie it may land
+// on either neighbour; the residual e = t h - d is exact (t h has at most 20
+// significant bits, both terms are multiples of 2^-24 below 2^17), equals
+// +-h/2 exactly there, and then the even neighbour is taken.
 __device__ __forceinline__ uint32_t quant_level(uint32_t x, const QuantParams& p, int L) {
   if (!p.hb) return 0u;
-  double r = rint((f16_bits_to_double(x) - p.mn) / p.h);
-  r = r < 0.0 ? 0.0 : (r > (double)L ? (double)L : r);
-  return (uint32_t)r;
+  const double d = f16_bits_to_double(x) - p.mn;
+  const double t = rint(d * p.inv);
+  const double e = fma(t, p.h, -d);
+  int q = (int)t;
+  if (fabs(e) == p.half && (q & 1)) q += e > 0.0 ? -1 : 1;
+  return (uint32_t)min(max(q, 0), L);
 }
 
 // The ints of run r, channel c in slot order: v[i] = q[order[r*32 + i]][c]
