@@ -1750,19 +1750,51 @@ void k_pv_gemv(GemvArgs a) {
   if (corrupt && lane == 0) latch(a.status, PACKKV_ECORRUPT);
   if (invalid && lane == 0) latch(a.status, PACKKV_EINVAL);
   if (!last_to_arrive(&a.tickets[s], a.splits, lane)) return;
-  constexpr int DL = D / 64;
+  // Merge in a fixed order: a half-wave adds up every other split (even
+  // splits in half 0, odd in half 1, each in split order) for NPL = D/32
+  // channels per lane, then the two halves are added.  The coherent loads
+  // of NU splits per half-wave are issued together, so 2 NU splits cost one
+  // memory round trip; a split past the last one reads zeros.
+  constexpr int NPL = D / 32;
+  constexpr int NU = NPL <= 4 ? 8 : 4;
+  constexpr uint32_t PB = D * 4;                    // bytes per partial
+  const int half = lane >> 5, d0 = (lane & 31) * NPL;
   for (int g = 0; g < a.G; ++g) {
     const float* src = a.ws + ((int64_t)s * a.G + g) * a.splits * D;
-    float sum[DL];
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(src, (uint32_t)a.splits * PB);
+    float o[NPL];
 #pragma unroll
-    for (int j = 0; j < DL; ++j) sum[j] = 0.f;
-#pragma unroll 8
-    for (int i = 0; i < a.splits; ++i)
+    for (int k = 0; k < NPL; ++k) o[k] = 0.f;
+    for (int i0 = 0; i0 < a.splits; i0 += 2 * NU) {
+      uint32_t v[NU][NPL];
 #pragma unroll
-      for (int j = 0; j < DL; ++j) sum[j] += load_partial(src + (int64_t)i * D + lane + 64 * j);
-    float* dst = a.out + ((int64_t)s * a.G + g) * D;
+      for (int u = 0; u < NU; ++u) {
+        const uint32_t off = (uint32_t)(i0 + 2 * u + half) * PB + 4u * (uint32_t)d0;
+        if constexpr (NPL == 2) {
+          const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCoherent));
+          v[u][0] = t[0];
+          v[u][1] = t[1];
+        } else {
 #pragma unroll
-    for (int j = 0; j < DL; ++j) dst[lane + 64 * j] = sum[j];
+          for (int c = 0; c < NPL; c += 4) {
+            const u32x4 t = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * c, 0, kCoherent));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[u][c + k] = t[k];
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int k = 0; k < NPL; ++k) o[k] += __uint_as_float(v[u][k]);
+    }
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) o[k] += __shfl_xor(o[k], 32, kWave);
+    if (half == 0) {
+      float* dst = a.out + ((int64_t)s * a.G + g) * D + d0;
+#pragma unroll
+      for (int c = 0; c < NPL; ++c) dst[c] = o[c];   // out needs only 4-byte alignment
+    }
   }
   reset_ticket(&a.tickets[s], lane);
 }
