@@ -3,7 +3,6 @@
 // here; every buffer belongs to the caller.
 #include <string.h>
 
-#include <algorithm>
 #include <cmath>
 #include <mutex>
 
@@ -276,16 +275,6 @@ int packkv_pv_gemv(const packkv_cache_t* c, const float* p, int64_t ld, int32_t 
   if (c->n_tokens < 1) return PACKKV_ESTATE;
   if (ld < c->n_tokens) return PACKKV_EINVAL;
   GemvArgs a = gemv_args(c, true, group);
-  // The V GEMV alone (fused attention keeps the shared division): at 3 and 4
-  // bits with one query and head_dim 128, twice the blocks per workgroup,
-  // about one round of one-wave workgroups instead of two.  Measured A/B in
-  // one process (30 rounds): append-64k 196.6 -> 184.7 us, llama7b-32k
-  // 119.6 -> 115.8 us; at 2 and 8 bits and with four queries it was slower or
-  // the same.  The workspace holds any division of at least 4 blocks.
-  if (group == 1 && c->cfg.head_dim == 128 && (c->cfg.bits == 3 || c->cfg.bits == 4)) {
-    a.blocks_per_wg = std::min(64, 2 * a.blocks_per_wg);
-    a.splits = (a.nb + a.blocks_per_wg - 1) / a.blocks_per_wg;
-  }
   a.G = group;
   a.p = p;
   a.ld = ld;
