@@ -73,7 +73,12 @@ int gemv_blocks_per_wg(int64_t n_streams, int nb, bool split_merge, int group, i
     j = bits <= 3 && group == 1 ? 4 : 2;
   }
   else {
-    j = (n_streams * (int64_t)nb + 7679) / 7680;
+    // at 3 bits with one query, about four rounds instead of two (shorter
+    // workgroups): measured in bench.py's step at append-64k, three
+    // alternating processes each, V GEMV 230.3 -> 220.5 us and fused
+    // attention 389.4 -> 387.1 us
+    const int64_t per = bits == 3 && group == 1 ? 15360 : 7680;
+    j = (n_streams * (int64_t)nb + per - 1) / per;
     j += j & 1;
     // several queries per block: twice the blocks, so the split partials
     // (one per query) stay few; measured with 4 queries and 128-token
